@@ -1,0 +1,183 @@
+"""Seeded synthetic inputs for the routed MoE layer and its decode traces.
+
+This module is the only code shared by the HIP path's harness and the CPU
+oracle.  It holds no step of the method: it draws random numbers, rounds them
+to the storage formats the layer consumes (bf16), lays expert weights out as
+host records, and generates routing traces.
+
+Citations: [FT] is the paper "FreeToken: Efficient Edge-Native MoE Serving with
+Bandwidth-Adaptive Execution" (arXiv 2608.16157).
+
+Record layout (one complete (layer, expert) pair, [FT] §3 and §4.2 "Expert banks"
+-- every tensor needed to evaluate one layer-expert pair sits in one record so a
+cache fill is one contiguous copy): bf16 words, row-major,
+
+    [ W_gate (d_ff x d) | W_up (d_ff x d) | W_down (d x d_ff) ]
+
+Host pool: records indexed by the flattened id  row = l_phys * E + e  ([FT] §4.2,
+banks use l*E+e as their leading dimension).  When the logical pool does not
+fit host memory the pool holds L_phys < L physical layers and logical layer l
+reads physical layer l mod L_phys; keys, bytes moved and timing are unchanged.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+STREAM_ROUTER = 0
+STREAM_EXPERT = 1
+STREAM_X = 2
+STREAM_TRACE = 3
+
+
+@dataclass(frozen=True)
+class Shape:
+    """Shape of one stack of routed MoE layers."""
+
+    L: int
+    E: int
+    d: int
+    d_ff: int
+    k: int
+
+    @property
+    def record_elems(self) -> int:
+        return 3 * self.d * self.d_ff
+
+    @property
+    def record_bytes(self) -> int:
+        return 2 * self.record_elems
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic workload (sizes and distributions of the pages' configurations)."""
+
+    name: str
+    config_id: int
+    shape: Shape
+    T: int
+    cache_rate: float  # fraction of the L*E (layer, expert) pairs the GPU cache holds
+    zipf_alpha: float = 1.1
+    reuse: float = 0.6
+    steps: int = 512
+
+    @property
+    def n_slots(self) -> int:
+        # N = floor(rate * L * E)
+        return int(np.floor(self.cache_rate * self.shape.L * self.shape.E + 1e-9))
+
+
+WORKLOADS = {
+    # single layer, all experts resident
+    "c1": Workload("c1-layer-d256-E8-top2", 1, Shape(1, 8, 256, 512, 2), 16, 1.0),
+    # decode: 40 layers, d=2048, E=128, top-8, d_ff=768, cache at 37 %
+    "c2": Workload("c2-decode-L40-d2048-E128-top8", 2, Shape(40, 128, 2048, 768, 8), 1, 0.37),
+    "c2b8": Workload("c2-decode-L40-d2048-E128-top8-b8", 2, Shape(40, 128, 2048, 768, 8), 8, 0.37),
+    # decode: 43 layers, d=4096, E=256, top-6, d_ff=2048, cache at 11 %
+    "c3": Workload("c3-decode-L43-d4096-E256-top6", 3, Shape(43, 256, 4096, 2048, 6), 1, 0.11),
+    # prefill: 8192-token chunk through the c3 layer shape
+    "c4": Workload("c4-prefill8k-L43-d4096-E256-top6", 4, Shape(43, 256, 4096, 2048, 6), 8192, 0.11),
+}
+
+
+def generator(config_id: int, stream: int, *extra: int, seed: int = 0) -> np.random.Generator:
+    """PCG64 stream keyed by (config, stream, extra...) under one base seed."""
+    ss = np.random.SeedSequence(entropy=seed, spawn_key=(config_id, stream) + tuple(int(e) for e in extra))
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """Round float values to bf16 (round to nearest, ties to even); returns uint16 words."""
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b) -> np.ndarray:
+    """Widen bf16 words to float32 (exact)."""
+    b = np.ascontiguousarray(np.asarray(b, dtype=np.uint16))
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def router_weights(w: Workload, layer: int, seed: int = 0) -> np.ndarray:
+    """W_r for one layer: bf16 words [E, d], values N(0, 0.02^2)."""
+    s = w.shape
+    g = generator(w.config_id, STREAM_ROUTER, layer, seed=seed)
+    return f32_to_bf16_bits(g.normal(0.0, 0.02, size=(s.E, s.d)))
+
+
+def expert_record(w: Workload, layer_phys: int, expert: int, seed: int = 0) -> np.ndarray:
+    """One expert record (bf16 words, layout in the module docstring), values N(0, 0.02^2)."""
+    s = w.shape
+    g = generator(w.config_id, STREAM_EXPERT, layer_phys, expert, seed=seed)
+    return f32_to_bf16_bits(g.normal(0.0, 0.02, size=s.record_elems))
+
+
+def host_pool_numpy(w: Workload, L_phys: int, seed: int = 0) -> np.ndarray:
+    """The whole host pool as uint16 [L_phys * E, record_elems] (small workloads only)."""
+    s = w.shape
+    pool = np.empty((L_phys * s.E, s.record_elems), dtype=np.uint16)
+    for lp in range(L_phys):
+        for e in range(s.E):
+            pool[lp * s.E + e] = expert_record(w, lp, e, seed=seed)
+    return pool
+
+
+def tokens(w: Workload, step: int, layer: int, T: int | None = None, seed: int = 0) -> np.ndarray:
+    """Layer input x for (step or chunk, layer): bf16 words [T, d], values N(0, 1)."""
+    s = w.shape
+    T = w.T if T is None else T
+    g = generator(w.config_id, STREAM_X, step, layer, seed=seed)
+    return f32_to_bf16_bits(g.normal(0.0, 1.0, size=(T, s.d)))
+
+
+def zipf_reuse_trace(L: int, E: int, k: int, B: int, steps: int, alpha: float, reuse: float,
+                     rng: np.random.Generator) -> np.ndarray:
+    """Routing trace int16 [steps, L, B, k] (expert ids ascending within a row).
+
+    Per layer a random permutation assigns popularity ranks; rank r has weight
+    (r+1)^-alpha.  Each batch stream is independent.  Step 0 draws k distinct
+    experts without replacement from the popularity law; every later step keeps
+    each of the previous step's k experts independently with probability
+    `reuse` and draws the rest without replacement, excluding the kept ones.
+    Sequential draws without replacement are taken as the top-k of
+    log-weight + Gumbel noise, which has the same law.
+    """
+    ranks = np.stack([rng.permutation(E) for _ in range(L)])  # ranks[l, r] = expert of rank r
+    logw_rank = -alpha * np.log(np.arange(1, E + 1, dtype=np.float64))
+    logw = np.empty((L, E))
+    logw[np.arange(L)[:, None], ranks] = logw_rank[None, :]
+    out = np.empty((steps, L, B, k), dtype=np.int16)
+    prev = None
+    li = np.arange(L)[:, None, None]
+    bi = np.arange(B)[None, :, None]
+    for s in range(steps):
+        key = logw[:, None, :] + rng.gumbel(size=(L, B, E))
+        if prev is not None:
+            keep = rng.random((L, B, k)) < reuse
+            kk = np.where(keep, np.inf, key[li, bi, prev])
+            key[li, bi, prev] = kk
+        sel = np.argpartition(-key, k - 1, axis=2)[:, :, :k]
+        sel.sort(axis=2)
+        out[s] = sel.astype(np.int16)
+        prev = sel
+    return out
+
+
+def trace_for(w: Workload, seed: int = 0, steps: int | None = None) -> np.ndarray:
+    s = w.shape
+    g = generator(w.config_id, STREAM_TRACE, seed=seed)
+    return zipf_reuse_trace(s.L, s.E, s.k, w.T, w.steps if steps is None else steps,
+                            w.zipf_alpha, w.reuse, g)
+
+
+def allowed_mask(trace_row: np.ndarray, E: int) -> np.ndarray:
+    """uint8 [B, E]: 1 where the trace routes token b to expert e."""
+    B = trace_row.shape[0]
+    m = np.zeros((B, E), dtype=np.uint8)
+    m[np.arange(B)[:, None], trace_row.astype(np.int64)] = 1
+    return m
