@@ -1,0 +1,299 @@
+/*
+ * ft.h -- C ABI of libft: a routed mixture-of-experts layer served from an
+ * elastic GPU expert cache over a host-resident expert pool, on one AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Citations:
+ *   [FT]  the paper "FreeToken: Efficient Edge-Native MoE Serving with
+ *         Bandwidth-Adaptive Execution" (arXiv 2608.16157), by section/equation.
+ *   [AIN] the page "FreeToken: bandwidth-adaptive edge MoE serving"
+ *         (ai-infrastructure.net), by section heading.
+ *
+ * Conventions
+ *   - Every call returns an int status: FT_OK (0), a negative error code, or a
+ *     positive warning.  No exception crosses the ABI.  ft_last_error() gives a
+ *     thread-local message for the last failing call on the calling thread.
+ *   - "device" pointers are HIP device allocations (e.g. torch CUDA tensors on
+ *     ROCm); "host" pointers are ordinary host memory; "pinned" pointers are
+ *     page-locked host memory from hipHostMalloc (ft_pool_alloc) or torch
+ *     pin_memory.  The caller owns every buffer it passes in; the library never
+ *     frees caller memory.
+ *   - Streams and events are passed as void* (hipStream_t / hipEvent_t).  A NULL
+ *     stream is HIP's default stream.  Kernel launches are asynchronous: a
+ *     launch error returns FT_EHIP, a fault inside a kernel surfaces at the next
+ *     synchronising call.
+ *   - bf16 tensors are arrays of uint16 words (the top half of an IEEE binary32).
+ *     Matrices are row-major.
+ *   - A context (ft_ctx_t) may be used by one host thread at a time.
+ *
+ * Expert record (the unit of residency, [FT] §3: a slot holds every tensor of
+ * one (layer, expert) pair; [FT] §4.2: banks are indexed by l*E + e): one
+ * contiguous record per expert, bf16, row-major:
+ *     [ W_gate (d_ff x d) | W_up (d_ff x d) | W_down (d x d_ff) ]
+ * S = ft_record_bytes(shape) = 6 * d * d_ff bytes.  The host pool holds L_phys*E
+ * records; logical layer l, expert e reads record (l mod L_phys)*E + e.
+ */
+#ifndef FT_H
+#define FT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define FT_OK 0
+#define FT_EINVAL (-1)        /* bad argument, shape or state */
+#define FT_ENOMEM (-2)        /* a host or pinned allocation failed, or a buffer is too small */
+#define FT_EBUSY (-3)         /* not at a safe point ([FT] §3.3: rebuild only at a safe point) */
+#define FT_ENOPIN (-4)        /* host pool is not pinned memory; fills are impossible ([FT] §4.2) */
+#define FT_ECAP (-5)          /* prefill overlap requested with fewer than 2E slots
+                                 ([AIN] "Failure modes": asserted at construction) */
+#define FT_EHIP (-6)          /* a HIP call failed */
+#define FT_EUNSUPPORTED (-7)  /* format or mode not built */
+#define FT_WOVERLAP_OFF 1     /* warning: resize left fewer than 2E slots, prefill overlap
+                                 disabled ([AIN] "Failure modes": warn-and-disable on rebuild) */
+
+#define FT_PLAN_CAP 512       /* max routed pairs T*k in one decode call */
+
+typedef enum { FT_W_BF16 = 0, FT_W_MXFP4 = 1 } ft_wfmt;
+
+/* Layer-stack shape.  L layers, E routed experts per layer, hidden size d,
+ * expert hidden size d_ff, k experts per token.  d and d_ff must be multiples of 8. */
+typedef struct {
+  int32_t L, E, d, d_ff, k;
+  int32_t fmt; /* ft_wfmt; only FT_W_BF16 is built */
+} ft_shape;
+
+/* Engine configuration ([AIN] "How to use it", flags table).
+ *   frac_q16        fetch fraction phi = B_P/B_H in Q16, computed once ([FT] Eq. 4;
+ *                   ft_frac_q16).
+ *   min_fill        fills kept per call even when the split gives fewer, capped at m
+ *                   ([FT] §3.2 "always retains at least one fill"; 0 = the shipped rule).
+ *   max_fetch       -1: q from the split; n >= 0: at most n fills per call (0 never fetches).
+ *   cpu_threads     worker threads of the CPU branch (0 = one per CPU in the affinity mask).
+ *   prefill_overlap 1 = full-layer double-buffered prefill ([FT] §3.1); needs >= 2E slots.
+ *   T_max           largest T of any call (sizes the workspace).
+ *   L_phys          physical layers in the host pool (0 = L). */
+typedef struct {
+  uint32_t frac_q16;
+  int32_t min_fill;
+  int32_t max_fetch;
+  int32_t cpu_threads;
+  int32_t prefill_overlap;
+  int32_t T_max;
+  int32_t L_phys;
+} ft_config;
+
+/* Decisions of one decode call ([FT] §3.2, §4.1 "Device-side cache control").
+ * U: distinct routed experts in first-occurrence order over (t, j), t-major.
+ * H: hits, M: misses (both in U order).  F = M[0:q] is filled into F_slot[i];
+ * C = M[q:] runs on the host.  G = H followed by F are the experts evaluated on
+ * the GPU, in slots G_slot.  route_slot[t*k+j] is the slot of the pair's expert
+ * or -1 (host); pair_group[t*k+j] its index in G or -1.  idx/gates are the
+ * router's output for the call (filled by ft_moe_decode_layer). */
+typedef struct {
+  int32_t layer, T, k;
+  int32_t n_u, n_h, n_m, q, n_c, avail;
+  int32_t U[FT_PLAN_CAP];
+  int32_t H[FT_PLAN_CAP];
+  int32_t M[FT_PLAN_CAP];
+  int32_t F_slot[FT_PLAN_CAP];
+  int32_t G_slot[FT_PLAN_CAP];
+  int32_t route_slot[FT_PLAN_CAP];
+  int32_t pair_group[FT_PLAN_CAP];
+  int32_t idx[FT_PLAN_CAP];
+  float gates[FT_PLAN_CAP];
+} ft_plan;
+
+/* Per-call measurements (host clock, microseconds). */
+typedef struct {
+  int32_t layer, T, n_u, hits, misses, q, n_c, reserved;
+  int64_t h2d_bytes;
+  double t_route_us;   /* router launch until its results reached the host */
+  double t_ctrl_us;    /* cache decisions */
+  double t_cpu_us;     /* CPU branch, from post to completion */
+  double t_total_us;   /* whole call, host side */
+} ft_step_stats;
+
+/* Cumulative counters since create or the last resize ([AIN] "How to run it in
+ * production": a rebuild resets hit/miss counters).  unique_* count distinct
+ * experts per call; read_* count routed (token, expert) pairs. */
+typedef struct {
+  int64_t calls, unique_hits, unique_misses, fills, cpu_experts;
+  int64_t reads, read_hits, read_fills, read_cpu;
+  int64_t h2d_bytes, prefill_layers, resizes;
+} ft_stats;
+
+typedef struct ft_ctx* ft_ctx_t;
+
+/* ---- errors ------------------------------------------------------------- */
+const char* ft_strerror(int status);
+const char* ft_last_error(void);
+
+/* ---- sizes and the split ----------------------------------------------- */
+
+/* Bytes of one expert record (S), 0 for an invalid shape. */
+size_t ft_record_bytes(const ft_shape* shape);
+
+/* Device workspace bytes a context needs for calls of up to T_max tokens. */
+size_t ft_workspace_bytes(const ft_shape* shape, int32_t T_max);
+
+/* [FT] Eq. (4): phi = B_P / B_H in Q16, rounded half to even; 0 when B_P <= 0,
+ * 65536 when B_P >= B_H (no residual host bandwidth, [FT] Eq. 2).  Bandwidths in
+ * any common unit. */
+uint32_t ft_frac_q16(double B_P, double B_H);
+
+/* Fetch count q for m unique misses ([FT] §3.2 Eqs. 1-4; [AIN] "The split, and
+ * what it is actually optimising"): lo = floor(m*fq/2^16); pick lo or lo+1,
+ * whichever has the smaller max(f*(2^16-fq), (m-f)*fq), lo on a tie; cap at m;
+ * raise to min(min_fill, m); cap at max_fetch when max_fetch >= 0; cap at avail
+ * (slots that may be evicted).  Returns q >= 0, or FT_EINVAL for m < 0 or
+ * frac_q16 > 65536. */
+int32_t ft_qstar_split(int32_t m, uint32_t frac_q16, int32_t min_fill, int32_t max_fetch,
+                       int32_t avail);
+
+/* ---- host pool -------------------------------------------------------------
+ * [FT] §3.3 pins the pool after filling it; here pinned memory must be allocated
+ * first (hipHostMalloc) and filled afterwards.  ft_pool_alloc returns pinned,
+ * host-cached, device-accessible memory owned by the caller, to be released with
+ * ft_pool_free.  Errors: FT_ENOMEM, FT_EHIP. */
+int ft_pool_alloc(size_t bytes, void** out);
+int ft_pool_free(void* ptr);
+
+/* Measures B_P (pinned host->device copies of whole records, `n_records` of them,
+ * on a fresh stream) and B_H (the host expert kernel over the same records at one
+ * token, `threads` workers; 0 = all) in bytes per second ([FT] §3.2, Table 1:
+ * both measured on the deployed tensor shapes).  dev_scratch must hold
+ * n_records records. */
+int ft_bench_bw(const ft_shape* shape, const void* host_pool, int32_t n_records,
+                void* dev_scratch, int32_t threads, double* B_P, double* B_H);
+
+/* ---- context -----------------------------------------------------------------
+ * host_pool: pinned pool of L_phys*E records (may be NULL for a decisions-only
+ * context: lookups and resizes work, device calls return FT_EINVAL).
+ * dev_slots: device buffer of n_slots records (the elastic cache, [FT] §3).
+ * dev_workspace: device buffer of at least ft_workspace_bytes(shape, T_max).
+ * The library allocates its pinned staging buffers and starts its CPU worker
+ * pool here.  Errors: FT_EINVAL (shape/config), FT_ECAP (prefill_overlap and
+ * n_slots < 2E), FT_ENOPIN (host_pool not pinned), FT_ENOMEM, FT_EHIP. */
+int ft_create(const ft_shape* shape, const ft_config* config, const void* host_pool,
+              size_t pool_bytes, void* dev_slots, int32_t n_slots, void* dev_workspace,
+              size_t workspace_bytes, ft_ctx_t* out);
+int ft_destroy(ft_ctx_t ctx);
+
+int ft_get_stats(ft_ctx_t ctx, ft_stats* out);
+int ft_reset_stats(ft_ctx_t ctx);
+int ft_get_config(ft_ctx_t ctx, ft_config* out);
+int32_t ft_n_slots(ft_ctx_t ctx);
+
+/* ---- kernels (stateless; usable without a context) -------------------------- */
+
+/* Router ([FT] §3.2: the router runs on the GPU and picks k experts per token).
+ * x: device bf16 [T, d]; w_router: device bf16 [E, d]; allowed: device uint8
+ * [T, E] or NULL (only allowed experts are ranked; each row must allow >= k).
+ * Logits are fp32 in a fixed order: element i belongs to lane (i mod 512)/8 of 64
+ * lanes, each lane adds its products in increasing i, then a_l += a_(l xor o) for
+ * o = 32..1, result lane 0.  Top-k by (logit desc, index asc), renormalised
+ * softmax gates.  Outputs (device): idx int32 [T, k] in rank order, gates fp32
+ * [T, k], logits fp32 [T, E].  Requires 1 <= k <= min(E, 8), E <= 1024,
+ * d % 8 == 0.  logits is required (it is the router's scratch between its two
+ * kernels); pass the same buffer back to read the logits. */
+int ft_router_topk(const void* x, const void* w_router, const uint8_t* allowed, int32_t T,
+                   int32_t d, int32_t E, int32_t k, int32_t* idx, float* gates, float* logits,
+                   void* stream);
+
+/* Stable grouping of P pairs by key (device int32 [P], -1 = left out) into
+ * n_groups groups: offsets int32 [n_groups+1] (exclusive prefix sum of counts),
+ * perm int32 [P] (pair ids ordered by (key, id); entries past offsets[n_groups]
+ * are unspecified), inv int32 [P] (position in perm or -1).  workspace: device,
+ * ft_permute_workspace_bytes(P, n_groups) bytes. */
+size_t ft_permute_workspace_bytes(int32_t P, int32_t n_groups);
+int ft_permute(const int32_t* key, int32_t P, int32_t n_groups, int32_t* offsets,
+               int32_t* perm, int32_t* inv, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* Grouped SwiGLU expert FFN over groups [g_begin, g_end):
+ *   out[i] = W_down (silu(W_gate x_t) * (W_up x_t))  for i in [offsets[g], offsets[g+1]),
+ *   t = perm[i] / k, with the record at slots + group_slot[g] * S.
+ * x: device bf16 [T, d]; out: device fp32 [offsets[n_groups], d] (rows in perm
+ * order); h_ws: device, offsets[n_groups] * d_ff * 4 bytes.  form: 0 auto, 1 the
+ * bandwidth-bound row-streaming form (few tokens per expert), 2 the MFMA tile form
+ * (many tokens per expert). */
+int ft_grouped_ffn(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t k,
+                   const void* slots, const int32_t* group_slot, const int32_t* offsets,
+                   const int32_t* perm, int32_t n_groups, int32_t g_begin, int32_t g_end,
+                   int32_t max_rows_per_group, void* h_ws, float* out, int32_t form,
+                   void* stream);
+
+/* Gate-weighted combine and exact merge ([FT] §3.2: the GPU and CPU partial sums
+ * merge into the exact MoE output):  y[t] = sum_{j: inv[t*k+j] >= 0, in j order}
+ * gates[t*k+j] * out[inv[t*k+j]]  +  cpu_partial[t]  (cpu_partial may be NULL).
+ * All device; y fp32 [T, d]. */
+int ft_combine(const float* out, const int32_t* inv, const float* gates,
+               const float* cpu_partial, int32_t T, int32_t k, int32_t d, float* y,
+               void* stream);
+
+/* ---- expert cache -------------------------------------------------------------- */
+
+/* Decisions of one decode call for routed ids idx_host (host int32 [T, k]):
+ * dedup, classify, split (ft_qstar_split with avail = n_slots - |H|), victims
+ * (non-hit slots by (recency, slot), empty first), LRU update (H and F touched in
+ * U order) and the slot rewrite ([FT] §3.2, §4.1).  Updates the residency state
+ * and counters; copies nothing.  T*k <= FT_PLAN_CAP. */
+int ft_expert_cache_lookup(ft_ctx_t ctx, int32_t layer, const int32_t* idx_host, int32_t T,
+                           ft_plan* plan);
+
+/* Copies the q records of plan->F into their slots with hipMemcpyAsync on
+ * `copy` (pinned host -> device; [FT] §3.2: fills proceed at the full PCIe rate).
+ * Waits on wait_event first if not NULL; records done_event after if not NULL. */
+int ft_expert_cache_fill(ft_ctx_t ctx, const ft_plan* plan, void* copy, void* wait_event,
+                         void* done_event);
+
+/* Rebuilds the cache over new_dev_slots (n_slots records; may equal the old
+ * buffer) at a safe point ([FT] §3.3): all slots empty, counters reset, recency
+ * clock kept.  FT_EBUSY if work the library issued is still running or a prefill
+ * is open.  Returns FT_WOVERLAP_OFF when prefill overlap had to be disabled
+ * (n_slots < 2E). */
+int ft_expert_cache_resize(ft_ctx_t ctx, void* new_dev_slots, int32_t new_n_slots);
+
+/* Residency of one (layer, expert): slot or -1. */
+int32_t ft_expert_cache_where(ft_ctx_t ctx, int32_t layer, int32_t expert);
+
+/* ---- layer forward ----------------------------------------------------------------- */
+
+/* One decode call of one MoE layer ([FT] §3.2, "In execution order"):
+ * router on `compute`; ids to the host; decisions; the CPU branch (C) starts on
+ * the worker pool; fills of F on `copy`; grouped FFN of H, then of F once its
+ * fills landed; merge of the CPU partial; combine into y.  Returns when y is
+ * enqueued on `compute` (the CPU branch has finished).
+ * x: device bf16 [T, d]; w_router: device bf16 [E, d]; allowed: device uint8
+ * [T, E] or NULL; y: device fp32 [T, d].  plan, stats: host, may be NULL.
+ * T <= min(T_max, FT_PLAN_CAP / k, 64). */
+int ft_moe_decode_layer(ft_ctx_t ctx, int32_t layer, const void* x, int32_t T,
+                        const void* w_router, const uint8_t* allowed, float* y, void* compute,
+                        void* copy, ft_plan* plan, ft_step_stats* stats);
+
+/* Full-layer double-buffered prefill ([FT] §3.1; §5.3 "Pipelined prefill").
+ * begin: reserve two buffers of E slots (victim order) and start loading layer 0
+ * on `copy`.  layer: (layers in order 0..L-1) start loading layer l+1 into the
+ * other buffer once layer l-1's compute is done, then compute layer l (router,
+ * grouping, grouped FFN, combine) from its buffer once its load landed.
+ * end: the last two layers processed (L-2 and L-1 after a full pass) stay
+ * resident for decode; waits for any layer prefetch still in flight.
+ * FT_EUNSUPPORTED when overlap is disabled (on-demand prefill is not built).
+ * In a decisions-only context begin/end change residency only (no copies). */
+int ft_moe_prefill_begin(ft_ctx_t ctx, void* copy);
+int ft_moe_prefill_layer(ft_ctx_t ctx, int32_t layer, const void* x, int32_t T,
+                         const void* w_router, float* y, void* compute, void* copy);
+int ft_moe_prefill_end(ft_ctx_t ctx);
+
+/* Device slot of expert e in the buffer serving `layer` during prefill, or -1. */
+int32_t ft_prefill_slot(ft_ctx_t ctx, int32_t layer, int32_t expert);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FT_H */

@@ -1,0 +1,58 @@
+// Residency state of the elastic GPU expert cache (host side).
+//
+// [FT] = "FreeToken: Efficient Edge-Native MoE Serving with Bandwidth-Adaptive
+// Execution" (arXiv 2608.16157).
+//   §3    one cache shared by all MoE layers, keyed on logical (layer, expert).
+//   §3.2  hits refresh recency, fills admit, eviction drops the least recently
+//         demanded entry; the m misses split into F (filled) and C (host).
+//   §4.1  per layer: dedup, classify, derive q, select the K least recently used
+//         victims in one pass and consume the first q, rewrite ids to slots or -1.
+//   §3.1  two full-layer prefill buffers are taken from the same slot pool.
+//   §3.3  rebuild for a new budget at a safe point.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/ft.h"
+
+namespace ft {
+
+class ExpertCache {
+ public:
+  ExpertCache(int L, int E, int n_slots);
+
+  int n_slots() const { return n_; }
+  int E() const { return E_; }
+
+  // One decode call's decisions for routed ids idx[T*k]; updates state.
+  int lookup(int layer, const int32_t* idx, int T, int k, uint32_t fq, int min_fill,
+             int max_fetch, ft_plan* plan);
+
+  // Prefill buffers: reserves 2E slots (victim order), returns FT_OK or FT_ECAP.
+  int prefill_begin();
+  int32_t prefill_slot(int layer, int e) const;
+  const std::vector<int32_t>& prefill_buffer(int b) const { return buf_[b]; }
+  bool prefill_open() const { return prefill_open_; }
+  void prefill_end(int L);
+
+  void resize(int n_slots);  // all slots empty, counters reset, clock kept
+  int32_t where(int layer, int e) const;
+
+  ft_stats stats{};
+
+ private:
+  // first `count` slots in (stamp, slot) order among those not excluded;
+  // one pass with a bounded max-heap (ties by slot index).
+  void select_victims(int count, const std::vector<uint8_t>& excluded, std::vector<int32_t>* out) const;
+
+  int L_, E_, n_;
+  int64_t clock_ = 0;
+  std::vector<int32_t> slot_key_;    // -1 empty, -2 reserved for prefill, else l*E+e
+  std::vector<int64_t> slot_stamp_;  // -1 for empty
+  std::vector<int32_t> where_;       // [L*E] slot or -1
+  std::vector<int32_t> buf_[2];
+  bool prefill_open_ = false;
+};
+
+}  // namespace ft

@@ -1,0 +1,286 @@
+// Host expert executor: the CPU branch of a decode step.
+//
+// [FT] = "FreeToken: Efficient Edge-Native MoE Serving with Bandwidth-Adaptive
+// Execution" (arXiv 2608.16157).  [FT] §3.2: experts of the CPU set C execute in
+// place from the host-resident pool and return gate-weighted per-token partial
+// outputs, concurrently with the GPU path.  [FT] §4.1 "Graph-resident CPU
+// execution": a persistent pool of workers pinned to cores, with SIMD kernels
+// that stay bound by host memory bandwidth.
+//
+// Work of one call: phase 1 computes h = silu(W_gate x) * (W_up x) for every
+// (expert, use) with rows of W_gate/W_up dealt to workers in blocks; phase 2
+// computes partial[t][c] = sum over the uses (expert, t, gate) of
+// gate * (W_down[c] . h) with output rows dealt in blocks, so every output row
+// is owned by one worker.  Each weight row is read once and applied to all the
+// uses of its expert.
+#include <immintrin.h>
+#include <pthread.h>
+#include <sched.h>
+
+#include <atomic>
+#include <cmath>
+#include <condition_variable>
+#include <cstring>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "internal.h"
+
+namespace ft {
+namespace {
+
+constexpr int MAXV = 8;  // activation vectors applied per weight row pass
+
+using RowDotsFn = void (*)(const uint16_t* w, int n, const float* const* xs, int nx, float* out);
+
+void row_dots_scalar(const uint16_t* w, int n, const float* const* xs, int nx, float* out) {
+  float acc[MAXV] = {0};
+  for (int i = 0; i < n; ++i) {
+    uint32_t u = (uint32_t)w[i] << 16;
+    float wf;
+    std::memcpy(&wf, &u, 4);
+    for (int v = 0; v < nx; ++v) acc[v] += wf * xs[v][i];
+  }
+  for (int v = 0; v < nx; ++v) out[v] = acc[v];
+}
+
+__attribute__((target("avx2,fma"))) void row_dots_avx2(const uint16_t* w, int n,
+                                                         const float* const* xs, int nx,
+                                                         float* out) {
+  __m256 acc[MAXV];
+  for (int v = 0; v < MAXV; ++v) acc[v] = _mm256_setzero_ps();
+  int i = 0;
+  for (; i + 8 <= n; i += 8) {
+    const __m128i a = _mm_loadu_si128(reinterpret_cast<const __m128i*>(w + i));
+    const __m256 wf = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(a), 16));
+    for (int v = 0; v < nx; ++v) acc[v] = _mm256_fmadd_ps(wf, _mm256_loadu_ps(xs[v] + i), acc[v]);
+  }
+  for (int v = 0; v < nx; ++v) {
+    __m128 s = _mm_add_ps(_mm256_castps256_ps128(acc[v]), _mm256_extractf128_ps(acc[v], 1));
+    s = _mm_hadd_ps(s, s);
+    s = _mm_hadd_ps(s, s);
+    float r = _mm_cvtss_f32(s);
+    for (int j = i; j < n; ++j) {
+      uint32_t u = (uint32_t)w[j] << 16;
+      float wf;
+      std::memcpy(&wf, &u, 4);
+      r += wf * xs[v][j];
+    }
+    out[v] = r;
+  }
+}
+
+__attribute__((target("avx512f,avx512bw"))) void row_dots_avx512(const uint16_t* w, int n,
+                                                                   const float* const* xs, int nx,
+                                                                   float* out) {
+  __m512 acc[MAXV];
+  for (int v = 0; v < MAXV; ++v) acc[v] = _mm512_setzero_ps();
+  int i = 0;
+  for (; i + 16 <= n; i += 16) {
+    const __m256i a = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(w + i));
+    const __m512 wf = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(a), 16));
+    for (int v = 0; v < nx; ++v) acc[v] = _mm512_fmadd_ps(wf, _mm512_loadu_ps(xs[v] + i), acc[v]);
+  }
+  for (int v = 0; v < nx; ++v) {
+    float r = _mm512_reduce_add_ps(acc[v]);
+    for (int j = i; j < n; ++j) {
+      uint32_t u = (uint32_t)w[j] << 16;
+      float wf;
+      std::memcpy(&wf, &u, 4);
+      r += wf * xs[v][j];
+    }
+    out[v] = r;
+  }
+}
+
+RowDotsFn pick_row_dots(const char** name) {
+  __builtin_cpu_init();
+  if (__builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw")) {
+    *name = "avx512";
+    return row_dots_avx512;
+  }
+  if (__builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma")) {
+    *name = "avx2";
+    return row_dots_avx2;
+  }
+  *name = "scalar";
+  return row_dots_scalar;
+}
+
+const char* g_simd_name = nullptr;
+RowDotsFn g_row_dots = nullptr;
+std::once_flag g_simd_once;
+
+inline float silu_f(float z) { return z / (1.0f + std::exp(-z)); }
+
+}  // namespace
+
+class CpuPool {
+ public:
+  explicit CpuPool(int threads) {
+    std::call_once(g_simd_once, [] { g_row_dots = pick_row_dots(&g_simd_name); });
+    cpu_set_t mask;
+    CPU_ZERO(&mask);
+    std::vector<int> cpus;
+    if (sched_getaffinity(0, sizeof(mask), &mask) == 0)
+      for (int c = 0; c < CPU_SETSIZE; ++c)
+        if (CPU_ISSET(c, &mask)) cpus.push_back(c);
+    if (threads <= 0) threads = cpus.empty() ? (int)std::thread::hardware_concurrency() : (int)cpus.size();
+    if (threads <= 0) threads = 1;
+    nthreads_ = threads;
+    for (int i = 0; i < threads; ++i) {
+      workers_.emplace_back([this, i] { run(i); });
+      if (!cpus.empty()) {
+        cpu_set_t one;
+        CPU_ZERO(&one);
+        CPU_SET(cpus[i % cpus.size()], &one);
+        pthread_setaffinity_np(workers_.back().native_handle(), sizeof(one), &one);
+      }
+    }
+  }
+
+  ~CpuPool() {
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      stop_ = true;
+      gen_.fetch_add(1, std::memory_order_release);
+    }
+    cv_.notify_all();
+    for (auto& t : workers_) t.join();
+  }
+
+  int threads() const { return nthreads_; }
+
+  void submit(const uint16_t* x, int T, int d, int d_ff, const CpuExpert* ex, int n_exp,
+              float* partial) {
+    T_ = T;
+    d_ = d;
+    d_ff_ = d_ff;
+    ex_ = ex;
+    n_exp_ = n_exp;
+    partial_ = partial;
+    xf_.resize((size_t)T * d);
+    for (size_t i = 0; i < (size_t)T * d; ++i) {
+      uint32_t u = (uint32_t)x[i] << 16;
+      std::memcpy(&xf_[i], &u, 4);
+    }
+    std::memset(partial, 0, sizeof(float) * (size_t)T * d);
+    use_base_.assign(n_exp + 1, 0);
+    for (int e = 0; e < n_exp; ++e) use_base_[e + 1] = use_base_[e] + ex[e].n_use;
+    h_.resize((size_t)use_base_[n_exp] * d_ff);
+    blocks1_ = (d_ff + RB1 - 1) / RB1;
+    items1_ = n_exp * blocks1_;
+    items2_ = (d + RB2 - 1) / RB2;
+    next1_.store(0, std::memory_order_relaxed);
+    next2_.store(0, std::memory_order_relaxed);
+    arrived_.store(0, std::memory_order_relaxed);
+    finished_.store(0, std::memory_order_relaxed);
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      gen_.fetch_add(1, std::memory_order_release);
+    }
+    cv_.notify_all();
+  }
+
+  void wait() {
+    while (finished_.load(std::memory_order_acquire) < nthreads_) _mm_pause();
+  }
+
+ private:
+  static constexpr int RB1 = 16;  // W_gate/W_up rows per phase-1 item
+  static constexpr int RB2 = 32;  // output rows per phase-2 item
+
+  void phase1(int item) {
+    const int e = item / blocks1_;
+    const int r0 = (item % blocks1_) * RB1;
+    const int r1 = std::min(d_ff_, r0 + RB1);
+    const CpuExpert& X = ex_[e];
+    const uint16_t* wg = X.rec;
+    const uint16_t* wu = X.rec + (size_t)d_ff_ * d_;
+    const float* xs[MAXV];
+    float zg[MAXV], zu[MAXV];
+    for (int u0 = 0; u0 < X.n_use; u0 += MAXV) {
+      const int nx = std::min(MAXV, X.n_use - u0);
+      for (int v = 0; v < nx; ++v) xs[v] = xf_.data() + (size_t)X.use[u0 + v].t * d_;
+      for (int r = r0; r < r1; ++r) {
+        g_row_dots(wg + (size_t)r * d_, d_, xs, nx, zg);
+        g_row_dots(wu + (size_t)r * d_, d_, xs, nx, zu);
+        for (int v = 0; v < nx; ++v)
+          h_[(size_t)(use_base_[e] + u0 + v) * d_ff_ + r] = silu_f(zg[v]) * zu[v];
+      }
+    }
+  }
+
+  void phase2(int item) {
+    const int c0 = item * RB2;
+    const int c1 = std::min(d_, c0 + RB2);
+    const float* hs[MAXV];
+    float o[MAXV];
+    for (int e = 0; e < n_exp_; ++e) {
+      const CpuExpert& X = ex_[e];
+      const uint16_t* wd = X.rec + (size_t)2 * d_ff_ * d_;
+      for (int u0 = 0; u0 < X.n_use; u0 += MAXV) {
+        const int nx = std::min(MAXV, X.n_use - u0);
+        for (int v = 0; v < nx; ++v) hs[v] = h_.data() + (size_t)(use_base_[e] + u0 + v) * d_ff_;
+        for (int c = c0; c < c1; ++c) {
+          g_row_dots(wd + (size_t)c * d_ff_, d_ff_, hs, nx, o);
+          for (int v = 0; v < nx; ++v) partial_[(size_t)X.use[u0 + v].t * d_ + c] += X.use[u0 + v].gate * o[v];
+        }
+      }
+    }
+  }
+
+  void run(int /*id*/) {
+    uint64_t seen = 0;
+    for (;;) {
+      // spin briefly for the next call, then sleep
+      int spins = 0;
+      while (gen_.load(std::memory_order_acquire) == seen && spins < 20000) {
+        _mm_pause();
+        ++spins;
+      }
+      if (gen_.load(std::memory_order_acquire) == seen) {
+        std::unique_lock<std::mutex> lk(mu_);
+        cv_.wait(lk, [&] { return gen_.load(std::memory_order_acquire) != seen; });
+      }
+      seen = gen_.load(std::memory_order_acquire);
+      if (stop_) return;
+      for (int it; (it = next1_.fetch_add(1, std::memory_order_relaxed)) < items1_;) phase1(it);
+      arrived_.fetch_add(1, std::memory_order_acq_rel);
+      while (arrived_.load(std::memory_order_acquire) < nthreads_) _mm_pause();
+      for (int it; (it = next2_.fetch_add(1, std::memory_order_relaxed)) < items2_;) phase2(it);
+      finished_.fetch_add(1, std::memory_order_acq_rel);
+    }
+  }
+
+  int nthreads_ = 1;
+  std::vector<std::thread> workers_;
+  std::mutex mu_;
+  std::condition_variable cv_;
+  std::atomic<uint64_t> gen_{0};
+  bool stop_ = false;
+
+  int T_ = 0, d_ = 0, d_ff_ = 0, n_exp_ = 0;
+  const CpuExpert* ex_ = nullptr;
+  float* partial_ = nullptr;
+  std::vector<float> xf_, h_;
+  std::vector<int> use_base_;
+  int blocks1_ = 0, items1_ = 0, items2_ = 0;
+  std::atomic<int> next1_{0}, next2_{0}, arrived_{0}, finished_{0};
+};
+
+CpuPool* cpu_pool_create(int threads) { return new CpuPool(threads); }
+void cpu_pool_destroy(CpuPool* p) { delete p; }
+int cpu_pool_threads(const CpuPool* p) { return p->threads(); }
+void cpu_pool_submit(CpuPool* p, const uint16_t* x, int T, int d, int d_ff, const CpuExpert* ex,
+                     int n_exp, float* partial) {
+  p->submit(x, T, d, d_ff, ex, n_exp, partial);
+}
+void cpu_pool_wait(CpuPool* p) { p->wait(); }
+const char* cpu_simd_name() {
+  std::call_once(g_simd_once, [] { g_row_dots = pick_row_dots(&g_simd_name); });
+  return g_simd_name;
+}
+
+}  // namespace ft

@@ -1,0 +1,64 @@
+// Internal declarations shared by the libft sources (not part of the C ABI).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/ft.h"
+
+namespace ft {
+
+// Thread-local error message for ft_last_error().
+void set_error(const std::string& msg);
+int fail(int status, const std::string& msg);
+
+// ---- kernel launchers (kernels.hip); all asynchronous on `stream` ----------
+// Each returns FT_OK or FT_EHIP (launch error) / FT_EINVAL (bad sizes).
+
+int launch_router(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, int T, int d,
+                  int E, int k, int32_t* idx, float* gates, float* logits_ws, void* stream);
+
+size_t permute_ws_bytes(int P, int n_groups);
+int launch_permute(const int32_t* key, int P, int n_groups, int32_t* offsets, int32_t* perm,
+                   int32_t* inv, void* ws, size_t ws_bytes, void* stream);
+
+// Row-streaming (GEMV-like) grouped FFN: h fp32 [rows, d_ff], out fp32 [rows, d].
+int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
+                    const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
+                    int g_begin, int g_end, int max_rows, float* h, float* out, void* stream);
+
+// MFMA tile grouped FFN: h bf16 [rows, d_ff] (in the fp32-sized workspace), out fp32 [rows, d].
+int launch_ffn_mfma(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
+                    const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
+                    int g_begin, int g_end, int max_rows, uint16_t* h, float* out, void* stream);
+
+int launch_combine(const float* out, const int32_t* inv, const float* gates,
+                   const float* cpu_partial, int T, int k, int d, float* y, void* stream);
+
+// ---- host expert kernel (cpu_exec.cpp) ----------------------------------------
+// One batch of CPU-branch work: experts `n_exp`, each with a record pointer and a
+// list of (token, gate) uses.  Computes partial[t] += sum gate * FFN_e(x[t]).
+struct CpuUse {
+  int32_t t;
+  float gate;
+};
+struct CpuExpert {
+  const uint16_t* rec;
+  int32_t n_use;
+  CpuUse use[64];
+};
+
+class CpuPool;
+CpuPool* cpu_pool_create(int threads);
+void cpu_pool_destroy(CpuPool*);
+int cpu_pool_threads(const CpuPool*);
+// Starts the work asynchronously; x is bf16 [T, d]; partial fp32 [T, d] is
+// overwritten (zeroed first).  Returns immediately.
+void cpu_pool_submit(CpuPool*, const uint16_t* x, int T, int d, int d_ff, const CpuExpert* ex,
+                     int n_exp, float* partial);
+// Blocks until the submitted work is done.
+void cpu_pool_wait(CpuPool*);
+const char* cpu_simd_name();
+
+}  // namespace ft

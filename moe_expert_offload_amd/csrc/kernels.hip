@@ -1,0 +1,771 @@
+// HIP kernels of the routed MoE layer for gfx950 (CDNA4, wavefront 64).
+//
+// Citations: [FT] = "FreeToken: Efficient Edge-Native MoE Serving with
+// Bandwidth-Adaptive Execution" (arXiv 2608.16157).
+//
+//   router      fp32 logits in a fixed summation order + wavefront top-k    [FT] §3.2
+//   permute     stable grouping of (token, rank) pairs by expert            (grouped evaluation, [FT] §3.2)
+//   ffn rows    grouped SwiGLU FFN, row-streaming form for few tokens/expert (decode, [FT] §3.2)
+//   ffn mfma    grouped SwiGLU FFN on bf16 MFMA tiles for many tokens/expert (prefill, [FT] §3.1)
+//   combine     gate-weighted sum in rank order + the host partial          ([FT] §3.2 exact merge)
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+
+#include "internal.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+// sum of the 8 products of two packed bf16x8 vectors, added into acc (any order)
+__device__ __forceinline__ float dot8(uint4 a, uint4 b, float acc) {
+  acc = fmaf(bf_lo(a.x), bf_lo(b.x), acc);
+  acc = fmaf(bf_hi(a.x), bf_hi(b.x), acc);
+  acc = fmaf(bf_lo(a.y), bf_lo(b.y), acc);
+  acc = fmaf(bf_hi(a.y), bf_hi(b.y), acc);
+  acc = fmaf(bf_lo(a.z), bf_lo(b.z), acc);
+  acc = fmaf(bf_hi(a.z), bf_hi(b.z), acc);
+  acc = fmaf(bf_lo(a.w), bf_lo(b.w), acc);
+  acc = fmaf(bf_hi(a.w), bf_hi(b.w), acc);
+  return acc;
+}
+
+__device__ __forceinline__ float dot8_f(uint4 a, float4 h0, float4 h1, float acc) {
+  acc = fmaf(bf_lo(a.x), h0.x, acc);
+  acc = fmaf(bf_hi(a.x), h0.y, acc);
+  acc = fmaf(bf_lo(a.y), h0.z, acc);
+  acc = fmaf(bf_hi(a.y), h0.w, acc);
+  acc = fmaf(bf_lo(a.z), h1.x, acc);
+  acc = fmaf(bf_hi(a.z), h1.y, acc);
+  acc = fmaf(bf_lo(a.w), h1.z, acc);
+  acc = fmaf(bf_hi(a.w), h1.w, acc);
+  return acc;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Blocks are dealt to the 8 XCDs round-robin; remap so that consecutive logical
+// blocks share an XCD (and its L2).
+__device__ __forceinline__ int xcd_logical_block(int b, int nb) {
+  const int q = nb >> 3, r = nb & 7, x = b & 7;
+  return x * q + (x < r ? x : r) + (b >> 3);
+}
+
+// ============================================================================
+// Router
+// ============================================================================
+
+// Element i of a dot product belongs to lane (i mod 512) / 8; a lane adds its
+// products in increasing i (chunk j = 0,1,..., then r = 0..7 inside the chunk);
+// positions past d contribute +0.0 products.  The 64 lane sums are combined by
+// a_l += a_(l xor o), o = 32..1.  Every fp32 step is an IEEE add of an exact
+// bf16 x bf16 product, so the bits do not depend on FMA contraction.
+template <int TT, int TE>
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ w,
+                                                            int T, int d, int E,
+                                                            float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * TT;
+  const int e0 = (blockIdx.y * 4 + wave) * TE;
+  if (e0 >= E) return;
+  float acc[TT][TE];
+#pragma unroll
+  for (int a = 0; a < TT; ++a)
+#pragma unroll
+    for (int b = 0; b < TE; ++b) acc[a][b] = 0.0f;
+  const int J = (d + 511) >> 9;
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < J; ++j) {
+    const int i0 = j * 512 + lane * 8;
+    const bool in = i0 < d;
+    uint4 xv[TT], wv[TE];
+#pragma unroll
+    for (int a = 0; a < TT; ++a) xv[a] = (in && t0 + a < T) ? ld16(x + (size_t)(t0 + a) * d + i0) : zero;
+#pragma unroll
+    for (int b = 0; b < TE; ++b) wv[b] = (in && e0 + b < E) ? ld16(w + (size_t)(e0 + b) * d + i0) : zero;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+#pragma unroll
+      for (int a = 0; a < TT; ++a) {
+        const uint32_t xw = (r >> 1) == 0 ? xv[a].x : (r >> 1) == 1 ? xv[a].y : (r >> 1) == 2 ? xv[a].z : xv[a].w;
+        const float xf = (r & 1) ? bf_hi(xw) : bf_lo(xw);
+#pragma unroll
+        for (int b = 0; b < TE; ++b) {
+          const uint32_t ww = (r >> 1) == 0 ? wv[b].x : (r >> 1) == 1 ? wv[b].y : (r >> 1) == 2 ? wv[b].z : wv[b].w;
+          const float wf = (r & 1) ? bf_hi(ww) : bf_lo(ww);
+          acc[a][b] = acc[a][b] + xf * wf;  // product exact in fp32
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < TT; ++a)
+#pragma unroll
+    for (int b = 0; b < TE; ++b) {
+      float v = acc[a][b];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v = v + __shfl_xor(v, o, WAVE);
+      acc[a][b] = v;
+    }
+  if (lane == 0) {
+#pragma unroll
+    for (int a = 0; a < TT; ++a)
+#pragma unroll
+      for (int b = 0; b < TE; ++b)
+        if (t0 + a < T && e0 + b < E) logits[(size_t)(t0 + a) * E + e0 + b] = acc[a][b];
+  }
+}
+
+__device__ __forceinline__ bool ranks_before(float va, int ea, float vb, int eb) {
+  return va > vb || (va == vb && ea < eb);
+}
+
+// One wavefront per token: k rounds of a (logit desc, index asc) arg-max over
+// the wave, each winner removed; then softmax over the k winners.
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
+                                                          const uint8_t* __restrict__ allowed,
+                                                          int T, int E, int k,
+                                                          int32_t* __restrict__ idx,
+                                                          float* __restrict__ gates) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float v[16];
+  bool ok[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int e = lane + 64 * s;
+    const bool in = e < E && (allowed == nullptr || allowed[(size_t)t * E + e] != 0);
+    ok[s] = in;
+    v[s] = in ? logits[(size_t)t * E + e] : 0.0f;
+  }
+  float sv[8];
+  int se[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    sv[r] = 0.0f;
+    se[r] = -1;
+    if (r < k) {
+      float bv = -INFINITY;
+      int be = INT_MAX;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int e = lane + 64 * s;
+        if (ok[s] && (be == INT_MAX || ranks_before(v[s], e, bv, be))) {
+          bv = v[s];
+          be = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, WAVE);
+        const int oe = __shfl_xor(be, o, WAVE);
+        if (oe != INT_MAX && (be == INT_MAX || ranks_before(ov, oe, bv, be))) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      if (be != INT_MAX) {
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+          if (lane + 64 * s == be) ok[s] = false;
+        sv[r] = bv;
+        se[r] = be;
+      }
+    }
+  }
+  if (lane == 0) {
+    float z[8], sum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      z[r] = (r < k && se[r] >= 0) ? expf(sv[r] - sv[0]) : 0.0f;
+      sum += z[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (r < k) {
+        idx[(size_t)t * k + r] = se[r];
+        gates[(size_t)t * k + r] = se[r] >= 0 ? z[r] / sum : 0.0f;
+      }
+  }
+}
+
+// ============================================================================
+// Permutation: stable counting sort of pair ids by group key
+// ============================================================================
+constexpr int PB = 256;
+
+__global__ __launch_bounds__(PB) void perm_count_kernel(const int32_t* __restrict__ key, int P, int G,
+                                                        int32_t* __restrict__ counts) {
+  extern __shared__ int32_t hist[];
+  for (int i = threadIdx.x; i < G; i += PB) hist[i] = 0;
+  __syncthreads();
+  const int p = blockIdx.x * PB + threadIdx.x;
+  if (p < P) {
+    const int g = key[p];
+    if (g >= 0 && g < G) atomicAdd(&hist[g], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G; i += PB) counts[(size_t)blockIdx.x * G + i] = hist[i];
+}
+
+// One block: per-group running bases over blocks, then the exclusive scan of the
+// group totals; counts[b][g] becomes the absolute first position of block b's
+// pairs of group g.
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int nblk, int G, int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets) {
+  __shared__ int32_t total[1025];
+  for (int g = threadIdx.x; g < G; g += 1024) {
+    int run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const int c = counts[(size_t)b * G + g];
+      counts[(size_t)b * G + g] = run;
+      run += c;
+    }
+    total[g] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int g = 0; g < G; ++g) {
+      const int c = total[g];
+      total[g] = run;
+      run += c;
+    }
+    total[G] = run;
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g <= G; g += 1024) offsets[g] = total[g];
+  for (int g = threadIdx.x; g < G; g += 1024) {
+    const int base = total[g];
+    for (int b = 0; b < nblk; ++b) counts[(size_t)b * G + g] += base;
+  }
+}
+
+__global__ __launch_bounds__(PB) void perm_scatter_kernel(const int32_t* __restrict__ key, int P, int G,
+                                                          const int32_t* __restrict__ base,
+                                                          int32_t* __restrict__ perm,
+                                                          int32_t* __restrict__ inv) {
+  __shared__ int32_t ks[PB];
+  const int p = blockIdx.x * PB + threadIdx.x;
+  int g = p < P ? key[p] : -1;
+  if (g >= G) g = -1;
+  ks[threadIdx.x] = g;
+  __syncthreads();
+  if (p >= P) return;
+  if (g < 0) {
+    inv[p] = -1;
+    return;
+  }
+  int rank = 0;
+  for (int q = 0; q < (int)threadIdx.x; ++q) rank += (ks[q] == g);
+  const int pos = base[(size_t)blockIdx.x * G + g] + rank;
+  perm[pos] = p;
+  inv[p] = pos;
+}
+
+// ============================================================================
+// Grouped SwiGLU FFN, row-streaming form (few tokens per expert)
+// ============================================================================
+// One wavefront per weight row.  Lane l reads the 16-byte pieces l, l+64, ... of
+// the row, so a wavefront streams 1 KB per load; the row is held in registers
+// while every token of the group is applied to it.
+
+template <int NT>
+__global__ __launch_bounds__(256) void ffn_gateup_rows_kernel(
+    const uint16_t* __restrict__ x, int d, int d_ff, int k, const uint16_t* __restrict__ slots,
+    size_t rec_elems, const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ perm, int g_begin, int blocks_per_group, float* __restrict__ h) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = g_begin + blockIdx.x / blocks_per_group;
+  const int row = (blockIdx.x % blocks_per_group) * 4 + wave;
+  if (row >= d_ff) return;
+  const int r0 = offsets[g];
+  const int n = offsets[g + 1] - r0;
+  if (n <= 0) return;
+  const uint16_t* rec = slots + (size_t)group_slot[g] * rec_elems;
+  const uint16_t* wg = rec + (size_t)row * d;
+  const uint16_t* wu = rec + (size_t)d_ff * d + (size_t)row * d;
+  const int J = (d + 511) >> 9;
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  for (int tb = 0; tb < n; tb += NT) {
+    float ag[NT], au[NT];
+    const uint16_t* xr[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      ag[i] = 0.0f;
+      au[i] = 0.0f;
+      xr[i] = (tb + i < n) ? x + (size_t)(perm[r0 + tb + i] / k) * d : nullptr;
+    }
+    for (int j0 = 0; j0 < J; j0 += 8) {
+      uint4 gw[8], uw[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int i0 = (j0 + jj) * 512 + lane * 8;
+        const bool in = (j0 + jj < J) && i0 < d;
+        gw[jj] = in ? ld16(wg + i0) : zero;
+        uw[jj] = in ? ld16(wu + i0) : zero;
+      }
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        if (xr[i] == nullptr) continue;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int i0 = (j0 + jj) * 512 + lane * 8;
+          if ((j0 + jj < J) && i0 < d) {
+            const uint4 xv = ld16(xr[i] + i0);
+            ag[i] = dot8(gw[jj], xv, ag[i]);
+            au[i] = dot8(uw[jj], xv, au[i]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      if (tb + i >= n) continue;
+      const float zg = wave_sum(ag[i]);
+      const float zu = wave_sum(au[i]);
+      if (lane == 0) h[(size_t)(r0 + tb + i) * d_ff + row] = silu(zg) * zu;
+    }
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void ffn_down_rows_kernel(
+    int d, int d_ff, const uint16_t* __restrict__ slots, size_t rec_elems,
+    const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, int g_begin,
+    int blocks_per_group, const float* __restrict__ h, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = g_begin + blockIdx.x / blocks_per_group;
+  const int row = (blockIdx.x % blocks_per_group) * 4 + wave;
+  if (row >= d) return;
+  const int r0 = offsets[g];
+  const int n = offsets[g + 1] - r0;
+  if (n <= 0) return;
+  const uint16_t* wd = slots + (size_t)group_slot[g] * rec_elems + (size_t)2 * d_ff * d + (size_t)row * d_ff;
+  const int J = (d_ff + 511) >> 9;
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  for (int tb = 0; tb < n; tb += NT) {
+    float acc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[i] = 0.0f;
+    for (int j0 = 0; j0 < J; j0 += 8) {
+      uint4 wv[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int i0 = (j0 + jj) * 512 + lane * 8;
+        wv[jj] = ((j0 + jj < J) && i0 < d_ff) ? ld16(wd + i0) : zero;
+      }
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        if (tb + i >= n) continue;
+        const float* hr = h + (size_t)(r0 + tb + i) * d_ff;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int i0 = (j0 + jj) * 512 + lane * 8;
+          if ((j0 + jj < J) && i0 < d_ff) {
+            const float4 h0 = *reinterpret_cast<const float4*>(hr + i0);
+            const float4 h1 = *reinterpret_cast<const float4*>(hr + i0 + 4);
+            acc[i] = dot8_f(wv[jj], h0, h1, acc[i]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      if (tb + i >= n) continue;
+      const float s = wave_sum(acc[i]);
+      if (lane == 0) out[(size_t)(r0 + tb + i) * d + row] = s;
+    }
+  }
+}
+
+// ============================================================================
+// Grouped SwiGLU FFN, MFMA tile form (many tokens per expert)
+// ============================================================================
+// v_mfma_f32_32x32x16_bf16 lane layout (checked on gfx950): lane l supplies
+// A[l%32][(l/32)*8 .. +7] and B^T[l%32][(l/32)*8 .. +7]; accumulator element v
+// of lane l is C[(v/4)*8 + (l/32)*4 + v%4][l%32].
+//
+// Block: 512 threads = 8 waves (4 along M x 2 along N); tile of up to 256 rows
+// of one expert (all its tokens in one pass for the usual ~200) and one column
+// tile of the weight; K staged through LDS in steps of 64 with the next step
+// prefetched into registers.  A weight tile is read from HBM once per expert.
+constexpr int TBM = 256;
+constexpr int TBK = 64;
+constexpr int LDK = TBK + 8;  // padded LDS row, in bf16 elements
+
+__device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* p) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// h[i][n0 + c] = silu(sum_k x[t_i][k] Wg[n0+c][k]) * (sum_k x[t_i][k] Wu[n0+c][k]),
+// column tile of 64 (each N-wave owns 32 gate and the same 32 up columns).
+__global__ __launch_bounds__(512) void ffn_gateup_mfma_kernel(
+    const uint16_t* __restrict__ x, int d, int d_ff, int k, const uint16_t* __restrict__ slots,
+    size_t rec_elems, const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ perm, int g_begin, int n_tiles, int n_blocks,
+    uint16_t* __restrict__ h) {
+  __shared__ __attribute__((aligned(16))) uint16_t sX[TBM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[128 * LDK];
+  const int lb = xcd_logical_block(blockIdx.x, n_blocks);
+  const int g = g_begin + lb / n_tiles;
+  const int n0 = (lb % n_tiles) * 64;
+  const int r0 = offsets[g];
+  const int n = offsets[g + 1] - r0;
+  if (n <= 0) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const uint16_t* rec = slots + (size_t)group_slot[g] * rec_elems;
+  // this thread's two weight chunks per stage: rows 0..63 gate, 64..127 up
+  const uint16_t* wrow[2];
+  int wlds[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch = tid + c * 512;
+    const int r = ch >> 3, c8 = ch & 7;
+    wrow[c] = (r < 64 ? rec + (size_t)(n0 + r) * d : rec + (size_t)d_ff * d + (size_t)(n0 + r - 64) * d) + c8 * 8;
+    wlds[c] = r * LDK + c8 * 8;
+  }
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  for (int m0 = 0; m0 < n; m0 += TBM) {
+    const uint16_t* xrow[4];
+    int xlds[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int ch = tid + c * 512;
+      const int r = ch >> 3, c8 = ch & 7;
+      xrow[c] = (m0 + r < n) ? x + (size_t)(perm[r0 + m0 + r] / k) * d + c8 * 8 : nullptr;
+      xlds[c] = r * LDK + c8 * 8;
+    }
+    const bool wave_active = (m0 + wm * 64) < n;
+    f32x16_t acc[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][v] = 0.0f;
+    uint4 px[4], pw[2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) px[c] = xrow[c] ? ld16(xrow[c]) : zero;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) pw[c] = ld16(wrow[c]);
+    for (int k0 = 0; k0 < d; k0 += TBK) {
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(&sX[xlds[c]]) = px[c];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) *reinterpret_cast<uint4*>(&sW[wlds[c]]) = pw[c];
+      __syncthreads();
+      if (k0 + TBK < d) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) px[c] = xrow[c] ? ld16(xrow[c] + k0 + TBK) : zero;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) pw[c] = ld16(wrow[c] + k0 + TBK);
+      }
+      if (wave_active) {
+#pragma unroll
+        for (int kk = 0; kk < TBK; kk += 16) {
+          const int kc = kk + (lane >> 5) * 8;
+          const bf16x8_t a0 = lds_frag(&sX[(wm * 64 + (lane & 31)) * LDK + kc]);
+          const bf16x8_t a1 = lds_frag(&sX[(wm * 64 + 32 + (lane & 31)) * LDK + kc]);
+          const bf16x8_t bg = lds_frag(&sW[(wn * 32 + (lane & 31)) * LDK + kc]);
+          const bf16x8_t bu = lds_frag(&sW[(64 + wn * 32 + (lane & 31)) * LDK + kc]);
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bg, acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bg, acc[1], 0, 0, 0);
+          acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bu, acc[2], 0, 0, 0);
+          acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bu, acc[3], 0, 0, 0);
+        }
+      }
+    }
+    if (wave_active) {
+      const int col = n0 + wn * 32 + (lane & 31);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * 64 + mb * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+          if (row < n) h[(size_t)(r0 + row) * d_ff + col] = f32_to_bf16_rne(silu(acc[mb][v]) * acc[2 + mb][v]);
+        }
+    }
+  }
+}
+
+// out[i][n0 + c] = sum_r h[i][r] Wd[n0+c][r]; column tile of 128 (each N-wave 64).
+__global__ __launch_bounds__(512) void ffn_down_mfma_kernel(
+    int d, int d_ff, const uint16_t* __restrict__ slots, size_t rec_elems,
+    const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, int g_begin,
+    int n_tiles, int n_blocks, const uint16_t* __restrict__ h, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[TBM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[128 * LDK];
+  const int lb = xcd_logical_block(blockIdx.x, n_blocks);
+  const int g = g_begin + lb / n_tiles;
+  const int n0 = (lb % n_tiles) * 128;
+  const int r0 = offsets[g];
+  const int n = offsets[g + 1] - r0;
+  if (n <= 0) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const uint16_t* wd = slots + (size_t)group_slot[g] * rec_elems + (size_t)2 * d_ff * d;
+  const uint16_t* wrow[2];
+  int wlds[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch = tid + c * 512;
+    const int r = ch >> 3, c8 = ch & 7;
+    wrow[c] = wd + (size_t)(n0 + r) * d_ff + c8 * 8;
+    wlds[c] = r * LDK + c8 * 8;
+  }
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  for (int m0 = 0; m0 < n; m0 += TBM) {
+    const uint16_t* arow[4];
+    int alds[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int ch = tid + c * 512;
+      const int r = ch >> 3, c8 = ch & 7;
+      arow[c] = (m0 + r < n) ? h + (size_t)(r0 + m0 + r) * d_ff + c8 * 8 : nullptr;
+      alds[c] = r * LDK + c8 * 8;
+    }
+    const bool wave_active = (m0 + wm * 64) < n;
+    f32x16_t acc[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][v] = 0.0f;
+    uint4 pa[4], pw[2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pa[c] = arow[c] ? ld16(arow[c]) : zero;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) pw[c] = ld16(wrow[c]);
+    for (int k0 = 0; k0 < d_ff; k0 += TBK) {
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(&sA[alds[c]]) = pa[c];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) *reinterpret_cast<uint4*>(&sW[wlds[c]]) = pw[c];
+      __syncthreads();
+      if (k0 + TBK < d_ff) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) pa[c] = arow[c] ? ld16(arow[c] + k0 + TBK) : zero;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) pw[c] = ld16(wrow[c] + k0 + TBK);
+      }
+      if (wave_active) {
+#pragma unroll
+        for (int kk = 0; kk < TBK; kk += 16) {
+          const int kc = kk + (lane >> 5) * 8;
+          const bf16x8_t a0 = lds_frag(&sA[(wm * 64 + (lane & 31)) * LDK + kc]);
+          const bf16x8_t a1 = lds_frag(&sA[(wm * 64 + 32 + (lane & 31)) * LDK + kc]);
+          const bf16x8_t b0 = lds_frag(&sW[(wn * 64 + (lane & 31)) * LDK + kc]);
+          const bf16x8_t b1 = lds_frag(&sW[(wn * 64 + 32 + (lane & 31)) * LDK + kc]);
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1], 0, 0, 0);
+          acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[2], 0, 0, 0);
+          acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[3], 0, 0, 0);
+        }
+      }
+    }
+    if (wave_active) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int col = n0 + wn * 64 + nb * 32 + (lane & 31);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = m0 + wm * 64 + mb * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+            if (row < n) out[(size_t)(r0 + row) * d + col] = acc[nb * 2 + mb][v];
+          }
+      }
+    }
+  }
+}
+
+// ============================================================================
+// Combine: y[t] = sum_j (in rank order) g[t,j] out[inv[t,j]] + cpu_partial[t]
+// ============================================================================
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ out,
+                                                      const int32_t* __restrict__ inv,
+                                                      const float* __restrict__ gates,
+                                                      const float* __restrict__ cpu, int T, int k,
+                                                      int d, float* __restrict__ y) {
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (t >= T || c >= d) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const int pos = inv[(size_t)t * k + j];
+    if (pos < 0) continue;
+    const float g = gates[(size_t)t * k + j];
+    const float4 o = *reinterpret_cast<const float4*>(out + (size_t)pos * d + c);
+    acc.x = fmaf(g, o.x, acc.x);
+    acc.y = fmaf(g, o.y, acc.y);
+    acc.z = fmaf(g, o.z, acc.z);
+    acc.w = fmaf(g, o.w, acc.w);
+  }
+  if (cpu != nullptr) {
+    const float4 p = *reinterpret_cast<const float4*>(cpu + (size_t)t * d + c);
+    acc.x += p.x;
+    acc.y += p.y;
+    acc.z += p.z;
+    acc.w += p.w;
+  }
+  *reinterpret_cast<float4*>(y + (size_t)t * d + c) = acc;
+}
+
+inline int launched(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return ft::fail(FT_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+  return FT_OK;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+namespace ft {
+
+int launch_router(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, int T, int d,
+                  int E, int k, int32_t* idx, float* gates, float* logits_ws, void* stream) {
+  if (T < 0 || d <= 0 || d % 8 != 0 || E <= 0 || E > 1024 || k < 1 || k > 8 || k > E)
+    return fail(FT_EINVAL, "router: need d%8==0, 1<=k<=min(E,8), E<=1024");
+  if (T == 0) return FT_OK;
+  if (!x || !w || !idx || !gates || !logits_ws || !aligned16(x) || !aligned16(w))
+    return fail(FT_EINVAL, "router: null or unaligned pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T >= 64) {
+    dim3 grid((T + 7) / 8, (E + 31) / 32);
+    router_logits_kernel<8, 8><<<grid, 256, 0, s>>>(x, w, T, d, E, logits_ws);
+  } else {
+    dim3 grid(T, (E + 15) / 16);
+    router_logits_kernel<1, 4><<<grid, 256, 0, s>>>(x, w, T, d, E, logits_ws);
+  }
+  if (int rc = launched("router_logits")) return rc;
+  router_topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits_ws, allowed, T, E, k, idx, gates);
+  return launched("router_topk");
+}
+
+size_t permute_ws_bytes(int P, int n_groups) {
+  const size_t nblk = (size_t)((P + PB - 1) / PB);
+  return (nblk > 0 ? nblk : 1) * (size_t)(n_groups > 0 ? n_groups : 1) * sizeof(int32_t);
+}
+
+int launch_permute(const int32_t* key, int P, int n_groups, int32_t* offsets, int32_t* perm,
+                   int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
+  if (P < 0 || n_groups < 1 || n_groups > 1024) return fail(FT_EINVAL, "permute: need 1<=n_groups<=1024");
+  if (ws_bytes < permute_ws_bytes(P, n_groups)) return fail(FT_ENOMEM, "permute: workspace too small");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int nblk = (P + PB - 1) / PB;
+  int32_t* counts = static_cast<int32_t*>(ws);
+  if (nblk > 0) {
+    perm_count_kernel<<<nblk, PB, n_groups * sizeof(int32_t), s>>>(key, P, n_groups, counts);
+    if (int rc = launched("perm_count")) return rc;
+  }
+  perm_scan_kernel<<<1, 1024, 0, s>>>(nblk, n_groups, counts, offsets);
+  if (int rc = launched("perm_scan")) return rc;
+  if (nblk > 0) {
+    perm_scatter_kernel<<<nblk, PB, 0, s>>>(key, P, n_groups, counts, perm, inv);
+    if (int rc = launched("perm_scatter")) return rc;
+  }
+  return FT_OK;
+}
+
+int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
+                    const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
+                    int g_begin, int g_end, int max_rows, float* h, float* out, void* stream) {
+  if (d <= 0 || d_ff <= 0 || d % 8 || d_ff % 8 || k < 1) return fail(FT_EINVAL, "ffn_rows: bad shape");
+  const int ng = g_end - g_begin;
+  if (ng <= 0) return FT_OK;
+  if (!aligned16(x) || !aligned16(slots) || !aligned16(h) || !aligned16(out))
+    return fail(FT_EINVAL, "ffn_rows: unaligned pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t rec_elems = (size_t)3 * d * d_ff;
+  const int bpg_up = (d_ff + 3) / 4;
+  const int bpg_dn = (d + 3) / 4;
+  const int nt = max_rows <= 1 ? 1 : max_rows <= 2 ? 2 : max_rows <= 4 ? 4 : 8;
+#define FT_ROWS_LAUNCH(NT)                                                                        \
+  ffn_gateup_rows_kernel<NT><<<ng * bpg_up, 256, 0, s>>>(x, d, d_ff, k, slots, rec_elems,        \
+                                                         group_slot, offsets, perm, g_begin,     \
+                                                         bpg_up, h);                             \
+  if (int rc = launched("ffn_gateup_rows")) return rc;                                          \
+  ffn_down_rows_kernel<NT><<<ng * bpg_dn, 256, 0, s>>>(d, d_ff, slots, rec_elems, group_slot,    \
+                                                       offsets, g_begin, bpg_dn, h, out);        \
+  return launched("ffn_down_rows");
+  switch (nt) {
+    case 1: { FT_ROWS_LAUNCH(1) }
+    case 2: { FT_ROWS_LAUNCH(2) }
+    case 4: { FT_ROWS_LAUNCH(4) }
+    default: { FT_ROWS_LAUNCH(8) }
+  }
+#undef FT_ROWS_LAUNCH
+}
+
+int launch_ffn_mfma(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
+                    const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
+                    int g_begin, int g_end, int /*max_rows*/, uint16_t* h, float* out,
+                    void* stream) {
+  if (d % 128 != 0 || d_ff % 64 != 0 || k < 1)
+    return fail(FT_EINVAL, "ffn_mfma: need d%128==0 and d_ff%64==0");
+  const int ng = g_end - g_begin;
+  if (ng <= 0) return FT_OK;
+  if (!aligned16(x) || !aligned16(slots) || !aligned16(h) || !aligned16(out))
+    return fail(FT_EINVAL, "ffn_mfma: unaligned pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t rec_elems = (size_t)3 * d * d_ff;
+  const int tiles_up = d_ff / 64;
+  const int nb_up = ng * tiles_up;
+  ffn_gateup_mfma_kernel<<<nb_up, 512, 0, s>>>(x, d, d_ff, k, slots, rec_elems, group_slot, offsets,
+                                               perm, g_begin, tiles_up, nb_up, h);
+  if (int rc = launched("ffn_gateup_mfma")) return rc;
+  const int tiles_dn = d / 128;
+  const int nb_dn = ng * tiles_dn;
+  ffn_down_mfma_kernel<<<nb_dn, 512, 0, s>>>(d, d_ff, slots, rec_elems, group_slot, offsets, g_begin,
+                                             tiles_dn, nb_dn, h, out);
+  return launched("ffn_down_mfma");
+}
+
+int launch_combine(const float* out, const int32_t* inv, const float* gates,
+                   const float* cpu_partial, int T, int k, int d, float* y, void* stream) {
+  if (T < 0 || k < 1 || d <= 0 || d % 4 != 0) return fail(FT_EINVAL, "combine: bad shape");
+  if (T == 0) return FT_OK;
+  if (T > 65535) return fail(FT_EINVAL, "combine: T > 65535");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  dim3 grid((d / 4 + 255) / 256, T);
+  combine_kernel<<<grid, 256, 0, s>>>(out, inv, gates, cpu_partial, T, k, d, y);
+  return launched("combine");
+}
+
+}  // namespace ft

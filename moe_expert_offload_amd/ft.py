@@ -1,0 +1,320 @@
+"""Thin ctypes binding of libft (C ABI in include/ft.h).
+
+Argument marshalling only: every call goes to the HIP/C++ library.  Functions
+keep the C names; tensor arguments may be torch tensors (their data_ptr() is
+passed), numpy arrays (host memory), raw integer addresses, or None for NULL.
+Streams are torch streams, raw handles, or None (the current torch stream).
+Loading fails loudly when the built library is missing.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libft.so")
+
+FT_OK = 0
+FT_EINVAL = -1
+FT_ENOMEM = -2
+FT_EBUSY = -3
+FT_ENOPIN = -4
+FT_ECAP = -5
+FT_EHIP = -6
+FT_EUNSUPPORTED = -7
+FT_WOVERLAP_OFF = 1
+FT_PLAN_CAP = 512
+FT_W_BF16 = 0
+FT_W_MXFP4 = 1
+
+EXPORTED = [
+    "ft_strerror", "ft_last_error", "ft_record_bytes", "ft_workspace_bytes", "ft_frac_q16",
+    "ft_qstar_split", "ft_pool_alloc", "ft_pool_free", "ft_bench_bw", "ft_create", "ft_destroy",
+    "ft_get_stats", "ft_reset_stats", "ft_get_config", "ft_n_slots", "ft_router_topk",
+    "ft_permute_workspace_bytes", "ft_permute", "ft_grouped_ffn", "ft_combine",
+    "ft_expert_cache_lookup", "ft_expert_cache_fill", "ft_expert_cache_resize",
+    "ft_expert_cache_where", "ft_moe_decode_layer", "ft_moe_prefill_begin", "ft_moe_prefill_layer",
+    "ft_moe_prefill_end", "ft_prefill_slot",
+]
+
+
+class ft_shape(C.Structure):
+    _fields_ = [("L", C.c_int32), ("E", C.c_int32), ("d", C.c_int32), ("d_ff", C.c_int32),
+                ("k", C.c_int32), ("fmt", C.c_int32)]
+
+
+class ft_config(C.Structure):
+    _fields_ = [("frac_q16", C.c_uint32), ("min_fill", C.c_int32), ("max_fetch", C.c_int32),
+                ("cpu_threads", C.c_int32), ("prefill_overlap", C.c_int32), ("T_max", C.c_int32),
+                ("L_phys", C.c_int32)]
+
+
+_A = C.c_int32 * FT_PLAN_CAP
+
+
+class ft_plan(C.Structure):
+    _fields_ = [("layer", C.c_int32), ("T", C.c_int32), ("k", C.c_int32), ("n_u", C.c_int32),
+                ("n_h", C.c_int32), ("n_m", C.c_int32), ("q", C.c_int32), ("n_c", C.c_int32),
+                ("avail", C.c_int32), ("U", _A), ("H", _A), ("M", _A), ("F_slot", _A), ("G_slot", _A),
+                ("route_slot", _A), ("pair_group", _A), ("idx", _A), ("gates", C.c_float * FT_PLAN_CAP)]
+
+
+class ft_step_stats(C.Structure):
+    _fields_ = [("layer", C.c_int32), ("T", C.c_int32), ("n_u", C.c_int32), ("hits", C.c_int32),
+                ("misses", C.c_int32), ("q", C.c_int32), ("n_c", C.c_int32), ("reserved", C.c_int32),
+                ("h2d_bytes", C.c_int64), ("t_route_us", C.c_double), ("t_ctrl_us", C.c_double),
+                ("t_cpu_us", C.c_double), ("t_total_us", C.c_double)]
+
+
+class ft_stats(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("calls", "unique_hits", "unique_misses", "fills", "cpu_experts",
+                                         "reads", "read_hits", "read_fills", "read_cpu", "h2d_bytes",
+                                         "prefill_layers", "resizes")]
+
+
+class FtError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: {status} ({msg})")
+        self.status = status
+
+
+_lib = None
+P = C.c_void_p
+I = C.c_int32
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libft.so not built at {LIB_PATH}; run `python -m moe_expert_offload_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        sig = {
+            "ft_strerror": (C.c_char_p, [C.c_int]),
+            "ft_last_error": (C.c_char_p, []),
+            "ft_record_bytes": (C.c_size_t, [C.POINTER(ft_shape)]),
+            "ft_workspace_bytes": (C.c_size_t, [C.POINTER(ft_shape), I]),
+            "ft_frac_q16": (C.c_uint32, [C.c_double, C.c_double]),
+            "ft_qstar_split": (I, [I, C.c_uint32, I, I, I]),
+            "ft_pool_alloc": (C.c_int, [C.c_size_t, C.POINTER(P)]),
+            "ft_pool_free": (C.c_int, [P]),
+            "ft_bench_bw": (C.c_int, [C.POINTER(ft_shape), P, I, P, I, C.POINTER(C.c_double), C.POINTER(C.c_double)]),
+            "ft_create": (C.c_int, [C.POINTER(ft_shape), C.POINTER(ft_config), P, C.c_size_t, P, I, P, C.c_size_t, C.POINTER(P)]),
+            "ft_destroy": (C.c_int, [P]),
+            "ft_get_stats": (C.c_int, [P, C.POINTER(ft_stats)]),
+            "ft_reset_stats": (C.c_int, [P]),
+            "ft_get_config": (C.c_int, [P, C.POINTER(ft_config)]),
+            "ft_n_slots": (I, [P]),
+            "ft_router_topk": (C.c_int, [P, P, P, I, I, I, I, P, P, P, P]),
+            "ft_permute_workspace_bytes": (C.c_size_t, [I, I]),
+            "ft_permute": (C.c_int, [P, I, I, P, P, P, P, C.c_size_t, P]),
+            "ft_grouped_ffn": (C.c_int, [P, I, I, I, I, P, P, P, P, I, I, I, I, P, P, I, P]),
+            "ft_combine": (C.c_int, [P, P, P, P, I, I, I, P, P]),
+            "ft_expert_cache_lookup": (C.c_int, [P, I, P, I, C.POINTER(ft_plan)]),
+            "ft_expert_cache_fill": (C.c_int, [P, C.POINTER(ft_plan), P, P, P]),
+            "ft_expert_cache_resize": (C.c_int, [P, P, I]),
+            "ft_expert_cache_where": (I, [P, I, I]),
+            "ft_moe_decode_layer": (C.c_int, [P, I, P, I, P, P, P, P, P, C.POINTER(ft_plan), C.POINTER(ft_step_stats)]),
+            "ft_moe_prefill_begin": (C.c_int, [P, P]),
+            "ft_moe_prefill_layer": (C.c_int, [P, I, P, I, P, P, P, P]),
+            "ft_moe_prefill_end": (C.c_int, [P]),
+            "ft_prefill_slot": (I, [P, I, I]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if hasattr(t, "data_ptr"):
+        return t.data_ptr()
+    if hasattr(t, "ctypes"):
+        return t.ctypes.data
+    raise TypeError(f"cannot pass {type(t)} as a pointer")
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(fn, st):
+    if st < 0:
+        raise FtError(fn, st, lib().ft_last_error().decode(errors="replace"))
+    return st
+
+
+# ---- plain calls ---------------------------------------------------------------
+
+def ft_strerror(st):
+    return lib().ft_strerror(st).decode()
+
+
+def ft_last_error():
+    return lib().ft_last_error().decode(errors="replace")
+
+
+def make_shape(L, E, d, d_ff, k, fmt=FT_W_BF16):
+    return ft_shape(L, E, d, d_ff, k, fmt)
+
+
+def make_config(frac_q16=65536, min_fill=1, max_fetch=-1, cpu_threads=0, prefill_overlap=0, T_max=1, L_phys=0):
+    return ft_config(frac_q16, min_fill, max_fetch, cpu_threads, prefill_overlap, T_max, L_phys)
+
+
+def ft_record_bytes(shape):
+    return lib().ft_record_bytes(C.byref(shape))
+
+
+def ft_workspace_bytes(shape, T_max):
+    return lib().ft_workspace_bytes(C.byref(shape), T_max)
+
+
+def ft_frac_q16(B_P, B_H):
+    return lib().ft_frac_q16(float(B_P), float(B_H))
+
+
+def ft_qstar_split(m, frac_q16, min_fill, max_fetch, avail):
+    return _check("ft_qstar_split", lib().ft_qstar_split(m, frac_q16, min_fill, max_fetch, avail))
+
+
+def ft_pool_alloc(nbytes):
+    p = P()
+    _check("ft_pool_alloc", lib().ft_pool_alloc(nbytes, C.byref(p)))
+    return p.value
+
+
+def ft_pool_free(ptr):
+    _check("ft_pool_free", lib().ft_pool_free(ptr))
+
+
+def ft_bench_bw(shape, host_pool, n_records, dev_scratch, threads=0):
+    bp, bh = C.c_double(), C.c_double()
+    _check("ft_bench_bw", lib().ft_bench_bw(C.byref(shape), _ptr(host_pool), n_records, _ptr(dev_scratch),
+                                            threads, C.byref(bp), C.byref(bh)))
+    return bp.value, bh.value
+
+
+def ft_create(shape, config, host_pool=None, pool_bytes=0, dev_slots=None, n_slots=0, dev_workspace=None,
+              workspace_bytes=0):
+    out = P()
+    _check("ft_create", lib().ft_create(C.byref(shape), C.byref(config), _ptr(host_pool), pool_bytes,
+                                        _ptr(dev_slots), n_slots, _ptr(dev_workspace), workspace_bytes,
+                                        C.byref(out)))
+    return out.value
+
+
+def ft_destroy(ctx):
+    return _check("ft_destroy", lib().ft_destroy(ctx))
+
+
+def ft_get_stats(ctx):
+    s = ft_stats()
+    _check("ft_get_stats", lib().ft_get_stats(ctx, C.byref(s)))
+    return {n: getattr(s, n) for n, _ in ft_stats._fields_}
+
+
+def ft_reset_stats(ctx):
+    return _check("ft_reset_stats", lib().ft_reset_stats(ctx))
+
+
+def ft_get_config(ctx):
+    c = ft_config()
+    _check("ft_get_config", lib().ft_get_config(ctx, C.byref(c)))
+    return c
+
+
+def ft_n_slots(ctx):
+    return lib().ft_n_slots(ctx)
+
+
+def ft_router_topk(x, w_router, allowed, T, d, E, k, idx, gates, logits, stream=None):
+    return _check("ft_router_topk", lib().ft_router_topk(_ptr(x), _ptr(w_router), _ptr(allowed), T, d, E, k,
+                                                         _ptr(idx), _ptr(gates), _ptr(logits), _stream(stream)))
+
+
+def ft_permute_workspace_bytes(P_, n_groups):
+    return lib().ft_permute_workspace_bytes(P_, n_groups)
+
+
+def ft_permute(key, P_, n_groups, offsets, perm, inv, workspace, workspace_bytes, stream=None):
+    return _check("ft_permute", lib().ft_permute(_ptr(key), P_, n_groups, _ptr(offsets), _ptr(perm), _ptr(inv),
+                                                 _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def ft_grouped_ffn(x, T, d, d_ff, k, slots, group_slot, offsets, perm, n_groups, g_begin, g_end,
+                   max_rows_per_group, h_ws, out, form=0, stream=None):
+    return _check("ft_grouped_ffn", lib().ft_grouped_ffn(
+        _ptr(x), T, d, d_ff, k, _ptr(slots), _ptr(group_slot), _ptr(offsets), _ptr(perm), n_groups, g_begin,
+        g_end, max_rows_per_group, _ptr(h_ws), _ptr(out), form, _stream(stream)))
+
+
+def ft_combine(out, inv, gates, cpu_partial, T, k, d, y, stream=None):
+    return _check("ft_combine", lib().ft_combine(_ptr(out), _ptr(inv), _ptr(gates), _ptr(cpu_partial), T, k, d,
+                                                 _ptr(y), _stream(stream)))
+
+
+def ft_expert_cache_lookup(ctx, layer, idx_host, T, plan=None):
+    plan = ft_plan() if plan is None else plan
+    _check("ft_expert_cache_lookup", lib().ft_expert_cache_lookup(ctx, layer, _ptr(idx_host), T, C.byref(plan)))
+    return plan
+
+
+def ft_expert_cache_fill(ctx, plan, copy_stream=None, wait_event=None, done_event=None):
+    return _check("ft_expert_cache_fill", lib().ft_expert_cache_fill(
+        ctx, C.byref(plan), _stream(copy_stream), _ptr(wait_event), _ptr(done_event)))
+
+
+def ft_expert_cache_resize(ctx, new_dev_slots, n_slots):
+    return _check("ft_expert_cache_resize", lib().ft_expert_cache_resize(ctx, _ptr(new_dev_slots), n_slots))
+
+
+def ft_expert_cache_where(ctx, layer, expert):
+    return lib().ft_expert_cache_where(ctx, layer, expert)
+
+
+def ft_moe_decode_layer(ctx, layer, x, T, w_router, allowed, y, compute=None, copy=None, plan=None, stats=None):
+    return _check("ft_moe_decode_layer", lib().ft_moe_decode_layer(
+        ctx, layer, _ptr(x), T, _ptr(w_router), _ptr(allowed), _ptr(y), _stream(compute), _stream(copy),
+        C.byref(plan) if plan is not None else None, C.byref(stats) if stats is not None else None))
+
+
+def ft_moe_prefill_begin(ctx, copy=None):
+    return _check("ft_moe_prefill_begin", lib().ft_moe_prefill_begin(ctx, _stream(copy)))
+
+
+def ft_moe_prefill_layer(ctx, layer, x, T, w_router, y, compute=None, copy=None):
+    return _check("ft_moe_prefill_layer", lib().ft_moe_prefill_layer(
+        ctx, layer, _ptr(x), T, _ptr(w_router), _ptr(y), _stream(compute), _stream(copy)))
+
+
+def ft_moe_prefill_end(ctx):
+    return _check("ft_moe_prefill_end", lib().ft_moe_prefill_end(ctx))
+
+
+def ft_prefill_slot(ctx, layer, expert):
+    return lib().ft_prefill_slot(ctx, layer, expert)
+
+
+def plan_dict(plan):
+    """Plan fields as Python lists (host)."""
+    n = plan.T * plan.k
+    return {
+        "layer": plan.layer, "U": list(plan.U[:plan.n_u]), "H": list(plan.H[:plan.n_h]),
+        "M": list(plan.M[:plan.n_m]), "q": plan.q, "n_c": plan.n_c, "avail": plan.avail,
+        "F_slot": list(plan.F_slot[:plan.q]), "G_slot": list(plan.G_slot[:plan.n_h + plan.q]),
+        "route_slot": list(plan.route_slot[:n]), "pair_group": list(plan.pair_group[:n]),
+        "idx": list(plan.idx[:n]), "gates": list(plan.gates[:n]),
+    }
