@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE layer served from an elastic expert cache, one MI355X.
+
+A step is one decode step through every layer of the stack: per layer the router,
+the cache decisions and the fetch split, the fills of F over PCIe, the CPU
+branch for C on the host cores, the grouped SwiGLU FFN of H and F, and the merge.
+Default workload: 40 stacked layers, d=2048, E=128, top-8, d_ff=768, bf16
+experts, batch 1, GPU cache 37 % of the (layer, expert) pairs, Zipf(1.1)
+popularity with 0.6 step-to-step reuse, fetch fraction from B_P and B_H
+measured on this machine.  Inputs are seeded and synthetic, resident in HBM
+(activations, router weights, routing masks) or pinned host memory (the pool)
+before the timed region starts.
+
+Also measured (unless --no-prefill): one 8192-token prefill chunk through the
+43-layer d=4096, E=256, top-6, d_ff=2048 shape with full-layer double buffering.
+
+Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE decode tok/s + 8k-token prefill tok/s (DSV4 shape); % of HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    src = os.path.join(ROOT, "moe_expert_offload_amd", "csrc", "kernels.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were
+    taken on the current kernel source (profiles/<kernel>__<workload>.counters.txt)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def phased_time(m, q, S, B_P, B_H):
+    # fills at B_P; host branch at B_H - B_P while the link is busy, B_H after
+    t_fill = q * S / B_P if q > 0 else 0.0
+    rest = (m - q) * S
+    done = max(B_H - B_P, 0.0) * t_fill
+    return t_fill if done >= rest else t_fill + (rest - done) / B_H
+
+
+def run_decode(args, torch, ft, synth, HostPool):
+    wl = synth.WORKLOADS[args.workload]
+    s = wl.shape
+    T = wl.T
+    S = s.record_bytes
+    steps_total = args.warmup + args.steps
+    steps_gen = steps_total + args.steps  # a second pass over further steps carries the kernel timing
+    L_phys = s.L if args.l_phys <= 0 else min(args.l_phys, s.L)
+    log(f"decode workload {wl.name}: pool {L_phys * s.E} records x {S / 1e6:.2f} MB = {L_phys * s.E * S / 1e9:.1f} GB")
+    t = time.time()
+    pool = HostPool(s.record_elems, L_phys * s.E)
+    synth.fill_records_torch(pool.view, wl.config_id, seed=args.seed)
+    log(f"pool allocated and filled in {time.time() - t:.1f} s")
+
+    fshape = ft.make_shape(s.L, s.E, s.d, s.d_ff, s.k)
+    scratch = torch.empty(64 * S, dtype=torch.uint8, device="cuda")
+    B_P, B_H = ft.ft_bench_bw(fshape, pool.ptr, 64, scratch, 0)
+    del scratch
+    fq = ft.ft_frac_q16(B_P, B_H) if args.frac_q16 < 0 else args.frac_q16
+    log(f"B_P {B_P / 1e9:.1f} GB/s, B_H {B_H / 1e9:.1f} GB/s, frac_q16 {fq}")
+
+    wr = [torch.from_numpy(synth.router_weights(wl, l, seed=args.seed).view(np.int16)).cuda() for l in range(s.L)]
+    tr = synth.trace_for(wl, seed=args.seed, steps=steps_gen)
+    allowed = np.zeros((steps_gen, s.L, T, s.E), dtype=np.uint8)
+    st_i, l_i, b_i = np.meshgrid(np.arange(steps_gen), np.arange(s.L), np.arange(T), indexing="ij")
+    for j in range(s.k):
+        allowed[st_i, l_i, b_i, tr[:, :, :, j].astype(np.int64)] = 1
+    allowed_d = torch.from_numpy(allowed).cuda()
+    xh = np.empty((steps_gen, s.L, T, s.d), dtype=np.uint16)
+    for st in range(steps_gen):
+        for l in range(s.L):
+            xh[st, l] = synth.tokens(wl, st, l, T=T, seed=args.seed)
+    xs = torch.from_numpy(xh.view(np.int16)).cuda()
+    del xh
+    ys = torch.empty((s.L, T, s.d), dtype=torch.float32, device="cuda")
+
+    N = wl.n_slots
+    cfg = ft.make_config(frac_q16=fq, min_fill=args.min_fill, max_fetch=args.max_fetch, cpu_threads=args.cpu_threads,
+                         prefill_overlap=0, T_max=T, L_phys=L_phys)
+    slots = torch.empty(N * S, dtype=torch.uint8, device="cuda")
+    wsb = ft.ft_workspace_bytes(fshape, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    ctx = ft.ft_create(fshape, cfg, pool.ptr, pool.nbytes, slots, N, ws, wsb)
+    compute = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    st_call = ft.ft_step_stats()
+    calls = []
+
+    def step(st, record):
+        for l in range(s.L):
+            ft.ft_moe_decode_layer(ctx, l, xs[st, l], T, wr[l], allowed_d[st, l], ys[l], compute, copy,
+                                   None, st_call)
+            if record:
+                calls.append((st_call.hits, st_call.misses, st_call.q, st_call.n_c, st_call.t_cpu_us,
+                               st_call.t_total_us, st_call.t_route_us, st_call.t_ctrl_us, st_call.t_issue_us,
+                               st_call.t_cpu_work_us, st_call.cpu_caller_items))
+
+    try:
+        for st in range(args.warmup):
+            step(st, False)
+        torch.cuda.synchronize()
+        ft.ft_reset_stats(ctx)
+        # timed region: the steps as they run in serving, no timing events
+        t0 = time.perf_counter()
+        for st in range(args.warmup, steps_total):
+            step(st, True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        stats = ft.ft_get_stats(ctx)
+        # second timed region over the next steps of the same trace: every grouped-FFN
+        # kernel launched with start/stop events (for the roofline)
+        ft.ft_profile_enable(ctx, True)
+        t2 = time.perf_counter()
+        for st in range(steps_total, steps_total + args.steps):
+            step(st, False)
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        prof = ft.ft_profile_read(ctx)
+        ft.ft_profile_enable(ctx, False)
+    finally:
+        ft.ft_destroy(ctx)
+    elapsed = t1 - t0
+    ms_gu = prof["ms_gateup"] / max(prof["launches"], 1)
+    ms_dn = prof["ms_down"] / max(prof["launches"], 1)
+    bytes_gu = prof["bytes_gateup"] / max(prof["launches"], 1)
+    bytes_dn = prof["bytes_down"] / max(prof["launches"], 1)
+    gu_gbs = prof["bytes_gateup"] / (prof["ms_gateup"] * 1e-3) / 1e9 if prof["ms_gateup"] > 0 else 0.0
+    dn_gbs = prof["bytes_down"] / (prof["ms_down"] * 1e-3) / 1e9 if prof["ms_down"] > 0 else 0.0
+    # modelled floor of the timed steps: per call the slower of the GPU weight stream
+    # and the miss path (fills at B_P next to the host branch, phase-aware)
+    floor_s = 0.0
+    for hits, misses, q, n_c, *_ in calls:
+        floor_s += max((hits + q) * S / (HBM_PEAK_GBS * 1e9), phased_time(misses, q, S, B_P, B_H))
+    reads = max(stats["reads"], 1)
+    res = {
+        "tok_s": args.steps * T / elapsed,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "workload": wl.name, "T": T, "L": s.L, "n_slots": N, "L_phys": L_phys,
+        "B_P_GBs": B_P / 1e9, "B_H_GBs": B_H / 1e9, "frac_q16": fq, "min_fill": args.min_fill,
+        "cpu_threads": args.cpu_threads,
+        "miss_rate_reads": 1.0 - stats["read_hits"] / reads,
+        "miss_rate_unique": stats["unique_misses"] / max(stats["unique_hits"] + stats["unique_misses"], 1),
+        "fills_per_step": stats["fills"] / args.steps, "cpu_experts_per_step": stats["cpu_experts"] / args.steps,
+        "h2d_GB_per_step": stats["h2d_bytes"] / args.steps / 1e9,
+        "modelled_floor_ms_per_step": floor_s / args.steps * 1e3,
+        "host_cpu_branch_ms_per_step": sum(c[4] for c in calls) / args.steps / 1e3,
+        "host_call_us": {
+            "route": float(np.mean([c[6] for c in calls])) if calls else 0.0,
+            "ctrl": float(np.mean([c[7] for c in calls])) if calls else 0.0,
+            "cpu_when_used": float(np.mean([c[4] for c in calls if c[3] > 0])) if any(c[3] > 0 for c in calls) else 0.0,
+            "cpu_work_when_used": float(np.mean([c[9] for c in calls if c[3] > 0])) if any(c[3] > 0 for c in calls) else 0.0,
+            "cpu_work_p50": float(np.percentile([c[9] for c in calls if c[3] > 0], 50)) if any(c[3] > 0 for c in calls) else 0.0,
+            "cpu_work_p90": float(np.percentile([c[9] for c in calls if c[3] > 0], 90)) if any(c[3] > 0 for c in calls) else 0.0,
+            "cpu_work_per_expert_p50": float(np.percentile([c[9] / c[3] for c in calls if c[3] > 0], 50)) if any(c[3] > 0 for c in calls) else 0.0,
+            "issue": float(np.mean([c[8] for c in calls])) if calls else 0.0,
+            "cpu_caller_items_when_used": float(np.mean([c[10] for c in calls if c[3] > 0])) if any(c[3] > 0 for c in calls) else 0.0,
+            "cpu_items_when_used": float(np.mean([c[3] * 48 + 64 for c in calls if c[3] > 0])) if any(c[3] > 0 for c in calls) else 0.0,
+            "issue_when_fill": float(np.mean([c[8] for c in calls if c[2] > 0])) if any(c[2] > 0 for c in calls) else 0.0,
+            "total": float(np.mean([c[5] for c in calls])) if calls else 0.0,
+        },
+        "timed_with_kernel_events_ms_per_step": (t3 - t2) / args.steps * 1e3,
+        "kernels": {
+            "ffn_gateup_rows": {"avg_us": ms_gu * 1e3, "bytes_per_launch": bytes_gu, "GBs": gu_gbs,
+                                "launches": prof["launches"]},
+            "ffn_down_rows": {"avg_us": ms_dn * 1e3, "bytes_per_launch": bytes_dn, "GBs": dn_gbs},
+        },
+    }
+    roofline = {"bound": "hbm", "kernel": "ffn_gateup_rows_kernel", "achieved": round(gu_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                "traffic": stored_traffic("ffn_gateup_rows_kernel", args.workload),
+                "avg_launch_us": round(ms_gu * 1e3, 3), "algorithmic_bytes_per_launch": round(bytes_gu)}
+    return res, roofline, (pool, wl, tr, fq, L_phys)
+
+
+def run_prefill(args, torch, ft, synth, HostPool):
+    wl = synth.WORKLOADS["c4"]
+    s = wl.shape
+    T = wl.T
+    S = s.record_bytes
+    L_phys = max(1, min(args.prefill_l_phys, s.L))
+    log(f"prefill workload {wl.name}: pool {L_phys * s.E} records = {L_phys * s.E * S / 1e9:.1f} GB (aliased)")
+    t = time.time()
+    pool = HostPool(s.record_elems, L_phys * s.E)
+    synth.fill_records_torch(pool.view, wl.config_id, seed=args.seed)
+    log(f"pool allocated and filled in {time.time() - t:.1f} s")
+    try:
+        fshape = ft.make_shape(s.L, s.E, s.d, s.d_ff, s.k)
+        N = wl.n_slots
+        cfg = ft.make_config(frac_q16=0, min_fill=0, max_fetch=0, cpu_threads=2, prefill_overlap=1, T_max=T,
+                             L_phys=L_phys)
+        slots = torch.empty(N * S, dtype=torch.uint8, device="cuda")
+        wsb = ft.ft_workspace_bytes(fshape, T)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        wr = [torch.from_numpy(synth.router_weights(wl, l, seed=args.seed).view(np.int16)).cuda() for l in range(s.L)]
+        xs = [synth.tokens_torch(wl.config_id, 0, l, T, s.d, seed=args.seed) for l in range(s.L)]
+        y = torch.empty((T, s.d), dtype=torch.float32, device="cuda")
+        ctx = ft.ft_create(fshape, cfg, pool.ptr, pool.nbytes, slots, N, ws, wsb)
+        compute = torch.cuda.current_stream()
+        copy = torch.cuda.Stream()
+        try:
+            # warm-up: two layers
+            ft.ft_moe_prefill_begin(ctx, copy)
+            for l in range(2):
+                ft.ft_moe_prefill_layer(ctx, l, xs[l], T, wr[l], y, compute, copy)
+            ft.ft_moe_prefill_end(ctx)
+            torch.cuda.synchronize()
+            ft.ft_profile_enable(ctx, True)
+            t0 = time.perf_counter()
+            ft.ft_moe_prefill_begin(ctx, copy)
+            for l in range(s.L):
+                ft.ft_moe_prefill_layer(ctx, l, xs[l], T, wr[l], y, compute, copy)
+            ft.ft_moe_prefill_end(ctx)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            prof = ft.ft_profile_read(ctx)
+            ft.ft_profile_enable(ctx, False)
+        finally:
+            ft.ft_destroy(ctx)
+    finally:
+        pool.free()
+    el = t1 - t0
+    ms = prof["ms_gateup"] + prof["ms_down"]
+    fl = prof["flops_gateup"] + prof["flops_down"]
+    tflops = fl / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+    by = prof["bytes_gateup"] + prof["bytes_down"]
+    return {
+        "tok_s": T / el, "s_per_chunk": el, "T": T, "L": s.L, "L_phys": L_phys, "n_slots": N,
+        "h2d_GB": s.L * s.E * S / 1e9, "h2d_GBs_effective": s.L * s.E * S / el / 1e9,
+        "ffn_kernel_ms_per_layer": ms / max(prof["launches"], 1),
+        "ffn_mfma": {"bound_note": "weight stream: HBM-bound at this shape", "TFLOPs": round(tflops, 1),
+                     "frac_of_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "GBs": round(by / (ms * 1e-3) / 1e9, 1) if ms > 0 else 0.0,
+                     "gateup_ms_per_layer": prof["ms_gateup"] / max(prof["launches"], 1),
+                     "down_ms_per_layer": prof["ms_down"] / max(prof["launches"], 1)},
+    }
+
+
+def cpu_baseline(args, pool, wl, tr, fq, L_phys, budget_s):
+    """The oracle as it stands, timed on the host over the first steps of the same trace."""
+    from threadpoolctl import threadpool_info
+
+    from moe_expert_offload_amd import synth
+    from oracle.cache import SlotTable
+    from oracle.ffn import moe_layer
+    from oracle.router import route
+
+    s = wl.shape
+    T = wl.T
+    cache = SlotTable(wl.n_slots, s.L, s.E)
+    wr = [synth.router_weights(wl, l, seed=args.seed) for l in range(s.L)]
+    done = 0
+    t0 = time.perf_counter()
+    while done < tr.shape[0]:
+        st = done
+        for l in range(s.L):
+            x = synth.tokens(wl, st, l, T=T, seed=args.seed)
+            allowed = synth.allowed_mask(tr[st, l], s.E)
+            idx, g, _ = route(x, wr[l], s.k, allowed)
+            cache.lookup(l, idx, fq, args.min_fill, -1)
+            moe_layer(x, idx, g, lambda e: pool.view[(l % L_phys) * s.E + e], s.d, s.d_ff)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(done * T / el, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {done} decode steps x {s.L} layers of the same trace and inputs "
+                      f"(fp64 NumPy oracle: router, cache decisions, exact layer output), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=192)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="c2", choices=["c2", "c2b8", "c3"])
+    ap.add_argument("--l-phys", type=int, default=0, help="physical layers in the host pool (0 = all)")
+    ap.add_argument("--min-fill", type=int, default=1)
+    ap.add_argument("--max-fetch", type=int, default=-1)
+    ap.add_argument("--frac-q16", type=int, default=-1, help="override the measured fetch fraction")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--prefill", dest="prefill", action="store_true", default=True)
+    ap.add_argument("--no-prefill", dest="prefill", action="store_false")
+    ap.add_argument("--prefill-l-phys", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from moe_expert_offload_amd import ft, synth
+    from moe_expert_offload_amd.pool import HostPool
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ft.lib()
+    dec, roof, keep = run_decode(args, torch, ft, synth, HostPool)
+    pool, wl, tr, fq, L_phys = keep
+    cpu = None
+    try:
+        if not args.no_cpu_baseline:
+            log("timing the CPU oracle on the host")
+            cpu = cpu_baseline(args, pool, wl, tr, fq, L_phys, args.cpu_budget_s)
+    finally:
+        pool.free()
+    pre = run_prefill(args, torch, ft, synth, HostPool) if args.prefill else None
+    out = {
+        "metric": METRIC, "value": round(dec["tok_s"], 3), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dec["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": dec["workload"], "global_batch": dec["T"], "layers": dec["L"],
+                   "cache_slots": dec["n_slots"], "parallelism": "single-gpu"},
+        "roofline": roof, "cpu_baseline": cpu, "decode": dec, "prefill": pre,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -73,7 +73,8 @@ typedef struct {
  *   min_fill        fills kept per call even when the split gives fewer, capped at m
  *                   ([FT] §3.2 "always retains at least one fill"; 0 = the shipped rule).
  *   max_fetch       -1: q from the split; n >= 0: at most n fills per call (0 never fetches).
- *   cpu_threads     worker threads of the CPU branch (0 = one per CPU in the affinity mask).
+ *   cpu_threads     worker threads of the CPU branch (0 = one per CPU of the affinity mask
+ *                   except the first, which is left to the calling thread).
  *   prefill_overlap 1 = full-layer double-buffered prefill ([FT] §3.1); needs >= 2E slots.
  *   T_max           largest T of any call (sizes the workspace).
  *   L_phys          physical layers in the host pool (0 = L). */
@@ -110,12 +111,15 @@ typedef struct {
 
 /* Per-call measurements (host clock, microseconds). */
 typedef struct {
-  int32_t layer, T, n_u, hits, misses, q, n_c, reserved;
+  int32_t layer, T, n_u, hits, misses, q, n_c;
+  int32_t cpu_caller_items; /* CPU-branch work items the calling thread did itself */
   int64_t h2d_bytes;
   double t_route_us;   /* router launch until its results reached the host */
   double t_ctrl_us;    /* cache decisions */
   double t_cpu_us;     /* CPU branch, from post to completion */
   double t_total_us;   /* whole call, host side */
+  double t_issue_us;   /* issuing the fills and the GPU work after the decisions */
+  double t_cpu_work_us; /* CPU branch, from post to its last work item */
 } ft_step_stats;
 
 /* Cumulative counters since create or the last resize ([AIN] "How to run it in
@@ -177,7 +181,8 @@ int ft_bench_bw(const ft_shape* shape, const void* host_pool, int32_t n_records,
  * dev_slots: device buffer of n_slots records (the elastic cache, [FT] §3).
  * dev_workspace: device buffer of at least ft_workspace_bytes(shape, T_max).
  * The library allocates its pinned staging buffers and starts its CPU worker
- * pool here.  Errors: FT_EINVAL (shape/config), FT_ECAP (prefill_overlap and
+ * pool here, and reads every page of the host pool once (in parallel) so that
+ * the CPU branch takes no first-touch page faults while serving.  Errors: FT_EINVAL (shape/config), FT_ECAP (prefill_overlap and
  * n_slots < 2E), FT_ENOPIN (host_pool not pinned), FT_ENOMEM, FT_EHIP. */
 int ft_create(const ft_shape* shape, const ft_config* config, const void* host_pool,
               size_t pool_bytes, void* dev_slots, int32_t n_slots, void* dev_workspace,
@@ -236,6 +241,17 @@ int ft_combine(const float* out, const int32_t* inv, const float* gates,
                const float* cpu_partial, int32_t T, int32_t k, int32_t d, float* y,
                void* stream);
 
+/* Host expert kernel, the CPU branch of a decode call ([FT] §3.2: experts of C run
+ * in place from the host pool and return gate-weighted per-token partials; §4.1:
+ * persistent workers with SIMD kernels).  For n_exp experts with bf16 records
+ * `records[i]` (host or pinned) and uses u in [use_off[i], use_off[i+1]) of token
+ * use_t[u] with gate use_g[u]:  partial[t] = sum over uses of g * FFN_i(x[t]),
+ * fp32, overwritten.  x: host bf16 [T, d].  threads: workers of a pool made for
+ * this call (0 = default count).  At most 64 uses per expert. */
+int ft_host_experts(const void* x, int32_t T, int32_t d, int32_t d_ff, const void* const* records,
+                    const int32_t* use_off, const int32_t* use_t, const float* use_g, int32_t n_exp,
+                    int32_t threads, float* partial);
+
 /* ---- expert cache -------------------------------------------------------------- */
 
 /* Decisions of one decode call for routed ids idx_host (host int32 [T, k]):
@@ -292,6 +308,25 @@ int ft_moe_prefill_end(ft_ctx_t ctx);
 
 /* Device slot of expert e in the buffer serving `layer` during prefill, or -1. */
 int32_t ft_prefill_slot(ft_ctx_t ctx, int32_t layer, int32_t expert);
+
+/* ---- kernel timing ---------------------------------------------------------------
+ * When enabled, each of the two kernels of every grouped-FFN launch issued by
+ * ft_moe_decode_layer and ft_moe_prefill_layer is launched with start and stop
+ * events that bracket the kernel itself (hipExtLaunchKernel), and
+ * its algorithmic bytes and flops are recorded: per expert group of n rows,
+ *   gate/up: 2*d*d_ff*2 weight bytes + n*d*2 (x) + n*d_ff*hb (h), 2*2*n*d*d_ff flops
+ *   down:    d*d_ff*2 weight bytes + n*d_ff*hb (h) + n*d*4 (out), 2*n*d*d_ff flops
+ * with hb = 4 in the row-streaming form and 2 in the MFMA form; groups with n = 0
+ * count nothing.  enable(1) clears what was recorded; read() waits for the
+ * recorded events and sums them. */
+typedef struct {
+  int64_t launches;
+  double ms_gateup, ms_down;
+  double bytes_gateup, bytes_down;
+  double flops_gateup, flops_down;
+} ft_profile;
+int ft_profile_enable(ft_ctx_t ctx, int32_t on);
+int ft_profile_read(ft_ctx_t ctx, ft_profile* out);
 
 #ifdef __cplusplus
 }

@@ -4,11 +4,13 @@
 // [FT] = "FreeToken: Efficient Edge-Native MoE Serving with Bandwidth-Adaptive
 // Execution" (arXiv 2608.16157).
 #include <hip/hip_runtime.h>
+#include <immintrin.h>
 
 #include <algorithm>
 #include <chrono>
 #include <cstring>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "cache.h"
@@ -44,6 +46,26 @@ double now_us() {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+void prefault_host(const void* p, size_t bytes, int threads) {
+  if (!p || bytes == 0) return;
+  threads = std::max(1, std::min(threads, 64));
+  const size_t page = 4096;
+  const size_t chunk = ((bytes / threads) / page + 1) * page;
+  std::vector<std::thread> ts;
+  for (int i = 0; i < threads; ++i) {
+    const size_t b = (size_t)i * chunk;
+    if (b >= bytes) break;
+    const size_t e = std::min(bytes, b + chunk);
+    ts.emplace_back([p, b, e, page] {
+      const volatile uint8_t* q = static_cast<const volatile uint8_t*>(p);
+      uint8_t acc = 0;
+      for (size_t o = b; o < e; o += page) acc ^= q[o];
+      (void)acc;
+    });
+  }
+  for (auto& t : ts) t.join();
+}
+
 bool shape_ok(const ft_shape* s) {
   return s && s->L > 0 && s->E > 0 && s->E <= 1024 && s->d > 0 && s->d % 8 == 0 && s->d_ff > 0 &&
          s->d_ff % 8 == 0 && s->k >= 1 && s->k <= 8 && s->k <= s->E && s->fmt == FT_W_BF16;
@@ -51,7 +73,7 @@ bool shape_ok(const ft_shape* s) {
 
 // Workspace carve: offsets of each device array for calls of up to T_max tokens.
 struct Carve {
-  size_t idx, gates, logits, key, gslot, bufslot, offsets, perm, inv, pws, h, out, cpu, total;
+  size_t ticket, idx, gates, logits, key, gslot, bufslot, offsets, perm, inv, pws, h, out, cpu, total;
   size_t pws_bytes;
   int g_max;
 };
@@ -67,6 +89,7 @@ Carve carve(const ft_shape* s, int T_max) {
     o += align256(bytes);
     return at;
   };
+  c.ticket = take(4);
   c.idx = take(P * 4);
   c.gates = take(P * 4);
   c.logits = take((size_t)T_max * s->E * 4);
@@ -110,6 +133,8 @@ struct ft_ctx {
   int32_t* h_key = nullptr;
   int32_t* h_gslot = nullptr;
   float* h_partial = nullptr;
+  uint32_t* h_flag = nullptr;  // router's publication sequence number
+  uint32_t route_seq = 0;
 
   hipEvent_t ev_route = nullptr, ev_fill = nullptr, ev_done = nullptr;
   hipEvent_t ev_pf_fill[2] = {nullptr, nullptr}, ev_pf_comp[2] = {nullptr, nullptr};
@@ -120,6 +145,18 @@ struct ft_ctx {
   ft_plan scratch_plan{};
   int prefill_next = -1;
 
+  // kernel timing (ft_profile_enable)
+  struct ProfRec {
+    hipEvent_t ev[4];
+    double bytes_up, bytes_dn, flops_up, flops_dn;
+    int32_t* offsets;  // pinned copy of the group offsets (prefill) or null
+    int n_groups, hb;
+  };
+  bool prof_on = false;
+  std::vector<ProfRec> prof;
+  std::vector<hipEvent_t> ev_free;
+  std::vector<int32_t*> off_free;
+
   template <typename T>
   T* wsp(size_t off) const { return reinterpret_cast<T*>(ws + off); }
   const uint16_t* record(int layer, int e) const {
@@ -127,6 +164,40 @@ struct ft_ctx {
   }
   uint16_t* slot_ptr(int s) const { return slots + (size_t)s * rec_elems; }
 };
+
+namespace {
+
+// Three timing events for one grouped-FFN launch, or null when timing is off.
+ft_ctx::ProfRec* prof_begin(ft_ctx* c) {
+  if (!c->prof_on) return nullptr;
+  ft_ctx::ProfRec r{};
+  for (int i = 0; i < 4; ++i) {
+    if (!c->ev_free.empty()) {
+      r.ev[i] = c->ev_free.back();
+      c->ev_free.pop_back();
+    } else if (hipEventCreate(&r.ev[i]) != hipSuccess) {
+      return nullptr;
+    }
+  }
+  c->prof.push_back(r);
+  return &c->prof.back();
+}
+
+// Algorithmic bytes and flops of one launch from its rows per group (see ft.h).
+void prof_account(ft_ctx* c, ft_ctx::ProfRec* r, const int* rows, int n_groups, int hb) {
+  const double d = c->shape.d, dff = c->shape.d_ff;
+  r->bytes_up = r->bytes_dn = r->flops_up = r->flops_dn = 0.0;
+  for (int g = 0; g < n_groups; ++g) {
+    const double n = rows[g];
+    if (n <= 0) continue;
+    r->bytes_up += 2.0 * d * dff * 2.0 + n * d * 2.0 + n * dff * hb;
+    r->bytes_dn += d * dff * 2.0 + n * dff * hb + n * d * 4.0;
+    r->flops_up += 4.0 * n * d * dff;
+    r->flops_dn += 2.0 * n * d * dff;
+  }
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -222,15 +293,23 @@ int ft_create(const ft_shape* shape, const ft_config* config, const void* host_p
         hipHostMalloc((void**)&c->h_x, (size_t)c->t_dec * shape->d * 2) != hipSuccess ||
         hipHostMalloc((void**)&c->h_key, P * 4) != hipSuccess ||
         hipHostMalloc((void**)&c->h_gslot, (size_t)(c->cv.g_max + 2 * shape->E) * 4) != hipSuccess ||
-        hipHostMalloc((void**)&c->h_partial, (size_t)c->t_dec * shape->d * 4) != hipSuccess)
+        hipHostMalloc((void**)&c->h_partial, (size_t)c->t_dec * shape->d * 4) != hipSuccess ||
+        hipHostMalloc((void**)&c->h_flag, 256) != hipSuccess)
       return bail(FT_ENOMEM, "create: pinned staging allocation failed");
     hipEvent_t* evs[] = {&c->ev_route, &c->ev_fill, &c->ev_done, &c->ev_pf_fill[0], &c->ev_pf_fill[1],
                          &c->ev_pf_comp[0], &c->ev_pf_comp[1]};
     for (hipEvent_t* e : evs)
       if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess)
         return bail(FT_EHIP, "create: hipEventCreate failed");
+    if (hipMemset(c->ws + c->cv.ticket, 0, 4) != hipSuccess) return bail(FT_EHIP, "create: hipMemset failed");
+    *c->h_flag = 0;
     c->cpu = ft::cpu_pool_create(config->cpu_threads);
     c->cfg.cpu_threads = ft::cpu_pool_threads(c->cpu);
+    // Pinned host memory is mapped into the process lazily: the first CPU access
+    // to each page faults (about a microsecond per 4 KB page, serialised per
+    // thread).  Touch the whole pool once here, in parallel, so the CPU branch
+    // never faults on the hot path.
+    prefault_host(host_pool, (size_t)c->L_phys * shape->E * c->S, c->cfg.cpu_threads + 1);
     c->dev = true;
   }
   *out = c;
@@ -248,7 +327,13 @@ int ft_destroy(ft_ctx_t c) {
                       c->ev_pf_comp[0], c->ev_pf_comp[1]};
   for (hipEvent_t e : evs)
     if (e) (void)hipEventDestroy(e);
-  void* pins[] = {c->h_idx, c->h_gates, c->h_x, c->h_key, c->h_gslot, c->h_partial};
+  for (auto& r : c->prof) {
+    for (hipEvent_t e : r.ev) c->ev_free.push_back(e);
+    if (r.offsets) c->off_free.push_back(r.offsets);
+  }
+  for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
+  for (int32_t* o : c->off_free) (void)hipHostFree(o);
+  void* pins[] = {c->h_idx, c->h_gates, c->h_x, c->h_key, c->h_gslot, c->h_partial, c->h_flag};
   for (void* p : pins)
     if (p) (void)hipHostFree(p);
   delete c->cache;
@@ -327,6 +412,34 @@ int ft_combine(const float* out, const int32_t* inv, const float* gates, const f
   return ft::launch_combine(out, inv, gates, cpu_partial, T, k, d, y, stream);
 }
 
+int ft_host_experts(const void* x, int32_t T, int32_t d, int32_t d_ff, const void* const* records,
+                    const int32_t* use_off, const int32_t* use_t, const float* use_g, int32_t n_exp,
+                    int32_t threads, float* partial) {
+  if (!x || !partial || T < 1 || d <= 0 || d_ff <= 0 || n_exp < 0 || (n_exp > 0 && (!records || !use_off)))
+    return fail(FT_EINVAL, "host_experts: bad argument");
+  std::vector<ft::CpuExpert> ex(n_exp);
+  for (int i = 0; i < n_exp; ++i) {
+    const int n = use_off[i + 1] - use_off[i];
+    if (n < 0 || n > 64 || !records[i]) return fail(FT_EINVAL, "host_experts: 0..64 uses per expert");
+    ex[i].rec = static_cast<const uint16_t*>(records[i]);
+    ex[i].n_use = n;
+    for (int u = 0; u < n; ++u) {
+      const int t = use_t[use_off[i] + u];
+      if (t < 0 || t >= T) return fail(FT_EINVAL, "host_experts: token out of range");
+      ex[i].use[u] = ft::CpuUse{t, use_g[use_off[i] + u]};
+    }
+  }
+  if (n_exp == 0) {
+    std::memset(partial, 0, sizeof(float) * (size_t)T * d);
+    return FT_OK;
+  }
+  ft::CpuPool* pool = ft::cpu_pool_create(threads);
+  ft::cpu_pool_submit(pool, static_cast<const uint16_t*>(x), T, d, d_ff, ex.data(), n_exp, partial);
+  ft::cpu_pool_wait(pool);
+  ft::cpu_pool_destroy(pool);
+  return FT_OK;
+}
+
 // ---- cache control --------------------------------------------------------------
 
 int ft_expert_cache_lookup(ft_ctx_t c, int32_t layer, const int32_t* idx_host, int32_t T, ft_plan* plan) {
@@ -396,14 +509,32 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
   float* d_gates = c->wsp<float>(c->cv.gates);
   // order after everything this context issued before, whatever the stream
   FT_HIP(hipStreamWaitEvent(cs, c->ev_done, 0));
-  if (int rc = ft::launch_router(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), allowed,
-                                 T, d, E, k, d_idx, d_gates, c->wsp<float>(c->cv.logits), cs))
+  // the router publishes ids, gates and x straight to pinned host memory, then a
+  // sequence number; the host spins on it (bounded), the event is the fallback
+  const uint32_t seq = ++c->route_seq == 0 ? ++c->route_seq : c->route_seq;
+  if (int rc = ft::launch_router_decode(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
+                                        allowed, T, d, E, k, c->wsp<float>(c->cv.logits), d_idx, d_gates,
+                                        c->wsp<unsigned int>(c->cv.ticket), c->h_idx, c->h_gates, c->h_x,
+                                        c->h_flag, seq, cs))
     return rc;
-  FT_HIP(hipMemcpyAsync(c->h_idx, d_idx, (size_t)P * 4, hipMemcpyDeviceToHost, cs));
-  FT_HIP(hipMemcpyAsync(c->h_gates, d_gates, (size_t)P * 4, hipMemcpyDeviceToHost, cs));
-  FT_HIP(hipMemcpyAsync(c->h_x, x, (size_t)T * d * 2, hipMemcpyDeviceToHost, cs));
   FT_HIP(hipEventRecord(c->ev_route, cs));
-  FT_HIP(hipEventSynchronize(c->ev_route));
+  {
+    bool seen = false;
+    const double spin_end = now_us() + 2000.0;
+    for (int i = 0;; ++i) {
+      if (__atomic_load_n(c->h_flag, __ATOMIC_ACQUIRE) == seq) {
+        seen = true;
+        break;
+      }
+      _mm_pause();
+      if ((i & 1023) == 1023 && now_us() > spin_end) break;
+    }
+    if (!seen) {
+      FT_HIP(hipEventSynchronize(c->ev_route));
+      if (__atomic_load_n(c->h_flag, __ATOMIC_ACQUIRE) != seq)
+        return fail(FT_EHIP, "decode: router finished without publishing its result");
+    }
+  }
   const double t1 = now_us();
   for (int i = 0; i < P; ++i)
     if (c->h_idx[i] < 0) return fail(FT_EINVAL, "decode: a token allows fewer than k experts");
@@ -438,7 +569,6 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
     c->cache->stats.h2d_bytes += (int64_t)q * (int64_t)c->S;
   }
   // GPU path: grouping, grouped FFN of H, then of F once filled
-  int32_t* d_key = c->wsp<int32_t>(c->cv.key);
   int32_t* d_gslot = c->wsp<int32_t>(c->cv.gslot);
   int32_t* d_off = c->wsp<int32_t>(c->cv.offsets);
   int32_t* d_perm = c->wsp<int32_t>(c->cv.perm);
@@ -453,31 +583,36 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
     for (int i = 0; i < P; ++i)
       if (p->pair_group[i] >= 0) max_rows = std::max(max_rows, ++cnt[p->pair_group[i]]);
   }
-  FT_HIP(hipMemcpyAsync(d_key, c->h_key, (size_t)P * 4, hipMemcpyHostToDevice, cs));
-  if (n_g > 0) FT_HIP(hipMemcpyAsync(d_gslot, c->h_gslot, (size_t)n_g * 4, hipMemcpyHostToDevice, cs));
-  if (int rc = ft::launch_permute(d_key, P, std::max(n_g, 1), d_off, d_perm, d_inv, c->ws + c->cv.pws,
-                                  c->cv.pws_bytes, cs))
+  // grouping reads the pair keys and group slots from pinned host memory
+  if (int rc = ft::launch_permute(c->h_key, P, std::max(n_g, 1), d_off, d_perm, d_inv, c->ws + c->cv.pws,
+                                  c->cv.pws_bytes, cs, c->h_gslot, d_gslot, n_g))
     return rc;
   const uint16_t* xs = static_cast<const uint16_t*>(x);
+  int rows_of[FT_PLAN_CAP] = {0};
+  for (int i = 0; i < P; ++i)
+    if (p->pair_group[i] >= 0) rows_of[p->pair_group[i]] += 1;
+  auto ffn = [&](int g0, int g1) -> int {
+    ft_ctx::ProfRec* r = prof_begin(c);
+    if (r) prof_account(c, r, rows_of + g0, g1 - g0, 4);
+    return ft::launch_ffn_rows(xs, d, c->shape.d_ff, k, c->slots, d_gslot, d_off, d_perm, g0, g1, max_rows, d_h,
+                               d_out, cs, r ? reinterpret_cast<void* const*>(r->ev) : nullptr);
+  };
   if (n_h > 0)
-    if (int rc = ft::launch_ffn_rows(xs, d, c->shape.d_ff, k, c->slots, d_gslot, d_off, d_perm, 0, n_h, max_rows,
-                                     d_h, d_out, cs))
-      return rc;
+    if (int rc = ffn(0, n_h)) return rc;
   if (q > 0) {
     FT_HIP(hipStreamWaitEvent(cs, c->ev_fill, 0));
-    if (int rc = ft::launch_ffn_rows(xs, d, c->shape.d_ff, k, c->slots, d_gslot, d_off, d_perm, n_h, n_g, max_rows,
-                                     d_h, d_out, cs))
-      return rc;
+    if (int rc = ffn(n_h, n_g)) return rc;
   }
   // merge of the CPU partial, then the combine
+  const double t3 = now_us();
   const float* cpu_part = nullptr;
-  double t_cpu = 0.0;
+  double t_cpu = 0.0, t_cpu_work = 0.0;
   if (n_c > 0) {
     ft::cpu_pool_wait(c->cpu);
     t_cpu = now_us() - t2;
-    float* d_cpu = c->wsp<float>(c->cv.cpu);
-    FT_HIP(hipMemcpyAsync(d_cpu, c->h_partial, (size_t)T * d * 4, hipMemcpyHostToDevice, cs));
-    cpu_part = d_cpu;
+    t_cpu_work = ft::cpu_pool_last_work_us(c->cpu);
+    if (st) st->cpu_caller_items = ft::cpu_pool_last_caller_items(c->cpu);
+    cpu_part = c->h_partial;  // the combine reads the host partial from pinned memory
   }
   if (int rc = ft::launch_combine(d_out, d_inv, d_gates, cpu_part, T, k, d, y, cs)) return rc;
   FT_HIP(hipEventRecord(c->ev_done, cs));
@@ -489,11 +624,14 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
     st->misses = p->n_m;
     st->q = q;
     st->n_c = n_c;
+    if (n_c == 0) st->cpu_caller_items = 0;
     st->h2d_bytes = (int64_t)q * (int64_t)c->S;
     st->t_route_us = t1 - t0;
     st->t_ctrl_us = t2 - t1;
     st->t_cpu_us = t_cpu;
     st->t_total_us = now_us() - t0;
+    st->t_issue_us = t3 - t2;
+    st->t_cpu_work_us = t_cpu_work;
   }
   return FT_OK;
 }
@@ -565,14 +703,29 @@ int ft_moe_prefill_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, co
   if (int rc = ft::launch_permute(d_idx, P, E, d_off, d_perm, d_inv, c->ws + c->cv.pws, c->cv.pws_bytes, cs))
     return rc;
   const uint16_t* xs = static_cast<const uint16_t*>(x);
-  if (d % 128 == 0 && d_ff % 64 == 0) {
+  const bool mfma = d % 128 == 0 && d_ff % 64 == 0;
+  ft_ctx::ProfRec* r = prof_begin(c);
+  void* const* evs = r ? reinterpret_cast<void* const*>(r->ev) : nullptr;
+  if (mfma) {
     if (int rc = ft::launch_ffn_mfma(xs, d, d_ff, k, c->slots, d_buf, d_off, d_perm, 0, E, T,
-                                     c->wsp<uint16_t>(c->cv.h), c->wsp<float>(c->cv.out), cs))
+                                     c->wsp<uint16_t>(c->cv.h), c->wsp<float>(c->cv.out), cs, evs))
       return rc;
   } else {
     if (int rc = ft::launch_ffn_rows(xs, d, d_ff, k, c->slots, d_buf, d_off, d_perm, 0, E, 8,
-                                     c->wsp<float>(c->cv.h), c->wsp<float>(c->cv.out), cs))
+                                     c->wsp<float>(c->cv.h), c->wsp<float>(c->cv.out), cs, evs))
       return rc;
+  }
+  if (r) {
+    // rows per group are known on the device only: keep a copy for ft_profile_read
+    if (!c->off_free.empty()) {
+      r->offsets = c->off_free.back();
+      c->off_free.pop_back();
+    } else if (hipHostMalloc((void**)&r->offsets, (size_t)(E + 1) * 4) != hipSuccess) {
+      r->offsets = nullptr;
+    }
+    r->n_groups = E;
+    r->hb = mfma ? 2 : 4;
+    if (r->offsets) FT_HIP(hipMemcpyAsync(r->offsets, d_off, (size_t)(E + 1) * 4, hipMemcpyDeviceToHost, cs));
   }
   if (int rc = ft::launch_combine(c->wsp<float>(c->cv.out), d_inv, d_gates, nullptr, T, k, d, y, cs)) return rc;
   FT_HIP(hipEventRecord(c->ev_pf_comp[b], cs));
@@ -595,6 +748,51 @@ int ft_moe_prefill_end(ft_ctx_t c) {
   // the last two layers processed stay resident (all L layers in a full prefill)
   c->cache->prefill_end(c->dev ? std::max(c->prefill_next, 0) : c->shape.L);
   c->prefill_next = -1;
+  return FT_OK;
+}
+
+// ---- kernel timing -----------------------------------------------------------------
+
+int ft_profile_enable(ft_ctx_t c, int32_t on) {
+  if (!c) return fail(FT_EINVAL, "profile_enable: null");
+  if (c->dev) {
+    FT_HIP(hipSetDevice(c->device));
+    for (auto& r : c->prof) {
+      for (hipEvent_t e : r.ev) {
+        (void)hipEventSynchronize(e);
+        c->ev_free.push_back(e);
+      }
+      if (r.offsets) c->off_free.push_back(r.offsets);
+    }
+  }
+  c->prof.clear();
+  c->prof_on = on != 0 && c->dev;
+  return FT_OK;
+}
+
+int ft_profile_read(ft_ctx_t c, ft_profile* out) {
+  if (!c || !out) return fail(FT_EINVAL, "profile_read: null");
+  *out = ft_profile{};
+  if (!c->dev) return FT_OK;
+  FT_HIP(hipSetDevice(c->device));
+  for (auto& r : c->prof) {
+    FT_HIP(hipEventSynchronize(r.ev[3]));
+    float a = 0.f, b = 0.f;
+    FT_HIP(hipEventElapsedTime(&a, r.ev[0], r.ev[1]));  // gate/up kernel, start to stop
+    FT_HIP(hipEventElapsedTime(&b, r.ev[2], r.ev[3]));  // down kernel, start to stop
+    if (r.offsets) {
+      std::vector<int> rows(r.n_groups);
+      for (int g = 0; g < r.n_groups; ++g) rows[g] = r.offsets[g + 1] - r.offsets[g];
+      prof_account(c, &r, rows.data(), r.n_groups, r.hb);
+    }
+    out->launches += 1;
+    out->ms_gateup += a;
+    out->ms_down += b;
+    out->bytes_gateup += r.bytes_up;
+    out->bytes_down += r.bytes_dn;
+    out->flops_gateup += r.flops_up;
+    out->flops_down += r.flops_dn;
+  }
   return FT_OK;
 }
 

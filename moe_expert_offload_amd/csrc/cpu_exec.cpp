@@ -18,6 +18,7 @@
 #include <sched.h>
 
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <condition_variable>
 #include <cstring>
@@ -126,15 +127,19 @@ class CpuPool {
     if (sched_getaffinity(0, sizeof(mask), &mask) == 0)
       for (int c = 0; c < CPU_SETSIZE; ++c)
         if (CPU_ISSET(c, &mask)) cpus.push_back(c);
-    if (threads <= 0) threads = cpus.empty() ? (int)std::thread::hardware_concurrency() : (int)cpus.size();
-    if (threads <= 0) threads = 1;
+    // By default one worker per CPU of the affinity mask except the first two,
+    // which are left to the calling thread (it also works while it waits) and to
+    // the HIP runtime; each worker is pinned to its own CPU.
+    const int ncpu = cpus.empty() ? (int)std::thread::hardware_concurrency() : (int)cpus.size();
+    const int reserved = ncpu > 4 ? 2 : (ncpu > 1 ? 1 : 0);
+    if (threads <= 0) threads = std::max(1, ncpu - reserved);
     nthreads_ = threads;
     for (int i = 0; i < threads; ++i) {
-      workers_.emplace_back([this, i] { run(i); });
-      if (!cpus.empty()) {
+      workers_.emplace_back([this] { run(); });
+      if ((int)cpus.size() > reserved) {
         cpu_set_t one;
         CPU_ZERO(&one);
-        CPU_SET(cpus[i % cpus.size()], &one);
+        CPU_SET(cpus[reserved + (i % (cpus.size() - reserved))], &one);
         pthread_setaffinity_np(workers_.back().native_handle(), sizeof(one), &one);
       }
     }
@@ -151,6 +156,8 @@ class CpuPool {
   }
 
   int threads() const { return nthreads_; }
+  double last_work_us() const { return t_done_us_; }
+  int last_caller_items() const { return caller_items_; }
 
   void submit(const uint16_t* x, int T, int d, int d_ff, const CpuExpert* ex, int n_exp,
               float* partial) {
@@ -172,24 +179,71 @@ class CpuPool {
     blocks1_ = (d_ff + RB1 - 1) / RB1;
     items1_ = n_exp * blocks1_;
     items2_ = (d + RB2 - 1) / RB2;
-    next1_.store(0, std::memory_order_relaxed);
-    next2_.store(0, std::memory_order_relaxed);
-    arrived_.store(0, std::memory_order_relaxed);
-    finished_.store(0, std::memory_order_relaxed);
+    // publish: the job fields above happen-before any item grab of this generation
+    const uint64_t g = (gen_.load(std::memory_order_relaxed) + 1) & 0xffffffffu;
+    cur_ = g;
+    done1_.store(0, std::memory_order_relaxed);
+    done2_.store(0, std::memory_order_relaxed);
+    t_submit_ = std::chrono::steady_clock::now();
+    next1_.store(g << 32, std::memory_order_release);
+    next2_.store(g << 32, std::memory_order_release);
     {
       std::lock_guard<std::mutex> lk(mu_);
-      gen_.fetch_add(1, std::memory_order_release);
+      gen_.store(g, std::memory_order_release);
     }
     cv_.notify_all();
   }
 
+  // The caller works on the current call too, then waits for every item to finish.
   void wait() {
-    while (finished_.load(std::memory_order_acquire) < nthreads_) _mm_pause();
+    caller_items_ = work(cur_);
+    for (int spins = 0; done2_.load(std::memory_order_acquire) < items2_; ++spins) {
+      if (spins < 4096)
+        _mm_pause();
+      else
+        std::this_thread::yield();
+    }
   }
 
  private:
+  static constexpr int kSpinUs = 20000;
   static constexpr int RB1 = 16;  // W_gate/W_up rows per phase-1 item
   static constexpr int RB2 = 32;  // output rows per phase-2 item
+
+  // Takes the next item of generation g from a tagged counter (gen << 32 | index);
+  // -1 when the counter belongs to another call or is exhausted.
+  static int grab(std::atomic<uint64_t>& next, uint64_t g, int items) {
+    uint64_t v = next.load(std::memory_order_acquire);
+    for (;;) {
+      if ((v >> 32) != g) return -1;
+      const int i = (int)(v & 0xffffffffu);
+      if (i >= items) return -1;
+      if (next.compare_exchange_weak(v, v + 1, std::memory_order_acq_rel, std::memory_order_acquire)) return i;
+    }
+  }
+
+  // Phase 1 items, then (once all phase-1 items of this call are done) phase 2
+  // items.  A thread that is descheduled while holding no item delays nothing.
+  int work(uint64_t g) {
+    int n = 0;
+    for (int it; (it = grab(next1_, g, items1_)) >= 0; ++n) {
+      phase1(it);
+      done1_.fetch_add(1, std::memory_order_acq_rel);
+    }
+    for (int spins = 0; done1_.load(std::memory_order_acquire) < items1_; ++spins) {
+      if ((next1_.load(std::memory_order_acquire) >> 32) != g) return n;  // call already over
+      if (spins < 4096)
+        _mm_pause();
+      else
+        std::this_thread::yield();
+    }
+    for (int it; (it = grab(next2_, g, items2_)) >= 0; ++n) {
+      phase2(it);
+      if (done2_.fetch_add(1, std::memory_order_acq_rel) == items2_ - 1)
+        t_done_us_ = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t_submit_).count();
+    }
+    return n;
+  }
 
   void phase1(int item) {
     const int e = item / blocks1_;
@@ -231,26 +285,23 @@ class CpuPool {
     }
   }
 
-  void run(int /*id*/) {
+  void run() {
     uint64_t seen = 0;
     for (;;) {
-      // spin briefly for the next call, then sleep
-      int spins = 0;
-      while (gen_.load(std::memory_order_acquire) == seen && spins < 20000) {
+      // spin for the next call for up to kSpinUs, then sleep: decode calls with a
+      // CPU set arrive a few layers apart and waking a sleeping pool is slow
+      const auto spin_end = std::chrono::steady_clock::now() + std::chrono::microseconds(kSpinUs);
+      for (int i = 0; gen_.load(std::memory_order_acquire) == seen; ++i) {
         _mm_pause();
-        ++spins;
+        if ((i & 255) == 255 && std::chrono::steady_clock::now() > spin_end) break;
       }
       if (gen_.load(std::memory_order_acquire) == seen) {
         std::unique_lock<std::mutex> lk(mu_);
-        cv_.wait(lk, [&] { return gen_.load(std::memory_order_acquire) != seen; });
+        cv_.wait(lk, [&] { return gen_.load(std::memory_order_acquire) != seen || stop_; });
       }
       seen = gen_.load(std::memory_order_acquire);
       if (stop_) return;
-      for (int it; (it = next1_.fetch_add(1, std::memory_order_relaxed)) < items1_;) phase1(it);
-      arrived_.fetch_add(1, std::memory_order_acq_rel);
-      while (arrived_.load(std::memory_order_acquire) < nthreads_) _mm_pause();
-      for (int it; (it = next2_.fetch_add(1, std::memory_order_relaxed)) < items2_;) phase2(it);
-      finished_.fetch_add(1, std::memory_order_acq_rel);
+      work(seen);
     }
   }
 
@@ -259,7 +310,8 @@ class CpuPool {
   std::mutex mu_;
   std::condition_variable cv_;
   std::atomic<uint64_t> gen_{0};
-  bool stop_ = false;
+  uint64_t cur_ = 0;
+  std::atomic<bool> stop_{false};
 
   int T_ = 0, d_ = 0, d_ff_ = 0, n_exp_ = 0;
   const CpuExpert* ex_ = nullptr;
@@ -267,7 +319,11 @@ class CpuPool {
   std::vector<float> xf_, h_;
   std::vector<int> use_base_;
   int blocks1_ = 0, items1_ = 0, items2_ = 0;
-  std::atomic<int> next1_{0}, next2_{0}, arrived_{0}, finished_{0};
+  std::atomic<uint64_t> next1_{0}, next2_{0};
+  std::atomic<int> done1_{0}, done2_{0};
+  std::chrono::steady_clock::time_point t_submit_{};
+  double t_done_us_ = 0.0;
+  int caller_items_ = 0;
 };
 
 CpuPool* cpu_pool_create(int threads) { return new CpuPool(threads); }
@@ -278,6 +334,8 @@ void cpu_pool_submit(CpuPool* p, const uint16_t* x, int T, int d, int d_ff, cons
   p->submit(x, T, d, d_ff, ex, n_exp, partial);
 }
 void cpu_pool_wait(CpuPool* p) { p->wait(); }
+double cpu_pool_last_work_us(const CpuPool* p) { return p->last_work_us(); }
+int cpu_pool_last_caller_items(const CpuPool* p) { return p->last_caller_items(); }
 const char* cpu_simd_name() {
   std::call_once(g_simd_once, [] { g_row_dots = pick_row_dots(&g_simd_name); });
   return g_simd_name;

@@ -19,19 +19,33 @@ int fail(int status, const std::string& msg);
 int launch_router(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, int T, int d,
                   int E, int k, int32_t* idx, float* gates, float* logits_ws, void* stream);
 
+// Decode router in one launch (T <= 64): also publishes idx, gates and x to
+// pinned host memory (pub_* may be null), then writes seq to *pub_flag; ticket
+// is a zeroed device counter.
+int launch_router_decode(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, int T, int d,
+                         int E, int k, float* logits_ws, int32_t* idx, float* gates,
+                         unsigned int* ticket, int32_t* pub_idx, float* pub_gates, uint16_t* pub_x,
+                         uint32_t* pub_flag, uint32_t seq, void* stream);
+
 size_t permute_ws_bytes(int P, int n_groups);
+// For P <= 1024 one block does everything and ws is not used; key may then live
+// in pinned host memory.  Optionally copies n_gslot group slots gslot_src -> gslot_dst.
 int launch_permute(const int32_t* key, int P, int n_groups, int32_t* offsets, int32_t* perm,
-                   int32_t* inv, void* ws, size_t ws_bytes, void* stream);
+                   int32_t* inv, void* ws, size_t ws_bytes, void* stream,
+                   const int32_t* gslot_src = nullptr, int32_t* gslot_dst = nullptr, int n_gslot = 0);
 
 // Row-streaming (GEMV-like) grouped FFN: h fp32 [rows, d_ff], out fp32 [rows, d].
+// ev (nullable): four hipEvent_t, start/stop of the gate/up kernel then of the down kernel.
 int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
                     const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
-                    int g_begin, int g_end, int max_rows, float* h, float* out, void* stream);
+                    int g_begin, int g_end, int max_rows, float* h, float* out, void* stream,
+                    void* const* ev = nullptr);
 
 // MFMA tile grouped FFN: h bf16 [rows, d_ff] (in the fp32-sized workspace), out fp32 [rows, d].
 int launch_ffn_mfma(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
                     const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
-                    int g_begin, int g_end, int max_rows, uint16_t* h, float* out, void* stream);
+                    int g_begin, int g_end, int max_rows, uint16_t* h, float* out, void* stream,
+                    void* const* ev = nullptr);
 
 int launch_combine(const float* out, const int32_t* inv, const float* gates,
                    const float* cpu_partial, int T, int k, int d, float* y, void* stream);
@@ -57,8 +71,12 @@ int cpu_pool_threads(const CpuPool*);
 // overwritten (zeroed first).  Returns immediately.
 void cpu_pool_submit(CpuPool*, const uint16_t* x, int T, int d, int d_ff, const CpuExpert* ex,
                      int n_exp, float* partial);
-// Blocks until the submitted work is done.
+// Blocks until the submitted work is done (the caller works on it too).
 void cpu_pool_wait(CpuPool*);
+// Microseconds from the last submit to the completion of its last work item.
+double cpu_pool_last_work_us(const CpuPool*);
+// Work items the calling thread did itself in the last call.
+int cpu_pool_last_caller_items(const CpuPool*);
 const char* cpu_simd_name();
 
 }  // namespace ft

@@ -8,6 +8,7 @@
 //   ffn rows    grouped SwiGLU FFN, row-streaming form for few tokens/expert (decode, [FT] §3.2)
 //   ffn mfma    grouped SwiGLU FFN on bf16 MFMA tiles for many tokens/expert (prefill, [FT] §3.1)
 //   combine     gate-weighted sum in rank order + the host partial          ([FT] §3.2 exact merge)
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -140,28 +141,35 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
 }
 
-__device__ __forceinline__ bool ranks_before(float va, int ea, float vb, int eb) {
-  return va > vb || (va == vb && ea < eb);
+// Order-preserving 64-bit key of (logit, expert): larger key = ranks first
+// (logit descending, then index ascending).  -0.0 and +0.0 map to one key.
+__device__ __forceinline__ unsigned long long rank_key(float v, int e) {
+  uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (uint32_t)(0x7fffffff - e);
 }
 
-// One wavefront per token: k rounds of a (logit desc, index asc) arg-max over
-// the wave, each winner removed; then softmax over the k winners.
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
-                                                          const uint8_t* __restrict__ allowed,
-                                                          int T, int E, int k,
-                                                          int32_t* __restrict__ idx,
-                                                          float* __restrict__ gates) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  float v[16];
-  bool ok[16];
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const unsigned long long w = __shfl_xor(v, o, WAVE);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Top-k of one token by one wavefront: k rounds of a wave arg-max over the
+// allowed experts, each winner removed; softmax over the k winners.  Writes the
+// device outputs and, when given, copies to pinned host memory.
+__device__ void topk_token(const float* __restrict__ lg, const uint8_t* __restrict__ allowed, int E,
+                           int k, int lane, int32_t* __restrict__ idx, float* __restrict__ gates,
+                           int32_t* pub_idx, float* pub_gates) {
+  unsigned long long key[16];
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
     const int e = lane + 64 * s;
-    const bool in = e < E && (allowed == nullptr || allowed[(size_t)t * E + e] != 0);
-    ok[s] = in;
-    v[s] = in ? logits[(size_t)t * E + e] : 0.0f;
+    const bool in = e < E && (allowed == nullptr || allowed[e] != 0);
+    key[s] = in ? rank_key(lg[e], e) : 0ull;
   }
   float sv[8];
   int se[8];
@@ -170,31 +178,17 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     sv[r] = 0.0f;
     se[r] = -1;
     if (r < k) {
-      float bv = -INFINITY;
-      int be = INT_MAX;
+      unsigned long long b = 0ull;
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const int e = lane + 64 * s;
-        if (ok[s] && (be == INT_MAX || ranks_before(v[s], e, bv, be))) {
-          bv = v[s];
-          be = e;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, WAVE);
-        const int oe = __shfl_xor(be, o, WAVE);
-        if (oe != INT_MAX && (be == INT_MAX || ranks_before(ov, oe, bv, be))) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if (be != INT_MAX) {
+      for (int s = 0; s < 16; ++s) b = key[s] > b ? key[s] : b;
+      b = wave_max_u64(b);
+      if (b != 0ull) {
+        const int e = 0x7fffffff - (int)(uint32_t)(b & 0xffffffffu);
 #pragma unroll
         for (int s = 0; s < 16; ++s)
-          if (lane + 64 * s == be) ok[s] = false;
-        sv[r] = bv;
-        se[r] = be;
+          if (lane + 64 * s == e) key[s] = 0ull;
+        se[r] = e;
+        sv[r] = lg[e];
       }
     }
   }
@@ -208,9 +202,102 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 #pragma unroll
     for (int r = 0; r < 8; ++r)
       if (r < k) {
-        idx[(size_t)t * k + r] = se[r];
-        gates[(size_t)t * k + r] = se[r] >= 0 ? z[r] / sum : 0.0f;
+        const float g = se[r] >= 0 ? z[r] / sum : 0.0f;
+        idx[r] = se[r];
+        gates[r] = g;
+        if (pub_idx) {
+          pub_idx[r] = se[r];
+          pub_gates[r] = g;
+        }
       }
+  }
+}
+
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
+                                                          const uint8_t* __restrict__ allowed,
+                                                          int T, int E, int k,
+                                                          int32_t* __restrict__ idx,
+                                                          float* __restrict__ gates) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_token(logits + (size_t)t * E, allowed ? allowed + (size_t)t * E : nullptr, E, k, lane,
+             idx + (size_t)t * k, gates + (size_t)t * k, nullptr, nullptr);
+}
+
+// Decode router in one launch: blocks compute logits (one token x 16 experts
+// each) and the blocks with blockIdx.y == 0 copy their token's x row to pinned
+// host memory; the last block to finish (device-scope fence + ticket counter,
+// no waiting) does the top-k of every token and publishes ids and gates to
+// pinned host memory.  `ticket` is a zeroed device counter, reset by the last
+// block.
+__global__ __launch_bounds__(256) void router_decode_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint8_t* __restrict__ allowed,
+    int T, int d, int E, int k, float* __restrict__ logits, int32_t* __restrict__ idx,
+    float* __restrict__ gates, unsigned int* __restrict__ ticket, int32_t* pub_idx, float* pub_gates,
+    uint16_t* pub_x, uint32_t* pub_flag, uint32_t seq) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x;
+  const int e0 = (blockIdx.y * 4 + wave) * 4;
+  if (e0 < E) {
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int J = (d + 511) >> 9;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < J; ++j) {
+      const int i0 = j * 512 + lane * 8;
+      const bool in = i0 < d;
+      const uint4 xv = in ? ld16(x + (size_t)t * d + i0) : zero;
+      uint4 wv[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) wv[b] = (in && e0 + b < E) ? ld16(w + (size_t)(e0 + b) * d + i0) : zero;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const uint32_t xw = (r >> 1) == 0 ? xv.x : (r >> 1) == 1 ? xv.y : (r >> 1) == 2 ? xv.z : xv.w;
+        const float xf = (r & 1) ? bf_hi(xw) : bf_lo(xw);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint32_t ww = (r >> 1) == 0 ? wv[b].x : (r >> 1) == 1 ? wv[b].y : (r >> 1) == 2 ? wv[b].z : wv[b].w;
+          const float wf = (r & 1) ? bf_hi(ww) : bf_lo(ww);
+          acc[b] = acc[b] + xf * wf;  // same order as router_logits_kernel
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float v = acc[b];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v = v + __shfl_xor(v, o, WAVE);
+      acc[b] = v;
+    }
+    if (lane == 0)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (e0 + b < E) logits[(size_t)t * E + e0 + b] = acc[b];
+  }
+  if (blockIdx.y == 0 && pub_x != nullptr)
+    for (int i = threadIdx.x * 8; i < d; i += 256 * 8)
+      *reinterpret_cast<uint4*>(pub_x + (size_t)t * d + i) = ld16(x + (size_t)t * d + i);
+  __threadfence();
+  __shared__ int last;
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(ticket, 1u) == gridDim.x * gridDim.y - 1;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  for (int tt = wave; tt < T; tt += 4)
+    topk_token(logits + (size_t)tt * E, allowed ? allowed + (size_t)tt * E : nullptr, E, k, lane,
+               idx + (size_t)tt * k, gates + (size_t)tt * k, pub_idx ? pub_idx + (size_t)tt * k : nullptr,
+               pub_gates ? pub_gates + (size_t)tt * k : nullptr);
+  __threadfence_system();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    *ticket = 0u;
+    if (pub_flag != nullptr) {
+      // every published value is visible before the host sees the sequence number
+      __threadfence_system();
+      *reinterpret_cast<volatile uint32_t*>(pub_flag) = seq;
+    }
   }
 }
 
@@ -218,6 +305,35 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 // Permutation: stable counting sort of pair ids by group key
 // ============================================================================
 constexpr int PB = 256;
+
+// Exclusive prefix sum of v over the 1024 threads of a block; returns the
+// exclusive value of this thread and writes the block total to *total.
+__device__ int block_exclusive_scan_1024(int v, int* total) {
+  __shared__ int wsum[16];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o, WAVE);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) wsum[wv] = inc;
+  __syncthreads();
+  if (wv == 0) {
+    int s = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int u = __shfl_up(s, o, WAVE);
+      if (lane >= o) s += u;
+    }
+    if (lane < 16) wsum[lane] = s;  // inclusive per-wave totals
+  }
+  __syncthreads();
+  const int base = wv > 0 ? wsum[wv - 1] : 0;
+  *total = wsum[15];
+  __syncthreads();
+  return base + inc - v;
+}
 
 __global__ __launch_bounds__(PB) void perm_count_kernel(const int32_t* __restrict__ key, int P, int G,
                                                         int32_t* __restrict__ counts) {
@@ -233,37 +349,26 @@ __global__ __launch_bounds__(PB) void perm_count_kernel(const int32_t* __restric
   for (int i = threadIdx.x; i < G; i += PB) counts[(size_t)blockIdx.x * G + i] = hist[i];
 }
 
-// One block: per-group running bases over blocks, then the exclusive scan of the
-// group totals; counts[b][g] becomes the absolute first position of block b's
-// pairs of group g.
+// One block of 1024 threads (G <= 1024): per-group running bases over blocks,
+// then the exclusive scan of the group totals; counts[b][g] becomes the absolute
+// first position of block b's pairs of group g.
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int nblk, int G, int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets) {
-  __shared__ int32_t total[1025];
-  for (int g = threadIdx.x; g < G; g += 1024) {
-    int run = 0;
+  const int g = threadIdx.x;
+  int run = 0;
+  if (g < G)
     for (int b = 0; b < nblk; ++b) {
       const int c = counts[(size_t)b * G + g];
       counts[(size_t)b * G + g] = run;
       run += c;
     }
-    total[g] = run;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int g = 0; g < G; ++g) {
-      const int c = total[g];
-      total[g] = run;
-      run += c;
-    }
-    total[G] = run;
-  }
-  __syncthreads();
-  for (int g = threadIdx.x; g <= G; g += 1024) offsets[g] = total[g];
-  for (int g = threadIdx.x; g < G; g += 1024) {
-    const int base = total[g];
+  int total;
+  const int base = block_exclusive_scan_1024(g < G ? run : 0, &total);
+  if (g < G) {
+    offsets[g] = base;
     for (int b = 0; b < nblk; ++b) counts[(size_t)b * G + g] += base;
   }
+  if (g == 0) offsets[G] = total;
 }
 
 __global__ __launch_bounds__(PB) void perm_scatter_kernel(const int32_t* __restrict__ key, int P, int G,
@@ -286,6 +391,47 @@ __global__ __launch_bounds__(PB) void perm_scatter_kernel(const int32_t* __restr
   const int pos = base[(size_t)blockIdx.x * G + g] + rank;
   perm[pos] = p;
   inv[p] = pos;
+}
+
+// All of the grouping in one block for P <= 1024 and G <= 1024 (decode).  key
+// and gslot_src may live in pinned host memory; gslot_src (n_gslot entries) is
+// copied to gslot_dst on the device for the FFN kernels.
+__global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* key, int P, int G,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ perm,
+                                                          int32_t* __restrict__ inv,
+                                                          const int32_t* gslot_src,
+                                                          int32_t* __restrict__ gslot_dst, int n_gslot) {
+  __shared__ int32_t cnt[1024];
+  __shared__ int32_t ks[1024];
+  const int tid = threadIdx.x;
+  cnt[tid] = 0;
+  int g = tid < P ? key[tid] : -1;
+  if (g >= G) g = -1;
+  ks[tid] = g;
+  if (gslot_src != nullptr && tid < n_gslot) gslot_dst[tid] = gslot_src[tid];
+  __syncthreads();
+  if (g >= 0) atomicAdd(&cnt[g], 1);
+  __syncthreads();
+  int total;
+  const int base = block_exclusive_scan_1024(tid < G ? cnt[tid] : 0, &total);
+  if (tid < G) {
+    offsets[tid] = base;
+    cnt[tid] = base;
+  }
+  if (tid == 0) offsets[G] = total;
+  __syncthreads();
+  if (tid < P) {
+    if (g < 0) {
+      inv[tid] = -1;
+    } else {
+      int rank = 0;
+      for (int q = 0; q < tid; ++q) rank += (ks[q] == g);
+      const int pos = cnt[g] + rank;
+      perm[pos] = tid;
+      inv[tid] = pos;
+    }
+  }
 }
 
 // ============================================================================
@@ -678,34 +824,68 @@ int launch_router(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, 
   return launched("router_topk");
 }
 
+int launch_router_decode(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, int T, int d,
+                         int E, int k, float* logits_ws, int32_t* idx, float* gates,
+                         unsigned int* ticket, int32_t* pub_idx, float* pub_gates, uint16_t* pub_x,
+                         uint32_t* pub_flag, uint32_t seq, void* stream) {
+  if (T < 1 || T > 64 || d <= 0 || d % 8 != 0 || E <= 0 || E > 1024 || k < 1 || k > 8 || k > E)
+    return fail(FT_EINVAL, "router: need T<=64, d%8==0, 1<=k<=min(E,8), E<=1024");
+  if (!aligned16(x) || !aligned16(w) || (pub_x && !aligned16(pub_x)))
+    return fail(FT_EINVAL, "router: unaligned pointer");
+  dim3 grid(T, (E + 15) / 16);
+  router_decode_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      x, w, allowed, T, d, E, k, logits_ws, idx, gates, ticket, pub_idx, pub_gates, pub_x, pub_flag, seq);
+  return launched("router_decode");
+}
+
 size_t permute_ws_bytes(int P, int n_groups) {
   const size_t nblk = (size_t)((P + PB - 1) / PB);
   return (nblk > 0 ? nblk : 1) * (size_t)(n_groups > 0 ? n_groups : 1) * sizeof(int32_t);
 }
 
 int launch_permute(const int32_t* key, int P, int n_groups, int32_t* offsets, int32_t* perm,
-                   int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
+                   int32_t* inv, void* ws, size_t ws_bytes, void* stream, const int32_t* gslot_src,
+                   int32_t* gslot_dst, int n_gslot) {
   if (P < 0 || n_groups < 1 || n_groups > 1024) return fail(FT_EINVAL, "permute: need 1<=n_groups<=1024");
-  if (ws_bytes < permute_ws_bytes(P, n_groups)) return fail(FT_ENOMEM, "permute: workspace too small");
+  if (n_gslot < 0 || n_gslot > 1024 || (n_gslot > 0 && (!gslot_src || !gslot_dst)))
+    return fail(FT_EINVAL, "permute: bad group-slot copy");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (P <= 1024) {
+    perm_small_kernel<<<1, 1024, 0, s>>>(key, P, n_groups, offsets, perm, inv, n_gslot > 0 ? gslot_src : nullptr,
+                                         gslot_dst, n_gslot);
+    return launched("perm_small");
+  }
+  if (ws_bytes < permute_ws_bytes(P, n_groups)) return fail(FT_ENOMEM, "permute: workspace too small");
+  if (n_gslot > 0) {
+    if (hipMemcpyAsync(gslot_dst, gslot_src, (size_t)n_gslot * 4, hipMemcpyDefault, s) != hipSuccess)
+      return fail(FT_EHIP, "permute: group-slot copy failed");
+  }
   const int nblk = (P + PB - 1) / PB;
   int32_t* counts = static_cast<int32_t*>(ws);
-  if (nblk > 0) {
-    perm_count_kernel<<<nblk, PB, n_groups * sizeof(int32_t), s>>>(key, P, n_groups, counts);
-    if (int rc = launched("perm_count")) return rc;
-  }
+  perm_count_kernel<<<nblk, PB, n_groups * sizeof(int32_t), s>>>(key, P, n_groups, counts);
+  if (int rc = launched("perm_count")) return rc;
   perm_scan_kernel<<<1, 1024, 0, s>>>(nblk, n_groups, counts, offsets);
   if (int rc = launched("perm_scan")) return rc;
-  if (nblk > 0) {
-    perm_scatter_kernel<<<nblk, PB, 0, s>>>(key, P, n_groups, counts, perm, inv);
-    if (int rc = launched("perm_scatter")) return rc;
+  perm_scatter_kernel<<<nblk, PB, 0, s>>>(key, P, n_groups, counts, perm, inv);
+  return launched("perm_scatter");
+}
+
+// Launches a kernel; with timing events, start/stop bracket the kernel itself.
+template <typename... KArgs, typename... Args>
+inline void timed_launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t s, void* const* ev,
+                         int which, Args... args) {
+  if (ev) {
+    hipExtLaunchKernelGGL(kern, grid, block, 0, s, static_cast<hipEvent_t>(ev[2 * which]),
+                          static_cast<hipEvent_t>(ev[2 * which + 1]), 0, args...);
+  } else {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, args...);
   }
-  return FT_OK;
 }
 
 int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
                     const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
-                    int g_begin, int g_end, int max_rows, float* h, float* out, void* stream) {
+                    int g_begin, int g_end, int max_rows, float* h, float* out, void* stream,
+                    void* const* ev) {
   if (d <= 0 || d_ff <= 0 || d % 8 || d_ff % 8 || k < 1) return fail(FT_EINVAL, "ffn_rows: bad shape");
   const int ng = g_end - g_begin;
   if (ng <= 0) return FT_OK;
@@ -717,12 +897,11 @@ int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
   const int bpg_dn = (d + 3) / 4;
   const int nt = max_rows <= 1 ? 1 : max_rows <= 2 ? 2 : max_rows <= 4 ? 4 : 8;
 #define FT_ROWS_LAUNCH(NT)                                                                        \
-  ffn_gateup_rows_kernel<NT><<<ng * bpg_up, 256, 0, s>>>(x, d, d_ff, k, slots, rec_elems,        \
-                                                         group_slot, offsets, perm, g_begin,     \
-                                                         bpg_up, h);                             \
-  if (int rc = launched("ffn_gateup_rows")) return rc;                                          \
-  ffn_down_rows_kernel<NT><<<ng * bpg_dn, 256, 0, s>>>(d, d_ff, slots, rec_elems, group_slot,    \
-                                                       offsets, g_begin, bpg_dn, h, out);        \
+  timed_launch(ffn_gateup_rows_kernel<NT>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
+               slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h);                   \
+  if (int rc = launched("ffn_gateup_rows")) return rc;                                            \
+  timed_launch(ffn_down_rows_kernel<NT>, dim3(ng * bpg_dn), dim3(256), s, ev, 1, d, d_ff, slots,   \
+               rec_elems, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out);             \
   return launched("ffn_down_rows");
   switch (nt) {
     case 1: { FT_ROWS_LAUNCH(1) }
@@ -736,7 +915,7 @@ int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
 int launch_ffn_mfma(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
                     const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
                     int g_begin, int g_end, int /*max_rows*/, uint16_t* h, float* out,
-                    void* stream) {
+                    void* stream, void* const* ev) {
   if (d % 128 != 0 || d_ff % 64 != 0 || k < 1)
     return fail(FT_EINVAL, "ffn_mfma: need d%128==0 and d_ff%64==0");
   const int ng = g_end - g_begin;
@@ -747,13 +926,13 @@ int launch_ffn_mfma(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
   const size_t rec_elems = (size_t)3 * d * d_ff;
   const int tiles_up = d_ff / 64;
   const int nb_up = ng * tiles_up;
-  ffn_gateup_mfma_kernel<<<nb_up, 512, 0, s>>>(x, d, d_ff, k, slots, rec_elems, group_slot, offsets,
-                                               perm, g_begin, tiles_up, nb_up, h);
+  timed_launch(ffn_gateup_mfma_kernel, dim3(nb_up), dim3(512), s, ev, 0, x, d, d_ff, k, slots, rec_elems,
+               group_slot, offsets, perm, g_begin, tiles_up, nb_up, h);
   if (int rc = launched("ffn_gateup_mfma")) return rc;
   const int tiles_dn = d / 128;
   const int nb_dn = ng * tiles_dn;
-  ffn_down_mfma_kernel<<<nb_dn, 512, 0, s>>>(d, d_ff, slots, rec_elems, group_slot, offsets, g_begin,
-                                             tiles_dn, nb_dn, h, out);
+  timed_launch(ffn_down_mfma_kernel, dim3(nb_dn), dim3(512), s, ev, 1, d, d_ff, slots, rec_elems, group_slot,
+               offsets, g_begin, tiles_dn, nb_dn, (const uint16_t*)h, out);
   return launched("ffn_down_mfma");
 }
 

@@ -34,7 +34,7 @@ EXPORTED = [
     "ft_permute_workspace_bytes", "ft_permute", "ft_grouped_ffn", "ft_combine",
     "ft_expert_cache_lookup", "ft_expert_cache_fill", "ft_expert_cache_resize",
     "ft_expert_cache_where", "ft_moe_decode_layer", "ft_moe_prefill_begin", "ft_moe_prefill_layer",
-    "ft_moe_prefill_end", "ft_prefill_slot",
+    "ft_moe_prefill_end", "ft_prefill_slot", "ft_profile_enable", "ft_profile_read", "ft_host_experts",
 ]
 
 
@@ -61,15 +61,22 @@ class ft_plan(C.Structure):
 
 class ft_step_stats(C.Structure):
     _fields_ = [("layer", C.c_int32), ("T", C.c_int32), ("n_u", C.c_int32), ("hits", C.c_int32),
-                ("misses", C.c_int32), ("q", C.c_int32), ("n_c", C.c_int32), ("reserved", C.c_int32),
+                ("misses", C.c_int32), ("q", C.c_int32), ("n_c", C.c_int32), ("cpu_caller_items", C.c_int32),
                 ("h2d_bytes", C.c_int64), ("t_route_us", C.c_double), ("t_ctrl_us", C.c_double),
-                ("t_cpu_us", C.c_double), ("t_total_us", C.c_double)]
+                ("t_cpu_us", C.c_double), ("t_total_us", C.c_double), ("t_issue_us", C.c_double),
+                ("t_cpu_work_us", C.c_double)]
 
 
 class ft_stats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("calls", "unique_hits", "unique_misses", "fills", "cpu_experts",
                                          "reads", "read_hits", "read_fills", "read_cpu", "h2d_bytes",
                                          "prefill_layers", "resizes")]
+
+
+class ft_profile(C.Structure):
+    _fields_ = [("launches", C.c_int64), ("ms_gateup", C.c_double), ("ms_down", C.c_double),
+                ("bytes_gateup", C.c_double), ("bytes_down", C.c_double), ("flops_gateup", C.c_double),
+                ("flops_down", C.c_double)]
 
 
 class FtError(RuntimeError):
@@ -120,6 +127,9 @@ def lib():
             "ft_moe_prefill_layer": (C.c_int, [P, I, P, I, P, P, P, P]),
             "ft_moe_prefill_end": (C.c_int, [P]),
             "ft_prefill_slot": (I, [P, I, I]),
+            "ft_profile_enable": (C.c_int, [P, I]),
+            "ft_profile_read": (C.c_int, [P, C.POINTER(ft_profile)]),
+            "ft_host_experts": (C.c_int, [P, I, I, I, C.POINTER(P), P, P, P, I, I, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -266,6 +276,13 @@ def ft_combine(out, inv, gates, cpu_partial, T, k, d, y, stream=None):
                                                  _ptr(y), _stream(stream)))
 
 
+def ft_host_experts(x, T, d, d_ff, records, use_off, use_t, use_g, n_exp, threads, partial):
+    """records: sequence of host addresses (or numpy arrays); other arrays numpy."""
+    recs = (P * max(n_exp, 1))(*[_ptr(r) for r in records])
+    return _check("ft_host_experts", lib().ft_host_experts(_ptr(x), T, d, d_ff, recs, _ptr(use_off), _ptr(use_t),
+                                                           _ptr(use_g), n_exp, threads, _ptr(partial)))
+
+
 def ft_expert_cache_lookup(ctx, layer, idx_host, T, plan=None):
     plan = ft_plan() if plan is None else plan
     _check("ft_expert_cache_lookup", lib().ft_expert_cache_lookup(ctx, layer, _ptr(idx_host), T, C.byref(plan)))
@@ -306,6 +323,16 @@ def ft_moe_prefill_end(ctx):
 
 def ft_prefill_slot(ctx, layer, expert):
     return lib().ft_prefill_slot(ctx, layer, expert)
+
+
+def ft_profile_enable(ctx, on=True):
+    return _check("ft_profile_enable", lib().ft_profile_enable(ctx, 1 if on else 0))
+
+
+def ft_profile_read(ctx):
+    p = ft_profile()
+    _check("ft_profile_read", lib().ft_profile_read(ctx, C.byref(p)))
+    return {n: getattr(p, n) for n, _ in ft_profile._fields_}
 
 
 def plan_dict(plan):

@@ -181,3 +181,30 @@ def allowed_mask(trace_row: np.ndarray, E: int) -> np.ndarray:
     m = np.zeros((B, E), dtype=np.uint8)
     m[np.arange(B)[:, None], trace_row.astype(np.int64)] = 1
     return m
+
+
+# ---- GPU-side generation for pools and activations too large for NumPy ---------
+# torch's CUDA generator, seeded per chunk; values N(0, std^2) rounded to bf16 by
+# torch's round-to-nearest-even conversion.  Used for the large workloads, where
+# the oracle reads the same host memory afterwards.
+
+def fill_records_torch(view, config_id: int, seed: int = 0, std: float = 0.02, chunk_rows: int = 16):
+    """Fills a uint16 [rows, record_elems] host array (pinned or not) with N(0, std^2) bf16."""
+    import torch
+    rows, n = view.shape
+    host_t = torch.from_numpy(view.reshape(-1).view(np.int16))
+    g = torch.Generator(device="cuda")
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        g.manual_seed(((seed * 1_000_003 + config_id) * 1_000_003 + r0) & 0x7FFFFFFFFFFFFFFF)
+        w = torch.randn((r1 - r0) * n, generator=g, device="cuda", dtype=torch.float32).mul_(std)
+        host_t[r0 * n:r1 * n].copy_(w.to(torch.bfloat16).view(torch.int16))
+    torch.cuda.synchronize()
+
+
+def tokens_torch(config_id: int, chunk: int, layer: int, T: int, d: int, seed: int = 0):
+    """Layer input on the GPU: bf16 bits as an int16 CUDA tensor [T, d], values N(0, 1)."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(((seed * 1_000_003 + config_id * 7919 + chunk) * 1_000_003 + layer) & 0x7FFFFFFFFFFFFFFF)
+    return torch.randn((T, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16).view(torch.int16)

@@ -5,12 +5,11 @@ from the oracle only.
 """
 from __future__ import annotations
 
-import ctypes as C
-
 import numpy as np
 
 from moe_expert_offload_amd import ft
-from moe_expert_offload_amd.synth import Shape
+from moe_expert_offload_amd.pool import HostPool
+from moe_expert_offload_amd.synth import Shape, fill_records_torch
 
 
 def torch_mod():
@@ -33,37 +32,15 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
-class PinnedPool:
-    """A pinned host pool of expert records from ft_pool_alloc, viewed as uint16 [rows, record_elems]."""
+class PinnedPool(HostPool):
+    """A pinned host pool of expert records, viewed as uint16 [rows, record_elems]."""
 
     def __init__(self, shape: Shape, rows: int):
+        super().__init__(shape.record_elems, rows)
         self.shape = shape
-        self.rows = rows
-        self.nbytes = rows * shape.record_bytes
-        self.ptr = ft.ft_pool_alloc(self.nbytes)
-        buf = (C.c_uint16 * (self.nbytes // 2)).from_address(self.ptr)
-        self.view = np.ctypeslib.as_array(buf).reshape(rows, shape.record_elems)
 
-    def fill_numpy(self, records):
-        self.view[:] = records
-
-    def fill_device_random(self, seed: int, std: float = 0.02, chunk: int = 16):
-        """Fill with N(0, std^2) rounded to bf16, generated on the GPU (fast for big pools)."""
-        torch = torch_mod()
-        g = torch.Generator(device="cuda")
-        host_t = torch.from_numpy(self.view.reshape(-1).view(np.int16))
-        n = self.shape.record_elems
-        for r0 in range(0, self.rows, chunk):
-            r1 = min(self.rows, r0 + chunk)
-            g.manual_seed(seed * 1_000_003 + r0)
-            w = torch.randn((r1 - r0) * n, generator=g, device="cuda", dtype=torch.float32).mul_(std)
-            host_t[r0 * n:r1 * n].copy_(w.to(torch.bfloat16).view(torch.int16))
-        torch.cuda.synchronize()
-
-    def free(self):
-        if self.ptr:
-            ft.ft_pool_free(self.ptr)
-            self.ptr = 0
+    def fill_device_random(self, config_id: int, seed: int = 0):
+        fill_records_torch(self.view, config_id, seed)
 
 
 class Engine:

@@ -160,3 +160,32 @@ def test_error_codes():
         ft.ft_destroy(ctx)
     assert ft.ft_record_bytes(shape) == 6 * 64 * 64
     assert ft.ft_workspace_bytes(shape, 8) > 0
+
+
+@pytest.mark.parametrize("T,d,d_ff,uses,threads", [
+    (1, 256, 512, [[0], [0]], 3),
+    (8, 520, 136, [[0, 3, 7], [2], [1, 2, 3, 4, 5, 6, 7, 0]], 4),
+    (2, 2048, 768, [[0, 1]], 0),
+])
+def test_host_expert_kernel_matches_oracle(T, d, d_ff, uses, threads):
+    """The CPU branch: gate-weighted partials of experts run on the host, against the fp64 oracle."""
+    from moe_expert_offload_amd.synth import f32_to_bf16_bits, generator
+    from oracle.common import bf16_to_f64, within_tolerance
+    from oracle.ffn import expert_ffn, split_record
+    rng = generator(50, T, d, d_ff)
+    n_exp = len(uses)
+    recs = [np.ascontiguousarray(f32_to_bf16_bits(rng.normal(0, 0.02, 3 * d * d_ff))) for _ in range(n_exp)]
+    x = f32_to_bf16_bits(rng.normal(0, 1, (T, d)))
+    use_off = np.cumsum([0] + [len(u) for u in uses]).astype(np.int32)
+    use_t = np.array([t for u in uses for t in u], np.int32)
+    use_g = rng.random(use_t.size).astype(np.float32)
+    partial = np.full((T, d), np.nan, np.float32)
+    ft.ft_host_experts(x, T, d, d_ff, recs, use_off, use_t, use_g, n_exp, threads, partial)
+    ref = np.zeros((T, d))
+    x64 = bf16_to_f64(x)
+    for i in range(n_exp):
+        W = split_record(recs[i], d, d_ff)
+        for u in range(use_off[i], use_off[i + 1]):
+            ref[use_t[u]] += float(use_g[u]) * expert_ffn(W, x64[use_t[u]:use_t[u] + 1])[0]
+    ok, mx, l1 = within_tolerance(partial, ref, 1e-4, 1e-5)
+    assert ok, (mx, l1)
