@@ -79,6 +79,9 @@ WORKLOADS = {
     "c3": Workload("c3-decode-L43-d4096-E256-top6", 3, Shape(43, 256, 4096, 2048, 6), 1, 0.11),
     # prefill: 8192-token chunk through the c3 layer shape
     "c4": Workload("c4-prefill8k-L43-d4096-E256-top6", 4, Shape(43, 256, 4096, 2048, 6), 8192, 0.11),
+    # the c3 shape with MXFP4 experts: 16384-token prefill (two 8192 chunks) and batch-1 decode
+    "c5": Workload("c5-mxfp4-L43-d4096-E256-top6", 5, Shape(43, 256, 4096, 2048, 6), 8192, 0.11),
+    "c5d": Workload("c5-mxfp4-decode-L43-d4096-E256-top6", 5, Shape(43, 256, 4096, 2048, 6), 1, 0.11),
 }
 
 
@@ -208,3 +211,103 @@ def tokens_torch(config_id: int, chunk: int, layer: int, T: int, d: int, seed: i
     g = torch.Generator(device="cuda")
     g.manual_seed(((seed * 1_000_003 + config_id * 7919 + chunk) * 1_000_003 + layer) & 0x7FFFFFFFFFFFFFFF)
     return torch.randn((T, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+
+
+# ---- MXFP4 expert records --------------------------------------------------------
+# Weights N(0, 0.02^2) converted to OCP MXFP4 (E2M1 elements, E8M0 scale per 32
+# consecutive elements along each matrix's reduction axis; shared exponent
+# floor(log2 max|v|) - 2, elements rounded to nearest even and clamped to +-6).
+# Record bytes: [gate codes d_ff x d/2 | up codes d_ff x d/2 | down codes d x d_ff/2 |
+# gate scales d_ff x d/32 | up scales d_ff x d/32 | down scales d x d_ff/32], the
+# lower-index element of each pair in the low nibble.
+
+# magnitudes 0 .5 1 1.5 2 3 4 6; midpoints with the tie direction of round-half-even
+_E2M1_STEPS = ((0.25, False), (0.75, True), (1.25, False), (1.75, True), (2.5, False), (3.5, True), (5.0, False))
+
+
+def mxfp4_record_bytes(d: int, d_ff: int) -> int:
+    return 3 * d * d_ff // 2 + 3 * d * d_ff // 32
+
+
+def _mx_quantize_np(w):
+    """w [rows, cols] float64 -> (codes uint8 [rows, cols], scales uint8 [rows, cols/32])."""
+    rows, cols = w.shape
+    b = w.reshape(rows, cols // 32, 32)
+    amax = np.abs(b).max(axis=2)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    e = np.clip(ex.astype(np.int64) - 1 - 2, -127, 127)
+    a = np.minimum(np.abs(b) / np.exp2(e)[..., None], 6.0)
+    mag = np.zeros(a.shape, np.uint8)
+    for t, incl in _E2M1_STEPS:
+        mag += (a >= t) if incl else (a > t)
+    codes = np.where((b < 0) & (mag > 0), mag | 8, mag).astype(np.uint8)
+    zero = amax == 0
+    scales = np.where(zero, 0, e + 127).astype(np.uint8)
+    codes[zero] = 0
+    return codes.reshape(rows, cols), scales
+
+
+def _pack_nibbles_np(codes):
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def mxfp4_record_from_weights(wg, wu, wd):
+    """Pack float weights (W_gate [d_ff,d], W_up [d_ff,d], W_down [d,d_ff]) into an MXFP4 record."""
+    parts_c, parts_s = [], []
+    for w in (wg, wu, wd):
+        c, sc = _mx_quantize_np(np.asarray(w, np.float64))
+        parts_c.append(_pack_nibbles_np(c).reshape(-1))
+        parts_s.append(sc.reshape(-1))
+    return np.concatenate(parts_c + parts_s)
+
+
+def mxfp4_expert_record(w: Workload, layer_phys: int, expert: int, seed: int = 0) -> np.ndarray:
+    """One MXFP4 expert record (uint8), from N(0, 0.02^2) weights."""
+    s = w.shape
+    g = generator(w.config_id, STREAM_EXPERT, layer_phys, expert, seed=seed)
+    wg = g.normal(0.0, 0.02, size=(s.d_ff, s.d))
+    wu = g.normal(0.0, 0.02, size=(s.d_ff, s.d))
+    wd = g.normal(0.0, 0.02, size=(s.d, s.d_ff))
+    return mxfp4_record_from_weights(wg, wu, wd)
+
+
+def fill_mxfp4_records_torch(view, d: int, d_ff: int, config_id: int, seed: int = 0, chunk_rows: int = 8):
+    """Fills a uint8 [rows, record_bytes] host array with MXFP4 records of N(0, 0.02^2)
+    weights generated and converted on the GPU (same conversion as above)."""
+    import torch
+    rows, nbytes = view.shape
+    assert nbytes == mxfp4_record_bytes(d, d_ff)
+    host_t = torch.from_numpy(view.reshape(-1))
+    g = torch.Generator(device="cuda")
+
+    def quant(w):  # w [n, R, C] float32 -> codes packed [n, R*C/2], scales [n, R*C/32]
+        n, R, Cc = w.shape
+        b = w.reshape(n, R, Cc // 32, 32)
+        amax = b.abs().amax(dim=3)
+        _, ex = torch.frexp(torch.where(amax > 0, amax, torch.ones_like(amax)))
+        e = (ex.to(torch.int32) - 3).clamp(-127, 127)
+        a = (b.abs() / torch.exp2(e.to(torch.float32)).unsqueeze(-1)).clamp(max=6.0)
+        mag = torch.zeros_like(a, dtype=torch.uint8)
+        for t, incl in _E2M1_STEPS:
+            mag += (a >= t).to(torch.uint8) if incl else (a > t).to(torch.uint8)
+        codes = torch.where((b < 0) & (mag > 0), mag | 8, mag)
+        zero = amax == 0
+        codes = torch.where(zero.unsqueeze(-1), torch.zeros_like(codes), codes)
+        scales = torch.where(zero, torch.zeros_like(e), e + 127).to(torch.uint8)
+        codes = codes.reshape(n, R, Cc)
+        packed = codes[:, :, 0::2] | (codes[:, :, 1::2] << 4)
+        return packed.reshape(n, -1), scales.reshape(n, -1)
+
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        n = r1 - r0
+        g.manual_seed(((seed * 1_000_003 + config_id) * 1_000_003 + 7 * r0 + 1) & 0x7FFFFFFFFFFFFFFF)
+        wg = torch.randn((n, d_ff, d), generator=g, device="cuda").mul_(0.02)
+        wu = torch.randn((n, d_ff, d), generator=g, device="cuda").mul_(0.02)
+        wd = torch.randn((n, d, d_ff), generator=g, device="cuda").mul_(0.02)
+        cg, sg = quant(wg)
+        cu, su = quant(wu)
+        cd, sd = quant(wd)
+        rec = torch.cat([cg, cu, cd, sg, su, sd], dim=1)
+        host_t[r0 * nbytes:r1 * nbytes].copy_(rec.reshape(-1))
+    torch.cuda.synchronize()
