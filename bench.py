@@ -82,7 +82,7 @@ def run_decode(args, torch, ft, synth, HostPool):
     L_phys = s.L if args.l_phys <= 0 else min(args.l_phys, s.L)
     log(f"decode workload {wl.name}: pool {L_phys * s.E} records x {S / 1e6:.2f} MB = {L_phys * s.E * S / 1e9:.1f} GB")
     t = time.time()
-    pool = HostPool(s.record_elems, L_phys * s.E)
+    pool = HostPool(L_phys * s.E, s.record_bytes, s.pool_dtype)
     synth.fill_records_torch(pool.view, wl.config_id, seed=args.seed)
     log(f"pool allocated and filled in {time.time() - t:.1f} s")
 
@@ -214,7 +214,7 @@ def run_prefill(args, torch, ft, synth, HostPool):
     L_phys = max(1, min(args.prefill_l_phys, s.L))
     log(f"prefill workload {wl.name}: pool {L_phys * s.E} records = {L_phys * s.E * S / 1e9:.1f} GB (aliased)")
     t = time.time()
-    pool = HostPool(s.record_elems, L_phys * s.E)
+    pool = HostPool(L_phys * s.E, s.record_bytes, s.pool_dtype)
     synth.fill_records_torch(pool.view, wl.config_id, seed=args.seed)
     log(f"pool allocated and filled in {time.time() - t:.1f} s")
     try:

@@ -28,10 +28,27 @@
  *
  * Expert record (the unit of residency, [FT] §3: a slot holds every tensor of
  * one (layer, expert) pair; [FT] §4.2: banks are indexed by l*E + e): one
- * contiguous record per expert, bf16, row-major:
- *     [ W_gate (d_ff x d) | W_up (d_ff x d) | W_down (d x d_ff) ]
- * S = ft_record_bytes(shape) = 6 * d * d_ff bytes.  The host pool holds L_phys*E
- * records; logical layer l, expert e reads record (l mod L_phys)*E + e.
+ * contiguous record per expert, row-major.
+ *   FT_W_BF16:  [ W_gate (d_ff x d) | W_up (d_ff x d) | W_down (d x d_ff) ] in bf16,
+ *               S = 6 * d * d_ff bytes.
+ *   FT_W_MXFP4 ([FT] §5.1: routed experts natively MXFP4; format of the OCP
+ *               Microscaling Formats v1.0): bytes
+ *               [ gate codes d_ff x d/2 | up codes d_ff x d/2 | down codes d x d_ff/2 |
+ *                 gate scales d_ff x d/32 | up scales d_ff x d/32 | down scales d x d_ff/32 ],
+ *               E2M1 codes two per byte (lower-index element in the low nibble),
+ *               one E8M0 scale per 32 consecutive elements along each matrix's
+ *               reduction axis (d for gate/up, d_ff for down); weight value =
+ *               e2m1(code) * 2^(scale - 127).  S = 3*d*d_ff/2 + 3*d*d_ff/32 bytes.
+ * S = ft_record_bytes(shape).  The host pool holds L_phys*E records; logical
+ * layer l, expert e reads record (l mod L_phys)*E + e.
+ *
+ * MXFP4 arithmetic: decode (the row-streaming form) and the CPU branch apply the
+ * exactly dequantised weights to the bf16 activations.  Prefill (the MFMA form)
+ * runs on gfx950's scaled MFMA with E4M3 x E2M1 operands: x and the SwiGLU output
+ * h are converted to MXFP8 (E4M3 elements, one E8M0 scale per 32 consecutive
+ * elements along the reduction axis, shared exponent floor(log2 max|v|) - 8,
+ * elements rounded to nearest even and clamped to +-448, an all-zero block gets
+ * scale 0 and zero codes) before each contraction; fp32 accumulation.
  */
 #ifndef FT_H
 #define FT_H
@@ -61,10 +78,11 @@ extern "C" {
 typedef enum { FT_W_BF16 = 0, FT_W_MXFP4 = 1 } ft_wfmt;
 
 /* Layer-stack shape.  L layers, E routed experts per layer, hidden size d,
- * expert hidden size d_ff, k experts per token.  d and d_ff must be multiples of 8. */
+ * expert hidden size d_ff, k experts per token.  d and d_ff must be multiples of 8
+ * (FT_W_BF16) or of 128 (FT_W_MXFP4). */
 typedef struct {
   int32_t L, E, d, d_ff, k;
-  int32_t fmt; /* ft_wfmt; only FT_W_BF16 is built */
+  int32_t fmt; /* ft_wfmt: expert record format */
 } ft_shape;
 
 /* Engine configuration ([AIN] "How to use it", flags table).
@@ -233,6 +251,23 @@ int ft_grouped_ffn(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t k,
                    int32_t max_rows_per_group, void* h_ws, float* out, int32_t form,
                    void* stream);
 
+/* The same grouped SwiGLU FFN over FT_W_MXFP4 records ([FT] §5.1 experts natively
+ * MXFP4; §4.1 dequantisation inside the kernels).  form 1: row-streaming, exactly
+ * dequantised weights applied to the bf16 x (the decode form); form 2: scaled MFMA,
+ * x and h converted to MXFP8 first (the prefill form; see "MXFP4 arithmetic" above).
+ * d % 128 == 0 and d_ff % 128 == 0.  n_rows = offsets[n_groups] (rows of out).
+ * workspace: device, at least ft_grouped_ffn_mx_workspace_bytes(T, d, d_ff, n_rows)
+ * bytes, 256-byte aligned; FT_ENOMEM when smaller.  It holds, each part starting at
+ * a 256-byte boundary: h fp32 [n_rows, d_ff]; x in MXFP8, codes [T, d] then scales
+ * [T, d/32]; h in MXFP8, codes [n_rows, d_ff] then scales [n_rows, d_ff/32]
+ * (form 1 uses h only).  These are readable after the call. */
+size_t ft_grouped_ffn_mx_workspace_bytes(int32_t T, int32_t d, int32_t d_ff, int32_t n_rows);
+int ft_grouped_ffn_mx(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t k,
+                      const void* slots, const int32_t* group_slot, const int32_t* offsets,
+                      const int32_t* perm, int32_t n_groups, int32_t g_begin, int32_t g_end,
+                      int32_t max_rows_per_group, int32_t n_rows, void* workspace,
+                      size_t workspace_bytes, float* out, int32_t form, void* stream);
+
 /* Gate-weighted combine and exact merge ([FT] §3.2: the GPU and CPU partial sums
  * merge into the exact MoE output):  y[t] = sum_{j: inv[t*k+j] >= 0, in j order}
  * gates[t*k+j] * out[inv[t*k+j]]  +  cpu_partial[t]  (cpu_partial may be NULL).
@@ -243,14 +278,15 @@ int ft_combine(const float* out, const int32_t* inv, const float* gates,
 
 /* Host expert kernel, the CPU branch of a decode call ([FT] §3.2: experts of C run
  * in place from the host pool and return gate-weighted per-token partials; §4.1:
- * persistent workers with SIMD kernels).  For n_exp experts with bf16 records
- * `records[i]` (host or pinned) and uses u in [use_off[i], use_off[i+1]) of token
- * use_t[u] with gate use_g[u]:  partial[t] = sum over uses of g * FFN_i(x[t]),
- * fp32, overwritten.  x: host bf16 [T, d].  threads: workers of a pool made for
- * this call (0 = default count).  At most 64 uses per expert. */
-int ft_host_experts(const void* x, int32_t T, int32_t d, int32_t d_ff, const void* const* records,
-                    const int32_t* use_off, const int32_t* use_t, const float* use_g, int32_t n_exp,
-                    int32_t threads, float* partial);
+ * persistent workers with SIMD kernels that dequantise in place).  For n_exp experts
+ * with records `records[i]` of format fmt (ft_wfmt; host or pinned) and uses u in
+ * [use_off[i], use_off[i+1]) of token use_t[u] with gate use_g[u]:
+ * partial[t] = sum over uses of g * FFN_i(x[t]), fp32, overwritten (MXFP4 weights
+ * exactly dequantised, activations bf16).  x: host bf16 [T, d].  threads: workers
+ * of a pool made for this call (0 = default count).  At most 64 uses per expert. */
+int ft_host_experts(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t fmt,
+                    const void* const* records, const int32_t* use_off, const int32_t* use_t,
+                    const float* use_g, int32_t n_exp, int32_t threads, float* partial);
 
 /* ---- expert cache -------------------------------------------------------------- */
 

@@ -31,6 +31,7 @@ HOST_FLAGS = ["-x", "c++", "-D__HIP_PLATFORM_AMD__", f"-I{os.path.join(ROCM, 'in
 # (source, compiler, extra flags): device code through hipcc, host code as plain C++
 SOURCES = [
     ("kernels.hip", HIPCC, [f"--offload-arch={ARCH}"] + DEVICE_FLAGS),
+    ("kernels_mx.hip", HIPCC, [f"--offload-arch={ARCH}"] + DEVICE_FLAGS),
     ("api.cpp", CXX, HOST_FLAGS),
     ("cache.cpp", CXX, HOST_FLAGS),
     ("qstar.cpp", CXX, HOST_FLAGS),
@@ -54,7 +55,7 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         cmd = [cc] + COMMON + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
         jobs.append((cmd, obj))
-    with ThreadPoolExecutor(max_workers=min(len(jobs), 5)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(jobs), 6)) as ex:
         outs = list(ex.map(lambda j: _run(j[0]), jobs))
     if verbose:
         for o in outs:

@@ -67,13 +67,19 @@ void prefault_host(const void* p, size_t bytes, int threads) {
 }
 
 bool shape_ok(const ft_shape* s) {
-  return s && s->L > 0 && s->E > 0 && s->E <= 1024 && s->d > 0 && s->d % 8 == 0 && s->d_ff > 0 &&
-         s->d_ff % 8 == 0 && s->k >= 1 && s->k <= 8 && s->k <= s->E && s->fmt == FT_W_BF16;
+  if (!s || s->L <= 0 || s->E <= 0 || s->E > 1024 || s->d <= 0 || s->d % 8 || s->d_ff <= 0 || s->d_ff % 8 ||
+      s->k < 1 || s->k > 8 || s->k > s->E)
+    return false;
+  if (s->fmt == FT_W_BF16) return true;
+  return s->fmt == FT_W_MXFP4 && s->d % 128 == 0 && s->d_ff % 128 == 0;
 }
+
+bool is_mx(const ft_shape* s) { return s->fmt == FT_W_MXFP4; }
 
 // Workspace carve: offsets of each device array for calls of up to T_max tokens.
 struct Carve {
   size_t ticket, idx, gates, logits, key, gslot, bufslot, offsets, perm, inv, pws, h, out, cpu, total;
+  size_t xq, xs, hq, hs;  // MXFP8 copies of x and h (MXFP4 experts only)
   size_t pws_bytes;
   int g_max;
 };
@@ -104,6 +110,12 @@ Carve carve(const ft_shape* s, int T_max) {
   c.h = take(P * s->d_ff * 4);
   c.out = take(P * s->d * 4);
   c.cpu = take((size_t)t_dec * s->d * 4);
+  if (is_mx(s)) {
+    c.xq = take((size_t)T_max * s->d);
+    c.xs = take((size_t)T_max * (s->d / 32));
+    c.hq = take(P * s->d_ff);
+    c.hs = take(P * (s->d_ff / 32));
+  }
   c.total = o;
   return c;
 }
@@ -113,11 +125,12 @@ Carve carve(const ft_shape* s, int T_max) {
 struct ft_ctx {
   ft_shape shape{};
   ft_config cfg{};
-  size_t S = 0, rec_elems = 0;
-  const uint16_t* pool = nullptr;
+  size_t S = 0;  // record bytes
+  bool mx = false;
+  const uint8_t* pool = nullptr;
   size_t pool_bytes = 0;
   int L_phys = 0;
-  uint16_t* slots = nullptr;
+  uint8_t* slots = nullptr;
   uint8_t* ws = nullptr;
   size_t ws_bytes = 0;
   Carve cv{};
@@ -159,10 +172,8 @@ struct ft_ctx {
 
   template <typename T>
   T* wsp(size_t off) const { return reinterpret_cast<T*>(ws + off); }
-  const uint16_t* record(int layer, int e) const {
-    return pool + ((size_t)(layer % L_phys) * shape.E + e) * rec_elems;
-  }
-  uint16_t* slot_ptr(int s) const { return slots + (size_t)s * rec_elems; }
+  const uint8_t* record(int layer, int e) const { return pool + ((size_t)(layer % L_phys) * shape.E + e) * S; }
+  uint8_t* slot_ptr(int s) const { return slots + (size_t)s * S; }
 };
 
 namespace {
@@ -184,14 +195,21 @@ ft_ctx::ProfRec* prof_begin(ft_ctx* c) {
 }
 
 // Algorithmic bytes and flops of one launch from its rows per group (see ft.h).
+// Per group of n rows: the expert's weights once, the n activation rows read, the
+// n result rows written.  hb: bytes per h element between the two kernels.  MXFP4
+// weights cost 1/2 + 1/32 byte per element; the MFMA form reads x and h as MXFP8
+// (1 + 1/32 bytes per element) after its conversion kernels.
 void prof_account(ft_ctx* c, ft_ctx::ProfRec* r, const int* rows, int n_groups, int hb) {
   const double d = c->shape.d, dff = c->shape.d_ff;
+  const double wb = c->mx ? (0.5 + 1.0 / 32.0) : 2.0;                   // weight bytes per element
+  const bool mx8 = c->mx && hb == 1;                                      // MXFP8 activations
+  const double xb = mx8 ? 1.0 + 1.0 / 32.0 : 2.0, hin = mx8 ? 1.0 + 1.0 / 32.0 : hb, hout = mx8 ? 4.0 : hb;
   r->bytes_up = r->bytes_dn = r->flops_up = r->flops_dn = 0.0;
   for (int g = 0; g < n_groups; ++g) {
     const double n = rows[g];
     if (n <= 0) continue;
-    r->bytes_up += 2.0 * d * dff * 2.0 + n * d * 2.0 + n * dff * hb;
-    r->bytes_dn += d * dff * 2.0 + n * dff * hb + n * d * 4.0;
+    r->bytes_up += 2.0 * d * dff * wb + n * d * xb + n * dff * hout;
+    r->bytes_dn += d * dff * wb + n * dff * hin + n * d * 4.0;
     r->flops_up += 4.0 * n * d * dff;
     r->flops_dn += 2.0 * n * d * dff;
   }
@@ -220,6 +238,7 @@ const char* ft_last_error(void) { return ft::g_last_error.c_str(); }
 
 size_t ft_record_bytes(const ft_shape* s) {
   if (!shape_ok(s)) return 0;
+  if (is_mx(s)) return ft::mx_record_bytes(s->d, s->d_ff);
   return (size_t)6 * s->d * s->d_ff;
 }
 
@@ -248,7 +267,9 @@ int ft_create(const ft_shape* shape, const ft_config* config, const void* host_p
               size_t workspace_bytes, ft_ctx_t* out) {
   if (!out) return fail(FT_EINVAL, "create: null out");
   *out = nullptr;
-  if (!shape_ok(shape)) return fail(shape && shape->fmt != FT_W_BF16 ? FT_EUNSUPPORTED : FT_EINVAL, "create: bad shape");
+  if (!shape_ok(shape))
+    return fail(shape && shape->fmt != FT_W_BF16 && shape->fmt != FT_W_MXFP4 ? FT_EUNSUPPORTED : FT_EINVAL,
+                "create: bad shape");
   if (!config || config->T_max < 1 || config->frac_q16 > 65536u || n_slots < 0 || config->max_fetch < -1)
     return fail(FT_EINVAL, "create: bad config");
   if (config->prefill_overlap && n_slots < 2 * shape->E)
@@ -259,7 +280,7 @@ int ft_create(const ft_shape* shape, const ft_config* config, const void* host_p
   c->L_phys = config->L_phys > 0 ? std::min(config->L_phys, shape->L) : shape->L;
   c->cfg.L_phys = c->L_phys;
   c->S = ft_record_bytes(shape);
-  c->rec_elems = c->S / 2;
+  c->mx = is_mx(shape);
   c->overlap = config->prefill_overlap != 0;
   c->t_dec = std::max(1, std::min(std::min(config->T_max, FT_PLAN_CAP / shape->k), 64));
   c->cache = new ft::ExpertCache(shape->L, shape->E, n_slots);
@@ -282,9 +303,9 @@ int ft_create(const ft_shape* shape, const ft_config* config, const void* host_p
       return bail(FT_ENOPIN, "create: host pool is not pinned host memory");
     }
     if (hipGetDevice(&c->device) != hipSuccess) return bail(FT_EHIP, "create: hipGetDevice failed");
-    c->pool = static_cast<const uint16_t*>(host_pool);
+    c->pool = static_cast<const uint8_t*>(host_pool);
     c->pool_bytes = pool_bytes;
-    c->slots = static_cast<uint16_t*>(dev_slots);
+    c->slots = static_cast<uint8_t*>(dev_slots);
     c->ws = static_cast<uint8_t*>(dev_workspace);
     c->ws_bytes = workspace_bytes;
     const size_t P = (size_t)FT_PLAN_CAP;
@@ -407,21 +428,56 @@ int ft_grouped_ffn(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t k,
                              static_cast<float*>(h_ws), out, stream);
 }
 
+size_t ft_grouped_ffn_mx_workspace_bytes(int32_t T, int32_t d, int32_t d_ff, int32_t n_rows) {
+  if (T < 0 || d <= 0 || d_ff <= 0 || n_rows < 0) return 0;
+  return align256((size_t)n_rows * d_ff * 4) + align256(ft::mx_act_ws_bytes(T, d)) +
+         align256(ft::mx_act_ws_bytes(n_rows, d_ff));
+}
+
+int ft_grouped_ffn_mx(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t k, const void* slots,
+                      const int32_t* group_slot, const int32_t* offsets, const int32_t* perm, int32_t n_groups,
+                      int32_t g_begin, int32_t g_end, int32_t max_rows_per_group, int32_t n_rows, void* workspace,
+                      size_t workspace_bytes, float* out, int32_t form, void* stream) {
+  if (T < 0 || g_begin < 0 || g_end > n_groups || g_begin > g_end) return fail(FT_EINVAL, "grouped_ffn_mx: bad group range");
+  if (d <= 0 || d_ff <= 0 || d % 128 || d_ff % 128) return fail(FT_EINVAL, "grouped_ffn_mx: need d%128==0 and d_ff%128==0");
+  if (n_rows < 0 || !workspace || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return fail(FT_EINVAL, "grouped_ffn_mx: need n_rows >= 0 and a 256-byte aligned workspace");
+  if (workspace_bytes < ft_grouped_ffn_mx_workspace_bytes(T, d, d_ff, n_rows))
+    return fail(FT_ENOMEM, "grouped_ffn_mx: workspace too small");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* h = reinterpret_cast<float*>(ws);
+  uint8_t* xq = ws + align256((size_t)n_rows * d_ff * 4);
+  uint8_t* xs = xq + (size_t)T * d;
+  uint8_t* hq = xq + align256(ft::mx_act_ws_bytes(T, d));
+  uint8_t* hs = hq + (size_t)n_rows * d_ff;
+  const uint8_t* sl = static_cast<const uint8_t*>(slots);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (form == 1)
+    return ft::launch_mx_ffn_rows(xb, d, d_ff, k, sl, group_slot, offsets, perm, g_begin, g_end, max_rows_per_group,
+                                  h, out, stream);
+  if (form == 2)
+    return ft::launch_mx_ffn_mfma(xb, T, d, d_ff, k, sl, group_slot, offsets, perm, g_begin, g_end, n_rows, xq, xs, h,
+                                  hq, hs, out, stream);
+  return fail(FT_EINVAL, "grouped_ffn_mx: form must be 1 or 2");
+}
+
 int ft_combine(const float* out, const int32_t* inv, const float* gates, const float* cpu_partial,
                int32_t T, int32_t k, int32_t d, float* y, void* stream) {
   return ft::launch_combine(out, inv, gates, cpu_partial, T, k, d, y, stream);
 }
 
-int ft_host_experts(const void* x, int32_t T, int32_t d, int32_t d_ff, const void* const* records,
+int ft_host_experts(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t fmt, const void* const* records,
                     const int32_t* use_off, const int32_t* use_t, const float* use_g, int32_t n_exp,
                     int32_t threads, float* partial) {
   if (!x || !partial || T < 1 || d <= 0 || d_ff <= 0 || n_exp < 0 || (n_exp > 0 && (!records || !use_off)))
     return fail(FT_EINVAL, "host_experts: bad argument");
+  if (fmt != FT_W_BF16 && fmt != FT_W_MXFP4) return fail(FT_EUNSUPPORTED, "host_experts: unknown format");
+  if (fmt == FT_W_MXFP4 && (d % 32 || d_ff % 32)) return fail(FT_EINVAL, "host_experts: MXFP4 needs d, d_ff % 32 == 0");
   std::vector<ft::CpuExpert> ex(n_exp);
   for (int i = 0; i < n_exp; ++i) {
     const int n = use_off[i + 1] - use_off[i];
     if (n < 0 || n > 64 || !records[i]) return fail(FT_EINVAL, "host_experts: 0..64 uses per expert");
-    ex[i].rec = static_cast<const uint16_t*>(records[i]);
+    ex[i].rec = records[i];
     ex[i].n_use = n;
     for (int u = 0; u < n; ++u) {
       const int t = use_t[use_off[i] + u];
@@ -434,7 +490,7 @@ int ft_host_experts(const void* x, int32_t T, int32_t d, int32_t d_ff, const voi
     return FT_OK;
   }
   ft::CpuPool* pool = ft::cpu_pool_create(threads);
-  ft::cpu_pool_submit(pool, static_cast<const uint16_t*>(x), T, d, d_ff, ex.data(), n_exp, partial);
+  ft::cpu_pool_submit(pool, static_cast<const uint16_t*>(x), T, d, d_ff, fmt, ex.data(), n_exp, partial);
   ft::cpu_pool_wait(pool);
   ft::cpu_pool_destroy(pool);
   return FT_OK;
@@ -478,7 +534,7 @@ int ft_expert_cache_resize(ft_ctx_t c, void* new_dev_slots, int32_t n) {
       if (q == hipErrorNotReady) return fail(FT_EBUSY, "resize: issued work still running");
       if (q != hipSuccess) return fail(FT_EHIP, std::string("resize: hipEventQuery: ") + hipGetErrorString(q));
     }
-    c->slots = static_cast<uint16_t*>(new_dev_slots);
+    c->slots = static_cast<uint8_t*>(new_dev_slots);
   }
   c->cache->resize(n);
   c->cache->stats.resizes += 1;
@@ -558,7 +614,7 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
       for (int pr = 0; pr < P; ++pr)
         if (c->h_idx[pr] == e && ex.n_use < 64) ex.use[ex.n_use++] = ft::CpuUse{pr / k, c->h_gates[pr]};
     }
-    ft::cpu_pool_submit(c->cpu, c->h_x, T, d, c->shape.d_ff, c->cpu_ex.data(), n_c, c->h_partial);
+    ft::cpu_pool_submit(c->cpu, c->h_x, T, d, c->shape.d_ff, c->shape.fmt, c->cpu_ex.data(), n_c, c->h_partial);
   }
   // fills of F on the copy stream
   if (q > 0) {
@@ -594,8 +650,12 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
   auto ffn = [&](int g0, int g1) -> int {
     ft_ctx::ProfRec* r = prof_begin(c);
     if (r) prof_account(c, r, rows_of + g0, g1 - g0, 4);
-    return ft::launch_ffn_rows(xs, d, c->shape.d_ff, k, c->slots, d_gslot, d_off, d_perm, g0, g1, max_rows, d_h,
-                               d_out, cs, r ? reinterpret_cast<void* const*>(r->ev) : nullptr);
+    void* const* ev = r ? reinterpret_cast<void* const*>(r->ev) : nullptr;
+    if (c->mx)
+      return ft::launch_mx_ffn_rows(xs, d, c->shape.d_ff, k, c->slots, d_gslot, d_off, d_perm, g0, g1, max_rows, d_h,
+                                    d_out, cs, ev);
+    return ft::launch_ffn_rows(xs, d, c->shape.d_ff, k, reinterpret_cast<const uint16_t*>(c->slots), d_gslot, d_off,
+                               d_perm, g0, g1, max_rows, d_h, d_out, cs, ev);
   };
   if (n_h > 0)
     if (int rc = ffn(0, n_h)) return rc;
@@ -706,12 +766,20 @@ int ft_moe_prefill_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, co
   const bool mfma = d % 128 == 0 && d_ff % 64 == 0;
   ft_ctx::ProfRec* r = prof_begin(c);
   void* const* evs = r ? reinterpret_cast<void* const*>(r->ev) : nullptr;
-  if (mfma) {
-    if (int rc = ft::launch_ffn_mfma(xs, d, d_ff, k, c->slots, d_buf, d_off, d_perm, 0, E, T,
+  const uint16_t* slots16 = reinterpret_cast<const uint16_t*>(c->slots);
+  if (c->mx) {
+    // MXFP4 experts on the scaled MFMA, x and h in MXFP8
+    if (int rc = ft::launch_mx_ffn_mfma(xs, T, d, d_ff, k, c->slots, d_buf, d_off, d_perm, 0, E, P,
+                                        c->wsp<uint8_t>(c->cv.xq), c->wsp<uint8_t>(c->cv.xs), c->wsp<float>(c->cv.h),
+                                        c->wsp<uint8_t>(c->cv.hq), c->wsp<uint8_t>(c->cv.hs),
+                                        c->wsp<float>(c->cv.out), cs, evs))
+      return rc;
+  } else if (mfma) {
+    if (int rc = ft::launch_ffn_mfma(xs, d, d_ff, k, slots16, d_buf, d_off, d_perm, 0, E, T,
                                      c->wsp<uint16_t>(c->cv.h), c->wsp<float>(c->cv.out), cs, evs))
       return rc;
   } else {
-    if (int rc = ft::launch_ffn_rows(xs, d, d_ff, k, c->slots, d_buf, d_off, d_perm, 0, E, 8,
+    if (int rc = ft::launch_ffn_rows(xs, d, d_ff, k, slots16, d_buf, d_off, d_perm, 0, E, 8,
                                      c->wsp<float>(c->cv.h), c->wsp<float>(c->cv.out), cs, evs))
       return rc;
   }
@@ -724,7 +792,7 @@ int ft_moe_prefill_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, co
       r->offsets = nullptr;
     }
     r->n_groups = E;
-    r->hb = mfma ? 2 : 4;
+    r->hb = c->mx ? 1 : (mfma ? 2 : 4);
     if (r->offsets) FT_HIP(hipMemcpyAsync(r->offsets, d_off, (size_t)(E + 1) * 4, hipMemcpyDeviceToHost, cs));
   }
   if (int rc = ft::launch_combine(c->wsp<float>(c->cv.out), d_inv, d_gates, nullptr, T, k, d, y, cs)) return rc;
@@ -839,14 +907,14 @@ int ft_bench_bw(const ft_shape* shape, const void* host_pool, int32_t n_records,
   std::vector<float> part((size_t)shape->d);
   std::vector<ft::CpuExpert> ex(n_records);
   for (int i = 0; i < n_records; ++i) {
-    ex[i].rec = static_cast<const uint16_t*>(host_pool) + (size_t)i * (S / 2);
+    ex[i].rec = static_cast<const uint8_t*>(host_pool) + (size_t)i * S;
     ex[i].n_use = 1;
     ex[i].use[0] = ft::CpuUse{0, 1.0f};
   }
   double best_us = 1e30;
   for (int rep = 0; rep < 4; ++rep) {
     const double a = now_us();
-    ft::cpu_pool_submit(pool, x.data(), 1, shape->d, shape->d_ff, ex.data(), n_records, part.data());
+    ft::cpu_pool_submit(pool, x.data(), 1, shape->d, shape->d_ff, shape->fmt, ex.data(), n_records, part.data());
     ft::cpu_pool_wait(pool);
     const double b = now_us() - a;
     if (rep > 0) best_us = std::min(best_us, b);

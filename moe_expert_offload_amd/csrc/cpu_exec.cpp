@@ -12,7 +12,9 @@
 // computes partial[t][c] = sum over the uses (expert, t, gate) of
 // gate * (W_down[c] . h) with output rows dealt in blocks, so every output row
 // is owned by one worker.  Each weight row is read once and applied to all the
-// uses of its expert.
+// uses of its expert.  MXFP4 records (OCP MX v1.0: E2M1 codes, one E8M0 scale per
+// 32 consecutive elements of a row) are dequantised in registers through a
+// 16-entry table, exactly (every E2M1 value times a power of two is an fp32).
 #include <immintrin.h>
 #include <pthread.h>
 #include <sched.h>
@@ -95,17 +97,99 @@ __attribute__((target("avx512f,avx512bw"))) void row_dots_avx512(const uint16_t*
   }
 }
 
+// ---- MXFP4 rows: codes (n/2 bytes, low nibble first) and n/32 E8M0 scales ----
+using MxRowDotsFn = void (*)(const uint8_t* codes, const uint8_t* sc, int n, const float* const* xs, int nx,
+                             float* out);
+
+constexpr float kE2M1[16] = {0.0f,  0.5f,  1.0f,  1.5f,  2.0f,  3.0f,  4.0f,  6.0f,
+                             -0.0f, -0.5f, -1.0f, -1.5f, -2.0f, -3.0f, -4.0f, -6.0f};
+
+inline float e8m0_f(uint8_t s) { return std::ldexp(1.0f, (int)s - 127); }
+
+void mx_row_dots_scalar(const uint8_t* codes, const uint8_t* sc, int n, const float* const* xs, int nx,
+                        float* out) {
+  float acc[MAXV] = {0};
+  for (int b = 0; b < n / 32; ++b) {
+    float w[32];
+    const float s = e8m0_f(sc[b]);
+    for (int i = 0; i < 16; ++i) {
+      w[2 * i] = kE2M1[codes[16 * b + i] & 15] * s;
+      w[2 * i + 1] = kE2M1[codes[16 * b + i] >> 4] * s;
+    }
+    for (int v = 0; v < nx; ++v)
+      for (int i = 0; i < 32; ++i) acc[v] += w[i] * xs[v][32 * b + i];
+  }
+  for (int v = 0; v < nx; ++v) out[v] = acc[v];
+}
+
+__attribute__((target("avx2,fma"))) void mx_row_dots_avx2(const uint8_t* codes, const uint8_t* sc, int n,
+                                                            const float* const* xs, int nx, float* out) {
+  const __m256 mag = _mm256_setr_ps(0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f);
+  const __m128i m4 = _mm_set1_epi8(0x0f);
+  __m256 acc[MAXV];
+  for (int v = 0; v < MAXV; ++v) acc[v] = _mm256_setzero_ps();
+  for (int b = 0; b < n / 32; ++b) {
+    const __m128i raw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(codes + 16 * b));
+    const __m128i lo = _mm_and_si128(raw, m4);
+    const __m128i hi = _mm_and_si128(_mm_srli_epi16(raw, 4), m4);
+    const __m128i el[2] = {_mm_unpacklo_epi8(lo, hi), _mm_unpackhi_epi8(lo, hi)};  // elements 0..15, 16..31
+    const __m256 s = _mm256_set1_ps(e8m0_f(sc[b]));
+    __m256 w[4];
+    for (int q = 0; q < 4; ++q) {
+      const __m128i src = (q & 1) ? _mm_srli_si128(el[q >> 1], 8) : el[q >> 1];
+      const __m256i c = _mm256_cvtepu8_epi32(src);
+      const __m256 m = _mm256_permutevar8x32_ps(mag, c);
+      const __m256 sign = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_and_si256(c, _mm256_set1_epi32(8)), 28));
+      w[q] = _mm256_mul_ps(_mm256_xor_ps(m, sign), s);
+    }
+    for (int v = 0; v < nx; ++v)
+      for (int q = 0; q < 4; ++q) acc[v] = _mm256_fmadd_ps(w[q], _mm256_loadu_ps(xs[v] + 32 * b + 8 * q), acc[v]);
+  }
+  for (int v = 0; v < nx; ++v) {
+    __m128 t = _mm_add_ps(_mm256_castps256_ps128(acc[v]), _mm256_extractf128_ps(acc[v], 1));
+    t = _mm_hadd_ps(t, t);
+    t = _mm_hadd_ps(t, t);
+    out[v] = _mm_cvtss_f32(t);
+  }
+}
+
+__attribute__((target("avx512f,avx512bw"))) void mx_row_dots_avx512(const uint8_t* codes, const uint8_t* sc, int n,
+                                                                      const float* const* xs, int nx, float* out) {
+  const __m512 lut = _mm512_loadu_ps(kE2M1);
+  const __m128i m4 = _mm_set1_epi8(0x0f);
+  __m512 acc[MAXV];
+  for (int v = 0; v < MAXV; ++v) acc[v] = _mm512_setzero_ps();
+  for (int b = 0; b < n / 32; ++b) {
+    const __m128i raw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(codes + 16 * b));
+    const __m128i lo = _mm_and_si128(raw, m4);
+    const __m128i hi = _mm_and_si128(_mm_srli_epi16(raw, 4), m4);
+    const __m512 s = _mm512_set1_ps(e8m0_f(sc[b]));
+    const __m512 w0 = _mm512_mul_ps(_mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpacklo_epi8(lo, hi)), lut), s);
+    const __m512 w1 = _mm512_mul_ps(_mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpackhi_epi8(lo, hi)), lut), s);
+    for (int v = 0; v < nx; ++v) {
+      acc[v] = _mm512_fmadd_ps(w0, _mm512_loadu_ps(xs[v] + 32 * b), acc[v]);
+      acc[v] = _mm512_fmadd_ps(w1, _mm512_loadu_ps(xs[v] + 32 * b + 16), acc[v]);
+    }
+  }
+  for (int v = 0; v < nx; ++v) out[v] = _mm512_reduce_add_ps(acc[v]);
+}
+
+MxRowDotsFn g_mx_row_dots = nullptr;
+
 RowDotsFn pick_row_dots(const char** name) {
   __builtin_cpu_init();
   if (__builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw")) {
     *name = "avx512";
+    g_mx_row_dots = mx_row_dots_avx512;
     return row_dots_avx512;
   }
   if (__builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma")) {
     *name = "avx2";
+    g_mx_row_dots = mx_row_dots_avx2;
     return row_dots_avx2;
   }
   *name = "scalar";
+  g_mx_row_dots = mx_row_dots_scalar;
   return row_dots_scalar;
 }
 
@@ -159,11 +243,12 @@ class CpuPool {
   double last_work_us() const { return t_done_us_; }
   int last_caller_items() const { return caller_items_; }
 
-  void submit(const uint16_t* x, int T, int d, int d_ff, const CpuExpert* ex, int n_exp,
+  void submit(const uint16_t* x, int T, int d, int d_ff, int fmt, const CpuExpert* ex, int n_exp,
               float* partial) {
     T_ = T;
     d_ = d;
     d_ff_ = d_ff;
+    mx_ = fmt == FT_W_MXFP4;
     ex_ = ex;
     n_exp_ = n_exp;
     partial_ = partial;
@@ -250,16 +335,23 @@ class CpuPool {
     const int r0 = (item % blocks1_) * RB1;
     const int r1 = std::min(d_ff_, r0 + RB1);
     const CpuExpert& X = ex_[e];
-    const uint16_t* wg = X.rec;
-    const uint16_t* wu = X.rec + (size_t)d_ff_ * d_;
+    const uint16_t* wg = static_cast<const uint16_t*>(X.rec);
+    const uint16_t* wu = wg + (size_t)d_ff_ * d_;
+    const uint8_t* rb = static_cast<const uint8_t*>(X.rec);
+    const size_t mc = (size_t)d_ff_ * d_ / 2, ms = (size_t)d_ff_ * d_ / 32;  // MXFP4 code / scale bytes per matrix
     const float* xs[MAXV];
     float zg[MAXV], zu[MAXV];
     for (int u0 = 0; u0 < X.n_use; u0 += MAXV) {
       const int nx = std::min(MAXV, X.n_use - u0);
       for (int v = 0; v < nx; ++v) xs[v] = xf_.data() + (size_t)X.use[u0 + v].t * d_;
       for (int r = r0; r < r1; ++r) {
-        g_row_dots(wg + (size_t)r * d_, d_, xs, nx, zg);
-        g_row_dots(wu + (size_t)r * d_, d_, xs, nx, zu);
+        if (mx_) {
+          g_mx_row_dots(rb + (size_t)r * (d_ / 2), rb + 3 * mc + (size_t)r * (d_ / 32), d_, xs, nx, zg);
+          g_mx_row_dots(rb + mc + (size_t)r * (d_ / 2), rb + 3 * mc + ms + (size_t)r * (d_ / 32), d_, xs, nx, zu);
+        } else {
+          g_row_dots(wg + (size_t)r * d_, d_, xs, nx, zg);
+          g_row_dots(wu + (size_t)r * d_, d_, xs, nx, zu);
+        }
         for (int v = 0; v < nx; ++v)
           h_[(size_t)(use_base_[e] + u0 + v) * d_ff_ + r] = silu_f(zg[v]) * zu[v];
       }
@@ -273,12 +365,18 @@ class CpuPool {
     float o[MAXV];
     for (int e = 0; e < n_exp_; ++e) {
       const CpuExpert& X = ex_[e];
-      const uint16_t* wd = X.rec + (size_t)2 * d_ff_ * d_;
+      const uint16_t* wd = static_cast<const uint16_t*>(X.rec) + (size_t)2 * d_ff_ * d_;
+      const uint8_t* rb = static_cast<const uint8_t*>(X.rec);
+      const size_t mc = (size_t)d_ff_ * d_ / 2, ms = (size_t)d_ff_ * d_ / 32;
       for (int u0 = 0; u0 < X.n_use; u0 += MAXV) {
         const int nx = std::min(MAXV, X.n_use - u0);
         for (int v = 0; v < nx; ++v) hs[v] = h_.data() + (size_t)(use_base_[e] + u0 + v) * d_ff_;
         for (int c = c0; c < c1; ++c) {
-          g_row_dots(wd + (size_t)c * d_ff_, d_ff_, hs, nx, o);
+          if (mx_)
+            g_mx_row_dots(rb + 2 * mc + (size_t)c * (d_ff_ / 2), rb + 3 * mc + 2 * ms + (size_t)c * (d_ff_ / 32), d_ff_,
+                          hs, nx, o);
+          else
+            g_row_dots(wd + (size_t)c * d_ff_, d_ff_, hs, nx, o);
           for (int v = 0; v < nx; ++v) partial_[(size_t)X.use[u0 + v].t * d_ + c] += X.use[u0 + v].gate * o[v];
         }
       }
@@ -314,6 +412,7 @@ class CpuPool {
   std::atomic<bool> stop_{false};
 
   int T_ = 0, d_ = 0, d_ff_ = 0, n_exp_ = 0;
+  bool mx_ = false;
   const CpuExpert* ex_ = nullptr;
   float* partial_ = nullptr;
   std::vector<float> xf_, h_;
@@ -329,9 +428,9 @@ class CpuPool {
 CpuPool* cpu_pool_create(int threads) { return new CpuPool(threads); }
 void cpu_pool_destroy(CpuPool* p) { delete p; }
 int cpu_pool_threads(const CpuPool* p) { return p->threads(); }
-void cpu_pool_submit(CpuPool* p, const uint16_t* x, int T, int d, int d_ff, const CpuExpert* ex,
+void cpu_pool_submit(CpuPool* p, const uint16_t* x, int T, int d, int d_ff, int fmt, const CpuExpert* ex,
                      int n_exp, float* partial) {
-  p->submit(x, T, d, d_ff, ex, n_exp, partial);
+  p->submit(x, T, d, d_ff, fmt, ex, n_exp, partial);
 }
 void cpu_pool_wait(CpuPool* p) { p->wait(); }
 double cpu_pool_last_work_us(const CpuPool* p) { return p->last_work_us(); }

@@ -47,6 +47,26 @@ int launch_ffn_mfma(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
                     int g_begin, int g_end, int max_rows, uint16_t* h, float* out, void* stream,
                     void* const* ev = nullptr);
 
+// ---- MXFP4 experts (kernels_mx.hip) ------------------------------------------------
+size_t mx_record_bytes(int d, int d_ff);
+
+// Row-streaming grouped FFN over MXFP4 records, bf16 x: h fp32 [rows, d_ff], out fp32 [rows, d].
+int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t* slots, const int32_t* group_slot,
+                       const int32_t* offsets, const int32_t* perm, int g_begin, int g_end, int max_rows, float* h,
+                       float* out, void* stream, void* const* ev = nullptr);
+
+// Bytes of an MXFP8 copy of rows x n activations (codes then one scale per 32).
+size_t mx_act_ws_bytes(int rows, int n);
+
+// Scaled-MFMA grouped FFN: converts x [T, d] to MXFP8 (xq codes [T, d], xs scales
+// [T, d/32]), gate/up into h fp32 [n_rows, d_ff], h to MXFP8 (hq, hs), then down
+// into out fp32 [n_rows, d], rows in perm order.  n_rows = offsets[g_end]: rows
+// [0, n_rows) of h are converted (those before offsets[g_begin] are not used).
+int launch_mx_ffn_mfma(const uint16_t* x, int T, int d, int d_ff, int k, const uint8_t* slots,
+                       const int32_t* group_slot, const int32_t* offsets, const int32_t* perm, int g_begin, int g_end,
+                       int n_rows, uint8_t* xq, uint8_t* xs, float* h, uint8_t* hq, uint8_t* hs, float* out,
+                       void* stream, void* const* ev = nullptr);
+
 int launch_combine(const float* out, const int32_t* inv, const float* gates,
                    const float* cpu_partial, int T, int k, int d, float* y, void* stream);
 
@@ -58,7 +78,7 @@ struct CpuUse {
   float gate;
 };
 struct CpuExpert {
-  const uint16_t* rec;
+  const void* rec;  // one record in the context's format (FT_W_BF16 or FT_W_MXFP4)
   int32_t n_use;
   CpuUse use[64];
 };
@@ -68,8 +88,8 @@ CpuPool* cpu_pool_create(int threads);
 void cpu_pool_destroy(CpuPool*);
 int cpu_pool_threads(const CpuPool*);
 // Starts the work asynchronously; x is bf16 [T, d]; partial fp32 [T, d] is
-// overwritten (zeroed first).  Returns immediately.
-void cpu_pool_submit(CpuPool*, const uint16_t* x, int T, int d, int d_ff, const CpuExpert* ex,
+// overwritten (zeroed first); fmt is the records' ft_wfmt.  Returns immediately.
+void cpu_pool_submit(CpuPool*, const uint16_t* x, int T, int d, int d_ff, int fmt, const CpuExpert* ex,
                      int n_exp, float* partial);
 // Blocks until the submitted work is done (the caller works on it too).
 void cpu_pool_wait(CpuPool*);

@@ -31,7 +31,8 @@ EXPORTED = [
     "ft_strerror", "ft_last_error", "ft_record_bytes", "ft_workspace_bytes", "ft_frac_q16",
     "ft_qstar_split", "ft_pool_alloc", "ft_pool_free", "ft_bench_bw", "ft_create", "ft_destroy",
     "ft_get_stats", "ft_reset_stats", "ft_get_config", "ft_n_slots", "ft_router_topk",
-    "ft_permute_workspace_bytes", "ft_permute", "ft_grouped_ffn", "ft_combine",
+    "ft_permute_workspace_bytes", "ft_permute", "ft_grouped_ffn", "ft_grouped_ffn_mx_workspace_bytes",
+    "ft_grouped_ffn_mx", "ft_combine",
     "ft_expert_cache_lookup", "ft_expert_cache_fill", "ft_expert_cache_resize",
     "ft_expert_cache_where", "ft_moe_decode_layer", "ft_moe_prefill_begin", "ft_moe_prefill_layer",
     "ft_moe_prefill_end", "ft_prefill_slot", "ft_profile_enable", "ft_profile_read", "ft_host_experts",
@@ -117,6 +118,8 @@ def lib():
             "ft_permute_workspace_bytes": (C.c_size_t, [I, I]),
             "ft_permute": (C.c_int, [P, I, I, P, P, P, P, C.c_size_t, P]),
             "ft_grouped_ffn": (C.c_int, [P, I, I, I, I, P, P, P, P, I, I, I, I, P, P, I, P]),
+            "ft_grouped_ffn_mx_workspace_bytes": (C.c_size_t, [I, I, I, I]),
+            "ft_grouped_ffn_mx": (C.c_int, [P, I, I, I, I, P, P, P, P, I, I, I, I, I, P, C.c_size_t, P, I, P]),
             "ft_combine": (C.c_int, [P, P, P, P, I, I, I, P, P]),
             "ft_expert_cache_lookup": (C.c_int, [P, I, P, I, C.POINTER(ft_plan)]),
             "ft_expert_cache_fill": (C.c_int, [P, C.POINTER(ft_plan), P, P, P]),
@@ -129,7 +132,7 @@ def lib():
             "ft_prefill_slot": (I, [P, I, I]),
             "ft_profile_enable": (C.c_int, [P, I]),
             "ft_profile_read": (C.c_int, [P, C.POINTER(ft_profile)]),
-            "ft_host_experts": (C.c_int, [P, I, I, I, C.POINTER(P), P, P, P, I, I, P]),
+            "ft_host_experts": (C.c_int, [P, I, I, I, I, C.POINTER(P), P, P, P, I, I, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -271,16 +274,27 @@ def ft_grouped_ffn(x, T, d, d_ff, k, slots, group_slot, offsets, perm, n_groups,
         g_end, max_rows_per_group, _ptr(h_ws), _ptr(out), form, _stream(stream)))
 
 
+def ft_grouped_ffn_mx_workspace_bytes(T, d, d_ff, n_rows):
+    return lib().ft_grouped_ffn_mx_workspace_bytes(T, d, d_ff, n_rows)
+
+
+def ft_grouped_ffn_mx(x, T, d, d_ff, k, slots, group_slot, offsets, perm, n_groups, g_begin, g_end,
+                      max_rows_per_group, n_rows, workspace, workspace_bytes, out, form, stream=None):
+    return _check("ft_grouped_ffn_mx", lib().ft_grouped_ffn_mx(
+        _ptr(x), T, d, d_ff, k, _ptr(slots), _ptr(group_slot), _ptr(offsets), _ptr(perm), n_groups, g_begin,
+        g_end, max_rows_per_group, n_rows, _ptr(workspace), workspace_bytes, _ptr(out), form, _stream(stream)))
+
+
 def ft_combine(out, inv, gates, cpu_partial, T, k, d, y, stream=None):
     return _check("ft_combine", lib().ft_combine(_ptr(out), _ptr(inv), _ptr(gates), _ptr(cpu_partial), T, k, d,
                                                  _ptr(y), _stream(stream)))
 
 
-def ft_host_experts(x, T, d, d_ff, records, use_off, use_t, use_g, n_exp, threads, partial):
+def ft_host_experts(x, T, d, d_ff, records, use_off, use_t, use_g, n_exp, threads, partial, fmt=FT_W_BF16):
     """records: sequence of host addresses (or numpy arrays); other arrays numpy."""
     recs = (P * max(n_exp, 1))(*[_ptr(r) for r in records])
-    return _check("ft_host_experts", lib().ft_host_experts(_ptr(x), T, d, d_ff, recs, _ptr(use_off), _ptr(use_t),
-                                                           _ptr(use_g), n_exp, threads, _ptr(partial)))
+    return _check("ft_host_experts", lib().ft_host_experts(_ptr(x), T, d, d_ff, fmt, recs, _ptr(use_off),
+                                                           _ptr(use_t), _ptr(use_g), n_exp, threads, _ptr(partial)))
 
 
 def ft_expert_cache_lookup(ctx, layer, idx_host, T, plan=None):

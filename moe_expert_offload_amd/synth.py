@@ -40,6 +40,7 @@ class Shape:
     d: int
     d_ff: int
     k: int
+    mxfp4: bool = False  # expert records in MXFP4 (else bf16)
 
     @property
     def record_elems(self) -> int:
@@ -47,7 +48,11 @@ class Shape:
 
     @property
     def record_bytes(self) -> int:
-        return 2 * self.record_elems
+        return mxfp4_record_bytes(self.d, self.d_ff) if self.mxfp4 else 2 * self.record_elems
+
+    @property
+    def pool_dtype(self):
+        return np.uint8 if self.mxfp4 else np.uint16
 
 
 @dataclass(frozen=True)
@@ -80,8 +85,8 @@ WORKLOADS = {
     # prefill: 8192-token chunk through the c3 layer shape
     "c4": Workload("c4-prefill8k-L43-d4096-E256-top6", 4, Shape(43, 256, 4096, 2048, 6), 8192, 0.11),
     # the c3 shape with MXFP4 experts: 16384-token prefill (two 8192 chunks) and batch-1 decode
-    "c5": Workload("c5-mxfp4-L43-d4096-E256-top6", 5, Shape(43, 256, 4096, 2048, 6), 8192, 0.11),
-    "c5d": Workload("c5-mxfp4-decode-L43-d4096-E256-top6", 5, Shape(43, 256, 4096, 2048, 6), 1, 0.11),
+    "c5": Workload("c5-mxfp4-L43-d4096-E256-top6", 5, Shape(43, 256, 4096, 2048, 6, True), 8192, 0.11),
+    "c5d": Workload("c5-mxfp4-decode-L43-d4096-E256-top6", 5, Shape(43, 256, 4096, 2048, 6, True), 1, 0.11),
 }
 
 

@@ -132,13 +132,24 @@ def act_block_index(n):
     return np.arange(n).reshape(n // 32, 32)
 
 
+def quantize_act_codes(v):
+    """MXFP8 E4M3 conversion of activation rows v [rows, n]: (element codes uint8
+    [rows, n], E8M0 scale codes uint8 [rows, n // 32])."""
+    v = np.atleast_2d(np.asarray(v, np.float64))
+    blocks = act_block_index(v.shape[1])
+    s, c = quantize_blocks(v[:, blocks], "e4m3")
+    codes = np.empty(v.shape, np.uint8)
+    codes[:, blocks] = c
+    return codes, s
+
+
 def quantize_act(v):
     """MXFP8 E4M3 quantisation of activation rows v [rows, n] -> dequantised fp64 values."""
     v = np.atleast_2d(np.asarray(v, np.float64))
     blocks = act_block_index(v.shape[1])
-    s, c = quantize_blocks(v[:, blocks], "e4m3")
+    c, s = quantize_act_codes(v)
     out = np.empty_like(v)
-    out[:, blocks] = e8m0_value(s)[..., None] * e4m3_value(c)
+    out[:, blocks] = e8m0_value(s)[..., None] * e4m3_value(c[:, blocks])
     return out
 
 

@@ -9,7 +9,7 @@ import numpy as np
 
 from moe_expert_offload_amd import ft
 from moe_expert_offload_amd.pool import HostPool
-from moe_expert_offload_amd.synth import Shape, fill_records_torch
+from moe_expert_offload_amd.synth import Shape, fill_mxfp4_records_torch, fill_records_torch
 
 
 def torch_mod():
@@ -33,14 +33,18 @@ def host(t):
 
 
 class PinnedPool(HostPool):
-    """A pinned host pool of expert records, viewed as uint16 [rows, record_elems]."""
+    """A pinned host pool of expert records: uint16 [rows, record_elems] (bf16) or
+    uint8 [rows, record_bytes] (MXFP4)."""
 
     def __init__(self, shape: Shape, rows: int):
-        super().__init__(shape.record_elems, rows)
+        super().__init__(rows, shape.record_bytes, shape.pool_dtype)
         self.shape = shape
 
     def fill_device_random(self, config_id: int, seed: int = 0):
-        fill_records_torch(self.view, config_id, seed)
+        if self.shape.mxfp4:
+            fill_mxfp4_records_torch(self.view, self.shape.d, self.shape.d_ff, config_id, seed)
+        else:
+            fill_records_torch(self.view, config_id, seed)
 
 
 class Engine:
@@ -50,7 +54,8 @@ class Engine:
                  min_fill=1, max_fetch=-1, cpu_threads=0, prefill_overlap=0, L_phys=0):
         torch = torch_mod()
         self.shape = shape
-        self.fshape = ft.make_shape(shape.L, shape.E, shape.d, shape.d_ff, shape.k)
+        self.fshape = ft.make_shape(shape.L, shape.E, shape.d, shape.d_ff, shape.k,
+                                    ft.FT_W_MXFP4 if shape.mxfp4 else ft.FT_W_BF16)
         self.cfg = ft.make_config(frac_q16, min_fill, max_fetch, cpu_threads, prefill_overlap, T_max, L_phys)
         S = shape.record_bytes
         self.slots = torch.empty(max(n_slots, 1) * S, dtype=torch.uint8, device="cuda")

@@ -145,9 +145,15 @@ def test_error_codes():
     with pytest.raises(ft.FtError) as ei:
         ft.ft_create(ft.make_shape(4, 16, 60, 64, 2), ft.make_config(), n_slots=8)
     assert ei.value.status == ft.FT_EINVAL
+    with pytest.raises(ft.FtError) as ei:  # MXFP4 needs d and d_ff multiples of 128
+        ft.ft_create(ft.make_shape(4, 16, 64, 128, 2, ft.FT_W_MXFP4), ft.make_config(), n_slots=8)
+    assert ei.value.status == ft.FT_EINVAL
     with pytest.raises(ft.FtError) as ei:
-        ft.ft_create(ft.make_shape(4, 16, 64, 64, 2, ft.FT_W_MXFP4), ft.make_config(), n_slots=8)
+        ft.ft_create(ft.make_shape(4, 16, 64, 64, 2, 7), ft.make_config(), n_slots=8)
     assert ei.value.status == ft.FT_EUNSUPPORTED
+    mxs = ft.make_shape(4, 16, 256, 384, 2, ft.FT_W_MXFP4)
+    assert ft.ft_record_bytes(mxs) == 3 * 256 * 384 // 2 + 3 * 256 * 384 // 32
+    ft.ft_destroy(ft.ft_create(mxs, ft.make_config(), n_slots=8))
     ctx = ft.ft_create(shape, ft.make_config(), n_slots=8)
     try:
         with pytest.raises(ft.FtError):  # routed id out of range
@@ -189,3 +195,34 @@ def test_host_expert_kernel_matches_oracle(T, d, d_ff, uses, threads):
             ref[use_t[u]] += float(use_g[u]) * expert_ffn(W, x64[use_t[u]:use_t[u] + 1])[0]
     ok, mx, l1 = within_tolerance(partial, ref, 1e-4, 1e-5)
     assert ok, (mx, l1)
+
+
+@pytest.mark.parametrize("T,d,d_ff,uses,threads", [
+    (1, 256, 512, [[0], [0]], 3),
+    (8, 384, 128, [[0, 3, 7], [2], [1, 2, 3, 4, 5, 6, 7, 0]], 4),
+    (2, 2048, 768, [[0, 1]], 0),
+])
+def test_host_expert_kernel_mxfp4_matches_oracle(T, d, d_ff, uses, threads):
+    """The CPU branch over MXFP4 records (in-kernel dequantisation) against the oracle's
+    exact dequantisation with bf16 activations."""
+    from moe_expert_offload_amd.synth import f32_to_bf16_bits, generator, mxfp4_record_from_weights
+    from oracle import mx
+    from oracle.common import bf16_to_f64, within_tolerance
+    rng = generator(51, T, d, d_ff)
+    n_exp = len(uses)
+    recs = [mxfp4_record_from_weights(rng.normal(0, 0.02, (d_ff, d)), rng.normal(0, 0.02, (d_ff, d)),
+                                      rng.normal(0, 0.02, (d, d_ff))) for _ in range(n_exp)]
+    x = f32_to_bf16_bits(rng.normal(0, 1, (T, d)))
+    use_off = np.cumsum([0] + [len(u) for u in uses]).astype(np.int32)
+    use_t = np.array([t for u in uses for t in u], np.int32)
+    use_g = rng.random(use_t.size).astype(np.float32)
+    partial = np.full((T, d), np.nan, np.float32)
+    ft.ft_host_experts(x, T, d, d_ff, recs, use_off, use_t, use_g, n_exp, threads, partial, fmt=ft.FT_W_MXFP4)
+    ref = np.zeros((T, d))
+    x64 = bf16_to_f64(x)
+    for i in range(n_exp):
+        W = mx.split_record(recs[i], d, d_ff)
+        for u in range(use_off[i], use_off[i + 1]):
+            ref[use_t[u]] += float(use_g[u]) * mx.expert_ffn_decode(W, x64[use_t[u]:use_t[u] + 1])[0]
+    ok, mxe, l1 = within_tolerance(partial, ref, 1e-4, 1e-5)
+    assert ok, (mxe, l1)
