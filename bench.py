@@ -13,6 +13,9 @@ before the timed region starts.
 
 Also measured (unless --no-prefill): one 8192-token prefill chunk through the
 43-layer d=4096, E=256, top-6, d_ff=2048 shape with full-layer double buffering.
+And (unless --no-mxfp4) the same shape with MXFP4 experts: a 16384-token prefill
+as two 8192-token chunks on the scaled MFMA, then batch-1 decode over a 512-step
+trace with the cache resized from 1210 to 605 slots at step 256 (a safe point).
 
 Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
 """
@@ -34,6 +37,7 @@ if ROOT not in sys.path:
 METRIC = "MoE decode tok/s + 8k-token prefill tok/s (DSV4 shape); % of HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published (E4M3 x E2M1 runs at the fp8 rate)
 
 
 def log(*a):
@@ -269,6 +273,129 @@ def run_prefill(args, torch, ft, synth, HostPool):
     }
 
 
+def run_mxfp4(args, torch, ft, synth, HostPool):
+    """MXFP4 experts at the 43-layer d=4096 shape: 2 x 8192-token prefill chunks, then
+    batch-1 decode over a trace with a resize at a safe point."""
+    wl, wd = synth.WORKLOADS["c5"], synth.WORKLOADS["c5d"]
+    s = wl.shape
+    S = s.record_bytes
+    T = wl.T
+    L_phys = s.L if args.mx_l_phys <= 0 else min(args.mx_l_phys, s.L)
+    log(f"mxfp4 workload {wl.name}: pool {L_phys * s.E} records x {S / 1e6:.2f} MB = {L_phys * s.E * S / 1e9:.1f} GB")
+    t = time.time()
+    pool = HostPool(L_phys * s.E, S, s.pool_dtype)
+    try:
+        synth.fill_mxfp4_records_torch(pool.view, s.d, s.d_ff, wl.config_id, seed=args.seed)
+        log(f"pool allocated and filled in {time.time() - t:.1f} s")
+        fshape = ft.make_shape(s.L, s.E, s.d, s.d_ff, s.k, ft.FT_W_MXFP4)
+        scratch = torch.empty(64 * S, dtype=torch.uint8, device="cuda")
+        B_P, B_H = ft.ft_bench_bw(fshape, pool.ptr, 64, scratch, 0)
+        del scratch
+        fq = ft.ft_frac_q16(B_P, B_H) if args.frac_q16 < 0 else args.frac_q16
+        log(f"mxfp4 B_P {B_P / 1e9:.1f} GB/s, B_H {B_H / 1e9:.1f} GB/s, frac_q16 {fq}")
+        N, N2 = wl.n_slots, wl.n_slots // 2
+        cfg = ft.make_config(frac_q16=fq, min_fill=args.min_fill, max_fetch=-1, cpu_threads=args.cpu_threads,
+                             prefill_overlap=1, T_max=T, L_phys=L_phys)
+        slots = torch.empty(N * S, dtype=torch.uint8, device="cuda")
+        wsb = ft.ft_workspace_bytes(fshape, T)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        wr = [torch.from_numpy(synth.router_weights(wl, l, seed=args.seed).view(np.int16)).cuda() for l in range(s.L)]
+        n_chunks = 2
+        xs = [[synth.tokens_torch(wl.config_id, c, l, T, s.d, seed=args.seed) for l in range(s.L)]
+              for c in range(n_chunks)]
+        y = torch.empty((T, s.d), dtype=torch.float32, device="cuda")
+        steps = args.mx_steps
+        tr = synth.trace_for(wd, seed=args.seed, steps=steps)
+        allowed = np.zeros((steps, s.L, 1, s.E), dtype=np.uint8)
+        st_i, l_i = np.meshgrid(np.arange(steps), np.arange(s.L), indexing="ij")
+        for j in range(s.k):
+            allowed[st_i, l_i, 0, tr[:, :, 0, j].astype(np.int64)] = 1
+        allowed_d = torch.from_numpy(allowed).cuda()
+        xh = np.stack([np.stack([synth.tokens(wd, st, l, T=1, seed=args.seed) for l in range(s.L)])
+                       for st in range(steps)])
+        xd = torch.from_numpy(xh.view(np.int16)).cuda()
+        yd = torch.empty((s.L, 1, s.d), dtype=torch.float32, device="cuda")
+        ctx = ft.ft_create(fshape, cfg, pool.ptr, pool.nbytes, slots, N, ws, wsb)
+        compute = torch.cuda.current_stream()
+        copy = torch.cuda.Stream()
+        try:
+            ft.ft_moe_prefill_begin(ctx, copy)  # warm-up: two layers of one chunk
+            for l in range(2):
+                ft.ft_moe_prefill_layer(ctx, l, xs[0][l], T, wr[l], y, compute, copy)
+            ft.ft_moe_prefill_end(ctx)
+            torch.cuda.synchronize()
+            ft.ft_profile_enable(ctx, True)
+            t0 = time.perf_counter()
+            for c in range(n_chunks):
+                ft.ft_moe_prefill_begin(ctx, copy)
+                for l in range(s.L):
+                    ft.ft_moe_prefill_layer(ctx, l, xs[c][l], T, wr[l], y, compute, copy)
+                ft.ft_moe_prefill_end(ctx)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            pprof = ft.ft_profile_read(ctx)
+            ft.ft_profile_enable(ctx, False)
+            del xs
+            ft.ft_reset_stats(ctx)
+            st_call = ft.ft_step_stats()
+            seg = []
+            for half in range(2):
+                if half == 1:
+                    torch.cuda.synchronize()
+                    tr0 = time.perf_counter()
+                    rc = ft.ft_expert_cache_resize(ctx, slots, N2)  # same buffer, half the slots
+                    t_resize = time.perf_counter() - tr0
+                    assert rc == ft.FT_OK, rc
+                ft.ft_profile_enable(ctx, True)
+                ta = time.perf_counter()
+                for st in range(half * steps // 2, (half + 1) * steps // 2):
+                    for l in range(s.L):
+                        ft.ft_moe_decode_layer(ctx, l, xd[st, l], 1, wr[l], allowed_d[st, l], yd[l], compute, copy,
+                                               None, st_call)
+                torch.cuda.synchronize()
+                tb = time.perf_counter()
+                seg.append((tb - ta, ft.ft_get_stats(ctx), ft.ft_profile_read(ctx)))
+                ft.ft_profile_enable(ctx, False)
+        finally:
+            ft.ft_destroy(ctx)
+    finally:
+        pool.free()
+    el_pf = t1 - t0
+    ms_pf = pprof["ms_gateup"] + pprof["ms_down"]
+    fl_pf = pprof["flops_gateup"] + pprof["flops_down"]
+    tf_gu = pprof["flops_gateup"] / (pprof["ms_gateup"] * 1e-3) / 1e12 if pprof["ms_gateup"] > 0 else 0.0
+    tf_dn = pprof["flops_down"] / (pprof["ms_down"] * 1e-3) / 1e12 if pprof["ms_down"] > 0 else 0.0
+    tf = fl_pf / (ms_pf * 1e-3) / 1e12 if ms_pf > 0 else 0.0
+    dec_el = seg[0][0] + seg[1][0]
+    dprof = {k: seg[0][2][k] + seg[1][2][k] for k in seg[0][2]}
+    gu_gbs = dprof["bytes_gateup"] / (dprof["ms_gateup"] * 1e-3) / 1e9 if dprof["ms_gateup"] > 0 else 0.0
+
+    def seg_info(i, n_slots):
+        el, st, _ = seg[i]
+        reads = max(st["reads"], 1)
+        return {"n_slots": n_slots, "steps": steps // 2, "tok_s": (steps // 2) / el, "ms_per_step": el / (steps // 2) * 1e3,
+                "miss_rate_reads": 1.0 - st["read_hits"] / reads, "fills_per_step": st["fills"] / (steps // 2),
+                "cpu_experts_per_step": st["cpu_experts"] / (steps // 2)}
+
+    return {
+        "workload": wl.name, "record_MB": S / 1e6, "L": s.L, "L_phys": L_phys, "B_P_GBs": B_P / 1e9,
+        "B_H_GBs": B_H / 1e9, "frac_q16": fq,
+        "prefill": {"tokens": n_chunks * T, "chunks": n_chunks, "tok_s": n_chunks * T / el_pf,
+                    "s_per_chunk": el_pf / n_chunks, "h2d_GB": n_chunks * s.L * s.E * S / 1e9,
+                    "h2d_GBs_effective": n_chunks * s.L * s.E * S / el_pf / 1e9,
+                    "ffn_ms_per_layer": ms_pf / max(pprof["launches"], 1),
+                    "mx_mfma": {"TFLOPs": round(tf, 1), "gateup_TFLOPs": round(tf_gu, 1),
+                                "down_TFLOPs": round(tf_dn, 1), "peak_TFLOPs": MFMA_FP8_PEAK_TFLOPS,
+                                "frac": round(tf / MFMA_FP8_PEAK_TFLOPS, 4),
+                                "note": "E4M3 x E2M1 scaled MFMA; times exclude the MXFP8 conversion kernels"}},
+        "decode": {"steps": steps, "tok_s": steps / dec_el, "ms_per_step": dec_el / steps * 1e3,
+                   "resize_at_step": steps // 2, "resize_ms": t_resize * 1e3,
+                   "before_resize": seg_info(0, N), "after_resize": seg_info(1, N2),
+                   "mx_gateup_rows": {"GBs": round(gu_gbs, 1), "frac_of_hbm_peak": round(gu_gbs / HBM_PEAK_GBS, 4),
+                                      "avg_us": dprof["ms_gateup"] / max(dprof["launches"], 1) * 1e3}},
+    }
+
+
 def cpu_baseline(args, pool, wl, tr, fq, L_phys, budget_s):
     """The oracle as it stands, timed on the host over the first steps of the same trace."""
     from threadpoolctl import threadpool_info
@@ -317,6 +444,11 @@ def main():
     ap.add_argument("--prefill", dest="prefill", action="store_true", default=True)
     ap.add_argument("--no-prefill", dest="prefill", action="store_false")
     ap.add_argument("--prefill-l-phys", type=int, default=2)
+    ap.add_argument("--mxfp4", dest="mxfp4", action="store_true", default=True)
+    ap.add_argument("--no-mxfp4", dest="mxfp4", action="store_false")
+    ap.add_argument("--mx-l-phys", type=int, default=16,
+                    help="physical layers of the MXFP4 pool (0 = all; pinned memory is capped near half of host RAM)")
+    ap.add_argument("--mx-steps", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     args = ap.parse_args()
@@ -342,6 +474,7 @@ def main():
     finally:
         pool.free()
     pre = run_prefill(args, torch, ft, synth, HostPool) if args.prefill else None
+    mxr = run_mxfp4(args, torch, ft, synth, HostPool) if args.mxfp4 else None
     out = {
         "metric": METRIC, "value": round(dec["tok_s"], 3), "unit": "tok/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dec["ms_per_step"], 4),
@@ -349,7 +482,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": dec["workload"], "global_batch": dec["T"], "layers": dec["L"],
                    "cache_slots": dec["n_slots"], "parallelism": "single-gpu"},
-        "roofline": roof, "cpu_baseline": cpu, "decode": dec, "prefill": pre,
+        "roofline": roof, "cpu_baseline": cpu, "decode": dec, "prefill": pre, "mxfp4": mxr,
     }
     print(json.dumps(out), flush=True)
 
