@@ -79,7 +79,7 @@ typedef enum { FT_W_BF16 = 0, FT_W_MXFP4 = 1 } ft_wfmt;
 
 /* Layer-stack shape.  L layers, E routed experts per layer, hidden size d,
  * expert hidden size d_ff, k experts per token.  d and d_ff must be multiples of 8
- * (FT_W_BF16) or of 128 (FT_W_MXFP4). */
+ * (FT_W_BF16); FT_W_MXFP4 needs d % 256 == 0 and d_ff % 128 == 0. */
 typedef struct {
   int32_t L, E, d, d_ff, k;
   int32_t fmt; /* ft_wfmt: expert record format */
@@ -244,7 +244,7 @@ int ft_permute(const int32_t* key, int32_t P, int32_t n_groups, int32_t* offsets
  * x: device bf16 [T, d]; out: device fp32 [offsets[n_groups], d] (rows in perm
  * order); h_ws: device, offsets[n_groups] * d_ff * 4 bytes.  form: 0 auto, 1 the
  * bandwidth-bound row-streaming form (few tokens per expert), 2 the MFMA tile form
- * (many tokens per expert). */
+ * (many tokens per expert; needs d % 256 == 0 and d_ff % 128 == 0). */
 int ft_grouped_ffn(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t k,
                    const void* slots, const int32_t* group_slot, const int32_t* offsets,
                    const int32_t* perm, int32_t n_groups, int32_t g_begin, int32_t g_end,
@@ -255,12 +255,14 @@ int ft_grouped_ffn(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t k,
  * MXFP4; §4.1 dequantisation inside the kernels).  form 1: row-streaming, exactly
  * dequantised weights applied to the bf16 x (the decode form); form 2: scaled MFMA,
  * x and h converted to MXFP8 first (the prefill form; see "MXFP4 arithmetic" above).
- * d % 128 == 0 and d_ff % 128 == 0.  n_rows = offsets[n_groups] (rows of out).
+ * form 1 needs d, d_ff % 64 == 0, form 2 d % 256 == 0 and d_ff % 128 == 0.
+ * n_rows = offsets[n_groups] (rows of out).
  * workspace: device, at least ft_grouped_ffn_mx_workspace_bytes(T, d, d_ff, n_rows)
  * bytes, 256-byte aligned; FT_ENOMEM when smaller.  It holds, each part starting at
  * a 256-byte boundary: h fp32 [n_rows, d_ff]; x in MXFP8, codes [T, d] then scales
  * [T, d/32]; h in MXFP8, codes [n_rows, d_ff] then scales [n_rows, d_ff/32]
- * (form 1 uses h only).  These are readable after the call. */
+ * (form 1 writes h fp32 only; form 2 writes the two MXFP8 parts only, converting
+ * h inside the gate/up kernel).  These are readable after the call. */
 size_t ft_grouped_ffn_mx_workspace_bytes(int32_t T, int32_t d, int32_t d_ff, int32_t n_rows);
 int ft_grouped_ffn_mx(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t k,
                       const void* slots, const int32_t* group_slot, const int32_t* offsets,

@@ -71,7 +71,7 @@ bool shape_ok(const ft_shape* s) {
       s->k < 1 || s->k > 8 || s->k > s->E)
     return false;
   if (s->fmt == FT_W_BF16) return true;
-  return s->fmt == FT_W_MXFP4 && s->d % 128 == 0 && s->d_ff % 128 == 0;
+  return s->fmt == FT_W_MXFP4 && s->d % 256 == 0 && s->d_ff % 128 == 0;
 }
 
 bool is_mx(const ft_shape* s) { return s->fmt == FT_W_MXFP4; }
@@ -414,10 +414,10 @@ int ft_grouped_ffn(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t k,
                    int32_t n_groups, int32_t g_begin, int32_t g_end, int32_t max_rows_per_group,
                    void* h_ws, float* out, int32_t form, void* stream) {
   if (T < 0 || g_begin < 0 || g_end > n_groups || g_begin > g_end) return fail(FT_EINVAL, "grouped_ffn: bad group range");
-  const bool mfma_ok = d % 128 == 0 && d_ff % 64 == 0;
+  const bool mfma_ok = d % 256 == 0 && d_ff % 128 == 0;
   if (form == 0) form = (mfma_ok && max_rows_per_group >= 32) ? 2 : 1;
   if (form == 2) {
-    if (!mfma_ok) return fail(FT_EINVAL, "grouped_ffn: MFMA form needs d%128==0 and d_ff%64==0");
+    if (!mfma_ok) return fail(FT_EINVAL, "grouped_ffn: MFMA form needs d%256==0 and d_ff%128==0");
     return ft::launch_ffn_mfma(static_cast<const uint16_t*>(x), d, d_ff, k, static_cast<const uint16_t*>(slots),
                                group_slot, offsets, perm, g_begin, g_end, max_rows_per_group,
                                static_cast<uint16_t*>(h_ws), out, stream);
@@ -439,7 +439,9 @@ int ft_grouped_ffn_mx(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t
                       int32_t g_begin, int32_t g_end, int32_t max_rows_per_group, int32_t n_rows, void* workspace,
                       size_t workspace_bytes, float* out, int32_t form, void* stream) {
   if (T < 0 || g_begin < 0 || g_end > n_groups || g_begin > g_end) return fail(FT_EINVAL, "grouped_ffn_mx: bad group range");
-  if (d <= 0 || d_ff <= 0 || d % 128 || d_ff % 128) return fail(FT_EINVAL, "grouped_ffn_mx: need d%128==0 and d_ff%128==0");
+  if (d <= 0 || d_ff <= 0 || d % 64 || d_ff % 64) return fail(FT_EINVAL, "grouped_ffn_mx: need d%64==0 and d_ff%64==0");
+  if (form == 2 && (d % 256 || d_ff % 128))
+    return fail(FT_EINVAL, "grouped_ffn_mx: the MFMA form needs d%256==0 and d_ff%128==0");
   if (n_rows < 0 || !workspace || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return fail(FT_EINVAL, "grouped_ffn_mx: need n_rows >= 0 and a 256-byte aligned workspace");
   if (workspace_bytes < ft_grouped_ffn_mx_workspace_bytes(T, d, d_ff, n_rows))
@@ -763,7 +765,7 @@ int ft_moe_prefill_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, co
   if (int rc = ft::launch_permute(d_idx, P, E, d_off, d_perm, d_inv, c->ws + c->cv.pws, c->cv.pws_bytes, cs))
     return rc;
   const uint16_t* xs = static_cast<const uint16_t*>(x);
-  const bool mfma = d % 128 == 0 && d_ff % 64 == 0;
+  const bool mfma = d % 256 == 0 && d_ff % 128 == 0;
   ft_ctx::ProfRec* r = prof_begin(c);
   void* const* evs = r ? reinterpret_cast<void* const*>(r->ev) : nullptr;
   const uint16_t* slots16 = reinterpret_cast<const uint16_t*>(c->slots);

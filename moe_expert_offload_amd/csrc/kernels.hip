@@ -559,202 +559,227 @@ __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
 // A[l%32][(l/32)*8 .. +7] and B^T[l%32][(l/32)*8 .. +7]; accumulator element v
 // of lane l is C[(v/4)*8 + (l/32)*4 + v%4][l%32].
 //
-// Block: 512 threads = 8 waves (4 along M x 2 along N); tile of up to 256 rows
-// of one expert (all its tokens in one pass for the usual ~200) and one column
-// tile of the weight; K staged through LDS in steps of 64 with the next step
-// prefetched into registers.  A weight tile is read from HBM once per expert.
-constexpr int TBM = 256;
-constexpr int TBK = 64;
-constexpr int LDK = TBK + 8;  // padded LDS row, in bf16 elements
+// Block: 256 threads = 4 waves, one per SIMD.  One pass covers up to 256 rows of
+// one expert (8 row subtiles of 32; the usual ~200 tokens of an 8k chunk in one
+// pass) and a column strip per wave: every weight element is read from HBM once
+// per pass, straight into the registers of the one wave that uses it.  Token rows
+// (operand A) are staged through LDS, double-buffered, and shared by the 4 waves.
+// K runs in stages of 64; inside a stage, MFMA i (0..3) takes in lane group g the
+// elements 32g + 8i .. +7, so a lane's weight data for a stage is 64 contiguous
+// bytes and A is read from LDS in the same order (the sum over k is unchanged).
+constexpr int XM = 256;       // rows per pass
+constexpr int XK = 64;        // K elements per stage
+constexpr int XLD = XK + 8;   // padded LDS row, in bf16 elements (144 B)
 
 __device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* p) {
   const uint4 u = *reinterpret_cast<const uint4*>(p);
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-// h[i][n0 + c] = silu(sum_k x[t_i][k] Wg[n0+c][k]) * (sum_k x[t_i][k] Wu[n0+c][k]),
-// column tile of 64 (each N-wave owns 32 gate and the same 32 up columns).
-__global__ __launch_bounds__(512) void ffn_gateup_mfma_kernel(
-    const uint16_t* __restrict__ x, int d, int d_ff, int k, const uint16_t* __restrict__ slots,
-    size_t rec_elems, const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ perm, int g_begin, int n_tiles, int n_blocks,
-    uint16_t* __restrict__ h) {
-  __shared__ __attribute__((aligned(16))) uint16_t sX[TBM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[128 * LDK];
-  const int lb = xcd_logical_block(blockIdx.x, n_blocks);
-  const int g = g_begin + lb / n_tiles;
-  const int n0 = (lb % n_tiles) * 64;
-  const int r0 = offsets[g];
-  const int n = offsets[g + 1] - r0;
-  if (n <= 0) return;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const uint16_t* rec = slots + (size_t)group_slot[g] * rec_elems;
-  // this thread's two weight chunks per stage: rows 0..63 gate, 64..127 up
-  const uint16_t* wrow[2];
-  int wlds[2];
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// Token-row staging of one stage: thread tid copies 16 B pieces (row tid/8 + 32j,
+// part tid%8) for j = 0..7.  Rows past the group's end read a valid row instead
+// (their products land in output rows that are never stored), so every load is
+// unconditional and the compiler can count outstanding loads exactly.
+struct RowStage {
+  const uint16_t* src[8];
+  uint4 v[8];
+  __device__ __forceinline__ void load(int k0) {
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int ch = tid + c * 512;
-    const int r = ch >> 3, c8 = ch & 7;
-    wrow[c] = (r < 64 ? rec + (size_t)(n0 + r) * d : rec + (size_t)d_ff * d + (size_t)(n0 + r - 64) * d) + c8 * 8;
-    wlds[c] = r * LDK + c8 * 8;
+    for (int j = 0; j < 8; ++j) v[j] = ld16(src[j] + k0);
   }
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  for (int m0 = 0; m0 < n; m0 += TBM) {
-    const uint16_t* xrow[4];
-    int xlds[4];
+  __device__ __forceinline__ void store(uint16_t* buf, int tid) const {
+    uint16_t* dst = buf + (tid >> 3) * XLD + (tid & 7) * 8;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int ch = tid + c * 512;
-      const int r = ch >> 3, c8 = ch & 7;
-      xrow[c] = (m0 + r < n) ? x + (size_t)(perm[r0 + m0 + r] / k) * d + c8 * 8 : nullptr;
-      xlds[c] = r * LDK + c8 * 8;
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(dst + 32 * j * XLD) = v[j];
+  }
+};
+
+// acc[a][c] += A(subtile a) x B(column subtile c) over one 64-element stage; w holds
+// the lane's 4 pieces for column subtile 0 then 4 for column subtile 1.  The A
+// fragments of K slice i + 1 are read from LDS while slice i multiplies.
+template <int NSUB>
+__device__ __forceinline__ void mfma_stage_bf16(f32x16_t (&acc)[8][2], const uint4 (&w)[8], const uint16_t* sx,
+                                                int lane) {
+  const int grp = lane >> 5;
+  const uint16_t* arow = sx + (lane & 31) * XLD + grp * 32;
+  bf16x8_t fa[2][NSUB];
+#pragma unroll
+  for (int a = 0; a < NSUB; ++a) fa[0][a] = lds_frag(arow + a * 32 * XLD);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < 3) {
+#pragma unroll
+      for (int a = 0; a < NSUB; ++a) fa[(i + 1) & 1][a] = lds_frag(arow + a * 32 * XLD + 8 * (i + 1));
     }
-    const bool wave_active = (m0 + wm * 64) < n;
-    f32x16_t acc[4];
+    const bf16x8_t b0 = as_bf16x8(w[i]);
+    const bf16x8_t b1 = as_bf16x8(w[4 + i]);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][v] = 0.0f;
-    uint4 px[4], pw[2];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) px[c] = xrow[c] ? ld16(xrow[c]) : zero;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) pw[c] = ld16(wrow[c]);
-    for (int k0 = 0; k0 < d; k0 += TBK) {
-      __syncthreads();
-#pragma unroll
-      for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(&sX[xlds[c]]) = px[c];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) *reinterpret_cast<uint4*>(&sW[wlds[c]]) = pw[c];
-      __syncthreads();
-      if (k0 + TBK < d) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) px[c] = xrow[c] ? ld16(xrow[c] + k0 + TBK) : zero;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) pw[c] = ld16(wrow[c] + k0 + TBK);
-      }
-      if (wave_active) {
-#pragma unroll
-        for (int kk = 0; kk < TBK; kk += 16) {
-          const int kc = kk + (lane >> 5) * 8;
-          const bf16x8_t a0 = lds_frag(&sX[(wm * 64 + (lane & 31)) * LDK + kc]);
-          const bf16x8_t a1 = lds_frag(&sX[(wm * 64 + 32 + (lane & 31)) * LDK + kc]);
-          const bf16x8_t bg = lds_frag(&sW[(wn * 32 + (lane & 31)) * LDK + kc]);
-          const bf16x8_t bu = lds_frag(&sW[(64 + wn * 32 + (lane & 31)) * LDK + kc]);
-          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bg, acc[0], 0, 0, 0);
-          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bg, acc[1], 0, 0, 0);
-          acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bu, acc[2], 0, 0, 0);
-          acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bu, acc[3], 0, 0, 0);
-        }
-      }
-    }
-    if (wave_active) {
-      const int col = n0 + wn * 32 + (lane & 31);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = m0 + wm * 64 + mb * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-          if (row < n) h[(size_t)(r0 + row) * d_ff + col] = f32_to_bf16_rne(silu(acc[mb][v]) * acc[2 + mb][v]);
-        }
+    for (int a = 0; a < NSUB; ++a) {
+      acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i & 1][a], b0, acc[a][0], 0, 0, 0);
+      acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i & 1][a], b1, acc[a][1], 0, 0, 0);
     }
   }
 }
 
-// out[i][n0 + c] = sum_r h[i][r] Wd[n0+c][r]; column tile of 128 (each N-wave 64).
-__global__ __launch_bounds__(512) void ffn_down_mfma_kernel(
-    int d, int d_ff, const uint16_t* __restrict__ slots, size_t rec_elems,
-    const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, int g_begin,
-    int n_tiles, int n_blocks, const uint16_t* __restrict__ h, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[TBM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[128 * LDK];
+__device__ __forceinline__ void load_w_stage(uint4 (&w)[8], const uint16_t* w0, const uint16_t* w1, int k0) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w[i] = ld16(w0 + k0 + 8 * i);
+    w[4 + i] = ld16(w1 + k0 + 8 * i);
+  }
+}
+
+// Runs the K loop of one pass (K = kdim, a multiple of 64) with A from `rs` and the
+// lane's weight rows w0, w1 (already offset by 32 * lane group), for NSUB row
+// subtiles.  Weights are prefetched four stages ahead (HBM latency under load is
+// a few stages of compute), token rows one stage ahead (they come from L2).
+// Prefetches past the last stage re-read the last stage (clamped) so the loop has
+// no conditional loads.
+template <int NSUB>
+__device__ __forceinline__ void mfma_pass_bf16(f32x16_t (&acc)[8][2], RowStage& rs, uint16_t (*sx)[XM * XLD],
+                                               const uint16_t* w0, const uint16_t* w1, int kdim, int tid,
+                                               int lane) {
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      acc[a][0][v] = 0.0f;
+      acc[a][1][v] = 0.0f;
+    }
+  // an opaque zero: the first weight loads of a pass would otherwise be hoisted out
+  // of the caller's row-pass loop and kept live (spilled) across it
+  int opaque = 0;
+  asm volatile("" : "+s"(opaque));
+  w0 += opaque;
+  w1 += opaque;
+  uint4 wr[4][8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) load_w_stage(wr[j], w0, w1, j * XK);
+  rs.load(0);
+  rs.store(sx[0], tid);
+  rs.load(XK);
+  __syncthreads();
+  const int klast = kdim - XK;
+  for (int k0 = 0; k0 < kdim; k0 += 4 * XK) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (k0 + j * XK >= kdim) break;
+      // stage k0 + j*XK: LDS buffer j&1, weights wr[j]; the next stage's rows go to
+      // the other buffer meanwhile
+      rs.store(sx[(j + 1) & 1], tid);
+      rs.load(min(k0 + (j + 2) * XK, klast));
+      mfma_stage_bf16<NSUB>(acc, wr[j], sx[j & 1], lane);
+      load_w_stage(wr[j], w0, w1, min(k0 + (j + 4) * XK, klast));
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ void mfma_pass_bf16_n(int nsub, f32x16_t (&acc)[8][2], RowStage& rs,
+                                                 uint16_t (*sx)[XM * XLD], const uint16_t* w0, const uint16_t* w1,
+                                                 int kdim, int tid, int lane) {
+  switch (nsub) {
+    case 1: mfma_pass_bf16<1>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
+    case 2: mfma_pass_bf16<2>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
+    case 3: mfma_pass_bf16<3>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
+    case 4: mfma_pass_bf16<4>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
+    case 5: mfma_pass_bf16<5>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
+    case 6: mfma_pass_bf16<6>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
+    case 7: mfma_pass_bf16<7>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
+    default: mfma_pass_bf16<8>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
+  }
+}
+
+// h[i][c] = silu(sum_k x[t_i][k] Wg[c][k]) * (sum_k x[t_i][k] Wu[c][k]) for the
+// 128 columns c of this block's strip (wave w: columns n0 + 32w .. +31 of both
+// W_gate and W_up), h in bf16.
+__global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(
+    const uint16_t* __restrict__ x, int d, int d_ff, int k, const uint16_t* __restrict__ slots,
+    size_t rec_elems, const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ perm, int g_begin, int n_tiles, int n_blocks,
+    uint16_t* __restrict__ h) {
+  __shared__ __attribute__((aligned(16))) uint16_t sX[2][XM * XLD];
   const int lb = xcd_logical_block(blockIdx.x, n_blocks);
   const int g = g_begin + lb / n_tiles;
   const int n0 = (lb % n_tiles) * 128;
   const int r0 = offsets[g];
   const int n = offsets[g + 1] - r0;
   if (n <= 0) return;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const uint16_t* wd = slots + (size_t)group_slot[g] * rec_elems + (size_t)2 * d_ff * d;
-  const uint16_t* wrow[2];
-  int wlds[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 5;
+  const uint16_t* rec = slots + (size_t)group_slot[g] * rec_elems;
+  const int col = n0 + wave * 32 + (lane & 31);
+  const uint16_t* wg = rec + (size_t)col * d + grp * 32;
+  const uint16_t* wu = rec + (size_t)d_ff * d + (size_t)col * d + grp * 32;
+  for (int m0 = 0; m0 < n; m0 += XM) {
+    const int rows = min(XM, n - m0);
+    const int nsub = (rows + 31) >> 5;
+    RowStage rs;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int ch = tid + c * 512;
-    const int r = ch >> 3, c8 = ch & 7;
-    wrow[c] = wd + (size_t)(n0 + r) * d_ff + c8 * 8;
-    wlds[c] = r * LDK + c8 * 8;
+    for (int j = 0; j < 8; ++j) {
+      const int r = min((tid >> 3) + 32 * j, rows - 1);
+      rs.src[j] = x + (size_t)(perm[r0 + m0 + r] / k) * d + (tid & 7) * 8;
+    }
+    f32x16_t acc[8][2];
+    mfma_pass_bf16_n(nsub, acc, rs, sX, wg, wu, d, tid, lane);
+    int g4 = grp * 4;
+    asm volatile("" : "+v"(g4));  // keeps the row indices below out of the prologue
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      if (a >= nsub) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = a * 32 + (v >> 2) * 8 + g4 + (v & 3);
+        if (row < rows)
+          h[(size_t)(r0 + m0 + row) * d_ff + col] = f32_to_bf16_rne(silu(acc[a][0][v]) * acc[a][1][v]);
+      }
+    }
   }
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  for (int m0 = 0; m0 < n; m0 += TBM) {
-    const uint16_t* arow[4];
-    int alds[4];
+}
+
+// out[i][c] = sum_r h[i][r] Wd[c][r] for the 256 columns of this block's strip
+// (wave w: columns n0 + 64w .. +63), h rows in perm order.
+__global__ __launch_bounds__(256) void ffn_down_mfma_kernel(
+    int d, int d_ff, const uint16_t* __restrict__ slots, size_t rec_elems,
+    const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, int g_begin,
+    int n_tiles, int n_blocks, const uint16_t* __restrict__ h, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t sX[2][XM * XLD];
+  const int lb = xcd_logical_block(blockIdx.x, n_blocks);
+  const int g = g_begin + lb / n_tiles;
+  const int n0 = (lb % n_tiles) * 256;
+  const int r0 = offsets[g];
+  const int n = offsets[g + 1] - r0;
+  if (n <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 5;
+  const uint16_t* wd = slots + (size_t)group_slot[g] * rec_elems + (size_t)2 * d_ff * d;
+  const int col = n0 + wave * 64 + (lane & 31);
+  const uint16_t* w0 = wd + (size_t)col * d_ff + grp * 32;
+  const uint16_t* w1 = w0 + (size_t)32 * d_ff;
+  for (int m0 = 0; m0 < n; m0 += XM) {
+    const int rows = min(XM, n - m0);
+    const int nsub = (rows + 31) >> 5;
+    RowStage rs;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int ch = tid + c * 512;
-      const int r = ch >> 3, c8 = ch & 7;
-      arow[c] = (m0 + r < n) ? h + (size_t)(r0 + m0 + r) * d_ff + c8 * 8 : nullptr;
-      alds[c] = r * LDK + c8 * 8;
+    for (int j = 0; j < 8; ++j) {
+      const int r = min((tid >> 3) + 32 * j, rows - 1);
+      rs.src[j] = h + (size_t)(r0 + m0 + r) * d_ff + (tid & 7) * 8;
     }
-    const bool wave_active = (m0 + wm * 64) < n;
-    f32x16_t acc[4];
+    f32x16_t acc[8][2];
+    mfma_pass_bf16_n(nsub, acc, rs, sX, w0, w1, d_ff, tid, lane);
+    int g4 = grp * 4;
+    asm volatile("" : "+v"(g4));  // keeps the row indices below out of the prologue
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a) {
+      if (a >= nsub) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][v] = 0.0f;
-    uint4 pa[4], pw[2];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) pa[c] = arow[c] ? ld16(arow[c]) : zero;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) pw[c] = ld16(wrow[c]);
-    for (int k0 = 0; k0 < d_ff; k0 += TBK) {
-      __syncthreads();
-#pragma unroll
-      for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(&sA[alds[c]]) = pa[c];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) *reinterpret_cast<uint4*>(&sW[wlds[c]]) = pw[c];
-      __syncthreads();
-      if (k0 + TBK < d_ff) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) pa[c] = arow[c] ? ld16(arow[c] + k0 + TBK) : zero;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) pw[c] = ld16(wrow[c] + k0 + TBK);
-      }
-      if (wave_active) {
-#pragma unroll
-        for (int kk = 0; kk < TBK; kk += 16) {
-          const int kc = kk + (lane >> 5) * 8;
-          const bf16x8_t a0 = lds_frag(&sA[(wm * 64 + (lane & 31)) * LDK + kc]);
-          const bf16x8_t a1 = lds_frag(&sA[(wm * 64 + 32 + (lane & 31)) * LDK + kc]);
-          const bf16x8_t b0 = lds_frag(&sW[(wn * 64 + (lane & 31)) * LDK + kc]);
-          const bf16x8_t b1 = lds_frag(&sW[(wn * 64 + 32 + (lane & 31)) * LDK + kc]);
-          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0], 0, 0, 0);
-          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1], 0, 0, 0);
-          acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[2], 0, 0, 0);
-          acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[3], 0, 0, 0);
+      for (int v = 0; v < 16; ++v) {
+        const int row = a * 32 + (v >> 2) * 8 + g4 + (v & 3);
+        if (row < rows) {
+          float* o = out + (size_t)(r0 + m0 + row) * d + col;
+          o[0] = acc[a][0][v];
+          o[32] = acc[a][1][v];
         }
-      }
-    }
-    if (wave_active) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int col = n0 + wn * 64 + nb * 32 + (lane & 31);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = m0 + wm * 64 + mb * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-            if (row < n) out[(size_t)(r0 + row) * d + col] = acc[nb * 2 + mb][v];
-          }
       }
     }
   }
@@ -916,22 +941,22 @@ int launch_ffn_mfma(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
                     const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
                     int g_begin, int g_end, int /*max_rows*/, uint16_t* h, float* out,
                     void* stream, void* const* ev) {
-  if (d % 128 != 0 || d_ff % 64 != 0 || k < 1)
-    return fail(FT_EINVAL, "ffn_mfma: need d%128==0 and d_ff%64==0");
+  if (d % 256 != 0 || d_ff % 128 != 0 || k < 1)
+    return fail(FT_EINVAL, "ffn_mfma: need d%256==0 and d_ff%128==0");
   const int ng = g_end - g_begin;
   if (ng <= 0) return FT_OK;
   if (!aligned16(x) || !aligned16(slots) || !aligned16(h) || !aligned16(out))
     return fail(FT_EINVAL, "ffn_mfma: unaligned pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t rec_elems = (size_t)3 * d * d_ff;
-  const int tiles_up = d_ff / 64;
+  const int tiles_up = d_ff / 128;
   const int nb_up = ng * tiles_up;
-  timed_launch(ffn_gateup_mfma_kernel, dim3(nb_up), dim3(512), s, ev, 0, x, d, d_ff, k, slots, rec_elems,
+  timed_launch(ffn_gateup_mfma_kernel, dim3(nb_up), dim3(256), s, ev, 0, x, d, d_ff, k, slots, rec_elems,
                group_slot, offsets, perm, g_begin, tiles_up, nb_up, h);
   if (int rc = launched("ffn_gateup_mfma")) return rc;
-  const int tiles_dn = d / 128;
+  const int tiles_dn = d / 256;
   const int nb_dn = ng * tiles_dn;
-  timed_launch(ffn_down_mfma_kernel, dim3(nb_dn), dim3(512), s, ev, 1, d, d_ff, slots, rec_elems, group_slot,
+  timed_launch(ffn_down_mfma_kernel, dim3(nb_dn), dim3(256), s, ev, 1, d, d_ff, slots, rec_elems, group_slot,
                offsets, g_begin, tiles_dn, nb_dn, (const uint16_t*)h, out);
   return launched("ffn_down_mfma");
 }

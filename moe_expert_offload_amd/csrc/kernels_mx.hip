@@ -265,234 +265,272 @@ __global__ __launch_bounds__(256) void mx_quant_act_kernel(const In* __restrict_
 }
 
 // ---- scaled-MFMA grouped FFN ---------------------------------------------------------
-// Tile: up to 256 rows of one expert x a column tile; 8 waves (4 along M x 2 along N);
-// K staged in steps of 128 (two MFMA steps) through LDS with register prefetch.
-constexpr int MTBM = 256;
-constexpr int MKB = 128;            // K elements per stage
-constexpr int ALD = MKB + 16;       // LDS bytes per A row (fp8, padded)
-constexpr int BLD = MKB / 2 + 16;   // LDS bytes per B row (fp4, padded)
+// Block: 256 threads = 4 waves, one per SIMD.  One pass covers up to 256 rows of one
+// expert (8 row subtiles of 32) and a column strip per wave, so every weight byte is
+// read from HBM once per pass, straight into the registers of the one wave that uses
+// it (prefetched four stages ahead).  Token rows (MXFP8 codes and their scales) are
+// staged through LDS, double-buffered, and shared by the 4 waves.
+// K runs in stages of 128 elements = two scaled MFMAs.  MFMA i (0, 1) of a stage
+// takes as its K positions 0..31 the stage's block i and as positions 32..63 its
+// block i + 2 (any pairing is exact as long as both operands and both scales follow
+// it); then a lane's E2M1 codes for a stage are 32 contiguous bytes per weight row.
+constexpr int QM = 256;        // rows per pass
+constexpr int QK = 128;        // K elements per stage
+constexpr int QLD = QK + 16;   // padded LDS row of fp8 codes (bytes)
 
 __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
   const int q = nb >> 3, r = nb & 7, x = b & 7;
   return x * q + (x < r ? x : r) + (b >> 3);
 }
 
-__device__ __forceinline__ v8i_t a_frag(const uint8_t* row, int ks, int grp) {
-  // bytes {64ks + 16g .. +15} and {64ks + 32 + 16g .. +15} of the staged row
-  const uint4 lo = *reinterpret_cast<const uint4*>(row + 64 * ks + 16 * grp);
-  const uint4 hi = *reinterpret_cast<const uint4*>(row + 64 * ks + 32 + 16 * grp);
-  v8i_t r;
-  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
-  return r;
+// Token-row staging of one stage: thread tid copies 16 B pieces (row tid/8 + 32j,
+// part tid%8) for j = 0..7, and the 4 scale bytes of row tid.  Rows past the group's
+// end read a valid row instead (their products land in rows that are never stored).
+struct QRowStage {
+  const uint8_t* src[8];
+  const uint8_t* ssrc;
+  uint4 v[8];
+  uint32_t sc;
+  __device__ __forceinline__ void load(int k0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const uint4*>(src[j] + k0);
+    sc = *reinterpret_cast<const uint32_t*>(ssrc + k0 / 32);
+  }
+  __device__ __forceinline__ void store(uint8_t* buf, uint32_t* sbuf, int tid) const {
+    uint8_t* dst = buf + (tid >> 3) * QLD + (tid & 7) * 16;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(dst + 32 * j * QLD) = v[j];
+    sbuf[tid] = sc;
+  }
+};
+
+// A lane's weights for one stage and two column subtiles: codes (2 x 16 B each) and
+// the 4 scale bytes of each of its two weight rows.
+struct QW {
+  uint4 c[4];   // [subtile 0: MFMA 0, 1][subtile 1: MFMA 0, 1]
+  uint32_t s[2];
+};
+
+__device__ __forceinline__ void load_qw(QW& w, const uint8_t* c0, const uint8_t* c1, const uint8_t* s0,
+                                        const uint8_t* s1, int k0) {
+  w.c[0] = *reinterpret_cast<const uint4*>(c0 + k0 / 2);
+  w.c[1] = *reinterpret_cast<const uint4*>(c0 + k0 / 2 + 16);
+  w.c[2] = *reinterpret_cast<const uint4*>(c1 + k0 / 2);
+  w.c[3] = *reinterpret_cast<const uint4*>(c1 + k0 / 2 + 16);
+  w.s[0] = *reinterpret_cast<const uint32_t*>(s0 + k0 / 32);
+  w.s[1] = *reinterpret_cast<const uint32_t*>(s1 + k0 / 32);
 }
 
-__device__ __forceinline__ v8i_t b_frag(const uint8_t* row, int ks, int grp) {
-  // 32 E2M1 codes = 16 bytes at K element 64ks + 32g
-  const uint4 v = *reinterpret_cast<const uint4*>(row + 32 * ks + 16 * grp);
+__device__ __forceinline__ v8i_t fp4_operand(uint4 c) {
   v8i_t r;
-  r[0] = (int)v.x; r[1] = (int)v.y; r[2] = (int)v.z; r[3] = (int)v.w;
+  r[0] = (int)c.x; r[1] = (int)c.y; r[2] = (int)c.z; r[3] = (int)c.w;
   r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
   return r;
 }
 
-// h[i][n0 + c] = silu(x_i . Wg[n0+c]) * (x_i . Wu[n0+c]) with x in MXFP8 (xq, xs) and
-// W in MXFP4; 64 columns per block (each N-wave 32 gate + the same 32 up columns).
-__global__ __launch_bounds__(512) void mx_gateup_mfma_kernel(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int d, int d_ff, int k,
-    const uint8_t* __restrict__ slots, const int32_t* __restrict__ group_slot,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, int g_begin, int n_tiles, int n_blocks,
-    float* __restrict__ h) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[MTBM * ALD];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[128 * BLD];
-  __shared__ uint32_t sAs[MTBM];   // 4 activation scales per row per stage
-  __shared__ uint32_t sBs[128];    // 4 weight scales per row per stage
-  const int lb = xcd_logical_block(blockIdx.x, n_blocks);
-  const int g = g_begin + lb / n_tiles;
-  const int n0 = (lb % n_tiles) * 64;
-  const int r0 = offsets[g];
-  const int n = offsets[g + 1] - r0;
-  if (n <= 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  const MxRec R = mx_rec(d, d_ff);
-  const uint8_t* rec = slots + (size_t)group_slot[g] * R.bytes;
-  // B: 128 rows (0..63 gate, 64..127 up) x 64 code bytes per stage: one 16-byte piece per thread
-  const int brow = tid >> 2, bq = tid & 3;
-  const uint8_t* bcode = rec + (brow < 64 ? R.g_codes + (size_t)(n0 + brow) * (d / 2)
-                                          : R.u_codes + (size_t)(n0 + brow - 64) * (d / 2)) + 16 * bq;
-  const uint8_t* bsc = rec + (brow < 64 ? R.g_sc + (size_t)(n0 + brow) * (d / 32)
-                                        : R.u_sc + (size_t)(n0 + brow - 64) * (d / 32));
-  for (int m0 = 0; m0 < n; m0 += MTBM) {
-    // A: 256 rows x 128 bytes per stage: four 16-byte pieces per thread (rows tid/8 + 64 i)
-    const uint8_t* arow[4];
-    const uint8_t* asrow[4];
+// acc[a][c] += A(subtile a) x B(column subtile c) over one 128-element stage.
+template <int NSUB>
+__device__ __forceinline__ void mx_mfma_stage(f32x16_t (&acc)[8][2], const QW& w, const uint8_t* sx,
+                                              const uint32_t* ss, int lane) {
+  const int grp = lane >> 5;
+  const uint8_t* arow = sx + (lane & 31) * QLD + 16 * grp;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 64 * i;
-      const bool in = m0 + r < n;
-      const size_t xr = in ? (size_t)(perm[r0 + m0 + r] / k) : 0;
-      arow[i] = in ? xq + xr * d + 16 * (tid & 7) : nullptr;
-      asrow[i] = in ? xs + xr * (d / 32) : nullptr;
-    }
-    const bool wave_active = (m0 + wm * 64) < n;
-    f32x16_t acc[4];
+  for (int i = 0; i < 2; ++i) {
+    const int blk = i + 2 * grp;  // stage block whose scale this lane group passes
+    const v8i_t b0 = fp4_operand(w.c[i]);
+    const v8i_t b1 = fp4_operand(w.c[2 + i]);
+    const int sb0 = (w.s[0] >> (8 * blk)) & 0xff, sb1 = (w.s[1] >> (8 * blk)) & 0xff;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][v] = 0.0f;
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    uint4 pa[4], pb;
-    uint32_t pas = 0, pbs = 0;
-    auto load_stage = [&](int k0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pa[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0) : zero;
-      pb = *reinterpret_cast<const uint4*>(bcode + k0 / 2);
-      // scales: threads 0..255 fetch 4 activation scales of row tid, 256..383 the weight scales
-      if (tid < 256) {
-        const int r = tid;
-        const bool in = m0 + r < n;
-        pas = in ? *reinterpret_cast<const uint32_t*>(xs + (size_t)(perm[r0 + m0 + r] / k) * (d / 32) + k0 / 32) : 0u;
-      } else if (tid < 384) {
-        const int r = tid - 256;
-        const uint8_t* sp = rec + (r < 64 ? R.g_sc + (size_t)(n0 + r) * (d / 32) : R.u_sc + (size_t)(n0 + r - 64) * (d / 32));
-        pbs = *reinterpret_cast<const uint32_t*>(sp + k0 / 32);
-      }
-    };
-    (void)asrow;
-    (void)bsc;
-    load_stage(0);
-    for (int k0 = 0; k0 < d; k0 += MKB) {
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sA[((tid >> 3) + 64 * i) * ALD + 16 * (tid & 7)]) = pa[i];
-      *reinterpret_cast<uint4*>(&sB[brow * BLD + 16 * bq]) = pb;
-      if (tid < 256) sAs[tid] = pas;
-      else if (tid < 384) sBs[tid - 256] = pbs;
-      __syncthreads();
-      if (k0 + MKB < d) load_stage(k0 + MKB);
-      if (wave_active) {
-        const int grp = lane >> 5;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int ra0 = wm * 64 + (lane & 31), ra1 = ra0 + 32;
-          const int rbg = wn * 32 + (lane & 31), rbu = 64 + rbg;
-          const v8i_t a0 = a_frag(&sA[ra0 * ALD], ks, grp);
-          const v8i_t a1 = a_frag(&sA[ra1 * ALD], ks, grp);
-          const v8i_t bg = b_frag(&sB[rbg * BLD], ks, grp);
-          const v8i_t bu = b_frag(&sB[rbu * BLD], ks, grp);
-          const int sh = 8 * (2 * ks + grp);
-          const int sa0 = (sAs[ra0] >> sh) & 0xff, sa1 = (sAs[ra1] >> sh) & 0xff;
-          const int sbg = (sBs[rbg] >> sh) & 0xff, sbu = (sBs[rbu] >> sh) & 0xff;
-          acc[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bg, acc[0], 0, 4, 0, sa0, 0, sbg);
-          acc[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bg, acc[1], 0, 4, 0, sa1, 0, sbg);
-          acc[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, bu, acc[2], 0, 4, 0, sa0, 0, sbu);
-          acc[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, bu, acc[3], 0, 4, 0, sa1, 0, sbu);
-        }
-      }
-    }
-    if (wave_active) {
-      const int col = n0 + wn * 32 + (lane & 31);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = m0 + wm * 64 + mb * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-          if (row < n) h[(size_t)(r0 + row) * d_ff + col] = silu(acc[mb][v]) * acc[2 + mb][v];
-        }
+    for (int a = 0; a < NSUB; ++a) {
+      const uint8_t* ap = arow + a * 32 * QLD + 32 * i;
+      const uint4 lo = *reinterpret_cast<const uint4*>(ap);
+      const uint4 hi = *reinterpret_cast<const uint4*>(ap + 64);
+      v8i_t af;
+      af[0] = (int)lo.x; af[1] = (int)lo.y; af[2] = (int)lo.z; af[3] = (int)lo.w;
+      af[4] = (int)hi.x; af[5] = (int)hi.y; af[6] = (int)hi.z; af[7] = (int)hi.w;
+      const int sa = (ss[a * 32 + (lane & 31)] >> (8 * blk)) & 0xff;
+      acc[a][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, b0, acc[a][0], 0, 4, 0, sa, 0, sb0);
+      acc[a][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, b1, acc[a][1], 0, 4, 0, sa, 0, sb1);
     }
   }
 }
 
-// out[i][n0 + c] = hq_i . Wd[n0+c] with h in MXFP8 (rows in perm order) and W in MXFP4;
-// 128 columns per block (each N-wave 64).
-__global__ __launch_bounds__(512) void mx_down_mfma_kernel(
-    const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, int d, int d_ff,
+// K loop of one pass (K = kdim, a multiple of 128).  Weight pointers are this lane's
+// two rows (codes already offset by 16 * lane group, scales at the row start).
+template <int NSUB>
+__device__ __forceinline__ void mx_mfma_pass(f32x16_t (&acc)[8][2], QRowStage& rs, uint8_t (*sx)[QM * QLD],
+                                             uint32_t (*ss)[QM], const uint8_t* c0, const uint8_t* c1,
+                                             const uint8_t* s0, const uint8_t* s1, int kdim, int tid, int lane) {
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      acc[a][0][v] = 0.0f;
+      acc[a][1][v] = 0.0f;
+    }
+  int opaque = 0;  // keeps the first weight loads inside the caller's row-pass loop
+  asm volatile("" : "+s"(opaque));
+  c0 += opaque;
+  c1 += opaque;
+  QW wr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) load_qw(wr[j], c0, c1, s0, s1, j * QK);
+  rs.load(0);
+  rs.store(sx[0], ss[0], tid);
+  rs.load(QK);
+  __syncthreads();
+  const int klast = kdim - QK;
+  for (int k0 = 0; k0 < kdim; k0 += 4 * QK) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (k0 + j * QK >= kdim) break;
+      rs.store(sx[(j + 1) & 1], ss[(j + 1) & 1], tid);
+      rs.load(min(k0 + (j + 2) * QK, klast));
+      mx_mfma_stage<NSUB>(acc, wr[j], sx[j & 1], ss[j & 1], lane);
+      load_qw(wr[j], c0, c1, s0, s1, min(k0 + (j + 4) * QK, klast));
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ void mx_mfma_pass_n(int nsub, f32x16_t (&acc)[8][2], QRowStage& rs,
+                                               uint8_t (*sx)[QM * QLD], uint32_t (*ss)[QM], const uint8_t* c0,
+                                               const uint8_t* c1, const uint8_t* s0, const uint8_t* s1, int kdim,
+                                               int tid, int lane) {
+  switch (nsub) {
+    case 1: mx_mfma_pass<1>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
+    case 2: mx_mfma_pass<2>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
+    case 3: mx_mfma_pass<3>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
+    case 4: mx_mfma_pass<4>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
+    case 5: mx_mfma_pass<5>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
+    case 6: mx_mfma_pass<6>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
+    case 7: mx_mfma_pass<7>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
+    default: mx_mfma_pass<8>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
+  }
+}
+
+// MXFP8 conversion of 32 values held one per lane by the 32 lanes of a lane group
+// (the 32 columns of one block of a row): returns this lane's E4M3 code; the block's
+// E8M0 scale code goes to *scale.  Same rule as mx_quant_act_kernel.
+__device__ __forceinline__ uint32_t mx8_group_code(float v, uint32_t* scale) {
+  float amax = fabsf(v);
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, WAVE));
+  if (!(amax > 0.0f)) {
+    *scale = 0u;
+    return 0u;
+  }
+  int e2;
+  (void)frexpf(amax, &e2);
+  int e = e2 - 1 - 8;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  *scale = (uint32_t)(e + 127);
+  return e4m3_code(v * ldexpf(1.0f, -e));
+}
+
+// h = silu(x Wg^T) * (x Wu^T) for the 128 columns of this block's strip (wave w:
+// columns n0 + 32w .. +31 of both W_gate and W_up), written in MXFP8: codes hq
+// [rows, d_ff] and scales hs [rows, d_ff/32] (a wave's 32 columns are one block).
+__global__ __launch_bounds__(256) void mx_gateup_mfma_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int d, int d_ff, int k,
     const uint8_t* __restrict__ slots, const int32_t* __restrict__ group_slot,
-    const int32_t* __restrict__ offsets, int g_begin, int n_tiles, int n_blocks, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[MTBM * ALD];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[128 * BLD];
-  __shared__ uint32_t sAs[MTBM];
-  __shared__ uint32_t sBs[128];
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, int g_begin, int n_tiles, int n_blocks,
+    uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
+  __shared__ __attribute__((aligned(16))) uint8_t sX[2][QM * QLD];
+  __shared__ uint32_t sS[2][QM];
   const int lb = xcd_logical_block(blockIdx.x, n_blocks);
   const int g = g_begin + lb / n_tiles;
   const int n0 = (lb % n_tiles) * 128;
   const int r0 = offsets[g];
   const int n = offsets[g + 1] - r0;
   if (n <= 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 5;
   const MxRec R = mx_rec(d, d_ff);
   const uint8_t* rec = slots + (size_t)group_slot[g] * R.bytes;
-  const int brow = tid >> 2, bq = tid & 3;
-  const uint8_t* bcode = rec + R.d_codes + (size_t)(n0 + brow) * (d_ff / 2) + 16 * bq;
-  for (int m0 = 0; m0 < n; m0 += MTBM) {
-    const uint8_t* arow[4];
+  const int col = n0 + wave * 32 + (lane & 31);
+  const uint8_t* cg = rec + R.g_codes + (size_t)col * (d / 2) + 32 * grp;
+  const uint8_t* cu = rec + R.u_codes + (size_t)col * (d / 2) + 32 * grp;
+  const uint8_t* sg = rec + R.g_sc + (size_t)col * (d / 32);
+  const uint8_t* su = rec + R.u_sc + (size_t)col * (d / 32);
+  for (int m0 = 0; m0 < n; m0 += QM) {
+    const int rows = min(QM, n - m0);
+    const int nsub = (rows + 31) >> 5;
+    QRowStage rs;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 64 * i;
-      arow[i] = (m0 + r < n) ? hq + (size_t)(r0 + m0 + r) * d_ff + 16 * (tid & 7) : nullptr;
+    for (int j = 0; j < 8; ++j) {
+      const int r = min((tid >> 3) + 32 * j, rows - 1);
+      rs.src[j] = xq + (size_t)(perm[r0 + m0 + r] / k) * d + (tid & 7) * 16;
     }
-    const bool wave_active = (m0 + wm * 64) < n;
-    f32x16_t acc[4];
+    rs.ssrc = xs + (size_t)(perm[r0 + m0 + min(tid, rows - 1)] / k) * (d / 32);
+    f32x16_t acc[8][2];
+    mx_mfma_pass_n(nsub, acc, rs, sX, sS, cg, cu, sg, su, d, tid, lane);
+    int g4 = grp * 4;
+    asm volatile("" : "+v"(g4));  // keeps the row indices below out of the prologue
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a) {
+      if (a >= nsub) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][v] = 0.0f;
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    uint4 pa[4], pb;
-    uint32_t pas = 0, pbs = 0;
-    auto load_stage = [&](int k0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pa[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0) : zero;
-      pb = *reinterpret_cast<const uint4*>(bcode + k0 / 2);
-      if (tid < 256) {
-        const int r = tid;
-        pas = (m0 + r < n) ? *reinterpret_cast<const uint32_t*>(hs + (size_t)(r0 + m0 + r) * (d_ff / 32) + k0 / 32) : 0u;
-      } else if (tid < 384) {
-        const int r = tid - 256;
-        pbs = *reinterpret_cast<const uint32_t*>(rec + R.d_sc + (size_t)(n0 + r) * (d_ff / 32) + k0 / 32);
-      }
-    };
-    load_stage(0);
-    for (int k0 = 0; k0 < d_ff; k0 += MKB) {
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sA[((tid >> 3) + 64 * i) * ALD + 16 * (tid & 7)]) = pa[i];
-      *reinterpret_cast<uint4*>(&sB[brow * BLD + 16 * bq]) = pb;
-      if (tid < 256) sAs[tid] = pas;
-      else if (tid < 384) sBs[tid - 256] = pbs;
-      __syncthreads();
-      if (k0 + MKB < d_ff) load_stage(k0 + MKB);
-      if (wave_active) {
-        const int grp = lane >> 5;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int ra0 = wm * 64 + (lane & 31), ra1 = ra0 + 32;
-          const int rb0 = wn * 64 + (lane & 31), rb1 = rb0 + 32;
-          const v8i_t a0 = a_frag(&sA[ra0 * ALD], ks, grp);
-          const v8i_t a1 = a_frag(&sA[ra1 * ALD], ks, grp);
-          const v8i_t b0 = b_frag(&sB[rb0 * BLD], ks, grp);
-          const v8i_t b1 = b_frag(&sB[rb1 * BLD], ks, grp);
-          const int sh = 8 * (2 * ks + grp);
-          const int sa0 = (sAs[ra0] >> sh) & 0xff, sa1 = (sAs[ra1] >> sh) & 0xff;
-          const int sb0 = (sBs[rb0] >> sh) & 0xff, sb1 = (sBs[rb1] >> sh) & 0xff;
-          acc[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, acc[0], 0, 4, 0, sa0, 0, sb0);
-          acc[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b0, acc[1], 0, 4, 0, sa1, 0, sb0);
-          acc[2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b1, acc[2], 0, 4, 0, sa0, 0, sb1);
-          acc[3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, acc[3], 0, 4, 0, sa1, 0, sb1);
+      for (int v = 0; v < 16; ++v) {
+        const int row = a * 32 + (v >> 2) * 8 + g4 + (v & 3);
+        uint32_t sc;
+        const uint32_t code = mx8_group_code(silu(acc[a][0][v]) * acc[a][1][v], &sc);
+        if (row < rows) {
+          const size_t gr = (size_t)(r0 + m0 + row);
+          hq[gr * d_ff + col] = (uint8_t)code;
+          if ((lane & 31) == 0) hs[gr * (d_ff / 32) + col / 32] = (uint8_t)sc;
         }
       }
     }
-    if (wave_active) {
+  }
+}
+
+// out[i][c] = hq_i . Wd[c] for the 256 columns of this block's strip (wave w: columns
+// n0 + 64w .. +63), h in MXFP8 with rows in perm order.
+__global__ __launch_bounds__(256) void mx_down_mfma_kernel(
+    const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, int d, int d_ff,
+    const uint8_t* __restrict__ slots, const int32_t* __restrict__ group_slot,
+    const int32_t* __restrict__ offsets, int g_begin, int n_tiles, int n_blocks, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t sX[2][QM * QLD];
+  __shared__ uint32_t sS[2][QM];
+  const int lb = xcd_logical_block(blockIdx.x, n_blocks);
+  const int g = g_begin + lb / n_tiles;
+  const int n0 = (lb % n_tiles) * 256;
+  const int r0 = offsets[g];
+  const int n = offsets[g + 1] - r0;
+  if (n <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 5;
+  const MxRec R = mx_rec(d, d_ff);
+  const uint8_t* rec = slots + (size_t)group_slot[g] * R.bytes;
+  const int col = n0 + wave * 64 + (lane & 31);
+  const uint8_t* c0 = rec + R.d_codes + (size_t)col * (d_ff / 2) + 32 * grp;
+  const uint8_t* c1 = c0 + (size_t)32 * (d_ff / 2);
+  const uint8_t* s0 = rec + R.d_sc + (size_t)col * (d_ff / 32);
+  const uint8_t* s1 = s0 + (size_t)32 * (d_ff / 32);
+  for (int m0 = 0; m0 < n; m0 += QM) {
+    const int rows = min(QM, n - m0);
+    const int nsub = (rows + 31) >> 5;
+    QRowStage rs;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int col = n0 + wn * 64 + nb * 32 + (lane & 31);
+    for (int j = 0; j < 8; ++j) {
+      const int r = min((tid >> 3) + 32 * j, rows - 1);
+      rs.src[j] = hq + (size_t)(r0 + m0 + r) * d_ff + (tid & 7) * 16;
+    }
+    rs.ssrc = hs + (size_t)(r0 + m0 + min(tid, rows - 1)) * (d_ff / 32);
+    f32x16_t acc[8][2];
+    mx_mfma_pass_n(nsub, acc, rs, sX, sS, c0, c1, s0, s1, d_ff, tid, lane);
+    int g4 = grp * 4;
+    asm volatile("" : "+v"(g4));
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+    for (int a = 0; a < 8; ++a) {
+      if (a >= nsub) continue;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = m0 + wm * 64 + mb * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-            if (row < n) out[(size_t)(r0 + row) * d + col] = acc[nb * 2 + mb][v];
-          }
+      for (int v = 0; v < 16; ++v) {
+        const int row = a * 32 + (v >> 2) * 8 + g4 + (v & 3);
+        if (row < rows) {
+          float* o = out + (size_t)(r0 + m0 + row) * d + col;
+          o[0] = acc[a][0][v];
+          o[32] = acc[a][1][v];
+        }
       }
     }
   }
@@ -563,26 +601,22 @@ int launch_mx_quant_bf16(const uint16_t* x, int rows, int n, uint8_t* q, uint8_t
 
 int launch_mx_ffn_mfma(const uint16_t* x, int T, int d, int d_ff, int k, const uint8_t* slots,
                        const int32_t* group_slot, const int32_t* offsets, const int32_t* perm, int g_begin, int g_end,
-                       int n_rows, uint8_t* xq, uint8_t* xs, float* h, uint8_t* hq, uint8_t* hs, float* out,
+                       int n_rows, uint8_t* xq, uint8_t* xs, float* /*h*/, uint8_t* hq, uint8_t* hs, float* out,
                        void* stream, void* const* ev) {
-  if (d % 128 || d_ff % 128 || k < 1) return fail(FT_EINVAL, "mx_ffn_mfma: need d%128==0 and d_ff%128==0");
+  if (d % 256 || d_ff % 128 || k < 1) return fail(FT_EINVAL, "mx_ffn_mfma: need d%256==0 and d_ff%128==0");
   const int ng = g_end - g_begin;
   if (ng <= 0 || n_rows <= 0) return FT_OK;
-  if (!aligned16(x) || !aligned16(slots) || !aligned16(xq) || !aligned16(hq) || !aligned16(h) || !aligned16(out) ||
+  if (!aligned16(x) || !aligned16(slots) || !aligned16(xq) || !aligned16(hq) || !aligned16(out) ||
       ((reinterpret_cast<uintptr_t>(xs) | reinterpret_cast<uintptr_t>(hs)) & 3u))
     return fail(FT_EINVAL, "mx_ffn_mfma: unaligned pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (int rc = launch_mx_quant_bf16(x, T, d, xq, xs, s)) return rc;
-  const int tiles_up = d_ff / 64, nb_up = ng * tiles_up;
-  timed_launch(mx_gateup_mfma_kernel, dim3(nb_up), dim3(512), s, ev, 0, (const uint8_t*)xq, (const uint8_t*)xs, d,
-               d_ff, k, slots, group_slot, offsets, perm, g_begin, tiles_up, nb_up, h);
+  const int tiles_up = d_ff / 128, nb_up = ng * tiles_up;
+  timed_launch(mx_gateup_mfma_kernel, dim3(nb_up), dim3(256), s, ev, 0, (const uint8_t*)xq, (const uint8_t*)xs, d,
+               d_ff, k, slots, group_slot, offsets, perm, g_begin, tiles_up, nb_up, hq, hs);
   if (int rc = launched("mx_gateup_mfma")) return rc;
-  // h rows are in permuted order already
-  const long long nthreads = (long long)n_rows * (d_ff / 32);
-  mx_quant_act_kernel<float><<<(unsigned)((nthreads + 255) / 256), 256, 0, s>>>(h, n_rows, d_ff, nullptr, 1, hq, hs);
-  if (int rc = launched("mx_quant_h")) return rc;
-  const int tiles_dn = d / 128, nb_dn = ng * tiles_dn;
-  timed_launch(mx_down_mfma_kernel, dim3(nb_dn), dim3(512), s, ev, 1, (const uint8_t*)hq, (const uint8_t*)hs, d, d_ff,
+  const int tiles_dn = d / 256, nb_dn = ng * tiles_dn;
+  timed_launch(mx_down_mfma_kernel, dim3(nb_dn), dim3(256), s, ev, 1, (const uint8_t*)hq, (const uint8_t*)hs, d, d_ff,
                slots, group_slot, offsets, g_begin, tiles_dn, nb_dn, out);
   return launched("mx_down_mfma");
 }

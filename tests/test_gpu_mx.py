@@ -70,11 +70,15 @@ def _mx_ffn_case(form, d, d_ff, rows, k=2, split=None, seed=0):
     ok, mxe, l1 = within_tolerance(got, ref)
     assert ok, (mxe, l1)
     if form == 2 and total > 0:
-        # the MXFP8 copies of x and h left in the workspace, bit for bit
+        # MXFP8 copies left in the workspace: x bit for bit; h (converted inside the
+        # gate/up kernel from its fp32 value) against the oracle's conversion of its
+        # fp64 h: equal except next to rounding boundaries.  The scaled MFMA sums its
+        # 64 products with an error of about 1e-4 of their absolute sum, so h carries
+        # absolute errors of that order relative to its row's size; a block's small
+        # elements may then move by more than one step, hence the X/8 of slack.
         wsh = host(ws)
         o_x = _align(total * d_ff * 4)
         o_h = o_x + _align(T * d + T * d // 32)
-        h = wsh[:total * d_ff * 4].view(np.float32).reshape(total, d_ff)
         xq = wsh[o_x:o_x + T * d].reshape(T, d)
         xs = wsh[o_x + T * d:o_x + T * d + T * d // 32].reshape(T, d // 32)
         rc, rs = mx.quantize_act_codes(x64)
@@ -82,8 +86,27 @@ def _mx_ffn_case(form, d, d_ff, rows, k=2, split=None, seed=0):
         assert xs[0, 0] == 0 and not xq[0, :32].any()
         hq = wsh[o_h:o_h + total * d_ff].reshape(total, d_ff)
         hs = wsh[o_h + total * d_ff:o_h + total * d_ff + total * d_ff // 32].reshape(total, d_ff // 32)
-        rc, rs = mx.quantize_act_codes(h.astype(np.float64))
-        assert np.array_equal(hq, rc) and np.array_equal(hs, rs)
+        xdq = mx.quantize_act(x64)
+        h_ref = np.zeros((total, d_ff))
+        for g in range(G):
+            wg, wu, _ = mx.split_record(recs[group_slot[g]], d, d_ff)
+            r = slice(offsets[g], offsets[g + 1])
+            xr = xdq[pair_ids[r] // k]
+            h_ref[r] = mx.silu(xr @ wg.T) * (xr @ wu.T)
+        rc, rs = mx.quantize_act_codes(h_ref)
+        assert (hq == rc).mean() >= 0.99 and (hs == rs).mean() >= 0.99
+        assert np.abs(hs.astype(int) - rs.astype(int)).max() <= 1
+        got_v = mx.e8m0_value(np.repeat(hs, 32, axis=1)) * mx.e4m3_value(hq)
+        ref_v = mx.e8m0_value(np.repeat(rs, 32, axis=1)) * mx.e4m3_value(rc)
+        step = np.maximum(np.abs(got_v), np.abs(ref_v)) / 8 + mx.e8m0_value(np.repeat(np.maximum(hs, rs), 32, axis=1)) / 8
+        bad = np.argwhere(np.abs(got_v - ref_v) > step)
+        if bad.size:
+            i, j = bad[0]
+            b = j // 32
+            pytest.fail(f"{len(bad)} h codes off by more than a step; first at row {i} col {j}: "
+                        f"gpu code {hq[i, j]} scale {hs[i, b]} value {got_v[i, j]}, oracle code {rc[i, j]} "
+                        f"scale {rs[i, b]} value {ref_v[i, j]}, h {h_ref[i, j]}, block amax "
+                        f"{np.abs(h_ref[i, 32 * b:32 * b + 32]).max()}")
 
 
 @pytest.mark.parametrize("d,d_ff,rows,split", [
