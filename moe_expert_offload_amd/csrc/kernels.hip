@@ -563,7 +563,8 @@ __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
 // one expert (8 row subtiles of 32; the usual ~200 tokens of an 8k chunk in one
 // pass) and a column strip per wave: every weight element is read from HBM once
 // per pass, straight into the registers of the one wave that uses it.  Token rows
-// (operand A) are staged through LDS, double-buffered, and shared by the 4 waves.
+// (operand A) are staged through LDS (three rotating buffers) and shared by the 4
+// waves.
 // K runs in stages of 64; inside a stage, MFMA i (0..3) takes in lane group g the
 // elements 32g + 8i .. +7, so a lane's weight data for a stage is 64 contiguous
 // bytes and A is read from LDS in the same order (the sum over k is unchanged).
@@ -597,28 +598,30 @@ struct RowStage {
 };
 
 // acc[a][c] += A(subtile a) x B(column subtile c) over one 64-element stage; w holds
-// the lane's 4 pieces for column subtile 0 then 4 for column subtile 1.  The A
-// fragments of K slice i + 1 are read from LDS while slice i multiplies.
+// the lane's 4 pieces for column subtile 0 then 4 for column subtile 1.  f0 holds the
+// A fragments of K slice 0 on entry; slice i + 1 is read from LDS while slice i
+// multiplies, and during the last slice the next stage's slice 0 is read from
+// sx_next into f0, so the MFMA pipe stays fed across the stage barrier.
 template <int NSUB>
 __device__ __forceinline__ void mfma_stage_bf16(f32x16_t (&acc)[8][2], const uint4 (&w)[8], const uint16_t* sx,
-                                                int lane) {
-  const int grp = lane >> 5;
-  const uint16_t* arow = sx + (lane & 31) * XLD + grp * 32;
-  bf16x8_t fa[2][NSUB];
-#pragma unroll
-  for (int a = 0; a < NSUB; ++a) fa[0][a] = lds_frag(arow + a * 32 * XLD);
+                                                const uint16_t* sx_next, bf16x8_t (&f0)[NSUB], int lane) {
+  const int off = (lane & 31) * XLD + (lane >> 5) * 32;
+  const uint16_t* arow = sx + off;
+  const uint16_t* nrow = sx_next + off;
+  bf16x8_t f1[NSUB];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (i < 3) {
+    bf16x8_t (&cur)[NSUB] = (i & 1) ? f1 : f0;
+    bf16x8_t (&nxt)[NSUB] = (i & 1) ? f0 : f1;
 #pragma unroll
-      for (int a = 0; a < NSUB; ++a) fa[(i + 1) & 1][a] = lds_frag(arow + a * 32 * XLD + 8 * (i + 1));
-    }
+    for (int a = 0; a < NSUB; ++a)
+      nxt[a] = lds_frag(i < 3 ? arow + a * 32 * XLD + 8 * (i + 1) : nrow + a * 32 * XLD);
     const bf16x8_t b0 = as_bf16x8(w[i]);
     const bf16x8_t b1 = as_bf16x8(w[4 + i]);
 #pragma unroll
     for (int a = 0; a < NSUB; ++a) {
-      acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i & 1][a], b0, acc[a][0], 0, 0, 0);
-      acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i & 1][a], b1, acc[a][1], 0, 0, 0);
+      acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[a], b0, acc[a][0], 0, 0, 0);
+      acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[a], b1, acc[a][1], 0, 0, 0);
     }
   }
 }
@@ -631,14 +634,17 @@ __device__ __forceinline__ void load_w_stage(uint4 (&w)[8], const uint16_t* w0, 
   }
 }
 
+constexpr int XBUF = XM * XLD;  // one LDS stage buffer, bf16 elements
+
 // Runs the K loop of one pass (K = kdim, a multiple of 64) with A from `rs` and the
 // lane's weight rows w0, w1 (already offset by 32 * lane group), for NSUB row
-// subtiles.  Weights are prefetched four stages ahead (HBM latency under load is
-// a few stages of compute), token rows one stage ahead (they come from L2).
-// Prefetches past the last stage re-read the last stage (clamped) so the loop has
-// no conditional loads.
+// subtiles.  Token rows rotate through three LDS buffers: stage s computes from
+// buffer s%3 while stage s+2's rows are stored into buffer (s+2)%3, so the reads of
+// stage s+1 may start before the barrier that closes stage s.  Weights are
+// prefetched four stages ahead; prefetches past the last stage re-read it (clamped)
+// so the loop has no conditional loads.
 template <int NSUB>
-__device__ __forceinline__ void mfma_pass_bf16(f32x16_t (&acc)[8][2], RowStage& rs, uint16_t (*sx)[XM * XLD],
+__device__ __forceinline__ void mfma_pass_bf16(f32x16_t (&acc)[8][2], RowStage& rs, uint16_t* sx,
                                                const uint16_t* w0, const uint16_t* w1, int kdim, int tid,
                                                int lane) {
 #pragma unroll
@@ -657,29 +663,38 @@ __device__ __forceinline__ void mfma_pass_bf16(f32x16_t (&acc)[8][2], RowStage& 
   uint4 wr[4][8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) load_w_stage(wr[j], w0, w1, j * XK);
-  rs.load(0);
-  rs.store(sx[0], tid);
-  rs.load(XK);
-  __syncthreads();
   const int klast = kdim - XK;
+  rs.load(0);
+  rs.store(sx, tid);
+  rs.load(min(XK, klast));
+  rs.store(sx + XBUF, tid);
+  rs.load(min(2 * XK, klast));
+  __syncthreads();
+  bf16x8_t f0[NSUB];
+  {
+    const uint16_t* arow = sx + (lane & 31) * XLD + (lane >> 5) * 32;
+#pragma unroll
+    for (int a = 0; a < NSUB; ++a) f0[a] = lds_frag(arow + a * 32 * XLD);
+  }
+  int b = 0;  // LDS buffer of the current stage
   for (int k0 = 0; k0 < kdim; k0 += 4 * XK) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (k0 + j * XK >= kdim) break;
-      // stage k0 + j*XK: LDS buffer j&1, weights wr[j]; the next stage's rows go to
-      // the other buffer meanwhile
-      rs.store(sx[(j + 1) & 1], tid);
-      rs.load(min(k0 + (j + 2) * XK, klast));
-      mfma_stage_bf16<NSUB>(acc, wr[j], sx[j & 1], lane);
+      const int b1 = b == 2 ? 0 : b + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+      rs.store(sx + b2 * XBUF, tid);                    // rows of stage s + 2
+      rs.load(min(k0 + (j + 3) * XK, klast));           // rows of stage s + 3
+      mfma_stage_bf16<NSUB>(acc, wr[j], sx + b * XBUF, sx + b1 * XBUF, f0, lane);
       load_w_stage(wr[j], w0, w1, min(k0 + (j + 4) * XK, klast));
       __syncthreads();
+      b = b1;
     }
   }
 }
 
-__device__ __forceinline__ void mfma_pass_bf16_n(int nsub, f32x16_t (&acc)[8][2], RowStage& rs,
-                                                 uint16_t (*sx)[XM * XLD], const uint16_t* w0, const uint16_t* w1,
-                                                 int kdim, int tid, int lane) {
+__device__ __forceinline__ void mfma_pass_bf16_n(int nsub, f32x16_t (&acc)[8][2], RowStage& rs, uint16_t* sx,
+                                                 const uint16_t* w0, const uint16_t* w1, int kdim, int tid,
+                                                 int lane) {
   switch (nsub) {
     case 1: mfma_pass_bf16<1>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
     case 2: mfma_pass_bf16<2>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
@@ -700,7 +715,7 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(
     size_t rec_elems, const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, int g_begin, int n_tiles, int n_blocks,
     uint16_t* __restrict__ h) {
-  __shared__ __attribute__((aligned(16))) uint16_t sX[2][XM * XLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[3 * XBUF];
   const int lb = xcd_logical_block(blockIdx.x, n_blocks);
   const int g = g_begin + lb / n_tiles;
   const int n0 = (lb % n_tiles) * 128;
@@ -744,7 +759,7 @@ __global__ __launch_bounds__(256) void ffn_down_mfma_kernel(
     int d, int d_ff, const uint16_t* __restrict__ slots, size_t rec_elems,
     const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, int g_begin,
     int n_tiles, int n_blocks, const uint16_t* __restrict__ h, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t sX[2][XM * XLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[3 * XBUF];
   const int lb = xcd_logical_block(blockIdx.x, n_blocks);
   const int g = g_begin + lb / n_tiles;
   const int n0 = (lb % n_tiles) * 256;

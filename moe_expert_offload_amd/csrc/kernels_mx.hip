@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void mx_quant_act_kernel(const In* __restrict_
 // expert (8 row subtiles of 32) and a column strip per wave, so every weight byte is
 // read from HBM once per pass, straight into the registers of the one wave that uses
 // it (prefetched four stages ahead).  Token rows (MXFP8 codes and their scales) are
-// staged through LDS, double-buffered, and shared by the 4 waves.
+// staged through LDS (three rotating buffers) and shared by the 4 waves.
 // K runs in stages of 128 elements = two scaled MFMAs.  MFMA i (0, 1) of a stage
 // takes as its K positions 0..31 the stage's block i and as positions 32..63 its
 // block i + 2 (any pairing is exact as long as both operands and both scales follow
@@ -277,6 +277,9 @@ __global__ __launch_bounds__(256) void mx_quant_act_kernel(const In* __restrict_
 constexpr int QM = 256;        // rows per pass
 constexpr int QK = 128;        // K elements per stage
 constexpr int QLD = QK + 16;   // padded LDS row of fp8 codes (bytes)
+#ifndef QDEPTH
+#define QDEPTH 4               // weight stages in flight
+#endif
 
 __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
   const int q = nb >> 3, r = nb & 7, x = b & 7;
@@ -328,39 +331,66 @@ __device__ __forceinline__ v8i_t fp4_operand(uint4 c) {
   return r;
 }
 
-// acc[a][c] += A(subtile a) x B(column subtile c) over one 128-element stage.
-template <int NSUB>
-__device__ __forceinline__ void mx_mfma_stage(f32x16_t (&acc)[8][2], const QW& w, const uint8_t* sx,
-                                              const uint32_t* ss, int lane) {
-  const int grp = lane >> 5;
-  const uint8_t* arow = sx + (lane & 31) * QLD + 16 * grp;
+// A operand of one row subtile for both MFMAs of a stage, and the row's 4 scale bytes.
+struct QA {
+  v8i_t f[2];
+  uint32_t s;
+};
+
+__device__ __forceinline__ void load_qa(QA& q, const uint8_t* arow, const uint32_t* srow) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int blk = i + 2 * grp;  // stage block whose scale this lane group passes
-    const v8i_t b0 = fp4_operand(w.c[i]);
-    const v8i_t b1 = fp4_operand(w.c[2 + i]);
-    const int sb0 = (w.s[0] >> (8 * blk)) & 0xff, sb1 = (w.s[1] >> (8 * blk)) & 0xff;
-#pragma unroll
-    for (int a = 0; a < NSUB; ++a) {
-      const uint8_t* ap = arow + a * 32 * QLD + 32 * i;
-      const uint4 lo = *reinterpret_cast<const uint4*>(ap);
-      const uint4 hi = *reinterpret_cast<const uint4*>(ap + 64);
-      v8i_t af;
-      af[0] = (int)lo.x; af[1] = (int)lo.y; af[2] = (int)lo.z; af[3] = (int)lo.w;
-      af[4] = (int)hi.x; af[5] = (int)hi.y; af[6] = (int)hi.z; af[7] = (int)hi.w;
-      const int sa = (ss[a * 32 + (lane & 31)] >> (8 * blk)) & 0xff;
-      acc[a][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, b0, acc[a][0], 0, 4, 0, sa, 0, sb0);
-      acc[a][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, b1, acc[a][1], 0, 4, 0, sa, 0, sb1);
-    }
+    const uint4 lo = *reinterpret_cast<const uint4*>(arow + 32 * i);
+    const uint4 hi = *reinterpret_cast<const uint4*>(arow + 32 * i + 64);
+    q.f[i][0] = (int)lo.x; q.f[i][1] = (int)lo.y; q.f[i][2] = (int)lo.z; q.f[i][3] = (int)lo.w;
+    q.f[i][4] = (int)hi.x; q.f[i][5] = (int)hi.y; q.f[i][6] = (int)hi.z; q.f[i][7] = (int)hi.w;
   }
+  q.s = *srow;
 }
+
+// acc[a][c] += A(subtile a) x B(column subtile c) over one 128-element stage.  q0
+// holds subtile 0's A operand on entry; subtile a + 1 is read from LDS while subtile a
+// multiplies, and during the last subtile the next stage's subtile 0 is read from
+// (sx_next, ss_next) into q0, so the MFMA pipe stays fed across the stage barrier.
+template <int NSUB>
+__device__ __forceinline__ void mx_mfma_stage(f32x16_t (&acc)[8][2], const QW& w, const uint8_t* sx,
+                                              const uint32_t* ss, const uint8_t* sx_next, const uint32_t* ss_next,
+                                              QA& q0, int lane) {
+  const int grp = lane >> 5;
+  const int aoff = (lane & 31) * QLD + 16 * grp;
+  const v8i_t b[4] = {fp4_operand(w.c[0]), fp4_operand(w.c[1]), fp4_operand(w.c[2]), fp4_operand(w.c[3])};
+  // lane group g passes the scales of stage blocks g*2 (MFMA 0) and g*2 + 1 (MFMA 1)
+  const int sh0 = 16 * grp, sh1 = 16 * grp + 8;
+  const int sb[4] = {(int)((w.s[0] >> sh0) & 0xff), (int)((w.s[0] >> sh1) & 0xff), (int)((w.s[1] >> sh0) & 0xff),
+                     (int)((w.s[1] >> sh1) & 0xff)};
+  QA q1;
+#pragma unroll
+  for (int a = 0; a < NSUB; ++a) {
+    QA& cur = (a & 1) ? q1 : q0;
+    QA& nxt = (a & 1) ? q0 : q1;
+    if (a + 1 < NSUB)
+      load_qa(nxt, sx + aoff + (a + 1) * 32 * QLD, ss + (lane & 31) + (a + 1) * 32);
+    else
+      load_qa(nxt, sx_next + aoff, ss_next + (lane & 31));
+    const int sa0 = (cur.s >> sh0) & 0xff, sa1 = (cur.s >> sh1) & 0xff;
+    acc[a][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.f[0], b[0], acc[a][0], 0, 4, 0, sa0, 0, sb[0]);
+    acc[a][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.f[0], b[2], acc[a][1], 0, 4, 0, sa0, 0, sb[2]);
+    acc[a][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.f[1], b[1], acc[a][0], 0, 4, 0, sa1, 0, sb[1]);
+    acc[a][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.f[1], b[3], acc[a][1], 0, 4, 0, sa1, 0, sb[3]);
+  }
+  if (NSUB & 1) q0 = q1;  // the next stage's subtile 0 landed in q1
+}
+
+constexpr int QBUF = QM * QLD;  // one LDS stage buffer of codes, bytes
 
 // K loop of one pass (K = kdim, a multiple of 128).  Weight pointers are this lane's
 // two rows (codes already offset by 16 * lane group, scales at the row start).
+// Token rows rotate through three LDS buffers: stage s computes from buffer s%3
+// while stage s+2's rows are stored into buffer (s+2)%3.
 template <int NSUB>
-__device__ __forceinline__ void mx_mfma_pass(f32x16_t (&acc)[8][2], QRowStage& rs, uint8_t (*sx)[QM * QLD],
-                                             uint32_t (*ss)[QM], const uint8_t* c0, const uint8_t* c1,
-                                             const uint8_t* s0, const uint8_t* s1, int kdim, int tid, int lane) {
+__device__ __forceinline__ void mx_mfma_pass(f32x16_t (&acc)[8][2], QRowStage& rs, uint8_t* sx, uint32_t* ss,
+                                             const uint8_t* c0, const uint8_t* c1, const uint8_t* s0,
+                                             const uint8_t* s1, int kdim, int tid, int lane) {
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
@@ -372,31 +402,37 @@ __device__ __forceinline__ void mx_mfma_pass(f32x16_t (&acc)[8][2], QRowStage& r
   asm volatile("" : "+s"(opaque));
   c0 += opaque;
   c1 += opaque;
-  QW wr[4];
+  QW wr[QDEPTH];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) load_qw(wr[j], c0, c1, s0, s1, j * QK);
-  rs.load(0);
-  rs.store(sx[0], ss[0], tid);
-  rs.load(QK);
-  __syncthreads();
+  for (int j = 0; j < QDEPTH; ++j) load_qw(wr[j], c0, c1, s0, s1, j * QK);
   const int klast = kdim - QK;
-  for (int k0 = 0; k0 < kdim; k0 += 4 * QK) {
+  rs.load(0);
+  rs.store(sx, ss, tid);
+  rs.load(min(QK, klast));
+  rs.store(sx + QBUF, ss + QM, tid);
+  rs.load(min(2 * QK, klast));
+  __syncthreads();
+  QA q0;
+  load_qa(q0, sx + (lane & 31) * QLD + 16 * (lane >> 5), ss + (lane & 31));
+  int b = 0;  // LDS buffer of the current stage
+  for (int k0 = 0; k0 < kdim; k0 += QDEPTH * QK) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < QDEPTH; ++j) {
       if (k0 + j * QK >= kdim) break;
-      rs.store(sx[(j + 1) & 1], ss[(j + 1) & 1], tid);
-      rs.load(min(k0 + (j + 2) * QK, klast));
-      mx_mfma_stage<NSUB>(acc, wr[j], sx[j & 1], ss[j & 1], lane);
-      load_qw(wr[j], c0, c1, s0, s1, min(k0 + (j + 4) * QK, klast));
+      const int b1 = b == 2 ? 0 : b + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+      rs.store(sx + b2 * QBUF, ss + b2 * QM, tid);      // rows of stage s + 2
+      rs.load(min(k0 + (j + 3) * QK, klast));           // rows of stage s + 3
+      mx_mfma_stage<NSUB>(acc, wr[j], sx + b * QBUF, ss + b * QM, sx + b1 * QBUF, ss + b1 * QM, q0, lane);
+      load_qw(wr[j], c0, c1, s0, s1, min(k0 + (j + QDEPTH) * QK, klast));
       __syncthreads();
+      b = b1;
     }
   }
 }
 
-__device__ __forceinline__ void mx_mfma_pass_n(int nsub, f32x16_t (&acc)[8][2], QRowStage& rs,
-                                               uint8_t (*sx)[QM * QLD], uint32_t (*ss)[QM], const uint8_t* c0,
-                                               const uint8_t* c1, const uint8_t* s0, const uint8_t* s1, int kdim,
-                                               int tid, int lane) {
+__device__ __forceinline__ void mx_mfma_pass_n(int nsub, f32x16_t (&acc)[8][2], QRowStage& rs, uint8_t* sx,
+                                               uint32_t* ss, const uint8_t* c0, const uint8_t* c1, const uint8_t* s0,
+                                               const uint8_t* s1, int kdim, int tid, int lane) {
   switch (nsub) {
     case 1: mx_mfma_pass<1>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
     case 2: mx_mfma_pass<2>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
@@ -409,23 +445,19 @@ __device__ __forceinline__ void mx_mfma_pass_n(int nsub, f32x16_t (&acc)[8][2], 
   }
 }
 
-// MXFP8 conversion of 32 values held one per lane by the 32 lanes of a lane group
-// (the 32 columns of one block of a row): returns this lane's E4M3 code; the block's
-// E8M0 scale code goes to *scale.  Same rule as mx_quant_act_kernel.
-__device__ __forceinline__ uint32_t mx8_group_code(float v, uint32_t* scale) {
-  float amax = fabsf(v);
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, WAVE));
+// E8M0 scale code of a block with maximum magnitude amax, and 2^-e to multiply its
+// elements by (OCP MX conversion for E4M3; an all-zero block gets code 0).
+__device__ __forceinline__ uint32_t mx8_scale(float amax, float* inv) {
   if (!(amax > 0.0f)) {
-    *scale = 0u;
+    *inv = 0.0f;
     return 0u;
   }
   int e2;
   (void)frexpf(amax, &e2);
   int e = e2 - 1 - 8;
   e = e < -127 ? -127 : (e > 127 ? 127 : e);
-  *scale = (uint32_t)(e + 127);
-  return e4m3_code(v * ldexpf(1.0f, -e));
+  *inv = ldexpf(1.0f, -e);
+  return (uint32_t)(e + 127);
 }
 
 // h = silu(x Wg^T) * (x Wu^T) for the 128 columns of this block's strip (wave w:
@@ -436,8 +468,8 @@ __global__ __launch_bounds__(256) void mx_gateup_mfma_kernel(
     const uint8_t* __restrict__ slots, const int32_t* __restrict__ group_slot,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, int g_begin, int n_tiles, int n_blocks,
     uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
-  __shared__ __attribute__((aligned(16))) uint8_t sX[2][QM * QLD];
-  __shared__ uint32_t sS[2][QM];
+  __shared__ __attribute__((aligned(16))) uint8_t sX[3 * QBUF];
+  __shared__ uint32_t sS[3 * QM];
   const int lb = xcd_logical_block(blockIdx.x, n_blocks);
   const int g = g_begin + lb / n_tiles;
   const int n0 = (lb % n_tiles) * 128;
@@ -464,23 +496,47 @@ __global__ __launch_bounds__(256) void mx_gateup_mfma_kernel(
     rs.ssrc = xs + (size_t)(perm[r0 + m0 + min(tid, rows - 1)] / k) * (d / 32);
     f32x16_t acc[8][2];
     mx_mfma_pass_n(nsub, acc, rs, sX, sS, cg, cu, sg, su, d, tid, lane);
+    // MXFP8 conversion of h: each wave's 32 columns are one block of every row.  A
+    // 32 x 32 subtile goes through this wave's corner of LDS (the pass ended with a
+    // barrier, so the staging buffers are free) so that each lane then holds 16
+    // consecutive values of one row: lanes 2r and 2r+1 share row r's block.
+    float* tile = reinterpret_cast<float*>(sX) + wave * 32 * 36;
     int g4 = grp * 4;
     asm volatile("" : "+v"(g4));  // keeps the row indices below out of the prologue
+    const int tr = lane >> 1, th = lane & 1;
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
       if (a >= nsub) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = a * 32 + (v >> 2) * 8 + g4 + (v & 3);
-        uint32_t sc;
-        const uint32_t code = mx8_group_code(silu(acc[a][0][v]) * acc[a][1][v], &sc);
-        if (row < rows) {
-          const size_t gr = (size_t)(r0 + m0 + row);
-          hq[gr * d_ff + col] = (uint8_t)code;
-          if ((lane & 31) == 0) hs[gr * (d_ff / 32) + col / 32] = (uint8_t)sc;
-        }
+      for (int v = 0; v < 16; ++v)
+        tile[((v >> 2) * 8 + g4 + (v & 3)) * 36 + (lane & 31)] = silu(acc[a][0][v]) * acc[a][1][v];
+      float hv[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 t4 = *reinterpret_cast<const float4*>(tile + tr * 36 + 16 * th + 4 * q);
+        hv[4 * q] = t4.x; hv[4 * q + 1] = t4.y; hv[4 * q + 2] = t4.z; hv[4 * q + 3] = t4.w;
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) amax = fmaxf(amax, fabsf(hv[q]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, WAVE));
+      float inv;
+      const uint32_t sc = mx8_scale(amax, &inv);
+      uint32_t pk[4];
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        pk[w4] = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pk[w4] |= (sc ? e4m3_code(hv[4 * w4 + j] * inv) : 0u) << (8 * j);
+      }
+      const int row = a * 32 + tr;
+      if (row < rows) {
+        const size_t gr = (size_t)(r0 + m0 + row);
+        *reinterpret_cast<uint4*>(hq + gr * d_ff + n0 + wave * 32 + 16 * th) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        if (th == 0) hs[gr * (d_ff / 32) + (n0 + wave * 32) / 32] = (uint8_t)sc;
       }
     }
+    __syncthreads();  // the next row pass restages into the same LDS
   }
 }
 
@@ -490,8 +546,8 @@ __global__ __launch_bounds__(256) void mx_down_mfma_kernel(
     const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, int d, int d_ff,
     const uint8_t* __restrict__ slots, const int32_t* __restrict__ group_slot,
     const int32_t* __restrict__ offsets, int g_begin, int n_tiles, int n_blocks, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t sX[2][QM * QLD];
-  __shared__ uint32_t sS[2][QM];
+  __shared__ __attribute__((aligned(16))) uint8_t sX[3 * QBUF];
+  __shared__ uint32_t sS[3 * QM];
   const int lb = xcd_logical_block(blockIdx.x, n_blocks);
   const int g = g_begin + lb / n_tiles;
   const int n0 = (lb % n_tiles) * 256;
