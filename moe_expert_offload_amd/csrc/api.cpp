@@ -149,6 +149,13 @@ struct ft_ctx {
   uint32_t* h_flag = nullptr;  // router's publication sequence number
   uint32_t route_seq = 0;
 
+  // device copy of the residency state and the device-side plan ([FT] §4.1)
+  ft::DevCache dc{};
+  int dev_cap = 0;               // slots the device arrays hold
+  bool dev_dirty = true;         // host state changed since the last upload
+  ft::DevPlan* d_plan = nullptr;  // device
+  ft::DevPlan* h_plan = nullptr;  // pinned publication
+
   hipEvent_t ev_route = nullptr, ev_fill = nullptr, ev_done = nullptr;
   hipEvent_t ev_pf_fill[2] = {nullptr, nullptr}, ev_pf_comp[2] = {nullptr, nullptr};
 
@@ -213,6 +220,55 @@ void prof_account(ft_ctx* c, ft_ctx::ProfRec* r, const int* rows, int n_groups, 
     r->flops_up += 4.0 * n * d * dff;
     r->flops_dn += 2.0 * n * d * dff;
   }
+}
+
+// Copies the host residency state to the device arrays the decode router's
+// decisions work on (at create and after every host-side change: resize, prefill,
+// stand-alone lookups).  Synchronous; only called at safe points.
+int upload_cache(ft_ctx* c) {
+  const ft::ExpertCache& h = *c->cache;
+  const int n = h.n_slots();
+  if (n > c->dev_cap) {
+    if (c->dc.slot_key) (void)hipFree(c->dc.slot_key);
+    if (c->dc.slot_stamp) (void)hipFree(c->dc.slot_stamp);
+    c->dc.slot_key = nullptr;
+    c->dc.slot_stamp = nullptr;
+    c->dev_cap = 0;
+    if (hipMalloc((void**)&c->dc.slot_key, (size_t)n * 4) != hipSuccess ||
+        hipMalloc((void**)&c->dc.slot_stamp, (size_t)n * 8) != hipSuccess)
+      return fail(FT_ENOMEM, "device cache state allocation failed");
+    c->dev_cap = n;
+  }
+  c->dc.n_slots = n;
+  const int64_t clk = h.clock();
+  if ((n > 0 && (hipMemcpy(c->dc.slot_key, h.slot_keys().data(), (size_t)n * 4, hipMemcpyHostToDevice) != hipSuccess ||
+                 hipMemcpy(c->dc.slot_stamp, h.slot_stamps().data(), (size_t)n * 8, hipMemcpyHostToDevice) !=
+                     hipSuccess)) ||
+      hipMemcpy(c->dc.where, h.where_table().data(), h.where_table().size() * 4, hipMemcpyHostToDevice) !=
+          hipSuccess ||
+      hipMemcpy(c->dc.clock, &clk, 8, hipMemcpyHostToDevice) != hipSuccess)
+    return fail(FT_EHIP, "device cache state upload failed");
+  c->dev_dirty = false;
+  return FT_OK;
+}
+
+// Hash of a host plan, as the device computes it for its decisions (plan_term).
+uint32_t host_plan_hash(const ft_plan& h, int P) {
+  uint32_t x = 0u;
+  int j = 0;
+  auto add = [&](int32_t v) { x += ft::plan_term(j++, v); };
+  add(h.n_u);
+  add(h.n_h);
+  add(h.n_m);
+  add(h.q);
+  add(h.avail);
+  for (int i = 0; i < h.n_u; ++i) add(h.U[i]);
+  for (int i = 0; i < h.n_h; ++i) add(h.H[i]);
+  for (int i = 0; i < h.n_m; ++i) add(h.M[i]);
+  for (int i = 0; i < h.n_h + h.q; ++i) add(h.G_slot[i]);
+  for (int i = 0; i < P; ++i) add(h.route_slot[i]);
+  for (int i = 0; i < P; ++i) add(h.pair_group[i]);
+  return x;
 }
 
 }  // namespace
@@ -323,6 +379,12 @@ int ft_create(const ft_shape* shape, const ft_config* config, const void* host_p
       if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess)
         return bail(FT_EHIP, "create: hipEventCreate failed");
     if (hipMemset(c->ws + c->cv.ticket, 0, 4) != hipSuccess) return bail(FT_EHIP, "create: hipMemset failed");
+    if (hipMalloc((void**)&c->dc.where, (size_t)shape->L * shape->E * 4) != hipSuccess ||
+        hipMalloc((void**)&c->dc.clock, 8) != hipSuccess ||
+        hipMalloc((void**)&c->d_plan, sizeof(ft::DevPlan)) != hipSuccess ||
+        hipHostMalloc((void**)&c->h_plan, sizeof(ft::DevPlan)) != hipSuccess)
+      return bail(FT_ENOMEM, "create: device cache state allocation failed");
+    c->dc.E = shape->E;
     *c->h_flag = 0;
     c->cpu = ft::cpu_pool_create(config->cpu_threads);
     c->cfg.cpu_threads = ft::cpu_pool_threads(c->cpu);
@@ -332,6 +394,10 @@ int ft_create(const ft_shape* shape, const ft_config* config, const void* host_p
     // never faults on the hot path.
     prefault_host(host_pool, (size_t)c->L_phys * shape->E * c->S, c->cfg.cpu_threads + 1);
     c->dev = true;
+    if (int rc = upload_cache(c)) {
+      ft_destroy(c);
+      return rc;
+    }
   }
   *out = c;
   return FT_OK;
@@ -354,9 +420,12 @@ int ft_destroy(ft_ctx_t c) {
   }
   for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
   for (int32_t* o : c->off_free) (void)hipHostFree(o);
-  void* pins[] = {c->h_idx, c->h_gates, c->h_x, c->h_key, c->h_gslot, c->h_partial, c->h_flag};
+  void* pins[] = {c->h_idx, c->h_gates, c->h_x, c->h_key, c->h_gslot, c->h_partial, c->h_flag, c->h_plan};
   for (void* p : pins)
     if (p) (void)hipHostFree(p);
+  void* devs[] = {c->dc.where, c->dc.slot_key, c->dc.slot_stamp, c->dc.clock, c->d_plan};
+  for (void* p : devs)
+    if (p) (void)hipFree(p);
   delete c->cache;
   delete c;
   return FT_OK;
@@ -502,6 +571,7 @@ int ft_host_experts(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t f
 
 int ft_expert_cache_lookup(ft_ctx_t c, int32_t layer, const int32_t* idx_host, int32_t T, ft_plan* plan) {
   if (!c || !idx_host || !plan) return fail(FT_EINVAL, "lookup: null argument");
+  c->dev_dirty = true;  // the device copy is refreshed before the next decode call
   return c->cache->lookup(layer, idx_host, T, c->shape.k, c->cfg.frac_q16, c->cfg.min_fill,
                           c->cfg.max_fetch, plan);
 }
@@ -540,6 +610,7 @@ int ft_expert_cache_resize(ft_ctx_t c, void* new_dev_slots, int32_t n) {
   }
   c->cache->resize(n);
   c->cache->stats.resizes += 1;
+  c->dev_dirty = true;
   if (c->overlap && n < 2 * c->shape.E) {
     c->overlap = false;
     ft::set_error("resize: fewer than 2E slots, prefill overlap disabled");
@@ -567,15 +638,56 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
   float* d_gates = c->wsp<float>(c->cv.gates);
   // order after everything this context issued before, whatever the stream
   FT_HIP(hipStreamWaitEvent(cs, c->ev_done, 0));
-  // the router publishes ids, gates and x straight to pinned host memory, then a
-  // sequence number; the host spins on it (bounded), the event is the fallback
+  if (c->dev_dirty) {
+    FT_HIP(hipStreamSynchronize(cs));
+    if (int rc = upload_cache(c)) return rc;
+  }
+  // [FT] §4.1 device-side cache control: the router's last block takes this call's
+  // decisions on the device and groups the pairs, so the grouped FFN of the hits
+  // is queued right behind it without waiting for the host.  It publishes ids,
+  // gates, x and the plan to pinned host memory, then a sequence number.
   const uint32_t seq = ++c->route_seq == 0 ? ++c->route_seq : c->route_seq;
+  ft::DecideArgs da{};
+  da.dc = c->dc;
+  da.plan = c->d_plan;
+  da.pub = c->h_plan;
+  da.layer = layer;
+  da.fq = c->cfg.frac_q16;
+  da.min_fill = c->cfg.min_fill;
+  da.max_fetch = c->cfg.max_fetch;
   if (int rc = ft::launch_router_decode(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
                                         allowed, T, d, E, k, c->wsp<float>(c->cv.logits), d_idx, d_gates,
                                         c->wsp<unsigned int>(c->cv.ticket), c->h_idx, c->h_gates, c->h_x,
-                                        c->h_flag, seq, cs))
+                                        c->h_flag, seq, cs, &da))
     return rc;
   FT_HIP(hipEventRecord(c->ev_route, cs));
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  float* d_h = c->wsp<float>(c->cv.h);
+  float* d_out = c->wsp<float>(c->cv.out);
+  const int nt_bound = T;  // rows per group are at most T
+  auto ffn = [&](int g0, int g1, int max_rows, const int32_t* g_hi, const int* rows_of) -> int {
+    ft_ctx::ProfRec* r = prof_begin(c);
+    if (r) {
+      if (rows_of) {
+        prof_account(c, r, rows_of + g0, g1 - g0, 4);
+      } else {
+        r->bytes_up = r->bytes_dn = r->flops_up = r->flops_dn = 0.0;  // filled in once the plan is known
+      }
+    }
+    void* const* ev = r ? reinterpret_cast<void* const*>(r->ev) : nullptr;
+    if (c->mx)
+      return ft::launch_mx_ffn_rows(xs, d, c->shape.d_ff, k, c->slots, c->d_plan->G_slot, c->d_plan->offsets,
+                                    c->d_plan->perm, g0, g1, max_rows, d_h, d_out, cs, ev, g_hi);
+    return ft::launch_ffn_rows(xs, d, c->shape.d_ff, k, reinterpret_cast<const uint16_t*>(c->slots),
+                               c->d_plan->G_slot, c->d_plan->offsets, c->d_plan->perm, g0, g1, max_rows, d_h,
+                               d_out, cs, ev, g_hi);
+  };
+  // grouped FFN of the hits, launched for every possible group and bounded on the
+  // device by the plan's n_h
+  const size_t prof_h = c->prof.size();
+  if (int rc = ffn(0, P, nt_bound, &c->d_plan->n_h, nullptr)) return rc;
+  // wait for the publication (bounded spin on the sequence number, the event is
+  // the fallback)
   {
     bool seen = false;
     const double spin_end = now_us() + 2000.0;
@@ -595,11 +707,22 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
   }
   const double t1 = now_us();
   for (int i = 0; i < P; ++i)
-    if (c->h_idx[i] < 0) return fail(FT_EINVAL, "decode: a token allows fewer than k experts");
-
+    if (c->h_idx[i] < 0) {
+      c->dev_dirty = true;
+      return fail(FT_EINVAL, "decode: a token allows fewer than k experts");
+    }
+  const ft::DevPlan& dp = *c->h_plan;
+  // the host controller takes the same decisions from the same ids: it keeps the
+  // counters and the state for safe-point operations, and checks the device
   ft_plan* p = plan_out ? plan_out : &c->scratch_plan;
-  if (int rc = c->cache->lookup(layer, c->h_idx, T, k, c->cfg.frac_q16, c->cfg.min_fill, c->cfg.max_fetch, p))
+  if (int rc = c->cache->lookup(layer, c->h_idx, T, k, c->cfg.frac_q16, c->cfg.min_fill, c->cfg.max_fetch, p)) {
+    c->dev_dirty = true;
     return rc;
+  }
+  if (dp.n_u != p->n_u || dp.q != p->q || dp.hash != host_plan_hash(*p, P)) {
+    c->dev_dirty = true;
+    return fail(FT_EHIP, "decode: device and host cache decisions differ");
+  }
   std::memcpy(p->idx, c->h_idx, (size_t)P * 4);
   std::memcpy(p->gates, c->h_gates, (size_t)P * 4);
   const int n_h = p->n_h, q = p->q, n_c = p->n_c, n_g = n_h + q;
@@ -618,53 +741,23 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
     }
     ft::cpu_pool_submit(c->cpu, c->h_x, T, d, c->shape.d_ff, c->shape.fmt, c->cpu_ex.data(), n_c, c->h_partial);
   }
-  // fills of F on the copy stream
+  // fills of F on the copy stream, then their grouped FFN
+  int rows_of[FT_PLAN_CAP] = {0};
+  int max_rows = 0;
+  for (int i = 0; i < P; ++i)
+    if (p->pair_group[i] >= 0) max_rows = std::max(max_rows, ++rows_of[p->pair_group[i]]);
   if (q > 0) {
-    FT_HIP(hipStreamWaitEvent(ps, c->ev_route, 0));
+    // no device-side wait is needed before the fills: the router has published, so
+    // every kernel queued before it has finished, and the victims exclude the slots
+    // that this call's hits read
     for (int i = 0; i < q; ++i)
       FT_HIP(hipMemcpyAsync(c->slot_ptr(p->F_slot[i]), c->record(layer, p->M[i]), c->S, hipMemcpyHostToDevice, ps));
     FT_HIP(hipEventRecord(c->ev_fill, ps));
     c->cache->stats.h2d_bytes += (int64_t)q * (int64_t)c->S;
-  }
-  // GPU path: grouping, grouped FFN of H, then of F once filled
-  int32_t* d_gslot = c->wsp<int32_t>(c->cv.gslot);
-  int32_t* d_off = c->wsp<int32_t>(c->cv.offsets);
-  int32_t* d_perm = c->wsp<int32_t>(c->cv.perm);
-  int32_t* d_inv = c->wsp<int32_t>(c->cv.inv);
-  float* d_h = c->wsp<float>(c->cv.h);
-  float* d_out = c->wsp<float>(c->cv.out);
-  std::memcpy(c->h_key, p->pair_group, (size_t)P * 4);
-  std::memcpy(c->h_gslot, p->G_slot, (size_t)std::max(n_g, 1) * 4);
-  int max_rows = 0;
-  {
-    int cnt[FT_PLAN_CAP] = {0};
-    for (int i = 0; i < P; ++i)
-      if (p->pair_group[i] >= 0) max_rows = std::max(max_rows, ++cnt[p->pair_group[i]]);
-  }
-  // grouping reads the pair keys and group slots from pinned host memory
-  if (int rc = ft::launch_permute(c->h_key, P, std::max(n_g, 1), d_off, d_perm, d_inv, c->ws + c->cv.pws,
-                                  c->cv.pws_bytes, cs, c->h_gslot, d_gslot, n_g))
-    return rc;
-  const uint16_t* xs = static_cast<const uint16_t*>(x);
-  int rows_of[FT_PLAN_CAP] = {0};
-  for (int i = 0; i < P; ++i)
-    if (p->pair_group[i] >= 0) rows_of[p->pair_group[i]] += 1;
-  auto ffn = [&](int g0, int g1) -> int {
-    ft_ctx::ProfRec* r = prof_begin(c);
-    if (r) prof_account(c, r, rows_of + g0, g1 - g0, 4);
-    void* const* ev = r ? reinterpret_cast<void* const*>(r->ev) : nullptr;
-    if (c->mx)
-      return ft::launch_mx_ffn_rows(xs, d, c->shape.d_ff, k, c->slots, d_gslot, d_off, d_perm, g0, g1, max_rows, d_h,
-                                    d_out, cs, ev);
-    return ft::launch_ffn_rows(xs, d, c->shape.d_ff, k, reinterpret_cast<const uint16_t*>(c->slots), d_gslot, d_off,
-                               d_perm, g0, g1, max_rows, d_h, d_out, cs, ev);
-  };
-  if (n_h > 0)
-    if (int rc = ffn(0, n_h)) return rc;
-  if (q > 0) {
     FT_HIP(hipStreamWaitEvent(cs, c->ev_fill, 0));
-    if (int rc = ffn(n_h, n_g)) return rc;
+    if (int rc = ffn(n_h, n_g, max_rows, nullptr, rows_of)) return rc;
   }
+  if (prof_h < c->prof.size()) prof_account(c, &c->prof[prof_h], rows_of, n_h, 4);
   // merge of the CPU partial, then the combine
   const double t3 = now_us();
   const float* cpu_part = nullptr;
@@ -676,7 +769,7 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
     if (st) st->cpu_caller_items = ft::cpu_pool_last_caller_items(c->cpu);
     cpu_part = c->h_partial;  // the combine reads the host partial from pinned memory
   }
-  if (int rc = ft::launch_combine(d_out, d_inv, d_gates, cpu_part, T, k, d, y, cs)) return rc;
+  if (int rc = ft::launch_combine(d_out, c->d_plan->inv, d_gates, cpu_part, T, k, d, y, cs)) return rc;
   FT_HIP(hipEventRecord(c->ev_done, cs));
   if (st) {
     st->layer = layer;
@@ -818,6 +911,7 @@ int ft_moe_prefill_end(ft_ctx_t c) {
   // the last two layers processed stay resident (all L layers in a full prefill)
   c->cache->prefill_end(c->dev ? std::max(c->prefill_next, 0) : c->shape.L);
   c->prefill_next = -1;
+  c->dev_dirty = true;
   return FT_OK;
 }
 
@@ -855,6 +949,7 @@ int ft_profile_read(ft_ctx_t c, ft_profile* out) {
       for (int g = 0; g < r.n_groups; ++g) rows[g] = r.offsets[g + 1] - r.offsets[g];
       prof_account(c, &r, rows.data(), r.n_groups, r.hb);
     }
+    if (r.bytes_up <= 0.0) continue;  // a decode launch whose plan had no group for it
     out->launches += 1;
     out->ms_gateup += a;
     out->ms_down += b;

@@ -39,6 +39,12 @@ class ExpertCache {
   void resize(int n_slots);  // all slots empty, counters reset, clock kept
   int32_t where(int layer, int e) const;
 
+  // the whole state, for a copy in device memory
+  const std::vector<int32_t>& slot_keys() const { return slot_key_; }
+  const std::vector<int64_t>& slot_stamps() const { return slot_stamp_; }
+  const std::vector<int32_t>& where_table() const { return where_; }
+  int64_t clock() const { return clock_; }
+
   ft_stats stats{};
 
  private:

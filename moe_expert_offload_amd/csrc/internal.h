@@ -19,13 +19,64 @@ int fail(int status, const std::string& msg);
 int launch_router(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, int T, int d,
                   int E, int k, int32_t* idx, float* gates, float* logits_ws, void* stream);
 
+// Decisions of one decode call as the device computes them ([FT] §4.1
+// "Device-side cache control"), with the grouping of the routed pairs: the
+// grouped FFN and the combine read offsets/perm/inv/G_slot from here.
+struct DevPlan {
+  int32_t P, n_u, n_h, n_m, q, n_c, avail, n_g;
+  uint32_t hash;  // plan_term hash of the decisions (the host compares it with its own)
+  int32_t U[FT_PLAN_CAP], H[FT_PLAN_CAP], M[FT_PLAN_CAP], F_slot[FT_PLAN_CAP], G_slot[FT_PLAN_CAP];
+  int32_t route_slot[FT_PLAN_CAP], pair_group[FT_PLAN_CAP];
+  int32_t offsets[FT_PLAN_CAP + 1], perm[FT_PLAN_CAP], inv[FT_PLAN_CAP];
+};
+
+// Hash of a plan: the sum over j of plan_term(j, v_j) for the sequence n_u, n_h,
+// n_m, q, avail, U, H, M, G_slot (n_h + q entries), route_slot and pair_group (P
+// entries each); a sum, so threads can form it in any order.
+#ifdef __HIPCC__
+#define FT_HD __host__ __device__
+#else
+#define FT_HD
+#endif
+FT_HD inline uint32_t plan_term(int j, int32_t v) {
+  uint32_t h = (uint32_t)v + 0x9e3779b9u * (uint32_t)(j + 1);
+  h ^= h >> 16;
+  h *= 0x85ebca6bu;
+  h ^= h >> 13;
+  h *= 0xc2b2ae35u;
+  h ^= h >> 16;
+  return h;
+}
+
+// Residency state of the cache in device memory (mirrors ExpertCache).
+struct DevCache {
+  int32_t* where;       // [L*E] slot or -1
+  int32_t* slot_key;    // [n_slots] l*E+e, or -1 empty
+  int64_t* slot_stamp;  // [n_slots] recency stamp, -1 empty
+  int64_t* clock;       // [1]
+  int32_t n_slots, E;
+};
+
+// What the decode router does after the top-k when decisions run on the device.
+struct DecideArgs {
+  DevCache dc;
+  DevPlan* plan;  // device
+  DevPlan* pub;   // pinned host copy for the host (scalars and the first P / n_u entries)
+  int32_t layer;
+  uint32_t fq;
+  int32_t min_fill, max_fetch;
+};
+
 // Decode router in one launch (T <= 64): also publishes idx, gates and x to
 // pinned host memory (pub_* may be null), then writes seq to *pub_flag; ticket
-// is a zeroed device counter.
+// is a zeroed device counter.  With `da`, the last block also takes the cache
+// decisions of the call on the device (dedup, classify, split, victims, slot
+// rewrite, stamps) and the grouping of the pairs, updates the device state and
+// publishes the plan before the flag.
 int launch_router_decode(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, int T, int d,
                          int E, int k, float* logits_ws, int32_t* idx, float* gates,
                          unsigned int* ticket, int32_t* pub_idx, float* pub_gates, uint16_t* pub_x,
-                         uint32_t* pub_flag, uint32_t seq, void* stream);
+                         uint32_t* pub_flag, uint32_t seq, void* stream, const DecideArgs* da = nullptr);
 
 size_t permute_ws_bytes(int P, int n_groups);
 // For P <= 1024 one block does everything and ws is not used; key may then live
@@ -36,10 +87,12 @@ int launch_permute(const int32_t* key, int P, int n_groups, int32_t* offsets, in
 
 // Row-streaming (GEMV-like) grouped FFN: h fp32 [rows, d_ff], out fp32 [rows, d].
 // ev (nullable): four hipEvent_t, start/stop of the gate/up kernel then of the down kernel.
+// g_hi (nullable, device): when given, only groups below *g_hi run (the launch
+// covers [g_begin, g_end) as an upper bound, for plans the host has not seen).
 int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
                     const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
                     int g_begin, int g_end, int max_rows, float* h, float* out, void* stream,
-                    void* const* ev = nullptr);
+                    void* const* ev = nullptr, const int32_t* g_hi = nullptr);
 
 // MFMA tile grouped FFN: h bf16 [rows, d_ff] (in the fp32-sized workspace), out fp32 [rows, d].
 int launch_ffn_mfma(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
@@ -53,7 +106,7 @@ size_t mx_record_bytes(int d, int d_ff);
 // Row-streaming grouped FFN over MXFP4 records, bf16 x: h fp32 [rows, d_ff], out fp32 [rows, d].
 int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t* slots, const int32_t* group_slot,
                        const int32_t* offsets, const int32_t* perm, int g_begin, int g_end, int max_rows, float* h,
-                       float* out, void* stream, void* const* ev = nullptr);
+                       float* out, void* stream, void* const* ev = nullptr, const int32_t* g_hi = nullptr);
 
 // Bytes of an MXFP8 copy of rows x n activations (codes then one scale per 32).
 size_t mx_act_ws_bytes(int rows, int n);

@@ -18,6 +18,10 @@
 
 namespace {
 
+using ft::DecideArgs;
+using ft::DevPlan;
+using ft::plan_term;
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -158,6 +162,13 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   return v;
 }
 
+// The logit a rank key was made from (zero comes back as +0, which the gate
+// arithmetic cannot tell from -0).
+__device__ __forceinline__ float key_logit(unsigned long long key) {
+  const uint32_t u = (uint32_t)(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
 // Top-k of one token by one wavefront: k rounds of a wave arg-max over the
 // allowed experts, each winner removed; softmax over the k winners.  Writes the
 // device outputs and, when given, copies to pinned host memory.
@@ -188,7 +199,7 @@ __device__ void topk_token(const float* __restrict__ lg, const uint8_t* __restri
         for (int s = 0; s < 16; ++s)
           if (lane + 64 * s == e) key[s] = 0ull;
         se[r] = e;
-        sv[r] = lg[e];
+        sv[r] = key_logit(b);
       }
     }
   }
@@ -225,55 +236,355 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
              idx + (size_t)t * k, gates + (size_t)t * k, nullptr, nullptr);
 }
 
-// Decode router in one launch: blocks compute logits (one token x 16 experts
-// each) and the blocks with blockIdx.y == 0 copy their token's x row to pinned
-// host memory; the last block to finish (device-scope fence + ticket counter,
-// no waiting) does the top-k of every token and publishes ids and gates to
-// pinned host memory.  `ticket` is a zeroed device counter, reset by the last
-// block.
-__global__ __launch_bounds__(256) void router_decode_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint8_t* __restrict__ allowed,
-    int T, int d, int E, int k, float* __restrict__ logits, int32_t* __restrict__ idx,
-    float* __restrict__ gates, unsigned int* __restrict__ ticket, int32_t* pub_idx, float* pub_gates,
-    uint16_t* pub_x, uint32_t* pub_flag, uint32_t seq) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int t = blockIdx.x;
-  const int e0 = (blockIdx.y * 4 + wave) * 4;
-  if (e0 < E) {
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const int J = (d + 511) >> 9;
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    for (int j = 0; j < J; ++j) {
-      const int i0 = j * 512 + lane * 8;
-      const bool in = i0 < d;
-      const uint4 xv = in ? ld16(x + (size_t)t * d + i0) : zero;
-      uint4 wv[4];
+// ---- device-side cache decisions ([FT] §4.1 "Device-side cache control") ----------
+// Exclusive prefix sum over the 256 threads of a block; *total gets the block sum.
+__device__ int block_excl_scan_256(int v, int* total) {
+  __shared__ int ws[4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int inc = v;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) wv[b] = (in && e0 + b < E) ? ld16(w + (size_t)(e0 + b) * d + i0) : zero;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o, WAVE);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) ws[wv] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const uint32_t xw = (r >> 1) == 0 ? xv.x : (r >> 1) == 1 ? xv.y : (r >> 1) == 2 ? xv.z : xv.w;
-        const float xf = (r & 1) ? bf_hi(xw) : bf_lo(xw);
+  for (int w = 0; w < 4; ++w) {
+    base += w < wv ? ws[w] : 0;
+    tot += ws[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+// q* of [FT] Eqs. (1)-(4) in Q16 with the floor and caps; the same integer rule as
+// ft_qstar_split on the host.
+__device__ int qstar_device(int m, uint32_t frac_q16, int min_fill, int max_fetch, int avail) {
+  if (m <= 0) return 0;
+  const long long fq = frac_q16, one = 65536;
+  const long long lo = ((long long)m * fq) >> 16;
+  const long long f0 = lo * (one - fq), h0 = (long long)(m - lo) * fq;
+  const long long f1 = (lo + 1) * (one - fq), h1 = (long long)(m - lo - 1) * fq;
+  const long long ms0 = f0 > h0 ? f0 : h0, ms1 = f1 > h1 ? f1 : h1;
+  long long q = ms1 < ms0 ? lo + 1 : lo;
+  if (q > m) q = m;
+  const long long floor_fill = min_fill < m ? min_fill : m;
+  if (q < floor_fill) q = floor_fill;
+  if (max_fetch >= 0 && q > max_fetch) q = max_fetch;
+  if (avail < 0) avail = 0;
+  if (q > avail) q = avail;
+  if (q < 0) q = 0;
+  return (int)q;
+}
+
+// (stamp, slot) order of victims, empty slots (stamp -1) first.
+__device__ __forceinline__ bool vkey_less(long long sa, int a, long long sb, int b) {
+  return sa < sb || (sa == sb && a < b);
+}
+
+// The decisions of one decode call, by the 256 threads of one block, for the P
+// routed ids in idx (device, written by this block): dedup in first-occurrence
+// order, classify against `where`, q from the split, the q least recently used
+// slots not holding a hit (by (stamp, slot)), eviction and admission, stamps of
+// H then F in first-occurrence order, the slot rewrite, and the stable grouping
+// of the pairs by G = H then F.  Same rule as ExpertCache::lookup.
+__device__ void decide_block(const DecideArgs& a, const int32_t* idx, int P) {
+  __shared__ int32_t s_id[FT_PLAN_CAP], s_u[FT_PLAN_CAP], s_pre[FT_PLAN_CAP], s_g[FT_PLAN_CAP];
+  __shared__ int32_t s_h[FT_PLAN_CAP], s_m[FT_PLAN_CAP], s_grp[FT_PLAN_CAP], s_cnt[FT_PLAN_CAP + 1];
+  __shared__ int32_t s_first[1024], s_pos[1024];
+  __shared__ long long s_bst[4];
+  __shared__ int s_bsl[4];
+  __shared__ int s_n_u, s_n_h, s_n_m, s_q;
+  __shared__ long long s_clock;
+  const int tid = threadIdx.x;
+  const int E = a.dc.E, base = a.layer * E;
+  DevPlan* pl = a.plan;
+  for (int i = tid; i < P; i += 256) s_id[i] = __hip_atomic_load(idx + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int e = tid; e < E; e += 256) {
+    s_first[e] = 0x7fffffff;
+    s_pos[e] = -1;
+  }
+  if (tid == 0) s_clock = *a.dc.clock;
+  __syncthreads();
+  // a token that allows fewer than k experts leaves -1 ids: no decisions, no groups
+  int bad = 0;
+  for (int i = tid; i < P; i += 256) bad |= s_id[i] < 0 || s_id[i] >= E;
+  if (__syncthreads_or(bad)) {
+    if (tid == 0) {
+      pl->n_u = -1;
+      pl->n_h = 0;
+      pl->n_g = 0;
+      pl->q = 0;
+      if (a.pub) a.pub->n_u = -1;
+    }
+    return;
+  }
+  for (int i = tid; i < P; i += 256) atomicMin(&s_first[s_id[i]], i);
+  __syncthreads();
+  // U: first occurrences in pair order
+  const int i0 = 2 * tid, i1 = 2 * tid + 1;
+  const int f0 = (i0 < P && s_first[s_id[i0]] == i0), f1 = (i1 < P && s_first[s_id[i1]] == i1);
+  int n_u;
+  int ex = block_excl_scan_256(f0 + f1, &n_u);
+  if (f0) s_u[ex] = s_id[i0];
+  if (f1) s_u[ex + f0] = s_id[i1];
+  __syncthreads();
+  // classify against the residency before this call
+  const int u0 = 2 * tid, u1 = 2 * tid + 1;
+  if (u0 < n_u) s_pre[u0] = a.dc.where[base + s_u[u0]];
+  if (u1 < n_u) s_pre[u1] = a.dc.where[base + s_u[u1]];
+  __syncthreads();
+  const int h0 = u0 < n_u && s_pre[u0] >= 0, h1 = u1 < n_u && s_pre[u1] >= 0;
+  const int m0 = u0 < n_u && !h0, m1 = u1 < n_u && !h1;
+  int n_h, n_m;
+  ex = block_excl_scan_256(h0 + h1, &n_h);
+  if (h0) s_h[ex] = u0;
+  if (h1) s_h[ex + h0] = u1;
+  ex = block_excl_scan_256(m0 + m1, &n_m);
+  if (m0) s_m[ex] = s_u[u0];
+  if (m1) s_m[ex + m0] = s_u[u1];
+  __syncthreads();
+  for (int i = tid; i < n_h; i += 256) {
+    s_pos[s_u[s_h[i]]] = i;  // group of a hit: its rank in H
+    s_g[i] = s_pre[s_h[i]];
+  }
+  if (tid == 0) {
+    s_n_u = n_u;
+    s_n_h = n_h;
+    s_n_m = n_m;
+    s_q = qstar_device(n_m, a.fq, a.min_fill, a.max_fetch, a.dc.n_slots - n_h);
+  }
+  __syncthreads();
+  const int q = s_q;
+  // victims: q rounds of the smallest (stamp, slot) above the previous pick, over
+  // the slots that do not hold a hit of this call.  Each thread keeps its slots'
+  // keys (stamp, or "not eligible") in registers when they fit.
+  constexpr int VR = 16;
+  long long vst[VR];
+  const int n_sl = a.dc.n_slots;
+  const bool in_regs = n_sl <= VR * 256;
+  if (q > 0 && in_regs) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const uint32_t ww = (r >> 1) == 0 ? wv[b].x : (r >> 1) == 1 ? wv[b].y : (r >> 1) == 2 ? wv[b].z : wv[b].w;
-          const float wf = (r & 1) ? bf_hi(ww) : bf_lo(ww);
-          acc[b] = acc[b] + xf * wf;  // same order as router_logits_kernel
+    for (int j = 0; j < VR; ++j) {
+      const int sl = tid + 256 * j;
+      vst[j] = 0x7fffffffffffffffll;
+      if (sl < n_sl) {
+        const int key = a.dc.slot_key[sl];
+        if (!(key >= base && key < base + E && s_pos[key - base] >= 0)) vst[j] = a.dc.slot_stamp[sl];
+      }
+    }
+  }
+  long long prev_st = -2;
+  int prev_sl = -1;
+  const int lane = tid & 63, wv = tid >> 6;
+  for (int r = 0; r < q; ++r) {
+    long long best_st = 0x7fffffffffffffffll;
+    int best_sl = 0x7fffffff;
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < VR; ++j) {
+        const int sl = tid + 256 * j;
+        const long long st = vst[j];
+        if (sl < n_sl && st != 0x7fffffffffffffffll && vkey_less(prev_st, prev_sl, st, sl) &&
+            vkey_less(st, sl, best_st, best_sl)) {
+          best_st = st;
+          best_sl = sl;
+        }
+      }
+    } else {
+      for (int sl = tid; sl < n_sl; sl += 256) {
+        const int key = a.dc.slot_key[sl];
+        if (key >= base && key < base + E && s_pos[key - base] >= 0) continue;  // holds a hit
+        const long long st = a.dc.slot_stamp[sl];
+        if (vkey_less(prev_st, prev_sl, st, sl) && vkey_less(st, sl, best_st, best_sl)) {
+          best_st = st;
+          best_sl = sl;
         }
       }
     }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      float v = acc[b];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) v = v + __shfl_xor(v, o, WAVE);
-      acc[b] = v;
+    for (int o = 32; o >= 1; o >>= 1) {
+      const long long ost = __shfl_xor(best_st, o, WAVE);
+      const int osl = __shfl_xor(best_sl, o, WAVE);
+      if (vkey_less(ost, osl, best_st, best_sl)) {
+        best_st = ost;
+        best_sl = osl;
+      }
     }
-    if (lane == 0)
+    if (lane == 0) {
+      s_bst[wv] = best_st;
+      s_bsl[wv] = best_sl;
+    }
+    __syncthreads();
+    best_st = s_bst[0];
+    best_sl = s_bsl[0];
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (e0 + b < E) logits[(size_t)t * E + e0 + b] = acc[b];
+    for (int w = 1; w < 4; ++w)
+      if (vkey_less(s_bst[w], s_bsl[w], best_st, best_sl)) {
+        best_st = s_bst[w];
+        best_sl = s_bsl[w];
+      }
+    if (tid == 0) s_g[n_h + r] = best_sl;
+    prev_st = best_st;
+    prev_sl = best_sl;
+    __syncthreads();
+  }
+  // eviction and admission of F = M[0:q] (sequential, q is small)
+  if (tid == 0) {
+    for (int i = 0; i < q; ++i) {
+      const int sl = s_g[n_h + i];
+      const int old = a.dc.slot_key[sl];
+      if (old >= 0) a.dc.where[old] = -1;
+      a.dc.slot_key[sl] = base + s_m[i];
+      a.dc.where[base + s_m[i]] = sl;
+    }
+  }
+  for (int i = tid; i < q; i += 256) s_pos[s_m[i]] = n_h + i;
+  __syncthreads();
+  // stamps: H and F in first-occurrence order
+  const int r0 = u0 < n_u && s_pos[s_u[u0]] >= 0, r1 = u1 < n_u && s_pos[s_u[u1]] >= 0;
+  int n_res;
+  ex = block_excl_scan_256(r0 + r1, &n_res);
+  if (r0) a.dc.slot_stamp[s_g[s_pos[s_u[u0]]]] = s_clock + ex + 1;
+  if (r1) a.dc.slot_stamp[s_g[s_pos[s_u[u1]]]] = s_clock + ex + r0 + 1;
+  if (tid == 0) *a.dc.clock = s_clock + n_res;
+  // slot rewrite and group of every pair
+  const int n_g = n_h + q;
+  for (int g = tid; g <= n_g; g += 256) s_cnt[g] = 0;
+  __syncthreads();
+  for (int i = tid; i < P; i += 256) {
+    const int g = s_pos[s_id[i]];
+    s_grp[i] = g;
+    if (g >= 0) atomicAdd(&s_cnt[g], 1);
+  }
+  __syncthreads();
+  // offsets over the groups (n_g <= 512: two per thread)
+  const int c0 = i0 < n_g ? s_cnt[i0] : 0, c1 = i1 < n_g ? s_cnt[i1] : 0;
+  int tot;
+  ex = block_excl_scan_256(c0 + c1, &tot);
+  if (i0 < n_g) pl->offsets[i0] = ex;
+  if (i1 < n_g) pl->offsets[i1] = ex + c0;
+  __syncthreads();
+  if (i0 < n_g) s_cnt[i0] = ex;
+  if (i1 < n_g) s_cnt[i1] = ex + c0;
+  if (tid == 0) pl->offsets[n_g] = tot;
+  __syncthreads();
+  for (int i = tid; i < P; i += 256) {
+    const int g = s_grp[i];
+    pl->pair_group[i] = g;
+    pl->route_slot[i] = g >= 0 ? s_g[g] : -1;
+    if (g < 0) {
+      pl->inv[i] = -1;
+    } else {
+      int rank = 0;
+      for (int j = 0; j < i; ++j) rank += s_grp[j] == g;
+      const int pos = s_cnt[g] + rank;
+      pl->perm[pos] = i;
+      pl->inv[i] = pos;
+    }
+  }
+  for (int i = tid; i < n_u; i += 256) pl->U[i] = s_u[i];
+  for (int i = tid; i < n_h; i += 256) pl->H[i] = s_u[s_h[i]];
+  for (int i = tid; i < n_m; i += 256) pl->M[i] = s_m[i];
+  for (int i = tid; i < n_g; i += 256) pl->G_slot[i] = s_g[i];
+  for (int i = tid; i < q; i += 256) pl->F_slot[i] = s_g[n_h + i];
+  if (tid == 0) {
+    pl->P = P;
+    pl->n_u = n_u;
+    pl->n_h = n_h;
+    pl->n_m = n_m;
+    pl->q = q;
+    pl->n_c = n_m - q;
+    pl->avail = a.dc.n_slots - n_h;
+    pl->n_g = n_g;
+  }
+  // the host takes the same decisions from the published ids; it checks them
+  // against a hash of the device's (plan_term summed over the sequence of values)
+  __shared__ uint32_t s_hash;
+  if (tid == 0) s_hash = 0u;
+  __syncthreads();
+  const int avail = a.dc.n_slots - n_h;
+  const int n_seq = 5 + n_u + n_h + n_m + n_g + 2 * P;
+  uint32_t part = 0u;
+  for (int j = tid; j < n_seq; j += 256) {
+    int v, r = j;
+    if (r < 5) {
+      v = r == 0 ? n_u : r == 1 ? n_h : r == 2 ? n_m : r == 3 ? q : avail;
+    } else if ((r -= 5) < n_u) {
+      v = s_u[r];
+    } else if ((r -= n_u) < n_h) {
+      v = s_u[s_h[r]];
+    } else if ((r -= n_h) < n_m) {
+      v = s_m[r];
+    } else if ((r -= n_m) < n_g) {
+      v = s_g[r];
+    } else if ((r -= n_g) < P) {
+      v = s_grp[r] >= 0 ? s_g[s_grp[r]] : -1;
+    } else {
+      v = s_grp[r - P];
+    }
+    part += plan_term(j, v);
+  }
+  atomicAdd(&s_hash, part);
+  __syncthreads();
+  if (tid == 0) {
+    pl->hash = s_hash;
+    if (a.pub != nullptr) {
+      a.pub->n_u = n_u;
+      a.pub->q = q;
+      a.pub->hash = s_hash;
+    }
+  }
+}
+
+// Decode router in one launch: one wavefront per (token, expert) logit (same
+// arithmetic order as router_logits_kernel: lane l owns elements (i mod 512)/8 ==
+// l, adds its products in increasing i, then a butterfly); the blocks with
+// blockIdx.y == 0 copy their token's x row to pinned host memory; the last block
+// to finish (device-scope fence + ticket counter, no waiting) does the top-k of
+// every token, the cache decisions when asked, and publishes to pinned host
+// memory.  `ticket` is a zeroed device counter, reset by the last block.
+__global__ __launch_bounds__(256) void router_decode_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint8_t* __restrict__ allowed,
+    int T, int d, int E, int k, float* __restrict__ logits, int32_t* __restrict__ idx,
+    float* __restrict__ gates, unsigned int* __restrict__ ticket, int32_t* pub_idx, float* pub_gates,
+    uint16_t* pub_x, uint32_t* pub_flag, uint32_t seq, DecideArgs da, int decide) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x;
+  const int e = blockIdx.y * 4 + wave;
+  if (e < E) {
+    float acc = 0.0f;
+    const int J = (d + 511) >> 9;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    for (int j0 = 0; j0 < J; j0 += 8) {
+      uint4 xv[8], wv[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int i0 = (j0 + jj) * 512 + lane * 8;
+        const bool in = j0 + jj < J && i0 < d;
+        xv[jj] = in ? ld16(x + (size_t)t * d + i0) : zero;
+        wv[jj] = in ? ld16(w + (size_t)e * d + i0) : zero;
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (j0 + jj >= J) break;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const uint32_t xw = (r >> 1) == 0 ? xv[jj].x : (r >> 1) == 1 ? xv[jj].y : (r >> 1) == 2 ? xv[jj].z : xv[jj].w;
+          const uint32_t ww = (r >> 1) == 0 ? wv[jj].x : (r >> 1) == 1 ? wv[jj].y : (r >> 1) == 2 ? wv[jj].z : wv[jj].w;
+          const float xf = (r & 1) ? bf_hi(xw) : bf_lo(xw);
+          const float wf = (r & 1) ? bf_hi(ww) : bf_lo(ww);
+          acc = acc + xf * wf;  // same order as router_logits_kernel
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o, WAVE);
+    if (lane == 0) logits[(size_t)t * E + e] = acc;
   }
   if (blockIdx.y == 0 && pub_x != nullptr)
     for (int i = threadIdx.x * 8; i < d; i += 256 * 8)
@@ -289,6 +600,9 @@ __global__ __launch_bounds__(256) void router_decode_kernel(
     topk_token(logits + (size_t)tt * E, allowed ? allowed + (size_t)tt * E : nullptr, E, k, lane,
                idx + (size_t)tt * k, gates + (size_t)tt * k, pub_idx ? pub_idx + (size_t)tt * k : nullptr,
                pub_gates ? pub_gates + (size_t)tt * k : nullptr);
+  __threadfence();
+  __syncthreads();
+  if (decide) decide_block(da, idx, T * k);
   __threadfence_system();
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -445,12 +759,13 @@ template <int NT>
 __global__ __launch_bounds__(256) void ffn_gateup_rows_kernel(
     const uint16_t* __restrict__ x, int d, int d_ff, int k, const uint16_t* __restrict__ slots,
     size_t rec_elems, const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ perm, int g_begin, int blocks_per_group, float* __restrict__ h) {
+    const int32_t* __restrict__ perm, int g_begin, int blocks_per_group, float* __restrict__ h,
+    const int32_t* __restrict__ g_hi) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
   const int row = (blockIdx.x % blocks_per_group) * 4 + wave;
-  if (row >= d_ff) return;
+  if (row >= d_ff || (g_hi != nullptr && g >= *g_hi)) return;
   const int r0 = offsets[g];
   const int n = offsets[g + 1] - r0;
   if (n <= 0) return;
@@ -505,12 +820,12 @@ template <int NT>
 __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
     int d, int d_ff, const uint16_t* __restrict__ slots, size_t rec_elems,
     const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, int g_begin,
-    int blocks_per_group, const float* __restrict__ h, float* __restrict__ out) {
+    int blocks_per_group, const float* __restrict__ h, float* __restrict__ out, const int32_t* __restrict__ g_hi) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
   const int row = (blockIdx.x % blocks_per_group) * 4 + wave;
-  if (row >= d) return;
+  if (row >= d || (g_hi != nullptr && g >= *g_hi)) return;
   const int r0 = offsets[g];
   const int n = offsets[g + 1] - r0;
   if (n <= 0) return;
@@ -867,14 +1182,19 @@ int launch_router(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, 
 int launch_router_decode(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, int T, int d,
                          int E, int k, float* logits_ws, int32_t* idx, float* gates,
                          unsigned int* ticket, int32_t* pub_idx, float* pub_gates, uint16_t* pub_x,
-                         uint32_t* pub_flag, uint32_t seq, void* stream) {
+                         uint32_t* pub_flag, uint32_t seq, void* stream, const DecideArgs* da) {
   if (T < 1 || T > 64 || d <= 0 || d % 8 != 0 || E <= 0 || E > 1024 || k < 1 || k > 8 || k > E)
     return fail(FT_EINVAL, "router: need T<=64, d%8==0, 1<=k<=min(E,8), E<=1024");
   if (!aligned16(x) || !aligned16(w) || (pub_x && !aligned16(pub_x)))
     return fail(FT_EINVAL, "router: unaligned pointer");
-  dim3 grid(T, (E + 15) / 16);
+  if (da && (T * k > FT_PLAN_CAP || !da->plan || !da->dc.where || (da->dc.n_slots > 0 && (!da->dc.slot_key ||
+                                                                                       !da->dc.slot_stamp))))
+    return fail(FT_EINVAL, "router: bad decision arguments");
+  DecideArgs none{};
+  dim3 grid(T, (E + 3) / 4);
   router_decode_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(
-      x, w, allowed, T, d, E, k, logits_ws, idx, gates, ticket, pub_idx, pub_gates, pub_x, pub_flag, seq);
+      x, w, allowed, T, d, E, k, logits_ws, idx, gates, ticket, pub_idx, pub_gates, pub_x, pub_flag, seq,
+      da ? *da : none, da ? 1 : 0);
   return launched("router_decode");
 }
 
@@ -925,7 +1245,7 @@ inline void timed_launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStrea
 int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
                     const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
                     int g_begin, int g_end, int max_rows, float* h, float* out, void* stream,
-                    void* const* ev) {
+                    void* const* ev, const int32_t* g_hi) {
   if (d <= 0 || d_ff <= 0 || d % 8 || d_ff % 8 || k < 1) return fail(FT_EINVAL, "ffn_rows: bad shape");
   const int ng = g_end - g_begin;
   if (ng <= 0) return FT_OK;
@@ -938,10 +1258,10 @@ int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
   const int nt = max_rows <= 1 ? 1 : max_rows <= 2 ? 2 : max_rows <= 4 ? 4 : 8;
 #define FT_ROWS_LAUNCH(NT)                                                                        \
   timed_launch(ffn_gateup_rows_kernel<NT>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
-               slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h);                   \
+               slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_hi);             \
   if (int rc = launched("ffn_gateup_rows")) return rc;                                            \
   timed_launch(ffn_down_rows_kernel<NT>, dim3(ng * bpg_dn), dim3(256), s, ev, 1, d, d_ff, slots,   \
-               rec_elems, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out);             \
+               rec_elems, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out, g_hi);       \
   return launched("ffn_down_rows");
   switch (nt) {
     case 1: { FT_ROWS_LAUNCH(1) }

@@ -111,12 +111,12 @@ template <int NT>
 __global__ __launch_bounds__(256) void mx_gateup_rows_kernel(
     const uint16_t* __restrict__ x, int d, int d_ff, int k, const uint8_t* __restrict__ slots,
     const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-    int g_begin, int blocks_per_group, float* __restrict__ h) {
+    int g_begin, int blocks_per_group, float* __restrict__ h, const int32_t* __restrict__ g_hi) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
   const int row = (blockIdx.x % blocks_per_group) * 4 + wave;
-  if (row >= d_ff) return;
+  if (row >= d_ff || (g_hi != nullptr && g >= *g_hi)) return;
   const int r0 = offsets[g];
   const int n = offsets[g + 1] - r0;
   if (n <= 0) return;
@@ -161,12 +161,12 @@ template <int NT>
 __global__ __launch_bounds__(256) void mx_down_rows_kernel(
     int d, int d_ff, const uint8_t* __restrict__ slots, const int32_t* __restrict__ group_slot,
     const int32_t* __restrict__ offsets, int g_begin, int blocks_per_group, const float* __restrict__ h,
-    float* __restrict__ out) {
+    float* __restrict__ out, const int32_t* __restrict__ g_hi) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
   const int row = (blockIdx.x % blocks_per_group) * 4 + wave;
-  if (row >= d) return;
+  if (row >= d || (g_hi != nullptr && g >= *g_hi)) return;
   const int r0 = offsets[g];
   const int n = offsets[g + 1] - r0;
   if (n <= 0) return;
@@ -619,7 +619,7 @@ size_t mx_record_bytes(int d, int d_ff) { return mx_rec(d, d_ff).bytes; }
 
 int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t* slots, const int32_t* group_slot,
                        const int32_t* offsets, const int32_t* perm, int g_begin, int g_end, int max_rows, float* h,
-                       float* out, void* stream, void* const* ev) {
+                       float* out, void* stream, void* const* ev, const int32_t* g_hi) {
   if (d % 64 || d_ff % 64 || k < 1) return fail(FT_EINVAL, "mx_ffn_rows: need d%64==0 and d_ff%64==0");
   const int ng = g_end - g_begin;
   if (ng <= 0) return FT_OK;
@@ -630,10 +630,10 @@ int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t*
   const int nt = max_rows <= 1 ? 1 : max_rows <= 2 ? 2 : max_rows <= 4 ? 4 : 8;
 #define FT_MX_ROWS(NT)                                                                                        \
   timed_launch(mx_gateup_rows_kernel<NT>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, slots,      \
-               group_slot, offsets, perm, g_begin, bpg_up, h);                                              \
+               group_slot, offsets, perm, g_begin, bpg_up, h, g_hi);                                        \
   if (int rc = launched("mx_gateup_rows")) return rc;                                                        \
   timed_launch(mx_down_rows_kernel<NT>, dim3(ng * bpg_dn), dim3(256), s, ev, 1, d, d_ff, slots, group_slot,  \
-               offsets, g_begin, bpg_dn, (const float*)h, out);                                               \
+               offsets, g_begin, bpg_dn, (const float*)h, out, g_hi);                                        \
   return launched("mx_down_rows");
   switch (nt) {
     case 1: { FT_MX_ROWS(1) }
