@@ -120,18 +120,18 @@ def run_decode(args, torch, ft, synth, HostPool):
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     ctx = ft.ft_create(fshape, cfg, pool.ptr, pool.nbytes, slots, N, ws, wsb)
     compute = torch.cuda.current_stream()
-    copy = torch.cuda.Stream()
     st_call = ft.ft_step_stats()
     calls = []
 
     def step(st, record):
         for l in range(s.L):
-            ft.ft_moe_decode_layer(ctx, l, xs[st, l], T, wr[l], allowed_d[st, l], ys[l], compute, copy,
+            ft.ft_moe_decode_layer(ctx, l, xs[st, l], T, wr[l], allowed_d[st, l], ys[l], compute,
                                    None, st_call)
             if record:
                 calls.append((st_call.hits, st_call.misses, st_call.q, st_call.n_c, st_call.t_cpu_us,
                                st_call.t_total_us, st_call.t_route_us, st_call.t_ctrl_us, st_call.t_issue_us,
-                               st_call.t_cpu_work_us, st_call.cpu_caller_items))
+                               st_call.t_cpu_work_us, st_call.cpu_caller_items, st_call.t_submit_us,
+                               st_call.t_between_us))
 
     try:
         for st in range(args.warmup):
@@ -195,6 +195,8 @@ def run_decode(args, torch, ft, synth, HostPool):
             "cpu_items_when_used": float(np.mean([c[3] * 48 + 64 for c in calls if c[3] > 0])) if any(c[3] > 0 for c in calls) else 0.0,
             "issue_when_fill": float(np.mean([c[8] for c in calls if c[2] > 0])) if any(c[2] > 0 for c in calls) else 0.0,
             "total": float(np.mean([c[5] for c in calls])) if calls else 0.0,
+            "submit": float(np.mean([c[11] for c in calls])) if calls else 0.0,
+            "between_calls": float(np.mean([c[12] for c in calls])) if calls else 0.0,
         },
         "timed_with_kernel_events_ms_per_step": (t3 - t2) / args.steps * 1e3,
         "kernels": {
@@ -350,7 +352,7 @@ def run_mxfp4(args, torch, ft, synth, HostPool):
                 ta = time.perf_counter()
                 for st in range(half * steps // 2, (half + 1) * steps // 2):
                     for l in range(s.L):
-                        ft.ft_moe_decode_layer(ctx, l, xd[st, l], 1, wr[l], allowed_d[st, l], yd[l], compute, copy,
+                        ft.ft_moe_decode_layer(ctx, l, xd[st, l], 1, wr[l], allowed_d[st, l], yd[l], compute,
                                                None, st_call)
                 torch.cuda.synchronize()
                 tb = time.perf_counter()

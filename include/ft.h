@@ -138,6 +138,8 @@ typedef struct {
   double t_total_us;   /* whole call, host side */
   double t_issue_us;   /* issuing the fills and the GPU work after the decisions */
   double t_cpu_work_us; /* CPU branch, from post to its last work item */
+  double t_submit_us;   /* posting the CPU branch to the worker threads */
+  double t_between_us;  /* caller's own time since the previous decode call returned (0 on the first) */
 } ft_step_stats;
 
 /* Cumulative counters since create or the last resize ([AIN] "How to run it in
@@ -185,8 +187,9 @@ int32_t ft_qstar_split(int32_t m, uint32_t frac_q16, int32_t min_fill, int32_t m
 int ft_pool_alloc(size_t bytes, void** out);
 int ft_pool_free(void* ptr);
 
-/* Measures B_P (pinned host->device copies of whole records, `n_records` of them,
- * on a fresh stream) and B_H (the host expert kernel over the same records at one
+/* Measures B_P (whole records read by the GPU from the pinned pool over PCIe into
+ * device memory, as the decode fills move them, `n_records` of them, one launch
+ * each, on a fresh stream) and B_H (the host expert kernel over the same records at one
  * token, `threads` workers; 0 = all) in bytes per second ([FT] §3.2, Table 1:
  * both measured on the deployed tensor shapes).  dev_scratch must hold
  * n_records records. */
@@ -318,17 +321,23 @@ int32_t ft_expert_cache_where(ft_ctx_t ctx, int32_t layer, int32_t expert);
 
 /* ---- layer forward ----------------------------------------------------------------- */
 
-/* One decode call of one MoE layer ([FT] §3.2, "In execution order"):
- * router on `compute`; ids to the host; decisions; the CPU branch (C) starts on
- * the worker pool; fills of F on `copy`; grouped FFN of H, then of F once its
- * fills landed; merge of the CPU partial; combine into y.  Returns when y is
- * enqueued on `compute` (the CPU branch has finished).
+/* One decode call of one MoE layer ([FT] §3.2, "In execution order"; §4.1,
+ * device-side cache control), every GPU step on `compute`: the router takes the
+ * call's decisions on the device (dedup, classify, q*, victims, stamps, grouping)
+ * and publishes ids, gates, x and a hash of the plan to pinned host memory; the
+ * fills of F are read by the GPU from the pinned pool over PCIe into the chosen
+ * slots; the grouped FFN of G = H then F.  Meanwhile the host controller takes
+ * the same decisions from the published ids (FT_EHIP if they differ from the
+ * device's) and runs the CPU branch (C) on the worker pool; then the merge of the
+ * CPU partial and the combine into y.  Returns when y is enqueued on `compute`
+ * (the CPU branch has finished).  The pool must be GPU-readable pinned memory
+ * (hipHostMalloc).
  * x: device bf16 [T, d]; w_router: device bf16 [E, d]; allowed: device uint8
  * [T, E] or NULL; y: device fp32 [T, d].  plan, stats: host, may be NULL.
  * T <= min(T_max, FT_PLAN_CAP / k, 64). */
 int ft_moe_decode_layer(ft_ctx_t ctx, int32_t layer, const void* x, int32_t T,
                         const void* w_router, const uint8_t* allowed, float* y, void* compute,
-                        void* copy, ft_plan* plan, ft_step_stats* stats);
+                        ft_plan* plan, ft_step_stats* stats);
 
 /* Full-layer double-buffered prefill ([FT] §3.1; §5.3 "Pipelined prefill").
  * begin: reserve two buffers of E slots (victim order) and start loading layer 0

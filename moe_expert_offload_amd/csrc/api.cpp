@@ -148,6 +148,7 @@ struct ft_ctx {
   float* h_partial = nullptr;
   uint32_t* h_flag = nullptr;  // router's publication sequence number
   uint32_t route_seq = 0;
+  double last_return_us = 0.0;  // host clock when the previous decode call returned
 
   // device copy of the residency state and the device-side plan ([FT] §4.1)
   ft::DevCache dc{};
@@ -156,7 +157,7 @@ struct ft_ctx {
   ft::DevPlan* d_plan = nullptr;  // device
   ft::DevPlan* h_plan = nullptr;  // pinned publication
 
-  hipEvent_t ev_route = nullptr, ev_fill = nullptr, ev_done = nullptr;
+  hipEvent_t ev_route = nullptr, ev_done = nullptr;
   hipEvent_t ev_pf_fill[2] = {nullptr, nullptr}, ev_pf_comp[2] = {nullptr, nullptr};
 
   ft::ExpertCache* cache = nullptr;
@@ -373,7 +374,7 @@ int ft_create(const ft_shape* shape, const ft_config* config, const void* host_p
         hipHostMalloc((void**)&c->h_partial, (size_t)c->t_dec * shape->d * 4) != hipSuccess ||
         hipHostMalloc((void**)&c->h_flag, 256) != hipSuccess)
       return bail(FT_ENOMEM, "create: pinned staging allocation failed");
-    hipEvent_t* evs[] = {&c->ev_route, &c->ev_fill, &c->ev_done, &c->ev_pf_fill[0], &c->ev_pf_fill[1],
+    hipEvent_t* evs[] = {&c->ev_route, &c->ev_done, &c->ev_pf_fill[0], &c->ev_pf_fill[1],
                          &c->ev_pf_comp[0], &c->ev_pf_comp[1]};
     for (hipEvent_t* e : evs)
       if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess)
@@ -410,7 +411,7 @@ int ft_destroy(ft_ctx_t c) {
     (void)hipDeviceSynchronize();
   }
   if (c->cpu) ft::cpu_pool_destroy(c->cpu);
-  hipEvent_t evs[] = {c->ev_route, c->ev_fill, c->ev_done, c->ev_pf_fill[0], c->ev_pf_fill[1],
+  hipEvent_t evs[] = {c->ev_route, c->ev_done, c->ev_pf_fill[0], c->ev_pf_fill[1],
                       c->ev_pf_comp[0], c->ev_pf_comp[1]};
   for (hipEvent_t e : evs)
     if (e) (void)hipEventDestroy(e);
@@ -599,7 +600,7 @@ int ft_expert_cache_resize(ft_ctx_t c, void* new_dev_slots, int32_t n) {
     if (n > 0 && (!new_dev_slots || (reinterpret_cast<uintptr_t>(new_dev_slots) & 255)))
       return fail(FT_EINVAL, "resize: need a 256-byte aligned slot buffer");
     FT_HIP(hipSetDevice(c->device));
-    hipEvent_t evs[] = {c->ev_route, c->ev_fill, c->ev_done, c->ev_pf_fill[0], c->ev_pf_fill[1],
+    hipEvent_t evs[] = {c->ev_route, c->ev_done, c->ev_pf_fill[0], c->ev_pf_fill[1],
                         c->ev_pf_comp[0], c->ev_pf_comp[1]};
     for (hipEvent_t e : evs) {
       const hipError_t q = hipEventQuery(e);
@@ -622,7 +623,7 @@ int ft_expert_cache_resize(ft_ctx_t c, void* new_dev_slots, int32_t n) {
 // ---- decode ------------------------------------------------------------------------
 
 int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, const void* w_router,
-                        const uint8_t* allowed, float* y, void* compute, void* copy, ft_plan* plan_out,
+                        const uint8_t* allowed, float* y, void* compute, ft_plan* plan_out,
                         ft_step_stats* st) {
   const double t0 = now_us();
   if (!c || !x || !w_router || !y) return fail(FT_EINVAL, "decode: null argument");
@@ -633,7 +634,6 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
   const int P = T * k;
   FT_HIP(hipSetDevice(c->device));
   hipStream_t cs = static_cast<hipStream_t>(compute);
-  hipStream_t ps = static_cast<hipStream_t>(copy);
   int32_t* d_idx = c->wsp<int32_t>(c->cv.idx);
   float* d_gates = c->wsp<float>(c->cv.gates);
   // order after everything this context issued before, whatever the stream
@@ -643,8 +643,8 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
     if (int rc = upload_cache(c)) return rc;
   }
   // [FT] §4.1 device-side cache control: the router's last block takes this call's
-  // decisions on the device and groups the pairs, so the grouped FFN of the hits
-  // is queued right behind it without waiting for the host.  It publishes ids,
+  // decisions on the device and groups the pairs, so the fills and the grouped FFN
+  // are queued right behind it without waiting for the host.  It publishes ids,
   // gates, x and the plan to pinned host memory, then a sequence number.
   const uint32_t seq = ++c->route_seq == 0 ? ++c->route_seq : c->route_seq;
   ft::DecideArgs da{};
@@ -682,10 +682,13 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
                                c->d_plan->G_slot, c->d_plan->offsets, c->d_plan->perm, g0, g1, max_rows, d_h,
                                d_out, cs, ev, g_hi);
   };
-  // grouped FFN of the hits, launched for every possible group and bounded on the
-  // device by the plan's n_h
+  // the fills of F, read by the GPU from the pinned pool over PCIe into the victim
+  // slots the device chose, then the grouped FFN of G = H then F, launched for every
+  // possible group and bounded on the device by the plan's n_g
+  if (int rc = ft::launch_fill(c->record(layer, 0), c->S, E, c->slots, c->cache->n_slots(), c->d_plan, cs))
+    return rc;
   const size_t prof_h = c->prof.size();
-  if (int rc = ffn(0, P, nt_bound, &c->d_plan->n_h, nullptr)) return rc;
+  if (int rc = ffn(0, P, nt_bound, &c->d_plan->n_g, nullptr)) return rc;
   // wait for the publication (bounded spin on the sequence number, the event is
   // the fallback)
   {
@@ -729,6 +732,7 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
   const double t2 = now_us();
 
   // CPU branch first ([FT] §3.2, "In execution order")
+  const double t_sub0 = now_us();
   if (n_c > 0) {
     c->cpu_ex.resize(n_c);
     for (int i = 0; i < n_c; ++i) {
@@ -741,23 +745,12 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
     }
     ft::cpu_pool_submit(c->cpu, c->h_x, T, d, c->shape.d_ff, c->shape.fmt, c->cpu_ex.data(), n_c, c->h_partial);
   }
-  // fills of F on the copy stream, then their grouped FFN
+  const double t_sub1 = now_us();
   int rows_of[FT_PLAN_CAP] = {0};
-  int max_rows = 0;
   for (int i = 0; i < P; ++i)
-    if (p->pair_group[i] >= 0) max_rows = std::max(max_rows, ++rows_of[p->pair_group[i]]);
-  if (q > 0) {
-    // no device-side wait is needed before the fills: the router has published, so
-    // every kernel queued before it has finished, and the victims exclude the slots
-    // that this call's hits read
-    for (int i = 0; i < q; ++i)
-      FT_HIP(hipMemcpyAsync(c->slot_ptr(p->F_slot[i]), c->record(layer, p->M[i]), c->S, hipMemcpyHostToDevice, ps));
-    FT_HIP(hipEventRecord(c->ev_fill, ps));
-    c->cache->stats.h2d_bytes += (int64_t)q * (int64_t)c->S;
-    FT_HIP(hipStreamWaitEvent(cs, c->ev_fill, 0));
-    if (int rc = ffn(n_h, n_g, max_rows, nullptr, rows_of)) return rc;
-  }
-  if (prof_h < c->prof.size()) prof_account(c, &c->prof[prof_h], rows_of, n_h, 4);
+    if (p->pair_group[i] >= 0) ++rows_of[p->pair_group[i]];
+  c->cache->stats.h2d_bytes += (int64_t)q * (int64_t)c->S;
+  if (prof_h < c->prof.size()) prof_account(c, &c->prof[prof_h], rows_of, n_g, 4);
   // merge of the CPU partial, then the combine
   const double t3 = now_us();
   const float* cpu_part = nullptr;
@@ -787,7 +780,10 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
     st->t_total_us = now_us() - t0;
     st->t_issue_us = t3 - t2;
     st->t_cpu_work_us = t_cpu_work;
+    st->t_submit_us = t_sub1 - t_sub0;
+    st->t_between_us = c->last_return_us > 0.0 ? t0 - c->last_return_us : 0.0;
   }
+  c->last_return_us = now_us();
   return FT_OK;
 }
 
@@ -981,12 +977,17 @@ int ft_bench_bw(const ft_shape* shape, const void* host_pool, int32_t n_records,
     cleanup();
     return fail(FT_EHIP, "bench_bw: event create failed");
   }
+  // B_P: the rate at which the decode fills move records, read by the GPU from the
+  // pinned pool over PCIe one record per launch
   float best_ms = 1e30f;
   for (int rep = 0; rep < 4; ++rep) {
     (void)hipEventRecord(e0, s);
     for (int i = 0; i < n_records; ++i)
-      (void)hipMemcpyAsync(static_cast<uint8_t*>(dev_scratch) + (size_t)i * S,
-                           static_cast<const uint8_t*>(host_pool) + (size_t)i * S, S, hipMemcpyHostToDevice, s);
+      if (int rc = ft::launch_h2d_copy(static_cast<const uint8_t*>(host_pool) + (size_t)i * S,
+                                       static_cast<uint8_t*>(dev_scratch) + (size_t)i * S, S, s)) {
+        cleanup();
+        return rc;
+      }
     (void)hipEventRecord(e1, s);
     if (hipEventSynchronize(e1) != hipSuccess) {
       cleanup();

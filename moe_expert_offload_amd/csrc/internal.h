@@ -73,6 +73,14 @@ struct DecideArgs {
 // decisions of the call on the device (dedup, classify, split, victims, slot
 // rewrite, stamps) and the grouping of the pairs, updates the device state and
 // publishes the plan before the flag.
+// Decode fills read by the GPU from the pinned pool over PCIe: records M[0:q] of a
+// layer (layer_base = its expert 0, S bytes each) into slots F_slot[0:q] of the
+// device plan; stream-ordered after the router that wrote the plan.
+int launch_fill(const uint8_t* layer_base, size_t S, int E, uint8_t* slots, int n_slots, const DevPlan* plan,
+                void* stream);
+// Plain copy of pinned host memory to device memory by the same kernel reads.
+int launch_h2d_copy(const void* src, void* dst, size_t bytes, void* stream);
+
 int launch_router_decode(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, int T, int d,
                          int E, int k, float* logits_ws, int32_t* idx, float* gates,
                          unsigned int* ticket, int32_t* pub_idx, float* pub_gates, uint16_t* pub_x,

@@ -153,12 +153,30 @@ __device__ __forceinline__ unsigned long long rank_key(float v, int e) {
   return ((unsigned long long)u << 32) | (uint32_t)(0x7fffffff - e);
 }
 
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Maximum over a wavefront whose 64 lanes are all active: within each row of 16
+// lanes by DPP (swap neighbours, swap pairs, mirror the half rows, mirror the
+// row), then across the four rows.
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const unsigned long long w = __shfl_xor(v, o, WAVE);
-    v = w > v ? w : v;
-  }
+  unsigned long long w;
+  w = dpp_u64<0xb1>(v);  // quad_perm [1,0,3,2]
+  v = w > v ? w : v;
+  w = dpp_u64<0x4e>(v);  // quad_perm [2,3,0,1]
+  v = w > v ? w : v;
+  w = dpp_u64<0x141>(v);  // row_half_mirror
+  v = w > v ? w : v;
+  w = dpp_u64<0x140>(v);  // row_mirror
+  v = w > v ? w : v;
+  w = __shfl_xor(v, 16, WAVE);
+  v = w > v ? w : v;
+  w = __shfl_xor(v, 32, WAVE);
+  v = w > v ? w : v;
   return v;
 }
 
@@ -170,14 +188,16 @@ __device__ __forceinline__ float key_logit(unsigned long long key) {
 }
 
 // Top-k of one token by one wavefront: k rounds of a wave arg-max over the
-// allowed experts, each winner removed; softmax over the k winners.  Writes the
-// device outputs and, when given, copies to pinned host memory.
-__device__ void topk_token(const float* __restrict__ lg, const uint8_t* __restrict__ allowed, int E,
-                           int k, int lane, int32_t* __restrict__ idx, float* __restrict__ gates,
-                           int32_t* pub_idx, float* pub_gates) {
-  unsigned long long key[16];
+// allowed experts (NS per lane), each winner removed; softmax over the k winners.
+// Writes the device outputs and, when given, copies to pinned host memory and the
+// ids to shared memory.
+template <int NS>
+__device__ __forceinline__ void topk_token_ns(const float* __restrict__ lg, const uint8_t* __restrict__ allowed, int E, int k,
+                              int lane, int32_t* __restrict__ idx, float* __restrict__ gates, int32_t* pub_idx,
+                              float* pub_gates, int32_t* s_ids) {
+  unsigned long long key[NS];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
+  for (int s = 0; s < NS; ++s) {
     const int e = lane + 64 * s;
     const bool in = e < E && (allowed == nullptr || allowed[e] != 0);
     key[s] = in ? rank_key(lg[e], e) : 0ull;
@@ -189,14 +209,14 @@ __device__ void topk_token(const float* __restrict__ lg, const uint8_t* __restri
     sv[r] = 0.0f;
     se[r] = -1;
     if (r < k) {
-      unsigned long long b = 0ull;
+      unsigned long long b = key[0];
 #pragma unroll
-      for (int s = 0; s < 16; ++s) b = key[s] > b ? key[s] : b;
+      for (int s = 1; s < NS; ++s) b = key[s] > b ? key[s] : b;
       b = wave_max_u64(b);
       if (b != 0ull) {
         const int e = 0x7fffffff - (int)(uint32_t)(b & 0xffffffffu);
 #pragma unroll
-        for (int s = 0; s < 16; ++s)
+        for (int s = 0; s < NS; ++s)
           if (lane + 64 * s == e) key[s] = 0ull;
         se[r] = e;
         sv[r] = key_logit(b);
@@ -220,8 +240,24 @@ __device__ void topk_token(const float* __restrict__ lg, const uint8_t* __restri
           pub_idx[r] = se[r];
           pub_gates[r] = g;
         }
+        if (s_ids) s_ids[r] = se[r];
       }
   }
+}
+
+__device__ __forceinline__ void topk_token(const float* __restrict__ lg, const uint8_t* __restrict__ allowed, int E,
+                                           int k, int lane, int32_t* __restrict__ idx, float* __restrict__ gates,
+                                           int32_t* pub_idx, float* pub_gates, int32_t* s_ids = nullptr) {
+  if (E <= 64)
+    topk_token_ns<1>(lg, allowed, E, k, lane, idx, gates, pub_idx, pub_gates, s_ids);
+  else if (E <= 128)
+    topk_token_ns<2>(lg, allowed, E, k, lane, idx, gates, pub_idx, pub_gates, s_ids);
+  else if (E <= 256)
+    topk_token_ns<4>(lg, allowed, E, k, lane, idx, gates, pub_idx, pub_gates, s_ids);
+  else if (E <= 512)
+    topk_token_ns<8>(lg, allowed, E, k, lane, idx, gates, pub_idx, pub_gates, s_ids);
+  else
+    topk_token_ns<16>(lg, allowed, E, k, lane, idx, gates, pub_idx, pub_gates, s_ids);
 }
 
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
@@ -280,35 +316,71 @@ __device__ int qstar_device(int m, uint32_t frac_q16, int min_fill, int max_fetc
   return (int)q;
 }
 
-// (stamp, slot) order of victims, empty slots (stamp -1) first.
-__device__ __forceinline__ bool vkey_less(long long sa, int a, long long sb, int b) {
-  return sa < sb || (sa == sb && a < b);
+// Cache state one decision reads, loaded before the top-k so that its latency
+// overlaps it: the layer's row of `where` (E <= 1024: four entries per thread),
+// every slot's key and stamp when n_slots <= 4096 (sixteen per thread; larger
+// caches are read during the victim search), and the recency clock.
+struct DecidePre {
+  int32_t wh[4];
+  int32_t key[16];
+  long long st[16];
+  long long clock;
+};
+
+__device__ __forceinline__ void decide_prefetch(const DecideArgs& a, DecidePre& pf) {
+  const int tid = threadIdx.x, E = a.dc.E, base = a.layer * E, n = a.dc.n_slots;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid + 256 * j;
+    pf.wh[j] = e < E ? a.dc.where[base + e] : -1;
+  }
+  if (n <= 4096) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int sl = tid + 256 * j;
+      pf.key[j] = sl < n ? a.dc.slot_key[sl] : -1;
+      pf.st[j] = sl < n ? a.dc.slot_stamp[sl] : 0;
+    }
+  }
+  pf.clock = *a.dc.clock;
+}
+
+// Victim order (stamp asc, slot asc) as one unsigned key: stamps are >= -1 and far
+// below 2^39, slots below 2^24; ~0 marks a slot that is not a candidate.
+__device__ __forceinline__ unsigned long long victim_key(long long st, int sl) {
+  return ((unsigned long long)(st + 1) << 24) | (unsigned long long)sl;
+}
+
+__device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
+  return ~wave_max_u64(~v);
 }
 
 // The decisions of one decode call, by the 256 threads of one block, for the P
-// routed ids in idx (device, written by this block): dedup in first-occurrence
-// order, classify against `where`, q from the split, the q least recently used
-// slots not holding a hit (by (stamp, slot)), eviction and admission, stamps of
-// H then F in first-occurrence order, the slot rewrite, and the stable grouping
-// of the pairs by G = H then F.  Same rule as ExpertCache::lookup.
-__device__ void decide_block(const DecideArgs& a, const int32_t* idx, int P) {
-  __shared__ int32_t s_id[FT_PLAN_CAP], s_u[FT_PLAN_CAP], s_pre[FT_PLAN_CAP], s_g[FT_PLAN_CAP];
-  __shared__ int32_t s_h[FT_PLAN_CAP], s_m[FT_PLAN_CAP], s_grp[FT_PLAN_CAP], s_cnt[FT_PLAN_CAP + 1];
-  __shared__ int32_t s_first[1024], s_pos[1024];
-  __shared__ long long s_bst[4];
-  __shared__ int s_bsl[4];
-  __shared__ int s_n_u, s_n_h, s_n_m, s_q;
-  __shared__ long long s_clock;
-  const int tid = threadIdx.x;
-  const int E = a.dc.E, base = a.layer * E;
+// routed ids in s_id (shared memory): dedup in first-occurrence order, classify
+// against `where`, q from the split, the q least recently used slots not holding
+// a hit (by (stamp, slot)), eviction and admission, stamps of H then F in
+// first-occurrence order, the slot rewrite, and the stable grouping of the pairs
+// by G = H then F.  Same rule as ExpertCache::lookup.  Every decision is made in
+// shared memory from the prefetched state; global memory is only written.
+__device__ void decide_block(const DecideArgs& a, const int32_t* s_id, int P, const DecidePre& pf) {
+  __shared__ int32_t s_u[FT_PLAN_CAP], s_g[FT_PLAN_CAP], s_h[FT_PLAN_CAP], s_m[FT_PLAN_CAP];
+  __shared__ int32_t s_vold[FT_PLAN_CAP];
+  __shared__ int32_t s_where[1024], s_first[1024], s_pos[1024];
+  __shared__ unsigned long long s_best[2][4];
+  __shared__ uint32_t s_hash;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int E = a.dc.E, base = a.layer * E, n_sl = a.dc.n_slots;
   DevPlan* pl = a.plan;
-  for (int i = tid; i < P; i += 256) s_id[i] = __hip_atomic_load(idx + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int e = tid; e < E; e += 256) {
-    s_first[e] = 0x7fffffff;
-    s_pos[e] = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid + 256 * j;
+    if (e < E) {
+      s_where[e] = pf.wh[j];
+      s_first[e] = 0x7fffffff;
+      s_pos[e] = -1;
+    }
   }
-  if (tid == 0) s_clock = *a.dc.clock;
-  __syncthreads();
+  if (tid == 0) s_hash = 0u;
   // a token that allows fewer than k experts leaves -1 ids: no decisions, no groups
   int bad = 0;
   for (int i = tid; i < P; i += 256) bad |= s_id[i] < 0 || s_id[i] >= E;
@@ -324,170 +396,142 @@ __device__ void decide_block(const DecideArgs& a, const int32_t* idx, int P) {
   }
   for (int i = tid; i < P; i += 256) atomicMin(&s_first[s_id[i]], i);
   __syncthreads();
-  // U: first occurrences in pair order
+  // U: first occurrences in pair order (two pairs per thread, P <= 512)
   const int i0 = 2 * tid, i1 = 2 * tid + 1;
-  const int f0 = (i0 < P && s_first[s_id[i0]] == i0), f1 = (i1 < P && s_first[s_id[i1]] == i1);
+  const int f0 = i0 < P && s_first[s_id[i0]] == i0, f1 = i1 < P && s_first[s_id[i1]] == i1;
   int n_u;
   int ex = block_excl_scan_256(f0 + f1, &n_u);
   if (f0) s_u[ex] = s_id[i0];
   if (f1) s_u[ex + f0] = s_id[i1];
   __syncthreads();
-  // classify against the residency before this call
+  // classify against the residency before this call; one scan counts H (low half)
+  // and M (high half)
   const int u0 = 2 * tid, u1 = 2 * tid + 1;
-  if (u0 < n_u) s_pre[u0] = a.dc.where[base + s_u[u0]];
-  if (u1 < n_u) s_pre[u1] = a.dc.where[base + s_u[u1]];
-  __syncthreads();
-  const int h0 = u0 < n_u && s_pre[u0] >= 0, h1 = u1 < n_u && s_pre[u1] >= 0;
+  const int e0 = u0 < n_u ? s_u[u0] : 0, e1 = u1 < n_u ? s_u[u1] : 0;
+  const int p0 = u0 < n_u ? s_where[e0] : -1, p1 = u1 < n_u ? s_where[e1] : -1;
+  const int h0 = u0 < n_u && p0 >= 0, h1 = u1 < n_u && p1 >= 0;
   const int m0 = u0 < n_u && !h0, m1 = u1 < n_u && !h1;
-  int n_h, n_m;
-  ex = block_excl_scan_256(h0 + h1, &n_h);
-  if (h0) s_h[ex] = u0;
-  if (h1) s_h[ex + h0] = u1;
-  ex = block_excl_scan_256(m0 + m1, &n_m);
-  if (m0) s_m[ex] = s_u[u0];
-  if (m1) s_m[ex + m0] = s_u[u1];
-  __syncthreads();
-  for (int i = tid; i < n_h; i += 256) {
-    s_pos[s_u[s_h[i]]] = i;  // group of a hit: its rank in H
-    s_g[i] = s_pre[s_h[i]];
+  int tot;
+  ex = block_excl_scan_256((h0 + h1) | ((m0 + m1) << 16), &tot);
+  const int n_h = tot & 0xffff, n_m = tot >> 16, xh = ex & 0xffff, xm = ex >> 16;
+  if (h0) {
+    s_h[xh] = e0;
+    s_g[xh] = p0;
+    s_pos[e0] = xh;  // group of a hit: its rank in H
   }
-  if (tid == 0) {
-    s_n_u = n_u;
-    s_n_h = n_h;
-    s_n_m = n_m;
-    s_q = qstar_device(n_m, a.fq, a.min_fill, a.max_fetch, a.dc.n_slots - n_h);
+  if (h1) {
+    s_h[xh + h0] = e1;
+    s_g[xh + h0] = p1;
+    s_pos[e1] = xh + h0;
   }
+  if (m0) s_m[xm] = e0;
+  if (m1) s_m[xm + m0] = e1;
+  const int avail = n_sl - n_h;
+  const int q = qstar_device(n_m, a.fq, a.min_fill, a.max_fetch, avail);
   __syncthreads();
-  const int q = s_q;
-  // victims: q rounds of the smallest (stamp, slot) above the previous pick, over
-  // the slots that do not hold a hit of this call.  Each thread keeps its slots'
-  // keys (stamp, or "not eligible") in registers when they fit.
-  constexpr int VR = 16;
-  long long vst[VR];
-  const int n_sl = a.dc.n_slots;
-  const bool in_regs = n_sl <= VR * 256;
+  // victims: q rounds of the smallest victim key above the previous pick, over the
+  // slots that hold neither a hit of this call nor a prefill reservation
+  const bool in_regs = n_sl <= 4096;
+  unsigned long long vk[16];
   if (q > 0 && in_regs) {
 #pragma unroll
-    for (int j = 0; j < VR; ++j) {
-      const int sl = tid + 256 * j;
-      vst[j] = 0x7fffffffffffffffll;
-      if (sl < n_sl) {
-        const int key = a.dc.slot_key[sl];
-        if (!(key >= base && key < base + E && s_pos[key - base] >= 0)) vst[j] = a.dc.slot_stamp[sl];
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int sl = tid + 256 * j, key = pf.key[j];
+      const bool hit = key >= base && key < base + E && s_pos[key - base] >= 0;
+      vk[j] = (sl < n_sl && !hit && key != -2) ? victim_key(pf.st[j], sl) : ~0ull;
     }
   }
-  long long prev_st = -2;
-  int prev_sl = -1;
-  const int lane = tid & 63, wv = tid >> 6;
+  unsigned long long prev = 0ull;
   for (int r = 0; r < q; ++r) {
-    long long best_st = 0x7fffffffffffffffll;
-    int best_sl = 0x7fffffff;
+    unsigned long long best = ~0ull;
     if (in_regs) {
 #pragma unroll
-      for (int j = 0; j < VR; ++j) {
-        const int sl = tid + 256 * j;
-        const long long st = vst[j];
-        if (sl < n_sl && st != 0x7fffffffffffffffll && vkey_less(prev_st, prev_sl, st, sl) &&
-            vkey_less(st, sl, best_st, best_sl)) {
-          best_st = st;
-          best_sl = sl;
-        }
-      }
+      for (int j = 0; j < 16; ++j)
+        if ((r == 0 || vk[j] > prev) && vk[j] < best) best = vk[j];
     } else {
       for (int sl = tid; sl < n_sl; sl += 256) {
         const int key = a.dc.slot_key[sl];
-        if (key >= base && key < base + E && s_pos[key - base] >= 0) continue;  // holds a hit
-        const long long st = a.dc.slot_stamp[sl];
-        if (vkey_less(prev_st, prev_sl, st, sl) && vkey_less(st, sl, best_st, best_sl)) {
-          best_st = st;
-          best_sl = sl;
-        }
+        if (key == -2 || (key >= base && key < base + E && s_pos[key - base] >= 0)) continue;
+        const unsigned long long v = victim_key(a.dc.slot_stamp[sl], sl);
+        if ((r == 0 || v > prev) && v < best) best = v;
       }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const long long ost = __shfl_xor(best_st, o, WAVE);
-      const int osl = __shfl_xor(best_sl, o, WAVE);
-      if (vkey_less(ost, osl, best_st, best_sl)) {
-        best_st = ost;
-        best_sl = osl;
-      }
-    }
-    if (lane == 0) {
-      s_bst[wv] = best_st;
-      s_bsl[wv] = best_sl;
-    }
+    best = wave_min_u64(best);
+    if (lane == 0) s_best[r & 1][wv] = best;
     __syncthreads();
-    best_st = s_bst[0];
-    best_sl = s_bsl[0];
+    best = s_best[r & 1][0];
 #pragma unroll
-    for (int w = 1; w < 4; ++w)
-      if (vkey_less(s_bst[w], s_bsl[w], best_st, best_sl)) {
-        best_st = s_bst[w];
-        best_sl = s_bsl[w];
+    for (int w = 1; w < 4; ++w) best = s_best[r & 1][w] < best ? s_best[r & 1][w] : best;
+    if (best == ~0ull) {
+      // fewer candidates than q (cannot happen while q <= avail and no prefill
+      // reservation exists): publish an invalid plan, write nothing
+      if (tid == 0) {
+        pl->n_u = -1;
+        pl->n_h = 0;
+        pl->n_g = 0;
+        pl->q = 0;
+        if (a.pub) a.pub->n_u = -1;
       }
-    if (tid == 0) s_g[n_h + r] = best_sl;
-    prev_st = best_st;
-    prev_sl = best_sl;
-    __syncthreads();
-  }
-  // eviction and admission of F = M[0:q] (sequential, q is small)
-  if (tid == 0) {
-    for (int i = 0; i < q; ++i) {
-      const int sl = s_g[n_h + i];
-      const int old = a.dc.slot_key[sl];
-      if (old >= 0) a.dc.where[old] = -1;
-      a.dc.slot_key[sl] = base + s_m[i];
-      a.dc.where[base + s_m[i]] = sl;
+      return;
     }
+    const int bsl = (int)(best & 0xffffffull);
+    // the owner of the slot records it and the key it held
+    if (bsl % 256 == tid) {
+      s_g[n_h + r] = bsl;
+      s_vold[r] = in_regs ? pf.key[0] : a.dc.slot_key[bsl];
+      if (in_regs) {
+#pragma unroll
+        for (int j = 1; j < 16; ++j)
+          if (bsl == tid + 256 * j) s_vold[r] = pf.key[j];
+      }
+    }
+    prev = best;
   }
-  for (int i = tid; i < q; i += 256) s_pos[s_m[i]] = n_h + i;
+  __syncthreads();
+  // eviction and admission of F = M[0:q]; the keys involved are all distinct
+  for (int r = tid; r < q; r += 256) {
+    const int sl = s_g[n_h + r], old = s_vold[r], e = s_m[r];
+    if (old >= 0) a.dc.where[old] = -1;
+    a.dc.slot_key[sl] = base + e;
+    a.dc.where[base + e] = sl;
+    s_pos[e] = n_h + r;
+  }
   __syncthreads();
   // stamps: H and F in first-occurrence order
-  const int r0 = u0 < n_u && s_pos[s_u[u0]] >= 0, r1 = u1 < n_u && s_pos[s_u[u1]] >= 0;
+  const int r0 = u0 < n_u && s_pos[e0] >= 0, r1 = u1 < n_u && s_pos[e1] >= 0;
   int n_res;
   ex = block_excl_scan_256(r0 + r1, &n_res);
-  if (r0) a.dc.slot_stamp[s_g[s_pos[s_u[u0]]]] = s_clock + ex + 1;
-  if (r1) a.dc.slot_stamp[s_g[s_pos[s_u[u1]]]] = s_clock + ex + r0 + 1;
-  if (tid == 0) *a.dc.clock = s_clock + n_res;
-  // slot rewrite and group of every pair
+  if (r0) a.dc.slot_stamp[s_g[s_pos[e0]]] = pf.clock + ex + 1;
+  if (r1) a.dc.slot_stamp[s_g[s_pos[e1]]] = pf.clock + ex + r0 + 1;
+  if (tid == 0) *a.dc.clock = pf.clock + n_res;
+  // slot rewrite and stable grouping of the pairs by G (counted directly: P is small)
   const int n_g = n_h + q;
-  for (int g = tid; g <= n_g; g += 256) s_cnt[g] = 0;
-  __syncthreads();
   for (int i = tid; i < P; i += 256) {
     const int g = s_pos[s_id[i]];
-    s_grp[i] = g;
-    if (g >= 0) atomicAdd(&s_cnt[g], 1);
-  }
-  __syncthreads();
-  // offsets over the groups (n_g <= 512: two per thread)
-  const int c0 = i0 < n_g ? s_cnt[i0] : 0, c1 = i1 < n_g ? s_cnt[i1] : 0;
-  int tot;
-  ex = block_excl_scan_256(c0 + c1, &tot);
-  if (i0 < n_g) pl->offsets[i0] = ex;
-  if (i1 < n_g) pl->offsets[i1] = ex + c0;
-  __syncthreads();
-  if (i0 < n_g) s_cnt[i0] = ex;
-  if (i1 < n_g) s_cnt[i1] = ex + c0;
-  if (tid == 0) pl->offsets[n_g] = tot;
-  __syncthreads();
-  for (int i = tid; i < P; i += 256) {
-    const int g = s_grp[i];
     pl->pair_group[i] = g;
     pl->route_slot[i] = g >= 0 ? s_g[g] : -1;
     if (g < 0) {
       pl->inv[i] = -1;
     } else {
-      int rank = 0;
-      for (int j = 0; j < i; ++j) rank += s_grp[j] == g;
-      const int pos = s_cnt[g] + rank;
+      int pos = 0;
+      for (int j = 0; j < P; ++j) {
+        const int gj = s_pos[s_id[j]];
+        pos += (gj >= 0 && gj < g) || (gj == g && j < i);
+      }
       pl->perm[pos] = i;
       pl->inv[i] = pos;
     }
   }
+  for (int g = tid; g <= n_g; g += 256) {
+    int off = 0;
+    for (int j = 0; j < P; ++j) {
+      const int gj = s_pos[s_id[j]];
+      off += gj >= 0 && gj < g;
+    }
+    pl->offsets[g] = off;
+  }
   for (int i = tid; i < n_u; i += 256) pl->U[i] = s_u[i];
-  for (int i = tid; i < n_h; i += 256) pl->H[i] = s_u[s_h[i]];
+  for (int i = tid; i < n_h; i += 256) pl->H[i] = s_h[i];
   for (int i = tid; i < n_m; i += 256) pl->M[i] = s_m[i];
   for (int i = tid; i < n_g; i += 256) pl->G_slot[i] = s_g[i];
   for (int i = tid; i < q; i += 256) pl->F_slot[i] = s_g[n_h + i];
@@ -498,15 +542,11 @@ __device__ void decide_block(const DecideArgs& a, const int32_t* idx, int P) {
     pl->n_m = n_m;
     pl->q = q;
     pl->n_c = n_m - q;
-    pl->avail = a.dc.n_slots - n_h;
+    pl->avail = avail;
     pl->n_g = n_g;
   }
   // the host takes the same decisions from the published ids; it checks them
   // against a hash of the device's (plan_term summed over the sequence of values)
-  __shared__ uint32_t s_hash;
-  if (tid == 0) s_hash = 0u;
-  __syncthreads();
-  const int avail = a.dc.n_slots - n_h;
   const int n_seq = 5 + n_u + n_h + n_m + n_g + 2 * P;
   uint32_t part = 0u;
   for (int j = tid; j < n_seq; j += 256) {
@@ -516,19 +556,22 @@ __device__ void decide_block(const DecideArgs& a, const int32_t* idx, int P) {
     } else if ((r -= 5) < n_u) {
       v = s_u[r];
     } else if ((r -= n_u) < n_h) {
-      v = s_u[s_h[r]];
+      v = s_h[r];
     } else if ((r -= n_h) < n_m) {
       v = s_m[r];
     } else if ((r -= n_m) < n_g) {
       v = s_g[r];
     } else if ((r -= n_g) < P) {
-      v = s_grp[r] >= 0 ? s_g[s_grp[r]] : -1;
+      const int g = s_pos[s_id[r]];
+      v = g >= 0 ? s_g[g] : -1;
     } else {
-      v = s_grp[r - P];
+      v = s_pos[s_id[r - P]];
     }
     part += plan_term(j, v);
   }
-  atomicAdd(&s_hash, part);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, WAVE);
+  if (lane == 0) atomicAdd(&s_hash, part);
   __syncthreads();
   if (tid == 0) {
     pl->hash = s_hash;
@@ -539,6 +582,41 @@ __device__ void decide_block(const DecideArgs& a, const int32_t* idx, int P) {
     }
   }
 }
+
+// ---- decode fills over PCIe ([FT] §3.2, the F set) ----------------------------------
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Copies n16 16-byte units from pinned host memory (read by the GPU over PCIe) to
+// device memory, the grid's threads striding over them.
+__device__ __forceinline__ void h2d_stride_copy(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
+                                                size_t n16) {
+  const size_t step = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += step)
+    dst[i] = __builtin_nontemporal_load(src + i);
+}
+
+// The fills of one decode call: records M[0:q] of the layer (layer_base points at
+// its expert 0 in the pinned pool) into slots F_slot[0:q], as the device decisions
+// in `plan` chose them; nothing when the plan is invalid or q is 0.
+__global__ __launch_bounds__(256) void fill_kernel(const uint8_t* __restrict__ layer_base, size_t S, int E,
+                                                   uint8_t* __restrict__ slots, int n_slots,
+                                                   const DevPlan* __restrict__ plan) {
+  const int q = plan->n_u < 0 ? 0 : plan->q;
+  if (q <= 0 || q > FT_PLAN_CAP) return;
+  for (int r = 0; r < q; ++r) {
+    const int e = plan->M[r], sl = plan->F_slot[r];
+    if (e < 0 || e >= E || sl < 0 || sl >= n_slots) continue;
+    h2d_stride_copy(reinterpret_cast<const u32x4_t*>(layer_base + (size_t)e * S),
+                    reinterpret_cast<u32x4_t*>(slots + (size_t)sl * S), S / 16);
+  }
+}
+
+__global__ __launch_bounds__(256) void h2d_copy_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                       size_t bytes) {
+  h2d_stride_copy(reinterpret_cast<const u32x4_t*>(src), reinterpret_cast<u32x4_t*>(dst), bytes / 16);
+}
+
+constexpr int kFillBlocks = 256;
 
 // Decode router in one launch: one wavefront per (token, expert) logit (same
 // arithmetic order as router_logits_kernel: lane l owns elements (i mod 512)/8 ==
@@ -596,13 +674,15 @@ __global__ __launch_bounds__(256) void router_decode_kernel(
   __syncthreads();
   if (!last) return;
   __threadfence();
+  __shared__ int32_t s_ids[FT_PLAN_CAP];
+  DecidePre pf;
+  if (decide) decide_prefetch(da, pf);
   for (int tt = wave; tt < T; tt += 4)
     topk_token(logits + (size_t)tt * E, allowed ? allowed + (size_t)tt * E : nullptr, E, k, lane,
                idx + (size_t)tt * k, gates + (size_t)tt * k, pub_idx ? pub_idx + (size_t)tt * k : nullptr,
-               pub_gates ? pub_gates + (size_t)tt * k : nullptr);
-  __threadfence();
+               pub_gates ? pub_gates + (size_t)tt * k : nullptr, s_ids + tt * k);
   __syncthreads();
-  if (decide) decide_block(da, idx, T * k);
+  if (decide) decide_block(da, s_ids, T * k, pf);
   __threadfence_system();
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -1179,6 +1259,25 @@ int launch_router(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, 
   return launched("router_topk");
 }
 
+int launch_fill(const uint8_t* layer_base, size_t S, int E, uint8_t* slots, int n_slots, const DevPlan* plan,
+                void* stream) {
+  if (!layer_base || !slots || !plan || S == 0 || S % 16 || E <= 0 || n_slots < 0)
+    return fail(FT_EINVAL, "fill: bad argument");
+  if ((reinterpret_cast<uintptr_t>(layer_base) | reinterpret_cast<uintptr_t>(slots)) & 15)
+    return fail(FT_EINVAL, "fill: unaligned pointer");
+  fill_kernel<<<kFillBlocks, 256, 0, static_cast<hipStream_t>(stream)>>>(layer_base, S, E, slots, n_slots, plan);
+  return launched("fill");
+}
+
+int launch_h2d_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst || bytes % 16 || ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15))
+    return fail(FT_EINVAL, "h2d_copy: need 16-byte aligned pointers and sizes");
+  if (bytes == 0) return FT_OK;
+  h2d_copy_kernel<<<kFillBlocks, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), bytes);
+  return launched("h2d_copy");
+}
+
 int launch_router_decode(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, int T, int d,
                          int E, int k, float* logits_ws, int32_t* idx, float* gates,
                          unsigned int* ticket, int32_t* pub_idx, float* pub_gates, uint16_t* pub_x,
@@ -1187,8 +1286,8 @@ int launch_router_decode(const uint16_t* x, const uint16_t* w, const uint8_t* al
     return fail(FT_EINVAL, "router: need T<=64, d%8==0, 1<=k<=min(E,8), E<=1024");
   if (!aligned16(x) || !aligned16(w) || (pub_x && !aligned16(pub_x)))
     return fail(FT_EINVAL, "router: unaligned pointer");
-  if (da && (T * k > FT_PLAN_CAP || !da->plan || !da->dc.where || (da->dc.n_slots > 0 && (!da->dc.slot_key ||
-                                                                                       !da->dc.slot_stamp))))
+  if (da && (T * k > FT_PLAN_CAP || !da->plan || !da->dc.where || da->dc.n_slots >= (1 << 24) ||
+             (da->dc.n_slots > 0 && (!da->dc.slot_key || !da->dc.slot_stamp))))
     return fail(FT_EINVAL, "router: bad decision arguments");
   DecideArgs none{};
   dim3 grid(T, (E + 3) / 4);

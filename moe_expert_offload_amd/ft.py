@@ -65,7 +65,7 @@ class ft_step_stats(C.Structure):
                 ("misses", C.c_int32), ("q", C.c_int32), ("n_c", C.c_int32), ("cpu_caller_items", C.c_int32),
                 ("h2d_bytes", C.c_int64), ("t_route_us", C.c_double), ("t_ctrl_us", C.c_double),
                 ("t_cpu_us", C.c_double), ("t_total_us", C.c_double), ("t_issue_us", C.c_double),
-                ("t_cpu_work_us", C.c_double)]
+                ("t_cpu_work_us", C.c_double), ("t_submit_us", C.c_double), ("t_between_us", C.c_double)]
 
 
 class ft_stats(C.Structure):
@@ -125,7 +125,7 @@ def lib():
             "ft_expert_cache_fill": (C.c_int, [P, C.POINTER(ft_plan), P, P, P]),
             "ft_expert_cache_resize": (C.c_int, [P, P, I]),
             "ft_expert_cache_where": (I, [P, I, I]),
-            "ft_moe_decode_layer": (C.c_int, [P, I, P, I, P, P, P, P, P, C.POINTER(ft_plan), C.POINTER(ft_step_stats)]),
+            "ft_moe_decode_layer": (C.c_int, [P, I, P, I, P, P, P, P, C.POINTER(ft_plan), C.POINTER(ft_step_stats)]),
             "ft_moe_prefill_begin": (C.c_int, [P, P]),
             "ft_moe_prefill_layer": (C.c_int, [P, I, P, I, P, P, P, P]),
             "ft_moe_prefill_end": (C.c_int, [P]),
@@ -316,9 +316,9 @@ def ft_expert_cache_where(ctx, layer, expert):
     return lib().ft_expert_cache_where(ctx, layer, expert)
 
 
-def ft_moe_decode_layer(ctx, layer, x, T, w_router, allowed, y, compute=None, copy=None, plan=None, stats=None):
+def ft_moe_decode_layer(ctx, layer, x, T, w_router, allowed, y, compute=None, plan=None, stats=None):
     return _check("ft_moe_decode_layer", lib().ft_moe_decode_layer(
-        ctx, layer, _ptr(x), T, _ptr(w_router), _ptr(allowed), _ptr(y), _stream(compute), _stream(copy),
+        ctx, layer, _ptr(x), T, _ptr(w_router), _ptr(allowed), _ptr(y), _stream(compute),
         C.byref(plan) if plan is not None else None, C.byref(stats) if stats is not None else None))
 
 

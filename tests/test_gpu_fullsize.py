@@ -56,7 +56,7 @@ def test_decode_full_size(key, L_phys, steps, y_every, fq):
                 x = synth.tokens(wl, st, l, T=T)
                 allowed = synth.allowed_mask(tr[st, l], s.E)
                 y = torch.empty((T, s.d), dtype=torch.float32, device="cuda")
-                ft.ft_moe_decode_layer(eng.ctx, l, dev_u16(x), T, wr_dev[l], dev(allowed), y, copy=eng.copy,
+                ft.ft_moe_decode_layer(eng.ctx, l, dev_u16(x), T, wr_dev[l], dev(allowed), y,
                                        plan=plan)
                 torch.cuda.synchronize()
                 idx, g, _ = route(x, wr[l], s.k, allowed)

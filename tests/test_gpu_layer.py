@@ -71,7 +71,7 @@ def test_decode_trace_parity(fq, min_fill, max_fetch, T, N):
                 allowed = allowed_mask(tr[step, l], s.E)
                 y = torch.empty((T, s.d), dtype=torch.float32, device="cuda")
                 ft.ft_moe_decode_layer(eng.ctx, l, dev_u16(x), T, wr_dev[l], dev(allowed), y,
-                                       copy=eng.copy, plan=plan)
+                                       plan=plan)
                 torch.cuda.synchronize()
                 ref = decode_layer(ref_cache, l, x, wr[l], s.k, lambda e: pool.view[l * s.E + e],
                                    s.d, s.d_ff, fq, min_fill, max_fetch, allowed)
@@ -102,7 +102,7 @@ def test_single_layer_configuration_all_resident():
         plan = ft.ft_plan()
         for call in range(3):
             y = torch.empty((16, s.d), dtype=torch.float32, device="cuda")
-            ft.ft_moe_decode_layer(eng.ctx, 0, xd, 16, wd, None, y, copy=eng.copy, plan=plan)
+            ft.ft_moe_decode_layer(eng.ctx, 0, xd, 16, wd, None, y, plan=plan)
             torch.cuda.synchronize()
             ref = decode_layer(ref_cache, 0, x, wr[0], s.k, lambda e: pool.view[e], s.d, s.d_ff, Q16)
             _compare_plan(plan, ref["plan"], ref["idx"])
@@ -139,7 +139,7 @@ def test_prefill_double_buffer_then_decode(T):
                     allowed = allowed_mask(tr[step, l], s.E)
                     y = torch.empty((2, s.d), dtype=torch.float32, device="cuda")
                     ft.ft_moe_decode_layer(eng.ctx, l, dev_u16(x), 2, wr_dev[l], dev(allowed), y,
-                                           copy=eng.copy, plan=plan)
+                                           plan=plan)
                     torch.cuda.synchronize()
                     ref = decode_layer(ref_cache, l, x, wr[l], s.k, lambda e: pool.view[l * s.E + e],
                                        s.d, s.d_ff, 40000, 1, -1, allowed)
@@ -194,7 +194,7 @@ def test_resize_at_safe_point_keeps_outputs():
                 allowed = allowed_mask(tr[step, l], s.E)
                 y = torch.empty((1, s.d), dtype=torch.float32, device="cuda")
                 ft.ft_moe_decode_layer(eng.ctx, l, dev_u16(x), 1, wr_dev[l], dev(allowed), y,
-                                       copy=eng.copy, plan=plan)
+                                       plan=plan)
                 torch.cuda.synchronize()
                 ref = decode_layer(ref_cache, l, x, wr[l], s.k, lambda e: pool.view[l * s.E + e],
                                    s.d, s.d_ff, 30000, 1, -1, allowed)

@@ -170,7 +170,7 @@ def test_mx_decode_trace_parity(fq, T):
                 allowed = allowed_mask(tr[step, l], s.E)
                 y = torch.empty((T, s.d), dtype=torch.float32, device="cuda")
                 ft.ft_moe_decode_layer(eng.ctx, l, dev_u16(x), T, wr_dev[l], dev(allowed), y,
-                                       copy=eng.copy, plan=plan)
+                                       plan=plan)
                 torch.cuda.synchronize()
                 ref = decode_layer(ref_cache, l, x, wr[l], s.k, lambda e: pool.view[l * s.E + e], s.d, s.d_ff,
                                    fq, 1 if fq else 0, -1 if fq else 0, allowed, fmt="mxfp4")
@@ -226,7 +226,7 @@ def test_mx_prefill_double_buffer_then_resize(T):
                 x = tokens(MXS, 40 + step, l, T=1)
                 allowed = allowed_mask(tr[step, l], s.E)
                 y = torch.empty((1, s.d), dtype=torch.float32, device="cuda")
-                ft.ft_moe_decode_layer(eng.ctx, l, dev_u16(x), 1, wr_dev[l], dev(allowed), y, copy=eng.copy,
+                ft.ft_moe_decode_layer(eng.ctx, l, dev_u16(x), 1, wr_dev[l], dev(allowed), y,
                                        plan=plan)
                 torch.cuda.synchronize()
                 ref = decode_layer(ref_cache, l, x, wr[l], s.k, lambda e: pool.view[l * s.E + e], s.d, s.d_ff,
@@ -282,7 +282,7 @@ def test_mx_full_size_prefill_chunk_and_decode():
                 wr = synth.router_weights(wd, l)
                 allowed = allowed_mask(tr[st, l], s.E)
                 y = torch.empty((1, s.d), dtype=torch.float32, device="cuda")
-                ft.ft_moe_decode_layer(eng.ctx, l, dev_u16(x), 1, dev_u16(wr), dev(allowed), y, copy=eng.copy,
+                ft.ft_moe_decode_layer(eng.ctx, l, dev_u16(x), 1, dev_u16(wr), dev(allowed), y,
                                        plan=plan)
                 torch.cuda.synchronize()
                 idx, g, _ = route(x, wr, s.k, allowed)

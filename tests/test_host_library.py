@@ -161,7 +161,7 @@ def test_error_codes():
         with pytest.raises(ft.FtError):  # T*k over the plan capacity
             ft.ft_expert_cache_lookup(ctx, 0, np.zeros((300, 2), np.int32), 300)
         with pytest.raises(ft.FtError):  # no device path in a decisions-only context
-            ft.ft_moe_decode_layer(ctx, 0, 16, 1, 16, None, 16, compute=0, copy=0)
+            ft.ft_moe_decode_layer(ctx, 0, 16, 1, 16, None, 16, compute=0)
     finally:
         ft.ft_destroy(ctx)
     assert ft.ft_record_bytes(shape) == 6 * 64 * 64
