@@ -87,7 +87,7 @@ def run_decode(args, torch, ft, synth, HostPool):
     log(f"decode workload {wl.name}: pool {L_phys * s.E} records x {S / 1e6:.2f} MB = {L_phys * s.E * S / 1e9:.1f} GB")
     t = time.time()
     pool = HostPool(L_phys * s.E, s.record_bytes, s.pool_dtype)
-    synth.fill_records_torch(pool.view, wl.config_id, seed=args.seed)
+    synth.fill_records_torch(pool.view, wl.seed_key, seed=args.seed)
     log(f"pool allocated and filled in {time.time() - t:.1f} s")
 
     fshape = ft.make_shape(s.L, s.E, s.d, s.d_ff, s.k)
@@ -213,7 +213,7 @@ def run_decode(args, torch, ft, synth, HostPool):
 
 
 def run_prefill(args, torch, ft, synth, HostPool):
-    wl = synth.WORKLOADS["c4"]
+    wl = synth.WORKLOADS["prefill8k-L43-d4096-E256-top6"]
     s = wl.shape
     T = wl.T
     S = s.record_bytes
@@ -221,7 +221,7 @@ def run_prefill(args, torch, ft, synth, HostPool):
     log(f"prefill workload {wl.name}: pool {L_phys * s.E} records = {L_phys * s.E * S / 1e9:.1f} GB (aliased)")
     t = time.time()
     pool = HostPool(L_phys * s.E, s.record_bytes, s.pool_dtype)
-    synth.fill_records_torch(pool.view, wl.config_id, seed=args.seed)
+    synth.fill_records_torch(pool.view, wl.seed_key, seed=args.seed)
     log(f"pool allocated and filled in {time.time() - t:.1f} s")
     try:
         fshape = ft.make_shape(s.L, s.E, s.d, s.d_ff, s.k)
@@ -232,7 +232,7 @@ def run_prefill(args, torch, ft, synth, HostPool):
         wsb = ft.ft_workspace_bytes(fshape, T)
         ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
         wr = [torch.from_numpy(synth.router_weights(wl, l, seed=args.seed).view(np.int16)).cuda() for l in range(s.L)]
-        xs = [synth.tokens_torch(wl.config_id, 0, l, T, s.d, seed=args.seed) for l in range(s.L)]
+        xs = [synth.tokens_torch(wl.seed_key, 0, l, T, s.d, seed=args.seed) for l in range(s.L)]
         y = torch.empty((T, s.d), dtype=torch.float32, device="cuda")
         ctx = ft.ft_create(fshape, cfg, pool.ptr, pool.nbytes, slots, N, ws, wsb)
         compute = torch.cuda.current_stream()
@@ -278,7 +278,7 @@ def run_prefill(args, torch, ft, synth, HostPool):
 def run_mxfp4(args, torch, ft, synth, HostPool):
     """MXFP4 experts at the 43-layer d=4096 shape: 2 x 8192-token prefill chunks, then
     batch-1 decode over a trace with a resize at a safe point."""
-    wl, wd = synth.WORKLOADS["c5"], synth.WORKLOADS["c5d"]
+    wl, wd = synth.WORKLOADS["mxfp4-prefill8k-L43-d4096-E256-top6"], synth.WORKLOADS["mxfp4-decode-L43-d4096-E256-top6"]
     s = wl.shape
     S = s.record_bytes
     T = wl.T
@@ -287,7 +287,7 @@ def run_mxfp4(args, torch, ft, synth, HostPool):
     t = time.time()
     pool = HostPool(L_phys * s.E, S, s.pool_dtype)
     try:
-        synth.fill_mxfp4_records_torch(pool.view, s.d, s.d_ff, wl.config_id, seed=args.seed)
+        synth.fill_mxfp4_records_torch(pool.view, s.d, s.d_ff, wl.seed_key, seed=args.seed)
         log(f"pool allocated and filled in {time.time() - t:.1f} s")
         fshape = ft.make_shape(s.L, s.E, s.d, s.d_ff, s.k, ft.FT_W_MXFP4)
         scratch = torch.empty(64 * S, dtype=torch.uint8, device="cuda")
@@ -303,7 +303,7 @@ def run_mxfp4(args, torch, ft, synth, HostPool):
         ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
         wr = [torch.from_numpy(synth.router_weights(wl, l, seed=args.seed).view(np.int16)).cuda() for l in range(s.L)]
         n_chunks = 2
-        xs = [[synth.tokens_torch(wl.config_id, c, l, T, s.d, seed=args.seed) for l in range(s.L)]
+        xs = [[synth.tokens_torch(wl.seed_key, c, l, T, s.d, seed=args.seed) for l in range(s.L)]
               for c in range(n_chunks)]
         y = torch.empty((T, s.d), dtype=torch.float32, device="cuda")
         steps = args.mx_steps
@@ -436,7 +436,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=192)
     ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c2b8", "c3"])
+    ap.add_argument("--workload", default="decode-L40-d2048-E128-top8",
+                    choices=["decode-L40-d2048-E128-top8", "decode-L40-d2048-E128-top8-b8", "decode-L43-d4096-E256-top6"])
     ap.add_argument("--l-phys", type=int, default=0, help="physical layers in the host pool (0 = all)")
     ap.add_argument("--min-fill", type=int, default=1)
     ap.add_argument("--max-fetch", type=int, default=-1)

@@ -60,7 +60,7 @@ class Workload:
     """One synthetic workload (sizes and distributions of the pages' configurations)."""
 
     name: str
-    config_id: int
+    seed_key: int
     shape: Shape
     T: int
     cache_rate: float  # fraction of the L*E (layer, expert) pairs the GPU cache holds
@@ -74,25 +74,26 @@ class Workload:
         return int(np.floor(self.cache_rate * self.shape.L * self.shape.E + 1e-9))
 
 
-WORKLOADS = {
+WORKLOADS = {w.name: w for w in (
     # single layer, all experts resident
-    "c1": Workload("c1-layer-d256-E8-top2", 1, Shape(1, 8, 256, 512, 2), 16, 1.0),
-    # decode: 40 layers, d=2048, E=128, top-8, d_ff=768, cache at 37 %
-    "c2": Workload("c2-decode-L40-d2048-E128-top8", 2, Shape(40, 128, 2048, 768, 8), 1, 0.37),
-    "c2b8": Workload("c2-decode-L40-d2048-E128-top8-b8", 2, Shape(40, 128, 2048, 768, 8), 8, 0.37),
+    Workload("layer-d256-E8-top2", 1, Shape(1, 8, 256, 512, 2), 16, 1.0),
+    # decode: 40 layers, d=2048, E=128, top-8, d_ff=768, cache at 37 %, batch 1 and 8
+    Workload("decode-L40-d2048-E128-top8", 2, Shape(40, 128, 2048, 768, 8), 1, 0.37),
+    Workload("decode-L40-d2048-E128-top8-b8", 2, Shape(40, 128, 2048, 768, 8), 8, 0.37),
     # decode: 43 layers, d=4096, E=256, top-6, d_ff=2048, cache at 11 %
-    "c3": Workload("c3-decode-L43-d4096-E256-top6", 3, Shape(43, 256, 4096, 2048, 6), 1, 0.11),
-    # prefill: 8192-token chunk through the c3 layer shape
-    "c4": Workload("c4-prefill8k-L43-d4096-E256-top6", 4, Shape(43, 256, 4096, 2048, 6), 8192, 0.11),
-    # the c3 shape with MXFP4 experts: 16384-token prefill (two 8192 chunks) and batch-1 decode
-    "c5": Workload("c5-mxfp4-L43-d4096-E256-top6", 5, Shape(43, 256, 4096, 2048, 6, True), 8192, 0.11),
-    "c5d": Workload("c5-mxfp4-decode-L43-d4096-E256-top6", 5, Shape(43, 256, 4096, 2048, 6, True), 1, 0.11),
-}
+    Workload("decode-L43-d4096-E256-top6", 3, Shape(43, 256, 4096, 2048, 6), 1, 0.11),
+    # prefill: 8192-token chunk through the same 43-layer shape
+    Workload("prefill8k-L43-d4096-E256-top6", 4, Shape(43, 256, 4096, 2048, 6), 8192, 0.11),
+    # the 43-layer shape with MXFP4 experts: 16384-token prefill (two 8192-token chunks)
+    # and batch-1 decode
+    Workload("mxfp4-prefill8k-L43-d4096-E256-top6", 5, Shape(43, 256, 4096, 2048, 6, True), 8192, 0.11),
+    Workload("mxfp4-decode-L43-d4096-E256-top6", 5, Shape(43, 256, 4096, 2048, 6, True), 1, 0.11),
+)}
 
 
-def generator(config_id: int, stream: int, *extra: int, seed: int = 0) -> np.random.Generator:
-    """PCG64 stream keyed by (config, stream, extra...) under one base seed."""
-    ss = np.random.SeedSequence(entropy=seed, spawn_key=(config_id, stream) + tuple(int(e) for e in extra))
+def generator(seed_key: int, stream: int, *extra: int, seed: int = 0) -> np.random.Generator:
+    """PCG64 stream keyed by (workload seed key, stream, extra...) under one base seed."""
+    ss = np.random.SeedSequence(entropy=seed, spawn_key=(seed_key, stream) + tuple(int(e) for e in extra))
     return np.random.Generator(np.random.PCG64(ss))
 
 
@@ -114,14 +115,14 @@ def bf16_bits_to_f32(b) -> np.ndarray:
 def router_weights(w: Workload, layer: int, seed: int = 0) -> np.ndarray:
     """W_r for one layer: bf16 words [E, d], values N(0, 0.02^2)."""
     s = w.shape
-    g = generator(w.config_id, STREAM_ROUTER, layer, seed=seed)
+    g = generator(w.seed_key, STREAM_ROUTER, layer, seed=seed)
     return f32_to_bf16_bits(g.normal(0.0, 0.02, size=(s.E, s.d)))
 
 
 def expert_record(w: Workload, layer_phys: int, expert: int, seed: int = 0) -> np.ndarray:
     """One expert record (bf16 words, layout in the module docstring), values N(0, 0.02^2)."""
     s = w.shape
-    g = generator(w.config_id, STREAM_EXPERT, layer_phys, expert, seed=seed)
+    g = generator(w.seed_key, STREAM_EXPERT, layer_phys, expert, seed=seed)
     return f32_to_bf16_bits(g.normal(0.0, 0.02, size=s.record_elems))
 
 
@@ -139,7 +140,7 @@ def tokens(w: Workload, step: int, layer: int, T: int | None = None, seed: int =
     """Layer input x for (step or chunk, layer): bf16 words [T, d], values N(0, 1)."""
     s = w.shape
     T = w.T if T is None else T
-    g = generator(w.config_id, STREAM_X, step, layer, seed=seed)
+    g = generator(w.seed_key, STREAM_X, step, layer, seed=seed)
     return f32_to_bf16_bits(g.normal(0.0, 1.0, size=(T, s.d)))
 
 
@@ -178,7 +179,7 @@ def zipf_reuse_trace(L: int, E: int, k: int, B: int, steps: int, alpha: float, r
 
 def trace_for(w: Workload, seed: int = 0, steps: int | None = None) -> np.ndarray:
     s = w.shape
-    g = generator(w.config_id, STREAM_TRACE, seed=seed)
+    g = generator(w.seed_key, STREAM_TRACE, seed=seed)
     return zipf_reuse_trace(s.L, s.E, s.k, w.T, w.steps if steps is None else steps,
                             w.zipf_alpha, w.reuse, g)
 
@@ -196,7 +197,7 @@ def allowed_mask(trace_row: np.ndarray, E: int) -> np.ndarray:
 # torch's round-to-nearest-even conversion.  Used for the large workloads, where
 # the oracle reads the same host memory afterwards.
 
-def fill_records_torch(view, config_id: int, seed: int = 0, std: float = 0.02, chunk_rows: int = 16):
+def fill_records_torch(view, seed_key: int, seed: int = 0, std: float = 0.02, chunk_rows: int = 16):
     """Fills a uint16 [rows, record_elems] host array (pinned or not) with N(0, std^2) bf16."""
     import torch
     rows, n = view.shape
@@ -204,17 +205,17 @@ def fill_records_torch(view, config_id: int, seed: int = 0, std: float = 0.02, c
     g = torch.Generator(device="cuda")
     for r0 in range(0, rows, chunk_rows):
         r1 = min(rows, r0 + chunk_rows)
-        g.manual_seed(((seed * 1_000_003 + config_id) * 1_000_003 + r0) & 0x7FFFFFFFFFFFFFFF)
+        g.manual_seed(((seed * 1_000_003 + seed_key) * 1_000_003 + r0) & 0x7FFFFFFFFFFFFFFF)
         w = torch.randn((r1 - r0) * n, generator=g, device="cuda", dtype=torch.float32).mul_(std)
         host_t[r0 * n:r1 * n].copy_(w.to(torch.bfloat16).view(torch.int16))
     torch.cuda.synchronize()
 
 
-def tokens_torch(config_id: int, chunk: int, layer: int, T: int, d: int, seed: int = 0):
+def tokens_torch(seed_key: int, chunk: int, layer: int, T: int, d: int, seed: int = 0):
     """Layer input on the GPU: bf16 bits as an int16 CUDA tensor [T, d], values N(0, 1)."""
     import torch
     g = torch.Generator(device="cuda")
-    g.manual_seed(((seed * 1_000_003 + config_id * 7919 + chunk) * 1_000_003 + layer) & 0x7FFFFFFFFFFFFFFF)
+    g.manual_seed(((seed * 1_000_003 + seed_key * 7919 + chunk) * 1_000_003 + layer) & 0x7FFFFFFFFFFFFFFF)
     return torch.randn((T, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
 
 
@@ -269,14 +270,14 @@ def mxfp4_record_from_weights(wg, wu, wd):
 def mxfp4_expert_record(w: Workload, layer_phys: int, expert: int, seed: int = 0) -> np.ndarray:
     """One MXFP4 expert record (uint8), from N(0, 0.02^2) weights."""
     s = w.shape
-    g = generator(w.config_id, STREAM_EXPERT, layer_phys, expert, seed=seed)
+    g = generator(w.seed_key, STREAM_EXPERT, layer_phys, expert, seed=seed)
     wg = g.normal(0.0, 0.02, size=(s.d_ff, s.d))
     wu = g.normal(0.0, 0.02, size=(s.d_ff, s.d))
     wd = g.normal(0.0, 0.02, size=(s.d, s.d_ff))
     return mxfp4_record_from_weights(wg, wu, wd)
 
 
-def fill_mxfp4_records_torch(view, d: int, d_ff: int, config_id: int, seed: int = 0, chunk_rows: int = 8):
+def fill_mxfp4_records_torch(view, d: int, d_ff: int, seed_key: int, seed: int = 0, chunk_rows: int = 8):
     """Fills a uint8 [rows, record_bytes] host array with MXFP4 records of N(0, 0.02^2)
     weights generated and converted on the GPU (same conversion as above)."""
     import torch
@@ -306,7 +307,7 @@ def fill_mxfp4_records_torch(view, d: int, d_ff: int, config_id: int, seed: int 
     for r0 in range(0, rows, chunk_rows):
         r1 = min(rows, r0 + chunk_rows)
         n = r1 - r0
-        g.manual_seed(((seed * 1_000_003 + config_id) * 1_000_003 + 7 * r0 + 1) & 0x7FFFFFFFFFFFFFFF)
+        g.manual_seed(((seed * 1_000_003 + seed_key) * 1_000_003 + 7 * r0 + 1) & 0x7FFFFFFFFFFFFFFF)
         wg = torch.randn((n, d_ff, d), generator=g, device="cuda").mul_(0.02)
         wu = torch.randn((n, d_ff, d), generator=g, device="cuda").mul_(0.02)
         wd = torch.randn((n, d, d_ff), generator=g, device="cuda").mul_(0.02)

@@ -40,11 +40,11 @@ class PinnedPool(HostPool):
         super().__init__(rows, shape.record_bytes, shape.pool_dtype)
         self.shape = shape
 
-    def fill_device_random(self, config_id: int, seed: int = 0):
+    def fill_device_random(self, seed_key: int, seed: int = 0):
         if self.shape.mxfp4:
-            fill_mxfp4_records_torch(self.view, self.shape.d, self.shape.d_ff, config_id, seed)
+            fill_mxfp4_records_torch(self.view, self.shape.d, self.shape.d_ff, seed_key, seed)
         else:
-            fill_records_torch(self.view, config_id, seed)
+            fill_records_torch(self.view, seed_key, seed)
 
 
 class Engine:

@@ -31,9 +31,9 @@ def _compare_plan(plan, ref_plan, ref_idx, where):
 
 
 @pytest.mark.parametrize("key,L_phys,steps,y_every,fq", [
-    ("c2", 40, 6, 4, 22337),     # 40 layers d=2048 E=128 top-8, batch 1, full pool, cache 37 %
-    ("c2b8", 40, 4, 16, 22337),  # same, batch 8
-    ("c3", 2, 3, 8, 18000),      # 43 layers d=4096 E=256 top-6, batch 1, cache 11 %, aliased pool
+    ("decode-L40-d2048-E128-top8", 40, 6, 4, 22337),     # 40 layers d=2048 E=128 top-8, batch 1, full pool, cache 37 %
+    ("decode-L40-d2048-E128-top8-b8", 40, 4, 16, 22337),  # same, batch 8
+    ("decode-L43-d4096-E256-top6", 2, 3, 8, 18000),      # 43 layers d=4096 E=256 top-6, batch 1, cache 11 %, aliased pool
 ])
 def test_decode_full_size(key, L_phys, steps, y_every, fq):
     torch = torch_mod()
@@ -42,7 +42,7 @@ def test_decode_full_size(key, L_phys, steps, y_every, fq):
     T = wl.T
     _say("decode full size", wl.name, "L_phys", L_phys)
     pool = PinnedPool(s, L_phys * s.E)
-    pool.fill_device_random(wl.config_id)
+    pool.fill_device_random(wl.seed_key)
     eng = Engine(s, pool, wl.n_slots, T_max=T, frac_q16=fq, L_phys=L_phys)
     try:
         ref_cache = SlotTable(wl.n_slots, s.L, s.E)
@@ -78,14 +78,14 @@ def test_prefill_8k_chunk_full_size():
     """8192-token chunk through the d=4096, E=256, top-6, d_ff=2048 layer shape with
     double buffering (aliased pool of 2 physical layers), first layers of the stack."""
     torch = torch_mod()
-    wl = synth.WORKLOADS["c4"]
+    wl = synth.WORKLOADS["prefill8k-L43-d4096-E256-top6"]
     s = wl.shape
     T = wl.T
     L_phys = 2
     n_layers = 3
     _say("prefill full size", wl.name)
     pool = PinnedPool(s, L_phys * s.E)
-    pool.fill_device_random(wl.config_id)
+    pool.fill_device_random(wl.seed_key)
     eng = Engine(s, pool, wl.n_slots, T_max=T, frac_q16=0, min_fill=0, max_fetch=0, prefill_overlap=1,
                  L_phys=L_phys, cpu_threads=2)
     try:
@@ -96,7 +96,7 @@ def test_prefill_8k_chunk_full_size():
         for l in range(n_layers):
             for e in (0, 1, s.E - 1):
                 assert ft.ft_prefill_slot(eng.ctx, l, e) == bufs[l % 2][e]
-            xd = synth.tokens_torch(wl.config_id, 0, l, T, s.d)
+            xd = synth.tokens_torch(wl.seed_key, 0, l, T, s.d)
             wr = synth.router_weights(wl, l)
             y = torch.empty((T, s.d), dtype=torch.float32, device="cuda")
             ft.ft_moe_prefill_layer(eng.ctx, l, xd, T, dev_u16(wr), y, copy=eng.copy)
@@ -127,10 +127,10 @@ def test_router_and_grouping_8k_full_size():
     torch = torch_mod()
     from oracle.permute import group_pairs
     from oracle.router import router_logits, topk
-    wl = synth.WORKLOADS["c4"]
+    wl = synth.WORKLOADS["prefill8k-L43-d4096-E256-top6"]
     s = wl.shape
     T = wl.T
-    xd = synth.tokens_torch(wl.config_id, 0, 0, T, s.d)
+    xd = synth.tokens_torch(wl.seed_key, 0, 0, T, s.d)
     wr = synth.router_weights(wl, 0)
     idx = torch.empty((T, s.k), dtype=torch.int32, device="cuda")
     g = torch.empty((T, s.k), dtype=torch.float32, device="cuda")

@@ -86,7 +86,7 @@ def test_decode_trace_parity(fq, min_fill, max_fetch, T, N):
         pool.free()
 
 
-C1 = Workload("c1-layer-d256-E8-top2", 1, Shape(1, 8, 256, 512, 2), 16, 1.0)
+C1 = Workload("layer-d256-E8-top2", 1, Shape(1, 8, 256, 512, 2), 16, 1.0)
 
 
 def test_single_layer_configuration_all_resident():

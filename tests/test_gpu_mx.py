@@ -243,12 +243,12 @@ def test_mx_full_size_prefill_chunk_and_decode():
     8192-token chunk through two layers (double-buffered, aliased pool of two
     physical layers), then batch-1 decode steps with the cache of 1210 slots."""
     torch = torch_mod()
-    wl = synth.WORKLOADS["c5"]
+    wl = synth.WORKLOADS["mxfp4-prefill8k-L43-d4096-E256-top6"]
     s = wl.shape
     L_phys = 2
     _say("mx full size", wl.name)
     pool = PinnedPool(s, L_phys * s.E)
-    pool.fill_device_random(wl.config_id)
+    pool.fill_device_random(wl.seed_key)
     eng = Engine(s, pool, wl.n_slots, T_max=wl.T, frac_q16=20000, prefill_overlap=1, L_phys=L_phys, cpu_threads=0)
     try:
         ref_cache = SlotTable(wl.n_slots, s.L, s.E)
@@ -256,7 +256,7 @@ def test_mx_full_size_prefill_chunk_and_decode():
         ref_cache.prefill_begin()
         outs = []
         for l in range(2):
-            xd = synth.tokens_torch(wl.config_id, 0, l, wl.T, s.d)
+            xd = synth.tokens_torch(wl.seed_key, 0, l, wl.T, s.d)
             wr = synth.router_weights(wl, l)
             y = torch.empty((wl.T, s.d), dtype=torch.float32, device="cuda")
             ft.ft_moe_prefill_layer(eng.ctx, l, xd, wl.T, dev_u16(wr), y, copy=eng.copy)
@@ -273,7 +273,7 @@ def test_mx_full_size_prefill_chunk_and_decode():
                                  form="prefill")
             ok, mxe, l1 = within_tolerance(host(y)[sample], ref_y)
             assert ok, (l, mxe, l1)
-        wd = synth.WORKLOADS["c5d"]
+        wd = synth.WORKLOADS["mxfp4-decode-L43-d4096-E256-top6"]
         tr = synth.trace_for(wd, steps=2)
         plan = ft.ft_plan()
         for st in range(2):

@@ -28,7 +28,7 @@ def test_seeded_and_workload_sizes():
     a = generator(1, 2, 5).normal(size=4)
     b = generator(1, 2, 5).normal(size=4)
     assert np.array_equal(a, b)
-    assert WORKLOADS["c2"].n_slots == 1894
-    assert WORKLOADS["c3"].n_slots == 1210
-    assert WORKLOADS["c2"].shape.record_bytes == 9437184
-    assert WORKLOADS["c3"].shape.record_bytes == 50331648
+    assert WORKLOADS["decode-L40-d2048-E128-top8"].n_slots == 1894
+    assert WORKLOADS["decode-L43-d4096-E256-top6"].n_slots == 1210
+    assert WORKLOADS["decode-L40-d2048-E128-top8"].shape.record_bytes == 9437184
+    assert WORKLOADS["decode-L43-d4096-E256-top6"].shape.record_bytes == 50331648
