@@ -44,15 +44,27 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// E2M1 code (4 bits) -> fp32: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.
-__device__ __forceinline__ float e2m1(uint32_t c) {
-  const uint32_t m = c & 7u;
-  const uint32_t bits = m >= 2u ? ((m << 22) + (126u << 23)) : (m == 1u ? 0x3f000000u : 0u);
-  return __uint_as_float(bits | ((c & 8u) << 28));
-}
-
 // 2^(s - 127) for an E8M0 byte (s < 255).
 __device__ __forceinline__ float e8m0(uint32_t s) { return s ? __uint_as_float(s << 23) : 1.17549435e-38f * 0.5f; }
+
+// gfx950 converts two E2M1 codes (byte `sel` of a word, the low nibble first) to a
+// pair of bf16 or fp32 values in one instruction; with scale 1 both are exact.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// acc + sum over the 8 elements of one code word times 4 words of bf16 pairs
+// (element 2b of the word in the low half of xw[b]); products summed in pairs.
+__device__ __forceinline__ float word_dot_bf16(uint32_t cw, const uint32_t (&xw)[4], float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 0),
+                                        __builtin_bit_cast(bf16x2_t, xw[0]), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 1),
+                                        __builtin_bit_cast(bf16x2_t, xw[1]), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 2),
+                                        __builtin_bit_cast(bf16x2_t, xw[2]), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, 1.0f, 3),
+                                        __builtin_bit_cast(bf16x2_t, xw[3]), acc, false);
+  return acc;
+}
 
 // sum over the 32 elements of one weight block (16 code bytes) times 32 bf16 activations
 __device__ __forceinline__ float block_dot_bf16(uint4 codes, const uint16_t* __restrict__ xb) {
@@ -62,13 +74,25 @@ __device__ __forceinline__ float block_dot_bf16(uint4 codes, const uint16_t* __r
   for (int q = 0; q < 4; ++q) {
     const uint4 xv = *reinterpret_cast<const uint4*>(xb + 8 * q);  // 8 bf16 = elements 8q..8q+7
     const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {  // code byte b of word q -> elements 8q+2b, 8q+2b+1
-      const uint32_t byte = (cw[q] >> (8 * b)) & 0xffu;
-      acc = fmaf(e2m1(byte & 0xfu), bf_lo(xw[b]), acc);
-      acc = fmaf(e2m1(byte >> 4), bf_hi(xw[b]), acc);
-    }
+    acc = word_dot_bf16(cw[q], xw, acc);
   }
+  return acc;
+}
+
+// acc + sum over the 8 elements of one code word times 8 fp32 values
+__device__ __forceinline__ float word_dot_f32(uint32_t cw, float4 h0, float4 h1, float acc) {
+  f32x2_t w = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0);
+  acc = fmaf(w.x, h0.x, acc);
+  acc = fmaf(w.y, h0.y, acc);
+  w = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1);
+  acc = fmaf(w.x, h0.z, acc);
+  acc = fmaf(w.y, h0.w, acc);
+  w = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2);
+  acc = fmaf(w.x, h1.x, acc);
+  acc = fmaf(w.y, h1.y, acc);
+  w = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3);
+  acc = fmaf(w.x, h1.z, acc);
+  acc = fmaf(w.y, h1.w, acc);
   return acc;
 }
 
@@ -79,13 +103,7 @@ __device__ __forceinline__ float block_dot_f32(uint4 codes, const float* __restr
   for (int q = 0; q < 4; ++q) {
     const float4 h0 = *reinterpret_cast<const float4*>(hb + 8 * q);
     const float4 h1 = *reinterpret_cast<const float4*>(hb + 8 * q + 4);
-    const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t byte = (cw[q] >> (8 * b)) & 0xffu;
-      acc = fmaf(e2m1(byte & 0xfu), hv[2 * b], acc);
-      acc = fmaf(e2m1(byte >> 4), hv[2 * b + 1], acc);
-    }
+    acc = word_dot_f32(cw[q], h0, h1, acc);
   }
   return acc;
 }
