@@ -104,7 +104,13 @@ using MxRowDotsFn = void (*)(const uint8_t* codes, const uint8_t* sc, int n, con
 constexpr float kE2M1[16] = {0.0f,  0.5f,  1.0f,  1.5f,  2.0f,  3.0f,  4.0f,  6.0f,
                              -0.0f, -0.5f, -1.0f, -1.5f, -2.0f, -3.0f, -4.0f, -6.0f};
 
-inline float e8m0_f(uint8_t s) { return std::ldexp(1.0f, (int)s - 127); }
+// 2^(s - 127) for an E8M0 byte: the exponent field itself, or 2^-127 (subnormal) for s = 0
+inline float e8m0_f(uint8_t s) {
+  const uint32_t u = s ? (uint32_t)s << 23 : 0x00400000u;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
 
 void mx_row_dots_scalar(const uint8_t* codes, const uint8_t* sc, int n, const float* const* xs, int nx,
                         float* out) {
@@ -153,25 +159,59 @@ __attribute__((target("avx2,fma"))) void mx_row_dots_avx2(const uint8_t* codes, 
   }
 }
 
+// The 32 weights of block b: codes through a 16-entry table scaled by the block's
+// E8M0 scale (elements 0..15 in w0, 16..31 in w1).
+__attribute__((target("avx512f,avx512bw"))) inline void mx_block_weights(const uint8_t* codes, const uint8_t* sc,
+                                                                         int b, __m512 lut, __m512& w0,
+                                                                         __m512& w1) {
+  const __m128i m4 = _mm_set1_epi8(0x0f);
+  const __m128i raw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(codes + 16 * b));
+  const __m128i lo = _mm_and_si128(raw, m4);
+  const __m128i hi = _mm_and_si128(_mm_srli_epi16(raw, 4), m4);
+  const __m512 lut_s = _mm512_mul_ps(lut, _mm512_set1_ps(e8m0_f(sc[b])));
+  w0 = _mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpacklo_epi8(lo, hi)), lut_s);
+  w1 = _mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpackhi_epi8(lo, hi)), lut_s);
+}
+
+// Independent accumulators per activation vector (two per block, four over two
+// blocks when there is one vector) keep the FMA latency off the critical path.
 __attribute__((target("avx512f,avx512bw"))) void mx_row_dots_avx512(const uint8_t* codes, const uint8_t* sc, int n,
                                                                       const float* const* xs, int nx, float* out) {
   const __m512 lut = _mm512_loadu_ps(kE2M1);
-  const __m128i m4 = _mm_set1_epi8(0x0f);
-  __m512 acc[MAXV];
-  for (int v = 0; v < MAXV; ++v) acc[v] = _mm512_setzero_ps();
-  for (int b = 0; b < n / 32; ++b) {
-    const __m128i raw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(codes + 16 * b));
-    const __m128i lo = _mm_and_si128(raw, m4);
-    const __m128i hi = _mm_and_si128(_mm_srli_epi16(raw, 4), m4);
-    const __m512 s = _mm512_set1_ps(e8m0_f(sc[b]));
-    const __m512 w0 = _mm512_mul_ps(_mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpacklo_epi8(lo, hi)), lut), s);
-    const __m512 w1 = _mm512_mul_ps(_mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpackhi_epi8(lo, hi)), lut), s);
+  const int nb = n / 32;
+  if (nx == 1) {
+    const float* x = xs[0];
+    __m512 a0 = _mm512_setzero_ps(), a1 = _mm512_setzero_ps(), a2 = _mm512_setzero_ps(), a3 = _mm512_setzero_ps();
+    int b = 0;
+    for (; b + 2 <= nb; b += 2) {
+      __m512 w0, w1, w2, w3;
+      mx_block_weights(codes, sc, b, lut, w0, w1);
+      mx_block_weights(codes, sc, b + 1, lut, w2, w3);
+      a0 = _mm512_fmadd_ps(w0, _mm512_loadu_ps(x + 32 * b), a0);
+      a1 = _mm512_fmadd_ps(w1, _mm512_loadu_ps(x + 32 * b + 16), a1);
+      a2 = _mm512_fmadd_ps(w2, _mm512_loadu_ps(x + 32 * b + 32), a2);
+      a3 = _mm512_fmadd_ps(w3, _mm512_loadu_ps(x + 32 * b + 48), a3);
+    }
+    for (; b < nb; ++b) {
+      __m512 w0, w1;
+      mx_block_weights(codes, sc, b, lut, w0, w1);
+      a0 = _mm512_fmadd_ps(w0, _mm512_loadu_ps(x + 32 * b), a0);
+      a1 = _mm512_fmadd_ps(w1, _mm512_loadu_ps(x + 32 * b + 16), a1);
+    }
+    out[0] = _mm512_reduce_add_ps(_mm512_add_ps(_mm512_add_ps(a0, a1), _mm512_add_ps(a2, a3)));
+    return;
+  }
+  __m512 acc0[MAXV], acc1[MAXV];
+  for (int v = 0; v < MAXV; ++v) acc0[v] = acc1[v] = _mm512_setzero_ps();
+  for (int b = 0; b < nb; ++b) {
+    __m512 w0, w1;
+    mx_block_weights(codes, sc, b, lut, w0, w1);
     for (int v = 0; v < nx; ++v) {
-      acc[v] = _mm512_fmadd_ps(w0, _mm512_loadu_ps(xs[v] + 32 * b), acc[v]);
-      acc[v] = _mm512_fmadd_ps(w1, _mm512_loadu_ps(xs[v] + 32 * b + 16), acc[v]);
+      acc0[v] = _mm512_fmadd_ps(w0, _mm512_loadu_ps(xs[v] + 32 * b), acc0[v]);
+      acc1[v] = _mm512_fmadd_ps(w1, _mm512_loadu_ps(xs[v] + 32 * b + 16), acc1[v]);
     }
   }
-  for (int v = 0; v < nx; ++v) out[v] = _mm512_reduce_add_ps(acc[v]);
+  for (int v = 0; v < nx; ++v) out[v] = _mm512_reduce_add_ps(_mm512_add_ps(acc0[v], acc1[v]));
 }
 
 MxRowDotsFn g_mx_row_dots = nullptr;

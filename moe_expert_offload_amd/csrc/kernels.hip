@@ -616,7 +616,7 @@ __global__ __launch_bounds__(256) void h2d_copy_kernel(const uint8_t* __restrict
   h2d_stride_copy(reinterpret_cast<const u32x4_t*>(src), reinterpret_cast<u32x4_t*>(dst), bytes / 16);
 }
 
-constexpr int kFillBlocks = 256;
+constexpr int kFillBlocks = 64;  // enough reads in flight for the link; more only congest it
 
 // Decode router in one launch: one wavefront per (token, expert) logit (same
 // arithmetic order as router_logits_kernel: lane l owns elements (i mod 512)/8 ==
