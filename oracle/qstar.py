@@ -88,3 +88,45 @@ def phased_step_time(m: int, q: int, S: float, B_P: float, B_H: float) -> float:
     if done_during_fill >= cpu_bytes:
         return t_fill
     return t_fill + (cpu_bytes - done_during_fill) / B_H
+
+
+# ---- the bandwidth profile: contended fraction and the hybrid gate ----------------
+#
+# [AIN] "How to use it" / "How to maintain it": the fetch fraction is computed once
+# at engine start from a per-machine bandwidth profile.  The preferred derivation
+# uses a contended pair -- the PCIe gather rate measured while the CPU expert
+# kernel runs (pcie_ov) and the CPU kernel's rate measured while the gather runs
+# (cpu_ov) -- as pcie_ov / (pcie_ov + cpu_ov); a profile without that pair falls
+# back to B_P / B_H, Eq. (4).  The two agree when the contention is total (the CPU
+# keeps only the residual B_H - B_P).  [AIN] "Why use it": the hybrid backend is
+# chosen only when B_H exceeds twice B_P, and only when every benched workload of
+# the expert format agrees; otherwise the plain offload backend.
+
+
+def frac_q16_contended(pcie_ov: float, cpu_ov: float) -> int:
+    """pcie_ov / (pcie_ov + cpu_ov) in Q16, rounded half to even, clamped to [0, 2^16]."""
+    if pcie_ov <= 0.0:
+        return 0
+    if cpu_ov <= 0.0:
+        return Q16
+    v = round(pcie_ov / (pcie_ov + cpu_ov) * Q16)
+    return int(min(Q16, max(0, v)))
+
+
+def fetch_fraction_q16(B_P: float, B_H: float, pcie_ov: float | None = None, cpu_ov: float | None = None) -> int:
+    """The contended pair when the profile has it (both rates positive), else Eq. (4)."""
+    if pcie_ov is not None and cpu_ov is not None and pcie_ov > 0.0 and cpu_ov > 0.0:
+        return frac_q16_contended(pcie_ov, cpu_ov)
+    return frac_q16(B_P, B_H)
+
+
+def hybrid_gate(B_P: float, B_H: float, threshold: float = 2.0) -> bool:
+    """One workload's verdict: hybrid only when B_H > threshold * B_P."""
+    return B_H > threshold * B_P
+
+
+def recommend_hybrid(pairs, threshold: float = 2.0) -> bool:
+    """Unanimous or offload: hybrid only when there is at least one benched workload
+    and every one of them passes the gate."""
+    pairs = list(pairs)
+    return len(pairs) > 0 and all(hybrid_gate(p, h, threshold) for p, h in pairs)

@@ -6,7 +6,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle.qstar import Q16, frac_q16, phased_step_time, q_rule, q_split
+from oracle.qstar import (Q16, fetch_fraction_q16, frac_q16, frac_q16_contended, hybrid_gate, phased_step_time,
+                          q_rule, q_split, recommend_hybrid)
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "qstar_pages.json")))
 
@@ -114,3 +115,46 @@ def test_caps_and_floor_order():
     assert q_split(5, 0, min_fill=3) == 3
     assert q_split(2, 0, min_fill=3) == 2
     assert q_split(4, Q16, avail=0) == 0
+
+
+def test_hybrid_gate_on_table1():
+    """Every Table 1 machine's printed ratio and gate verdict (threshold 2.0)."""
+    g = GOLD["gate_table1"]
+    rows = {r["system"]: (r["B_P"], r["B_H"]) for r in GOLD["table1"]["rows"]}
+    for r in g["rows"]:
+        B_P, B_H = rows[r["system"]]
+        assert round(B_H / B_P, 2) == pytest.approx(r["ratio"]), r
+        assert hybrid_gate(B_P, B_H, g["threshold"]) == r["hybrid"], r
+    # the gate is strict: exactly twice B_P does not pass
+    assert not hybrid_gate(10.0, 20.0) and hybrid_gate(10.0, 20.000001)
+
+
+def test_recommendation_is_unanimous_or_offload():
+    t1 = [(r["B_P"], r["B_H"]) for r in GOLD["table1"]["rows"]]
+    assert recommend_hybrid([t1[1], t1[2], t1[4], t1[5]])  # the four machines that pass
+    assert not recommend_hybrid(t1)                        # a mixed verdict resolves to offload
+    assert not recommend_hybrid([t1[0]])
+    assert not recommend_hybrid([])                        # no benched workload, no upgrade
+
+
+def test_contended_fraction_closed_forms():
+    """Under total contention (the CPU keeps only B_H - B_P while the link runs) the
+    contended fraction is Eq. (4) exactly; when the CPU kernel never saturates DRAM
+    (cpu_ov = B_H) it is B_P / (B_P + B_H), below Eq. (4)."""
+    for r in GOLD["table1"]["rows"]:
+        B_P, B_H = r["B_P"], r["B_H"]
+        assert frac_q16_contended(B_P, B_H - B_P) == frac_q16(B_P, B_H), r
+        low = frac_q16_contended(B_P, B_H)
+        assert low == round(B_P / (B_P + B_H) * Q16)
+        assert low < frac_q16(B_P, B_H)
+
+
+def test_contended_fraction_rounding_and_fallback():
+    # ties go to even: 2^16 * 1/131072 = 0.5 -> 0, 2^16 * 3/131072 = 1.5 -> 2
+    assert frac_q16_contended(1.0, 131071.0) == 0
+    assert frac_q16_contended(3.0, 131069.0) == 2
+    assert frac_q16_contended(0.0, 5.0) == 0 and frac_q16_contended(5.0, 0.0) == Q16
+    # a profile without the pair falls back to Eq. (4)
+    assert fetch_fraction_q16(52.7, 77.3) == frac_q16(52.7, 77.3)
+    assert fetch_fraction_q16(52.7, 77.3, 0.0, 30.0) == frac_q16(52.7, 77.3)
+    assert fetch_fraction_q16(52.7, 77.3, 50.0, 30.0) == frac_q16_contended(50.0, 30.0)
