@@ -76,6 +76,15 @@ def phased_time(m, q, S, B_P, B_H):
     return t_fill if done >= rest else t_fill + (rest - done) / B_H
 
 
+def bw_profile(ft, fshape, pool, scratch, B_P, B_H):
+    """The contended pair next to B_P and B_H: both fetch fractions and the 2x hybrid gate
+    (the split itself uses Eq. 4, B_P / B_H)."""
+    po, co = ft.ft_bench_bw_contended(fshape, pool.ptr, 64, scratch, 0)
+    return {"pcie_ov_GBs": round(po / 1e9, 2), "cpu_ov_GBs": round(co / 1e9, 2),
+            "frac_q16_eq4": ft.ft_frac_q16(B_P, B_H), "frac_q16_contended": ft.ft_frac_q16_contended(po, co),
+            "hybrid_gate_2x": ft.ft_recommend_hybrid([B_P], [B_H], 2.0)}
+
+
 def run_decode(args, torch, ft, synth, HostPool):
     wl = synth.WORKLOADS[args.workload]
     s = wl.shape
@@ -93,6 +102,7 @@ def run_decode(args, torch, ft, synth, HostPool):
     fshape = ft.make_shape(s.L, s.E, s.d, s.d_ff, s.k)
     scratch = torch.empty(64 * S, dtype=torch.uint8, device="cuda")
     B_P, B_H = ft.ft_bench_bw(fshape, pool.ptr, 64, scratch, 0)
+    bwp = bw_profile(ft, fshape, pool, scratch, B_P, B_H)
     del scratch
     fq = ft.ft_frac_q16(B_P, B_H) if args.frac_q16 < 0 else args.frac_q16
     log(f"B_P {B_P / 1e9:.1f} GB/s, B_H {B_H / 1e9:.1f} GB/s, frac_q16 {fq}")
@@ -174,7 +184,7 @@ def run_decode(args, torch, ft, synth, HostPool):
         "tok_s": args.steps * T / elapsed,
         "ms_per_step": elapsed / args.steps * 1e3,
         "workload": wl.name, "T": T, "L": s.L, "n_slots": N, "L_phys": L_phys,
-        "B_P_GBs": B_P / 1e9, "B_H_GBs": B_H / 1e9, "frac_q16": fq, "min_fill": args.min_fill,
+        "B_P_GBs": B_P / 1e9, "B_H_GBs": B_H / 1e9, "frac_q16": fq, "bw_profile": bwp, "min_fill": args.min_fill,
         "cpu_threads": args.cpu_threads,
         "miss_rate_reads": 1.0 - stats["read_hits"] / reads,
         "miss_rate_unique": stats["unique_misses"] / max(stats["unique_hits"] + stats["unique_misses"], 1),
@@ -292,6 +302,7 @@ def run_mxfp4(args, torch, ft, synth, HostPool):
         fshape = ft.make_shape(s.L, s.E, s.d, s.d_ff, s.k, ft.FT_W_MXFP4)
         scratch = torch.empty(64 * S, dtype=torch.uint8, device="cuda")
         B_P, B_H = ft.ft_bench_bw(fshape, pool.ptr, 64, scratch, 0)
+        bwp = bw_profile(ft, fshape, pool, scratch, B_P, B_H)
         del scratch
         fq = ft.ft_frac_q16(B_P, B_H) if args.frac_q16 < 0 else args.frac_q16
         log(f"mxfp4 B_P {B_P / 1e9:.1f} GB/s, B_H {B_H / 1e9:.1f} GB/s, frac_q16 {fq}")
@@ -381,7 +392,7 @@ def run_mxfp4(args, torch, ft, synth, HostPool):
 
     return {
         "workload": wl.name, "record_MB": S / 1e6, "L": s.L, "L_phys": L_phys, "B_P_GBs": B_P / 1e9,
-        "B_H_GBs": B_H / 1e9, "frac_q16": fq,
+        "B_H_GBs": B_H / 1e9, "frac_q16": fq, "bw_profile": bwp,
         "prefill": {"tokens": n_chunks * T, "chunks": n_chunks, "tok_s": n_chunks * T / el_pf,
                     "s_per_chunk": el_pf / n_chunks, "h2d_GB": n_chunks * s.L * s.E * S / 1e9,
                     "h2d_GBs_effective": n_chunks * s.L * s.E * S / el_pf / 1e9,

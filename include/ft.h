@@ -70,6 +70,8 @@ extern "C" {
                                  ([AIN] "Failure modes": asserted at construction) */
 #define FT_EHIP (-6)          /* a HIP call failed */
 #define FT_EUNSUPPORTED (-7)  /* format or mode not built */
+#define FT_ENOPROFILE (-8)    /* no usable bandwidth profile (missing, unreadable, or for another
+                                 expert format: [AIN] "How to maintain it", no guessing) */
 #define FT_WOVERLAP_OFF 1     /* warning: resize left fewer than 2E slots, prefill overlap
                                  disabled ([AIN] "Failure modes": warn-and-disable on rebuild) */
 
@@ -186,6 +188,47 @@ int32_t ft_qstar_split(int32_t m, uint32_t frac_q16, int32_t min_fill, int32_t m
  * ft_pool_free.  Errors: FT_ENOMEM, FT_EHIP. */
 int ft_pool_alloc(size_t bytes, void** out);
 int ft_pool_free(void* ptr);
+
+/* ---- bandwidth profile ([AIN] "How to use it", "How to maintain it") --------
+ * A machine's profile for one expert format: B_P and B_H measured apart, and the
+ * contended pair measured together (pcie_ov: the PCIe rate while the CPU expert
+ * kernel runs; cpu_ov: the CPU kernel's rate while the PCIe reads run; 0 when not
+ * measured).  Bytes per second. */
+typedef struct {
+  double B_P, B_H, pcie_ov, cpu_ov;
+  int32_t fmt; /* ft_wfmt the profile was measured with */
+} ft_bw_profile;
+
+/* pcie_ov / (pcie_ov + cpu_ov) in Q16, rounded half to even: 0 when pcie_ov <= 0,
+ * 65536 when cpu_ov <= 0.  Equals ft_frac_q16(B_P, B_H) when the contention is
+ * total (cpu_ov = B_H - B_P, pcie_ov = B_P). */
+uint32_t ft_frac_q16_contended(double pcie_ov, double cpu_ov);
+
+/* The fetch fraction a profile gives: the contended pair when both rates are
+ * positive, else Eq. (4) from B_P and B_H.  0 for a null profile. */
+uint32_t ft_fetch_fraction_q16(const ft_bw_profile* profile);
+
+/* The hybrid gate ([AIN] "Why use it"): 1 (hybrid) only when every one of the n
+ * benched workloads of a format has B_H > threshold * B_P, else 0 (plain offload;
+ * also for n = 0).  FT_EINVAL for n < 0, null arrays with n > 0, or threshold <= 0. */
+int32_t ft_recommend_hybrid(const double* B_P, const double* B_H, int32_t n, double threshold);
+
+/* Measures the contended pair: record reads over PCIe into dev_scratch (records
+ * [0, n_records/2) of the pool, one launch per record, kept in flight) while the
+ * host expert kernel runs over records [n_records/2, n_records) at one token
+ * (`threads` workers, 0 = all); each rate counts only work done while the other
+ * side ran.  n_records >= 2; dev_scratch holds n_records/2 records. */
+int ft_bench_bw_contended(const ft_shape* shape, const void* host_pool, int32_t n_records,
+                          void* dev_scratch, int32_t threads, double* pcie_ov, double* cpu_ov);
+
+/* Profile files, one per GPU and expert format: `out` gets
+ * "<dir>/ft_bw_<GPU UUID in hex>_<bf16|mxfp4>.txt" (FT_ENOMEM if out_len is too
+ * small).  save writes the profile as text; load reads one back and returns
+ * FT_ENOPROFILE when the file is missing or unreadable, lacks B_P or B_H, or was
+ * measured for a format other than `fmt`. */
+int ft_bw_profile_path(int32_t device, int32_t fmt, const char* dir, char* out, size_t out_len);
+int ft_bw_profile_save(const char* path, const ft_bw_profile* profile);
+int ft_bw_profile_load(const char* path, int32_t fmt, ft_bw_profile* profile);
 
 /* Measures B_P (whole records read by the GPU from the pinned pool over PCIe into
  * device memory, as the decode fills move them, `n_records` of them, one launch

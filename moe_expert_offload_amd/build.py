@@ -35,6 +35,7 @@ SOURCES = [
     ("api.cpp", CXX, HOST_FLAGS),
     ("cache.cpp", CXX, HOST_FLAGS),
     ("qstar.cpp", CXX, HOST_FLAGS),
+    ("bwprofile.cpp", CXX, HOST_FLAGS),
     ("cpu_exec.cpp", CXX, HOST_FLAGS),
 ]
 

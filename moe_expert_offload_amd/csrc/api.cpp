@@ -286,6 +286,7 @@ const char* ft_strerror(int st) {
     case FT_ECAP: return "prefill overlap needs at least 2E slots";
     case FT_EHIP: return "HIP error";
     case FT_EUNSUPPORTED: return "unsupported";
+    case FT_ENOPROFILE: return "no usable bandwidth profile";
     case FT_WOVERLAP_OFF: return "warning: prefill overlap disabled";
     default: return "unknown status";
   }
@@ -958,6 +959,91 @@ int ft_profile_read(ft_ctx_t c, ft_profile* out) {
 }
 
 // ---- bandwidth probe ---------------------------------------------------------------
+
+// [AIN] "How to maintain it": the contended pair.  Record reads over PCIe are kept
+// in flight (a second pass is queued whenever fewer than two are outstanding) while
+// the host expert kernel runs passes over other records; the CPU rate counts the
+// passes it finished, the PCIe rate the read passes finished before the CPU stopped.
+int ft_bench_bw_contended(const ft_shape* shape, const void* host_pool, int32_t n_records, void* dev_scratch,
+                          int32_t threads, double* pcie_ov, double* cpu_ov) {
+  if (!shape_ok(shape) || !host_pool || !dev_scratch || n_records < 2 || !pcie_ov || !cpu_ov)
+    return fail(FT_EINVAL, "bench_bw_contended: bad argument (n_records >= 2)");
+  const size_t S = ft_record_bytes(shape);
+  const int n_gpu = n_records / 2, n_cpu = n_records - n_gpu;
+  const uint8_t* pool = static_cast<const uint8_t*>(host_pool);
+  hipStream_t s = nullptr;
+  FT_HIP(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+  std::vector<hipEvent_t> ends;
+  hipEvent_t start = nullptr;
+  ft::CpuPool* cpu = nullptr;
+  auto cleanup = [&]() {
+    (void)hipStreamSynchronize(s);
+    for (hipEvent_t e : ends) (void)hipEventDestroy(e);
+    if (start) (void)hipEventDestroy(start);
+    (void)hipStreamDestroy(s);
+    if (cpu) ft::cpu_pool_destroy(cpu);
+  };
+  auto enqueue_pass = [&]() -> int {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return fail(FT_EHIP, "bench_bw_contended: hipEventCreate failed");
+    ends.push_back(e);
+    for (int i = 0; i < n_gpu; ++i)
+      if (int rc = ft::launch_h2d_copy(pool + (size_t)i * S, static_cast<uint8_t*>(dev_scratch) + (size_t)i * S, S, s))
+        return rc;
+    if (hipEventRecord(e, s) != hipSuccess) return fail(FT_EHIP, "bench_bw_contended: hipEventRecord failed");
+    return FT_OK;
+  };
+  cpu = ft::cpu_pool_create(threads);
+  std::vector<uint16_t> x((size_t)shape->d, 0x3c00);  // 2^-7 in bf16 words
+  std::vector<float> part((size_t)shape->d);
+  std::vector<ft::CpuExpert> ex(n_cpu);
+  for (int i = 0; i < n_cpu; ++i) {
+    ex[i].rec = pool + (size_t)(n_gpu + i) * S;
+    ex[i].n_use = 1;
+    ex[i].use[0] = ft::CpuUse{0, 1.0f};
+  }
+  if (hipEventCreate(&start) != hipSuccess || hipEventRecord(start, s) != hipSuccess) {
+    cleanup();
+    return fail(FT_EHIP, "bench_bw_contended: start event failed");
+  }
+  for (int i = 0; i < 2; ++i)
+    if (int rc = enqueue_pass()) {
+      cleanup();
+      return rc;
+    }
+  size_t done_seen = 0;
+  auto completed = [&]() {
+    while (done_seen < ends.size() && hipEventQuery(ends[done_seen]) == hipSuccess) ++done_seen;
+    return done_seen;
+  };
+  const double t0 = now_us();
+  int passes = 0;
+  while (passes < 3 || (now_us() - t0 < 150000.0 && passes < 256)) {
+    ft::cpu_pool_submit(cpu, x.data(), 1, shape->d, shape->d_ff, shape->fmt, ex.data(), n_cpu, part.data());
+    ft::cpu_pool_wait(cpu);
+    ++passes;
+    while (ends.size() - completed() < 2)
+      if (int rc = enqueue_pass()) {
+        cleanup();
+        return rc;
+      }
+  }
+  const double t_cpu = now_us() - t0;
+  const size_t gpu_done = completed();
+  if (gpu_done == 0) {
+    cleanup();
+    return fail(FT_EHIP, "bench_bw_contended: no PCIe pass finished while the host kernel ran");
+  }
+  float ms = 0.f;
+  if (hipEventElapsedTime(&ms, start, ends[gpu_done - 1]) != hipSuccess || !(ms > 0.f)) {
+    cleanup();
+    return fail(FT_EHIP, "bench_bw_contended: event timing failed");
+  }
+  *cpu_ov = (double)passes * n_cpu * S / (t_cpu * 1e-6);
+  *pcie_ov = (double)gpu_done * n_gpu * S / (ms * 1e-3);
+  cleanup();
+  return FT_OK;
+}
 
 int ft_bench_bw(const ft_shape* shape, const void* host_pool, int32_t n_records, void* dev_scratch,
                 int32_t threads, double* B_P, double* B_H) {

@@ -45,3 +45,31 @@ extern "C" int32_t ft_qstar_split(int32_t m, uint32_t frac_q16, int32_t min_fill
   if (q < 0) q = 0;
   return (int32_t)q;
 }
+
+// ---- the bandwidth profile's fraction and the hybrid gate -----------------------------
+// [AIN] "How to maintain it": the preferred fraction uses the contended pair,
+// pcie_ov / (pcie_ov + cpu_ov); a profile without it falls back to Eq. (4).
+extern "C" uint32_t ft_frac_q16_contended(double pcie_ov, double cpu_ov) {
+  if (!(pcie_ov > 0.0)) return 0u;
+  if (!(cpu_ov > 0.0)) return 65536u;
+  const double v = std::nearbyint(pcie_ov / (pcie_ov + cpu_ov) * 65536.0);
+  if (v <= 0.0) return 0u;
+  if (v >= 65536.0) return 65536u;
+  return (uint32_t)v;
+}
+
+extern "C" uint32_t ft_fetch_fraction_q16(const ft_bw_profile* p) {
+  if (!p) return 0u;
+  if (p->pcie_ov > 0.0 && p->cpu_ov > 0.0) return ft_frac_q16_contended(p->pcie_ov, p->cpu_ov);
+  return ft_frac_q16(p->B_P, p->B_H);
+}
+
+// [AIN] "Why use it": hybrid only when B_H > threshold * B_P for every benched
+// workload of the format ("unanimous or offload").
+extern "C" int32_t ft_recommend_hybrid(const double* B_P, const double* B_H, int32_t n, double threshold) {
+  if (n < 0 || (n > 0 && (!B_P || !B_H)) || !(threshold > 0.0)) return FT_EINVAL;
+  if (n == 0) return 0;
+  for (int32_t i = 0; i < n; ++i)
+    if (!(B_H[i] > threshold * B_P[i])) return 0;
+  return 1;
+}

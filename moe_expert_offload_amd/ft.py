@@ -22,6 +22,7 @@ FT_ENOPIN = -4
 FT_ECAP = -5
 FT_EHIP = -6
 FT_EUNSUPPORTED = -7
+FT_ENOPROFILE = -8
 FT_WOVERLAP_OFF = 1
 FT_PLAN_CAP = 512
 FT_W_BF16 = 0
@@ -36,7 +37,14 @@ EXPORTED = [
     "ft_expert_cache_lookup", "ft_expert_cache_fill", "ft_expert_cache_resize",
     "ft_expert_cache_where", "ft_moe_decode_layer", "ft_moe_prefill_begin", "ft_moe_prefill_layer",
     "ft_moe_prefill_end", "ft_prefill_slot", "ft_profile_enable", "ft_profile_read", "ft_host_experts",
+    "ft_frac_q16_contended", "ft_fetch_fraction_q16", "ft_recommend_hybrid", "ft_bench_bw_contended",
+    "ft_bw_profile_path", "ft_bw_profile_save", "ft_bw_profile_load",
 ]
+
+
+class ft_bw_profile(C.Structure):
+    _fields_ = [("B_P", C.c_double), ("B_H", C.c_double), ("pcie_ov", C.c_double), ("cpu_ov", C.c_double),
+                ("fmt", C.c_int32)]
 
 
 class ft_shape(C.Structure):
@@ -104,6 +112,14 @@ def lib():
             "ft_record_bytes": (C.c_size_t, [C.POINTER(ft_shape)]),
             "ft_workspace_bytes": (C.c_size_t, [C.POINTER(ft_shape), I]),
             "ft_frac_q16": (C.c_uint32, [C.c_double, C.c_double]),
+            "ft_frac_q16_contended": (C.c_uint32, [C.c_double, C.c_double]),
+            "ft_fetch_fraction_q16": (C.c_uint32, [C.POINTER(ft_bw_profile)]),
+            "ft_recommend_hybrid": (I, [C.POINTER(C.c_double), C.POINTER(C.c_double), I, C.c_double]),
+            "ft_bench_bw_contended": (C.c_int, [C.POINTER(ft_shape), P, I, P, I, C.POINTER(C.c_double),
+                                                C.POINTER(C.c_double)]),
+            "ft_bw_profile_path": (C.c_int, [I, I, C.c_char_p, C.c_char_p, C.c_size_t]),
+            "ft_bw_profile_save": (C.c_int, [C.c_char_p, C.POINTER(ft_bw_profile)]),
+            "ft_bw_profile_load": (C.c_int, [C.c_char_p, I, C.POINTER(ft_bw_profile)]),
             "ft_qstar_split": (I, [I, C.c_uint32, I, I, I]),
             "ft_pool_alloc": (C.c_int, [C.c_size_t, C.POINTER(P)]),
             "ft_pool_free": (C.c_int, [P]),
@@ -197,6 +213,50 @@ def ft_workspace_bytes(shape, T_max):
 
 def ft_frac_q16(B_P, B_H):
     return lib().ft_frac_q16(float(B_P), float(B_H))
+
+
+def ft_frac_q16_contended(pcie_ov, cpu_ov):
+    return lib().ft_frac_q16_contended(float(pcie_ov), float(cpu_ov))
+
+
+def ft_fetch_fraction_q16(profile):
+    return lib().ft_fetch_fraction_q16(C.byref(profile))
+
+
+def ft_recommend_hybrid(B_P, B_H, threshold=2.0):
+    """B_P, B_H: sequences (one entry per benched workload of a format); True for hybrid."""
+    n = len(B_P)
+    arr = C.c_double * max(n, 1)
+    r = lib().ft_recommend_hybrid(arr(*B_P), arr(*B_H), n, float(threshold))
+    return bool(_check("ft_recommend_hybrid", r))
+
+
+def ft_bench_bw_contended(shape, host_pool, n_records, dev_scratch, threads=0):
+    po, co = C.c_double(), C.c_double()
+    _check("ft_bench_bw_contended", lib().ft_bench_bw_contended(C.byref(shape), _ptr(host_pool), n_records,
+                                                                _ptr(dev_scratch), threads, C.byref(po),
+                                                                C.byref(co)))
+    return po.value, co.value
+
+
+def ft_bw_profile_path(device, fmt, directory):
+    buf = C.create_string_buffer(4096)
+    _check("ft_bw_profile_path", lib().ft_bw_profile_path(device, fmt, directory.encode(), buf, 4096))
+    return buf.value.decode()
+
+
+def ft_bw_profile_save(path, profile):
+    return _check("ft_bw_profile_save", lib().ft_bw_profile_save(path.encode(), C.byref(profile)))
+
+
+def ft_bw_profile_load(path, fmt):
+    """The stored profile, or None when there is no usable one (FT_ENOPROFILE)."""
+    p = ft_bw_profile()
+    st = lib().ft_bw_profile_load(path.encode(), fmt, C.byref(p))
+    if st == FT_ENOPROFILE:
+        return None
+    _check("ft_bw_profile_load", st)
+    return p
 
 
 def ft_qstar_split(m, frac_q16, min_fill, max_fetch, avail):

@@ -156,3 +156,30 @@ def test_combine(with_cpu):
         if with_cpu:
             ref[t] += cpu[t]
     assert np.allclose(host(y), ref, rtol=1e-5, atol=1e-5)
+
+
+def test_contended_bandwidth_pair_and_profile_file(tmp_path):
+    """The contended pair at the 40-layer d=2048 shape: each rate is positive and,
+    measured while the other side runs, not above its uncontended value (10 %
+    measurement slack); the profile file keyed by this GPU's UUID round-trips and
+    gives the contended fraction."""
+    from moe_expert_offload_amd.synth import Shape
+    from tests.gpu_helpers import PinnedPool
+    torch = torch_mod()
+    s = Shape(40, 128, 2048, 768, 8)
+    pool = PinnedPool(s, 16)
+    pool.fill_device_random(2)
+    shape = ft.make_shape(s.L, s.E, s.d, s.d_ff, s.k)
+    scratch = torch.empty(8 * s.record_bytes, dtype=torch.uint8, device="cuda")
+    _say("bench_bw and bench_bw_contended, 16 records")
+    B_P, B_H = ft.ft_bench_bw(shape, pool.ptr, 8, scratch, 0)
+    po, co = ft.ft_bench_bw_contended(shape, pool.ptr, 16, scratch, 0)
+    _say(f"B_P {B_P / 1e9:.1f} B_H {B_H / 1e9:.1f} pcie_ov {po / 1e9:.1f} cpu_ov {co / 1e9:.1f} GB/s")
+    assert 0.0 < po <= 1.1 * B_P
+    assert 0.0 < co <= 1.1 * B_H
+    path = ft.ft_bw_profile_path(torch.cuda.current_device(), ft.FT_W_BF16, str(tmp_path))
+    assert path.startswith(str(tmp_path) + "/ft_bw_") and path.endswith("_bf16.txt") and len(path) > len(str(tmp_path)) + 40
+    ft.ft_bw_profile_save(path, ft.ft_bw_profile(B_P, B_H, po, co, ft.FT_W_BF16))
+    prof = ft.ft_bw_profile_load(path, ft.FT_W_BF16)
+    assert ft.ft_fetch_fraction_q16(prof) == ft.ft_frac_q16_contended(po, co)
+    assert ft.ft_bw_profile_load(path, ft.FT_W_MXFP4) is None

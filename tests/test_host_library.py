@@ -2,6 +2,7 @@
 and its host-side decisions (fetch split, cache residency, prefill buffers,
 resize) are bit-exact with the oracle.  No call here touches a GPU."""
 import ctypes as C
+import json
 import os
 import re
 
@@ -226,3 +227,54 @@ def test_host_expert_kernel_mxfp4_matches_oracle(T, d, d_ff, uses, threads):
             ref[use_t[u]] += float(use_g[u]) * mx.expert_ffn_decode(W, x64[use_t[u]:use_t[u] + 1])[0]
     ok, mxe, l1 = within_tolerance(partial, ref, 1e-4, 1e-5)
     assert ok, (mxe, l1)
+
+
+# ---- the bandwidth profile: contended fraction, hybrid gate, profile files --------
+
+def test_contended_fraction_bit_exact():
+    from oracle.qstar import fetch_fraction_q16, frac_q16_contended
+    rng = np.random.default_rng(7)
+    pairs = [(52.7, 24.6), (25.1, 38.1), (0.0, 5.0), (5.0, 0.0), (1.0, 131071.0), (3.0, 131069.0)]
+    pairs += [(float(a), float(b)) for a, b in rng.uniform(0.01, 300, size=(2000, 2))]
+    for po, co in pairs:
+        assert ft.ft_frac_q16_contended(po, co) == frac_q16_contended(po, co), (po, co)
+    for bp, bh, po, co in rng.uniform(0.0, 300, size=(500, 4)):
+        for pair in ((po, co), (0.0, co), (po, 0.0)):
+            prof = ft.ft_bw_profile(float(bp), float(bh), float(pair[0]), float(pair[1]), ft.FT_W_BF16)
+            assert ft.ft_fetch_fraction_q16(prof) == fetch_fraction_q16(bp, bh, *pair)
+
+
+def test_hybrid_recommendation_matches_oracle():
+    from oracle.qstar import recommend_hybrid
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "qstar_pages.json")))
+    t1 = [(r["B_P"], r["B_H"]) for r in gold["table1"]["rows"]]
+    rng = np.random.default_rng(8)
+    cases = [t1, t1[1:3], [t1[1], t1[2], t1[4], t1[5]], [t1[0]], [t1[3]], [], [(10.0, 20.0)], [(10.0, 20.01)]]
+    cases += [[tuple(p) for p in rng.uniform(1, 100, size=(int(rng.integers(1, 5)), 2))] for _ in range(300)]
+    for c in cases:
+        for thr in (2.0, 1.5):
+            got = ft.ft_recommend_hybrid([p for p, _ in c], [h for _, h in c], thr)
+            assert got == recommend_hybrid(c, thr), (c, thr)
+    with pytest.raises(ft.FtError):
+        ft.ft_recommend_hybrid([1.0], [3.0], 0.0)
+
+
+def test_bandwidth_profile_file_round_trip(tmp_path):
+    path = str(tmp_path / "prof_bf16.txt")
+    prof = ft.ft_bw_profile(55.1e9, 163.3e9, 50.2e9, 101.7e9, ft.FT_W_BF16)
+    ft.ft_bw_profile_save(path, prof)
+    back = ft.ft_bw_profile_load(path, ft.FT_W_BF16)
+    assert (back.B_P, back.B_H, back.pcie_ov, back.cpu_ov, back.fmt) == (55.1e9, 163.3e9, 50.2e9, 101.7e9, 0)
+    # a profile says nothing about another expert format, and a missing file is no profile
+    assert ft.ft_bw_profile_load(path, ft.FT_W_MXFP4) is None
+    assert ft.ft_bw_profile_load(str(tmp_path / "absent.txt"), ft.FT_W_BF16) is None
+    # a profile without the contended pair falls back to Eq. (4)
+    path2 = str(tmp_path / "prof_mx.txt")
+    ft.ft_bw_profile_save(path2, ft.ft_bw_profile(55.8e9, 156.0e9, 0.0, 0.0, ft.FT_W_MXFP4))
+    p2 = ft.ft_bw_profile_load(path2, ft.FT_W_MXFP4)
+    assert ft.ft_fetch_fraction_q16(p2) == ft.ft_frac_q16(55.8e9, 156.0e9)
+    # incomplete files are refused
+    (tmp_path / "bad.txt").write_text("format: bf16\nB_P: 1e9\n")
+    assert ft.ft_bw_profile_load(str(tmp_path / "bad.txt"), ft.FT_W_BF16) is None
+    with pytest.raises(ft.FtError):
+        ft.ft_bw_profile_save(path, ft.ft_bw_profile(0.0, 1.0, 0.0, 0.0, ft.FT_W_BF16))
