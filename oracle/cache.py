@@ -33,6 +33,17 @@ Readings of this build (the pages leave these open):
     B[l % 2] with expert e in B[l % 2][e]; at end, layers L-2 then L-1 are
     registered (e ascending), each touching the clock; a copy of the same key
     elsewhere is emptied; buffer slots left unregistered become empty.
+  * on-demand prefill ([FT] §3.1: the fallback when the pool cannot spare two
+    full layers, and the serial loading left when the second buffer is off):
+    per layer, after routing, U (first occurrence over the chunk's (t, j)) splits
+    into resident H and missing M; M is loaded in rounds of at most avail =
+    (slots not holding a hit) experts, each round taking victims like a decode
+    fill (victim order before the round, M order) and computing its experts
+    once their loads land; round 0 also computes H.  Touches: round 0 touches
+    H and its batch in U order, each later round its batch in order.  Hit slots
+    are never victims within the layer; a round may evict what an earlier round
+    of the same layer loaded (after that round computed).  No slot at all for a
+    miss is an error.  Decode counters are untouched.
 """
 from __future__ import annotations
 
@@ -214,6 +225,40 @@ class SlotTable:
                     self.slot_stamp[s] = -1
         self.buffers = None
 
+    def prefill_on_demand(self, layer, idx):
+        """Rounds of one on-demand prefill layer: a list of {"fill": [(e, slot)],
+        "compute": [(e, slot)]}; returns (U, H, M, rounds)."""
+        U = _first_occurrence(idx)
+        H = [e for e in U if self.key(layer, e) in self.where]
+        M = [e for e in U if self.key(layer, e) not in self.where]
+        hit_slots = {self.where[self.key(layer, e)] for e in H}
+        rounds, done, r = [], 0, 0
+        while r == 0 or done < len(M):
+            V = self._victim_order(hit_slots)
+            n = min(len(V), len(M) - done)
+            if n == 0 and done < len(M):
+                raise ValueError("on-demand prefill: no slot to load a miss into")
+            batch = M[done:done + n]
+            fills = []
+            for i, e in enumerate(batch):
+                s = V[i]
+                old = self.slot_key[s]
+                if old >= 0:
+                    del self.where[old]
+                kk = self.key(layer, e)
+                self.slot_key[s] = kk
+                self.where[kk] = s
+                fills.append((e, s))
+            touched = [e for e in U if e in set(H) | set(batch)] if r == 0 else batch
+            for e in touched:
+                self.clock += 1
+                self.slot_stamp[self.where[self.key(layer, e)]] = self.clock
+            hits = [(e, self.where[self.key(layer, e)]) for e in H] if r == 0 else []
+            rounds.append({"fill": fills, "compute": hits + fills})
+            done += n
+            r += 1
+        return U, H, M, rounds
+
     def resize(self, N_new):
         self._reset(N_new)
 
@@ -302,6 +347,44 @@ class OrderedLRU:
                 if s not in used:
                     heapq.heappush(self.free, s)
         self.buffers = None
+
+    def prefill_on_demand(self, layer, idx):
+        U = _first_occurrence(idx)
+        tag = lambda e: (layer, e)
+        H = [e for e in U if tag(e) in self.od]
+        M = [e for e in U if tag(e) not in self.od]
+        hit_tags = {tag(e) for e in H}
+        rounds, done, r = [], 0, 0
+        while r == 0 or done < len(M):
+            want = len(M) - done
+            victims = []  # (slot, evicted tag or None), in victim order before this round
+            while len(victims) < want and self.free:
+                victims.append((heapq.heappop(self.free), None))
+            if len(victims) < want:
+                for t_old, s in self.od.items():  # least recent first
+                    if t_old in hit_tags:
+                        continue
+                    victims.append((s, t_old))
+                    if len(victims) == want:
+                        break
+            if not victims and want > 0:
+                raise ValueError("on-demand prefill: no slot to load a miss into")
+            batch = M[done:done + len(victims)]
+            fills = []
+            for e, (s, t_old) in zip(batch, victims):
+                if t_old is not None:
+                    del self.od[t_old]
+                self.od[tag(e)] = s
+                fills.append((e, s))
+            in_round = set(H) | set(batch) if r == 0 else set(batch)
+            for e in (U if r == 0 else batch):
+                if e in in_round:
+                    self.od.move_to_end(tag(e))
+            hits = [(e, self.od[tag(e)]) for e in H] if r == 0 else []
+            rounds.append({"fill": fills, "compute": hits + fills})
+            done += len(batch)
+            r += 1
+        return U, H, M, rounds
 
     def resize(self, N_new):
         self.N = N_new

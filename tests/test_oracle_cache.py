@@ -145,3 +145,73 @@ def test_dedup_closed_form_uniform():
     # the page prints its own Monte Carlo estimate of the gain to 3 decimals
     assert abs(B * k / closed - g["gain_uniform"]) < 2e-3
     assert abs(B * k / mean - g["gain_uniform"]) < 4e-3
+
+
+# ---- on-demand prefill ------------------------------------------------------------
+
+def _prefill_idx(rng, T, E, k):
+    return np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+
+
+@pytest.mark.parametrize("N,T", [(5, 16), (20, 40), (31, 64), (64, 8), (100, 200), (1, 6), (33, 300)])
+def test_on_demand_prefill_simulators_agree(N, T):
+    """The two independent simulators give the same rounds and residency over decode
+    steps interleaved with on-demand prefill layers, at pools smaller and larger than
+    one layer's expert set."""
+    L, E, k = 4, 32, 4
+    rng = np.random.default_rng(N * 31 + T)
+    a, b = SlotTable(N, L, E), OrderedLRU(N, L, E)
+    tr = zipf_reuse_trace(L, E, k, 1, 6, 1.1, 0.6, rng)
+    for s in range(6):
+        for layer in range(L):
+            _same_plan(a.lookup(layer, tr[s, layer], 30000), b.lookup(layer, tr[s, layer], 30000))
+        for layer in range(L):
+            idx = _prefill_idx(rng, T, E, k)
+            ra, rb = a.prefill_on_demand(layer, idx), b.prefill_on_demand(layer, idx)
+            assert ra == rb
+            _check_invariants(a, N)
+            U, H, M, rounds = ra
+            # every routed expert is computed exactly once; hits are never evicted in the layer
+            computed = [e for rd in rounds for e, _ in rd["compute"]]
+            assert sorted(computed) == sorted(U) and len(computed) == len(set(computed))
+            hit_slots = {sl for e, sl in rounds[0]["compute"] if e in H}
+            avail = N - len(H)
+            for i, rd in enumerate(rounds):
+                slots = [sl for _, sl in rd["fill"]]
+                assert len(slots) == len(set(slots)) and not (set(slots) & hit_slots)
+                assert len(rd["fill"]) == (avail if i < len(rounds) - 1 else len(M) - avail * (len(rounds) - 1))
+            assert len(rounds) == max(1, -(-len(M) // avail)) if M else len(rounds) == 1
+    assert a.resident() == b.resident()
+
+
+def test_on_demand_prefill_special_cases():
+    L, E, k = 2, 16, 2
+    idx = np.array([[3, 1], [1, 7], [9, 3], [0, 7]])  # U = 3, 1, 7, 9, 0
+    # cold cache with room: one round, misses into the empty slots in ascending order, U order
+    a = SlotTable(40, L, E)
+    U, H, M, rounds = a.prefill_on_demand(0, idx)
+    assert U == [3, 1, 7, 9, 0] and H == [] and M == U
+    assert rounds == [{"fill": [(3, 0), (1, 1), (7, 2), (9, 3), (0, 4)],
+                       "compute": [(3, 0), (1, 1), (7, 2), (9, 3), (0, 4)]}]
+    assert [a.slot_stamp[s] for s in range(5)] == [1, 2, 3, 4, 5]
+    # the same layer again: all hits, one round, nothing loaded, touched in U order
+    U, H, M, rounds = a.prefill_on_demand(0, idx)
+    assert H == U and rounds == [{"fill": [], "compute": [(3, 0), (1, 1), (7, 2), (9, 3), (0, 4)]}]
+    assert [a.slot_stamp[s] for s in range(5)] == [6, 7, 8, 9, 10]
+    # a single slot: one expert per round, each evicting the previous; the last stays
+    b = SlotTable(1, L, E)
+    U, H, M, rounds = b.prefill_on_demand(1, idx)
+    assert [rd["fill"] for rd in rounds] == [[(3, 0)], [(1, 0)], [(7, 0)], [(9, 0)], [(0, 0)]]
+    assert b.resident() == {1 * E + 0: 0}
+    # two slots, one of them a hit of this layer: the misses cycle through the other
+    c = SlotTable(2, L, E)
+    c.prefill_on_demand(0, np.array([[5, 6]]))     # 5 -> slot 0, 6 -> slot 1
+    U, H, M, rounds = c.prefill_on_demand(0, np.array([[6, 2], [4, 6]]))
+    assert H == [6] and M == [2, 4]
+    assert rounds[0] == {"fill": [(2, 0)], "compute": [(6, 1), (2, 0)]}
+    assert rounds[1] == {"fill": [(4, 0)], "compute": [(4, 0)]}
+    # no slot for a miss: 4 holds the only slot and is a hit, 5 has nowhere to go
+    for sim in (SlotTable(1, L, E), OrderedLRU(1, L, E)):
+        sim.prefill_on_demand(0, np.array([[4, 4]]))
+        with pytest.raises(ValueError):
+            sim.prefill_on_demand(0, np.array([[4, 5]]))
