@@ -129,6 +129,22 @@ typedef struct {
   float gates[FT_PLAN_CAP];
 } ft_plan;
 
+/* The decisions of one on-demand prefill layer ([FT] §3.1: the fallback when the
+ * slot pool cannot spare two full layers, and the serial loading left when the
+ * second buffer is off).  The chunk's distinct routed experts U (first occurrence
+ * over (t, j), t-major) are computed in group order: the n_h hits (U order), then
+ * the misses in rounds of at most the slots not holding a hit, each round's
+ * misses loaded into LRU victims (victim order before the round, M order).  Round
+ * r computes groups [r ? round_end[r-1] : 0, round_end[r]); its loads are its
+ * groups at or after n_h.  Experts are < FT_E_MAX. */
+#define FT_E_MAX 1024
+typedef struct {
+  int32_t layer, n_u, n_h, n_rounds;
+  int32_t group_expert[FT_E_MAX];
+  int32_t group_slot[FT_E_MAX];
+  int32_t round_end[FT_E_MAX];
+} ft_prefill_plan;
+
 /* Per-call measurements (host clock, microseconds). */
 typedef struct {
   int32_t layer, T, n_u, hits, misses, q, n_c;
@@ -346,6 +362,13 @@ int ft_host_experts(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t f
 int ft_expert_cache_lookup(ft_ctx_t ctx, int32_t layer, const int32_t* idx_host, int32_t T,
                            ft_plan* plan);
 
+/* The decisions of one on-demand prefill layer (see ft_prefill_plan) for the
+ * chunk's routed ids idx_host [T, k], in a decisions-only context with an
+ * on-demand prefill open: updates residency and copies nothing.  FT_ECAP when a
+ * miss has no slot. */
+int ft_expert_cache_prefill_on_demand(ft_ctx_t ctx, int32_t layer, const int32_t* idx_host, int32_t T,
+                                      ft_prefill_plan* plan);
+
 /* Copies the q records of plan->F into their slots with hipMemcpyAsync on
  * `copy` (pinned host -> device; [FT] §3.2: fills proceed at the full PCIe rate).
  * Waits on wait_event first if not NULL; records done_event after if not NULL. */
@@ -382,14 +405,19 @@ int ft_moe_decode_layer(ft_ctx_t ctx, int32_t layer, const void* x, int32_t T,
                         const void* w_router, const uint8_t* allowed, float* y, void* compute,
                         ft_plan* plan, ft_step_stats* stats);
 
-/* Full-layer double-buffered prefill ([FT] §3.1; §5.3 "Pipelined prefill").
+/* Prefill ([FT] §3.1; §5.3 "Pipelined prefill"), layers in order 0..L-1.
+ * Full-layer double buffering, with overlap on and at least 2E slots:
  * begin: reserve two buffers of E slots (victim order) and start loading layer 0
- * on `copy`.  layer: (layers in order 0..L-1) start loading layer l+1 into the
- * other buffer once layer l-1's compute is done, then compute layer l (router,
- * grouping, grouped FFN, combine) from its buffer once its load landed.
- * end: the last two layers processed (L-2 and L-1 after a full pass) stay
- * resident for decode; waits for any layer prefetch still in flight.
- * FT_EUNSUPPORTED when overlap is disabled (on-demand prefill is not built).
+ * on `copy`.  layer: start loading layer l+1 into the other buffer once layer
+ * l-1's compute is done, then compute layer l (router, grouping, grouped FFN,
+ * combine) from its buffer once its load landed.  end: the last two layers
+ * processed (L-2 and L-1 after a full pass) stay resident for decode; waits for
+ * any layer prefetch still in flight.
+ * On-demand, with overlap off or fewer than 2E slots (the pages' fallback): begin
+ * reserves nothing; layer routes, brings the ids to the host, takes the decisions
+ * of ft_expert_cache_prefill_on_demand, runs the hits' FFN, then per round loads
+ * the round's misses on `copy` and runs their FFN once they landed, and combines;
+ * FT_ECAP when a miss has no slot.  end only closes the prefill.
  * In a decisions-only context begin/end change residency only (no copies). */
 int ft_moe_prefill_begin(ft_ctx_t ctx, void* copy);
 int ft_moe_prefill_layer(ft_ctx_t ctx, int32_t layer, const void* x, int32_t T,

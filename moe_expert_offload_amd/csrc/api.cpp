@@ -145,6 +145,8 @@ struct ft_ctx {
   uint16_t* h_x = nullptr;
   int32_t* h_key = nullptr;
   int32_t* h_gslot = nullptr;
+  int32_t* h_pf_idx = nullptr;  // pinned: routed ids of an on-demand prefill layer (T_max x k)
+  ft_prefill_plan pf_plan{};    // decisions of the current on-demand prefill layer
   float* h_partial = nullptr;
   uint32_t* h_flag = nullptr;  // router's publication sequence number
   uint32_t route_seq = 0;
@@ -373,7 +375,8 @@ int ft_create(const ft_shape* shape, const ft_config* config, const void* host_p
         hipHostMalloc((void**)&c->h_key, P * 4) != hipSuccess ||
         hipHostMalloc((void**)&c->h_gslot, (size_t)(c->cv.g_max + 2 * shape->E) * 4) != hipSuccess ||
         hipHostMalloc((void**)&c->h_partial, (size_t)c->t_dec * shape->d * 4) != hipSuccess ||
-        hipHostMalloc((void**)&c->h_flag, 256) != hipSuccess)
+        hipHostMalloc((void**)&c->h_flag, 256) != hipSuccess ||
+        hipHostMalloc((void**)&c->h_pf_idx, (size_t)c->cfg.T_max * shape->k * 4) != hipSuccess)
       return bail(FT_ENOMEM, "create: pinned staging allocation failed");
     hipEvent_t* evs[] = {&c->ev_route, &c->ev_done, &c->ev_pf_fill[0], &c->ev_pf_fill[1],
                          &c->ev_pf_comp[0], &c->ev_pf_comp[1]};
@@ -422,7 +425,8 @@ int ft_destroy(ft_ctx_t c) {
   }
   for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
   for (int32_t* o : c->off_free) (void)hipHostFree(o);
-  void* pins[] = {c->h_idx, c->h_gates, c->h_x, c->h_key, c->h_gslot, c->h_partial, c->h_flag, c->h_plan};
+  void* pins[] = {c->h_idx,     c->h_gates, c->h_x,    c->h_key, c->h_gslot,
+                  c->h_partial, c->h_flag,  c->h_plan, c->h_pf_idx};
   for (void* p : pins)
     if (p) (void)hipHostFree(p);
   void* devs[] = {c->dc.where, c->dc.slot_key, c->dc.slot_stamp, c->dc.clock, c->d_plan};
@@ -576,6 +580,13 @@ int ft_expert_cache_lookup(ft_ctx_t c, int32_t layer, const int32_t* idx_host, i
   c->dev_dirty = true;  // the device copy is refreshed before the next decode call
   return c->cache->lookup(layer, idx_host, T, c->shape.k, c->cfg.frac_q16, c->cfg.min_fill,
                           c->cfg.max_fetch, plan);
+}
+
+int ft_expert_cache_prefill_on_demand(ft_ctx_t c, int32_t layer, const int32_t* idx_host, int32_t T,
+                                      ft_prefill_plan* plan) {
+  if (!c || !idx_host || !plan || T < 0) return fail(FT_EINVAL, "prefill_on_demand: null argument");
+  if (c->dev) return fail(FT_EINVAL, "prefill_on_demand: a device context runs its prefill through ft_moe_prefill_layer");
+  return c->cache->prefill_on_demand(layer, idx_host, T * c->shape.k, plan);
 }
 
 int ft_expert_cache_fill(ft_ctx_t c, const ft_plan* p, void* copy, void* wait_event, void* done_event) {
@@ -806,7 +817,13 @@ static int enqueue_layer_load(ft_ctx_t c, int layer, hipStream_t ps) {
 
 int ft_moe_prefill_begin(ft_ctx_t c, void* copy) {
   if (!c) return fail(FT_EINVAL, "prefill_begin: null");
-  if (!c->overlap) return fail(FT_EUNSUPPORTED, "prefill_begin: overlap disabled; on-demand prefill is not built");
+  // [FT] §3.1: without two spare full layers (or with overlap off) prefill loads each
+  // layer's routed experts on demand
+  if (!c->overlap || c->cache->n_slots() < 2 * c->shape.E) {
+    if (int rc = c->cache->prefill_begin_on_demand()) return rc;
+    c->prefill_next = 0;
+    return FT_OK;
+  }
   if (!c->dev) return c->cache->prefill_begin();  // decisions-only context: residency only
   FT_HIP(hipSetDevice(c->device));
   if (int rc = c->cache->prefill_begin()) return rc;
@@ -824,15 +841,94 @@ int ft_moe_prefill_begin(ft_ctx_t c, void* copy) {
   return FT_OK;
 }
 
+// One on-demand prefill layer ([FT] §3.1 fallback; the decisions are
+// ExpertCache::prefill_on_demand): route, bring the ids to the host, decide, group
+// the pairs in the plan's group order, run the hits' FFN, then per round load the
+// round's misses on `copy` (after the previous round's compute, whose slots they
+// may reuse) and run their FFN once the loads landed; combine.
+static int prefill_layer_on_demand(ft_ctx_t c, int layer, const uint16_t* xs, int T, const uint16_t* w_router,
+                                   float* y, hipStream_t cs, hipStream_t ps) {
+  const int k = c->shape.k, d = c->shape.d, E = c->shape.E, d_ff = c->shape.d_ff;
+  const int P = T * k;
+  int32_t* d_idx = c->wsp<int32_t>(c->cv.idx);
+  float* d_gates = c->wsp<float>(c->cv.gates);
+  int32_t* d_key = c->wsp<int32_t>(c->cv.key);
+  int32_t* d_gslot = c->wsp<int32_t>(c->cv.gslot);
+  int32_t* d_rank = c->wsp<int32_t>(c->cv.bufslot);
+  int32_t* d_off = c->wsp<int32_t>(c->cv.offsets);
+  int32_t* d_perm = c->wsp<int32_t>(c->cv.perm);
+  int32_t* d_inv = c->wsp<int32_t>(c->cv.inv);
+  FT_HIP(hipStreamWaitEvent(cs, c->ev_done, 0));
+  if (int rc = ft::launch_router(xs, w_router, nullptr, T, d, E, k, d_idx, d_gates, c->wsp<float>(c->cv.logits), cs))
+    return rc;
+  FT_HIP(hipMemcpyAsync(c->h_pf_idx, d_idx, (size_t)P * 4, hipMemcpyDeviceToHost, cs));
+  FT_HIP(hipEventRecord(c->ev_route, cs));
+  FT_HIP(hipEventSynchronize(c->ev_route));
+  ft_prefill_plan& pl = c->pf_plan;
+  if (int rc = c->cache->prefill_on_demand(layer, c->h_pf_idx, P, &pl)) return rc;
+  // group of every routed expert, slot of every group (pinned staging; the previous
+  // layer's copies out of it finished before this layer's router ran)
+  int32_t* h_rank = c->h_gslot + c->cv.g_max;
+  for (int e = 0; e < E; ++e) h_rank[e] = -1;
+  for (int g = 0; g < pl.n_u; ++g) {
+    h_rank[pl.group_expert[g]] = g;
+    c->h_gslot[g] = pl.group_slot[g];
+  }
+  FT_HIP(hipMemcpyAsync(d_rank, h_rank, (size_t)E * 4, hipMemcpyHostToDevice, cs));
+  FT_HIP(hipMemcpyAsync(d_gslot, c->h_gslot, (size_t)pl.n_u * 4, hipMemcpyHostToDevice, cs));
+  if (int rc = ft::launch_remap(d_idx, d_rank, E, P, d_key, cs)) return rc;
+  if (int rc = ft::launch_permute(d_key, P, pl.n_u, d_off, d_perm, d_inv, c->ws + c->cv.pws, c->cv.pws_bytes, cs))
+    return rc;
+  const bool mfma = d % 256 == 0 && d_ff % 128 == 0;
+  const uint16_t* slots16 = reinterpret_cast<const uint16_t*>(c->slots);
+  auto ffn = [&](int g0, int g1) -> int {
+    if (g1 <= g0) return FT_OK;
+    if (c->mx)
+      return ft::launch_mx_ffn_mfma(xs, T, d, d_ff, k, c->slots, d_gslot, d_off, d_perm, g0, g1, P,
+                                    c->wsp<uint8_t>(c->cv.xq), c->wsp<uint8_t>(c->cv.xs), c->wsp<float>(c->cv.h),
+                                    c->wsp<uint8_t>(c->cv.hq), c->wsp<uint8_t>(c->cv.hs), c->wsp<float>(c->cv.out),
+                                    cs, nullptr);
+    if (mfma)
+      return ft::launch_ffn_mfma(xs, d, d_ff, k, slots16, d_gslot, d_off, d_perm, g0, g1, T, c->wsp<uint16_t>(c->cv.h),
+                                 c->wsp<float>(c->cv.out), cs, nullptr);
+    return ft::launch_ffn_rows(xs, d, d_ff, k, slots16, d_gslot, d_off, d_perm, g0, g1, 8, c->wsp<float>(c->cv.h),
+                               c->wsp<float>(c->cv.out), cs, nullptr);
+  };
+  // every earlier reader of a slot a round-0 load may take is before this point
+  FT_HIP(hipEventRecord(c->ev_pf_comp[0], cs));
+  if (int rc = ffn(0, pl.n_h)) return rc;
+  for (int r = 0; r < pl.n_rounds; ++r) {
+    const int g0 = std::max(r ? pl.round_end[r - 1] : 0, pl.n_h), g1 = pl.round_end[r];
+    if (g1 <= g0) continue;
+    FT_HIP(hipStreamWaitEvent(ps, c->ev_pf_comp[0], 0));
+    for (int g = g0; g < g1; ++g)
+      FT_HIP(hipMemcpyAsync(c->slot_ptr(pl.group_slot[g]), c->record(layer, pl.group_expert[g]), c->S,
+                            hipMemcpyHostToDevice, ps));
+    c->cache->stats.h2d_bytes += (int64_t)(g1 - g0) * (int64_t)c->S;
+    FT_HIP(hipEventRecord(c->ev_pf_fill[0], ps));
+    FT_HIP(hipStreamWaitEvent(cs, c->ev_pf_fill[0], 0));
+    if (int rc = ffn(g0, g1)) return rc;
+    FT_HIP(hipEventRecord(c->ev_pf_comp[0], cs));
+  }
+  if (int rc = ft::launch_combine(c->wsp<float>(c->cv.out), d_inv, d_gates, nullptr, T, k, d, y, cs)) return rc;
+  FT_HIP(hipEventRecord(c->ev_done, cs));
+  c->prefill_next = layer + 1;
+  return FT_OK;
+}
+
 int ft_moe_prefill_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, const void* w_router, float* y,
                          void* compute, void* copy) {
   if (!c || !x || !w_router || !y) return fail(FT_EINVAL, "prefill_layer: null argument");
   if (!c->cache->prefill_open()) return fail(FT_EINVAL, "prefill_layer: no open prefill");
   if (layer != c->prefill_next) return fail(FT_EINVAL, "prefill_layer: layers must come in order 0..L-1");
   if (T < 1 || T > c->cfg.T_max) return fail(FT_EINVAL, "prefill_layer: T out of range");
+  if (!c->dev) return fail(FT_EINVAL, "prefill_layer: context has no device path");
   FT_HIP(hipSetDevice(c->device));
   hipStream_t cs = static_cast<hipStream_t>(compute);
   hipStream_t ps = static_cast<hipStream_t>(copy);
+  if (c->cache->prefill_on_demand_mode())
+    return prefill_layer_on_demand(c, layer, static_cast<const uint16_t*>(x), T,
+                                   static_cast<const uint16_t*>(w_router), y, cs, ps);
   const int k = c->shape.k, d = c->shape.d, E = c->shape.E, d_ff = c->shape.d_ff;
   const int b = layer & 1;
   // stream layer l+1 into the other buffer once layer l-1 (its last reader) is done

@@ -26,6 +26,7 @@ void ExpertCache::resize(int n_slots) {
   buf_[0].clear();
   buf_[1].clear();
   prefill_open_ = false;
+  on_demand_ = false;
   const int64_t resizes = stats.resizes;
   stats = ft_stats{};
   stats.resizes = resizes;
@@ -176,13 +177,84 @@ int ExpertCache::prefill_begin() {
   return FT_OK;
 }
 
+int ExpertCache::prefill_begin_on_demand() {
+  if (prefill_open_) return fail(FT_EBUSY, "prefill already open");
+  prefill_open_ = true;
+  on_demand_ = true;
+  return FT_OK;
+}
+
+int ExpertCache::prefill_on_demand(int layer, const int32_t* idx, int P, ft_prefill_plan* p) {
+  if (!prefill_open_ || !on_demand_) return fail(FT_EINVAL, "prefill_on_demand: no open on-demand prefill");
+  if (layer < 0 || layer >= L_ || P < 0 || !p || E_ > FT_E_MAX)
+    return fail(FT_EINVAL, "prefill_on_demand: bad layer, pair count or plan");
+  for (int i = 0; i < P; ++i)
+    if (idx[i] < 0 || idx[i] >= E_) return fail(FT_EINVAL, "prefill_on_demand: routed id out of range");
+  // U in first-occurrence order, then H and M in U order
+  std::vector<uint8_t> seen(E_, 0);
+  std::vector<int32_t> U, H, M;
+  for (int i = 0; i < P; ++i)
+    if (!seen[idx[i]]) {
+      seen[idx[i]] = 1;
+      U.push_back(idx[i]);
+    }
+  const size_t base = (size_t)layer * E_;
+  for (int32_t e : U) (where_[base + e] >= 0 ? H : M).push_back(e);
+  std::vector<uint8_t> excluded(n_, 0), in_round(E_, 0);
+  for (int32_t e : H) excluded[where_[base + e]] = 1;
+  p->layer = layer;
+  p->n_u = (int32_t)U.size();
+  p->n_h = (int32_t)H.size();
+  p->n_rounds = 0;
+  int g = 0;
+  for (int32_t e : H) {
+    p->group_expert[g] = e;
+    p->group_slot[g++] = where_[base + e];
+  }
+  std::vector<int32_t> victims;
+  size_t done = 0;
+  for (int r = 0; r == 0 || done < M.size(); ++r) {
+    const size_t want = M.size() - done;
+    select_victims((int)want, excluded, &victims);
+    if (victims.empty() && want > 0) return fail(FT_ECAP, "prefill_on_demand: no slot to load a miss into");
+    const size_t n = victims.size();
+    for (size_t i = 0; i < n; ++i) {
+      const int s = victims[i];
+      const int32_t e = M[done + i];
+      if (slot_key_[s] >= 0) where_[slot_key_[s]] = -1;
+      slot_key_[s] = (int32_t)(base + e);
+      where_[base + e] = s;
+      p->group_expert[g] = e;
+      p->group_slot[g++] = s;
+    }
+    // touches: round 0 its hits and loads in U order, later rounds their loads in order
+    if (r == 0) {
+      for (int32_t e : H) in_round[e] = 1;
+      for (size_t i = 0; i < n; ++i) in_round[M[done + i]] = 1;
+      for (int32_t e : U)
+        if (in_round[e]) slot_stamp_[where_[base + e]] = ++clock_;
+    } else {
+      for (size_t i = 0; i < n; ++i) slot_stamp_[where_[base + M[done + i]]] = ++clock_;
+    }
+    p->round_end[p->n_rounds++] = g;
+    done += n;
+  }
+  stats.prefill_layers += 1;
+  return FT_OK;
+}
+
 int32_t ExpertCache::prefill_slot(int layer, int e) const {
-  if (!prefill_open_ || layer < 0 || e < 0 || e >= E_) return -1;
+  if (!prefill_open_ || on_demand_ || layer < 0 || e < 0 || e >= E_) return -1;
   return buf_[layer & 1][e];
 }
 
 void ExpertCache::prefill_end(int L) {
   if (!prefill_open_) return;
+  if (on_demand_) {  // residency was updated layer by layer
+    prefill_open_ = false;
+    on_demand_ = false;
+    return;
+  }
   std::vector<uint8_t> used(n_, 0);
   for (int layer = L - 2; layer <= L - 1; ++layer) {
     if (layer < 0) continue;

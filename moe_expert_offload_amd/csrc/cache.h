@@ -7,7 +7,9 @@
 //         demanded entry; the m misses split into F (filled) and C (host).
 //   §4.1  per layer: dedup, classify, derive q, select the K least recently used
 //         victims in one pass and consume the first q, rewrite ids to slots or -1.
-//   §3.1  two full-layer prefill buffers are taken from the same slot pool.
+//   §3.1  two full-layer prefill buffers are taken from the same slot pool; when
+//         the pool cannot spare them (or overlap is off) prefill loads the routed
+//         experts of each layer on demand.
 //   §3.3  rebuild for a new budget at a safe point.
 #pragma once
 
@@ -31,6 +33,13 @@ class ExpertCache {
 
   // Prefill buffers: reserves 2E slots (victim order), returns FT_OK or FT_ECAP.
   int prefill_begin();
+  // On-demand prefill: opens a prefill with no buffers; each layer then calls
+  // prefill_on_demand with the chunk's routed ids (T x k).  Its misses are loaded in
+  // rounds of at most the slots not holding a hit, LRU victims per round (round 0
+  // also computes the hits).  FT_ECAP when a miss has no slot at all.
+  int prefill_begin_on_demand();
+  int prefill_on_demand(int layer, const int32_t* idx, int P, ft_prefill_plan* plan);
+  bool prefill_on_demand_mode() const { return prefill_open_ && on_demand_; }
   int32_t prefill_slot(int layer, int e) const;
   const std::vector<int32_t>& prefill_buffer(int b) const { return buf_[b]; }
   bool prefill_open() const { return prefill_open_; }
@@ -59,6 +68,7 @@ class ExpertCache {
   std::vector<int32_t> where_;       // [L*E] slot or -1
   std::vector<int32_t> buf_[2];
   bool prefill_open_ = false;
+  bool on_demand_ = false;
 };
 
 }  // namespace ft

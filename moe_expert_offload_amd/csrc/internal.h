@@ -73,6 +73,9 @@ struct DecideArgs {
 // decisions of the call on the device (dedup, classify, split, victims, slot
 // rewrite, stamps) and the grouping of the pairs, updates the device state and
 // publishes the plan before the flag.
+// key[i] = map[idx[i]] (-1 for ids outside [0, n_map)).
+int launch_remap(const int32_t* idx, const int32_t* map, int n_map, int P, int32_t* key, void* stream);
+
 // Decode fills read by the GPU from the pinned pool over PCIe: records M[0:q] of a
 // layer (layer_base = its expert 0, S bytes each) into slots F_slot[0:q] of the
 // device plan; stream-ordered after the router that wrote the plan.

@@ -583,6 +583,16 @@ __device__ void decide_block(const DecideArgs& a, const int32_t* s_id, int P, co
   }
 }
 
+// key[i] = map[idx[i]]: the group of each routed pair from a per-expert table.
+__global__ __launch_bounds__(256) void remap_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ map,
+                                                    int n_map, int P, int32_t* __restrict__ key) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < P) {
+    const int e = idx[i];
+    key[i] = (e >= 0 && e < n_map) ? map[e] : -1;
+  }
+}
+
 // ---- decode fills over PCIe ([FT] §3.2, the F set) ----------------------------------
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -1257,6 +1267,13 @@ int launch_router(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, 
   if (int rc = launched("router_logits")) return rc;
   router_topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits_ws, allowed, T, E, k, idx, gates);
   return launched("router_topk");
+}
+
+int launch_remap(const int32_t* idx, const int32_t* map, int n_map, int P, int32_t* key, void* stream) {
+  if (P < 0 || n_map < 1 || !idx || !map || !key) return fail(FT_EINVAL, "remap: bad argument");
+  if (P == 0) return FT_OK;
+  remap_kernel<<<(P + 255) / 256, 256, 0, static_cast<hipStream_t>(stream)>>>(idx, map, n_map, P, key);
+  return launched("remap");
 }
 
 int launch_fill(const uint8_t* layer_base, size_t S, int E, uint8_t* slots, int n_slots, const DevPlan* plan,

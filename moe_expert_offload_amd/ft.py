@@ -38,8 +38,17 @@ EXPORTED = [
     "ft_expert_cache_where", "ft_moe_decode_layer", "ft_moe_prefill_begin", "ft_moe_prefill_layer",
     "ft_moe_prefill_end", "ft_prefill_slot", "ft_profile_enable", "ft_profile_read", "ft_host_experts",
     "ft_frac_q16_contended", "ft_fetch_fraction_q16", "ft_recommend_hybrid", "ft_bench_bw_contended",
-    "ft_bw_profile_path", "ft_bw_profile_save", "ft_bw_profile_load",
+    "ft_bw_profile_path", "ft_bw_profile_save", "ft_bw_profile_load", "ft_expert_cache_prefill_on_demand",
 ]
+
+
+FT_E_MAX = 1024
+
+
+class ft_prefill_plan(C.Structure):
+    _fields_ = [("layer", C.c_int32), ("n_u", C.c_int32), ("n_h", C.c_int32), ("n_rounds", C.c_int32),
+                ("group_expert", C.c_int32 * FT_E_MAX), ("group_slot", C.c_int32 * FT_E_MAX),
+                ("round_end", C.c_int32 * FT_E_MAX)]
 
 
 class ft_bw_profile(C.Structure):
@@ -118,6 +127,7 @@ def lib():
             "ft_bench_bw_contended": (C.c_int, [C.POINTER(ft_shape), P, I, P, I, C.POINTER(C.c_double),
                                                 C.POINTER(C.c_double)]),
             "ft_bw_profile_path": (C.c_int, [I, I, C.c_char_p, C.c_char_p, C.c_size_t]),
+            "ft_expert_cache_prefill_on_demand": (C.c_int, [P, I, P, I, C.POINTER(ft_prefill_plan)]),
             "ft_bw_profile_save": (C.c_int, [C.c_char_p, C.POINTER(ft_bw_profile)]),
             "ft_bw_profile_load": (C.c_int, [C.c_char_p, I, C.POINTER(ft_bw_profile)]),
             "ft_qstar_split": (I, [I, C.c_uint32, I, I, I]),
@@ -355,6 +365,22 @@ def ft_host_experts(x, T, d, d_ff, records, use_off, use_t, use_g, n_exp, thread
     recs = (P * max(n_exp, 1))(*[_ptr(r) for r in records])
     return _check("ft_host_experts", lib().ft_host_experts(_ptr(x), T, d, d_ff, fmt, recs, _ptr(use_off),
                                                            _ptr(use_t), _ptr(use_g), n_exp, threads, _ptr(partial)))
+
+
+def ft_expert_cache_prefill_on_demand(ctx, layer, idx_host, T):
+    """Decisions of one on-demand prefill layer: (U_groups, n_h, rounds) with rounds a list of
+    {"fill": [(e, slot)], "compute": [(e, slot)]} in the plan's group order."""
+    p = ft_prefill_plan()
+    _check("ft_expert_cache_prefill_on_demand", lib().ft_expert_cache_prefill_on_demand(
+        ctx, layer, _ptr(idx_host), T, C.byref(p)))
+    groups = [(p.group_expert[g], p.group_slot[g]) for g in range(p.n_u)]
+    rounds, g0 = [], 0
+    for r in range(p.n_rounds):
+        g1 = p.round_end[r]
+        rounds.append({"fill": [gs for i, gs in enumerate(groups[g0:g1], g0) if i >= p.n_h],
+                       "compute": groups[g0:g1]})
+        g0 = g1
+    return groups, p.n_h, rounds
 
 
 def ft_expert_cache_lookup(ctx, layer, idx_host, T, plan=None):

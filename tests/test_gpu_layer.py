@@ -173,6 +173,59 @@ def test_prefill_double_buffer_then_decode(T):
         pool.free()
 
 
+@pytest.mark.parametrize("N", [5, 20, 40])
+def test_prefill_on_demand_then_decode(N):
+    """On-demand prefill (overlap off; below 2E slots it is the only prefill): every
+    layer's output within tolerance, the residency after it equal to the oracle's
+    rounds (5 slots: several rounds per layer; 20: one full layer at a time; 40:
+    the serial form of the double buffer), then decode from that state."""
+    torch = torch_mod()
+    T = 200
+    _say("prefill on demand", N)
+    s = PF.shape
+    pool, wr = _stack(PF)
+    eng = Engine(s, pool, N, T_max=T, frac_q16=40000, prefill_overlap=0, cpu_threads=4)
+    try:
+        ref_cache = SlotTable(N, s.L, s.E)
+        wr_dev = [dev_u16(w) for w in wr]
+        plan = ft.ft_plan()
+        tr = zipf_reuse_trace(s.L, s.E, s.k, 2, 4, 1.1, 0.6, generator(13, N))
+
+        def decode_steps(steps):
+            for step in steps:
+                for l in range(s.L):
+                    x = tokens(PF, 300 + step, l, T=2)
+                    allowed = allowed_mask(tr[step, l], s.E)
+                    y = torch.empty((2, s.d), dtype=torch.float32, device="cuda")
+                    ft.ft_moe_decode_layer(eng.ctx, l, dev_u16(x), 2, wr_dev[l], dev(allowed), y, plan=plan)
+                    torch.cuda.synchronize()
+                    ref = decode_layer(ref_cache, l, x, wr[l], s.k, lambda e: pool.view[l * s.E + e],
+                                       s.d, s.d_ff, 40000, 1, -1, allowed)
+                    _compare_plan(plan, ref["plan"], ref["idx"])
+                    assert within_tolerance(host(y), ref["y"])[0]
+
+        decode_steps(range(2))
+        ft.ft_moe_prefill_begin(eng.ctx, eng.copy)
+        assert ft.ft_prefill_slot(eng.ctx, 0, 0) == -1
+        for l in range(s.L):
+            x = tokens(PF, 0, l, T=T)
+            y = torch.empty((T, s.d), dtype=torch.float32, device="cuda")
+            ft.ft_moe_prefill_layer(eng.ctx, l, dev_u16(x), T, wr_dev[l], y, copy=eng.copy)
+            torch.cuda.synchronize()
+            ref = prefill_layer(x, wr[l], s.k, lambda e: pool.view[l * s.E + e], s.d, s.d_ff)
+            ref_cache.prefill_on_demand(l, ref["idx"])
+            ok, mx, l1 = within_tolerance(host(y), ref["y"])
+            assert ok, (l, mx, l1)
+        ft.ft_moe_prefill_end(eng.ctx)
+        for l in range(s.L):
+            for e in range(s.E):
+                assert ft.ft_expert_cache_where(eng.ctx, l, e) == ref_cache.where.get(l * s.E + e, -1)
+        decode_steps(range(2, 4))
+    finally:
+        eng.destroy()
+        pool.free()
+
+
 def test_resize_at_safe_point_keeps_outputs():
     torch = torch_mod()
     s = SMALL.shape

@@ -233,6 +233,21 @@ def test_mx_prefill_double_buffer_then_resize(T):
                                    30000, 1, -1, allowed, fmt="mxfp4")
                 _compare_plan(plan, ref["plan"], ref["idx"], (step, l))
                 assert within_tolerance(host(y), ref["y"])[0], (step, l)
+        # with 20 < 2E slots the next prefill loads each layer's routed experts on demand
+        ft.ft_moe_prefill_begin(eng.ctx, eng.copy)
+        for l in range(s.L):
+            x = tokens(MXS, 7, l, T=T)
+            y = torch.empty((T, s.d), dtype=torch.float32, device="cuda")
+            ft.ft_moe_prefill_layer(eng.ctx, l, dev_u16(x), T, wr_dev[l], y, copy=eng.copy)
+            torch.cuda.synchronize()
+            ref = prefill_layer(x, wr[l], s.k, lambda e: pool.view[l * s.E + e], s.d, s.d_ff, fmt="mxfp4")
+            ref_cache.prefill_on_demand(l, ref["idx"])
+            ok, mxe, l1 = within_tolerance(host(y), ref["y"])
+            assert ok, ("on demand", l, mxe, l1)
+        ft.ft_moe_prefill_end(eng.ctx)
+        for l in range(s.L):
+            for e in range(s.E):
+                assert ft.ft_expert_cache_where(eng.ctx, l, e) == ref_cache.where.get(l * s.E + e, -1)
     finally:
         eng.destroy()
         pool.free()

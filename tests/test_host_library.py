@@ -128,12 +128,55 @@ def test_prefill_residency_and_resize_match_oracle():
                 idx = np.ascontiguousarray(tr[s, layer].astype(np.int32))
                 ft.ft_expert_cache_lookup(ctx, layer, idx, B, plan)
                 _compare(plan, ref.lookup(layer, idx, 40000))
-        # shrinking below 2E disables the prefill overlap with a warning code
+        # shrinking below 2E disables the prefill overlap with a warning code; prefill then
+        # falls back to on-demand loading
         assert ft.ft_expert_cache_resize(ctx, None, 2 * E - 1) == ft.FT_WOVERLAP_OFF
+        ref.resize(2 * E - 1)
         assert ft.ft_get_config(ctx).prefill_overlap == 0
-        with pytest.raises(ft.FtError) as ei:
-            ft.ft_moe_prefill_begin(ctx, 0)
-        assert ei.value.status == ft.FT_EUNSUPPORTED
+        ft.ft_moe_prefill_begin(ctx, 0)
+        assert ft.ft_prefill_slot(ctx, 0, 0) == -1
+        for layer in range(L):
+            idx = np.ascontiguousarray(np.stack([rng.choice(E, size=k, replace=False) for _ in range(20)]).astype(np.int32))
+            groups, n_h, rounds = ft.ft_expert_cache_prefill_on_demand(ctx, layer, idx, 20)
+            U, H, M, ref_rounds = ref.prefill_on_demand(layer, idx)
+            assert rounds == ref_rounds and n_h == len(H) and [e for e, _ in groups] == H + M
+        ft.ft_moe_prefill_end(ctx)
+        for layer in range(L):
+            for e in range(E):
+                assert ft.ft_expert_cache_where(ctx, layer, e) == ref.where.get(layer * E + e, -1)
+    finally:
+        ft.ft_destroy(ctx)
+
+
+@pytest.mark.parametrize("N,T", [(5, 16), (12, 40), (40, 64), (1, 4), (33, 200)])
+def test_on_demand_prefill_decisions_bit_exact(N, T):
+    """The C++ controller's on-demand prefill rounds and residency against the oracle,
+    interleaved with decode lookups, over pools smaller than one layer's experts and
+    larger than two."""
+    L, E, k = 4, 16, 3
+    rng = np.random.default_rng(N * 13 + T)
+    tr = zipf_reuse_trace(L, E, k, 1, 8, 1.1, 0.6, rng)
+    ctx = _ctx(L, E, 64, 200, k, N, 40000, overlap=0)
+    try:
+        ref = SlotTable(N, L, E)
+        plan = ft.ft_plan()
+        for s in range(8):
+            for layer in range(L):
+                idx = np.ascontiguousarray(tr[s, layer].astype(np.int32))
+                ft.ft_expert_cache_lookup(ctx, layer, idx, 1, plan)
+                _compare(plan, ref.lookup(layer, idx, 40000))
+            if s % 3 == 1:
+                ft.ft_moe_prefill_begin(ctx, 0)
+                for layer in range(L):
+                    idx = np.ascontiguousarray(
+                        np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32))
+                    groups, n_h, rounds = ft.ft_expert_cache_prefill_on_demand(ctx, layer, idx, T)
+                    U, H, M, ref_rounds = ref.prefill_on_demand(layer, idx)
+                    assert rounds == ref_rounds and n_h == len(H)
+                ft.ft_moe_prefill_end(ctx)
+        for layer in range(L):
+            for e in range(E):
+                assert ft.ft_expert_cache_where(ctx, layer, e) == ref.where.get(layer * E + e, -1)
     finally:
         ft.ft_destroy(ctx)
 
