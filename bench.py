@@ -266,6 +266,24 @@ def run_prefill(args, torch, ft, synth, HostPool):
             ft.ft_profile_enable(ctx, False)
         finally:
             ft.ft_destroy(ctx)
+        el_off = None
+        if args.prefill_ablation:
+            # the second buffer disabled: each layer's routed experts load on demand after
+            # its routing, serialised against its compute
+            cfg_off = ft.make_config(frac_q16=0, min_fill=0, max_fetch=0, cpu_threads=2, prefill_overlap=0, T_max=T,
+                                     L_phys=L_phys)
+            ctx = ft.ft_create(fshape, cfg_off, pool.ptr, pool.nbytes, slots, N, ws, wsb)
+            try:
+                log("prefill with overlap off (on-demand loading)")
+                t2 = time.perf_counter()
+                ft.ft_moe_prefill_begin(ctx, copy)
+                for l in range(s.L):
+                    ft.ft_moe_prefill_layer(ctx, l, xs[l], T, wr[l], y, compute, copy)
+                ft.ft_moe_prefill_end(ctx)
+                torch.cuda.synchronize()
+                el_off = time.perf_counter() - t2
+            finally:
+                ft.ft_destroy(ctx)
     finally:
         pool.free()
     el = t1 - t0
@@ -282,6 +300,10 @@ def run_prefill(args, torch, ft, synth, HostPool):
                      "GBs": round(by / (ms * 1e-3) / 1e9, 1) if ms > 0 else 0.0,
                      "gateup_ms_per_layer": prof["ms_gateup"] / max(prof["launches"], 1),
                      "down_ms_per_layer": prof["ms_down"] / max(prof["launches"], 1)},
+        "overlap_off": None if el_off is None else {
+            "tok_s": T / el_off, "s_per_chunk": el_off,
+            "throughput_loss_pct": round(100.0 * (1.0 - el / el_off), 2),
+            "note": "second buffer disabled: on-demand loading after each layer's routing"},
     }
 
 
@@ -458,6 +480,8 @@ def main():
     ap.add_argument("--prefill", dest="prefill", action="store_true", default=True)
     ap.add_argument("--no-prefill", dest="prefill", action="store_false")
     ap.add_argument("--prefill-l-phys", type=int, default=2)
+    ap.add_argument("--no-prefill-ablation", dest="prefill_ablation", action="store_false", default=True,
+                    help="skip the overlap-off prefill pass")
     ap.add_argument("--mxfp4", dest="mxfp4", action="store_true", default=True)
     ap.add_argument("--no-mxfp4", dest="mxfp4", action="store_false")
     ap.add_argument("--mx-l-phys", type=int, default=16,
