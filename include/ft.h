@@ -250,8 +250,9 @@ int ft_bw_profile_load(const char* path, int32_t fmt, ft_bw_profile* profile);
  * device memory, as the decode fills move them, `n_records` of them, one launch
  * each, on a fresh stream) and B_H (the host expert kernel over the same records at one
  * token, `threads` workers; 0 = all) in bytes per second ([FT] §3.2, Table 1:
- * both measured on the deployed tensor shapes).  dev_scratch must hold
- * n_records records. */
+ * both measured on the deployed tensor shapes).  Each is the fastest of several
+ * passes after a warm-up pass (B_H: passes over at least 100 ms).  dev_scratch
+ * must hold n_records records. */
 int ft_bench_bw(const ft_shape* shape, const void* host_pool, int32_t n_records,
                 void* dev_scratch, int32_t threads, double* B_P, double* B_H);
 
