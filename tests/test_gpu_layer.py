@@ -55,19 +55,34 @@ SMALL = Workload("small-decode", 11, Shape(4, 32, 256, 512, 4), 2, 0.3)
     (Q16, 1, -1, 4, 128),     # capacity = all pairs: only compulsory misses
 ])
 def test_decode_trace_parity(fq, min_fill, max_fetch, T, N):
+    _decode_trace(SMALL, fq, min_fill, max_fetch, T, N)
+
+
+# d = 200 and d_ff = 328: rows whose length is not a multiple of the 512 elements a
+# wavefront reads per load; calls of 1 to 9 tokens (row-streaming kernels with 1, 8
+# and 2 x 8 tokens per pass)
+RAGGED = Workload("ragged-decode", 13, Shape(3, 12, 200, 328, 3), 2, 0.5)
+
+
+@pytest.mark.parametrize("T", [1, 5, 8, 9])
+def test_decode_ragged_shape_parity(T):
+    _decode_trace(RAGGED, 20000, 1, -1, T, 14)
+
+
+def _decode_trace(wl, fq, min_fill, max_fetch, T, N):
     torch = torch_mod()
-    _say("decode", fq, min_fill, max_fetch, T, N)
-    s = SMALL.shape
-    pool, wr = _stack(SMALL)
-    eng = Engine(s, pool, N, T_max=8, frac_q16=fq, min_fill=min_fill, max_fetch=max_fetch, cpu_threads=4)
+    _say("decode", wl.name, fq, min_fill, max_fetch, T, N)
+    s = wl.shape
+    pool, wr = _stack(wl)
+    eng = Engine(s, pool, N, T_max=max(T, 8), frac_q16=fq, min_fill=min_fill, max_fetch=max_fetch, cpu_threads=4)
     try:
         ref_cache = SlotTable(N, s.L, s.E)
-        tr = zipf_reuse_trace(s.L, s.E, s.k, T, 6, 1.1, 0.6, generator(11, 3, T))
+        tr = zipf_reuse_trace(s.L, s.E, s.k, T, 6, 1.1, 0.6, generator(wl.seed_key, 3, T))
         wr_dev = [dev_u16(w) for w in wr]
         plan = ft.ft_plan()
         for step in range(tr.shape[0]):
             for l in range(s.L):
-                x = tokens(SMALL, step, l, T=T)
+                x = tokens(wl, step, l, T=T)
                 allowed = allowed_mask(tr[step, l], s.E)
                 y = torch.empty((T, s.d), dtype=torch.float32, device="cuda")
                 ft.ft_moe_decode_layer(eng.ctx, l, dev_u16(x), T, wr_dev[l], dev(allowed), y,
