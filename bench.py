@@ -464,6 +464,52 @@ def cpu_baseline(args, pool, wl, tr, fq, L_phys, budget_s):
                       f"(fp64 NumPy oracle: router, cache decisions, exact layer output), {el:.1f} s"}
 
 
+PAGES_FIG4B = {  # [FT] §5.3 "Expert locality": decode-read miss rates at the RTX 5090 serving capacity
+    "37%": {"lru": 0.16, "hotset": 0.41, "static": 0.62, "model": "Qwen3.6-35B-A3B traces"},
+    "11%": {"lru": 0.39, "hotset": 0.59, "static": 0.89, "model": "DeepSeek-V4-Flash traces"},
+}
+
+
+def run_placement(args, ft, synth):
+    """Fig. 4b replay on synthetic traces (host only): decode-read miss rate of the
+    engine's global LRU, a prefill-chosen hot set and a routing-blind static split,
+    per cache capacity, for the 40-layer and 43-layer shapes; and the batch-dedup
+    study (distinct experts per layer and step against batch size)."""
+    out = {"requests": args.replay_requests, "prompt": args.replay_prompt, "decode": args.replay_decode,
+           "trace": "Zipf(1.1) popularity per layer, 0.6 token-to-token reuse, one stream per request",
+           "pages_fig4b": PAGES_FIG4B, "shapes": {}}
+    pols = {"lru": ft.FT_PLACE_LRU, "hotset": ft.FT_PLACE_HOTSET, "static": ft.FT_PLACE_STATIC}
+    t0 = time.perf_counter()
+    for name in ("decode-L40-d2048-E128-top8", "decode-L43-d4096-E256-top6"):
+        wl = synth.WORKLOADS[name]
+        s = wl.shape
+        steps = args.replay_prompt + args.replay_decode
+        tr = synth.zipf_reuse_trace(s.L, s.E, s.k, args.replay_requests, steps, wl.zipf_alpha, wl.reuse,
+                                    synth.generator(wl.seed_key, synth.STREAM_TRACE, 1, seed=args.seed))
+        ids = np.ascontiguousarray(np.transpose(tr, (2, 0, 1, 3)).astype(np.int32))
+        fshape = ft.make_shape(s.L, s.E, s.d, s.d_ff, s.k)
+        rows = {}
+        for cap in (0.05, 0.11, 0.20, 0.37, 0.60, 1.00):
+            N = int(cap * s.L * s.E)
+            row = {"n_slots": N}
+            for pname, pol in pols.items():
+                reads, misses = ft.ft_replay_placement(pol, fshape, N, ids, args.replay_prompt)
+                row[pname] = round(misses / max(reads, 1), 4)
+            rows[f"{round(cap * 100)}%"] = row
+        # batch dedup: distinct experts per (step, layer) for B concurrent streams
+        dedup = {}
+        for B in (1, 4, 8):
+            tb = synth.zipf_reuse_trace(s.L, s.E, s.k, B, 64, wl.zipf_alpha, wl.reuse,
+                                        synth.generator(wl.seed_key, synth.STREAM_TRACE, 2, B, seed=args.seed))
+            uniq = np.mean([len(np.unique(tb[st, l])) for st in range(tb.shape[0]) for l in range(s.L)])
+            uni = s.E * (1.0 - (1.0 - s.k / s.E) ** B)
+            dedup[f"B={B}"] = {"distinct_zipf": round(float(uniq), 3), "gain_zipf": round(B * s.k / uniq, 4),
+                               "distinct_uniform_closed_form": round(uni, 3), "gain_uniform": round(B * s.k / uni, 4)}
+        out["shapes"][name] = {"L": s.L, "E": s.E, "k": s.k, "miss_rate_by_capacity": rows, "batch_dedup": dedup}
+    out["seconds"] = round(time.perf_counter() - t0, 2)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,6 +533,11 @@ def main():
     ap.add_argument("--mx-l-phys", type=int, default=16,
                     help="physical layers of the MXFP4 pool (0 = all; pinned memory is capped near half of host RAM)")
     ap.add_argument("--mx-steps", type=int, default=512)
+    ap.add_argument("--no-replay", dest="replay", action="store_false", default=True,
+                    help="skip the Fig. 4b placement replay (host only)")
+    ap.add_argument("--replay-requests", type=int, default=4)
+    ap.add_argument("--replay-prompt", type=int, default=512)
+    ap.add_argument("--replay-decode", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     args = ap.parse_args()
@@ -513,6 +564,7 @@ def main():
         pool.free()
     pre = run_prefill(args, torch, ft, synth, HostPool) if args.prefill else None
     mxr = run_mxfp4(args, torch, ft, synth, HostPool) if args.mxfp4 else None
+    rep = run_placement(args, ft, synth) if args.replay else None
     out = {
         "metric": METRIC, "value": round(dec["tok_s"], 3), "unit": "tok/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dec["ms_per_step"], 4),
@@ -521,6 +573,7 @@ def main():
         "config": {"workload": dec["workload"], "global_batch": dec["T"], "layers": dec["L"],
                    "cache_slots": dec["n_slots"], "parallelism": "single-gpu"},
         "roofline": roof, "cpu_baseline": cpu, "decode": dec, "prefill": pre, "mxfp4": mxr,
+        "placement_replay": rep,
     }
     print(json.dumps(out), flush=True)
 

@@ -447,6 +447,33 @@ typedef struct {
 int ft_profile_enable(ft_ctx_t ctx, int32_t on);
 int ft_profile_read(ft_ctx_t ctx, ft_profile* out);
 
+/* ---- placement replay ([FT] §5.3 "Expert locality", Fig. 4b) ---------------------
+ * Replays a routing trace against one placement policy at a cache of n_slots
+ * (layer, expert) pairs and counts the decode-time expert reads and how many of
+ * them miss the GPU.  Host only; touches no device.
+ *   ids int32 [n_requests][prompt + decode][L][k], expert ids in [0, E): requests
+ *   served one after another at batch 1, `prompt` prefill tokens then `decode`
+ *   decode steps each; only the decode steps are counted (k reads per step and
+ *   layer).
+ * Policies:
+ *   FT_PLACE_LRU     the engine's global LRU (the controller ft_moe_decode_layer
+ *                    uses) with every miss filled (q = m); each prefill is the
+ *                    engine's: two full-layer buffers when n_slots >= 2E (the last
+ *                    two layers stay), else on-demand loading of each layer's routed
+ *                    experts (FT_ECAP when a miss finds no slot).  The cache
+ *                    persists across requests.
+ *   FT_PLACE_HOTSET  after each prefill the resident set becomes the n_slots pairs
+ *                    that prefill routed most often (ties to the lower l*E + e, pairs
+ *                    never routed fill the rest in that order); fixed during decode.
+ *   FT_PLACE_STATIC  routing-blind: the last n_slots pairs in l*E + e order.
+ * E <= FT_E_MAX, 1 <= k <= min(8, E).  FT_EINVAL for bad arguments or ids. */
+#define FT_PLACE_LRU 0
+#define FT_PLACE_HOTSET 1
+#define FT_PLACE_STATIC 2
+int ft_replay_placement(int32_t policy, const ft_shape* shape, int32_t n_slots, const int32_t* ids,
+                        int32_t n_requests, int32_t prompt, int32_t decode, int64_t* reads,
+                        int64_t* misses);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,6 +37,7 @@ SOURCES = [
     ("qstar.cpp", CXX, HOST_FLAGS),
     ("bwprofile.cpp", CXX, HOST_FLAGS),
     ("cpu_exec.cpp", CXX, HOST_FLAGS),
+    ("placement.cpp", CXX, HOST_FLAGS),
 ]
 
 

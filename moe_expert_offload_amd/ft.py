@@ -27,6 +27,9 @@ FT_WOVERLAP_OFF = 1
 FT_PLAN_CAP = 512
 FT_W_BF16 = 0
 FT_W_MXFP4 = 1
+FT_PLACE_LRU = 0
+FT_PLACE_HOTSET = 1
+FT_PLACE_STATIC = 2
 
 EXPORTED = [
     "ft_strerror", "ft_last_error", "ft_record_bytes", "ft_workspace_bytes", "ft_frac_q16",
@@ -39,6 +42,7 @@ EXPORTED = [
     "ft_moe_prefill_end", "ft_prefill_slot", "ft_profile_enable", "ft_profile_read", "ft_host_experts",
     "ft_frac_q16_contended", "ft_fetch_fraction_q16", "ft_recommend_hybrid", "ft_bench_bw_contended",
     "ft_bw_profile_path", "ft_bw_profile_save", "ft_bw_profile_load", "ft_expert_cache_prefill_on_demand",
+    "ft_replay_placement",
 ]
 
 
@@ -134,6 +138,8 @@ def lib():
             "ft_pool_alloc": (C.c_int, [C.c_size_t, C.POINTER(P)]),
             "ft_pool_free": (C.c_int, [P]),
             "ft_bench_bw": (C.c_int, [C.POINTER(ft_shape), P, I, P, I, C.POINTER(C.c_double), C.POINTER(C.c_double)]),
+            "ft_replay_placement": (C.c_int, [I, C.POINTER(ft_shape), I, P, I, I, I, C.POINTER(C.c_int64),
+                                              C.POINTER(C.c_int64)]),
             "ft_create": (C.c_int, [C.POINTER(ft_shape), C.POINTER(ft_config), P, C.c_size_t, P, I, P, C.c_size_t, C.POINTER(P)]),
             "ft_destroy": (C.c_int, [P]),
             "ft_get_stats": (C.c_int, [P, C.POINTER(ft_stats)]),
@@ -288,6 +294,20 @@ def ft_bench_bw(shape, host_pool, n_records, dev_scratch, threads=0):
     _check("ft_bench_bw", lib().ft_bench_bw(C.byref(shape), _ptr(host_pool), n_records, _ptr(dev_scratch),
                                             threads, C.byref(bp), C.byref(bh)))
     return bp.value, bh.value
+
+
+def ft_replay_placement(policy, shape, n_slots, ids, prompt):
+    """(decode reads, decode misses) of a trace ids int32 [requests, prompt + decode, L, k]
+    under one placement policy (FT_PLACE_*).  Host only."""
+    import numpy as np
+    a = np.ascontiguousarray(ids, dtype=np.int32)
+    if a.ndim != 4 or a.shape[2] != shape.L or a.shape[3] != shape.k or a.shape[1] < prompt:
+        raise ValueError("ids must be [requests, prompt + decode, L, k]")
+    reads, misses = C.c_int64(), C.c_int64()
+    _check("ft_replay_placement", lib().ft_replay_placement(
+        policy, C.byref(shape), n_slots, a.ctypes.data_as(C.c_void_p), a.shape[0], prompt, a.shape[1] - prompt,
+        C.byref(reads), C.byref(misses)))
+    return reads.value, misses.value
 
 
 def ft_create(shape, config, host_pool=None, pool_bytes=0, dev_slots=None, n_slots=0, dev_workspace=None,

@@ -26,4 +26,5 @@ Modules:
   cache    two independent LRU residency simulators  -- parity pinned
   permute  stable grouping of (token, slot) pairs    -- parity pinned
   layer    decode / prefill layer composition        -- pinned through the above
+  placement  Fig. 4b placement replay (LRU, hot set, static split) -- parity pinned
 """

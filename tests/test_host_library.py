@@ -321,3 +321,39 @@ def test_bandwidth_profile_file_round_trip(tmp_path):
     assert ft.ft_bw_profile_load(str(tmp_path / "bad.txt"), ft.FT_W_BF16) is None
     with pytest.raises(ft.FtError):
         ft.ft_bw_profile_save(path, ft.ft_bw_profile(0.0, 1.0, 0.0, 0.0, ft.FT_W_BF16))
+
+
+@pytest.mark.parametrize("L,E,k,R,prompt,decode,key", [
+    (4, 16, 2, 3, 12, 30, 21),     # small pool: on-demand prefill below 2E slots
+    (6, 32, 4, 2, 40, 25, 22),
+    (5, 128, 8, 2, 64, 20, 23),    # the 40-layer shape's experts per layer and top-k
+])
+def test_placement_replay_matches_oracle(L, E, k, R, prompt, decode, key):
+    """Fig. 4b replay: decode reads and misses of every policy, bit-exact with the
+    oracle at capacities below and above 2E (or an error in both)."""
+    from oracle.placement import replay
+    from moe_expert_offload_amd.synth import generator
+    tr = zipf_reuse_trace(L, E, k, R, prompt + decode, 1.1, 0.6, generator(key, 3))
+    ids = np.ascontiguousarray(np.transpose(tr, (2, 0, 1, 3)).astype(np.int32))
+    shape = ft.make_shape(L, E, 64, 64, k)
+    pols = {"lru": ft.FT_PLACE_LRU, "hotset": ft.FT_PLACE_HOTSET, "static": ft.FT_PLACE_STATIC}
+    for N in sorted({0, k, E - 1, E + 3, 2 * E - 1, 2 * E, 2 * E + 5, L * E // 3, L * E // 2, L * E, L * E + 7}):
+        for name, pol in pols.items():
+            try:
+                want = replay(name, ids, L, E, N, prompt)
+            except ValueError:
+                with pytest.raises(ft.FtError) as ei:
+                    ft.ft_replay_placement(pol, shape, N, ids, prompt)
+                assert ei.value.status == ft.FT_ECAP and name == "lru"
+                continue
+            assert ft.ft_replay_placement(pol, shape, N, ids, prompt) == want, (name, N)
+
+
+def test_placement_replay_rejects_bad_input():
+    shape = ft.make_shape(2, 8, 64, 64, 2)
+    ids = np.zeros((1, 3, 2, 2), dtype=np.int32)
+    with pytest.raises(ft.FtError):
+        ft.ft_replay_placement(7, shape, 4, ids, 1)
+    ids[0, 2, 1, 0] = 8
+    with pytest.raises(ft.FtError):
+        ft.ft_replay_placement(ft.FT_PLACE_STATIC, shape, 4, ids, 1)
