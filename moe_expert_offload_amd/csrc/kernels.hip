@@ -38,6 +38,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Buffer loads over one expert record: a scalar resource (base, size in bytes) and a
+// 32-bit byte offset per lane; the hardware range check returns zeros for offsets
+// past the size, so masked pieces cost no branch (kOOB is past every record).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
@@ -54,6 +67,16 @@ __device__ __forceinline__ float dot8(uint4 a, uint4 b, float acc) {
   acc = fmaf(bf_hi(a.z), bf_hi(b.z), acc);
   acc = fmaf(bf_lo(a.w), bf_lo(b.w), acc);
   acc = fmaf(bf_hi(a.w), bf_hi(b.w), acc);
+  return acc;
+}
+
+// the same with the packed bf16 dot instruction (fp32 accumulation), no unpacking
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot8_pk(uint4 a, uint4 b, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), acc, false);
   return acc;
 }
 
@@ -841,11 +864,16 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* key, in
 // ============================================================================
 // Grouped SwiGLU FFN, row-streaming form (few tokens per expert)
 // ============================================================================
-// One wavefront per weight row.  Lane l reads the 16-byte pieces l, l+64, ... of
-// the row, so a wavefront streams 1 KB per load; the row is held in registers
-// while every token of the group is applied to it.
+// gate/up: one wavefront per row pair (gate row r, up row r).  Lane l reads the
+// 16-byte pieces l, l+64, ... of each row, so a wavefront streams 1 KB per load;
+// the rows are held in registers while every token of the group is applied to them.
+// down: one wavefront per 4 consecutive rows of W_down, read as one contiguous span
+// (6 KB at d_ff = 768), each 16-byte piece added into the sum of the row it lies in.
+// Both read the group's metadata in one round of independent loads and the record
+// through a buffer resource (masked pieces read as zeros), weights before anything
+// the arithmetic needs.
 
-template <int NT>
+template <int NT, int JC>
 __global__ __launch_bounds__(256) void ffn_gateup_rows_kernel(
     const uint16_t* __restrict__ x, int d, int d_ff, int k, const uint16_t* __restrict__ slots,
     size_t rec_elems, const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets,
@@ -855,15 +883,16 @@ __global__ __launch_bounds__(256) void ffn_gateup_rows_kernel(
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
   const int row = (blockIdx.x % blocks_per_group) * 4 + wave;
-  if (row >= d_ff || (g_hi != nullptr && g >= *g_hi)) return;
+  const int ghi = g_hi != nullptr ? *g_hi : INT_MAX;
+  const int slot = group_slot[g];
   const int r0 = offsets[g];
-  const int n = offsets[g + 1] - r0;
-  if (n <= 0) return;
-  const uint16_t* rec = slots + (size_t)group_slot[g] * rec_elems;
-  const uint16_t* wg = rec + (size_t)row * d;
-  const uint16_t* wu = rec + (size_t)d_ff * d + (size_t)row * d;
+  const int r1 = offsets[g + 1];
+  if (row >= d_ff || g >= ghi || r1 <= r0) return;
+  const int n = r1 - r0;
+  const __amdgpu_buffer_rsrc_t rec = buf_rsrc(slots + (size_t)slot * rec_elems, (uint32_t)(rec_elems * 2));
+  const uint32_t og = (uint32_t)row * (uint32_t)d * 2u;
+  const uint32_t ou = (uint32_t)(d_ff + row) * (uint32_t)d * 2u;
   const int J = (d + 511) >> 9;
-  const uint4 zero = make_uint4(0, 0, 0, 0);
   for (int tb = 0; tb < n; tb += NT) {
     float ag[NT], au[NT];
     const uint16_t* xr[NT];
@@ -871,27 +900,31 @@ __global__ __launch_bounds__(256) void ffn_gateup_rows_kernel(
     for (int i = 0; i < NT; ++i) {
       ag[i] = 0.0f;
       au[i] = 0.0f;
-      xr[i] = (tb + i < n) ? x + (size_t)(perm[r0 + tb + i] / k) * d : nullptr;
+      xr[i] = nullptr;
     }
-    for (int j0 = 0; j0 < J; j0 += 8) {
-      uint4 gw[8], uw[8];
+    for (int j0 = 0; j0 < J; j0 += JC) {
+      uint4 gw[JC], uw[JC];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
+      for (int jj = 0; jj < JC; ++jj) {
         const int i0 = (j0 + jj) * 512 + lane * 8;
         const bool in = (j0 + jj < J) && i0 < d;
-        gw[jj] = in ? ld16(wg + i0) : zero;
-        uw[jj] = in ? ld16(wu + i0) : zero;
+        gw[jj] = buf_ld16(rec, in ? og + (uint32_t)i0 * 2u : kOOB);
+        uw[jj] = buf_ld16(rec, in ? ou + (uint32_t)i0 * 2u : kOOB);
+      }
+      if (j0 == 0) {  // token rows, looked up once the first weights are in flight
+#pragma unroll
+        for (int i = 0; i < NT; ++i) xr[i] = (tb + i < n) ? x + (size_t)(perm[r0 + tb + i] / k) * d : nullptr;
       }
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         if (xr[i] == nullptr) continue;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
+        for (int jj = 0; jj < JC; ++jj) {
           const int i0 = (j0 + jj) * 512 + lane * 8;
           if ((j0 + jj < J) && i0 < d) {
             const uint4 xv = ld16(xr[i] + i0);
-            ag[i] = dot8(gw[jj], xv, ag[i]);
-            au[i] = dot8(uw[jj], xv, au[i]);
+            ag[i] = dot8_pk(gw[jj], xv, ag[i]);
+            au[i] = dot8_pk(uw[jj], xv, au[i]);
           }
         }
       }
@@ -911,48 +944,59 @@ __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
     int d, int d_ff, const uint16_t* __restrict__ slots, size_t rec_elems,
     const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, int g_begin,
     int blocks_per_group, const float* __restrict__ h, float* __restrict__ out, const int32_t* __restrict__ g_hi) {
+  constexpr int RW = 4;  // W_down rows per wavefront
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
-  const int row = (blockIdx.x % blocks_per_group) * 4 + wave;
-  if (row >= d || (g_hi != nullptr && g >= *g_hi)) return;
+  const int row0 = ((blockIdx.x % blocks_per_group) * 4 + wave) * RW;
+  const int ghi = g_hi != nullptr ? *g_hi : INT_MAX;
+  const int slot = group_slot[g];
   const int r0 = offsets[g];
-  const int n = offsets[g + 1] - r0;
-  if (n <= 0) return;
-  const uint16_t* wd = slots + (size_t)group_slot[g] * rec_elems + (size_t)2 * d_ff * d + (size_t)row * d_ff;
-  const int J = (d_ff + 511) >> 9;
-  const uint4 zero = make_uint4(0, 0, 0, 0);
+  const int r1 = offsets[g + 1];
+  if (row0 >= d || g >= ghi || r1 <= r0) return;
+  const int n = r1 - r0;
+  const __amdgpu_buffer_rsrc_t rec = buf_rsrc(slots + (size_t)slot * rec_elems, (uint32_t)(rec_elems * 2));
+  const int span = min(RW, d - row0) * d_ff;  // elements of this wave's rows, contiguous
+  const uint32_t base = ((uint32_t)2 * d_ff * d + (uint32_t)row0 * d_ff) * 2u;
+  const int J = (span + 511) >> 9;
   for (int tb = 0; tb < n; tb += NT) {
-    float acc[NT];
+    float acc[NT][RW];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) acc[i] = 0.0f;
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int r = 0; r < RW; ++r) acc[i][r] = 0.0f;
     for (int j0 = 0; j0 < J; j0 += 8) {
       uint4 wv[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
-        const int i0 = (j0 + jj) * 512 + lane * 8;
-        wv[jj] = ((j0 + jj < J) && i0 < d_ff) ? ld16(wd + i0) : zero;
+        const int e0 = (j0 + jj) * 512 + lane * 8;
+        wv[jj] = buf_ld16(rec, (j0 + jj < J && e0 < span) ? base + (uint32_t)e0 * 2u : kOOB);
       }
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        if (tb + i >= n) continue;
-        const float* hr = h + (size_t)(r0 + tb + i) * d_ff;
+      for (int jj = 0; jj < 8; ++jj) {
+        const int e0 = (j0 + jj) * 512 + lane * 8;
+        if (j0 + jj >= J || e0 >= span) continue;
+        const int rr = e0 / d_ff;  // a piece never straddles two rows (d_ff % 8 == 0)
+        const int col = e0 - rr * d_ff;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int i0 = (j0 + jj) * 512 + lane * 8;
-          if ((j0 + jj < J) && i0 < d_ff) {
-            const float4 h0 = *reinterpret_cast<const float4*>(hr + i0);
-            const float4 h1 = *reinterpret_cast<const float4*>(hr + i0 + 4);
-            acc[i] = dot8_f(wv[jj], h0, h1, acc[i]);
-          }
+        for (int i = 0; i < NT; ++i) {
+          if (tb + i >= n) continue;
+          const float* hr = h + (size_t)(r0 + tb + i) * d_ff + col;
+          const float v = dot8_f(wv[jj], *reinterpret_cast<const float4*>(hr),
+                                 *reinterpret_cast<const float4*>(hr + 4), 0.0f);
+#pragma unroll
+          for (int r = 0; r < RW; ++r) acc[i][r] += rr == r ? v : 0.0f;
         }
       }
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       if (tb + i >= n) continue;
-      const float s = wave_sum(acc[i]);
-      if (lane == 0) out[(size_t)(r0 + tb + i) * d + row] = s;
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        const float sum = wave_sum(acc[i][r]);
+        if (lane == 0 && row0 + r < d) out[(size_t)(r0 + tb + i) * d + row0 + r] = sum;
+      }
     }
   }
 }
@@ -1369,13 +1413,18 @@ int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
     return fail(FT_EINVAL, "ffn_rows: unaligned pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t rec_elems = (size_t)3 * d * d_ff;
+  if ((size_t)rec_elems * 2 >= ((size_t)1 << 31)) return fail(FT_EINVAL, "ffn_rows: record over 2 GiB");
   const int bpg_up = (d_ff + 3) / 4;
-  const int bpg_dn = (d + 3) / 4;
+  const int bpg_dn = (d + 15) / 16;
   const int nt = max_rows <= 1 ? 1 : max_rows <= 2 ? 2 : max_rows <= 4 ? 4 : 8;
-#define FT_ROWS_LAUNCH(NT)                                                                        \
-  timed_launch(ffn_gateup_rows_kernel<NT>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
-               slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_hi);             \
-  if (int rc = launched("ffn_gateup_rows")) return rc;                                            \
+#define FT_ROWS_LAUNCH(NT)                                                                          \
+  if (d <= 2048)                                                                                    \
+    timed_launch(ffn_gateup_rows_kernel<NT, 4>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
+                 slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_hi);             \
+  else                                                                                              \
+    timed_launch(ffn_gateup_rows_kernel<NT, 8>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
+                 slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_hi);             \
+  if (int rc = launched("ffn_gateup_rows")) return rc;                                              \
   timed_launch(ffn_down_rows_kernel<NT>, dim3(ng * bpg_dn), dim3(256), s, ev, 1, d, d_ff, slots,   \
                rec_elems, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out, g_hi);       \
   return launched("ffn_down_rows");
