@@ -44,9 +44,15 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
-    src = os.path.join(ROOT, "moe_expert_offload_amd", "csrc", "kernels.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+def kernel_source_hash(kernel: str):
+    """Hash of one kernel's definition in kernels.hip (from its signature to the first
+    closing brace at column 0), so that counters stay valid while other kernels change."""
+    src = open(os.path.join(ROOT, "moe_expert_offload_amd", "csrc", "kernels.hip")).read()
+    at = src.find(f"void {kernel}(")
+    if at < 0:
+        return None
+    end = src.find("\n}\n", at)
+    return hashlib.sha256(src[at:end].encode()).hexdigest()[:16]
 
 
 def stored_traffic(kernel: str, workload: str):
@@ -60,7 +66,7 @@ def stored_traffic(kernel: str, workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -85,7 +91,9 @@ def bw_profile(ft, fshape, pool, scratch, B_P, B_H):
             "hybrid_gate_2x": ft.ft_recommend_hybrid([B_P], [B_H], 2.0)}
 
 
-def run_decode(args, torch, ft, synth, HostPool):
+def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warmup=None):
+    if workload is not None:  # a second decode leg with its own sizes
+        args = argparse.Namespace(**{**vars(args), "workload": workload, "steps": steps, "warmup": warmup})
     wl = synth.WORKLOADS[args.workload]
     s = wl.shape
     T = wl.T
@@ -533,6 +541,10 @@ def main():
     ap.add_argument("--mx-l-phys", type=int, default=16,
                     help="physical layers of the MXFP4 pool (0 = all; pinned memory is capped near half of host RAM)")
     ap.add_argument("--mx-steps", type=int, default=512)
+    ap.add_argument("--no-batch8", dest="batch8", action="store_false", default=True,
+                    help="skip the batch-8 decode leg of the 40-layer stack")
+    ap.add_argument("--b8-steps", type=int, default=64)
+    ap.add_argument("--b8-warmup", type=int, default=16)
     ap.add_argument("--no-replay", dest="replay", action="store_false", default=True,
                     help="skip the Fig. 4b placement replay (host only)")
     ap.add_argument("--replay-requests", type=int, default=4)
@@ -562,6 +574,16 @@ def main():
             cpu = cpu_baseline(args, pool, wl, tr, fq, L_phys, args.cpu_budget_s)
     finally:
         pool.free()
+    b8 = None
+    if args.batch8 and args.workload == "decode-L40-d2048-E128-top8":
+        # the same 40-layer stack at batch 8 (8 tokens per call)
+        d8, r8, k8 = run_decode(args, torch, ft, synth, HostPool, "decode-L40-d2048-E128-top8-b8",
+                                args.b8_steps, args.b8_warmup)
+        k8[0].free()
+        b8 = {"tok_s": d8["tok_s"], "ms_per_step": d8["ms_per_step"], "roofline": r8,
+              "miss_rate_reads": d8["miss_rate_reads"], "fills_per_step": d8["fills_per_step"],
+              "cpu_experts_per_step": d8["cpu_experts_per_step"], "kernels": d8["kernels"],
+              "steps": args.b8_steps, "warmup": args.b8_warmup}
     pre = run_prefill(args, torch, ft, synth, HostPool) if args.prefill else None
     mxr = run_mxfp4(args, torch, ft, synth, HostPool) if args.mxfp4 else None
     rep = run_placement(args, ft, synth) if args.replay else None
@@ -572,7 +594,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": dec["workload"], "global_batch": dec["T"], "layers": dec["L"],
                    "cache_slots": dec["n_slots"], "parallelism": "single-gpu"},
-        "roofline": roof, "cpu_baseline": cpu, "decode": dec, "prefill": pre, "mxfp4": mxr,
+        "roofline": roof, "cpu_baseline": cpu, "decode": dec, "decode_batch8": b8, "prefill": pre, "mxfp4": mxr,
         "placement_replay": rep,
     }
     print(json.dumps(out), flush=True)

@@ -22,6 +22,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 
 #include "internal.h"
@@ -79,6 +80,18 @@ __device__ __forceinline__ float block_dot_bf16(uint4 codes, const uint16_t* __r
   return acc;
 }
 
+// the same with the 32 activations already in registers (4 x 8 bf16)
+__device__ __forceinline__ float block_dot_bf16_r(uint4 codes, const uint4 (&xv)[4]) {
+  const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
+  float acc = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t xw[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+    acc = word_dot_bf16(cw[q], xw, acc);
+  }
+  return acc;
+}
+
 // acc + sum over the 8 elements of one code word times 8 fp32 values
 __device__ __forceinline__ float word_dot_f32(uint32_t cw, float4 h0, float4 h1, float acc) {
   f32x2_t w = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0);
@@ -124,8 +137,29 @@ __device__ __host__ inline MxRec mx_rec(int d, int d_ff) {
   return r;
 }
 
-// ---- decode: one wavefront per weight row, lane l takes blocks l, l+64, ... ----
-template <int NT>
+// ---- decode: row-streaming form ---------------------------------------------------
+// gate/up: one wavefront per 2 row pairs (gate and up rows r, r+1; 1 pair beyond
+// d = 4096); lane l takes the 32-element blocks l, l+64, ... of each row (16 code
+// bytes and one scale byte each) and reads the token's activations for them once.
+// down: one wavefront per 4 consecutive rows of W_down, whose codes (and scales) are
+// one contiguous span; lane l takes blocks l, l+64, ... of the span, each added into
+// the sum of the row it lies in.  Both read the group's metadata in one round of
+// independent loads, then every code block and scale of the lane through a buffer
+// resource (masked ones read as zeros), before anything the arithmetic needs.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOOB = 0x80000000u;  // past every record: buffer loads return zeros
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+__device__ __forceinline__ uint32_t buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+
+template <int NB, int RG>  // NB: blocks per lane and row (d <= 2048 * NB); RG row pairs per wavefront
 __global__ __launch_bounds__(256) void mx_gateup_rows_kernel(
     const uint16_t* __restrict__ x, int d, int d_ff, int k, const uint8_t* __restrict__ slots,
     const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
@@ -133,84 +167,119 @@ __global__ __launch_bounds__(256) void mx_gateup_rows_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
-  const int row = (blockIdx.x % blocks_per_group) * 4 + wave;
-  if (row >= d_ff || (g_hi != nullptr && g >= *g_hi)) return;
+  const int row0 = ((blockIdx.x % blocks_per_group) * 4 + wave) * RG;
+  const int ghi = g_hi != nullptr ? *g_hi : INT_MAX;
+  const int slot = group_slot[g];
   const int r0 = offsets[g];
-  const int n = offsets[g + 1] - r0;
-  if (n <= 0) return;
+  const int r1 = offsets[g + 1];
+  if (row0 >= d_ff || g >= ghi || r1 <= r0) return;
+  const int n = r1 - r0;
   const MxRec R = mx_rec(d, d_ff);
-  const uint8_t* rec = slots + (size_t)group_slot[g] * R.bytes;
-  const uint8_t* gc = rec + R.g_codes + (size_t)row * (d / 2);
-  const uint8_t* uc = rec + R.u_codes + (size_t)row * (d / 2);
-  const uint8_t* gs = rec + R.g_sc + (size_t)row * (d / 32);
-  const uint8_t* us = rec + R.u_sc + (size_t)row * (d / 32);
+  const __amdgpu_buffer_rsrc_t rec = buf_rsrc(slots + (size_t)slot * R.bytes, (uint32_t)R.bytes);
   const int nb = d / 32;  // blocks per row
-  for (int tb = 0; tb < n; tb += NT) {
-    float ag[NT], au[NT];
-    const uint16_t* xr[NT];
+  uint4 cg[RG][NB], cu[RG][NB];
+  uint32_t sg[RG][NB], su[RG][NB];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      ag[i] = 0.0f;
-      au[i] = 0.0f;
-      xr[i] = (tb + i < n) ? x + (size_t)(perm[r0 + tb + i] / k) * d : nullptr;
+  for (int r = 0; r < RG; ++r) {
+    const int row = row0 + r;
+    const uint32_t gc = (uint32_t)(R.g_codes + (size_t)row * (d / 2)), uc = (uint32_t)(R.u_codes + (size_t)row * (d / 2));
+    const uint32_t gs = (uint32_t)(R.g_sc + (size_t)row * nb), us = (uint32_t)(R.u_sc + (size_t)row * nb);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int b = lane + 64 * j;
+      const bool in = row < d_ff && b < nb;
+      cg[r][j] = buf_ld16(rec, in ? gc + 16u * b : kOOB);
+      cu[r][j] = buf_ld16(rec, in ? uc + 16u * b : kOOB);
+      sg[r][j] = buf_ld8(rec, in ? gs + b : kOOB);
+      su[r][j] = buf_ld8(rec, in ? us + b : kOOB);
     }
-    for (int b = lane; b < nb; b += 64) {
-      const uint4 cgv = *reinterpret_cast<const uint4*>(gc + 16 * b);
-      const uint4 cuv = *reinterpret_cast<const uint4*>(uc + 16 * b);
-      const float sg = e8m0(gs[b]), su = e8m0(us[b]);
+  }
+  // one token at a time: its 32 activations per block of the lane are read once and
+  // applied to all RG row pairs
+  for (int t = 0; t < n; ++t) {
+    const uint16_t* xr = x + (size_t)(perm[r0 + t] / k) * d;
+    uint4 xv[NB][4];
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        if (xr[i] == nullptr) continue;
-        ag[i] = fmaf(block_dot_bf16(cgv, xr[i] + 32 * b), sg, ag[i]);
-        au[i] = fmaf(block_dot_bf16(cuv, xr[i] + 32 * b), su, au[i]);
+    for (int j = 0; j < NB; ++j) {
+      const int b = lane + 64 * j;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        xv[j][q] = b < nb ? *reinterpret_cast<const uint4*>(xr + 32 * b + 8 * q) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      float ag = 0.0f, au = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (lane + 64 * j >= nb) continue;
+        ag = fmaf(block_dot_bf16_r(cg[r][j], xv[j]), e8m0(sg[r][j]), ag);
+        au = fmaf(block_dot_bf16_r(cu[r][j], xv[j]), e8m0(su[r][j]), au);
       }
-    }
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      if (tb + i >= n) continue;
-      const float zg = wave_sum(ag[i]);
-      const float zu = wave_sum(au[i]);
-      if (lane == 0) h[(size_t)(r0 + tb + i) * d_ff + row] = silu(zg) * zu;
+      const float zg = wave_sum(ag);
+      const float zu = wave_sum(au);
+      if (lane == 0 && row0 + r < d_ff) h[(size_t)(r0 + t) * d_ff + row0 + r] = silu(zg) * zu;
     }
   }
 }
 
-template <int NT>
+template <int NT, int NB>  // NB: blocks per lane over 4 rows (d_ff <= 512 * NB)
 __global__ __launch_bounds__(256) void mx_down_rows_kernel(
     int d, int d_ff, const uint8_t* __restrict__ slots, const int32_t* __restrict__ group_slot,
     const int32_t* __restrict__ offsets, int g_begin, int blocks_per_group, const float* __restrict__ h,
     float* __restrict__ out, const int32_t* __restrict__ g_hi) {
+  constexpr int RW = 4;  // W_down rows per wavefront
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
-  const int row = (blockIdx.x % blocks_per_group) * 4 + wave;
-  if (row >= d || (g_hi != nullptr && g >= *g_hi)) return;
+  const int row0 = ((blockIdx.x % blocks_per_group) * 4 + wave) * RW;
+  const int ghi = g_hi != nullptr ? *g_hi : INT_MAX;
+  const int slot = group_slot[g];
   const int r0 = offsets[g];
-  const int n = offsets[g + 1] - r0;
-  if (n <= 0) return;
+  const int r1 = offsets[g + 1];
+  if (row0 >= d || g >= ghi || r1 <= r0) return;
+  const int n = r1 - r0;
   const MxRec R = mx_rec(d, d_ff);
-  const uint8_t* rec = slots + (size_t)group_slot[g] * R.bytes;
-  const uint8_t* dc = rec + R.d_codes + (size_t)row * (d_ff / 2);
-  const uint8_t* ds = rec + R.d_sc + (size_t)row * (d_ff / 32);
-  const int nb = d_ff / 32;
-  for (int tb = 0; tb < n; tb += NT) {
-    float acc[NT];
+  const __amdgpu_buffer_rsrc_t rec = buf_rsrc(slots + (size_t)slot * R.bytes, (uint32_t)R.bytes);
+  const int nb = d_ff / 32;                    // blocks per row
+  const int span = min(RW, d - row0) * nb;     // blocks of this wave's rows, contiguous
+  const uint32_t dc = (uint32_t)(R.d_codes + (size_t)row0 * (d_ff / 2)), ds = (uint32_t)(R.d_sc + (size_t)row0 * nb);
+  uint4 cv[NB];
+  uint32_t sv[NB];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) acc[i] = 0.0f;
-    for (int b = lane; b < nb; b += 64) {
-      const uint4 cv = *reinterpret_cast<const uint4*>(dc + 16 * b);
-      const float sc = e8m0(ds[b]);
+  for (int j = 0; j < NB; ++j) {
+    const int p = lane + 64 * j;
+    const bool in = p < span;
+    cv[j] = buf_ld16(rec, in ? dc + 16u * p : kOOB);
+    sv[j] = buf_ld8(rec, in ? ds + p : kOOB);
+  }
+  for (int tb = 0; tb < n; tb += NT) {
+    float acc[NT][RW];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int r = 0; r < RW; ++r) acc[i][r] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int p = lane + 64 * j;
+      if (p >= span) continue;
+      const int rr = p / nb, cb = p - rr * nb;
+      const float sc = e8m0(sv[j]);
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         if (tb + i >= n) continue;
-        acc[i] = fmaf(block_dot_f32(cv, h + (size_t)(r0 + tb + i) * d_ff + 32 * b), sc, acc[i]);
+        const float v = block_dot_f32(cv[j], h + (size_t)(r0 + tb + i) * d_ff + 32 * cb) * sc;
+#pragma unroll
+        for (int r = 0; r < RW; ++r) acc[i][r] += rr == r ? v : 0.0f;
       }
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       if (tb + i >= n) continue;
-      const float s = wave_sum(acc[i]);
-      if (lane == 0) out[(size_t)(r0 + tb + i) * d + row] = s;
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        const float sum = wave_sum(acc[i][r]);
+        if (lane == 0 && row0 + r < d) out[(size_t)(r0 + tb + i) * d + row0 + r] = sum;
+      }
     }
   }
 }
@@ -644,14 +713,25 @@ int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t*
   if (!aligned16(x) || !aligned16(slots) || !aligned16(h) || !aligned16(out))
     return fail(FT_EINVAL, "mx_ffn_rows: unaligned pointer");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int bpg_up = (d_ff + 3) / 4, bpg_dn = (d + 3) / 4;
+  if (mx_rec(d, d_ff).bytes >= ((size_t)1 << 31)) return fail(FT_EINVAL, "mx_ffn_rows: record over 2 GiB");
+  if (d > 8192 || d_ff > 4096) return fail(FT_EINVAL, "mx_ffn_rows: need d <= 8192 and d_ff <= 4096");
+  // gate/up: 2 row pairs per wavefront up to d = 4096 (2 blocks per lane), 1 beyond
+  const int rg = d <= 4096 ? 2 : 1;
+  const int bpg_up = (d_ff + 4 * rg - 1) / (4 * rg), bpg_dn = (d + 15) / 16;
   const int nt = max_rows <= 1 ? 1 : max_rows <= 2 ? 2 : max_rows <= 4 ? 4 : 8;
-#define FT_MX_ROWS(NT)                                                                                        \
-  timed_launch(mx_gateup_rows_kernel<NT>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, slots,      \
-               group_slot, offsets, perm, g_begin, bpg_up, h, g_hi);                                        \
-  if (int rc = launched("mx_gateup_rows")) return rc;                                                        \
-  timed_launch(mx_down_rows_kernel<NT>, dim3(ng * bpg_dn), dim3(256), s, ev, 1, d, d_ff, slots, group_slot,  \
-               offsets, g_begin, bpg_dn, (const float*)h, out, g_hi);                                        \
+  // blocks per lane: gate/up ceil(d/32/64), down ceil(4*d_ff/32/64)
+  const int nbu = (d / 32 + 63) / 64, nbd = (d_ff / 8 + 63) / 64;
+#define FT_MX_UP(NB)                                                                                         \
+  timed_launch(mx_gateup_rows_kernel<NB, NB <= 2 ? 2 : 1>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
+               slots, group_slot, offsets, perm, g_begin, bpg_up, h, g_hi)
+#define FT_MX_DN(NT, NB)                                                                                     \
+  timed_launch(mx_down_rows_kernel<NT, NB>, dim3(ng * bpg_dn), dim3(256), s, ev, 1, d, d_ff, slots, group_slot, \
+               offsets, g_begin, bpg_dn, (const float*)h, out, g_hi)
+#define FT_MX_ROWS(NT)                                                     \
+  if (nbu <= 1) FT_MX_UP(1); else if (nbu <= 2) FT_MX_UP(2); else FT_MX_UP(4);            \
+  if (int rc = launched("mx_gateup_rows")) return rc;                      \
+  if (nbd <= 1) FT_MX_DN(NT, 1); else if (nbd <= 2) FT_MX_DN(NT, 2);       \
+  else if (nbd <= 4) FT_MX_DN(NT, 4); else FT_MX_DN(NT, 8);                \
   return launched("mx_down_rows");
   switch (nt) {
     case 1: { FT_MX_ROWS(1) }
@@ -659,6 +739,8 @@ int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t*
     case 4: { FT_MX_ROWS(4) }
     default: { FT_MX_ROWS(8) }
   }
+#undef FT_MX_UP
+#undef FT_MX_DN
 #undef FT_MX_ROWS
 }
 
