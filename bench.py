@@ -435,7 +435,10 @@ def run_mxfp4(args, torch, ft, synth, HostPool):
                    "resize_at_step": steps // 2, "resize_ms": t_resize * 1e3,
                    "before_resize": seg_info(0, N), "after_resize": seg_info(1, N2),
                    "mx_gateup_rows": {"GBs": round(gu_gbs, 1), "frac_of_hbm_peak": round(gu_gbs / HBM_PEAK_GBS, 4),
-                                      "avg_us": dprof["ms_gateup"] / max(dprof["launches"], 1) * 1e3}},
+                                      "avg_us": dprof["ms_gateup"] / max(dprof["launches"], 1) * 1e3},
+                   "mx_down_rows": {"GBs": round(dprof["bytes_down"] / (dprof["ms_down"] * 1e-3) / 1e9, 1)
+                                    if dprof["ms_down"] > 0 else 0.0,
+                                    "avg_us": dprof["ms_down"] / max(dprof["launches"], 1) * 1e3}},
     }
 
 

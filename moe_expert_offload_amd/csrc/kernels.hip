@@ -11,6 +11,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 
@@ -868,7 +869,8 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* key, in
 // 16-byte pieces l, l+64, ... of each row, so a wavefront streams 1 KB per load;
 // the rows are held in registers while every token of the group is applied to them.
 // down: one wavefront per 4 consecutive rows of W_down, read as one contiguous span
-// (6 KB at d_ff = 768), each 16-byte piece added into the sum of the row it lies in.
+// (6 KB at d_ff = 768), each 16-byte piece added into the sum of the row it lies in;
+// the group's h rows are staged in LDS once per block (64 KB at most per batch).
 // Both read the group's metadata in one round of independent loads and the record
 // through a buffer resource (masked pieces read as zeros), weights before anything
 // the arithmetic needs.
@@ -945,6 +947,7 @@ __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
     const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, int g_begin,
     int blocks_per_group, const float* __restrict__ h, float* __restrict__ out, const int32_t* __restrict__ g_hi) {
   constexpr int RW = 4;  // W_down rows per wavefront
+  extern __shared__ float sh[];  // h rows of a batch of tokens [nt][d_ff], read by all 4 wavefronts
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
@@ -953,13 +956,19 @@ __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
   const int slot = group_slot[g];
   const int r0 = offsets[g];
   const int r1 = offsets[g + 1];
-  if (row0 >= d || g >= ghi || r1 <= r0) return;
+  if (g >= ghi || r1 <= r0) return;  // the whole block: it stages h below
   const int n = r1 - r0;
   const __amdgpu_buffer_rsrc_t rec = buf_rsrc(slots + (size_t)slot * rec_elems, (uint32_t)(rec_elems * 2));
-  const int span = min(RW, d - row0) * d_ff;  // elements of this wave's rows, contiguous
+  const int span = row0 < d ? min(RW, d - row0) * d_ff : 0;  // elements of this wave's rows, contiguous
   const uint32_t base = ((uint32_t)2 * d_ff * d + (uint32_t)row0 * d_ff) * 2u;
   const int J = (span + 511) >> 9;
-  for (int tb = 0; tb < n; tb += NT) {
+  const int per = min(NT, max(1, 16384 / d_ff));  // token rows per batch: at most 64 KB of h
+  for (int tb = 0; tb < n; tb += per) {
+    const int nt = min(per, n - tb);
+    __syncthreads();  // the previous batch's h is no longer read
+    for (int i = threadIdx.x * 4; i < nt * d_ff; i += 256 * 4)
+      *reinterpret_cast<float4*>(sh + i) = *reinterpret_cast<const float4*>(h + (size_t)(r0 + tb) * d_ff + i);
+    __syncthreads();
     float acc[NT][RW];
 #pragma unroll
     for (int i = 0; i < NT; ++i)
@@ -980,8 +989,8 @@ __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
         const int col = e0 - rr * d_ff;
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
-          if (tb + i >= n) continue;
-          const float* hr = h + (size_t)(r0 + tb + i) * d_ff + col;
+          if (i >= nt) continue;
+          const float* hr = sh + i * d_ff + col;
           const float v = dot8_f(wv[jj], *reinterpret_cast<const float4*>(hr),
                                  *reinterpret_cast<const float4*>(hr + 4), 0.0f);
 #pragma unroll
@@ -989,9 +998,10 @@ __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
         }
       }
     }
+    if (span == 0) continue;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      if (tb + i >= n) continue;
+      if (i >= nt) continue;
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
         const float sum = wave_sum(acc[i][r]);
@@ -1390,6 +1400,19 @@ int launch_permute(const int32_t* key, int P, int n_groups, int32_t* offsets, in
   return launched("perm_scatter");
 }
 
+// Launches a kernel with dynamic shared memory; with timing events, start/stop
+// bracket the kernel itself.
+template <typename... KArgs, typename... Args>
+inline void timed_launch_shm(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shm, hipStream_t s,
+                             void* const* ev, int which, Args... args) {
+  if (ev) {
+    hipExtLaunchKernelGGL(kern, grid, block, shm, s, static_cast<hipEvent_t>(ev[2 * which]),
+                          static_cast<hipEvent_t>(ev[2 * which + 1]), 0, args...);
+  } else {
+    hipLaunchKernelGGL(kern, grid, block, shm, s, args...);
+  }
+}
+
 // Launches a kernel; with timing events, start/stop bracket the kernel itself.
 template <typename... KArgs, typename... Args>
 inline void timed_launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t s, void* const* ev,
@@ -1414,6 +1437,7 @@ int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t rec_elems = (size_t)3 * d * d_ff;
   if ((size_t)rec_elems * 2 >= ((size_t)1 << 31)) return fail(FT_EINVAL, "ffn_rows: record over 2 GiB");
+  if (d_ff > 16384) return fail(FT_EINVAL, "ffn_rows: need d_ff <= 16384");
   const int bpg_up = (d_ff + 3) / 4;
   const int bpg_dn = (d + 15) / 16;
   const int nt = max_rows <= 1 ? 1 : max_rows <= 2 ? 2 : max_rows <= 4 ? 4 : 8;
@@ -1425,8 +1449,9 @@ int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
     timed_launch(ffn_gateup_rows_kernel<NT, 8>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
                  slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_hi);             \
   if (int rc = launched("ffn_gateup_rows")) return rc;                                              \
-  timed_launch(ffn_down_rows_kernel<NT>, dim3(ng * bpg_dn), dim3(256), s, ev, 1, d, d_ff, slots,   \
-               rec_elems, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out, g_hi);       \
+  timed_launch_shm(ffn_down_rows_kernel<NT>, dim3(ng * bpg_dn), dim3(256),                         \
+                   (size_t)std::min(NT, std::max(1, 16384 / d_ff)) * d_ff * 4, s, ev, 1, d, d_ff, slots, \
+                   rec_elems, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out, g_hi);   \
   return launched("ffn_down_rows");
   switch (nt) {
     case 1: { FT_ROWS_LAUNCH(1) }

@@ -22,6 +22,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 
@@ -228,6 +229,7 @@ __global__ __launch_bounds__(256) void mx_down_rows_kernel(
     const int32_t* __restrict__ offsets, int g_begin, int blocks_per_group, const float* __restrict__ h,
     float* __restrict__ out, const int32_t* __restrict__ g_hi) {
   constexpr int RW = 4;  // W_down rows per wavefront
+  extern __shared__ float sh[];  // h rows of a batch of tokens [nt][d_ff], read by all 4 wavefronts
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
@@ -236,12 +238,12 @@ __global__ __launch_bounds__(256) void mx_down_rows_kernel(
   const int slot = group_slot[g];
   const int r0 = offsets[g];
   const int r1 = offsets[g + 1];
-  if (row0 >= d || g >= ghi || r1 <= r0) return;
+  if (g >= ghi || r1 <= r0) return;  // the whole block: it stages h below
   const int n = r1 - r0;
   const MxRec R = mx_rec(d, d_ff);
   const __amdgpu_buffer_rsrc_t rec = buf_rsrc(slots + (size_t)slot * R.bytes, (uint32_t)R.bytes);
-  const int nb = d_ff / 32;                    // blocks per row
-  const int span = min(RW, d - row0) * nb;     // blocks of this wave's rows, contiguous
+  const int nb = d_ff / 32;                              // blocks per row
+  const int span = row0 < d ? min(RW, d - row0) * nb : 0;  // blocks of this wave's rows, contiguous
   const uint32_t dc = (uint32_t)(R.d_codes + (size_t)row0 * (d_ff / 2)), ds = (uint32_t)(R.d_sc + (size_t)row0 * nb);
   uint4 cv[NB];
   uint32_t sv[NB];
@@ -252,7 +254,13 @@ __global__ __launch_bounds__(256) void mx_down_rows_kernel(
     cv[j] = buf_ld16(rec, in ? dc + 16u * p : kOOB);
     sv[j] = buf_ld8(rec, in ? ds + p : kOOB);
   }
-  for (int tb = 0; tb < n; tb += NT) {
+  const int per = min(NT, max(1, 16384 / d_ff));  // token rows per batch: at most 64 KB of h
+  for (int tb = 0; tb < n; tb += per) {
+    const int nt = min(per, n - tb);
+    __syncthreads();  // the previous batch's h is no longer read
+    for (int i = threadIdx.x * 4; i < nt * d_ff; i += 256 * 4)
+      *reinterpret_cast<float4*>(sh + i) = *reinterpret_cast<const float4*>(h + (size_t)(r0 + tb) * d_ff + i);
+    __syncthreads();
     float acc[NT][RW];
 #pragma unroll
     for (int i = 0; i < NT; ++i)
@@ -266,15 +274,16 @@ __global__ __launch_bounds__(256) void mx_down_rows_kernel(
       const float sc = e8m0(sv[j]);
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
-        if (tb + i >= n) continue;
-        const float v = block_dot_f32(cv[j], h + (size_t)(r0 + tb + i) * d_ff + 32 * cb) * sc;
+        if (i >= nt) continue;
+        const float v = block_dot_f32(cv[j], sh + i * d_ff + 32 * cb) * sc;
 #pragma unroll
         for (int r = 0; r < RW; ++r) acc[i][r] += rr == r ? v : 0.0f;
       }
     }
+    if (span == 0) continue;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      if (tb + i >= n) continue;
+      if (i >= nt) continue;
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
         const float sum = wave_sum(acc[i][r]);
@@ -698,6 +707,17 @@ inline void timed_launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStrea
   }
 }
 
+template <typename... KArgs, typename... Args>
+inline void timed_launch_shm(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shm, hipStream_t s,
+                             void* const* ev, int which, Args... args) {
+  if (ev) {
+    hipExtLaunchKernelGGL(kern, grid, block, shm, s, static_cast<hipEvent_t>(ev[2 * which]),
+                          static_cast<hipEvent_t>(ev[2 * which + 1]), 0, args...);
+  } else {
+    hipLaunchKernelGGL(kern, grid, block, shm, s, args...);
+  }
+}
+
 }  // namespace
 
 namespace ft {
@@ -725,8 +745,9 @@ int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t*
   timed_launch(mx_gateup_rows_kernel<NB, NB <= 2 ? 2 : 1>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
                slots, group_slot, offsets, perm, g_begin, bpg_up, h, g_hi)
 #define FT_MX_DN(NT, NB)                                                                                     \
-  timed_launch(mx_down_rows_kernel<NT, NB>, dim3(ng * bpg_dn), dim3(256), s, ev, 1, d, d_ff, slots, group_slot, \
-               offsets, g_begin, bpg_dn, (const float*)h, out, g_hi)
+  timed_launch_shm(mx_down_rows_kernel<NT, NB>, dim3(ng * bpg_dn), dim3(256),                                 \
+                   (size_t)std::min(NT, std::max(1, 16384 / d_ff)) * d_ff * 4, s, ev, 1, d,                     \
+                   d_ff, slots, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out, g_hi)
 #define FT_MX_ROWS(NT)                                                     \
   if (nbu <= 1) FT_MX_UP(1); else if (nbu <= 2) FT_MX_UP(2); else FT_MX_UP(4);            \
   if (int rc = launched("mx_gateup_rows")) return rc;                      \
