@@ -184,9 +184,19 @@ __device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
   return ((unsigned long long)hi << 32) | lo;
 }
 
-// Maximum over a wavefront whose 64 lanes are all active: within each row of 16
-// lanes by DPP (swap neighbours, swap pairs, mirror the half rows, mirror the
-// row), then across the four rows.
+// v from the lane DPP control CTRL names, in the rows ROWS selects; other lanes keep v
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long dpp_rows_u64(unsigned long long v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, CTRL, ROWS, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), CTRL,
+                                                           ROWS, 0xf, false);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Maximum over a wavefront whose 64 lanes are all active, all in DPP: within each
+// row of 16 lanes (swap neighbours, swap pairs, mirror the half rows, mirror the
+// row), then lane 15 of rows 0 and 2 into rows 1 and 3 and lane 31 into rows 2 and
+// 3, which leaves the maximum in lane 63; returned to every lane.
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
   unsigned long long w;
   w = dpp_u64<0xb1>(v);  // quad_perm [1,0,3,2]
@@ -197,11 +207,13 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   v = w > v ? w : v;
   w = dpp_u64<0x140>(v);  // row_mirror
   v = w > v ? w : v;
-  w = __shfl_xor(v, 16, WAVE);
+  w = dpp_rows_u64<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
   v = w > v ? w : v;
-  w = __shfl_xor(v, 32, WAVE);
+  w = dpp_rows_u64<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
   v = w > v ? w : v;
-  return v;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((unsigned long long)hi << 32) | lo;
 }
 
 // The logit a rank key was made from (zero comes back as +0, which the gate
@@ -420,36 +432,62 @@ __device__ void decide_block(const DecideArgs& a, const int32_t* s_id, int P, co
   }
   for (int i = tid; i < P; i += 256) atomicMin(&s_first[s_id[i]], i);
   __syncthreads();
-  // U: first occurrences in pair order (two pairs per thread, P <= 512)
-  const int i0 = 2 * tid, i1 = 2 * tid + 1;
-  const int f0 = i0 < P && s_first[s_id[i0]] == i0, f1 = i1 < P && s_first[s_id[i1]] == i1;
-  int n_u;
-  int ex = block_excl_scan_256(f0 + f1, &n_u);
-  if (f0) s_u[ex] = s_id[i0];
-  if (f1) s_u[ex + f0] = s_id[i1];
+  // Calls of at most 64 pairs (every decode call of up to 8 tokens) take the
+  // counting steps with ballots, one pair or one distinct expert per lane; every
+  // wavefront computes the same values and wavefront 0 stores them.  Larger calls
+  // take block-wide scans, two per thread.
+  const bool small = P <= 64;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  const int i0 = small ? lane : 2 * tid, i1 = 2 * tid + 1;
+  // U: first occurrences in pair order
+  int n_u, ex;
+  const int f0 = i0 < P && s_first[s_id[i0]] == i0, f1 = !small && i1 < P && s_first[s_id[i1]] == i1;
+  if (small) {
+    const unsigned long long b = __ballot(f0);
+    n_u = __popcll(b);
+    ex = __popcll(b & lt);
+    if (f0 && wv == 0) s_u[ex] = s_id[i0];
+  } else {
+    ex = block_excl_scan_256(f0 + f1, &n_u);
+    if (f0) s_u[ex] = s_id[i0];
+    if (f1) s_u[ex + f0] = s_id[i1];
+  }
   __syncthreads();
-  // classify against the residency before this call; one scan counts H (low half)
-  // and M (high half)
-  const int u0 = 2 * tid, u1 = 2 * tid + 1;
-  const int e0 = u0 < n_u ? s_u[u0] : 0, e1 = u1 < n_u ? s_u[u1] : 0;
-  const int p0 = u0 < n_u ? s_where[e0] : -1, p1 = u1 < n_u ? s_where[e1] : -1;
-  const int h0 = u0 < n_u && p0 >= 0, h1 = u1 < n_u && p1 >= 0;
-  const int m0 = u0 < n_u && !h0, m1 = u1 < n_u && !h1;
-  int tot;
-  ex = block_excl_scan_256((h0 + h1) | ((m0 + m1) << 16), &tot);
-  const int n_h = tot & 0xffff, n_m = tot >> 16, xh = ex & 0xffff, xm = ex >> 16;
-  if (h0) {
-    s_h[xh] = e0;
-    s_g[xh] = p0;
-    s_pos[e0] = xh;  // group of a hit: its rank in H
+  // classify against the residency before this call; H and M keep U order
+  const int u0 = small ? lane : 2 * tid, u1 = 2 * tid + 1;
+  const int e0 = u0 < n_u ? s_u[u0] : 0, e1 = !small && u1 < n_u ? s_u[u1] : 0;
+  const int p0 = u0 < n_u ? s_where[e0] : -1, p1 = !small && u1 < n_u ? s_where[e1] : -1;
+  const int h0 = u0 < n_u && p0 >= 0, h1 = !small && u1 < n_u && p1 >= 0;
+  const int m0 = u0 < n_u && !h0, m1 = !small && u1 < n_u && !h1;
+  int n_h, n_m, xh, xm;
+  if (small) {
+    const unsigned long long bh = __ballot(h0), bm = __ballot(m0);
+    n_h = __popcll(bh);
+    n_m = __popcll(bm);
+    xh = __popcll(bh & lt);
+    xm = __popcll(bm & lt);
+  } else {
+    int tot;
+    ex = block_excl_scan_256((h0 + h1) | ((m0 + m1) << 16), &tot);
+    n_h = tot & 0xffff;
+    n_m = tot >> 16;
+    xh = ex & 0xffff;
+    xm = ex >> 16;
   }
-  if (h1) {
-    s_h[xh + h0] = e1;
-    s_g[xh + h0] = p1;
-    s_pos[e1] = xh + h0;
+  if (!small || wv == 0) {
+    if (h0) {
+      s_h[xh] = e0;
+      s_g[xh] = p0;
+      s_pos[e0] = xh;  // group of a hit: its rank in H
+    }
+    if (h1) {
+      s_h[xh + h0] = e1;
+      s_g[xh + h0] = p1;
+      s_pos[e1] = xh + h0;
+    }
+    if (m0) s_m[xm] = e0;
+    if (m1) s_m[xm + m0] = e1;
   }
-  if (m0) s_m[xm] = e0;
-  if (m1) s_m[xm + m0] = e1;
   const int avail = n_sl - n_h;
   const int q = qstar_device(n_m, a.fq, a.min_fill, a.max_fetch, avail);
   __syncthreads();
@@ -522,37 +560,67 @@ __device__ void decide_block(const DecideArgs& a, const int32_t* s_id, int P, co
   }
   __syncthreads();
   // stamps: H and F in first-occurrence order
-  const int r0 = u0 < n_u && s_pos[e0] >= 0, r1 = u1 < n_u && s_pos[e1] >= 0;
+  const int r0 = u0 < n_u && s_pos[e0] >= 0, r1 = !small && u1 < n_u && s_pos[e1] >= 0;
   int n_res;
-  ex = block_excl_scan_256(r0 + r1, &n_res);
-  if (r0) a.dc.slot_stamp[s_g[s_pos[e0]]] = pf.clock + ex + 1;
-  if (r1) a.dc.slot_stamp[s_g[s_pos[e1]]] = pf.clock + ex + r0 + 1;
+  if (small) {
+    const unsigned long long b = __ballot(r0);
+    n_res = __popcll(b);
+    ex = __popcll(b & lt);
+  } else {
+    ex = block_excl_scan_256(r0 + r1, &n_res);
+  }
+  if (!small || wv == 0) {
+    if (r0) a.dc.slot_stamp[s_g[s_pos[e0]]] = pf.clock + ex + 1;
+    if (r1) a.dc.slot_stamp[s_g[s_pos[e1]]] = pf.clock + ex + r0 + 1;
+  }
   if (tid == 0) *a.dc.clock = pf.clock + n_res;
-  // slot rewrite and stable grouping of the pairs by G (counted directly: P is small)
+  // slot rewrite and stable grouping of the pairs by G
   const int n_g = n_h + q;
-  for (int i = tid; i < P; i += 256) {
-    const int g = s_pos[s_id[i]];
-    pl->pair_group[i] = g;
-    pl->route_slot[i] = g >= 0 ? s_g[g] : -1;
-    if (g < 0) {
-      pl->inv[i] = -1;
-    } else {
-      int pos = 0;
+  if (small) {
+    // lane i holds pair i: per group v, the pairs in it are ranked by ballot
+    if (wv == 0) {
+      const int g = lane < P ? s_pos[s_id[lane]] : -1;
+      int run = 0, pos = -1;
+      for (int v = 0; v < n_g; ++v) {
+        const unsigned long long b = __ballot(g == v);
+        if (g == v) pos = run + __popcll(b & lt);
+        if (lane == 0) pl->offsets[v] = run;
+        run += __popcll(b);
+      }
+      if (lane == 0) pl->offsets[n_g] = run;
+      if (lane < P) {
+        pl->pair_group[lane] = g;
+        pl->route_slot[lane] = g >= 0 ? s_g[g] : -1;
+        pl->inv[lane] = g >= 0 ? pos : -1;
+        if (g >= 0) pl->perm[pos] = lane;
+      }
+    }
+  } else {
+    // counted directly per pair and per group
+    for (int i = tid; i < P; i += 256) {
+      const int g = s_pos[s_id[i]];
+      pl->pair_group[i] = g;
+      pl->route_slot[i] = g >= 0 ? s_g[g] : -1;
+      if (g < 0) {
+        pl->inv[i] = -1;
+      } else {
+        int pos = 0;
+        for (int j = 0; j < P; ++j) {
+          const int gj = s_pos[s_id[j]];
+          pos += (gj >= 0 && gj < g) || (gj == g && j < i);
+        }
+        pl->perm[pos] = i;
+        pl->inv[i] = pos;
+      }
+    }
+    for (int g = tid; g <= n_g; g += 256) {
+      int off = 0;
       for (int j = 0; j < P; ++j) {
         const int gj = s_pos[s_id[j]];
-        pos += (gj >= 0 && gj < g) || (gj == g && j < i);
+        off += gj >= 0 && gj < g;
       }
-      pl->perm[pos] = i;
-      pl->inv[i] = pos;
+      pl->offsets[g] = off;
     }
-  }
-  for (int g = tid; g <= n_g; g += 256) {
-    int off = 0;
-    for (int j = 0; j < P; ++j) {
-      const int gj = s_pos[s_id[j]];
-      off += gj >= 0 && gj < g;
-    }
-    pl->offsets[g] = off;
   }
   for (int i = tid; i < n_u; i += 256) pl->U[i] = s_u[i];
   for (int i = tid; i < n_h; i += 256) pl->H[i] = s_h[i];
@@ -654,11 +722,10 @@ constexpr int kFillBlocks = 64;  // enough reads in flight for the link; more on
 
 // Decode router in one launch: one wavefront per (token, expert) logit (same
 // arithmetic order as router_logits_kernel: lane l owns elements (i mod 512)/8 ==
-// l, adds its products in increasing i, then a butterfly); the blocks with
-// blockIdx.y == 0 copy their token's x row to pinned host memory; the last block
-// to finish (device-scope fence + ticket counter, no waiting) does the top-k of
-// every token, the cache decisions when asked, and publishes to pinned host
-// memory.  `ticket` is a zeroed device counter, reset by the last block.
+// l, adds its products in increasing i, then a butterfly); the last block to
+// finish (device-scope fence + ticket counter, no waiting) does the top-k of every
+// token, the cache decisions when asked, copies x to pinned host memory and
+// publishes there.  `ticket` is a zeroed device counter, reset by the last block.
 __global__ __launch_bounds__(256) void router_decode_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint8_t* __restrict__ allowed,
     int T, int d, int E, int k, float* __restrict__ logits, int32_t* __restrict__ idx,
@@ -698,9 +765,6 @@ __global__ __launch_bounds__(256) void router_decode_kernel(
     for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o, WAVE);
     if (lane == 0) logits[(size_t)t * E + e] = acc;
   }
-  if (blockIdx.y == 0 && pub_x != nullptr)
-    for (int i = threadIdx.x * 8; i < d; i += 256 * 8)
-      *reinterpret_cast<uint4*>(pub_x + (size_t)t * d + i) = ld16(x + (size_t)t * d + i);
   __threadfence();
   __shared__ int last;
   __syncthreads();
@@ -717,6 +781,11 @@ __global__ __launch_bounds__(256) void router_decode_kernel(
                pub_gates ? pub_gates + (size_t)tt * k : nullptr, s_ids + tt * k);
   __syncthreads();
   if (decide) decide_block(da, s_ids, T * k, pf);
+  // x for the host's CPU branch, written over PCIe here so that only the final
+  // fence waits for it
+  if (pub_x != nullptr)
+    for (int i = threadIdx.x * 8; i < T * d; i += 256 * 8)
+      *reinterpret_cast<uint4*>(pub_x + i) = ld16(x + i);
   __threadfence_system();
   __syncthreads();
   if (threadIdx.x == 0) {
