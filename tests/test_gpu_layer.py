@@ -53,6 +53,8 @@ SMALL = Workload("small-decode", 11, Shape(4, 32, 256, 512, 4), 2, 0.3)
     (0, 0, 0, 3, 40),         # never fetch: everything misses to the CPU
     (30000, 1, 2, 8, 40),     # fixed fetch cap, batch 8
     (Q16, 1, -1, 4, 128),     # capacity = all pairs: only compulsory misses
+    (20000, 1, -1, 17, 40),   # 68 pairs: decisions by block-wide scans (more than 64 pairs)
+    (20000, 1, -1, 64, 96),   # 64 tokens, the largest decode call (256 pairs)
 ])
 def test_decode_trace_parity(fq, min_fill, max_fetch, T, N):
     _decode_trace(SMALL, fq, min_fill, max_fetch, T, N)
