@@ -336,7 +336,7 @@ int ft_grouped_ffn_mx(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t
 /* Gate-weighted combine and exact merge ([FT] §3.2: the GPU and CPU partial sums
  * merge into the exact MoE output):  y[t] = sum_{j: inv[t*k+j] >= 0, in j order}
  * gates[t*k+j] * out[inv[t*k+j]]  +  cpu_partial[t]  (cpu_partial may be NULL).
- * All device; y fp32 [T, d]. */
+ * All device; y fp32 [T, d]; 1 <= k <= 8 and d % 4 == 0, else FT_EINVAL. */
 int ft_combine(const float* out, const int32_t* inv, const float* gates,
                const float* cpu_partial, int32_t T, int32_t k, int32_t d, float* y,
                void* stream);

@@ -1339,19 +1339,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = blockIdx.y;
   const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (t >= T || c >= d) return;
+  // every load first (k <= 8): the pairs' positions and gates, then their rows and the
+  // host partial, so the call waits for memory once; then the sum in rank order
+  int pos[8];
+  float g[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pos[j] = j < k ? inv[(size_t)t * k + j] : -1;
+    g[j] = j < k ? gates[(size_t)t * k + j] : 0.0f;
+  }
+  float4 o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    o[j] = pos[j] >= 0 ? *reinterpret_cast<const float4*>(out + (size_t)pos[j] * d + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 p = cpu != nullptr ? *reinterpret_cast<const float4*>(cpu + (size_t)t * d + c) : make_float4(0.f, 0.f, 0.f, 0.f);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int pos = inv[(size_t)t * k + j];
-    if (pos < 0) continue;
-    const float g = gates[(size_t)t * k + j];
-    const float4 o = *reinterpret_cast<const float4*>(out + (size_t)pos * d + c);
-    acc.x = fmaf(g, o.x, acc.x);
-    acc.y = fmaf(g, o.y, acc.y);
-    acc.z = fmaf(g, o.z, acc.z);
-    acc.w = fmaf(g, o.w, acc.w);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (pos[j] < 0) continue;
+    acc.x = fmaf(g[j], o[j].x, acc.x);
+    acc.y = fmaf(g[j], o[j].y, acc.y);
+    acc.z = fmaf(g[j], o[j].z, acc.z);
+    acc.w = fmaf(g[j], o[j].w, acc.w);
   }
   if (cpu != nullptr) {
-    const float4 p = *reinterpret_cast<const float4*>(cpu + (size_t)t * d + c);
     acc.x += p.x;
     acc.y += p.y;
     acc.z += p.z;
@@ -1557,7 +1568,7 @@ int launch_ffn_mfma(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
 
 int launch_combine(const float* out, const int32_t* inv, const float* gates,
                    const float* cpu_partial, int T, int k, int d, float* y, void* stream) {
-  if (T < 0 || k < 1 || d <= 0 || d % 4 != 0) return fail(FT_EINVAL, "combine: bad shape");
+  if (T < 0 || k < 1 || k > 8 || d <= 0 || d % 4 != 0) return fail(FT_EINVAL, "combine: bad shape (1 <= k <= 8, d % 4 == 0)");
   if (T == 0) return FT_OK;
   if (T > 65535) return fail(FT_EINVAL, "combine: T > 65535");
   hipStream_t s = static_cast<hipStream_t>(stream);
