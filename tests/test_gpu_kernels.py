@@ -31,6 +31,9 @@ def _say(*a):
     (300, 4096, 256, 6, False, False),  # tile path for many tokens
     (70, 520, 33, 3, False, False),     # ragged d and E
     (5, 256, 16, 4, False, True),       # all-equal logits: ties go to the lower index
+    (3, 256, 1024, 8, False, False),    # the largest expert count (16 experts per lane)
+    (1, 2048, 600, 8, True, False),     # 600 experts, trace-driven
+    (2, 64, 1, 1, False, False),        # one expert: top-1 of 1, gate 1
 ])
 def test_router_bit_exact(T, d, E, k, use_allowed, zero_x):
     torch = torch_mod()
@@ -120,6 +123,7 @@ def _ffn_case(form, d, d_ff, rows, k=2, split=None, seed=0):
     (2048, 768, [8, 5, 1, 2], None),
     (4096, 2048, [1, 2, 4], None),
     (520, 136, [2, 9], None),           # ragged sizes
+    (256, 4096, [6, 1], None),          # d_ff = 4096: h staged in LDS 4 rows at a time
 ])
 def test_grouped_ffn_rows_form(d, d_ff, rows, split):
     _ffn_case(1, d, d_ff, rows, split=split)
@@ -134,12 +138,12 @@ def test_grouped_ffn_mfma_form(d, d_ff, rows):
     _ffn_case(2, d, d_ff, rows)
 
 
-@pytest.mark.parametrize("with_cpu", [False, True])
-def test_combine(with_cpu):
+@pytest.mark.parametrize("with_cpu,k", [(False, 3), (True, 3), (True, 8)])
+def test_combine(with_cpu, k):
     torch = torch_mod()
-    _say("combine", with_cpu)
-    rng = generator(93, int(with_cpu))
-    T, k, d = 5, 3, 256
+    _say("combine", with_cpu, k)
+    rng = generator(93, int(with_cpu), k)
+    T, d = 5, 256
     inv = np.arange(T * k, dtype=np.int32)
     inv[[1, 7, 14]] = -1
     out = rng.normal(size=(T * k, d)).astype(np.float32)

@@ -114,6 +114,7 @@ def _mx_ffn_case(form, d, d_ff, rows, k=2, split=None, seed=0):
     (2048, 768, [1] * 6, 2),            # decode shape, hits then fills
     (4096, 2048, [1, 2], None),         # the MXFP4 decode shape
     (384, 128, [9, 1], None),
+    (256, 4096, [6, 1], None),          # d_ff = 4096: h staged in LDS 4 rows at a time
 ])
 def test_mx_grouped_ffn_rows_form(d, d_ff, rows, split):
     _mx_ffn_case(1, d, d_ff, rows, split=split)
