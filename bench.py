@@ -11,6 +11,8 @@ measured on this machine.  Inputs are seeded and synthetic, resident in HBM
 (activations, router weights, routing masks) or pinned host memory (the pool)
 before the timed region starts.
 
+Also measured: the same stack without the at-least-one-fill floor (min_fill = 0,
+unless --no-min-fill0) and at batch 8 (unless --no-batch8).
 Also measured (unless --no-prefill): one 8192-token prefill chunk through the
 43-layer d=4096, E=256, top-6, d_ff=2048 shape with full-layer double buffering.
 And (unless --no-mxfp4) the same shape with MXFP4 experts: a 16384-token prefill
@@ -91,9 +93,12 @@ def bw_profile(ft, fshape, pool, scratch, B_P, B_H):
             "hybrid_gate_2x": ft.ft_recommend_hybrid([B_P], [B_H], 2.0)}
 
 
-def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warmup=None):
-    if workload is not None:  # a second decode leg with its own sizes
+def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warmup=None, overrides=None,
+               pool=None):
+    if workload is not None:  # a further decode leg with its own sizes
         args = argparse.Namespace(**{**vars(args), "workload": workload, "steps": steps, "warmup": warmup})
+    if overrides:
+        args = argparse.Namespace(**{**vars(args), **overrides})
     wl = synth.WORKLOADS[args.workload]
     s = wl.shape
     T = wl.T
@@ -102,10 +107,11 @@ def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warm
     steps_gen = steps_total + args.steps  # a second pass over further steps carries the kernel timing
     L_phys = s.L if args.l_phys <= 0 else min(args.l_phys, s.L)
     log(f"decode workload {wl.name}: pool {L_phys * s.E} records x {S / 1e6:.2f} MB = {L_phys * s.E * S / 1e9:.1f} GB")
-    t = time.time()
-    pool = HostPool(L_phys * s.E, s.record_bytes, s.pool_dtype)
-    synth.fill_records_torch(pool.view, wl.seed_key, seed=args.seed)
-    log(f"pool allocated and filled in {time.time() - t:.1f} s")
+    if pool is None:
+        t = time.time()
+        pool = HostPool(L_phys * s.E, s.record_bytes, s.pool_dtype)
+        synth.fill_records_torch(pool.view, wl.seed_key, seed=args.seed)
+        log(f"pool allocated and filled in {time.time() - t:.1f} s")
 
     fshape = ft.make_shape(s.L, s.E, s.d, s.d_ff, s.k)
     scratch = torch.empty(64 * S, dtype=torch.uint8, device="cuda")
@@ -548,6 +554,10 @@ def main():
                     help="skip the batch-8 decode leg of the 40-layer stack")
     ap.add_argument("--b8-steps", type=int, default=64)
     ap.add_argument("--b8-warmup", type=int, default=16)
+    ap.add_argument("--no-min-fill0", dest="min_fill0", action="store_false", default=True,
+                    help="skip the decode leg without the at-least-one-fill floor")
+    ap.add_argument("--mf0-steps", type=int, default=64)
+    ap.add_argument("--mf0-warmup", type=int, default=32)
     ap.add_argument("--no-replay", dest="replay", action="store_false", default=True,
                     help="skip the Fig. 4b placement replay (host only)")
     ap.add_argument("--replay-requests", type=int, default=4)
@@ -571,10 +581,21 @@ def main():
     dec, roof, keep = run_decode(args, torch, ft, synth, HostPool)
     pool, wl, tr, fq, L_phys = keep
     cpu = None
+    mf0 = None
     try:
         if not args.no_cpu_baseline:
             log("timing the CPU oracle on the host")
             cpu = cpu_baseline(args, pool, wl, tr, fq, L_phys, args.cpu_budget_s)
+        if args.min_fill0 and args.min_fill != 0:
+            # the same stack and trace without the at-least-one-fill floor: q is the Q16
+            # split alone, so single misses go to the host cores
+            log("decode with min_fill = 0")
+            d0, _, _ = run_decode(args, torch, ft, synth, HostPool, args.workload, args.mf0_steps, args.mf0_warmup,
+                                  {"min_fill": 0}, pool)
+            mf0 = {k: d0[k] for k in ("tok_s", "ms_per_step", "min_fill", "miss_rate_reads", "fills_per_step",
+                                      "cpu_experts_per_step", "h2d_GB_per_step", "host_cpu_branch_ms_per_step",
+                                      "modelled_floor_ms_per_step")}
+            mf0.update({"steps": args.mf0_steps, "warmup": args.mf0_warmup})
     finally:
         pool.free()
     b8 = None
@@ -597,7 +618,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": dec["workload"], "global_batch": dec["T"], "layers": dec["L"],
                    "cache_slots": dec["n_slots"], "parallelism": "single-gpu"},
-        "roofline": roof, "cpu_baseline": cpu, "decode": dec, "decode_batch8": b8, "prefill": pre, "mxfp4": mxr,
+        "roofline": roof, "cpu_baseline": cpu, "decode": dec, "decode_min_fill0": mf0, "decode_batch8": b8,
+        "prefill": pre, "mxfp4": mxr,
         "placement_replay": rep,
     }
     print(json.dumps(out), flush=True)
