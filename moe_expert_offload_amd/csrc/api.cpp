@@ -493,9 +493,10 @@ int ft_grouped_ffn(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t k,
   if (form == 0) form = (mfma_ok && max_rows_per_group >= 32) ? 2 : 1;
   if (form == 2) {
     if (!mfma_ok) return fail(FT_EINVAL, "grouped_ffn: MFMA form needs d%256==0 and d_ff%128==0");
-    return ft::launch_ffn_mfma(static_cast<const uint16_t*>(x), d, d_ff, k, static_cast<const uint16_t*>(slots),
-                               group_slot, offsets, perm, g_begin, g_end, max_rows_per_group,
-                               static_cast<uint16_t*>(h_ws), out, stream);
+    // rows of h are pairs (t, j) of the T tokens: at most T * k
+    return ft::launch_ffn_mfma(static_cast<const uint16_t*>(x), T, d, d_ff, k, static_cast<const uint16_t*>(slots),
+                               group_slot, offsets, perm, g_begin, g_end, T * k, static_cast<uint16_t*>(h_ws), out,
+                               stream);
   }
   if (form != 1) return fail(FT_EINVAL, "grouped_ffn: form must be 0, 1 or 2");
   return ft::launch_ffn_rows(static_cast<const uint16_t*>(x), d, d_ff, k, static_cast<const uint16_t*>(slots),
@@ -889,8 +890,8 @@ static int prefill_layer_on_demand(ft_ctx_t c, int layer, const uint16_t* xs, in
                                     c->wsp<uint8_t>(c->cv.hq), c->wsp<uint8_t>(c->cv.hs), c->wsp<float>(c->cv.out),
                                     cs, nullptr);
     if (mfma)
-      return ft::launch_ffn_mfma(xs, d, d_ff, k, slots16, d_gslot, d_off, d_perm, g0, g1, T, c->wsp<uint16_t>(c->cv.h),
-                                 c->wsp<float>(c->cv.out), cs, nullptr);
+      return ft::launch_ffn_mfma(xs, T, d, d_ff, k, slots16, d_gslot, d_off, d_perm, g0, g1, P,
+                                 c->wsp<uint16_t>(c->cv.h), c->wsp<float>(c->cv.out), cs, nullptr);
     return ft::launch_ffn_rows(xs, d, d_ff, k, slots16, d_gslot, d_off, d_perm, g0, g1, 8, c->wsp<float>(c->cv.h),
                                c->wsp<float>(c->cv.out), cs, nullptr);
   };
@@ -963,7 +964,7 @@ int ft_moe_prefill_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, co
                                         c->wsp<float>(c->cv.out), cs, evs))
       return rc;
   } else if (mfma) {
-    if (int rc = ft::launch_ffn_mfma(xs, d, d_ff, k, slots16, d_buf, d_off, d_perm, 0, E, T,
+    if (int rc = ft::launch_ffn_mfma(xs, T, d, d_ff, k, slots16, d_buf, d_off, d_perm, 0, E, P,
                                      c->wsp<uint16_t>(c->cv.h), c->wsp<float>(c->cv.out), cs, evs))
       return rc;
   } else {

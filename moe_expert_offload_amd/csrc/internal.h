@@ -106,9 +106,10 @@ int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
                     void* const* ev = nullptr, const int32_t* g_hi = nullptr);
 
 // MFMA tile grouped FFN: h bf16 [rows, d_ff] (in the fp32-sized workspace), out fp32 [rows, d].
-int launch_ffn_mfma(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
+// n_rows: rows of h and out (offsets[n_groups] at most; bounds the h reads)
+int launch_ffn_mfma(const uint16_t* x, int T, int d, int d_ff, int k, const uint16_t* slots,
                     const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
-                    int g_begin, int g_end, int max_rows, uint16_t* h, float* out, void* stream,
+                    int g_begin, int g_end, int n_rows, uint16_t* h, float* out, void* stream,
                     void* const* ev = nullptr);
 
 // ---- MXFP4 experts (kernels_mx.hip) ------------------------------------------------

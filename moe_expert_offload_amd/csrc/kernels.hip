@@ -1089,92 +1089,90 @@ __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
 //
 // Block: 256 threads = 4 waves, one per SIMD.  One pass covers up to 256 rows of
 // one expert (8 row subtiles of 32; the usual ~200 tokens of an 8k chunk in one
-// pass) and a column strip per wave: every weight element is read from HBM once
-// per pass, straight into the registers of the one wave that uses it.  Token rows
-// (operand A) are staged through LDS (three rotating buffers) and shared by the 4
-// waves.
-// K runs in stages of 64; inside a stage, MFMA i (0..3) takes in lane group g the
-// elements 32g + 8i .. +7, so a lane's weight data for a stage is 64 contiguous
-// bytes and A is read from LDS in the same order (the sum over k is unchanged).
-constexpr int XM = 256;       // rows per pass
-constexpr int XK = 64;        // K elements per stage
-constexpr int XLD = XK + 8;   // padded LDS row, in bf16 elements (144 B)
+// pass) and 256 weight rows ("B columns"), 64 per wave: every weight element is
+// read from HBM once per pass.  Both operands go straight from memory into LDS
+// (`buffer_load ... lds`, 16 bytes per lane, no registers in between): K runs in
+// stages of 32 elements through 4 buffers per operand ([256][32] bf16, 16 KB), the
+// loads of stage s + 3 in flight while stage s multiplies.  In a buffer, 16-byte
+// piece p of row r sits at piece p ^ ((r >> 1) & 3), so the 8 lanes of one LDS read
+// phase hit 8 different bank groups.  Inside a stage, MFMA slice i (0, 1) takes in
+// lane group g the elements 16i + 8g .. +7.
+//
+// The loop's loads are issued by inline asm and waited for by one explicit
+// `s_waitcnt vmcnt` per stage: the compiler's own waits drain every load at the
+// loop head and before any LDS read that follows an LDS-direct load.  The 8 loads
+// of a stage go out one after each MFMA pair, so their issue overlaps the MFMAs
+// instead of stalling the wavefront in front of them.
+constexpr int XM = 256;                 // rows per pass
+constexpr int XK = 32;                  // K elements per stage
+constexpr int XNB = 4;                  // buffers per operand
+constexpr int XB = XM * XK;             // one buffer, bf16 elements (16 KB)
 
-__device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* p) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+__device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* buf, int r, int piece) {
+  const uint4 u = *reinterpret_cast<const uint4*>(buf + r * XK + ((piece ^ ((r >> 1) & 3)) * 8));
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+// One 16-byte-per-lane load from buffer `rs` at byte offset off + kbytes into LDS
+// at byte address lds + 16 * lane.  Out-of-range offsets read zeros.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t kbytes, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(off), "s"(rs), "s"(kbytes) : "memory", "m0");
+}
 
-// Token-row staging of one stage: thread tid copies 16 B pieces (row tid/8 + 32j,
-// part tid%8) for j = 0..7.  Rows past the group's end read a valid row instead
-// (their products land in output rows that are never stored), so every load is
-// unconditional and the compiler can count outstanding loads exactly.
-struct RowStage {
-  const uint16_t* src[8];
-  uint4 v[8];
-  __device__ __forceinline__ void load(int k0) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = ld16(src[j] + k0);
-  }
-  __device__ __forceinline__ void store(uint16_t* buf, int tid) const {
-    uint16_t* dst = buf + (tid >> 3) * XLD + (tid & 7) * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(dst + 32 * j * XLD) = v[j];
-  }
-};
+// Load q (0..3) of wave w covers buffer rows 16 (4w + q) + lane/4, physical piece
+// lane%4; the lane's source piece is the logical one stored there.
+__device__ __forceinline__ int lds_load_row(int wave, int q, int lane) { return 16 * (4 * wave + q) + (lane >> 2); }
+__device__ __forceinline__ int lds_load_piece(int r, int lane) { return (lane & 3) ^ ((r >> 1) & 3); }
 
-// acc[a][c] += A(subtile a) x B(column subtile c) over one 64-element stage; w holds
-// the lane's 4 pieces for column subtile 0 then 4 for column subtile 1.  f0 holds the
-// A fragments of K slice 0 on entry; slice i + 1 is read from LDS while slice i
-// multiplies, and during the last slice the next stage's slice 0 is read from
-// sx_next into f0, so the MFMA pipe stays fed across the stage barrier.
-template <int NSUB>
-__device__ __forceinline__ void mfma_stage_bf16(f32x16_t (&acc)[8][2], const uint4 (&w)[8], const uint16_t* sx,
-                                                const uint16_t* sx_next, bf16x8_t (&f0)[NSUB], int lane) {
-  const int off = (lane & 31) * XLD + (lane >> 5) * 32;
-  const uint16_t* arow = sx + off;
-  const uint16_t* nrow = sx_next + off;
-  bf16x8_t f1[NSUB];
+// acc[a][c] += A(row subtile a) x B(column subtile c of this wave) over one stage.
+// Slice 1's operands are read from LDS while slice 0 multiplies; `issue(t)` sends
+// load t (0..7) of a later stage after the t-th MFMA pair.
+template <int NSUB, typename F>
+__device__ __forceinline__ void mfma_stage_bf16(f32x16_t (&acc)[8][2], const uint16_t* sa, const uint16_t* sb,
+                                                int wave, int lane, F&& issue) {
+  const int m = lane & 31, g = lane >> 5;
+  bf16x8_t fa[2][NSUB], fb[2][2];
+  fb[0][0] = lds_frag(sb, wave * 64 + m, g);
+  fb[0][1] = lds_frag(sb, wave * 64 + 32 + m, g);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bf16x8_t (&cur)[NSUB] = (i & 1) ? f1 : f0;
-    bf16x8_t (&nxt)[NSUB] = (i & 1) ? f0 : f1;
+  for (int a = 0; a < NSUB; ++a) fa[0][a] = lds_frag(sa, a * 32 + m, g);
 #pragma unroll
-    for (int a = 0; a < NSUB; ++a)
-      nxt[a] = lds_frag(i < 3 ? arow + a * 32 * XLD + 8 * (i + 1) : nrow + a * 32 * XLD);
-    const bf16x8_t b0 = as_bf16x8(w[i]);
-    const bf16x8_t b1 = as_bf16x8(w[4 + i]);
+  for (int i = 0; i < 2; ++i) {
 #pragma unroll
     for (int a = 0; a < NSUB; ++a) {
-      acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[a], b0, acc[a][0], 0, 0, 0);
-      acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[a], b1, acc[a][1], 0, 0, 0);
+      acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][a], fb[i][0], acc[a][0], 0, 0, 0);
+      acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][a], fb[i][1], acc[a][1], 0, 0, 0);
+      if (i == 0) {
+        if (a == 0) {
+          fb[1][0] = lds_frag(sb, wave * 64 + m, 2 + g);
+          fb[1][1] = lds_frag(sb, wave * 64 + 32 + m, 2 + g);
+        }
+        fa[1][a] = lds_frag(sa, a * 32 + m, 2 + g);
+        __builtin_amdgcn_sched_barrier(0);  // keep these reads here, ahead of slice 1
+      }
+      const int t = i * NSUB + a;
+      if (t < 8) issue(t);
     }
   }
-}
-
-__device__ __forceinline__ void load_w_stage(uint4 (&w)[8], const uint16_t* w0, const uint16_t* w1, int k0) {
+  if (2 * NSUB < 8) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    w[i] = ld16(w0 + k0 + 8 * i);
-    w[4 + i] = ld16(w1 + k0 + 8 * i);
+    for (int t = 2 * NSUB; t < 8; ++t) issue(t);
   }
 }
 
-constexpr int XBUF = XM * XLD;  // one LDS stage buffer, bf16 elements
-
-// Runs the K loop of one pass (K = kdim, a multiple of 64) with A from `rs` and the
-// lane's weight rows w0, w1 (already offset by 32 * lane group), for NSUB row
-// subtiles.  Token rows rotate through three LDS buffers: stage s computes from
-// buffer s%3 while stage s+2's rows are stored into buffer (s+2)%3, so the reads of
-// stage s+1 may start before the barrier that closes stage s.  Weights are
-// prefetched four stages ahead; prefetches past the last stage re-read it (clamped)
-// so the loop has no conditional loads.
+// K loop of one pass (kdim a multiple of 32).  rx/roff: token rows (this lane's 4
+// load offsets), rw/woff: weight rows.  Issue order: stages 0..2, then stage s
+// issues stage s + 3; at the top of stage s the 16 loads of stages s + 1 and s + 2
+// may still fly.  Loads past the last stage re-read it.
 template <int NSUB>
-__device__ __forceinline__ void mfma_pass_bf16(f32x16_t (&acc)[8][2], RowStage& rs, uint16_t* sx,
-                                               const uint16_t* w0, const uint16_t* w1, int kdim, int tid,
-                                               int lane) {
+__device__ __forceinline__ void mfma_pass_bf16(f32x16_t (&acc)[8][2], __amdgpu_buffer_rsrc_t rx,
+                                               const uint32_t (&roff)[4], __amdgpu_buffer_rsrc_t rw,
+                                               const uint32_t (&woff)[4], uint16_t* sx, uint16_t* sw, int kdim,
+                                               int wave, int lane) {
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
@@ -1182,90 +1180,98 @@ __device__ __forceinline__ void mfma_pass_bf16(f32x16_t (&acc)[8][2], RowStage& 
       acc[a][0][v] = 0.0f;
       acc[a][1][v] = 0.0f;
     }
-  // an opaque zero: the first weight loads of a pass would otherwise be hoisted out
-  // of the caller's row-pass loop and kept live (spilled) across it
-  int opaque = 0;
-  asm volatile("" : "+s"(opaque));
-  w0 += opaque;
-  w1 += opaque;
-  uint4 wr[4][8];
+  const uint32_t lx = (uint32_t)(uintptr_t)(lds_u16*)sx + (uint32_t)(4 * wave * 1024);
+  const uint32_t lw = (uint32_t)(uintptr_t)(lds_u16*)sw + (uint32_t)(4 * wave * 1024);
+  const uint32_t klast = (uint32_t)(kdim - XK) * 2u;
+  auto kb = [&](int st) { return min((uint32_t)st * (uint32_t)(XK * 2), klast); };
 #pragma unroll
-  for (int j = 0; j < 4; ++j) load_w_stage(wr[j], w0, w1, j * XK);
-  const int klast = kdim - XK;
-  rs.load(0);
-  rs.store(sx, tid);
-  rs.load(min(XK, klast));
-  rs.store(sx + XBUF, tid);
-  rs.load(min(2 * XK, klast));
-  __syncthreads();
-  bf16x8_t f0[NSUB];
-  {
-    const uint16_t* arow = sx + (lane & 31) * XLD + (lane >> 5) * 32;
+  for (int j = 0; j < XNB - 1; ++j) {
 #pragma unroll
-    for (int a = 0; a < NSUB; ++a) f0[a] = lds_frag(arow + a * 32 * XLD);
+    for (int q = 0; q < 4; ++q) lds_load16(rx, roff[q], kb(j), lx + (uint32_t)(j * XB * 2 + q * 1024));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lds_load16(rw, woff[q], kb(j), lw + (uint32_t)(j * XB * 2 + q * 1024));
   }
-  int b = 0;  // LDS buffer of the current stage
-  for (int k0 = 0; k0 < kdim; k0 += 4 * XK) {
+  const int nst = kdim / XK;
+  for (int s0 = 0; s0 < nst; s0 += XNB) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (k0 + j * XK >= kdim) break;
-      const int b1 = b == 2 ? 0 : b + 1, b2 = b1 == 2 ? 0 : b1 + 1;
-      rs.store(sx + b2 * XBUF, tid);                    // rows of stage s + 2
-      rs.load(min(k0 + (j + 3) * XK, klast));           // rows of stage s + 3
-      mfma_stage_bf16<NSUB>(acc, wr[j], sx + b * XBUF, sx + b1 * XBUF, f0, lane);
-      load_w_stage(wr[j], w0, w1, min(k0 + (j + 4) * XK, klast));
-      __syncthreads();
-      b = b1;
+    for (int j = 0; j < XNB; ++j) {
+      const int st = s0 + j;
+      if (st >= nst) break;
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"((XNB - 2) * 8) : "memory");
+      __syncthreads();  // every wave's loads of this stage have landed
+      const int nb = (j + XNB - 1) % XNB;  // the buffer stage s - 1 used, free after the barrier
+      const uint32_t kbn = kb(st + XNB - 1);
+      const uint32_t bx = lx + (uint32_t)(nb * XB * 2), bw = lw + (uint32_t)(nb * XB * 2);
+      mfma_stage_bf16<NSUB>(acc, sx + j * XB, sw + j * XB, wave, lane, [&](int t) {
+        if (t < 4)
+          lds_load16(rx, roff[t & 3], kbn, bx + (uint32_t)((t & 3) * 1024));
+        else
+          lds_load16(rw, woff[t & 3], kbn, bw + (uint32_t)((t & 3) * 1024));
+      });
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // the buffers are free for the next pass
 }
 
-__device__ __forceinline__ void mfma_pass_bf16_n(int nsub, f32x16_t (&acc)[8][2], RowStage& rs, uint16_t* sx,
-                                                 const uint16_t* w0, const uint16_t* w1, int kdim, int tid,
-                                                 int lane) {
+__device__ __forceinline__ void mfma_pass_bf16_n(int nsub, f32x16_t (&acc)[8][2], __amdgpu_buffer_rsrc_t rx,
+                                                 const uint32_t (&roff)[4], __amdgpu_buffer_rsrc_t rw,
+                                                 const uint32_t (&woff)[4], uint16_t* sx, uint16_t* sw, int kdim,
+                                                 int wave, int lane) {
   switch (nsub) {
-    case 1: mfma_pass_bf16<1>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
-    case 2: mfma_pass_bf16<2>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
-    case 3: mfma_pass_bf16<3>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
-    case 4: mfma_pass_bf16<4>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
-    case 5: mfma_pass_bf16<5>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
-    case 6: mfma_pass_bf16<6>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
-    case 7: mfma_pass_bf16<7>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
-    default: mfma_pass_bf16<8>(acc, rs, sx, w0, w1, kdim, tid, lane); break;
+    case 1: mfma_pass_bf16<1>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
+    case 2: mfma_pass_bf16<2>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
+    case 3: mfma_pass_bf16<3>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
+    case 4: mfma_pass_bf16<4>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
+    case 5: mfma_pass_bf16<5>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
+    case 6: mfma_pass_bf16<6>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
+    case 7: mfma_pass_bf16<7>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
+    default: mfma_pass_bf16<8>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
   }
 }
 
 // h[i][c] = silu(sum_k x[t_i][k] Wg[c][k]) * (sum_k x[t_i][k] Wu[c][k]) for the
 // 128 columns c of this block's strip (wave w: columns n0 + 32w .. +31 of both
-// W_gate and W_up), h in bf16.
+// W_gate and W_up, B columns 64w .. +31 and 64w + 32 .. +63 of the weight buffer),
+// h in bf16.
 __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(
-    const uint16_t* __restrict__ x, int d, int d_ff, int k, const uint16_t* __restrict__ slots,
+    const uint16_t* __restrict__ x, int T, int d, int d_ff, int k, const uint16_t* __restrict__ slots,
     size_t rec_elems, const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, int g_begin, int n_tiles, int n_blocks,
     uint16_t* __restrict__ h) {
-  __shared__ __attribute__((aligned(16))) uint16_t sX[3 * XBUF];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX[XNB * XB];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW[XNB * XB];
   const int lb = xcd_logical_block(blockIdx.x, n_blocks);
   const int g = g_begin + lb / n_tiles;
   const int n0 = (lb % n_tiles) * 128;
   const int r0 = offsets[g];
   const int n = offsets[g + 1] - r0;
   if (n <= 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), grp = lane >> 5;
   const uint16_t* rec = slots + (size_t)group_slot[g] * rec_elems;
+  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(rec, (uint32_t)((size_t)2 * d * d_ff * 2));
+  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x, (uint32_t)((size_t)T * d * 2));
+  uint32_t woff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int bc = lds_load_row(wave, q, lane);  // B column: wave bc/64, gate or up (bc/32)&1, column bc%32
+    const int wrow = ((bc >> 5) & 1) * d_ff + n0 + (bc >> 6) * 32 + (bc & 31);
+    woff[q] = (uint32_t)((size_t)wrow * d + lds_load_piece(bc, lane) * 8) * 2u;
+  }
   const int col = n0 + wave * 32 + (lane & 31);
-  const uint16_t* wg = rec + (size_t)col * d + grp * 32;
-  const uint16_t* wu = rec + (size_t)d_ff * d + (size_t)col * d + grp * 32;
   for (int m0 = 0; m0 < n; m0 += XM) {
     const int rows = min(XM, n - m0);
     const int nsub = (rows + 31) >> 5;
-    RowStage rs;
+    // rows past the group's end load a valid row; their products are never stored
+    uint32_t roff[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = min((tid >> 3) + 32 * j, rows - 1);
-      rs.src[j] = x + (size_t)(perm[r0 + m0 + r] / k) * d + (tid & 7) * 8;
+    for (int q = 0; q < 4; ++q) {
+      const int r = lds_load_row(wave, q, lane);
+      const int rr = min(r, rows - 1);
+      roff[q] = (uint32_t)((size_t)(perm[r0 + m0 + rr] / k) * d + lds_load_piece(r, lane) * 8) * 2u;
     }
     f32x16_t acc[8][2];
-    mfma_pass_bf16_n(nsub, acc, rs, sX, wg, wu, d, tid, lane);
+    mfma_pass_bf16_n(nsub, acc, rx, roff, rw, woff, sX, sW, d, wave, lane);
     int g4 = grp * 4;
     asm volatile("" : "+v"(g4));  // keeps the row indices below out of the prologue
 #pragma unroll
@@ -1284,32 +1290,40 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(
 // out[i][c] = sum_r h[i][r] Wd[c][r] for the 256 columns of this block's strip
 // (wave w: columns n0 + 64w .. +63), h rows in perm order.
 __global__ __launch_bounds__(256) void ffn_down_mfma_kernel(
-    int d, int d_ff, const uint16_t* __restrict__ slots, size_t rec_elems,
+    int P, int d, int d_ff, const uint16_t* __restrict__ slots, size_t rec_elems,
     const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, int g_begin,
     int n_tiles, int n_blocks, const uint16_t* __restrict__ h, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t sX[3 * XBUF];
+  __shared__ __attribute__((aligned(1024))) uint16_t sX[XNB * XB];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW[XNB * XB];
   const int lb = xcd_logical_block(blockIdx.x, n_blocks);
   const int g = g_begin + lb / n_tiles;
   const int n0 = (lb % n_tiles) * 256;
   const int r0 = offsets[g];
   const int n = offsets[g + 1] - r0;
   if (n <= 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), grp = lane >> 5;
   const uint16_t* wd = slots + (size_t)group_slot[g] * rec_elems + (size_t)2 * d_ff * d;
+  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(wd, (uint32_t)((size_t)d * d_ff * 2));
+  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(h, (uint32_t)((size_t)P * d_ff * 2));
+  uint32_t woff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int bc = lds_load_row(wave, q, lane);  // output column n0 + bc
+    woff[q] = (uint32_t)((size_t)(n0 + bc) * d_ff + lds_load_piece(bc, lane) * 8) * 2u;
+  }
   const int col = n0 + wave * 64 + (lane & 31);
-  const uint16_t* w0 = wd + (size_t)col * d_ff + grp * 32;
-  const uint16_t* w1 = w0 + (size_t)32 * d_ff;
   for (int m0 = 0; m0 < n; m0 += XM) {
     const int rows = min(XM, n - m0);
     const int nsub = (rows + 31) >> 5;
-    RowStage rs;
+    uint32_t roff[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = min((tid >> 3) + 32 * j, rows - 1);
-      rs.src[j] = h + (size_t)(r0 + m0 + r) * d_ff + (tid & 7) * 8;
+    for (int q = 0; q < 4; ++q) {
+      const int r = lds_load_row(wave, q, lane);
+      const int rr = min(r, rows - 1);
+      roff[q] = (uint32_t)((size_t)(r0 + m0 + rr) * d_ff + lds_load_piece(r, lane) * 8) * 2u;
     }
     f32x16_t acc[8][2];
-    mfma_pass_bf16_n(nsub, acc, rs, sX, w0, w1, d_ff, tid, lane);
+    mfma_pass_bf16_n(nsub, acc, rx, roff, rw, woff, sX, sW, d_ff, wave, lane);
     int g4 = grp * 4;
     asm volatile("" : "+v"(g4));  // keeps the row indices below out of the prologue
 #pragma unroll
@@ -1542,27 +1556,31 @@ int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
 #undef FT_ROWS_LAUNCH
 }
 
-int launch_ffn_mfma(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
+int launch_ffn_mfma(const uint16_t* x, int T, int d, int d_ff, int k, const uint16_t* slots,
                     const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
-                    int g_begin, int g_end, int /*max_rows*/, uint16_t* h, float* out,
+                    int g_begin, int g_end, int n_rows, uint16_t* h, float* out,
                     void* stream, void* const* ev) {
-  if (d % 256 != 0 || d_ff % 128 != 0 || k < 1)
+  if (d % 256 != 0 || d_ff % 128 != 0 || k < 1 || T < 0 || n_rows < 0)
     return fail(FT_EINVAL, "ffn_mfma: need d%256==0 and d_ff%128==0");
   const int ng = g_end - g_begin;
   if (ng <= 0) return FT_OK;
   if (!aligned16(x) || !aligned16(slots) || !aligned16(h) || !aligned16(out))
     return fail(FT_EINVAL, "ffn_mfma: unaligned pointer");
+  // the kernels address x, h and a record through 32-bit buffer offsets
+  const size_t lim = (size_t)1 << 31;
+  if ((size_t)T * d * 2 >= lim || (size_t)n_rows * d_ff * 2 >= lim || (size_t)3 * d * d_ff * 2 >= lim)
+    return fail(FT_EINVAL, "ffn_mfma: x, h or a record over 2 GiB");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t rec_elems = (size_t)3 * d * d_ff;
   const int tiles_up = d_ff / 128;
   const int nb_up = ng * tiles_up;
-  timed_launch(ffn_gateup_mfma_kernel, dim3(nb_up), dim3(256), s, ev, 0, x, d, d_ff, k, slots, rec_elems,
+  timed_launch(ffn_gateup_mfma_kernel, dim3(nb_up), dim3(256), s, ev, 0, x, T, d, d_ff, k, slots, rec_elems,
                group_slot, offsets, perm, g_begin, tiles_up, nb_up, h);
   if (int rc = launched("ffn_gateup_mfma")) return rc;
   const int tiles_dn = d / 256;
   const int nb_dn = ng * tiles_dn;
-  timed_launch(ffn_down_mfma_kernel, dim3(nb_dn), dim3(256), s, ev, 1, d, d_ff, slots, rec_elems, group_slot,
-               offsets, g_begin, tiles_dn, nb_dn, (const uint16_t*)h, out);
+  timed_launch(ffn_down_mfma_kernel, dim3(nb_dn), dim3(256), s, ev, 1, n_rows, d, d_ff, slots, rec_elems,
+               group_slot, offsets, g_begin, tiles_dn, nb_dn, (const uint16_t*)h, out);
   return launched("ffn_down_mfma");
 }
 
