@@ -94,6 +94,9 @@ __device__ __forceinline__ float dot8_f(uint4 a, float4 h0, float4 h1, float acc
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// The same through the hardware exp2 and reciprocal (a few ulp), for values that are
+// rounded to bf16 right after (the prefill MFMA epilogue).
+__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Blocks are dealt to the 8 XCDs round-robin; remap so that consecutive logical
 // blocks share an XCD (and its L2).
@@ -1281,7 +1284,7 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(
       for (int v = 0; v < 16; ++v) {
         const int row = a * 32 + (v >> 2) * 8 + g4 + (v & 3);
         if (row < rows)
-          h[(size_t)(r0 + m0 + row) * d_ff + col] = f32_to_bf16_rne(silu(acc[a][0][v]) * acc[a][1][v]);
+          h[(size_t)(r0 + m0 + row) * d_ff + col] = f32_to_bf16_rne(silu_fast(acc[a][0][v]) * acc[a][1][v]);
       }
     }
   }

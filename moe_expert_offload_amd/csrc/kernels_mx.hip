@@ -45,6 +45,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// The same through the hardware exp2 and reciprocal (a few ulp), for values that are
+// converted to MXFP8 right after (the prefill MFMA epilogue).
+__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // 2^(s - 127) for an E8M0 byte (s < 255).
 __device__ __forceinline__ float e8m0(uint32_t s) { return s ? __uint_as_float(s << 23) : 1.17549435e-38f * 0.5f; }
@@ -605,7 +608,7 @@ __global__ __launch_bounds__(256) void mx_gateup_mfma_kernel(
       if (a >= nsub) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        tile[((v >> 2) * 8 + g4 + (v & 3)) * 36 + (lane & 31)] = silu(acc[a][0][v]) * acc[a][1][v];
+        tile[((v >> 2) * 8 + g4 + (v & 3)) * 36 + (lane & 31)] = silu_fast(acc[a][0][v]) * acc[a][1][v];
       float hv[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
