@@ -1167,15 +1167,133 @@ __device__ __forceinline__ void mfma_stage_bf16(f32x16_t (&acc)[8][2], const uin
   }
 }
 
-// K loop of one pass (kdim a multiple of 32).  rx/roff: token rows (this lane's 4
-// load offsets), rw/woff: weight rows.  Issue order: stages 0..2, then stage s
-// issues stage s + 3; at the top of stage s the 16 loads of stages s + 1 and s + 2
-// may still fly.  Loads past the last stage re-read it.
+// The grid is persistent: a block takes logical blocks b, b + grid, b + 2 grid, ...
+// (in the XCD-aware order, so the tiles running on one XCD at a time belong to few
+// experts and share its L2), each split into passes of up to XM rows; a pass is one
+// "item".  The loads of every stage go out three stages ahead across item boundaries,
+// so the first stages of the next item are in flight while the current one finishes
+// and runs its epilogue.
+struct MfmaArgs {
+  const uint16_t* x;       // gate/up: token rows [T][d]
+  const uint16_t* h;       // down: h rows [n_rows][d_ff] in perm order
+  const uint16_t* slots;
+  const int32_t* group_slot;
+  const int32_t* offsets;
+  const int32_t* perm;
+  uint16_t* h_out;         // gate/up output
+  float* out;              // down output
+  size_t rec_elems;
+  int T, n_rows, d, d_ff, k, g_begin, n_tiles, n_blocks;
+};
+
+struct MfmaItem {
+  int g, n0, r0, m0, rows, nsub;
+  __amdgpu_buffer_rsrc_t rw;  // the group's weight rows
+  uint32_t roff[4], woff[4];  // this lane's load offsets (bytes, stage 0)
+};
+
+// Advances (i, m0) over this block's passes and sets up the next item; false at the end.
+template <bool DOWN>
+__device__ __forceinline__ bool next_item(const MfmaArgs& A, int& i, int& m0, MfmaItem& it, int wave, int lane) {
+  const int tile = DOWN ? 256 : 128;
+  for (;;) {
+    const int hb = blockIdx.x + i * gridDim.x;
+    if (hb >= A.n_blocks) return false;
+    const int lb = xcd_logical_block(hb, A.n_blocks);
+    const int g = A.g_begin + lb / A.n_tiles;
+    const int r0 = A.offsets[g];
+    const int n = A.offsets[g + 1] - r0;
+    if (m0 >= n) {  // this logical block is done (or empty): the next one
+      ++i;
+      m0 = 0;
+      continue;
+    }
+    it.g = g;
+    it.n0 = (lb % A.n_tiles) * tile;
+    it.r0 = r0;
+    it.m0 = m0;
+    it.rows = min(XM, n - m0);
+    it.nsub = (it.rows + 31) >> 5;
+    const uint16_t* rec = A.slots + (size_t)A.group_slot[g] * A.rec_elems;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int bc = lds_load_row(wave, q, lane);
+      const int r = bc, rr = min(r, it.rows - 1);  // rows past the end load a valid row
+      if (DOWN) {  // B column bc is output column n0 + bc
+        it.woff[q] = (uint32_t)((size_t)(it.n0 + bc) * A.d_ff + lds_load_piece(bc, lane) * 8) * 2u;
+        it.roff[q] = (uint32_t)((size_t)(r0 + m0 + rr) * A.d_ff + lds_load_piece(r, lane) * 8) * 2u;
+      } else {  // B column bc: wave bc/64, gate or up (bc/32)&1, column bc%32
+        const int wrow = ((bc >> 5) & 1) * A.d_ff + it.n0 + (bc >> 6) * 32 + (bc & 31);
+        it.woff[q] = (uint32_t)((size_t)wrow * A.d + lds_load_piece(bc, lane) * 8) * 2u;
+        it.roff[q] = (uint32_t)((size_t)(A.perm[r0 + m0 + rr] / A.k) * A.d + lds_load_piece(r, lane) * 8) * 2u;
+      }
+    }
+    it.rw = DOWN ? buf_rsrc(rec + (size_t)2 * A.d_ff * A.d, (uint32_t)((size_t)A.d * A.d_ff * 2))
+                 : buf_rsrc(rec, (uint32_t)((size_t)2 * A.d * A.d_ff * 2));
+    m0 += XM;
+    return true;
+  }
+}
+
+// Writes one item's results from the accumulators.
+template <bool DOWN>
+__device__ __forceinline__ void mfma_epilogue(const MfmaArgs& A, const MfmaItem& it, const f32x16_t (&acc)[8][2],
+                                              int wave, int lane) {
+  int g4 = (lane >> 5) * 4;
+  asm volatile("" : "+v"(g4));  // keeps the row indices below out of the loop
+  if (DOWN) {  // wave w: columns n0 + 64w .. +63
+    const int col = it.n0 + wave * 64 + (lane & 31);
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      if (a >= it.nsub) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = a * 32 + (v >> 2) * 8 + g4 + (v & 3);
+        if (row < it.rows) {
+          float* o = A.out + (size_t)(it.r0 + it.m0 + row) * A.d + col;
+          o[0] = acc[a][0][v];
+          o[32] = acc[a][1][v];
+        }
+      }
+    }
+  } else {  // wave w: columns n0 + 32w .. +31 of both W_gate and W_up
+    const int col = it.n0 + wave * 32 + (lane & 31);
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      if (a >= it.nsub) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = a * 32 + (v >> 2) * 8 + g4 + (v & 3);
+        if (row < it.rows)
+          A.h_out[(size_t)(it.r0 + it.m0 + row) * A.d_ff + col] =
+              f32_to_bf16_rne(silu_fast(acc[a][0][v]) * acc[a][1][v]);
+      }
+    }
+  }
+}
+
+// Load t (0..7) of stage st of item it, into buffer st % XNB (lx, lw: this wave's part
+// of the row and weight buffers).
+__device__ __forceinline__ void mfma_load(__amdgpu_buffer_rsrc_t rx, const MfmaItem& it, int st, int t,
+                                          uint32_t klast, uint32_t lx, uint32_t lw) {
+  const uint32_t kbyte = min((uint32_t)st * (uint32_t)(XK * 2), klast);
+  const uint32_t b = (uint32_t)((st % XNB) * XB * 2);
+  if (t < 4)
+    lds_load16(rx, it.roff[t & 3], kbyte, lx + b + (uint32_t)((t & 3) * 1024));
+  else
+    lds_load16(it.rw, it.woff[t & 3], kbyte, lw + b + (uint32_t)((t & 3) * 1024));
+}
+
+// The K loop of one item (kdim a multiple of 128, so every item starts in buffer 0),
+// its first XNB - 1 stages already issued.  Stage s issues stage s + 3 of this item or,
+// past its end, of the next one (re-reading this item's last stage when there is
+// none); at the top of stage s its own loads are older than the 16 of the next two
+// stages.  Anything else the compiler issues in between only adds newer operations,
+// which keeps the count safe.
 template <int NSUB>
-__device__ __forceinline__ void mfma_pass_bf16(f32x16_t (&acc)[8][2], __amdgpu_buffer_rsrc_t rx,
-                                               const uint32_t (&roff)[4], __amdgpu_buffer_rsrc_t rw,
-                                               const uint32_t (&woff)[4], uint16_t* sx, uint16_t* sw, int kdim,
-                                               int wave, int lane) {
+__device__ __forceinline__ void mfma_item_bf16(f32x16_t (&acc)[8][2], __amdgpu_buffer_rsrc_t rx, const MfmaItem& cur,
+                                               const MfmaItem& nxt, bool has_nxt, uint16_t* sx, uint16_t* sw,
+                                               int kdim, int wave, int lane, uint32_t lx, uint32_t lw) {
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
@@ -1183,166 +1301,77 @@ __device__ __forceinline__ void mfma_pass_bf16(f32x16_t (&acc)[8][2], __amdgpu_b
       acc[a][0][v] = 0.0f;
       acc[a][1][v] = 0.0f;
     }
-  const uint32_t lx = (uint32_t)(uintptr_t)(lds_u16*)sx + (uint32_t)(4 * wave * 1024);
-  const uint32_t lw = (uint32_t)(uintptr_t)(lds_u16*)sw + (uint32_t)(4 * wave * 1024);
-  const uint32_t klast = (uint32_t)(kdim - XK) * 2u;
-  auto kb = [&](int st) { return min((uint32_t)st * (uint32_t)(XK * 2), klast); };
-#pragma unroll
-  for (int j = 0; j < XNB - 1; ++j) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lds_load16(rx, roff[q], kb(j), lx + (uint32_t)(j * XB * 2 + q * 1024));
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lds_load16(rw, woff[q], kb(j), lw + (uint32_t)(j * XB * 2 + q * 1024));
-  }
   const int nst = kdim / XK;
+  const uint32_t klast = (uint32_t)(kdim - XK) * 2u;
   for (int s0 = 0; s0 < nst; s0 += XNB) {
 #pragma unroll
     for (int j = 0; j < XNB; ++j) {
       const int st = s0 + j;
-      if (st >= nst) break;
       asm volatile("s_waitcnt vmcnt(%0)" :: "n"((XNB - 2) * 8) : "memory");
-      __syncthreads();  // every wave's loads of this stage have landed
-      const int nb = (j + XNB - 1) % XNB;  // the buffer stage s - 1 used, free after the barrier
-      const uint32_t kbn = kb(st + XNB - 1);
-      const uint32_t bx = lx + (uint32_t)(nb * XB * 2), bw = lw + (uint32_t)(nb * XB * 2);
-      mfma_stage_bf16<NSUB>(acc, sx + j * XB, sw + j * XB, wave, lane, [&](int t) {
-        if (t < 4)
-          lds_load16(rx, roff[t & 3], kbn, bx + (uint32_t)((t & 3) * 1024));
-        else
-          lds_load16(rw, woff[t & 3], kbn, bw + (uint32_t)((t & 3) * 1024));
-      });
+      __syncthreads();  // every wave's loads of this stage have landed; stage s - 1 is done
+      const int sn = st + XNB - 1;
+      const bool in_cur = sn < nst || !has_nxt;
+      const MfmaItem& it = in_cur ? cur : nxt;
+      const int sl = in_cur ? sn : sn - nst;
+      mfma_stage_bf16<NSUB>(acc, sx + j * XB, sw + j * XB, wave, lane,
+                            [&](int t) { mfma_load(rx, it, sl, t, klast, lx, lw); });
     }
+  }
+}
+
+template <bool DOWN>
+__device__ __forceinline__ void mfma_persistent(const MfmaArgs& A, uint16_t* sx, uint16_t* sw) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kdim = DOWN ? A.d_ff : A.d;
+  const __amdgpu_buffer_rsrc_t rx = DOWN ? buf_rsrc(A.h, (uint32_t)((size_t)A.n_rows * A.d_ff * 2))
+                                         : buf_rsrc(A.x, (uint32_t)((size_t)A.T * A.d * 2));
+  int ci = 0, cm = 0;  // cursor over this block's passes
+  MfmaItem cur, nxt;
+  if (!next_item<DOWN>(A, ci, cm, cur, wave, lane)) return;  // block-uniform
+  bool has_nxt = next_item<DOWN>(A, ci, cm, nxt, wave, lane);
+  const uint32_t lx = (uint32_t)(uintptr_t)(lds_u16*)sx + (uint32_t)(4 * wave * 1024);
+  const uint32_t lw = (uint32_t)(uintptr_t)(lds_u16*)sw + (uint32_t)(4 * wave * 1024);
+  const uint32_t klast = (uint32_t)(kdim - XK) * 2u;
+#pragma unroll
+  for (int j = 0; j < XNB - 1; ++j)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) mfma_load(rx, cur, j, t, klast, lx, lw);
+  for (;;) {
+    f32x16_t acc[8][2];
+    switch (cur.nsub) {
+      case 1: mfma_item_bf16<1>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
+      case 2: mfma_item_bf16<2>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
+      case 3: mfma_item_bf16<3>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
+      case 4: mfma_item_bf16<4>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
+      case 5: mfma_item_bf16<5>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
+      case 6: mfma_item_bf16<6>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
+      case 7: mfma_item_bf16<7>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
+      default: mfma_item_bf16<8>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
+    }
+    mfma_epilogue<DOWN>(A, cur, acc, wave, lane);  // the next item's first stages are in flight
+    if (!has_nxt) break;
+    cur = nxt;
+    has_nxt = next_item<DOWN>(A, ci, cm, nxt, wave, lane);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();  // the buffers are free for the next pass
+  __syncthreads();  // no LDS load is left in flight when the block ends
 }
 
-__device__ __forceinline__ void mfma_pass_bf16_n(int nsub, f32x16_t (&acc)[8][2], __amdgpu_buffer_rsrc_t rx,
-                                                 const uint32_t (&roff)[4], __amdgpu_buffer_rsrc_t rw,
-                                                 const uint32_t (&woff)[4], uint16_t* sx, uint16_t* sw, int kdim,
-                                                 int wave, int lane) {
-  switch (nsub) {
-    case 1: mfma_pass_bf16<1>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
-    case 2: mfma_pass_bf16<2>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
-    case 3: mfma_pass_bf16<3>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
-    case 4: mfma_pass_bf16<4>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
-    case 5: mfma_pass_bf16<5>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
-    case 6: mfma_pass_bf16<6>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
-    case 7: mfma_pass_bf16<7>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
-    default: mfma_pass_bf16<8>(acc, rx, roff, rw, woff, sx, sw, kdim, wave, lane); break;
-  }
-}
-
-// h[i][c] = silu(sum_k x[t_i][k] Wg[c][k]) * (sum_k x[t_i][k] Wu[c][k]) for the
-// 128 columns c of this block's strip (wave w: columns n0 + 32w .. +31 of both
-// W_gate and W_up, B columns 64w .. +31 and 64w + 32 .. +63 of the weight buffer),
-// h in bf16.
-__global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(
-    const uint16_t* __restrict__ x, int T, int d, int d_ff, int k, const uint16_t* __restrict__ slots,
-    size_t rec_elems, const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ perm, int g_begin, int n_tiles, int n_blocks,
-    uint16_t* __restrict__ h) {
+// h[i][c] = silu(sum_k x[t_i][k] Wg[c][k]) * (sum_k x[t_i][k] Wu[c][k]) for the 128
+// columns c of each strip (wave w: columns n0 + 32w .. +31 of both W_gate and W_up,
+// B columns 64w .. +31 and 64w + 32 .. +63 of the weight buffer), h in bf16.
+__global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(MfmaArgs A) {
   __shared__ __attribute__((aligned(1024))) uint16_t sX[XNB * XB];
   __shared__ __attribute__((aligned(1024))) uint16_t sW[XNB * XB];
-  const int lb = xcd_logical_block(blockIdx.x, n_blocks);
-  const int g = g_begin + lb / n_tiles;
-  const int n0 = (lb % n_tiles) * 128;
-  const int r0 = offsets[g];
-  const int n = offsets[g + 1] - r0;
-  if (n <= 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), grp = lane >> 5;
-  const uint16_t* rec = slots + (size_t)group_slot[g] * rec_elems;
-  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(rec, (uint32_t)((size_t)2 * d * d_ff * 2));
-  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x, (uint32_t)((size_t)T * d * 2));
-  uint32_t woff[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int bc = lds_load_row(wave, q, lane);  // B column: wave bc/64, gate or up (bc/32)&1, column bc%32
-    const int wrow = ((bc >> 5) & 1) * d_ff + n0 + (bc >> 6) * 32 + (bc & 31);
-    woff[q] = (uint32_t)((size_t)wrow * d + lds_load_piece(bc, lane) * 8) * 2u;
-  }
-  const int col = n0 + wave * 32 + (lane & 31);
-  for (int m0 = 0; m0 < n; m0 += XM) {
-    const int rows = min(XM, n - m0);
-    const int nsub = (rows + 31) >> 5;
-    // rows past the group's end load a valid row; their products are never stored
-    uint32_t roff[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = lds_load_row(wave, q, lane);
-      const int rr = min(r, rows - 1);
-      roff[q] = (uint32_t)((size_t)(perm[r0 + m0 + rr] / k) * d + lds_load_piece(r, lane) * 8) * 2u;
-    }
-    f32x16_t acc[8][2];
-    mfma_pass_bf16_n(nsub, acc, rx, roff, rw, woff, sX, sW, d, wave, lane);
-    int g4 = grp * 4;
-    asm volatile("" : "+v"(g4));  // keeps the row indices below out of the prologue
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      if (a >= nsub) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = a * 32 + (v >> 2) * 8 + g4 + (v & 3);
-        if (row < rows)
-          h[(size_t)(r0 + m0 + row) * d_ff + col] = f32_to_bf16_rne(silu_fast(acc[a][0][v]) * acc[a][1][v]);
-      }
-    }
-  }
+  mfma_persistent<false>(A, sX, sW);
 }
 
-// out[i][c] = sum_r h[i][r] Wd[c][r] for the 256 columns of this block's strip
-// (wave w: columns n0 + 64w .. +63), h rows in perm order.
-__global__ __launch_bounds__(256) void ffn_down_mfma_kernel(
-    int P, int d, int d_ff, const uint16_t* __restrict__ slots, size_t rec_elems,
-    const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, int g_begin,
-    int n_tiles, int n_blocks, const uint16_t* __restrict__ h, float* __restrict__ out) {
+// out[i][c] = sum_r h[i][r] Wd[c][r] for the 256 columns of each strip (wave w:
+// columns n0 + 64w .. +63), h rows in perm order.
+__global__ __launch_bounds__(256) void ffn_down_mfma_kernel(MfmaArgs A) {
   __shared__ __attribute__((aligned(1024))) uint16_t sX[XNB * XB];
   __shared__ __attribute__((aligned(1024))) uint16_t sW[XNB * XB];
-  const int lb = xcd_logical_block(blockIdx.x, n_blocks);
-  const int g = g_begin + lb / n_tiles;
-  const int n0 = (lb % n_tiles) * 256;
-  const int r0 = offsets[g];
-  const int n = offsets[g + 1] - r0;
-  if (n <= 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), grp = lane >> 5;
-  const uint16_t* wd = slots + (size_t)group_slot[g] * rec_elems + (size_t)2 * d_ff * d;
-  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(wd, (uint32_t)((size_t)d * d_ff * 2));
-  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(h, (uint32_t)((size_t)P * d_ff * 2));
-  uint32_t woff[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int bc = lds_load_row(wave, q, lane);  // output column n0 + bc
-    woff[q] = (uint32_t)((size_t)(n0 + bc) * d_ff + lds_load_piece(bc, lane) * 8) * 2u;
-  }
-  const int col = n0 + wave * 64 + (lane & 31);
-  for (int m0 = 0; m0 < n; m0 += XM) {
-    const int rows = min(XM, n - m0);
-    const int nsub = (rows + 31) >> 5;
-    uint32_t roff[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = lds_load_row(wave, q, lane);
-      const int rr = min(r, rows - 1);
-      roff[q] = (uint32_t)((size_t)(r0 + m0 + rr) * d_ff + lds_load_piece(r, lane) * 8) * 2u;
-    }
-    f32x16_t acc[8][2];
-    mfma_pass_bf16_n(nsub, acc, rx, roff, rw, woff, sX, sW, d_ff, wave, lane);
-    int g4 = grp * 4;
-    asm volatile("" : "+v"(g4));  // keeps the row indices below out of the prologue
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      if (a >= nsub) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = a * 32 + (v >> 2) * 8 + g4 + (v & 3);
-        if (row < rows) {
-          float* o = out + (size_t)(r0 + m0 + row) * d + col;
-          o[0] = acc[a][0][v];
-          o[32] = acc[a][1][v];
-        }
-      }
-    }
-  }
+  mfma_persistent<true>(A, sX, sW);
 }
 
 // ============================================================================
@@ -1573,17 +1602,38 @@ int launch_ffn_mfma(const uint16_t* x, int T, int d, int d_ff, int k, const uint
   const size_t lim = (size_t)1 << 31;
   if ((size_t)T * d * 2 >= lim || (size_t)n_rows * d_ff * 2 >= lim || (size_t)3 * d * d_ff * 2 >= lim)
     return fail(FT_EINVAL, "ffn_mfma: x, h or a record over 2 GiB");
+  // one block per compute unit (128 KB of LDS each), a multiple of the 8 XCDs
+  static int n_cu = 0;
+  if (n_cu <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+      n_cu = 256;
+  }
+  auto grid_for = [&](int nb) { return nb <= n_cu ? nb : (n_cu / 8) * 8; };
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t rec_elems = (size_t)3 * d * d_ff;
-  const int tiles_up = d_ff / 128;
-  const int nb_up = ng * tiles_up;
-  timed_launch(ffn_gateup_mfma_kernel, dim3(nb_up), dim3(256), s, ev, 0, x, T, d, d_ff, k, slots, rec_elems,
-               group_slot, offsets, perm, g_begin, tiles_up, nb_up, h);
+  MfmaArgs A{};
+  A.x = x;
+  A.h = h;
+  A.slots = slots;
+  A.group_slot = group_slot;
+  A.offsets = offsets;
+  A.perm = perm;
+  A.h_out = h;
+  A.out = out;
+  A.rec_elems = (size_t)3 * d * d_ff;
+  A.T = T;
+  A.n_rows = n_rows;
+  A.d = d;
+  A.d_ff = d_ff;
+  A.k = k;
+  A.g_begin = g_begin;
+  A.n_tiles = d_ff / 128;
+  A.n_blocks = ng * A.n_tiles;
+  timed_launch(ffn_gateup_mfma_kernel, dim3(grid_for(A.n_blocks)), dim3(256), s, ev, 0, A);
   if (int rc = launched("ffn_gateup_mfma")) return rc;
-  const int tiles_dn = d / 256;
-  const int nb_dn = ng * tiles_dn;
-  timed_launch(ffn_down_mfma_kernel, dim3(nb_dn), dim3(256), s, ev, 1, n_rows, d, d_ff, slots, rec_elems,
-               group_slot, offsets, g_begin, tiles_dn, nb_dn, (const uint16_t*)h, out);
+  A.n_tiles = d / 256;
+  A.n_blocks = ng * A.n_tiles;
+  timed_launch(ffn_down_mfma_kernel, dim3(grid_for(A.n_blocks)), dim3(256), s, ev, 1, A);
   return launched("ffn_down_mfma");
 }
 

@@ -138,6 +138,13 @@ def test_grouped_ffn_mfma_form(d, d_ff, rows):
     _ffn_case(2, d, d_ff, rows)
 
 
+@pytest.mark.parametrize("split", [None, 150])
+def test_grouped_ffn_mfma_form_more_tiles_than_blocks(split):
+    """300 groups of one tile each: more tiles than compute units, so every block of the
+    persistent MFMA kernels runs several (and empty groups are skipped in between)."""
+    _ffn_case(2, 256, 128, [(i * 37) % 70 for i in range(300)], split=split)
+
+
 @pytest.mark.parametrize("with_cpu,k", [(False, 3), (True, 3), (True, 8)])
 def test_combine(with_cpu, k):
     torch = torch_mod()
