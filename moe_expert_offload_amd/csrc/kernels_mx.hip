@@ -523,6 +523,13 @@ __device__ __forceinline__ void mx_mfma_pass(f32x16_t (&acc)[8][2], QRowStage& r
       rs.load(min(k0 + (j + 3) * QK, klast));           // rows of stage s + 3
       mx_mfma_stage<NSUB>(acc, wr[j], sx + b * QBUF, ss + b * QM, sx + b1 * QBUF, ss + b1 * QM, q0, lane);
       load_qw(wr[j], c0, c1, s0, s1, min(k0 + (j + QDEPTH) * QK, klast));
+      // the stage's 15 global loads (9 row pieces, 6 weight pieces) one between each two
+      // MFMAs, so that their issue overlaps the MFMAs instead of queueing in front of them
+#pragma unroll
+      for (int i = 0; i < 15; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
       __syncthreads();
       b = b1;
     }
