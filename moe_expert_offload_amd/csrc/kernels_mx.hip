@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256) void mx_quant_act_kernel(const In* __restrict_
 // Block: 256 threads = 4 waves, one per SIMD.  One pass covers up to 256 rows of one
 // expert (8 row subtiles of 32) and a column strip per wave, so every weight byte is
 // read from HBM once per pass, straight into the registers of the one wave that uses
-// it (prefetched four stages ahead).  Token rows (MXFP8 codes and their scales) are
+// it (prefetched three stages ahead).  Token rows (MXFP8 codes and their scales) are
 // staged through LDS (three rotating buffers) and shared by the 4 waves.
 // K runs in stages of 128 elements = two scaled MFMAs.  MFMA i (0, 1) of a stage
 // takes as its K positions 0..31 the stage's block i and as positions 32..63 its
@@ -377,7 +377,7 @@ constexpr int QM = 256;        // rows per pass
 constexpr int QK = 128;        // K elements per stage
 constexpr int QLD = QK + 16;   // padded LDS row of fp8 codes (bytes)
 #ifndef QDEPTH
-#define QDEPTH 4               // weight stages in flight
+#define QDEPTH 3               // weight stages in flight
 #endif
 
 __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
