@@ -25,11 +25,18 @@ void ExpertCache::resize(int n_slots) {
   std::fill(where_.begin(), where_.end(), -1);
   buf_[0].clear();
   buf_[1].clear();
+  buf_layer_[0] = buf_layer_[1] = -1;
   prefill_open_ = false;
   on_demand_ = false;
   const int64_t resizes = stats.resizes;
   stats = ft_stats{};
   stats.resizes = resizes;
+}
+
+void ExpertCache::clear_residency() {
+  std::fill(slot_key_.begin(), slot_key_.end(), kEmpty);
+  std::fill(slot_stamp_.begin(), slot_stamp_.end(), -1);
+  std::fill(where_.begin(), where_.end(), -1);
 }
 
 int32_t ExpertCache::where(int layer, int e) const {
@@ -168,6 +175,7 @@ int ExpertCache::prefill_begin() {
   if ((int)order.size() < 2 * E_) return fail(FT_ECAP, "not enough slots for two prefill buffers");
   buf_[0].assign(order.begin(), order.begin() + E_);
   buf_[1].assign(order.begin() + E_, order.begin() + 2 * E_);
+  buf_layer_[0] = buf_layer_[1] = -1;
   for (int s : order) {
     if (slot_key_[s] >= 0) where_[slot_key_[s]] = -1;
     slot_key_[s] = kReserved;
@@ -248,19 +256,38 @@ int32_t ExpertCache::prefill_slot(int layer, int e) const {
   return buf_[layer & 1][e];
 }
 
-void ExpertCache::prefill_end(int L) {
+void ExpertCache::prefill_set_buffer_layer(int b, int layer) {
+  if (b < 0 || b > 1) return;
+  buf_layer_[b] = (layer >= 0 && layer < L_) ? layer : -1;
+}
+
+void ExpertCache::prefill_end_full_pass() {
+  if (prefill_open_ && !on_demand_) {
+    if (L_ >= 2) prefill_set_buffer_layer((L_ - 2) & 1, L_ - 2);
+    prefill_set_buffer_layer((L_ - 1) & 1, L_ - 1);
+  }
+  prefill_end();
+}
+
+void ExpertCache::prefill_end() {
   if (!prefill_open_) return;
   if (on_demand_) {  // residency was updated layer by layer
     prefill_open_ = false;
     on_demand_ = false;
     return;
   }
+  // [FT] §3.1: layer l+1 streams into the other buffer while layer l computes, so a
+  // buffer may hold a layer that was loaded but never computed (a pass ended early);
+  // what each buffer holds is what survives, in ascending layer order
+  int order[2] = {0, 1};
+  if (buf_layer_[1] >= 0 && (buf_layer_[0] < 0 || buf_layer_[1] < buf_layer_[0])) std::swap(order[0], order[1]);
   std::vector<uint8_t> used(n_, 0);
-  for (int layer = L - 2; layer <= L - 1; ++layer) {
+  for (int b : order) {
+    const int layer = buf_layer_[b];
     if (layer < 0) continue;
-    const std::vector<int32_t>& b = buf_[layer & 1];
+    const std::vector<int32_t>& buf = buf_[b];
     for (int e = 0; e < E_; ++e) {
-      const int s = b[e];
+      const int s = buf[e];
       const size_t key = (size_t)layer * E_ + e;
       const int32_t old = where_[key];
       if (old >= 0 && old != s) {
@@ -281,6 +308,7 @@ void ExpertCache::prefill_end(int L) {
       }
   buf_[0].clear();
   buf_[1].clear();
+  buf_layer_[0] = buf_layer_[1] = -1;
   prefill_open_ = false;
 }
 

@@ -43,9 +43,22 @@ class ExpertCache {
   int32_t prefill_slot(int layer, int e) const;
   const std::vector<int32_t>& prefill_buffer(int b) const { return buf_[b]; }
   bool prefill_open() const { return prefill_open_; }
-  void prefill_end(int L);
+  // Which layer's records buffer b holds once its issued loads land (-1: none, or a
+  // load that was not issued completely).  Set as loads are issued.
+  void prefill_set_buffer_layer(int b, int layer);
+  int prefill_buffer_layer(int b) const { return buf_layer_[b]; }
+  // Ends the prefill.  Double-buffered: the layer each buffer holds becomes resident
+  // (ascending layer order, e ascending, each touching the clock; a copy of the same
+  // key elsewhere is emptied); buffer slots holding no layer become empty.
+  void prefill_end();
+  // A whole pass in a context that issues no loads (residency only): the buffers
+  // end holding layers L-2 and L-1, as after a full pass, then prefill_end().
+  void prefill_end_full_pass();
 
   void resize(int n_slots);  // all slots empty, counters reset, clock kept
+  // All slots empty, counters and clock kept: for when the slots' contents can no
+  // longer be trusted (the device acted on decisions the host did not take).
+  void clear_residency();
   int32_t where(int layer, int e) const;
 
   // the whole state, for a copy in device memory
@@ -67,6 +80,7 @@ class ExpertCache {
   std::vector<int64_t> slot_stamp_;  // -1 for empty
   std::vector<int32_t> where_;       // [L*E] slot or -1
   std::vector<int32_t> buf_[2];
+  int32_t buf_layer_[2] = {-1, -1};
   bool prefill_open_ = false;
   bool on_demand_ = false;
 };

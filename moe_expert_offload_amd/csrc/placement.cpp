@@ -56,7 +56,7 @@ extern "C" int ft_replay_placement(int32_t policy, const ft_shape* shape, int32_
       if (prompt > 0) {
         if (n_slots >= 2 * E) {  // two full-layer buffers, the last two layers stay
           if (int rc = cache.prefill_begin()) return rc;
-          cache.prefill_end(L);
+          cache.prefill_end_full_pass();
         } else {  // the on-demand fallback: each layer's routed experts loaded in rounds
           if (int rc = cache.prefill_begin_on_demand()) return rc;
           std::vector<int32_t> layer_ids((size_t)prompt * k);
@@ -64,11 +64,11 @@ extern "C" int ft_replay_placement(int32_t policy, const ft_shape* shape, int32_
             for (int s = 0; s < prompt; ++s)
               for (int j = 0; j < k; ++j) layer_ids[(size_t)s * k + j] = req[(size_t)s * per_step + (size_t)l * k + j];
             if (int rc = cache.prefill_on_demand(l, layer_ids.data(), prompt * k, &pplan)) {
-              cache.prefill_end(L);
+              cache.prefill_end();
               return rc;
             }
           }
-          cache.prefill_end(L);
+          cache.prefill_end();
         }
       }
       for (int s = prompt; s < steps; ++s)

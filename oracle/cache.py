@@ -1,7 +1,9 @@
 """GPU expert-cache residency: classify, split, LRU update, slot rewrite, prefill, resize.
 
-Test infrastructure (see the package docstring).  Two simulators that share
-no code are given so each can be checked against the other.
+Test infrastructure (see the package docstring).  Two simulators, written
+apart (each its own dedup, victim order, plan and counters; both take q from
+the pinned split rule of oracle.qstar), so each can be checked against the
+other.
 
 Pages:
   [FT] §3 one elastic cache shared by all MoE layers, keyed on logical
@@ -30,9 +32,12 @@ Readings of this build (the pages leave these open):
     counters and keeps the clock.
   * prefill: at begin, the first 2E slots in victim order (no hits to protect)
     become buffers B0 = first E, B1 = next E and lose their keys; layer l uses
-    B[l % 2] with expert e in B[l % 2][e]; at end, layers L-2 then L-1 are
-    registered (e ascending), each touching the clock; a copy of the same key
-    elsewhere is emptied; buffer slots left unregistered become empty.
+    B[l % 2] with expert e in B[l % 2][e].  Layer 0 loads at begin and layer l+1
+    streams into the other buffer while layer l computes ([FT] §3.1), so after
+    n of the L layers the buffers hold layers n-1 and n (n < L), or L-2 and L-1
+    after the whole pass.  At end the layers the buffers hold are registered
+    (ascending layer, e ascending), each touching the clock; a copy of the same
+    key elsewhere is emptied; buffer slots left unregistered become empty.
   * on-demand prefill ([FT] §3.1: the fallback when the pool cannot spare two
     full layers, and the serial loading left when the second buffer is off):
     per layer, after routing, U (first occurrence over the chunk's (t, j)) splits
@@ -93,7 +98,7 @@ class Counters:
     read_cpu: int = 0
 
 
-def _first_occurrence(idx):
+def _first_occurrence(idx):  # simulator A
     seen, out = set(), []
     for e in np.asarray(idx).reshape(-1).tolist():
         if e not in seen:
@@ -102,7 +107,7 @@ def _first_occurrence(idx):
     return out
 
 
-def _finish_plan(layer, idx, U, H, M, q, F_slots, avail, slot_of, counters):
+def _finish_plan(layer, idx, U, H, M, q, F_slots, avail, slot_of, counters):  # simulator A
     idx = np.asarray(idx)
     F = M[:q]
     C = M[q:]
@@ -200,9 +205,15 @@ class SlotTable:
     def prefill_slot(self, layer, e):
         return self.buffers[layer % 2][e]
 
-    def prefill_end(self, L):
+    def prefill_end(self, n_done):
+        """End a double-buffered prefill after n_done of the L layers were computed
+        (n_done = L for a whole pass)."""
         used = set()
-        for layer in (L - 2, L - 1):
+        if n_done < self.L:
+            held = [n_done - 1, n_done]
+        else:
+            held = [self.L - 2, self.L - 1]
+        for layer in held:
             if layer < 0:
                 continue
             buf = self.buffers[layer % 2]
@@ -279,7 +290,8 @@ class OrderedLRU:
         self.buffers = None
 
     def lookup(self, layer, idx, fq, min_fill=1, max_fetch=-1):
-        U = _first_occurrence(idx)
+        idx = np.asarray(idx)
+        U = list(dict.fromkeys(int(e) for e in idx.reshape(-1)))  # insertion order = first occurrence
         tag = lambda e: (layer, e)
         H = [e for e in U if tag(e) in self.od]
         M = [e for e in U if tag(e) not in self.od]
@@ -309,8 +321,30 @@ class OrderedLRU:
         for e in U:
             if e in gpu:
                 self.od.move_to_end(tag(e))
-        return _finish_plan(layer, idx, U, H, M, q, F_slots, avail,
-                            lambda e: self.od[tag(e)], self.counters)
+        return self._plan(layer, idx, U, H, M, q, F_slots, avail)
+
+    def _plan(self, layer, idx, U, H, M, q, F_slots, avail):
+        """The plan and the counters of one call, from the ordered map (written apart
+        from simulator A's: slots looked up in the map, read counts by set membership
+        over the whole id array)."""
+        F, C = M[:q], M[q:]
+        G = H + F
+        G_slots = [self.od[(layer, e)] for e in G]
+        flat = idx.reshape(-1)
+        route = np.array([self.od[(layer, int(e))] if int(e) in G else -1 for e in flat], np.int32)
+        group = np.array([G.index(int(e)) if int(e) in G else -1 for e in flat], np.int32)
+        c = self.counters
+        c.calls += 1
+        c.unique_hits += len(H)
+        c.unique_misses += len(M)
+        c.fills += len(F)
+        c.cpu_experts += len(C)
+        c.reads += flat.size
+        c.read_hits += int(np.isin(flat, np.array(H, dtype=flat.dtype)).sum())
+        c.read_fills += int(np.isin(flat, np.array(F, dtype=flat.dtype)).sum())
+        c.read_cpu += int(np.isin(flat, np.array(C, dtype=flat.dtype)).sum())
+        return Plan(layer, U, H, M, q, F, C, list(F_slots), avail, route.reshape(idx.shape), G, G_slots,
+                    group.reshape(idx.shape))
 
     def _all_in_victim_order(self):
         return sorted(self.free) + list(self.od.values())
@@ -331,9 +365,12 @@ class OrderedLRU:
     def prefill_slot(self, layer, e):
         return self.buffers[layer % 2][e]
 
-    def prefill_end(self, L):
+    def prefill_end(self, n_done):
+        # the buffers hold the last layer computed and the one streamed in during its
+        # compute; after the whole pass, the last two layers
+        last = min(n_done, self.L - 1)
         used = set()
-        for layer in (L - 2, L - 1):
+        for layer in (last - 1, last):
             if layer < 0:
                 continue
             buf = self.buffers[layer % 2]
@@ -349,7 +386,7 @@ class OrderedLRU:
         self.buffers = None
 
     def prefill_on_demand(self, layer, idx):
-        U = _first_occurrence(idx)
+        U = list(dict.fromkeys(int(e) for e in np.asarray(idx).reshape(-1)))
         tag = lambda e: (layer, e)
         H = [e for e in U if tag(e) in self.od]
         M = [e for e in U if tag(e) not in self.od]

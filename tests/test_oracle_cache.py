@@ -215,3 +215,19 @@ def test_on_demand_prefill_special_cases():
         sim.prefill_on_demand(0, np.array([[4, 4]]))
         with pytest.raises(ValueError):
             sim.prefill_on_demand(0, np.array([[4, 5]]))
+
+
+@pytest.mark.parametrize("n_done", [0, 1, 2, 3, 5, 6])
+def test_prefill_ended_early_keeps_what_the_buffers_hold(n_done):
+    """[FT] §3.1: layer l+1 streams into the other buffer while layer l computes, so
+    after n_done < L layers the buffers hold layers n_done-1 and n_done (never
+    n_done-2, whose buffer the prefetch of n_done overwrote); after the whole pass
+    L-2 and L-1.  Both simulators, and the slots are exactly the buffer slots."""
+    L, E = 6, 4
+    a, b = SlotTable(20, L, E), OrderedLRU(20, L, E)
+    bufs = a.prefill_begin()
+    assert b.prefill_begin() == bufs
+    a.prefill_end(n_done), b.prefill_end(n_done)
+    held = [n_done - 1, n_done] if n_done < L else [L - 2, L - 1]
+    want = {l * E + e: bufs[l % 2][e] for l in held if l >= 0 for e in range(E)}
+    assert a.resident() == want and b.resident() == want
