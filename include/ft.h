@@ -411,9 +411,11 @@ int ft_moe_decode_layer(ft_ctx_t ctx, int32_t layer, const void* x, int32_t T,
  * begin: reserve two buffers of E slots (victim order) and start loading layer 0
  * on `copy`.  layer: start loading layer l+1 into the other buffer once layer
  * l-1's compute is done, then compute layer l (router, grouping, grouped FFN,
- * combine) from its buffer once its load landed.  end: the last two layers
- * processed (L-2 and L-1 after a full pass) stay resident for decode; waits for
- * any layer prefetch still in flight.
+ * combine) from its buffer once its load landed.  end: waits for any layer load
+ * still in flight; then the layers the two buffers hold stay resident for decode:
+ * L-2 and L-1 after a whole pass; after a pass ended early at n layers, layer n-1
+ * and layer n (streamed in while n-1 computed); a buffer whose load was not issued
+ * completely (a failed call) holds no layer and its slots become empty.
  * On-demand, with overlap off or fewer than 2E slots (the pages' fallback): begin
  * reserves nothing; layer routes, brings the ids to the host, takes the decisions
  * of ft_expert_cache_prefill_on_demand, runs the hits' FFN, then per round loads
@@ -424,6 +426,14 @@ int ft_moe_prefill_begin(ft_ctx_t ctx, void* copy);
 int ft_moe_prefill_layer(ft_ctx_t ctx, int32_t layer, const void* x, int32_t T,
                          const void* w_router, float* y, void* compute, void* copy);
 int ft_moe_prefill_end(ft_ctx_t ctx);
+
+/* The routed ids (int32 [T, k]) and gates (fp32 [T, k]) of the context's last
+ * successful ft_moe_decode_layer or ft_moe_prefill_layer call ([FT] §3.2: the
+ * router's top-k and renormalised gates), copied out of the device workspace into
+ * idx and gates (device or host memory; either may be NULL) with hipMemcpyAsync on
+ * `stream`, which the caller orders after that call (its compute stream does).  T
+ * must be that call's T.  FT_EINVAL before any layer call or for another T. */
+int ft_layer_routing(ft_ctx_t ctx, int32_t* idx, float* gates, int32_t T, void* stream);
 
 /* Device slot of expert e in the buffer serving `layer` during prefill, or -1. */
 int32_t ft_prefill_slot(ft_ctx_t ctx, int32_t layer, int32_t expert);

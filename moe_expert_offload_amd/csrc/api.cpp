@@ -167,6 +167,7 @@ struct ft_ctx {
   std::vector<ft::CpuExpert> cpu_ex;
   ft_plan scratch_plan{};
   int prefill_next = -1;
+  int last_T = 0;  // T of the last successful layer call (its ids and gates stay in the workspace)
 
   // kernel timing (ft_profile_enable)
   struct ProfRec {
@@ -464,6 +465,17 @@ int32_t ft_expert_cache_where(ft_ctx_t c, int32_t layer, int32_t expert) {
   return c ? c->cache->where(layer, expert) : -1;
 }
 
+int ft_layer_routing(ft_ctx_t c, int32_t* idx, float* gates, int32_t T, void* stream) {
+  if (!c || !c->dev) return fail(FT_EINVAL, "layer_routing: no context with a device path");
+  if (c->last_T <= 0 || T != c->last_T) return fail(FT_EINVAL, "layer_routing: no layer call of this T");
+  FT_HIP(hipSetDevice(c->device));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t n = (size_t)T * c->shape.k;
+  if (idx) FT_HIP(hipMemcpyAsync(idx, c->wsp<int32_t>(c->cv.idx), n * 4, hipMemcpyDefault, s));
+  if (gates) FT_HIP(hipMemcpyAsync(gates, c->wsp<float>(c->cv.gates), n * 4, hipMemcpyDefault, s));
+  return FT_OK;
+}
+
 int32_t ft_prefill_slot(ft_ctx_t c, int32_t layer, int32_t expert) {
   return c ? c->cache->prefill_slot(layer, expert) : -1;
 }
@@ -722,23 +734,30 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
     }
   }
   const double t1 = now_us();
+  // From here on the device has already acted on its own decisions (fills into its
+  // victim slots are queued).  If the host cannot confirm them, no slot's contents
+  // can be trusted: empty the cache (the next call uploads the empty state, after
+  // this call's queued work) before reporting the error.
+  auto distrust = [&](int st, const char* msg) {
+    c->cache->clear_residency();
+    c->dev_dirty = true;
+    return fail(st, msg);
+  };
+  // a token that allows fewer than k experts: the device took no decisions (no
+  // fills, no groups), so residency is unchanged on both sides
   for (int i = 0; i < P; ++i)
-    if (c->h_idx[i] < 0) {
-      c->dev_dirty = true;
-      return fail(FT_EINVAL, "decode: a token allows fewer than k experts");
-    }
+    if (c->h_idx[i] < 0) return fail(FT_EINVAL, "decode: a token allows fewer than k experts");
   const ft::DevPlan& dp = *c->h_plan;
   // the host controller takes the same decisions from the same ids: it keeps the
   // counters and the state for safe-point operations, and checks the device
   ft_plan* p = plan_out ? plan_out : &c->scratch_plan;
   if (int rc = c->cache->lookup(layer, c->h_idx, T, k, c->cfg.frac_q16, c->cfg.min_fill, c->cfg.max_fetch, p)) {
+    c->cache->clear_residency();
     c->dev_dirty = true;
     return rc;
   }
-  if (dp.n_u != p->n_u || dp.q != p->q || dp.hash != host_plan_hash(*p, P)) {
-    c->dev_dirty = true;
-    return fail(FT_EHIP, "decode: device and host cache decisions differ");
-  }
+  if (dp.n_u != p->n_u || dp.q != p->q || dp.hash != host_plan_hash(*p, P))
+    return distrust(FT_EHIP, "decode: device and host cache decisions differ");
   std::memcpy(p->idx, c->h_idx, (size_t)P * 4);
   std::memcpy(p->gates, c->h_gates, (size_t)P * 4);
   const int n_h = p->n_h, q = p->q, n_c = p->n_c, n_g = n_h + q;
@@ -796,13 +815,17 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
     st->t_submit_us = t_sub1 - t_sub0;
     st->t_between_us = c->last_return_us > 0.0 ? t0 - c->last_return_us : 0.0;
   }
+  c->last_T = T;
   c->last_return_us = now_us();
   return FT_OK;
 }
 
 // ---- prefill -----------------------------------------------------------------------
 
+// Loads all E records of `layer` into its buffer on `ps`.  The buffer is recorded as
+// holding the layer only once every copy was issued.
 static int enqueue_layer_load(ft_ctx_t c, int layer, hipStream_t ps) {
+  c->cache->prefill_set_buffer_layer(layer & 1, -1);
   const std::vector<int32_t>& b = c->cache->prefill_buffer(layer & 1);
   const int E = c->shape.E;
   int e = 0;
@@ -813,6 +836,7 @@ static int enqueue_layer_load(ft_ctx_t c, int layer, hipStream_t ps) {
     e += run;
   }
   c->cache->stats.h2d_bytes += (int64_t)E * (int64_t)c->S;
+  c->cache->prefill_set_buffer_layer(layer & 1, layer);
   return FT_OK;
 }
 
@@ -914,6 +938,7 @@ static int prefill_layer_on_demand(ft_ctx_t c, int layer, const uint16_t* xs, in
   if (int rc = ft::launch_combine(c->wsp<float>(c->cv.out), d_inv, d_gates, nullptr, T, k, d, y, cs)) return rc;
   FT_HIP(hipEventRecord(c->ev_done, cs));
   c->prefill_next = layer + 1;
+  c->last_T = T;
   return FT_OK;
 }
 
@@ -989,6 +1014,7 @@ int ft_moe_prefill_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, co
   FT_HIP(hipEventRecord(c->ev_done, cs));
   c->prefill_next = layer + 1;
   c->cache->stats.prefill_layers += 1;
+  c->last_T = T;
   return FT_OK;
 }
 
@@ -1002,8 +1028,12 @@ int ft_moe_prefill_end(ft_ctx_t c) {
     FT_HIP(hipEventSynchronize(c->ev_pf_fill[0]));
     FT_HIP(hipEventSynchronize(c->ev_pf_fill[1]));
   }
-  // the last two layers processed stay resident (all L layers in a full prefill)
-  c->cache->prefill_end(c->dev ? std::max(c->prefill_next, 0) : c->shape.L);
+  // what the two buffers hold stays resident: the last layer computed and the one
+  // streamed in during its compute (L-2 and L-1 after a whole pass)
+  if (c->dev)
+    c->cache->prefill_end();
+  else
+    c->cache->prefill_end_full_pass();
   c->prefill_next = -1;
   c->dev_dirty = true;
   return FT_OK;

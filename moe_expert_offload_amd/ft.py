@@ -42,7 +42,7 @@ EXPORTED = [
     "ft_moe_prefill_end", "ft_prefill_slot", "ft_profile_enable", "ft_profile_read", "ft_host_experts",
     "ft_frac_q16_contended", "ft_fetch_fraction_q16", "ft_recommend_hybrid", "ft_bench_bw_contended",
     "ft_bw_profile_path", "ft_bw_profile_save", "ft_bw_profile_load", "ft_expert_cache_prefill_on_demand",
-    "ft_replay_placement",
+    "ft_replay_placement", "ft_layer_routing",
 ]
 
 
@@ -162,6 +162,7 @@ def lib():
             "ft_moe_prefill_layer": (C.c_int, [P, I, P, I, P, P, P, P]),
             "ft_moe_prefill_end": (C.c_int, [P]),
             "ft_prefill_slot": (I, [P, I, I]),
+            "ft_layer_routing": (C.c_int, [P, P, P, I, P]),
             "ft_profile_enable": (C.c_int, [P, I]),
             "ft_profile_read": (C.c_int, [P, C.POINTER(ft_profile)]),
             "ft_host_experts": (C.c_int, [P, I, I, I, I, C.POINTER(P), P, P, P, I, I, P]),
@@ -439,6 +440,10 @@ def ft_moe_prefill_layer(ctx, layer, x, T, w_router, y, compute=None, copy=None)
 
 def ft_moe_prefill_end(ctx):
     return _check("ft_moe_prefill_end", lib().ft_moe_prefill_end(ctx))
+
+
+def ft_layer_routing(ctx, idx, gates, T, stream=None):
+    return _check("ft_layer_routing", lib().ft_layer_routing(ctx, _ptr(idx), _ptr(gates), T, _stream(stream)))
 
 
 def ft_prefill_slot(ctx, layer, expert):

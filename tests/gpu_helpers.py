@@ -69,3 +69,25 @@ class Engine:
         if self.ctx:
             ft.ft_destroy(self.ctx)
             self.ctx = None
+
+
+def tile_cover_tokens(idx, E):
+    """Tokens whose outputs reach every expert group of a chunk's grouping (pairs
+    grouped stably by expert, as the oracle groups them): the first row of every
+    non-empty group; rows 31 and 32 and the last row of the largest group (the
+    32-row sub-tile edge and the ragged tail); rows 255 and 256 of every group that
+    passes 256 rows (the two sides of the 256-row pass edge)."""
+    from oracle.permute import group_pairs
+    off, perm, _ = group_pairs(idx, E)
+    k = idx.shape[1]
+    sizes = np.diff(off)
+    rows = []
+    for g in range(E):
+        if sizes[g] == 0:
+            continue
+        rows.append(off[g])
+        if sizes[g] > 256:
+            rows += [off[g] + 255, off[g] + 256]
+    big = int(np.argmax(sizes))
+    rows += [off[big] + r for r in (31, 32, sizes[big] - 1) if r < sizes[big]]
+    return np.unique(perm[np.asarray(rows, np.int64)] // k), sizes

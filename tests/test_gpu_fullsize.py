@@ -13,7 +13,7 @@ from oracle.cache import SlotTable
 from oracle.common import within_tolerance
 from oracle.ffn import moe_layer
 from oracle.router import route
-from tests.gpu_helpers import Engine, PinnedPool, dev, dev_u16, host, torch_mod
+from tests.gpu_helpers import Engine, PinnedPool, dev, dev_u16, host, tile_cover_tokens, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -76,13 +76,16 @@ def test_decode_full_size(key, L_phys, steps, y_every, fq):
 
 def test_prefill_8k_chunk_full_size():
     """8192-token chunk through the d=4096, E=256, top-6, d_ff=2048 layer shape with
-    double buffering (aliased pool of 2 physical layers), first layers of the stack."""
+    double buffering (aliased pool of 2 physical layers), first two layers of the
+    stack: the ids each layer call routed, all 8192 x 6, bit-exact; y on tokens that
+    reach every one of the 256 expert groups (first row, the 32-row and 256-row tile
+    edges, the last row of the largest group); residency after a pass ended early."""
     torch = torch_mod()
     wl = synth.WORKLOADS["prefill8k-L43-d4096-E256-top6"]
     s = wl.shape
     T = wl.T
     L_phys = 2
-    n_layers = 3
+    n_layers = 2
     _say("prefill full size", wl.name)
     pool = PinnedPool(s, L_phys * s.E)
     pool.fill_device_random(wl.seed_key)
@@ -99,21 +102,27 @@ def test_prefill_8k_chunk_full_size():
             xd = synth.tokens_torch(wl.seed_key, 0, l, T, s.d)
             wr = synth.router_weights(wl, l)
             y = torch.empty((T, s.d), dtype=torch.float32, device="cuda")
+            ids = torch.empty((T, s.k), dtype=torch.int32, device="cuda")
             ft.ft_moe_prefill_layer(eng.ctx, l, xd, T, dev_u16(wr), y, copy=eng.copy)
-            outs.append((l, xd, wr, y))
+            ft.ft_layer_routing(eng.ctx, ids, None, T)  # same stream, before the next layer's router
+            outs.append((l, xd, wr, y, ids))
         ft.ft_moe_prefill_end(eng.ctx)
         ref_cache.prefill_end(n_layers)
         torch.cuda.synchronize()
-        rng = np.random.default_rng(4)
-        for l, xd, wr, y in outs:
+        for l, xd, wr, y, ids in outs:
             x = host(xd).view(np.uint16)
-            sample = np.sort(rng.choice(T, 12, replace=False))
-            idx, g, _ = route(x[sample], wr, s.k)
-            ref_y = moe_layer(x[sample], idx, g, lambda e: pool.view[(l % L_phys) * s.E + e], s.d, s.d_ff)
+            _say("oracle routing of layer", l)
+            idx, g, _ = route(x, wr, s.k, workers=8)
+            assert np.array_equal(host(ids), idx), l
+            sample, sizes = tile_cover_tokens(idx, s.E)
+            assert int((sizes > 0).sum()) >= 250
+            _say("oracle outputs of layer", l, "on", sample.size, "tokens")
+            ref_y = moe_layer(x, idx, g, lambda e: pool.view[(l % L_phys) * s.E + e], s.d, s.d_ff, tokens=sample,
+                              workers=8)
             ok, mx, l1 = within_tolerance(host(y)[sample], ref_y)
             assert ok, (l, mx, l1)
         res = ref_cache.resident()
-        for l in range(n_layers):
+        for l in range(n_layers + 1):
             for e in range(0, s.E, 37):
                 assert ft.ft_expert_cache_where(eng.ctx, l, e) == res.get(l * s.E + e, -1)
     finally:
@@ -145,7 +154,7 @@ def test_router_and_grouping_8k_full_size():
     ft.ft_permute(idx, P, s.E, off, perm, inv, ws, wsb)
     torch.cuda.synchronize()
     x = host(xd).view(np.uint16)
-    ref_lg = router_logits(x, wr)
+    ref_lg = router_logits(x, wr, workers=8)
     assert np.array_equal(host(lg).view(np.uint32), ref_lg.view(np.uint32))
     ref_idx = topk(ref_lg, s.k)
     assert np.array_equal(host(idx), ref_idx)

@@ -18,7 +18,7 @@ from oracle.common import bf16_to_f64, within_tolerance
 from oracle.layer import decode_layer, prefill_layer
 from oracle.qstar import Q16
 from oracle.router import route
-from tests.gpu_helpers import Engine, PinnedPool, dev, dev_u16, host, torch_mod
+from tests.gpu_helpers import Engine, PinnedPool, dev, dev_u16, host, tile_cover_tokens, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -257,7 +257,8 @@ def test_mx_prefill_double_buffer_then_resize(T):
 def test_mx_full_size_prefill_chunk_and_decode():
     """The MXFP4 configuration at full size: d=4096, E=256, top-6, d_ff=2048; one
     8192-token chunk through two layers (double-buffered, aliased pool of two
-    physical layers), then batch-1 decode steps with the cache of 1210 slots."""
+    physical layers): every routed id bit-exact, y on tokens reaching every expert
+    group and the tile edges; then batch-1 decode steps with the cache of 1210 slots."""
     torch = torch_mod()
     wl = synth.WORKLOADS["mxfp4-prefill8k-L43-d4096-E256-top6"]
     s = wl.shape
@@ -275,18 +276,22 @@ def test_mx_full_size_prefill_chunk_and_decode():
             xd = synth.tokens_torch(wl.seed_key, 0, l, wl.T, s.d)
             wr = synth.router_weights(wl, l)
             y = torch.empty((wl.T, s.d), dtype=torch.float32, device="cuda")
+            ids = torch.empty((wl.T, s.k), dtype=torch.int32, device="cuda")
             ft.ft_moe_prefill_layer(eng.ctx, l, xd, wl.T, dev_u16(wr), y, copy=eng.copy)
-            outs.append((l, xd, wr, y))
+            ft.ft_layer_routing(eng.ctx, ids, None, wl.T)
+            outs.append((l, xd, wr, y, ids))
         ft.ft_moe_prefill_end(eng.ctx)
         ref_cache.prefill_end(2)
         torch.cuda.synchronize()
-        rng = np.random.default_rng(5)
-        for l, xd, wr, y in outs:
+        for l, xd, wr, y, ids in outs:
             x = host(xd).view(np.uint16)
-            sample = np.sort(rng.choice(wl.T, 4, replace=False))
-            idx, g, _ = route(x[sample], wr, s.k)
-            ref_y = mx.moe_layer(x[sample], idx, g, lambda e: pool.view[(l % L_phys) * s.E + e], s.d, s.d_ff,
-                                 form="prefill")
+            _say("oracle routing of layer", l)
+            idx, g, _ = route(x, wr, s.k, workers=8)
+            assert np.array_equal(host(ids), idx), l  # every id the prefill layer routed
+            sample, sizes = tile_cover_tokens(idx, s.E)
+            _say("oracle outputs of layer", l, "on", sample.size, "tokens")
+            ref_y = mx.moe_layer(x, idx, g, lambda e: pool.view[(l % L_phys) * s.E + e], s.d, s.d_ff,
+                                 form="prefill", tokens=sample, workers=8)
             ok, mxe, l1 = within_tolerance(host(y)[sample], ref_y)
             assert ok, (l, mxe, l1)
         wd = synth.WORKLOADS["mxfp4-decode-L43-d4096-E256-top6"]
