@@ -14,9 +14,18 @@ and the layer output  y[t] = sum_j g[t,j] * FFN_{idx[t,j]}(x[t])  (j in rank ord
 Expert records are bf16 words laid out [W_gate (d_ff x d) | W_up (d_ff x d) |
 W_down (d x d_ff)], row-major.
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from .common import bf16_to_f64
+
+
+def _map(fn, items, workers):
+    if workers <= 1:
+        return map(fn, items)
+    with ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(fn, items))
 
 
 def split_record(record_bits, d, d_ff):
@@ -46,12 +55,14 @@ def expert_ffn(weights, x):
     return h @ wd.T
 
 
-def moe_layer(x_bits, idx, g, record_of, d, d_ff, tokens=None):
+def moe_layer(x_bits, idx, g, record_of, d, d_ff, tokens=None, workers=1):
     """Sparse layer output y [T or len(tokens), d] (float64).
 
     record_of(e) returns the bf16 record of expert e of this layer.  ``tokens``
     restricts the computation to a sample of token rows (for large inputs).
-    The k gate-weighted expert outputs of a token are summed in rank order j."""
+    The k gate-weighted expert outputs of a token are summed in rank order j.
+    ``workers`` > 1 evaluates the experts on that many threads (each expert's
+    arithmetic is unchanged; only its wall time is shared)."""
     x = bf16_to_f64(x_bits)
     idx = np.asarray(idx)
     g = np.asarray(g, np.float64)
@@ -59,10 +70,13 @@ def moe_layer(x_bits, idx, g, record_of, d, d_ff, tokens=None):
     k = idx.shape[1]
     sub = idx[rows]
     contrib = np.zeros((rows.size, k, d))
-    for e in np.unique(sub):
+
+    def one(e):
         w = split_record(record_of(int(e)), d, d_ff)
         sel_t, sel_j = np.nonzero(sub == e)
-        out = expert_ffn(w, x[rows[sel_t]])
+        return sel_t, sel_j, expert_ffn(w, x[rows[sel_t]])
+
+    for sel_t, sel_j, out in _map(one, np.unique(sub), workers):
         contrib[sel_t, sel_j] = g[rows[sel_t], sel_j][:, None] * out
     y = np.zeros((rows.size, d))
     for j in range(k):

@@ -37,6 +37,7 @@ down scales d x d_ff/32], all row-major.
 import numpy as np
 
 from .common import bf16_to_f64
+from .ffn import _map
 
 E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 E2M1_EMAX = 2
@@ -44,10 +45,13 @@ E4M3_EMAX = 8
 E4M3_MAX = 448.0
 
 
+# the 16 code values: bit 3 is the sign, bits 0-2 index the magnitude (code 8 is -0)
+_E2M1_SIGNED = np.concatenate([E2M1_MAG, -E2M1_MAG])
+
+
 def e2m1_value(codes):
     c = np.asarray(codes, np.uint8) & 0xF
-    v = E2M1_MAG[c & 7]
-    return np.where(c & 8, -v, v)
+    return np.take(_E2M1_SIGNED, c)
 
 
 def e4m3_value(codes):
@@ -203,8 +207,9 @@ def expert_ffn_prefill(W, x):
     return quantize_act(h) @ wd.T
 
 
-def moe_layer(x_bits, idx, g, record_of, d, d_ff, form="decode", tokens=None):
-    """y [rows, d] = sum_j g[t,j] FFN_idx[t,j](x[t]) in rank order, with MXFP4 experts."""
+def moe_layer(x_bits, idx, g, record_of, d, d_ff, form="decode", tokens=None, workers=1):
+    """y [rows, d] = sum_j g[t,j] FFN_idx[t,j](x[t]) in rank order, with MXFP4 experts
+    (``workers`` > 1: experts evaluated on that many threads, arithmetic unchanged)."""
     x = bf16_to_f64(x_bits)
     idx = np.asarray(idx)
     g = np.asarray(g, np.float64)
@@ -213,10 +218,14 @@ def moe_layer(x_bits, idx, g, record_of, d, d_ff, form="decode", tokens=None):
     k = idx.shape[1]
     ffn = expert_ffn_decode if form == "decode" else expert_ffn_prefill
     contrib = np.zeros((rows.size, k, d))
-    for e in np.unique(sub):
+
+    def one(e):
         W = split_record(record_of(int(e)), d, d_ff)
         sel_t, sel_j = np.nonzero(sub == e)
-        contrib[sel_t, sel_j] = g[rows[sel_t], sel_j][:, None] * ffn(W, x[rows[sel_t]])
+        return sel_t, sel_j, ffn(W, x[rows[sel_t]])
+
+    for sel_t, sel_j, out in _map(one, np.unique(sub), workers):
+        contrib[sel_t, sel_j] = g[rows[sel_t], sel_j][:, None] * out
     y = np.zeros((rows.size, d))
     for j in range(k):
         y = y + contrib[:, j]

@@ -21,14 +21,16 @@ multiply-add gives the same bits.
 import numpy as np
 
 from .common import bf16_to_f32
+from .ffn import _map
 
 LANES = 64
 VEC = 8
 CHUNK = LANES * VEC  # 512
 
 
-def router_logits(x_bits, w_bits) -> np.ndarray:
-    """fp32 logits [T, E] of x [T, d] against W_r [E, d] (bf16 words), in the order above."""
+def router_logits(x_bits, w_bits, workers=1) -> np.ndarray:
+    """fp32 logits [T, E] of x [T, d] against W_r [E, d] (bf16 words), in the order above
+    (``workers`` > 1: blocks of tokens on that many threads, arithmetic unchanged)."""
     x = bf16_to_f32(x_bits)
     w = bf16_to_f32(w_bits)
     T, d = x.shape
@@ -43,7 +45,8 @@ def router_logits(x_bits, w_bits) -> np.ndarray:
     out = np.empty((T, E), np.float32)
     tb = max(1, 4096 // max(E, 1))
     lanes = np.arange(LANES)
-    for t0 in range(0, T, tb):
+
+    def block(t0):
         t1 = min(T, t0 + tb)
         acc = np.zeros((t1 - t0, E, LANES), np.float32)
         for j in range(J):
@@ -53,6 +56,8 @@ def router_logits(x_bits, w_bits) -> np.ndarray:
         for o in (32, 16, 8, 4, 2, 1):
             acc = acc + acc[:, :, lanes ^ o]
         out[t0:t1] = acc[:, :, 0]
+
+    list(_map(block, range(0, T, tb), workers))
     return out
 
 
@@ -81,8 +86,8 @@ def gates(logits, idx) -> np.ndarray:
     return z / z.sum(axis=1, keepdims=True)
 
 
-def route(x_bits, w_bits, k, allowed=None):
+def route(x_bits, w_bits, k, allowed=None, workers=1):
     """(idx int32 [T,k], gates fp64 [T,k], logits fp32 [T,E])."""
-    lg = router_logits(x_bits, w_bits)
+    lg = router_logits(x_bits, w_bits, workers)
     idx = topk(lg, k, allowed)
     return idx, gates(lg, idx), lg
