@@ -4,20 +4,24 @@
 A step is one decode step through every layer of the stack: per layer the router,
 the cache decisions and the fetch split, the fills of F over PCIe, the CPU
 branch for C on the host cores, the grouped SwiGLU FFN of H and F, and the merge.
-Default workload: 40 stacked layers, d=2048, E=128, top-8, d_ff=768, bf16
-experts, batch 1, GPU cache 37 % of the (layer, expert) pairs, Zipf(1.1)
-popularity with 0.6 step-to-step reuse, fetch fraction from B_P and B_H
-measured on this machine.  Inputs are seeded and synthetic, resident in HBM
-(activations, router weights, routing masks) or pinned host memory (the pool)
-before the timed region starts.
+Headline workload: 43 stacked layers, d=4096, E=256, top-6, d_ff=2048, bf16
+experts in pinned host memory, batch 1, GPU cache 11 % of the (layer, expert)
+pairs (1210 slots), Zipf(1.1) popularity with 0.6 step-to-step reuse, fetch
+fraction from B_P and B_H measured on this machine.  The cache is warmed by at
+least 64 trace steps before timing, whatever --warmup says.  Inputs are seeded and
+synthetic, resident in HBM (activations, router weights, routing masks) or pinned
+host memory (the pool) before the timed region starts.
 
-Also measured: the same stack without the at-least-one-fill floor (min_fill = 0,
-unless --no-min-fill0) and at batch 8 (unless --no-batch8).
-Also measured (unless --no-prefill): one 8192-token prefill chunk through the
-43-layer d=4096, E=256, top-6, d_ff=2048 shape with full-layer double buffering.
-And (unless --no-mxfp4) the same shape with MXFP4 experts: a 16384-token prefill
-as two 8192-token chunks on the scaled MFMA, then batch-1 decode over a 512-step
-trace with the cache resized from 1210 to 605 slots at step 256 (a safe point).
+Also measured: the 40-layer d=2048, E=128, top-8, d_ff=768 stack (cache 37 %) at
+batch 1, without the at-least-one-fill floor (min_fill = 0), and at batch 8
+(unless --no-config2); one 8192-token prefill chunk through the 43-layer shape with
+full-layer double buffering, and with the second buffer off (unless --no-prefill);
+the same shape with MXFP4 experts: a 16384-token prefill as two 8192-token chunks on
+the scaled MFMA, then batch-1 decode over a 512-step trace with the cache resized
+from 1210 to 605 slots at step 256 (unless --no-mxfp4); the placement replay.
+
+--counter-calibration runs only a plain device copy of known size (for scaling
+rocprofv3's FETCH_SIZE and WRITE_SIZE to bytes) and prints its own JSON line.
 
 Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
 """
@@ -37,6 +41,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MoE decode tok/s + 8k-token prefill tok/s (DSV4 shape); % of HBM/MFMA peak"
+HEADLINE = "decode-L43-d4096-E256-top6"
+CONFIG2 = "decode-L40-d2048-E128-top8"
+CACHE_WARMUP_STEPS = 64  # trace steps that warm the cold cache before any timed step
+# physical layers of the pinned pool when --l-phys is 0: the 43-layer bf16 pool
+# (554 GB) does not fit host memory, so it aliases 4 physical layers (51.5 GB);
+# keys, bytes moved and timing are those of the logical pool
+L_PHYS_DEFAULT = {HEADLINE: 4}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published (E4M3 x E2M1 runs at the fp8 rate)
@@ -76,6 +87,13 @@ def stored_traffic(kernel: str, workload: str):
         return None
 
 
+def default_l_phys(args, wl):
+    s = wl.shape
+    if args.l_phys > 0:
+        return min(args.l_phys, s.L)
+    return L_PHYS_DEFAULT.get(wl.name, s.L)
+
+
 def phased_time(m, q, S, B_P, B_H):
     # fills at B_P; host branch at B_H - B_P while the link is busy, B_H after
     t_fill = q * S / B_P if q > 0 else 0.0
@@ -103,9 +121,11 @@ def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warm
     s = wl.shape
     T = wl.T
     S = s.record_bytes
-    steps_total = args.warmup + args.steps
+    # the cache starts cold: at least CACHE_WARMUP_STEPS trace steps run before timing
+    warm = max(CACHE_WARMUP_STEPS, args.warmup)
+    steps_total = warm + args.steps
     steps_gen = steps_total + args.steps  # a second pass over further steps carries the kernel timing
-    L_phys = s.L if args.l_phys <= 0 else min(args.l_phys, s.L)
+    L_phys = default_l_phys(args, wl)
     log(f"decode workload {wl.name}: pool {L_phys * s.E} records x {S / 1e6:.2f} MB = {L_phys * s.E * S / 1e9:.1f} GB")
     if pool is None:
         t = time.time()
@@ -158,13 +178,13 @@ def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warm
                                st_call.t_between_us))
 
     try:
-        for st in range(args.warmup):
+        for st in range(warm):
             step(st, False)
         torch.cuda.synchronize()
         ft.ft_reset_stats(ctx)
         # timed region: the steps as they run in serving, no timing events
         t0 = time.perf_counter()
-        for st in range(args.warmup, steps_total):
+        for st in range(warm, steps_total):
             step(st, True)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
@@ -197,7 +217,8 @@ def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warm
     res = {
         "tok_s": args.steps * T / elapsed,
         "ms_per_step": elapsed / args.steps * 1e3,
-        "workload": wl.name, "T": T, "L": s.L, "n_slots": N, "L_phys": L_phys,
+        "workload": wl.name, "T": T, "L": s.L, "n_slots": N, "L_phys": L_phys, "cache_warmup_steps": warm,
+        "timed_steps": args.steps,
         "B_P_GBs": B_P / 1e9, "B_H_GBs": B_H / 1e9, "frac_q16": fq, "bw_profile": bwp, "min_fill": args.min_fill,
         "cpu_threads": args.cpu_threads,
         "miss_rate_reads": 1.0 - stats["read_hits"] / reads,
@@ -448,9 +469,30 @@ def run_mxfp4(args, torch, ft, synth, HostPool):
     }
 
 
-def cpu_baseline(args, pool, wl, tr, fq, L_phys, budget_s):
-    """The oracle as it stands, timed on the host over the first steps of the same trace."""
-    from threadpoolctl import threadpool_info
+def host_info():
+    """CPU model, logical CPUs, physical cores (distinct (package, core) pairs) and the
+    CPUs this process may run on."""
+    model, cores, cur = None, set(), {}
+    with open("/proc/cpuinfo") as f:
+        for line in list(f) + [""]:
+            if ":" not in line:
+                if "physical id" in cur and "core id" in cur:
+                    cores.add((cur["physical id"], cur["core id"]))
+                cur = {}
+                continue
+            k, v = (t.strip() for t in line.split(":", 1))
+            cur[k] = v
+            if k == "model name" and model is None:
+                model = v
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "physical_cores": len(cores) or None,
+            "cpus_available": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline(args, pool, wl, tr, fq, L_phys, budget_s, one_thread_budget_s):
+    """The oracle as it stands, timed on the host cores over the first (step, layer)
+    calls of the same trace and inputs: a bounded sample, scaled to tok/s through the
+    time per layer call.  Once with BLAS on every CPU of the run, once on one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from moe_expert_offload_amd import synth
     from oracle.cache import SlotTable
@@ -459,26 +501,41 @@ def cpu_baseline(args, pool, wl, tr, fq, L_phys, budget_s):
 
     s = wl.shape
     T = wl.T
-    cache = SlotTable(wl.n_slots, s.L, s.E)
     wr = [synth.router_weights(wl, l, seed=args.seed) for l in range(s.L)]
-    done = 0
-    t0 = time.perf_counter()
-    while done < tr.shape[0]:
-        st = done
-        for l in range(s.L):
+
+    def timed(budget):
+        cache = SlotTable(wl.n_slots, s.L, s.E)
+        calls = 0
+        t0 = time.perf_counter()
+        while calls < tr.shape[0] * s.L:
+            st, l = divmod(calls, s.L)
             x = synth.tokens(wl, st, l, T=T, seed=args.seed)
             allowed = synth.allowed_mask(tr[st, l], s.E)
             idx, g, _ = route(x, wr[l], s.k, allowed)
             cache.lookup(l, idx, fq, args.min_fill, -1)
             moe_layer(x, idx, g, lambda e: pool.view[(l % L_phys) * s.E + e], s.d, s.d_ff)
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    el = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": round(done * T / el, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {done} decode steps x {s.L} layers of the same trace and inputs "
-                      f"(fp64 NumPy oracle: router, cache decisions, exact layer output), {el:.1f} s"}
+            calls += 1
+            if time.perf_counter() - t0 > budget:
+                break
+        el = time.perf_counter() - t0
+        step_s = el / calls * s.L
+        return T / step_s, calls, el
+
+    n_all = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=n_all):
+        v_all, c_all, e_all = timed(budget_s)
+        blas = [{k: p.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer")}
+                for p in threadpool_info()]
+    with threadpool_limits(limits=1):
+        v_one, c_one, e_one = timed(one_thread_budget_s)
+    what = (f"{{n}} layer calls (first steps of the same trace and inputs, {s.L} layers per step) of the fp64 "
+            f"NumPy oracle: router, cache decisions, exact layer output; {{el:.1f}} s, scaled to tok/s by "
+            f"the time per layer call")
+    return {"value": round(v_all, 5), "unit": "tok/s", "cores": n_all, "kind": "oracle",
+            "sample": what.format(n=c_all, el=e_all),
+            "one_thread": {"value": round(v_one, 5), "unit": "tok/s", "cores": 1,
+                           "sample": what.format(n=c_one, el=e_one)},
+            "host": host_info(), "blas": blas}
 
 
 PAGES_FIG4B = {  # [FT] §5.3 "Expert locality": decode-read miss rates at the RTX 5090 serving capacity
@@ -527,19 +584,71 @@ def run_placement(args, ft, synth):
     return out
 
 
+def counter_calibration(torch, mib=1024):
+    """A plain device copy of a known size, three times: run under rocprofv3 --pmc
+    FETCH_SIZE (or WRITE_SIZE), its reading per dispatch divided into the bytes each
+    copy moves is the factor that turns that counter into bytes."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"counter_calibration": "device-to-device copy", "bytes_read_per_copy": mib << 20,
+            "bytes_written_per_copy": mib << 20, "copies": 3}
+
+
+def run_config2(args, torch, ft, synth, HostPool):
+    """The 40-layer d=2048, E=128, top-8 stack (cache 37 %) on one pool: batch 1, batch 1
+    without the fill floor, batch 8; each after the fixed cache warm-up."""
+    out = {}
+    log(f"decode {CONFIG2}, batch 1")
+    d1, r1, keep = run_decode(args, torch, ft, synth, HostPool, CONFIG2, args.c2_steps, 0)
+    pool = keep[0]
+    try:
+        out["batch1"] = {k: d1[k] for k in ("tok_s", "ms_per_step", "workload", "n_slots", "L_phys", "cache_warmup_steps",
+                                            "timed_steps", "B_P_GBs", "B_H_GBs", "frac_q16", "min_fill",
+                                            "miss_rate_reads", "fills_per_step", "cpu_experts_per_step",
+                                            "h2d_GB_per_step", "modelled_floor_ms_per_step", "host_call_us",
+                                            "kernels")}
+        out["batch1"]["roofline"] = r1
+        if args.min_fill0 and args.min_fill != 0:
+            # q is the Q16 split alone, so single misses go to the host cores
+            log("decode with min_fill = 0")
+            d0, _, _ = run_decode(args, torch, ft, synth, HostPool, CONFIG2, args.mf0_steps, 0, {"min_fill": 0}, pool)
+            out["min_fill0"] = {k: d0[k] for k in ("tok_s", "ms_per_step", "min_fill", "miss_rate_reads",
+                                                   "fills_per_step", "cpu_experts_per_step", "h2d_GB_per_step",
+                                                   "host_cpu_branch_ms_per_step", "modelled_floor_ms_per_step",
+                                                   "cache_warmup_steps", "timed_steps")}
+        if args.batch8:
+            log("decode batch 8")
+            d8, r8, _ = run_decode(args, torch, ft, synth, HostPool, CONFIG2 + "-b8", args.b8_steps, 0, None, pool)
+            out["batch8"] = {"tok_s": d8["tok_s"], "ms_per_step": d8["ms_per_step"], "roofline": r8,
+                             "miss_rate_reads": d8["miss_rate_reads"], "fills_per_step": d8["fills_per_step"],
+                             "cpu_experts_per_step": d8["cpu_experts_per_step"], "kernels": d8["kernels"],
+                             "cache_warmup_steps": d8["cache_warmup_steps"], "timed_steps": d8["timed_steps"]}
+    finally:
+        pool.free()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=192)
-    ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--workload", default="decode-L40-d2048-E128-top8",
-                    choices=["decode-L40-d2048-E128-top8", "decode-L40-d2048-E128-top8-b8", "decode-L43-d4096-E256-top6"])
-    ap.add_argument("--l-phys", type=int, default=0, help="physical layers in the host pool (0 = all)")
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=CACHE_WARMUP_STEPS,
+                    help=f"untimed steps before timing (at least {CACHE_WARMUP_STEPS} run in any case: cache warm-up)")
+    ap.add_argument("--workload", default=HEADLINE, choices=[HEADLINE, CONFIG2, CONFIG2 + "-b8"])
+    ap.add_argument("--l-phys", type=int, default=0,
+                    help="physical layers in the host pool (0 = all, 4 for the 43-layer bf16 pool)")
     ap.add_argument("--min-fill", type=int, default=1)
     ap.add_argument("--max-fetch", type=int, default=-1)
     ap.add_argument("--frac-q16", type=int, default=-1, help="override the measured fetch fraction")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-config2", dest="config2", action="store_false", default=True,
+                    help="skip the 40-layer d=2048 legs (batch 1, min_fill = 0, batch 8)")
+    ap.add_argument("--c2-steps", type=int, default=64)
     ap.add_argument("--prefill", dest="prefill", action="store_true", default=True)
     ap.add_argument("--no-prefill", dest="prefill", action="store_false")
     ap.add_argument("--prefill-l-phys", type=int, default=2)
@@ -553,11 +662,9 @@ def main():
     ap.add_argument("--no-batch8", dest="batch8", action="store_false", default=True,
                     help="skip the batch-8 decode leg of the 40-layer stack")
     ap.add_argument("--b8-steps", type=int, default=64)
-    ap.add_argument("--b8-warmup", type=int, default=16)
     ap.add_argument("--no-min-fill0", dest="min_fill0", action="store_false", default=True,
                     help="skip the decode leg without the at-least-one-fill floor")
     ap.add_argument("--mf0-steps", type=int, default=64)
-    ap.add_argument("--mf0-warmup", type=int, default=32)
     ap.add_argument("--no-replay", dest="replay", action="store_false", default=True,
                     help="skip the Fig. 4b placement replay (host only)")
     ap.add_argument("--replay-requests", type=int, default=4)
@@ -565,6 +672,9 @@ def main():
     ap.add_argument("--replay-decode", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--cpu-budget-1t-s", type=float, default=8.0)
+    ap.add_argument("--counter-calibration", action="store_true",
+                    help="only a plain device copy of known size, for rocprofv3 counter scaling")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -573,41 +683,25 @@ def main():
 
     import torch
 
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.counter_calibration:
+        print(json.dumps(counter_calibration(torch)), flush=True)
+        return
+
     from moe_expert_offload_amd import ft, synth
     from moe_expert_offload_amd.pool import HostPool
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     ft.lib()
     dec, roof, keep = run_decode(args, torch, ft, synth, HostPool)
     pool, wl, tr, fq, L_phys = keep
     cpu = None
-    mf0 = None
     try:
         if not args.no_cpu_baseline:
             log("timing the CPU oracle on the host")
-            cpu = cpu_baseline(args, pool, wl, tr, fq, L_phys, args.cpu_budget_s)
-        if args.min_fill0 and args.min_fill != 0:
-            # the same stack and trace without the at-least-one-fill floor: q is the Q16
-            # split alone, so single misses go to the host cores
-            log("decode with min_fill = 0")
-            d0, _, _ = run_decode(args, torch, ft, synth, HostPool, args.workload, args.mf0_steps, args.mf0_warmup,
-                                  {"min_fill": 0}, pool)
-            mf0 = {k: d0[k] for k in ("tok_s", "ms_per_step", "min_fill", "miss_rate_reads", "fills_per_step",
-                                      "cpu_experts_per_step", "h2d_GB_per_step", "host_cpu_branch_ms_per_step",
-                                      "modelled_floor_ms_per_step")}
-            mf0.update({"steps": args.mf0_steps, "warmup": args.mf0_warmup})
+            cpu = cpu_baseline(args, pool, wl, tr, fq, L_phys, args.cpu_budget_s, args.cpu_budget_1t_s)
     finally:
         pool.free()
-    b8 = None
-    if args.batch8 and args.workload == "decode-L40-d2048-E128-top8":
-        # the same 40-layer stack at batch 8 (8 tokens per call)
-        d8, r8, k8 = run_decode(args, torch, ft, synth, HostPool, "decode-L40-d2048-E128-top8-b8",
-                                args.b8_steps, args.b8_warmup)
-        k8[0].free()
-        b8 = {"tok_s": d8["tok_s"], "ms_per_step": d8["ms_per_step"], "roofline": r8,
-              "miss_rate_reads": d8["miss_rate_reads"], "fills_per_step": d8["fills_per_step"],
-              "cpu_experts_per_step": d8["cpu_experts_per_step"], "kernels": d8["kernels"],
-              "steps": args.b8_steps, "warmup": args.b8_warmup}
+    c2 = run_config2(args, torch, ft, synth, HostPool) if args.config2 and args.workload == HEADLINE else None
     pre = run_prefill(args, torch, ft, synth, HostPool) if args.prefill else None
     mxr = run_mxfp4(args, torch, ft, synth, HostPool) if args.mxfp4 else None
     rep = run_placement(args, ft, synth) if args.replay else None
@@ -617,8 +711,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": dec["workload"], "global_batch": dec["T"], "layers": dec["L"],
-                   "cache_slots": dec["n_slots"], "parallelism": "single-gpu"},
-        "roofline": roof, "cpu_baseline": cpu, "decode": dec, "decode_min_fill0": mf0, "decode_batch8": b8,
+                   "cache_slots": dec["n_slots"], "cache_warmup_steps": dec["cache_warmup_steps"],
+                   "pool_physical_layers": dec["L_phys"], "parallelism": "single-gpu"},
+        "roofline": roof, "cpu_baseline": cpu, "decode": dec, "decode_L40": c2,
         "prefill": pre, "mxfp4": mxr,
         "placement_replay": rep,
     }
