@@ -301,6 +301,20 @@ int ft_permute(const int32_t* key, int32_t P, int32_t n_groups, int32_t* offsets
                int32_t* perm, int32_t* inv, void* workspace, size_t workspace_bytes,
                void* stream);
 
+/* ft_permute for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels
+ * and results, with the per-block group counts in a fixed device array of the
+ * library (ft_permute_noalloc_max_scratch_bytes() = 1 MiB, enough for P <= 65536
+ * at any n_groups <= 1024) instead of a workspace.  Calls no allocating routine.
+ * Each GPU has its own array, held until the process ends and shared by every
+ * call on that GPU: calls that overlap on one GPU (different streams, or host
+ * threads) race on it.  FT_EINVAL when ft_permute_workspace_bytes(P, n_groups)
+ * exceeds the array, for bad sizes or null pointers; FT_EHIP when the array's
+ * device address cannot be looked up. */
+size_t ft_permute_noalloc_max_scratch_bytes(void);
+int ft_permute_noalloc(const int32_t* key, int32_t P, int32_t n_groups, int32_t* offsets,
+                       int32_t* perm, int32_t* inv, void* stream);
+
 /* Grouped SwiGLU expert FFN over groups [g_begin, g_end):
  *   out[i] = W_down (silu(W_gate x_t) * (W_up x_t))  for i in [offsets[g], offsets[g+1]),
  *   t = perm[i] / k, with the record at slots + group_slot[g] * S.

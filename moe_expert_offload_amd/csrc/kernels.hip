@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 #include "internal.h"
 
@@ -1649,3 +1650,68 @@ int launch_combine(const float* out, const int32_t* inv, const float* gates,
 }
 
 }  // namespace ft
+
+// ============================================================================
+// Grouping without allocation
+// ============================================================================
+// ft_permute_noalloc: ft_permute with its per-block group counts in a fixed
+// device array instead of a caller workspace.  Each GPU the library runs on
+// holds its own copy of the array until the process ends; host code reaches it
+// only through the address hipGetSymbolAddress returns on that device (the
+// array's name is a host-side stand-in, not a device address).
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;  // P <= 65536 pairs at any n_groups <= 1024
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / sizeof(int32_t)];
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device with that
+// device current; null with the error set on failure.
+void* scratch_for_current_device() {
+  int dev = -1;
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge != hipSuccess) {
+    ft::set_error(std::string("permute_noalloc: hipGetDevice: ") + hipGetErrorString(ge));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    ft::set_error("permute_noalloc: device index beyond the library's table");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      ft::set_error(std::string("permute_noalloc: hipGetSymbolAddress: ") + hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_dev[dev] = ptr;
+  }
+  return g_scratch_dev[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ft_permute_noalloc_max_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int ft_permute_noalloc(const int32_t* key, int32_t P, int32_t n_groups, int32_t* offsets, int32_t* perm,
+                       int32_t* inv, void* stream) {
+  if (P < 0 || n_groups < 1 || n_groups > 1024) return ft::fail(FT_EINVAL, "permute_noalloc: need P >= 0 and 1<=n_groups<=1024");
+  if ((P > 0 && (!key || !perm || !inv)) || !offsets) return ft::fail(FT_EINVAL, "permute_noalloc: null pointer");
+  const size_t need = ft::permute_ws_bytes(P, n_groups);
+  if (need > kNoAllocScratchBytes)
+    return ft::fail(FT_EINVAL, "permute_noalloc: P and n_groups need " + std::to_string(need) +
+                                   " bytes of scratch, more than its fixed " +
+                                   std::to_string(kNoAllocScratchBytes));
+  void* ws = scratch_for_current_device();
+  if (!ws) return FT_EHIP;
+  return ft::launch_permute(key, P, n_groups, offsets, perm, inv, ws, kNoAllocScratchBytes, stream);
+}
+
+}  // extern "C"

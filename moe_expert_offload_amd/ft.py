@@ -42,7 +42,7 @@ EXPORTED = [
     "ft_moe_prefill_end", "ft_prefill_slot", "ft_profile_enable", "ft_profile_read", "ft_host_experts",
     "ft_frac_q16_contended", "ft_fetch_fraction_q16", "ft_recommend_hybrid", "ft_bench_bw_contended",
     "ft_bw_profile_path", "ft_bw_profile_save", "ft_bw_profile_load", "ft_expert_cache_prefill_on_demand",
-    "ft_replay_placement", "ft_layer_routing",
+    "ft_replay_placement", "ft_layer_routing", "ft_permute_noalloc", "ft_permute_noalloc_max_scratch_bytes",
 ]
 
 
@@ -149,6 +149,8 @@ def lib():
             "ft_router_topk": (C.c_int, [P, P, P, I, I, I, I, P, P, P, P]),
             "ft_permute_workspace_bytes": (C.c_size_t, [I, I]),
             "ft_permute": (C.c_int, [P, I, I, P, P, P, P, C.c_size_t, P]),
+            "ft_permute_noalloc": (C.c_int, [P, I, I, P, P, P, P]),
+            "ft_permute_noalloc_max_scratch_bytes": (C.c_size_t, []),
             "ft_grouped_ffn": (C.c_int, [P, I, I, I, I, P, P, P, P, I, I, I, I, P, P, I, P]),
             "ft_grouped_ffn_mx_workspace_bytes": (C.c_size_t, [I, I, I, I]),
             "ft_grouped_ffn_mx": (C.c_int, [P, I, I, I, I, P, P, P, P, I, I, I, I, I, P, C.c_size_t, P, I, P]),
@@ -356,6 +358,15 @@ def ft_permute_workspace_bytes(P_, n_groups):
 def ft_permute(key, P_, n_groups, offsets, perm, inv, workspace, workspace_bytes, stream=None):
     return _check("ft_permute", lib().ft_permute(_ptr(key), P_, n_groups, _ptr(offsets), _ptr(perm), _ptr(inv),
                                                  _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def ft_permute_noalloc(key, P_, n_groups, offsets, perm, inv, stream=None):
+    return _check("ft_permute_noalloc", lib().ft_permute_noalloc(_ptr(key), P_, n_groups, _ptr(offsets), _ptr(perm),
+                                                                 _ptr(inv), _stream(stream)))
+
+
+def ft_permute_noalloc_max_scratch_bytes():
+    return lib().ft_permute_noalloc_max_scratch_bytes()
 
 
 def ft_grouped_ffn(x, T, d, d_ff, k, slots, group_slot, offsets, perm, n_groups, g_begin, g_end,
