@@ -675,6 +675,8 @@ def main():
     ap.add_argument("--cpu-budget-1t-s", type=float, default=8.0)
     ap.add_argument("--counter-calibration", action="store_true",
                     help="only a plain device copy of known size, for rocprofv3 counter scaling")
+    ap.add_argument("--skip-headline", action="store_true",
+                    help="profiling runs of the other legs only: the headline decode is not run and no value is reported")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -692,19 +694,24 @@ def main():
     from moe_expert_offload_amd.pool import HostPool
 
     ft.lib()
-    dec, roof, keep = run_decode(args, torch, ft, synth, HostPool)
-    pool, wl, tr, fq, L_phys = keep
-    cpu = None
-    try:
-        if not args.no_cpu_baseline:
-            log("timing the CPU oracle on the host")
-            cpu = cpu_baseline(args, pool, wl, tr, fq, L_phys, args.cpu_budget_s, args.cpu_budget_1t_s)
-    finally:
-        pool.free()
+    dec, roof, cpu = None, None, None
+    if not args.skip_headline:
+        dec, roof, keep = run_decode(args, torch, ft, synth, HostPool)
+        pool, wl, tr, fq, L_phys = keep
+        try:
+            if not args.no_cpu_baseline:
+                log("timing the CPU oracle on the host")
+                cpu = cpu_baseline(args, pool, wl, tr, fq, L_phys, args.cpu_budget_s, args.cpu_budget_1t_s)
+        finally:
+            pool.free()
     c2 = run_config2(args, torch, ft, synth, HostPool) if args.config2 and args.workload == HEADLINE else None
     pre = run_prefill(args, torch, ft, synth, HostPool) if args.prefill else None
     mxr = run_mxfp4(args, torch, ft, synth, HostPool) if args.mxfp4 else None
     rep = run_placement(args, ft, synth) if args.replay else None
+    if dec is None:
+        print(json.dumps({"profiling_run": True, "decode_L40": c2, "prefill": pre, "mxfp4": mxr,
+                          "placement_replay": rep}), flush=True)
+        return
     out = {
         "metric": METRIC, "value": round(dec["tok_s"], 3), "unit": "tok/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dec["ms_per_step"], 4),
