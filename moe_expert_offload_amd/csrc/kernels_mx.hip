@@ -226,13 +226,27 @@ __global__ __launch_bounds__(256) void mx_gateup_rows_kernel(
   }
 }
 
-template <int NT, int NB>  // NB: blocks per lane over 4 rows (d_ff <= 512 * NB)
+// h rows staged in LDS with each 32-element block at a stride of 36 floats: a lane
+// reads the 32 consecutive values of its block, and at that stride the 16-byte reads
+// of 16 consecutive lanes (blocks) fall on distinct banks (a 32-float stride would put
+// every lane of the wavefront on the same banks).
+constexpr int kHStride = 36;
+
+// Token rows of h a down block stages at once: at most 64 KB of padded rows.
+__host__ __device__ inline int mx_down_rows_per_batch(int nt_max, int d_ff) {
+  const int per_row = (d_ff / 32) * kHStride;
+  const int fit = 16384 / per_row;
+  return nt_max < (fit > 1 ? fit : 1) ? nt_max : (fit > 1 ? fit : 1);
+}
+
+// C64: d_ff = 2048 with RW = 8 (64 blocks per row, NB = 8): lane l owns block l of
+// every one of its rows, so it reads its 32 h values of a token from LDS once.
+template <int NT, int NB, int RW, bool C64 = false>  // NB: blocks per lane over RW rows (RW * d_ff <= 2048 * NB)
 __global__ __launch_bounds__(256) void mx_down_rows_kernel(
     int d, int d_ff, const uint8_t* __restrict__ slots, const int32_t* __restrict__ group_slot,
     const int32_t* __restrict__ offsets, int g_begin, int blocks_per_group, const float* __restrict__ h,
     float* __restrict__ out, const int32_t* __restrict__ g_hi) {
-  constexpr int RW = 4;  // W_down rows per wavefront
-  extern __shared__ float sh[];  // h rows of a batch of tokens [nt][d_ff], read by all 4 wavefronts
+  extern __shared__ float sh[];  // h rows of a batch of tokens, [nt][d_ff / 32][kHStride]
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
@@ -257,30 +271,59 @@ __global__ __launch_bounds__(256) void mx_down_rows_kernel(
     cv[j] = buf_ld16(rec, in ? dc + 16u * p : kOOB);
     sv[j] = buf_ld8(rec, in ? ds + p : kOOB);
   }
-  const int per = min(NT, max(1, 16384 / d_ff));  // token rows per batch: at most 64 KB of h
+  const int per = mx_down_rows_per_batch(NT, d_ff);
+  const int tok_stride = nb * kHStride;
   for (int tb = 0; tb < n; tb += per) {
     const int nt = min(per, n - tb);
     __syncthreads();  // the previous batch's h is no longer read
-    for (int i = threadIdx.x * 4; i < nt * d_ff; i += 256 * 4)
-      *reinterpret_cast<float4*>(sh + i) = *reinterpret_cast<const float4*>(h + (size_t)(r0 + tb) * d_ff + i);
+    for (int i = threadIdx.x * 4; i < nt * d_ff; i += 256 * 4) {
+      const int ti = i / d_ff, e = i - ti * d_ff;
+      *reinterpret_cast<float4*>(sh + ti * tok_stride + (e >> 5) * kHStride + (e & 31)) =
+          *reinterpret_cast<const float4*>(h + (size_t)(r0 + tb) * d_ff + i);
+    }
     __syncthreads();
     float acc[NT][RW];
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
       for (int r = 0; r < RW; ++r) acc[i][r] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int p = lane + 64 * j;
-      if (p >= span) continue;
-      const int rr = p / nb, cb = p - rr * nb;
-      const float sc = e8m0(sv[j]);
+    if constexpr (C64) {
+      // row j of the wave is code block j of the lane; its h block is block `lane`
+      // one code word (8 elements) of every row at a time against the same 8 h values
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         if (i >= nt) continue;
-        const float v = block_dot_f32(cv[j], sh + i * d_ff + 32 * cb) * sc;
+        const float* hb = sh + i * tok_stride + lane * kHStride;
 #pragma unroll
-        for (int r = 0; r < RW; ++r) acc[i][r] += rr == r ? v : 0.0f;
+        for (int q = 0; q < 4; ++q) {
+          const float4 h0 = *reinterpret_cast<const float4*>(hb + 8 * q);
+          const float4 h1 = *reinterpret_cast<const float4*>(hb + 8 * q + 4);
+#pragma unroll
+          for (int j = 0; j < RW; ++j) {
+            uint32_t w = q == 0 ? cv[j].x : q == 1 ? cv[j].y : q == 2 ? cv[j].z : cv[j].w;
+            // converted where used: hoisted out of the token loop, the conversions of all
+            // rows would hold 256 values per lane
+            asm volatile("" : "+v"(w));
+            acc[i][j] = word_dot_f32(w, h0, h1, acc[i][j]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < RW; ++j) acc[i][j] *= e8m0(sv[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int p = lane + 64 * j;
+        if (p >= span) continue;
+        const int rr = p / nb, cb = p - rr * nb;
+        const float sc = e8m0(sv[j]);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          if (i >= nt) continue;
+          const float v = block_dot_f32(cv[j], sh + i * tok_stride + cb * kHStride) * sc;
+#pragma unroll
+          for (int r = 0; r < RW; ++r) acc[i][r] += rr == r ? v : 0.0f;
+        }
       }
     }
     if (span == 0) continue;
@@ -747,22 +790,36 @@ int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t*
   if (d > 8192 || d_ff > 4096) return fail(FT_EINVAL, "mx_ffn_rows: need d <= 8192 and d_ff <= 4096");
   // gate/up: 2 row pairs per wavefront up to d = 4096 (2 blocks per lane), 1 beyond
   const int rg = d <= 4096 ? 2 : 1;
-  const int bpg_up = (d_ff + 4 * rg - 1) / (4 * rg), bpg_dn = (d + 15) / 16;
+  const int bpg_up = (d_ff + 4 * rg - 1) / (4 * rg);
   const int nt = max_rows <= 1 ? 1 : max_rows <= 2 ? 2 : max_rows <= 4 ? 4 : 8;
-  // blocks per lane: gate/up ceil(d/32/64), down ceil(4*d_ff/32/64)
-  const int nbu = (d / 32 + 63) / 64, nbd = (d_ff / 8 + 63) / 64;
+  // blocks per lane: gate/up ceil(d/32/64); down ceil(RW*d_ff/32/64) with RW = 8 rows per
+  // wavefront up to d_ff = 2048, 4 beyond
+  const int nbu = (d / 32 + 63) / 64;
+  const int rw = d_ff <= 2048 ? 8 : 4;
+  const int nbd = (rw * (d_ff / 32) + 63) / 64;
+  const int bpg_dn = (d + 4 * rw - 1) / (4 * rw);
 #define FT_MX_UP(NB)                                                                                         \
   timed_launch(mx_gateup_rows_kernel<NB, NB <= 2 ? 2 : 1>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
                slots, group_slot, offsets, perm, g_begin, bpg_up, h, g_hi)
-#define FT_MX_DN(NT, NB)                                                                                     \
-  timed_launch_shm(mx_down_rows_kernel<NT, NB>, dim3(ng * bpg_dn), dim3(256),                                 \
-                   (size_t)std::min(NT, std::max(1, 16384 / d_ff)) * d_ff * 4, s, ev, 1, d,                     \
+#define FT_MX_DN(NT, NB, RW)                                                                                 \
+  timed_launch_shm(mx_down_rows_kernel<NT, NB, RW>, dim3(ng * bpg_dn), dim3(256),                             \
+                   (size_t)mx_down_rows_per_batch(NT, d_ff) * (d_ff / 32) * kHStride * 4, s, ev, 1, d,         \
+                   d_ff, slots, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out, g_hi)
+#define FT_MX_DN64(NT)                                                                                       \
+  timed_launch_shm(mx_down_rows_kernel<NT, 8, 8, true>, dim3(ng * bpg_dn), dim3(256),                          \
+                   (size_t)mx_down_rows_per_batch(NT, d_ff) * (d_ff / 32) * kHStride * 4, s, ev, 1, d,         \
                    d_ff, slots, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out, g_hi)
 #define FT_MX_ROWS(NT)                                                     \
   if (nbu <= 1) FT_MX_UP(1); else if (nbu <= 2) FT_MX_UP(2); else FT_MX_UP(4);            \
   if (int rc = launched("mx_gateup_rows")) return rc;                      \
-  if (nbd <= 1) FT_MX_DN(NT, 1); else if (nbd <= 2) FT_MX_DN(NT, 2);       \
-  else if (nbd <= 4) FT_MX_DN(NT, 4); else FT_MX_DN(NT, 8);                \
+  if (rw == 8 && d_ff == 2048) {                                          \
+    FT_MX_DN64(NT);                                                        \
+  } else if (rw == 8) {                                                    \
+    if (nbd <= 1) FT_MX_DN(NT, 1, 8); else if (nbd <= 2) FT_MX_DN(NT, 2, 8);  \
+    else if (nbd <= 4) FT_MX_DN(NT, 4, 8); else FT_MX_DN(NT, 8, 8);         \
+  } else {                                                                 \
+    FT_MX_DN(NT, 8, 4);                                                    \
+  }                                                                        \
   return launched("mx_down_rows");
   switch (nt) {
     case 1: { FT_MX_ROWS(1) }
@@ -773,6 +830,7 @@ int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t*
 #undef FT_MX_UP
 #undef FT_MX_DN
 #undef FT_MX_ROWS
+#undef FT_MX_DN64
 }
 
 size_t mx_act_ws_bytes(int rows, int n) { return (size_t)rows * n + (size_t)rows * (n / 32); }
