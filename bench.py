@@ -166,8 +166,22 @@ def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warm
     compute = torch.cuda.current_stream()
     st_call = ft.ft_step_stats()
     calls = []
+    graph_mode = getattr(args, "mode", "eager") == "graph"
+    graph = None
+    if graph_mode:
+        # fixed buffers the graph reads and writes; each step's inputs are copied in
+        # (inside the timed region)
+        xb = torch.empty((s.L, T, s.d), dtype=torch.int16, device="cuda")
+        ab = torch.empty((s.L, T, s.E), dtype=torch.uint8, device="cuda")
+        yb = torch.empty((s.L, T, s.d), dtype=torch.float32, device="cuda")
+        graph = ft.ft_decode_graph_create(ctx, T, xb, wr, ab, yb)
 
     def step(st, record):
+        if graph_mode:
+            xb.copy_(xs[st])
+            ab.copy_(allowed_d[st])
+            ft.ft_decode_graph_launch(graph, compute)
+            return
         for l in range(s.L):
             ft.ft_moe_decode_layer(ctx, l, xs[st, l], T, wr[l], allowed_d[st, l], ys[l], compute,
                                    None, st_call)
@@ -188,18 +202,25 @@ def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warm
             step(st, True)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        if graph_mode:
+            ft.ft_decode_graph_status(graph)
         stats = ft.ft_get_stats(ctx)
         # second timed region over the next steps of the same trace: every grouped-FFN
-        # kernel launched with start/stop events (for the roofline)
-        ft.ft_profile_enable(ctx, True)
-        t2 = time.perf_counter()
-        for st in range(steps_total, steps_total + args.steps):
-            step(st, False)
-        torch.cuda.synchronize()
-        t3 = time.perf_counter()
-        prof = ft.ft_profile_read(ctx)
-        ft.ft_profile_enable(ctx, False)
+        # kernel launched with start/stop events (for the roofline; eager calls only)
+        prof = {"launches": 0, "ms_gateup": 0.0, "ms_down": 0.0, "bytes_gateup": 0.0, "bytes_down": 0.0}
+        t2 = t3 = time.perf_counter()
+        if not graph_mode:
+            ft.ft_profile_enable(ctx, True)
+            t2 = time.perf_counter()
+            for st in range(steps_total, steps_total + args.steps):
+                step(st, False)
+            torch.cuda.synchronize()
+            t3 = time.perf_counter()
+            prof = ft.ft_profile_read(ctx)
+            ft.ft_profile_enable(ctx, False)
     finally:
+        if graph:
+            ft.ft_decode_graph_destroy(graph)
         ft.ft_destroy(ctx)
     elapsed = t1 - t0
     ms_gu = prof["ms_gateup"] / max(prof["launches"], 1)
@@ -214,7 +235,11 @@ def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warm
     for hits, misses, q, n_c, *_ in calls:
         floor_s += max((hits + q) * S / (HBM_PEAK_GBS * 1e9), phased_time(misses, q, S, B_P, B_H))
     reads = max(stats["reads"], 1)
+    if graph_mode:
+        # per-call records are not collected in graph mode: the floor from the counters
+        floor_s = None
     res = {
+        "mode": "graph" if graph_mode else "eager",
         "tok_s": args.steps * T / elapsed,
         "ms_per_step": elapsed / args.steps * 1e3,
         "workload": wl.name, "T": T, "L": s.L, "n_slots": N, "L_phys": L_phys, "cache_warmup_steps": warm,
@@ -225,7 +250,7 @@ def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warm
         "miss_rate_unique": stats["unique_misses"] / max(stats["unique_hits"] + stats["unique_misses"], 1),
         "fills_per_step": stats["fills"] / args.steps, "cpu_experts_per_step": stats["cpu_experts"] / args.steps,
         "h2d_GB_per_step": stats["h2d_bytes"] / args.steps / 1e9,
-        "modelled_floor_ms_per_step": floor_s / args.steps * 1e3,
+        "modelled_floor_ms_per_step": floor_s / args.steps * 1e3 if floor_s is not None else None,
         "host_cpu_branch_ms_per_step": sum(c[4] for c in calls) / args.steps / 1e3,
         "host_call_us": {
             "route": float(np.mean([c[6] for c in calls])) if calls else 0.0,
@@ -646,6 +671,8 @@ def main():
     ap.add_argument("--frac-q16", type=int, default=-1, help="override the measured fetch fraction")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-graph", dest="graph", action="store_false", default=True,
+                    help="skip the headline decode replayed from the graph-resident step")
     ap.add_argument("--no-config2", dest="config2", action="store_false", default=True,
                     help="skip the 40-layer d=2048 legs (batch 1, min_fill = 0, batch 8)")
     ap.add_argument("--c2-steps", type=int, default=64)
@@ -695,10 +722,20 @@ def main():
 
     ft.lib()
     dec, roof, cpu = None, None, None
+    gdec = None
     if not args.skip_headline:
         dec, roof, keep = run_decode(args, torch, ft, synth, HostPool)
         pool, wl, tr, fq, L_phys = keep
         try:
+            if args.graph:
+                # the same workload, pool and trace, each step replayed from one HIP graph
+                log("decode through the graph-resident step")
+                g, _, _ = run_decode(args, torch, ft, synth, HostPool, args.workload, args.steps, args.warmup,
+                                     {"mode": "graph"}, pool)
+                gdec = {k: g[k] for k in ("mode", "tok_s", "ms_per_step", "miss_rate_reads", "fills_per_step",
+                                          "cpu_experts_per_step", "h2d_GB_per_step", "cache_warmup_steps",
+                                          "timed_steps", "B_P_GBs", "B_H_GBs", "frac_q16")}
+                gdec["eager_tok_s"] = dec["tok_s"]
             if not args.no_cpu_baseline:
                 log("timing the CPU oracle on the host")
                 cpu = cpu_baseline(args, pool, wl, tr, fq, L_phys, args.cpu_budget_s, args.cpu_budget_1t_s)
@@ -720,7 +757,7 @@ def main():
         "config": {"workload": dec["workload"], "global_batch": dec["T"], "layers": dec["L"],
                    "cache_slots": dec["n_slots"], "cache_warmup_steps": dec["cache_warmup_steps"],
                    "pool_physical_layers": dec["L_phys"], "parallelism": "single-gpu"},
-        "roofline": roof, "cpu_baseline": cpu, "decode": dec, "decode_L40": c2,
+        "roofline": roof, "cpu_baseline": cpu, "decode": dec, "decode_graph": gdec, "decode_L40": c2,
         "prefill": pre, "mxfp4": mxr,
         "placement_replay": rep,
     }

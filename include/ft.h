@@ -420,6 +420,38 @@ int ft_moe_decode_layer(ft_ctx_t ctx, int32_t layer, const void* x, int32_t T,
                         const void* w_router, const uint8_t* allowed, float* y, void* compute,
                         ft_plan* plan, ft_step_stats* stats);
 
+/* ---- graph-resident decode step ([FT] §4.1 "Graph-resident CPU execution") -------
+ * One decode step through every layer (0..L-1 in order) replayed from one HIP graph.
+ * Per layer, on one chain: the router with the device's cache decisions, the fills of
+ * F read over PCIe, the grouped FFN of G = H then F, and the combine; forked off after
+ * the router, a host node that takes the host controller's decisions from the
+ * published ids, checks them against the device's (plan hash) and runs the CPU branch
+ * (C) on the worker pool; the combine waits for both.  The same kernels, decisions
+ * and arithmetic as ft_moe_decode_layer.
+ * Fixed buffers, owned by the caller, read or written at every launch: x device bf16
+ * [L, T, d] (layer l's input at x + l*T*d), allowed device uint8 [L, T, E] or NULL,
+ * y device fp32 [L, T, d]; w_router: host array of L device pointers (bf16 [E, d]).
+ * The caller writes each step's inputs into x (and allowed) before the launch.
+ * create: captures and instantiates the graph for T tokens (1 <= T <= min(T_max,
+ * FT_PLAN_CAP / k, 64)).
+ * launch: enqueues one step on `stream` (asynchronous) after everything the context
+ * issued before; first returns the error, if any, that an earlier step's host node
+ * met (FT_EHIP: the device's decisions differed from the host's; FT_EINVAL: a token
+ * allowed fewer than k experts).  The device keeps deciding for that step's later
+ * layers while the host nodes stop, so the cache was emptied; that step's y is
+ * undefined from the failing layer on.  Re-captures the graph
+ * when a resize or a larger cache state changed what the kernels were built with.
+ * While steps are in flight the host nodes update the context's host state: make no
+ * other call on the context (except further launches on the same stream) until the
+ * stream is synchronised.  status: the error an earlier step's host node met, or
+ * FT_OK (clears it).  FT_EBUSY while a prefill is open. */
+typedef struct ft_decode_graph* ft_decode_graph_t;
+int ft_decode_graph_create(ft_ctx_t ctx, int32_t T, const void* x, const void* const* w_router,
+                           const uint8_t* allowed, float* y, ft_decode_graph_t* out);
+int ft_decode_graph_launch(ft_decode_graph_t graph, void* stream);
+int ft_decode_graph_status(ft_decode_graph_t graph);
+int ft_decode_graph_destroy(ft_decode_graph_t graph);
+
 /* Prefill ([FT] §3.1; §5.3 "Pipelined prefill"), layers in order 0..L-1.
  * Full-layer double buffering, with overlap on and at least 2E slots:
  * begin: reserve two buffers of E slots (victim order) and start loading layer 0

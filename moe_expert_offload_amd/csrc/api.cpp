@@ -7,6 +7,7 @@
 #include <immintrin.h>
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <cstring>
 #include <string>
@@ -817,6 +818,250 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
   }
   c->last_T = T;
   c->last_return_us = now_us();
+  return FT_OK;
+}
+
+}  // extern "C"
+
+// ---- graph-resident decode step ------------------------------------------------------
+// [FT] §4.1 "Graph-resident CPU execution": a whole decode step replayed from one HIP
+// graph.  Per layer: the router with the device's decisions, the fills, the grouped
+// FFN and the combine on one chain; forked off after the router, a host node that
+// takes the host controller's decisions from the published ids, checks them against
+// the device's (plan hash) and runs the CPU branch; the combine waits for both.
+
+struct ft_decode_graph {
+  ft_ctx* c = nullptr;
+  int T = 0;
+  const uint16_t* x = nullptr;
+  std::vector<const uint16_t*> w_router;
+  const uint8_t* allowed = nullptr;
+  float* y = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipStream_t cap = nullptr, side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  // what the captured kernels have baked in; a change (resize, a larger device state)
+  // means a new capture
+  const uint8_t* slots = nullptr;
+  int n_slots = -1;
+  ft::DevCache dc{};
+  struct NodeArg {
+    ft_decode_graph* g;
+    int layer;
+  };
+  std::vector<NodeArg> args;
+  std::atomic<int> status{FT_OK};  // first error a host node met since the last report
+  std::string error;
+  ft_plan plan{};
+};
+
+namespace {
+
+// The host node of one layer.  Runs on the runtime's callback thread once the layer's
+// router finished (its publication to pinned memory is complete); calls no HIP API.
+void decode_graph_host_node(void* p) {
+  auto* a = static_cast<ft_decode_graph::NodeArg*>(p);
+  ft_decode_graph* g = a->g;
+  ft_ctx* c = g->c;
+  const int T = g->T, k = c->shape.k, d = c->shape.d, P = T * k, layer = a->layer;
+  std::memset(c->h_partial, 0, sizeof(float) * (size_t)T * d);
+  if (g->status.load(std::memory_order_relaxed) != FT_OK) return;  // after an error, no more decisions
+  // The device keeps deciding (and filling) for this step's later layers while the
+  // host nodes stop: after any error no slot's contents can be trusted.
+  auto failed = [&](int st, const char* msg, bool) {
+    c->cache->clear_residency();
+    c->dev_dirty = true;
+    int expected = FT_OK;
+    if (g->status.compare_exchange_strong(expected, st)) g->error = msg;
+  };
+  for (int i = 0; i < P; ++i)
+    if (c->h_idx[i] < 0) return failed(FT_EINVAL, "decode graph: a token allows fewer than k experts", false);
+  ft_plan* pl = &g->plan;
+  if (c->cache->lookup(layer, c->h_idx, T, k, c->cfg.frac_q16, c->cfg.min_fill, c->cfg.max_fetch, pl) != FT_OK)
+    return failed(FT_EINVAL, "decode graph: host lookup failed", true);
+  const ft::DevPlan& dp = *c->h_plan;
+  if (dp.n_u != pl->n_u || dp.q != pl->q || dp.hash != host_plan_hash(*pl, P))
+    return failed(FT_EHIP, "decode graph: device and host cache decisions differ", true);
+  c->cache->stats.h2d_bytes += (int64_t)pl->q * (int64_t)c->S;
+  const int q = pl->q, n_c = pl->n_c;
+  if (n_c == 0) return;
+  c->cpu_ex.resize(n_c);
+  for (int i = 0; i < n_c; ++i) {
+    ft::CpuExpert& ex = c->cpu_ex[i];
+    const int e = pl->M[q + i];
+    ex.rec = c->record(layer, e);
+    ex.n_use = 0;
+    for (int pr = 0; pr < P; ++pr)
+      if (c->h_idx[pr] == e && ex.n_use < 64) ex.use[ex.n_use++] = ft::CpuUse{pr / k, c->h_gates[pr]};
+  }
+  ft::cpu_pool_submit(c->cpu, c->h_x, T, d, c->shape.d_ff, c->shape.fmt, c->cpu_ex.data(), n_c, c->h_partial);
+  ft::cpu_pool_wait(c->cpu);
+}
+
+void release_capture(ft_decode_graph* g) {
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  g->exec = nullptr;
+  g->graph = nullptr;
+}
+
+// Captures the step on the graph's private streams.
+int capture_decode_graph(ft_decode_graph* g) {
+  ft_ctx* c = g->c;
+  release_capture(g);
+  const int T = g->T, k = c->shape.k, d = c->shape.d, E = c->shape.E, d_ff = c->shape.d_ff, L = c->shape.L;
+  const int P = T * k;
+  int32_t* d_idx = c->wsp<int32_t>(c->cv.idx);
+  float* d_gates = c->wsp<float>(c->cv.gates);
+  float* d_h = c->wsp<float>(c->cv.h);
+  float* d_out = c->wsp<float>(c->cv.out);
+  ft::DecideArgs da{};
+  da.dc = c->dc;
+  da.plan = c->d_plan;
+  da.pub = c->h_plan;
+  da.fq = c->cfg.frac_q16;
+  da.min_fill = c->cfg.min_fill;
+  da.max_fetch = c->cfg.max_fetch;
+  FT_HIP(hipStreamBeginCapture(g->cap, hipStreamCaptureModeRelaxed));
+  int rc = FT_OK;
+  for (int l = 0; l < L && rc == FT_OK; ++l) {
+    const uint16_t* xl = g->x + (size_t)l * T * d;
+    const uint8_t* al = g->allowed ? g->allowed + (size_t)l * T * E : nullptr;
+    da.layer = l;
+    // sequence number 0 in the publication: the eager path never waits for it
+    rc = ft::launch_router_decode(xl, g->w_router[l], al, T, d, E, k, c->wsp<float>(c->cv.logits), d_idx, d_gates,
+                                  c->wsp<unsigned int>(c->cv.ticket), c->h_idx, c->h_gates, c->h_x, c->h_flag, 0u,
+                                  g->cap, &da);
+    if (rc) break;
+    if (hipEventRecord(g->fork, g->cap) != hipSuccess) {
+      rc = fail(FT_EHIP, "decode graph: capture of the fork failed");
+      break;
+    }
+    if ((rc = ft::launch_fill(c->record(l, 0), c->S, E, c->slots, c->cache->n_slots(), c->d_plan, g->cap))) break;
+    if (c->mx)
+      rc = ft::launch_mx_ffn_rows(xl, d, d_ff, k, c->slots, c->d_plan->G_slot, c->d_plan->offsets, c->d_plan->perm, 0,
+                                  P, T, d_h, d_out, g->cap, nullptr, &c->d_plan->n_g);
+    else
+      rc = ft::launch_ffn_rows(xl, d, d_ff, k, reinterpret_cast<const uint16_t*>(c->slots), c->d_plan->G_slot,
+                               c->d_plan->offsets, c->d_plan->perm, 0, P, T, d_h, d_out, g->cap, nullptr,
+                               &c->d_plan->n_g);
+    if (rc) break;
+    // the host node depends on the router alone; captured after the fills and the FFN
+    // so that a runtime walking the nodes in capture order submits those first
+    if (hipStreamWaitEvent(g->side, g->fork, 0) != hipSuccess ||
+        hipLaunchHostFunc(g->side, decode_graph_host_node, &g->args[l]) != hipSuccess ||
+        hipEventRecord(g->join, g->side) != hipSuccess || hipStreamWaitEvent(g->cap, g->join, 0) != hipSuccess) {
+      rc = fail(FT_EHIP, "decode graph: capture of the host node failed");
+      break;
+    }
+    rc = ft::launch_combine(d_out, c->d_plan->inv, d_gates, c->h_partial, T, k, d, g->y + (size_t)l * T * d, g->cap);
+  }
+  hipGraph_t graph = nullptr;
+  const hipError_t ec = hipStreamEndCapture(g->cap, &graph);
+  if (rc) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return rc;
+  }
+  if (ec != hipSuccess || !graph) return fail(FT_EHIP, std::string("decode graph: end of capture: ") + hipGetErrorString(ec));
+  g->graph = graph;
+  const hipError_t ei = hipGraphInstantiate(&g->exec, graph, nullptr, nullptr, 0);
+  if (ei != hipSuccess) {
+    release_capture(g);
+    return fail(FT_EHIP, std::string("decode graph: instantiate: ") + hipGetErrorString(ei));
+  }
+  g->slots = c->slots;
+  g->n_slots = c->cache->n_slots();
+  g->dc = c->dc;
+  return FT_OK;
+}
+
+bool capture_stale(const ft_decode_graph* g) {
+  const ft_ctx* c = g->c;
+  return !g->exec || g->slots != c->slots || g->n_slots != c->cache->n_slots() || g->dc.where != c->dc.where ||
+         g->dc.slot_key != c->dc.slot_key || g->dc.slot_stamp != c->dc.slot_stamp || g->dc.clock != c->dc.clock ||
+         g->dc.n_slots != c->dc.n_slots;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ft_decode_graph_create(ft_ctx_t c, int32_t T, const void* x, const void* const* w_router, const uint8_t* allowed,
+                           float* y, ft_decode_graph_t* out) {
+  if (!out) return fail(FT_EINVAL, "decode_graph_create: null out");
+  *out = nullptr;
+  if (!c || !x || !w_router || !y) return fail(FT_EINVAL, "decode_graph_create: null argument");
+  if (!c->dev) return fail(FT_EINVAL, "decode_graph_create: context has no device path");
+  if (T < 1 || T > c->t_dec) return fail(FT_EINVAL, "decode_graph_create: T out of range");
+  for (int l = 0; l < c->shape.L; ++l)
+    if (!w_router[l]) return fail(FT_EINVAL, "decode_graph_create: null router weights");
+  FT_HIP(hipSetDevice(c->device));
+  auto* g = new ft_decode_graph();
+  g->c = c;
+  g->T = T;
+  g->x = static_cast<const uint16_t*>(x);
+  g->allowed = allowed;
+  g->y = y;
+  for (int l = 0; l < c->shape.L; ++l) g->w_router.push_back(static_cast<const uint16_t*>(w_router[l]));
+  g->args.resize(c->shape.L);
+  for (int l = 0; l < c->shape.L; ++l) g->args[l] = ft_decode_graph::NodeArg{g, l};
+  if (hipStreamCreateWithFlags(&g->cap, hipStreamNonBlocking) != hipSuccess ||
+      hipStreamCreateWithFlags(&g->side, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&g->fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&g->join, hipEventDisableTiming) != hipSuccess) {
+    ft_decode_graph_destroy(g);
+    return fail(FT_EHIP, "decode_graph_create: stream or event creation failed");
+  }
+  if (c->dev_dirty) {
+    if (int rc = upload_cache(c)) {
+      ft_decode_graph_destroy(g);
+      return rc;
+    }
+  }
+  if (int rc = capture_decode_graph(g)) {
+    ft_decode_graph_destroy(g);
+    return rc;
+  }
+  *out = g;
+  return FT_OK;
+}
+
+int ft_decode_graph_status(ft_decode_graph_t g) {
+  if (!g) return fail(FT_EINVAL, "decode_graph_status: null");
+  const int st = g->status.exchange(FT_OK);
+  if (st != FT_OK) return fail(st, g->error);
+  return FT_OK;
+}
+
+int ft_decode_graph_launch(ft_decode_graph_t g, void* stream) {
+  if (!g) return fail(FT_EINVAL, "decode_graph_launch: null");
+  ft_ctx* c = g->c;
+  if (int st = ft_decode_graph_status(g)) return st;
+  if (c->cache->prefill_open()) return fail(FT_EBUSY, "decode_graph_launch: a prefill is open");
+  FT_HIP(hipSetDevice(c->device));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FT_HIP(hipStreamWaitEvent(s, c->ev_done, 0));
+  if (c->dev_dirty) {
+    FT_HIP(hipStreamSynchronize(s));
+    if (int rc = upload_cache(c)) return rc;
+  }
+  if (capture_stale(g))
+    if (int rc = capture_decode_graph(g)) return rc;
+  FT_HIP(hipGraphLaunch(g->exec, s));
+  FT_HIP(hipEventRecord(c->ev_done, s));
+  return FT_OK;
+}
+
+int ft_decode_graph_destroy(ft_decode_graph_t g) {
+  if (!g) return FT_OK;
+  if (g->cap) (void)hipStreamSynchronize(g->cap);
+  release_capture(g);
+  if (g->fork) (void)hipEventDestroy(g->fork);
+  if (g->join) (void)hipEventDestroy(g->join);
+  if (g->cap) (void)hipStreamDestroy(g->cap);
+  if (g->side) (void)hipStreamDestroy(g->side);
+  delete g;
   return FT_OK;
 }
 

@@ -42,7 +42,8 @@ EXPORTED = [
     "ft_moe_prefill_end", "ft_prefill_slot", "ft_profile_enable", "ft_profile_read", "ft_host_experts",
     "ft_frac_q16_contended", "ft_fetch_fraction_q16", "ft_recommend_hybrid", "ft_bench_bw_contended",
     "ft_bw_profile_path", "ft_bw_profile_save", "ft_bw_profile_load", "ft_expert_cache_prefill_on_demand",
-    "ft_replay_placement", "ft_layer_routing", "ft_permute_noalloc", "ft_permute_noalloc_max_scratch_bytes",
+    "ft_replay_placement", "ft_layer_routing", "ft_decode_graph_create",
+    "ft_decode_graph_launch", "ft_decode_graph_status", "ft_decode_graph_destroy", "ft_permute_noalloc", "ft_permute_noalloc_max_scratch_bytes",
 ]
 
 
@@ -165,6 +166,10 @@ def lib():
             "ft_moe_prefill_end": (C.c_int, [P]),
             "ft_prefill_slot": (I, [P, I, I]),
             "ft_layer_routing": (C.c_int, [P, P, P, I, P]),
+            "ft_decode_graph_create": (C.c_int, [P, I, P, C.POINTER(P), P, P, C.POINTER(P)]),
+            "ft_decode_graph_launch": (C.c_int, [P, P]),
+            "ft_decode_graph_status": (C.c_int, [P]),
+            "ft_decode_graph_destroy": (C.c_int, [P]),
             "ft_profile_enable": (C.c_int, [P, I]),
             "ft_profile_read": (C.c_int, [P, C.POINTER(ft_profile)]),
             "ft_host_experts": (C.c_int, [P, I, I, I, I, C.POINTER(P), P, P, P, I, I, P]),
@@ -455,6 +460,27 @@ def ft_moe_prefill_end(ctx):
 
 def ft_layer_routing(ctx, idx, gates, T, stream=None):
     return _check("ft_layer_routing", lib().ft_layer_routing(ctx, _ptr(idx), _ptr(gates), T, _stream(stream)))
+
+
+def ft_decode_graph_create(ctx, T, x, w_router, allowed, y):
+    """w_router: sequence of L device tensors or addresses."""
+    arr = (P * len(w_router))(*[_ptr(w) for w in w_router])
+    out = P()
+    _check("ft_decode_graph_create", lib().ft_decode_graph_create(ctx, T, _ptr(x), arr, _ptr(allowed), _ptr(y),
+                                                                  C.byref(out)))
+    return out.value
+
+
+def ft_decode_graph_launch(graph, stream=None):
+    return _check("ft_decode_graph_launch", lib().ft_decode_graph_launch(graph, _stream(stream)))
+
+
+def ft_decode_graph_status(graph):
+    return _check("ft_decode_graph_status", lib().ft_decode_graph_status(graph))
+
+
+def ft_decode_graph_destroy(graph):
+    return _check("ft_decode_graph_destroy", lib().ft_decode_graph_destroy(graph))
 
 
 def ft_prefill_slot(ctx, layer, expert):
