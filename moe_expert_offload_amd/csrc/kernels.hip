@@ -1098,8 +1098,8 @@ __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
 // (`buffer_load ... lds`, 16 bytes per lane, no registers in between): K runs in
 // stages of 32 elements through 4 buffers per operand ([256][32] bf16, 16 KB), the
 // loads of stage s + 3 in flight while stage s multiplies.  In a buffer, 16-byte
-// piece p of row r sits at piece p ^ ((r >> 1) & 3), so the 8 lanes of one LDS read
-// phase hit 8 different bank groups.  Inside a stage, MFMA slice i (0, 1) takes in
+// piece p of row r sits at piece p ^ lds_swz(r), so the 8 or 16 lanes of one LDS read
+// phase hit as many different bank groups.  Inside a stage, MFMA slice i (0, 1) takes in
 // lane group g the elements 16i + 8g .. +7.
 //
 // The loop's loads are issued by inline asm and waited for by one explicit
@@ -1114,8 +1114,13 @@ constexpr int XB = XM * XK;             // one buffer, bf16 elements (16 KB)
 
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
+// Physical position of 16-byte piece p of buffer row r: p ^ swz(r).  A read phase of 8
+// lanes (rows r..r+7, 32 banks) or of 16 lanes (rows r..r+15, 64 banks) then touches
+// 8 or 16 different bank groups.
+__device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
 __device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* buf, int r, int piece) {
-  const uint4 u = *reinterpret_cast<const uint4*>(buf + r * XK + ((piece ^ ((r >> 1) & 3)) * 8));
+  const uint4 u = *reinterpret_cast<const uint4*>(buf + r * XK + ((piece ^ lds_swz(r)) * 8));
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
@@ -1130,7 +1135,7 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, uint32_t o
 // Load q (0..3) of wave w covers buffer rows 16 (4w + q) + lane/4, physical piece
 // lane%4; the lane's source piece is the logical one stored there.
 __device__ __forceinline__ int lds_load_row(int wave, int q, int lane) { return 16 * (4 * wave + q) + (lane >> 2); }
-__device__ __forceinline__ int lds_load_piece(int r, int lane) { return (lane & 3) ^ ((r >> 1) & 3); }
+__device__ __forceinline__ int lds_load_piece(int r, int lane) { return (lane & 3) ^ lds_swz(r); }
 
 // acc[a][c] += A(row subtile a) x B(column subtile c of this wave) over one stage.
 // Slice 1's operands are read from LDS while slice 0 multiplies; `issue(t)` sends
