@@ -1095,12 +1095,16 @@ __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
 // one expert (8 row subtiles of 32; the usual ~200 tokens of an 8k chunk in one
 // pass) and 256 weight rows ("B columns"), 64 per wave: every weight element is
 // read from HBM once per pass.  Both operands go straight from memory into LDS
-// (`buffer_load ... lds`, 16 bytes per lane, no registers in between): K runs in
-// stages of 32 elements through 4 buffers per operand ([256][32] bf16, 16 KB), the
-// loads of stage s + 3 in flight while stage s multiplies.  In a buffer, 16-byte
-// piece p of row r sits at piece p ^ lds_swz(r), so the 8 or 16 lanes of one LDS read
-// phase hit as many different bank groups.  Inside a stage, MFMA slice i (0, 1) takes in
-// lane group g the elements 16i + 8g .. +7.
+// (`buffer_load ... lds`, 16 bytes per lane, no registers in between).  K runs in
+// stages of 32 elements.  Token rows go through 4 buffers ([256][32] bf16, 16 KB), the
+// loads of stage s + 3 in flight while stage s multiplies.  Weights go through 3
+// buffers of double stages ([256][64] bf16, 32 KB): each weight row is read 128 bytes
+// at a time, since a stream of 64-byte pieces of many rows reaches only ~4.5 TB/s
+// where 128-byte pieces reach ~6.3 TB/s (probe at one block per compute unit); half a
+// double stage is issued per stage, two to four stages ahead.  160 KB of LDS in all.
+// In a buffer, 16-byte piece p of row r sits at piece p ^ swz(r), so the 8 or 16
+// lanes of one LDS read phase hit as many different bank groups.  Inside a stage,
+// MFMA slice i (0, 1) takes in lane group g the elements 16i + 8g .. +7.
 //
 // The loop's loads are issued by inline asm and waited for by one explicit
 // `s_waitcnt vmcnt` per stage: the compiler's own waits drain every load at the
@@ -1109,18 +1113,27 @@ __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
 // instead of stalling the wavefront in front of them.
 constexpr int XM = 256;                 // rows per pass
 constexpr int XK = 32;                  // K elements per stage
-constexpr int XNB = 4;                  // buffers per operand
-constexpr int XB = XM * XK;             // one buffer, bf16 elements (16 KB)
+constexpr int XNB = 4;                  // token-row buffers
+constexpr int XB = XM * XK;             // one token-row buffer, bf16 elements (16 KB)
+constexpr int WK = 64;                  // K elements per weight double stage (128 bytes of a row)
+constexpr int WNB = 3;                  // weight double-stage buffers
+constexpr int WB = XM * WK;             // one weight buffer, bf16 elements (32 KB)
 
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-// Physical position of 16-byte piece p of buffer row r: p ^ swz(r).  A read phase of 8
-// lanes (rows r..r+7, 32 banks) or of 16 lanes (rows r..r+15, 64 banks) then touches
-// 8 or 16 different bank groups.
+// Physical position of 16-byte piece p of token-row buffer row r: p ^ swz(r).  A read
+// phase of 8 lanes (rows r..r+7, 32 banks) or of 16 lanes (rows r..r+15, 64 banks)
+// then touches 8 or 16 different bank groups.
 __device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+// The same for the 8 pieces of a weight buffer row (128 bytes).
+__device__ __forceinline__ int lds_swz_w(int r) { return (r ^ (r >> 3)) & 7; }
 
 __device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* buf, int r, int piece) {
   const uint4 u = *reinterpret_cast<const uint4*>(buf + r * XK + ((piece ^ lds_swz(r)) * 8));
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+__device__ __forceinline__ bf16x8_t lds_frag_w(const uint16_t* buf, int r, int piece) {
+  const uint4 u = *reinterpret_cast<const uint4*>(buf + r * WK + ((piece ^ lds_swz_w(r)) * 8));
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
@@ -1132,21 +1145,26 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, uint32_t o
                :: "s"(m0), "v"(off), "s"(rs), "s"(kbytes) : "memory", "m0");
 }
 
-// Load q (0..3) of wave w covers buffer rows 16 (4w + q) + lane/4, physical piece
-// lane%4; the lane's source piece is the logical one stored there.
+// Token rows: load q (0..3) of wave w covers buffer rows 16 (4w + q) + lane/4, physical
+// piece lane%4.  Weights: load u (0..7) of wave w covers buffer rows 64w + 8u + lane/8,
+// physical piece lane%8.  The lane's source piece is the logical one stored there.
 __device__ __forceinline__ int lds_load_row(int wave, int q, int lane) { return 16 * (4 * wave + q) + (lane >> 2); }
 __device__ __forceinline__ int lds_load_piece(int r, int lane) { return (lane & 3) ^ lds_swz(r); }
+__device__ __forceinline__ int lds_wload_row(int wave, int u, int lane) { return 64 * wave + 8 * u + (lane >> 3); }
+__device__ __forceinline__ int lds_wload_piece(int r, int lane) { return (lane & 7) ^ lds_swz_w(r); }
 
-// acc[a][c] += A(row subtile a) x B(column subtile c of this wave) over one stage.
+// acc[a][c] += A(row subtile a) x B(column subtile c of this wave) over one stage; the
+// stage's weights are half `half` (K elements 32 half .. +31) of a weight buffer.
 // Slice 1's operands are read from LDS while slice 0 multiplies; `issue(t)` sends
 // load t (0..7) of a later stage after the t-th MFMA pair.
 template <int NSUB, typename F>
 __device__ __forceinline__ void mfma_stage_bf16(f32x16_t (&acc)[8][2], const uint16_t* sa, const uint16_t* sb,
-                                                int wave, int lane, F&& issue) {
+                                                int half, int wave, int lane, F&& issue) {
   const int m = lane & 31, g = lane >> 5;
+  const int pb = 4 * half + g;
   bf16x8_t fa[2][NSUB], fb[2][2];
-  fb[0][0] = lds_frag(sb, wave * 64 + m, g);
-  fb[0][1] = lds_frag(sb, wave * 64 + 32 + m, g);
+  fb[0][0] = lds_frag_w(sb, wave * 64 + m, pb);
+  fb[0][1] = lds_frag_w(sb, wave * 64 + 32 + m, pb);
 #pragma unroll
   for (int a = 0; a < NSUB; ++a) fa[0][a] = lds_frag(sa, a * 32 + m, g);
 #pragma unroll
@@ -1157,8 +1175,8 @@ __device__ __forceinline__ void mfma_stage_bf16(f32x16_t (&acc)[8][2], const uin
       acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][a], fb[i][1], acc[a][1], 0, 0, 0);
       if (i == 0) {
         if (a == 0) {
-          fb[1][0] = lds_frag(sb, wave * 64 + m, 2 + g);
-          fb[1][1] = lds_frag(sb, wave * 64 + 32 + m, 2 + g);
+          fb[1][0] = lds_frag_w(sb, wave * 64 + m, pb + 2);
+          fb[1][1] = lds_frag_w(sb, wave * 64 + 32 + m, pb + 2);
         }
         fa[1][a] = lds_frag(sa, a * 32 + m, 2 + g);
         __builtin_amdgcn_sched_barrier(0);  // keep these reads here, ahead of slice 1
@@ -1176,9 +1194,9 @@ __device__ __forceinline__ void mfma_stage_bf16(f32x16_t (&acc)[8][2], const uin
 // The grid is persistent: a block takes logical blocks b, b + grid, b + 2 grid, ...
 // (in the XCD-aware order, so the tiles running on one XCD at a time belong to few
 // experts and share its L2), each split into passes of up to XM rows; a pass is one
-// "item".  The loads of every stage go out three stages ahead across item boundaries,
-// so the first stages of the next item are in flight while the current one finishes
-// and runs its epilogue.
+// "item".  The loads go out three stages ahead (token rows) and two to four stages
+// ahead (weights) across item boundaries, so the first stages of the next item are in
+// flight while the current one finishes and runs its epilogue.
 struct MfmaArgs {
   const uint16_t* x;       // gate/up: token rows [T][d]
   const uint16_t* h;       // down: h rows [n_rows][d_ff] in perm order
@@ -1195,7 +1213,7 @@ struct MfmaArgs {
 struct MfmaItem {
   int g, n0, r0, m0, rows, nsub;
   __amdgpu_buffer_rsrc_t rw;  // the group's weight rows
-  uint32_t roff[4], woff[4];  // this lane's load offsets (bytes, stage 0)
+  uint32_t roff[4], woff[8];  // this lane's load offsets (bytes, K position 0)
 };
 
 // Advances (i, m0) over this block's passes and sets up the next item; false at the end.
@@ -1223,15 +1241,18 @@ __device__ __forceinline__ bool next_item(const MfmaArgs& A, int& i, int& m0, Mf
     const uint16_t* rec = A.slots + (size_t)A.group_slot[g] * A.rec_elems;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int bc = lds_load_row(wave, q, lane);
-      const int r = bc, rr = min(r, it.rows - 1);  // rows past the end load a valid row
-      if (DOWN) {  // B column bc is output column n0 + bc
-        it.woff[q] = (uint32_t)((size_t)(it.n0 + bc) * A.d_ff + lds_load_piece(bc, lane) * 8) * 2u;
-        it.roff[q] = (uint32_t)((size_t)(r0 + m0 + rr) * A.d_ff + lds_load_piece(r, lane) * 8) * 2u;
-      } else {  // B column bc: wave bc/64, gate or up (bc/32)&1, column bc%32
+      const int r = lds_load_row(wave, q, lane), rr = min(r, it.rows - 1);  // rows past the end load a valid row
+      it.roff[q] = DOWN ? (uint32_t)((size_t)(r0 + m0 + rr) * A.d_ff + lds_load_piece(r, lane) * 8) * 2u
+                        : (uint32_t)((size_t)(A.perm[r0 + m0 + rr] / A.k) * A.d + lds_load_piece(r, lane) * 8) * 2u;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int bc = lds_wload_row(wave, u, lane);
+      if (DOWN)  // B column bc is output column n0 + bc
+        it.woff[u] = (uint32_t)((size_t)(it.n0 + bc) * A.d_ff + lds_wload_piece(bc, lane) * 8) * 2u;
+      else {  // B column bc: wave bc/64, gate or up (bc/32)&1, column bc%32
         const int wrow = ((bc >> 5) & 1) * A.d_ff + it.n0 + (bc >> 6) * 32 + (bc & 31);
-        it.woff[q] = (uint32_t)((size_t)wrow * A.d + lds_load_piece(bc, lane) * 8) * 2u;
-        it.roff[q] = (uint32_t)((size_t)(A.perm[r0 + m0 + rr] / A.k) * A.d + lds_load_piece(r, lane) * 8) * 2u;
+        it.woff[u] = (uint32_t)((size_t)wrow * A.d + lds_wload_piece(bc, lane) * 8) * 2u;
       }
     }
     it.rw = DOWN ? buf_rsrc(rec + (size_t)2 * A.d_ff * A.d, (uint32_t)((size_t)A.d * A.d_ff * 2))
@@ -1278,28 +1299,35 @@ __device__ __forceinline__ void mfma_epilogue(const MfmaArgs& A, const MfmaItem&
   }
 }
 
-// Load t (0..7) of stage st of item it, into buffer st % XNB (lx, lw: this wave's part
-// of the row and weight buffers).
-__device__ __forceinline__ void mfma_load(__amdgpu_buffer_rsrc_t rx, const MfmaItem& it, int st, int t,
-                                          uint32_t klast, uint32_t lx, uint32_t lw) {
+// Token-row load q of stage st of item it into buffer st % XNB (lx: this wave's part).
+__device__ __forceinline__ void mfma_load_x(__amdgpu_buffer_rsrc_t rx, const MfmaItem& it, int st, int q,
+                                            uint32_t klast, uint32_t lx) {
   const uint32_t kbyte = min((uint32_t)st * (uint32_t)(XK * 2), klast);
-  const uint32_t b = (uint32_t)((st % XNB) * XB * 2);
-  if (t < 4)
-    lds_load16(rx, it.roff[t & 3], kbyte, lx + b + (uint32_t)((t & 3) * 1024));
-  else
-    lds_load16(it.rw, it.woff[t & 3], kbyte, lw + b + (uint32_t)((t & 3) * 1024));
+  lds_load16(rx, it.roff[q], kbyte, lx + (uint32_t)((st % XNB) * XB * 2 + q * 1024));
 }
 
-// The K loop of one item (kdim a multiple of 128, so every item starts in buffer 0),
-// its first XNB - 1 stages already issued.  Stage s issues stage s + 3 of this item or,
-// past its end, of the next one (re-reading this item's last stage when there is
-// none); at the top of stage s its own loads are older than the 16 of the next two
-// stages.  Anything else the compiler issues in between only adds newer operations,
-// which keeps the count safe.
+// Weight load u of double stage ds of item it into weight buffer `slot` (lw: this
+// wave's part).
+__device__ __forceinline__ void mfma_load_w(const MfmaItem& it, int ds, int u, uint32_t klast, uint32_t lw,
+                                            int slot) {
+  const uint32_t kbyte = min((uint32_t)ds * (uint32_t)(WK * 2), klast);
+  lds_load16(it.rw, it.woff[u], kbyte, lw + (uint32_t)(slot * WB * 2 + u * 1024));
+}
+
+__device__ __forceinline__ int mod3(int v) { return v % 3; }
+
+// The K loop of one item (kdim a multiple of 128, so every item starts in token-row
+// buffer 0; weight double stage ds sits in buffer (wbase + ds) % 3, wbase carried from
+// item to item).  Stage s issues the token rows of stage s + 3 and half s % 2 of the
+// weights of double stage s / 2 + 2, of this item or, past its end, of the next one
+// (re-reading this item's last stage when there is none).  At the top of stage s its
+// own loads (rows issued at s - 3, weights at or before s - 3) are older than the 16
+// of the two stages before it.  Anything else the compiler issues in between only adds
+// newer operations, which keeps the count safe.
 template <int NSUB>
 __device__ __forceinline__ void mfma_item_bf16(f32x16_t (&acc)[8][2], __amdgpu_buffer_rsrc_t rx, const MfmaItem& cur,
                                                const MfmaItem& nxt, bool has_nxt, uint16_t* sx, uint16_t* sw,
-                                               int kdim, int wave, int lane, uint32_t lx, uint32_t lw) {
+                                               int kdim, int wave, int lane, uint32_t lx, uint32_t lw, int wbase) {
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
@@ -1307,8 +1335,8 @@ __device__ __forceinline__ void mfma_item_bf16(f32x16_t (&acc)[8][2], __amdgpu_b
       acc[a][0][v] = 0.0f;
       acc[a][1][v] = 0.0f;
     }
-  const int nst = kdim / XK;
-  const uint32_t klast = (uint32_t)(kdim - XK) * 2u;
+  const int nst = kdim / XK, nds = kdim / WK;
+  const uint32_t klast_x = (uint32_t)(kdim - XK) * 2u, klast_w = (uint32_t)(kdim - WK) * 2u;
   for (int s0 = 0; s0 < nst; s0 += XNB) {
 #pragma unroll
     for (int j = 0; j < XNB; ++j) {
@@ -1316,11 +1344,20 @@ __device__ __forceinline__ void mfma_item_bf16(f32x16_t (&acc)[8][2], __amdgpu_b
       asm volatile("s_waitcnt vmcnt(%0)" :: "n"((XNB - 2) * 8) : "memory");
       __syncthreads();  // every wave's loads of this stage have landed; stage s - 1 is done
       const int sn = st + XNB - 1;
-      const bool in_cur = sn < nst || !has_nxt;
-      const MfmaItem& it = in_cur ? cur : nxt;
-      const int sl = in_cur ? sn : sn - nst;
-      mfma_stage_bf16<NSUB>(acc, sx + j * XB, sw + j * XB, wave, lane,
-                            [&](int t) { mfma_load(rx, it, sl, t, klast, lx, lw); });
+      const bool x_cur = sn < nst || !has_nxt;
+      const MfmaItem& xi = x_cur ? cur : nxt;
+      const int xs = x_cur ? sn : sn - nst;
+      const int dn = (st >> 1) + 2, wh = st & 1;
+      const bool w_cur = dn < nds || !has_nxt;
+      const MfmaItem& wi = w_cur ? cur : nxt;
+      const int wd = w_cur ? dn : dn - nds;
+      const int wslot = mod3(wbase + dn);
+      mfma_stage_bf16<NSUB>(acc, sx + j * XB, sw + mod3(wbase + (st >> 1)) * WB, wh, wave, lane, [&](int t) {
+        if (t < 4)
+          mfma_load_x(rx, xi, xs, t, klast_x, lx);
+        else
+          mfma_load_w(wi, wd, 4 * wh + (t - 4), klast_w, lw, wslot);
+      });
     }
   }
 }
@@ -1336,28 +1373,39 @@ __device__ __forceinline__ void mfma_persistent(const MfmaArgs& A, uint16_t* sx,
   if (!next_item<DOWN>(A, ci, cm, cur, wave, lane)) return;  // block-uniform
   bool has_nxt = next_item<DOWN>(A, ci, cm, nxt, wave, lane);
   const uint32_t lx = (uint32_t)(uintptr_t)(lds_u16*)sx + (uint32_t)(4 * wave * 1024);
-  const uint32_t lw = (uint32_t)(uintptr_t)(lds_u16*)sw + (uint32_t)(4 * wave * 1024);
-  const uint32_t klast = (uint32_t)(kdim - XK) * 2u;
+  const uint32_t lw = (uint32_t)(uintptr_t)(lds_u16*)sw + (uint32_t)(8 * wave * 1024);
+  const uint32_t klast_x = (uint32_t)(kdim - XK) * 2u, klast_w = (uint32_t)(kdim - WK) * 2u;
+  // the loads stages -4 .. -1 would have issued, in the same order: weights of double
+  // stages 0 and 1 (in halves), token rows of stages 0, 1, 2
 #pragma unroll
-  for (int j = 0; j < XNB - 1; ++j)
+  for (int u = 0; u < 4; ++u) mfma_load_w(cur, 0, u, klast_w, lw, 0);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) mfma_load(rx, cur, j, t, klast, lx, lw);
+  for (int j = 0; j < 3; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mfma_load_x(rx, cur, j, q, klast_x, lx);
+    const int ds = (j + 1) >> 1, h = (j + 1) & 1;  // (0, 1), (1, 0), (1, 1)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mfma_load_w(cur, ds, 4 * h + u, klast_w, lw, ds);
+  }
+  int wbase = 0;
+  const int nds = kdim / WK;
   for (;;) {
     f32x16_t acc[8][2];
     switch (cur.nsub) {
-      case 1: mfma_item_bf16<1>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
-      case 2: mfma_item_bf16<2>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
-      case 3: mfma_item_bf16<3>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
-      case 4: mfma_item_bf16<4>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
-      case 5: mfma_item_bf16<5>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
-      case 6: mfma_item_bf16<6>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
-      case 7: mfma_item_bf16<7>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
-      default: mfma_item_bf16<8>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw); break;
+      case 1: mfma_item_bf16<1>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw, wbase); break;
+      case 2: mfma_item_bf16<2>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw, wbase); break;
+      case 3: mfma_item_bf16<3>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw, wbase); break;
+      case 4: mfma_item_bf16<4>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw, wbase); break;
+      case 5: mfma_item_bf16<5>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw, wbase); break;
+      case 6: mfma_item_bf16<6>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw, wbase); break;
+      case 7: mfma_item_bf16<7>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw, wbase); break;
+      default: mfma_item_bf16<8>(acc, rx, cur, nxt, has_nxt, sx, sw, kdim, wave, lane, lx, lw, wbase); break;
     }
     mfma_epilogue<DOWN>(A, cur, acc, wave, lane);  // the next item's first stages are in flight
     if (!has_nxt) break;
     cur = nxt;
     has_nxt = next_item<DOWN>(A, ci, cm, nxt, wave, lane);
+    wbase = mod3(wbase + nds);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();  // no LDS load is left in flight when the block ends
@@ -1368,7 +1416,7 @@ __device__ __forceinline__ void mfma_persistent(const MfmaArgs& A, uint16_t* sx,
 // B columns 64w .. +31 and 64w + 32 .. +63 of the weight buffer), h in bf16.
 __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(MfmaArgs A) {
   __shared__ __attribute__((aligned(1024))) uint16_t sX[XNB * XB];
-  __shared__ __attribute__((aligned(1024))) uint16_t sW[XNB * XB];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW[WNB * WB];
   mfma_persistent<false>(A, sX, sW);
 }
 
@@ -1376,7 +1424,7 @@ __global__ __launch_bounds__(256) void ffn_gateup_mfma_kernel(MfmaArgs A) {
 // columns n0 + 64w .. +63), h rows in perm order.
 __global__ __launch_bounds__(256) void ffn_down_mfma_kernel(MfmaArgs A) {
   __shared__ __attribute__((aligned(1024))) uint16_t sX[XNB * XB];
-  __shared__ __attribute__((aligned(1024))) uint16_t sW[XNB * XB];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW[WNB * WB];
   mfma_persistent<true>(A, sX, sW);
 }
 
@@ -1608,7 +1656,7 @@ int launch_ffn_mfma(const uint16_t* x, int T, int d, int d_ff, int k, const uint
   const size_t lim = (size_t)1 << 31;
   if ((size_t)T * d * 2 >= lim || (size_t)n_rows * d_ff * 2 >= lim || (size_t)3 * d * d_ff * 2 >= lim)
     return fail(FT_EINVAL, "ffn_mfma: x, h or a record over 2 GiB");
-  // one block per compute unit (128 KB of LDS each), a multiple of the 8 XCDs
+  // one block per compute unit (160 KB of LDS each), a multiple of the 8 XCDs
   static int n_cu = 0;
   if (n_cu <= 0) {
     int dev = 0;
