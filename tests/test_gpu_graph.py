@@ -160,3 +160,59 @@ def test_graph_step_error_empties_cache_and_reports():
             ft.ft_decode_graph_destroy(graph)
         eng.destroy()
         pool.free()
+
+
+def test_graph_step_full_size_headline_shape():
+    """The graph-resident step at the 43-layer d=4096 E=256 top-6 batch-1 shape, 1210 slots,
+    pool of 2 physical layers: decisions (residency and counters after every step) equal
+    the oracle's on every step, y of every layer within tolerance on the last step."""
+    torch = torch_mod()
+    from moe_expert_offload_amd import synth
+    from oracle.ffn import moe_layer
+    from oracle.router import route
+    wl = synth.WORKLOADS["decode-L43-d4096-E256-top6"]
+    s = wl.shape
+    T, L_phys, fq, steps = 1, 2, 18000, 3
+    _say("decode graph full size", wl.name)
+    pool = PinnedPool(s, L_phys * s.E)
+    pool.fill_device_random(wl.seed_key)
+    eng = Engine(s, pool, wl.n_slots, T_max=T, frac_q16=fq, L_phys=L_phys)
+    graph = None
+    try:
+        ref = SlotTable(wl.n_slots, s.L, s.E)
+        tr = synth.trace_for(wl, steps=steps)
+        wr = [synth.router_weights(wl, l) for l in range(s.L)]
+        wr_dev = [dev_u16(w) for w in wr]
+        xb = torch.zeros((s.L, T, s.d), dtype=torch.int16, device="cuda")
+        ab = torch.zeros((s.L, T, s.E), dtype=torch.uint8, device="cuda")
+        yb = torch.zeros((s.L, T, s.d), dtype=torch.float32, device="cuda")
+        graph = ft.ft_decode_graph_create(eng.ctx, T, xb, wr_dev, ab, yb)
+        for st in range(steps):
+            xs = [synth.tokens(wl, st, l, T=T) for l in range(s.L)]
+            masks = [synth.allowed_mask(tr[st, l], s.E) for l in range(s.L)]
+            for l in range(s.L):
+                xb[l].copy_(dev_u16(xs[l]))
+                ab[l].copy_(dev(masks[l]))
+            ft.ft_decode_graph_launch(graph)
+            torch.cuda.synchronize()
+            ft.ft_decode_graph_status(graph)
+            got = host(yb)
+            for l in range(s.L):
+                idx, g, _ = route(xs[l], wr[l], s.k, masks[l])
+                ref.lookup(l, idx, fq, 1, -1)
+                if st == steps - 1:
+                    ref_y = moe_layer(xs[l], idx, g, lambda e: pool.view[(l % L_phys) * s.E + e], s.d, s.d_ff)
+                    ok, mx, l1 = within_tolerance(got[l], ref_y)
+                    assert ok, (st, l, mx, l1)
+            res = ref.resident()
+            for l in range(s.L):
+                for e in range(0, s.E, 5):
+                    assert ft.ft_expert_cache_where(eng.ctx, l, e) == res.get(l * s.E + e, -1), (st, l, e)
+            stt = ft.ft_get_stats(eng.ctx)
+            c = ref.counters
+            assert (stt["fills"], stt["cpu_experts"], stt["read_hits"]) == (c.fills, c.cpu_experts, c.read_hits), st
+    finally:
+        if graph:
+            ft.ft_decode_graph_destroy(graph)
+        eng.destroy()
+        pool.free()
