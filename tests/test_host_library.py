@@ -212,6 +212,45 @@ def test_error_codes():
     assert ft.ft_workspace_bytes(shape, 8) > 0
 
 
+def test_argument_checks_before_any_device_call():
+    """Entry points refuse bad arguments with FT_EINVAL before touching a device: the
+    routing read-back and the decode graph need a context with a device path and a
+    matching T; the no-alloc permutation refuses sizes beyond its fixed scratch array.
+    Addresses passed here are never dereferenced."""
+    shape = ft.make_shape(4, 16, 64, 64, 2)
+    ctx = ft.ft_create(shape, ft.make_config(), n_slots=8)
+    fake = 1 << 20
+    try:
+        for call in (lambda: ft.ft_layer_routing(ctx, fake, fake, 1, stream=0),
+                     lambda: ft.ft_decode_graph_create(ctx, 1, fake, [fake] * 4, None, fake)):
+            with pytest.raises(ft.FtError) as ei:
+                call()
+            assert ei.value.status == ft.FT_EINVAL
+            assert "device path" in str(ei.value)
+    finally:
+        ft.ft_destroy(ctx)
+    for g in (None, 0):
+        with pytest.raises(ft.FtError) as ei:
+            ft.ft_decode_graph_launch(g, stream=0)
+        assert ei.value.status == ft.FT_EINVAL
+        with pytest.raises(ft.FtError) as ei:
+            ft.ft_decode_graph_status(g)
+        assert ei.value.status == ft.FT_EINVAL
+        ft.ft_decode_graph_destroy(g)  # destroying nothing is not an error
+    cap = ft.ft_permute_noalloc_max_scratch_bytes()
+    assert cap == 1 << 20
+    # largest P the array holds at 1024 groups fits; one past the byte bound does not
+    P_fit = max(p for p in range(0, 1 << 18, 256) if ft.ft_permute_workspace_bytes(p, 1024) <= cap)
+    assert P_fit >= 65536
+    for P_, n_groups in ((16 * P_fit, 1024), (-1, 8), (16, 0), (16, 1025)):
+        with pytest.raises(ft.FtError) as ei:
+            ft.ft_permute_noalloc(fake, P_, n_groups, fake, fake, fake, stream=0)
+        assert ei.value.status == ft.FT_EINVAL
+    with pytest.raises(ft.FtError) as ei:  # null key with pairs to group
+        ft.ft_permute_noalloc(None, 16, 8, fake, fake, fake, stream=0)
+    assert ei.value.status == ft.FT_EINVAL
+
+
 @pytest.mark.parametrize("T,d,d_ff,uses,threads", [
     (1, 256, 512, [[0], [0]], 3),
     (8, 520, 136, [[0, 3, 7], [2], [1, 2, 3, 4, 5, 6, 7, 0]], 4),
