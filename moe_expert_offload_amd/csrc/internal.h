@@ -67,12 +67,6 @@ struct DecideArgs {
   int32_t min_fill, max_fetch;
 };
 
-// Decode router in one launch (T <= 64): also publishes idx, gates and x to
-// pinned host memory (pub_* may be null), then writes seq to *pub_flag; ticket
-// is a zeroed device counter.  With `da`, the last block also takes the cache
-// decisions of the call on the device (dedup, classify, split, victims, slot
-// rewrite, stamps) and the grouping of the pairs, updates the device state and
-// publishes the plan before the flag.
 // key[i] = map[idx[i]] (-1 for ids outside [0, n_map)).
 int launch_remap(const int32_t* idx, const int32_t* map, int n_map, int P, int32_t* key, void* stream);
 
@@ -84,6 +78,12 @@ int launch_fill(const uint8_t* layer_base, size_t S, int E, uint8_t* slots, int 
 // Plain copy of pinned host memory to device memory by the same kernel reads.
 int launch_h2d_copy(const void* src, void* dst, size_t bytes, void* stream);
 
+// Decode router in one launch (T <= 64): also publishes idx, gates and x to
+// pinned host memory (pub_* may be null), then writes seq to *pub_flag; ticket
+// is a zeroed device counter (left zeroed).  With `da`, the last
+// block also takes the cache decisions of the call on the device (dedup,
+// classify, split, victims, slot rewrite, stamps) and the grouping of the pairs,
+// updates the device state and publishes the plan before the flag.
 int launch_router_decode(const uint16_t* x, const uint16_t* w, const uint8_t* allowed, int T, int d,
                          int E, int k, float* logits_ws, int32_t* idx, float* gates,
                          unsigned int* ticket, int32_t* pub_idx, float* pub_gates, uint16_t* pub_x,

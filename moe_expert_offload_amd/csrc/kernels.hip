@@ -229,25 +229,36 @@ __device__ __forceinline__ float key_logit(unsigned long long key) {
 
 // Top-k of one token by one wavefront: k rounds of a wave arg-max over the
 // allowed experts (NS per lane), each winner removed; softmax over the k winners.
-// Writes the device outputs and, when given, copies to pinned host memory and the
-// ids to shared memory.
+// Lanes 0..k-1 write the k ids and gates to idx/gates (global or shared memory).
+// The logits are loaded together with the mask rather than behind it, and a
+// wavefront with two tokens loads both before it selects.
 template <int NS>
-__device__ __forceinline__ void topk_token_ns(const float* __restrict__ lg, const uint8_t* __restrict__ allowed, int E, int k,
-                              int lane, int32_t* __restrict__ idx, float* __restrict__ gates, int32_t* pub_idx,
-                              float* pub_gates, int32_t* s_ids) {
-  unsigned long long key[NS];
+struct TopkIn {
+  float v[NS];
+  uint8_t ok[NS];
+};
+
+template <int NS>
+__device__ __forceinline__ void topk_load(const float* __restrict__ lg, const uint8_t* __restrict__ allowed, int E,
+                                          int lane, TopkIn<NS>& in) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int e = lane + 64 * s;
-    const bool in = e < E && (allowed == nullptr || allowed[e] != 0);
-    key[s] = in ? rank_key(lg[e], e) : 0ull;
+    in.v[s] = e < E ? lg[e] : 0.0f;
+    in.ok[s] = e < E && (allowed == nullptr || allowed[e] != 0);
   }
-  float sv[8];
-  int se[8];
+}
+
+template <int NS>
+__device__ __forceinline__ void topk_pick(const TopkIn<NS>& in, int k, int lane, int32_t* idx, float* gates) {
+  unsigned long long key[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) key[s] = in.ok[s] ? rank_key(in.v[s], lane + 64 * s) : 0ull;
+  // winner r goes to lane r (value and expert); the largest logit is uniform
+  float my_v = 0.0f, top = 0.0f;
+  int my_e = -1;
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    sv[r] = 0.0f;
-    se[r] = -1;
     if (r < k) {
       unsigned long long b = key[0];
 #pragma unroll
@@ -258,46 +269,54 @@ __device__ __forceinline__ void topk_token_ns(const float* __restrict__ lg, cons
 #pragma unroll
         for (int s = 0; s < NS; ++s)
           if (lane + 64 * s == e) key[s] = 0ull;
-        se[r] = e;
-        sv[r] = key_logit(b);
+        const float v = key_logit(b);
+        if (r == 0) top = v;
+        if (lane == r) {
+          my_v = v;
+          my_e = e;
+        }
       }
     }
   }
-  if (lane == 0) {
-    float z[8], sum = 0.0f;
+  // softmax over the k winners, one per lane, summed by a butterfly over 8 lanes
+  const float z = (lane < k && my_e >= 0) ? expf(my_v - top) : 0.0f;
+  float sum = z;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      z[r] = (r < k && se[r] >= 0) ? expf(sv[r] - sv[0]) : 0.0f;
-      sum += z[r];
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      if (r < k) {
-        const float g = se[r] >= 0 ? z[r] / sum : 0.0f;
-        idx[r] = se[r];
-        gates[r] = g;
-        if (pub_idx) {
-          pub_idx[r] = se[r];
-          pub_gates[r] = g;
-        }
-        if (s_ids) s_ids[r] = se[r];
-      }
+  for (int o = 1; o < 8; o <<= 1) sum += __shfl_xor(sum, o, WAVE);
+  if (lane < k) {
+    idx[lane] = my_e;
+    gates[lane] = my_e >= 0 ? z / sum : 0.0f;
   }
 }
 
-__device__ __forceinline__ void topk_token(const float* __restrict__ lg, const uint8_t* __restrict__ allowed, int E,
-                                           int k, int lane, int32_t* __restrict__ idx, float* __restrict__ gates,
-                                           int32_t* pub_idx, float* pub_gates, int32_t* s_ids = nullptr) {
+// Tokens first, first + step, ... of logits [T, E] by one wavefront, two at a time.
+template <int NS>
+__device__ __forceinline__ void topk_tokens_ns(const float* __restrict__ logits, const uint8_t* __restrict__ allowed,
+                                               int T, int E, int k, int first, int step, int lane, int32_t* idx,
+                                               float* gates) {
+  for (int t = first; t < T; t += 2 * step) {
+    const int t1 = t + step;
+    TopkIn<NS> a, b;
+    topk_load<NS>(logits + (size_t)t * E, allowed ? allowed + (size_t)t * E : nullptr, E, lane, a);
+    if (t1 < T) topk_load<NS>(logits + (size_t)t1 * E, allowed ? allowed + (size_t)t1 * E : nullptr, E, lane, b);
+    topk_pick<NS>(a, k, lane, idx + (size_t)t * k, gates + (size_t)t * k);
+    if (t1 < T) topk_pick<NS>(b, k, lane, idx + (size_t)t1 * k, gates + (size_t)t1 * k);
+  }
+}
+
+__device__ __forceinline__ void topk_tokens(const float* __restrict__ logits, const uint8_t* __restrict__ allowed,
+                                            int T, int E, int k, int first, int step, int lane, int32_t* idx,
+                                            float* gates) {
   if (E <= 64)
-    topk_token_ns<1>(lg, allowed, E, k, lane, idx, gates, pub_idx, pub_gates, s_ids);
+    topk_tokens_ns<1>(logits, allowed, T, E, k, first, step, lane, idx, gates);
   else if (E <= 128)
-    topk_token_ns<2>(lg, allowed, E, k, lane, idx, gates, pub_idx, pub_gates, s_ids);
+    topk_tokens_ns<2>(logits, allowed, T, E, k, first, step, lane, idx, gates);
   else if (E <= 256)
-    topk_token_ns<4>(lg, allowed, E, k, lane, idx, gates, pub_idx, pub_gates, s_ids);
+    topk_tokens_ns<4>(logits, allowed, T, E, k, first, step, lane, idx, gates);
   else if (E <= 512)
-    topk_token_ns<8>(lg, allowed, E, k, lane, idx, gates, pub_idx, pub_gates, s_ids);
+    topk_tokens_ns<8>(logits, allowed, T, E, k, first, step, lane, idx, gates);
   else
-    topk_token_ns<16>(lg, allowed, E, k, lane, idx, gates, pub_idx, pub_gates, s_ids);
+    topk_tokens_ns<16>(logits, allowed, T, E, k, first, step, lane, idx, gates);
 }
 
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
@@ -308,8 +327,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_token(logits + (size_t)t * E, allowed ? allowed + (size_t)t * E : nullptr, E, k, lane,
-             idx + (size_t)t * k, gates + (size_t)t * k, nullptr, nullptr);
+  topk_tokens(logits, allowed, t + 1, E, k, t, 1, lane, idx, gates);
 }
 
 // ---- device-side cache decisions ([FT] §4.1 "Device-side cache control") ----------
@@ -401,7 +419,9 @@ __device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v)
 // a hit (by (stamp, slot)), eviction and admission, stamps of H then F in
 // first-occurrence order, the slot rewrite, and the stable grouping of the pairs
 // by G = H then F.  Same rule as ExpertCache::lookup.  Every decision is made in
-// shared memory from the prefetched state; global memory is only written.
+// shared memory from the prefetched state.  Global memory is only written, and
+// only after the last barrier: a barrier waits for the block's stores in flight,
+// so stores issued before one would put their round trip on the critical path.
 __device__ void decide_block(const DecideArgs& a, const int32_t* s_id, int P, const DecidePre& pf) {
   __shared__ int32_t s_u[FT_PLAN_CAP], s_g[FT_PLAN_CAP], s_h[FT_PLAN_CAP], s_m[FT_PLAN_CAP];
   __shared__ int32_t s_vold[FT_PLAN_CAP];
@@ -530,7 +550,7 @@ __device__ void decide_block(const DecideArgs& a, const int32_t* s_id, int P, co
     for (int w = 1; w < 4; ++w) best = s_best[r & 1][w] < best ? s_best[r & 1][w] : best;
     if (best == ~0ull) {
       // fewer candidates than q (cannot happen while q <= avail and no prefill
-      // reservation exists): publish an invalid plan, write nothing
+      // reservation exists): publish an invalid plan, change nothing
       if (tid == 0) {
         pl->n_u = -1;
         pl->n_h = 0;
@@ -554,16 +574,11 @@ __device__ void decide_block(const DecideArgs& a, const int32_t* s_id, int P, co
     prev = best;
   }
   __syncthreads();
-  // eviction and admission of F = M[0:q]; the keys involved are all distinct
-  for (int r = tid; r < q; r += 256) {
-    const int sl = s_g[n_h + r], old = s_vold[r], e = s_m[r];
-    if (old >= 0) a.dc.where[old] = -1;
-    a.dc.slot_key[sl] = base + e;
-    a.dc.where[base + e] = sl;
-    s_pos[e] = n_h + r;
-  }
+  // admission of F = M[0:q]: its group is n_h + r (in shared memory; the device
+  // state is written at the end)
+  for (int r = tid; r < q; r += 256) s_pos[s_m[r]] = n_h + r;
   __syncthreads();
-  // stamps: H and F in first-occurrence order
+  // stamps: H and F in first-occurrence order (written at the end)
   const int r0 = u0 < n_u && s_pos[e0] >= 0, r1 = !small && u1 < n_u && s_pos[e1] >= 0;
   int n_res;
   if (small) {
@@ -573,13 +588,49 @@ __device__ void decide_block(const DecideArgs& a, const int32_t* s_id, int P, co
   } else {
     ex = block_excl_scan_256(r0 + r1, &n_res);
   }
+  const int n_g = n_h + q;
+  // the host takes the same decisions from the published ids; it checks them
+  // against a hash of the device's (plan_term summed over the sequence of values)
+  const int n_seq = 5 + n_u + n_h + n_m + n_g + 2 * P;
+  uint32_t part = 0u;
+  for (int j = tid; j < n_seq; j += 256) {
+    int v, r = j;
+    if (r < 5) {
+      v = r == 0 ? n_u : r == 1 ? n_h : r == 2 ? n_m : r == 3 ? q : avail;
+    } else if ((r -= 5) < n_u) {
+      v = s_u[r];
+    } else if ((r -= n_u) < n_h) {
+      v = s_h[r];
+    } else if ((r -= n_h) < n_m) {
+      v = s_m[r];
+    } else if ((r -= n_m) < n_g) {
+      v = s_g[r];
+    } else if ((r -= n_g) < P) {
+      const int g = s_pos[s_id[r]];
+      v = g >= 0 ? s_g[g] : -1;
+    } else {
+      v = s_pos[s_id[r - P]];
+    }
+    part += plan_term(j, v);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, WAVE);
+  if (lane == 0) atomicAdd(&s_hash, part);
+  __syncthreads();
+  // ---- stores: no barrier from here on
+  // eviction and admission; the keys involved are all distinct
+  for (int r = tid; r < q; r += 256) {
+    const int sl = s_g[n_h + r], old = s_vold[r], e = s_m[r];
+    if (old >= 0) a.dc.where[old] = -1;
+    a.dc.slot_key[sl] = base + e;
+    a.dc.where[base + e] = sl;
+  }
   if (!small || wv == 0) {
     if (r0) a.dc.slot_stamp[s_g[s_pos[e0]]] = pf.clock + ex + 1;
     if (r1) a.dc.slot_stamp[s_g[s_pos[e1]]] = pf.clock + ex + r0 + 1;
   }
   if (tid == 0) *a.dc.clock = pf.clock + n_res;
   // slot rewrite and stable grouping of the pairs by G
-  const int n_g = n_h + q;
   if (small) {
     // lane i holds pair i: per group v, the pairs in it are ranked by ballot
     if (wv == 0) {
@@ -640,36 +691,6 @@ __device__ void decide_block(const DecideArgs& a, const int32_t* s_id, int P, co
     pl->n_c = n_m - q;
     pl->avail = avail;
     pl->n_g = n_g;
-  }
-  // the host takes the same decisions from the published ids; it checks them
-  // against a hash of the device's (plan_term summed over the sequence of values)
-  const int n_seq = 5 + n_u + n_h + n_m + n_g + 2 * P;
-  uint32_t part = 0u;
-  for (int j = tid; j < n_seq; j += 256) {
-    int v, r = j;
-    if (r < 5) {
-      v = r == 0 ? n_u : r == 1 ? n_h : r == 2 ? n_m : r == 3 ? q : avail;
-    } else if ((r -= 5) < n_u) {
-      v = s_u[r];
-    } else if ((r -= n_u) < n_h) {
-      v = s_h[r];
-    } else if ((r -= n_h) < n_m) {
-      v = s_m[r];
-    } else if ((r -= n_m) < n_g) {
-      v = s_g[r];
-    } else if ((r -= n_g) < P) {
-      const int g = s_pos[s_id[r]];
-      v = g >= 0 ? s_g[g] : -1;
-    } else {
-      v = s_pos[s_id[r - P]];
-    }
-    part += plan_term(j, v);
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, WAVE);
-  if (lane == 0) atomicAdd(&s_hash, part);
-  __syncthreads();
-  if (tid == 0) {
     pl->hash = s_hash;
     if (a.pub != nullptr) {
       a.pub->n_u = n_u;
@@ -724,50 +745,99 @@ __global__ __launch_bounds__(256) void h2d_copy_kernel(const uint8_t* __restrict
 
 constexpr int kFillBlocks = 64;  // enough reads in flight for the link; more only congest it
 
-// Decode router in one launch: one wavefront per (token, expert) logit (same
-// arithmetic order as router_logits_kernel: lane l owns elements (i mod 512)/8 ==
-// l, adds its products in increasing i, then a butterfly); the last block to
-// finish (device-scope fence + ticket counter, no waiting) does the top-k of every
-// token, the cache decisions when asked, copies x to pinned host memory and
+// Decode router in one launch.  Logits: wavefront w of block (bx, by) computes
+// the TE experts from (4 bx + w) TE on for the TT tokens from by TT on, with the
+// arithmetic order of router_logits_kernel (lane l owns elements (i mod 512)/8 ==
+// l, adds its products in increasing i, then a butterfly), loading JB chunks of
+// 512 elements per operand at once.  Several logits per wavefront keep the grid at
+// a few tens of blocks: every block's arrival (a device-scope fence and atomic on
+// one counter) lengthens the wait of the last one.  The last block
+// to arrive (device-scope fence + ticket counter, no waiting) does the top-k of
+// every token, the cache decisions when asked, copies x to pinned host memory and
 // publishes there.  `ticket` is a zeroed device counter, reset by the last block.
+__device__ __forceinline__ uint4 keep_if(uint4 v, bool c) {
+  return make_uint4(c ? v.x : 0u, c ? v.y : 0u, c ? v.z : 0u, c ? v.w : 0u);
+}
+
+template <int TT, int TE>
 __global__ __launch_bounds__(256) void router_decode_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const uint8_t* __restrict__ allowed,
     int T, int d, int E, int k, float* __restrict__ logits, int32_t* __restrict__ idx,
     float* __restrict__ gates, unsigned int* __restrict__ ticket, int32_t* pub_idx, float* pub_gates,
     uint16_t* pub_x, uint32_t* pub_flag, uint32_t seq, DecideArgs da, int decide) {
+  constexpr int JB = 40 / (TT + TE) < 8 ? 40 / (TT + TE) : 8;  // at most 40 16-byte loads in flight
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int t = blockIdx.x;
-  const int e = blockIdx.y * 4 + wave;
-  if (e < E) {
-    float acc = 0.0f;
-    const int J = (d + 511) >> 9;
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    for (int j0 = 0; j0 < J; j0 += 8) {
-      uint4 xv[8], wv[8];
+  const int t0 = blockIdx.y * TT;
+  const int e0 = (blockIdx.x * 4 + wave) * TE;
+  if (e0 < E) {
+    float acc[TT][TE];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
+    for (int a = 0; a < TT; ++a)
+#pragma unroll
+      for (int b = 0; b < TE; ++b) acc[a][b] = 0.0f;
+    const int J = (d + 511) >> 9;
+    for (int j0 = 0; j0 < J; j0 += JB) {
+      // every load is issued unconditionally from a clamped (in-bounds) address and
+      // the operands past the ends are zeroed afterwards: loads under a branch come
+      // out one behind the other
+      uint4 xv[JB][TT], wv[JB][TE];
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj) {
         const int i0 = (j0 + jj) * 512 + lane * 8;
         const bool in = j0 + jj < J && i0 < d;
-        xv[jj] = in ? ld16(x + (size_t)t * d + i0) : zero;
-        wv[jj] = in ? ld16(w + (size_t)e * d + i0) : zero;
+        const int ic = in ? i0 : 0;
+#pragma unroll
+        for (int a = 0; a < TT; ++a) {
+          const int ta = t0 + a < T ? t0 + a : T - 1;
+          xv[jj][a] = ld16(x + (size_t)ta * d + ic);
+        }
+#pragma unroll
+        for (int b = 0; b < TE; ++b) {
+          const int eb = e0 + b < E ? e0 + b : E - 1;
+          wv[jj][b] = ld16(w + (size_t)eb * d + ic);
+        }
+      }
+      // only the positions past d need zeros (as in router_logits_kernel); the
+      // logits of tokens and experts past the ends are not stored
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj) {
+        const bool in = j0 + jj < J && (j0 + jj) * 512 + lane * 8 < d;
+#pragma unroll
+        for (int a = 0; a < TT; ++a) xv[jj][a] = keep_if(xv[jj][a], in);
+#pragma unroll
+        for (int b = 0; b < TE; ++b) wv[jj][b] = keep_if(wv[jj][b], in);
       }
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        if (j0 + jj >= J) break;
+      for (int jj = 0; jj < JB; ++jj) {
+        if (j0 + jj >= J) continue;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          const uint32_t xw = (r >> 1) == 0 ? xv[jj].x : (r >> 1) == 1 ? xv[jj].y : (r >> 1) == 2 ? xv[jj].z : xv[jj].w;
-          const uint32_t ww = (r >> 1) == 0 ? wv[jj].x : (r >> 1) == 1 ? wv[jj].y : (r >> 1) == 2 ? wv[jj].z : wv[jj].w;
-          const float xf = (r & 1) ? bf_hi(xw) : bf_lo(xw);
-          const float wf = (r & 1) ? bf_hi(ww) : bf_lo(ww);
-          acc = acc + xf * wf;  // same order as router_logits_kernel
+#pragma unroll
+          for (int a = 0; a < TT; ++a) {
+            const uint32_t xw = (r >> 1) == 0 ? xv[jj][a].x : (r >> 1) == 1 ? xv[jj][a].y
+                              : (r >> 1) == 2 ? xv[jj][a].z : xv[jj][a].w;
+            const float xf = (r & 1) ? bf_hi(xw) : bf_lo(xw);
+#pragma unroll
+            for (int b = 0; b < TE; ++b) {
+              const uint32_t ww = (r >> 1) == 0 ? wv[jj][b].x : (r >> 1) == 1 ? wv[jj][b].y
+                                : (r >> 1) == 2 ? wv[jj][b].z : wv[jj][b].w;
+              const float wf = (r & 1) ? bf_hi(ww) : bf_lo(ww);
+              acc[a][b] = acc[a][b] + xf * wf;  // same order as router_logits_kernel
+            }
+          }
         }
       }
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o, WAVE);
-    if (lane == 0) logits[(size_t)t * E + e] = acc;
+    for (int a = 0; a < TT; ++a)
+#pragma unroll
+      for (int b = 0; b < TE; ++b) {
+        float v = acc[a][b];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) v = v + __shfl_xor(v, o, WAVE);
+        if (lane == 0 && t0 + a < T && e0 + b < E) logits[(size_t)(t0 + a) * E + e0 + b] = v;
+      }
   }
   __threadfence();
   __shared__ int last;
@@ -777,16 +847,26 @@ __global__ __launch_bounds__(256) void router_decode_kernel(
   if (!last) return;
   __threadfence();
   __shared__ int32_t s_ids[FT_PLAN_CAP];
+  __shared__ float s_gates[FT_PLAN_CAP];
+  // the cache state (written by earlier launches) is loaded here, not by every
+  // block: all blocks reading the same few kilobytes at once slows their logits
   DecidePre pf;
   if (decide) decide_prefetch(da, pf);
-  for (int tt = wave; tt < T; tt += 4)
-    topk_token(logits + (size_t)tt * E, allowed ? allowed + (size_t)tt * E : nullptr, E, k, lane,
-               idx + (size_t)tt * k, gates + (size_t)tt * k, pub_idx ? pub_idx + (size_t)tt * k : nullptr,
-               pub_gates ? pub_gates + (size_t)tt * k : nullptr, s_ids + tt * k);
+  topk_tokens(logits, allowed, T, E, k, wave, 4, lane, s_ids, s_gates);
   __syncthreads();
   if (decide) decide_block(da, s_ids, T * k, pf);
-  // x for the host's CPU branch, written over PCIe here so that only the final
-  // fence waits for it
+  // Every store of the block's results comes after its last barrier, so their
+  // round trips (the host copies' over PCIe) overlap: ids and gates, their host
+  // copies, and x for the host's CPU branch.
+  const int P = T * k;
+  for (int i = threadIdx.x; i < P; i += 256) {
+    idx[i] = s_ids[i];
+    gates[i] = s_gates[i];
+    if (pub_idx != nullptr) {
+      pub_idx[i] = s_ids[i];
+      pub_gates[i] = s_gates[i];
+    }
+  }
   if (pub_x != nullptr)
     for (int i = threadIdx.x * 8; i < T * d; i += 256 * 8)
       *reinterpret_cast<uint4*>(pub_x + i) = ld16(x + i);
@@ -1541,10 +1621,27 @@ int launch_router_decode(const uint16_t* x, const uint16_t* w, const uint8_t* al
              (da->dc.n_slots > 0 && (!da->dc.slot_key || !da->dc.slot_stamp))))
     return fail(FT_EINVAL, "router: bad decision arguments");
   DecideArgs none{};
-  dim3 grid(T, (E + 3) / 4);
-  router_decode_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(
-      x, w, allowed, T, d, E, k, logits_ws, idx, gates, ticket, pub_idx, pub_gates, pub_x, pub_flag, seq,
-      da ? *da : none, da ? 1 : 0);
+  const DecideArgs dargs = da ? *da : none;
+  const int dec = da ? 1 : 0;
+  // tokens per wavefront: all of them up to 8.  Experts per wavefront: more of them
+  // means fewer blocks to wait for at the ticket but longer logits per block; the
+  // choice measured best at E = 128 and 256 (one token: 2 per wavefront, 16 or 32
+  // blocks; eight tokens: 1 per wavefront, 32 blocks at E = 128)
+  const int tt = T == 1 ? 1 : T <= 4 ? 4 : 8;
+  const int te = T == 1 ? (E <= 64 ? 1 : E <= 256 ? 2 : 4) : (E <= 128 ? 1 : E <= 256 ? 2 : 4);
+  const dim3 grid((E + 4 * te - 1) / (4 * te), (T + tt - 1) / tt);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define FT_ROUTER_DECODE(TT_, TE_)                                                                                 \
+  router_decode_kernel<TT_, TE_><<<grid, 256, 0, s>>>(x, w, allowed, T, d, E, k, logits_ws, idx, gates, ticket, \
+                                                       pub_idx, pub_gates, pub_x, pub_flag, seq, dargs, dec)
+  if (tt == 1) {
+    if (te == 1) FT_ROUTER_DECODE(1, 1); else if (te == 2) FT_ROUTER_DECODE(1, 2); else FT_ROUTER_DECODE(1, 4);
+  } else if (tt == 4) {
+    if (te == 1) FT_ROUTER_DECODE(4, 1); else if (te == 2) FT_ROUTER_DECODE(4, 2); else FT_ROUTER_DECODE(4, 4);
+  } else {
+    if (te == 1) FT_ROUTER_DECODE(8, 1); else if (te == 2) FT_ROUTER_DECODE(8, 2); else FT_ROUTER_DECODE(8, 4);
+  }
+#undef FT_ROUTER_DECODE
   return launched("router_decode");
 }
 

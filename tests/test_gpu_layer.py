@@ -71,7 +71,21 @@ def test_decode_ragged_shape_parity(T):
     _decode_trace(RAGGED, 20000, 1, -1, T, 14)
 
 
-def _decode_trace(wl, fq, min_fill, max_fetch, T, N):
+# The decode router computes TT tokens x TE experts per wavefront (TT = 1, 4 or 8
+# by T; TE = 1, 2 or 4 by E and T): every pair of them, several token groups, E not
+# a multiple of the experts per block, and d with a partial last 512-element chunk.
+@pytest.mark.parametrize("E,d,k,T", [
+    (64, 200, 4, 1), (64, 200, 4, 4), (64, 200, 4, 13),
+    (100, 1032, 6, 1), (100, 1032, 6, 3), (100, 1032, 6, 8),
+    (256, 1032, 6, 1), (256, 1032, 6, 4), (256, 1032, 6, 8),
+    (600, 520, 8, 1), (600, 520, 8, 3), (600, 520, 8, 13),
+])
+def test_decode_router_blocking_parity(E, d, k, T):
+    wl = Workload(f"decode-E{E}-d{d}-top{k}", 20 + E % 7, Shape(2, E, d, 64, k), T, 0.5)
+    _decode_trace(wl, 20000, 1, -1, T, max(2 * T * k, E // 2), steps=3)
+
+
+def _decode_trace(wl, fq, min_fill, max_fetch, T, N, steps=6):
     torch = torch_mod()
     _say("decode", wl.name, fq, min_fill, max_fetch, T, N)
     s = wl.shape
@@ -79,7 +93,7 @@ def _decode_trace(wl, fq, min_fill, max_fetch, T, N):
     eng = Engine(s, pool, N, T_max=max(T, 8), frac_q16=fq, min_fill=min_fill, max_fetch=max_fetch, cpu_threads=4)
     try:
         ref_cache = SlotTable(N, s.L, s.E)
-        tr = zipf_reuse_trace(s.L, s.E, s.k, T, 6, 1.1, 0.6, generator(wl.seed_key, 3, T))
+        tr = zipf_reuse_trace(s.L, s.E, s.k, T, steps, 1.1, 0.6, generator(wl.seed_key, 3, T))
         wr_dev = [dev_u16(w) for w in wr]
         plan = ft.ft_plan()
         for step in range(tr.shape[0]):
