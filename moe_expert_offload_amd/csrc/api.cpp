@@ -160,8 +160,9 @@ struct ft_ctx {
   ft::DevPlan* d_plan = nullptr;  // device
   ft::DevPlan* h_plan = nullptr;  // pinned publication
 
-  hipEvent_t ev_route = nullptr, ev_done = nullptr;
+  hipEvent_t ev_route = nullptr, ev_done = nullptr, ev_hffn = nullptr;
   hipEvent_t ev_pf_fill[2] = {nullptr, nullptr}, ev_pf_comp[2] = {nullptr, nullptr};
+  hipStream_t side = nullptr;  // decode of 4 or more tokens: the hits' FFN beside the fills
 
   ft::ExpertCache* cache = nullptr;
   ft::CpuPool* cpu = nullptr;
@@ -380,11 +381,13 @@ int ft_create(const ft_shape* shape, const ft_config* config, const void* host_p
         hipHostMalloc((void**)&c->h_flag, 256) != hipSuccess ||
         hipHostMalloc((void**)&c->h_pf_idx, (size_t)c->cfg.T_max * shape->k * 4) != hipSuccess)
       return bail(FT_ENOMEM, "create: pinned staging allocation failed");
-    hipEvent_t* evs[] = {&c->ev_route, &c->ev_done, &c->ev_pf_fill[0], &c->ev_pf_fill[1],
+    hipEvent_t* evs[] = {&c->ev_route, &c->ev_done, &c->ev_hffn, &c->ev_pf_fill[0], &c->ev_pf_fill[1],
                          &c->ev_pf_comp[0], &c->ev_pf_comp[1]};
     for (hipEvent_t* e : evs)
       if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess)
         return bail(FT_EHIP, "create: hipEventCreate failed");
+    if (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess)
+      return bail(FT_EHIP, "create: hipStreamCreate failed");
     if (hipMemset(c->ws + c->cv.ticket, 0, 4) != hipSuccess) return bail(FT_EHIP, "create: hipMemset failed");
     if (hipMalloc((void**)&c->dc.where, (size_t)shape->L * shape->E * 4) != hipSuccess ||
         hipMalloc((void**)&c->dc.clock, 8) != hipSuccess ||
@@ -417,10 +420,11 @@ int ft_destroy(ft_ctx_t c) {
     (void)hipDeviceSynchronize();
   }
   if (c->cpu) ft::cpu_pool_destroy(c->cpu);
-  hipEvent_t evs[] = {c->ev_route, c->ev_done, c->ev_pf_fill[0], c->ev_pf_fill[1],
+  hipEvent_t evs[] = {c->ev_route, c->ev_done, c->ev_hffn, c->ev_pf_fill[0], c->ev_pf_fill[1],
                       c->ev_pf_comp[0], c->ev_pf_comp[1]};
   for (hipEvent_t e : evs)
     if (e) (void)hipEventDestroy(e);
+  if (c->side) (void)hipStreamDestroy(c->side);
   for (auto& r : c->prof) {
     for (hipEvent_t e : r.ev) c->ev_free.push_back(e);
     if (r.offsets) c->off_free.push_back(r.offsets);
@@ -626,7 +630,7 @@ int ft_expert_cache_resize(ft_ctx_t c, void* new_dev_slots, int32_t n) {
     if (n > 0 && (!new_dev_slots || (reinterpret_cast<uintptr_t>(new_dev_slots) & 255)))
       return fail(FT_EINVAL, "resize: need a 256-byte aligned slot buffer");
     FT_HIP(hipSetDevice(c->device));
-    hipEvent_t evs[] = {c->ev_route, c->ev_done, c->ev_pf_fill[0], c->ev_pf_fill[1],
+    hipEvent_t evs[] = {c->ev_route, c->ev_done, c->ev_hffn, c->ev_pf_fill[0], c->ev_pf_fill[1],
                         c->ev_pf_comp[0], c->ev_pf_comp[1]};
     for (hipEvent_t e : evs) {
       const hipError_t q = hipEventQuery(e);
@@ -691,7 +695,10 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
   float* d_h = c->wsp<float>(c->cv.h);
   float* d_out = c->wsp<float>(c->cv.out);
   const int nt_bound = T;  // rows per group are at most T
-  auto ffn = [&](int g0, int g1, int max_rows, const int32_t* g_hi, const int* rows_of) -> int {
+  // grouped FFN over groups [g0, g1) on stream s, further bounded on the device by
+  // *g_lo and *g_hi when given
+  auto ffn = [&](hipStream_t s, int g0, int g1, const int32_t* g_lo, const int32_t* g_hi,
+                 const int* rows_of) -> int {
     ft_ctx::ProfRec* r = prof_begin(c);
     if (r) {
       if (rows_of) {
@@ -703,18 +710,37 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
     void* const* ev = r ? reinterpret_cast<void* const*>(r->ev) : nullptr;
     if (c->mx)
       return ft::launch_mx_ffn_rows(xs, d, c->shape.d_ff, k, c->slots, c->d_plan->G_slot, c->d_plan->offsets,
-                                    c->d_plan->perm, g0, g1, max_rows, d_h, d_out, cs, ev, g_hi);
+                                    c->d_plan->perm, g0, g1, nt_bound, d_h, d_out, s, ev, g_lo, g_hi);
     return ft::launch_ffn_rows(xs, d, c->shape.d_ff, k, reinterpret_cast<const uint16_t*>(c->slots),
-                               c->d_plan->G_slot, c->d_plan->offsets, c->d_plan->perm, g0, g1, max_rows, d_h,
-                               d_out, cs, ev, g_hi);
+                               c->d_plan->G_slot, c->d_plan->offsets, c->d_plan->perm, g0, g1, nt_bound, d_h,
+                               d_out, s, ev, g_lo, g_hi);
   };
-  // the fills of F, read by the GPU from the pinned pool over PCIe into the victim
-  // slots the device chose, then the grouped FFN of G = H then F, launched for every
-  // possible group and bounded on the device by the plan's n_g
+  // The fills of F are read by the GPU from the pinned pool over PCIe into the victim
+  // slots the device chose, right behind the router.  The grouped FFN of G = H then F
+  // is launched for every possible group and bounded on the device by the plan.
+  // With 4 or more tokens the hits' FFN (bounded by n_h) runs on a side stream beside
+  // the fills, since it reads only slots that no fill of this call writes, and the
+  // FFN of F follows the fills once the host has seen q (below).  With fewer tokens
+  // the hits' FFN is too short to pay for the two cross-stream waits (measured on
+  // one MI355X, 40 layers d=2048 E=128 top-8 at one fetch fraction: the split takes
+  // batch 8 from 271 to 282 tok/s, batch 1 from 146 down to 134), and the whole FFN
+  // follows the fills.
+  const bool split_h = T >= 4;
+  const size_t prof_h = c->prof.size();
+  if (split_h) {
+    FT_HIP(hipStreamWaitEvent(c->side, c->ev_route, 0));
+    if (int rc = ffn(c->side, 0, P, nullptr, &c->d_plan->n_h, nullptr)) return rc;
+    FT_HIP(hipEventRecord(c->ev_hffn, c->side));
+  }
   if (int rc = ft::launch_fill(c->record(layer, 0), c->S, E, c->slots, c->cache->n_slots(), c->d_plan, cs))
     return rc;
-  const size_t prof_h = c->prof.size();
-  if (int rc = ffn(0, P, nt_bound, &c->d_plan->n_g, nullptr)) return rc;
+  if (split_h) {
+    // everything issued so far is behind ev_done, also when this call ends in an error
+    FT_HIP(hipStreamWaitEvent(cs, c->ev_hffn, 0));
+    FT_HIP(hipEventRecord(c->ev_done, cs));
+  } else {
+    if (int rc = ffn(cs, 0, P, nullptr, &c->d_plan->n_g, nullptr)) return rc;
+  }
   // wait for the publication (bounded spin on the sequence number, the event is
   // the fallback)
   {
@@ -783,7 +809,10 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
   for (int i = 0; i < P; ++i)
     if (p->pair_group[i] >= 0) ++rows_of[p->pair_group[i]];
   c->cache->stats.h2d_bytes += (int64_t)q * (int64_t)c->S;
-  if (prof_h < c->prof.size()) prof_account(c, &c->prof[prof_h], rows_of, n_g, 4);
+  if (prof_h < c->prof.size()) prof_account(c, &c->prof[prof_h], rows_of, split_h ? n_h : n_g, 4);
+  // the FFN of F = groups [n_h, n_g), behind the fills
+  if (split_h && q > 0)
+    if (int rc = ffn(cs, n_h, n_g, nullptr, nullptr, rows_of)) return rc;
   // merge of the CPU partial, then the combine
   const double t3 = now_us();
   const float* cpu_part = nullptr;
@@ -941,11 +970,11 @@ int capture_decode_graph(ft_decode_graph* g) {
     if ((rc = ft::launch_fill(c->record(l, 0), c->S, E, c->slots, c->cache->n_slots(), c->d_plan, g->cap))) break;
     if (c->mx)
       rc = ft::launch_mx_ffn_rows(xl, d, d_ff, k, c->slots, c->d_plan->G_slot, c->d_plan->offsets, c->d_plan->perm, 0,
-                                  P, T, d_h, d_out, g->cap, nullptr, &c->d_plan->n_g);
+                                  P, T, d_h, d_out, g->cap, nullptr, nullptr, &c->d_plan->n_g);
     else
       rc = ft::launch_ffn_rows(xl, d, d_ff, k, reinterpret_cast<const uint16_t*>(c->slots), c->d_plan->G_slot,
                                c->d_plan->offsets, c->d_plan->perm, 0, P, T, d_h, d_out, g->cap, nullptr,
-                               &c->d_plan->n_g);
+                               nullptr, &c->d_plan->n_g);
     if (rc) break;
     // the host node depends on the router alone; captured after the fills and the FFN
     // so that a runtime walking the nodes in capture order submits those first

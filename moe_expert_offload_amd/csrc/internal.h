@@ -98,12 +98,13 @@ int launch_permute(const int32_t* key, int P, int n_groups, int32_t* offsets, in
 
 // Row-streaming (GEMV-like) grouped FFN: h fp32 [rows, d_ff], out fp32 [rows, d].
 // ev (nullable): four hipEvent_t, start/stop of the gate/up kernel then of the down kernel.
-// g_hi (nullable, device): when given, only groups below *g_hi run (the launch
-// covers [g_begin, g_end) as an upper bound, for plans the host has not seen).
+// g_lo, g_hi (nullable, device): when given, only groups from *g_lo and below *g_hi
+// run (the launch covers [g_begin, g_end) as a bound, for plans the host has not
+// seen).
 int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
                     const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
                     int g_begin, int g_end, int max_rows, float* h, float* out, void* stream,
-                    void* const* ev = nullptr, const int32_t* g_hi = nullptr);
+                    void* const* ev = nullptr, const int32_t* g_lo = nullptr, const int32_t* g_hi = nullptr);
 
 // MFMA tile grouped FFN: h bf16 [rows, d_ff] (in the fp32-sized workspace), out fp32 [rows, d].
 // n_rows: rows of h and out (offsets[n_groups] at most; bounds the h reads)
@@ -118,7 +119,8 @@ size_t mx_record_bytes(int d, int d_ff);
 // Row-streaming grouped FFN over MXFP4 records, bf16 x: h fp32 [rows, d_ff], out fp32 [rows, d].
 int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t* slots, const int32_t* group_slot,
                        const int32_t* offsets, const int32_t* perm, int g_begin, int g_end, int max_rows, float* h,
-                       float* out, void* stream, void* const* ev = nullptr, const int32_t* g_hi = nullptr);
+                       float* out, void* stream, void* const* ev = nullptr, const int32_t* g_lo = nullptr,
+                       const int32_t* g_hi = nullptr);
 
 // Bytes of an MXFP8 copy of rows x n activations (codes then one scale per 32).
 size_t mx_act_ws_bytes(int rows, int n);

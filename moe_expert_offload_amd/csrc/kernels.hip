@@ -1033,16 +1033,17 @@ __global__ __launch_bounds__(256) void ffn_gateup_rows_kernel(
     const uint16_t* __restrict__ x, int d, int d_ff, int k, const uint16_t* __restrict__ slots,
     size_t rec_elems, const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, int g_begin, int blocks_per_group, float* __restrict__ h,
-    const int32_t* __restrict__ g_hi) {
+    const int32_t* __restrict__ g_lo, const int32_t* __restrict__ g_hi) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
   const int row = (blockIdx.x % blocks_per_group) * 4 + wave;
+  const int glo = g_lo != nullptr ? *g_lo : INT_MIN;
   const int ghi = g_hi != nullptr ? *g_hi : INT_MAX;
   const int slot = group_slot[g];
   const int r0 = offsets[g];
   const int r1 = offsets[g + 1];
-  if (row >= d_ff || g >= ghi || r1 <= r0) return;
+  if (row >= d_ff || g < glo || g >= ghi || r1 <= r0) return;
   const int n = r1 - r0;
   const __amdgpu_buffer_rsrc_t rec = buf_rsrc(slots + (size_t)slot * rec_elems, (uint32_t)(rec_elems * 2));
   const uint32_t og = (uint32_t)row * (uint32_t)d * 2u;
@@ -1098,18 +1099,20 @@ template <int NT>
 __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
     int d, int d_ff, const uint16_t* __restrict__ slots, size_t rec_elems,
     const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, int g_begin,
-    int blocks_per_group, const float* __restrict__ h, float* __restrict__ out, const int32_t* __restrict__ g_hi) {
+    int blocks_per_group, const float* __restrict__ h, float* __restrict__ out, const int32_t* __restrict__ g_lo,
+    const int32_t* __restrict__ g_hi) {
   constexpr int RW = 4;  // W_down rows per wavefront
   extern __shared__ float sh[];  // h rows of a batch of tokens [nt][d_ff], read by all 4 wavefronts
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
   const int row0 = ((blockIdx.x % blocks_per_group) * 4 + wave) * RW;
+  const int glo = g_lo != nullptr ? *g_lo : INT_MIN;
   const int ghi = g_hi != nullptr ? *g_hi : INT_MAX;
   const int slot = group_slot[g];
   const int r0 = offsets[g];
   const int r1 = offsets[g + 1];
-  if (g >= ghi || r1 <= r0) return;  // the whole block: it stages h below
+  if (g < glo || g >= ghi || r1 <= r0) return;  // the whole block: it stages h below
   const int n = r1 - r0;
   const __amdgpu_buffer_rsrc_t rec = buf_rsrc(slots + (size_t)slot * rec_elems, (uint32_t)(rec_elems * 2));
   const int span = row0 < d ? min(RW, d - row0) * d_ff : 0;  // elements of this wave's rows, contiguous
@@ -1705,7 +1708,7 @@ inline void timed_launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStrea
 int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
                     const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
                     int g_begin, int g_end, int max_rows, float* h, float* out, void* stream,
-                    void* const* ev, const int32_t* g_hi) {
+                    void* const* ev, const int32_t* g_lo, const int32_t* g_hi) {
   if (d <= 0 || d_ff <= 0 || d % 8 || d_ff % 8 || k < 1) return fail(FT_EINVAL, "ffn_rows: bad shape");
   const int ng = g_end - g_begin;
   if (ng <= 0) return FT_OK;
@@ -1721,14 +1724,14 @@ int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
 #define FT_ROWS_LAUNCH(NT)                                                                          \
   if (d <= 2048)                                                                                    \
     timed_launch(ffn_gateup_rows_kernel<NT, 4>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
-                 slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_hi);             \
+                 slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_lo, g_hi);             \
   else                                                                                              \
     timed_launch(ffn_gateup_rows_kernel<NT, 8>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
-                 slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_hi);             \
+                 slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_lo, g_hi);             \
   if (int rc = launched("ffn_gateup_rows")) return rc;                                              \
   timed_launch_shm(ffn_down_rows_kernel<NT>, dim3(ng * bpg_dn), dim3(256),                         \
                    (size_t)std::min(NT, std::max(1, 16384 / d_ff)) * d_ff * 4, s, ev, 1, d, d_ff, slots, \
-                   rec_elems, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out, g_hi);   \
+                   rec_elems, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out, g_lo, g_hi);   \
   return launched("ffn_down_rows");
   switch (nt) {
     case 1: { FT_ROWS_LAUNCH(1) }

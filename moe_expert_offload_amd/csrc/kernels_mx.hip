@@ -167,16 +167,18 @@ template <int NB, int RG>  // NB: blocks per lane and row (d <= 2048 * NB); RG r
 __global__ __launch_bounds__(256) void mx_gateup_rows_kernel(
     const uint16_t* __restrict__ x, int d, int d_ff, int k, const uint8_t* __restrict__ slots,
     const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-    int g_begin, int blocks_per_group, float* __restrict__ h, const int32_t* __restrict__ g_hi) {
+    int g_begin, int blocks_per_group, float* __restrict__ h, const int32_t* __restrict__ g_lo,
+    const int32_t* __restrict__ g_hi) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
   const int row0 = ((blockIdx.x % blocks_per_group) * 4 + wave) * RG;
+  const int glo = g_lo != nullptr ? *g_lo : INT_MIN;
   const int ghi = g_hi != nullptr ? *g_hi : INT_MAX;
   const int slot = group_slot[g];
   const int r0 = offsets[g];
   const int r1 = offsets[g + 1];
-  if (row0 >= d_ff || g >= ghi || r1 <= r0) return;
+  if (row0 >= d_ff || g < glo || g >= ghi || r1 <= r0) return;
   const int n = r1 - r0;
   const MxRec R = mx_rec(d, d_ff);
   const __amdgpu_buffer_rsrc_t rec = buf_rsrc(slots + (size_t)slot * R.bytes, (uint32_t)R.bytes);
@@ -245,17 +247,18 @@ template <int NT, int NB, int RW, bool C64 = false>  // NB: blocks per lane over
 __global__ __launch_bounds__(256) void mx_down_rows_kernel(
     int d, int d_ff, const uint8_t* __restrict__ slots, const int32_t* __restrict__ group_slot,
     const int32_t* __restrict__ offsets, int g_begin, int blocks_per_group, const float* __restrict__ h,
-    float* __restrict__ out, const int32_t* __restrict__ g_hi) {
+    float* __restrict__ out, const int32_t* __restrict__ g_lo, const int32_t* __restrict__ g_hi) {
   extern __shared__ float sh[];  // h rows of a batch of tokens, [nt][d_ff / 32][kHStride]
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
   const int row0 = ((blockIdx.x % blocks_per_group) * 4 + wave) * RW;
+  const int glo = g_lo != nullptr ? *g_lo : INT_MIN;
   const int ghi = g_hi != nullptr ? *g_hi : INT_MAX;
   const int slot = group_slot[g];
   const int r0 = offsets[g];
   const int r1 = offsets[g + 1];
-  if (g >= ghi || r1 <= r0) return;  // the whole block: it stages h below
+  if (g < glo || g >= ghi || r1 <= r0) return;  // the whole block: it stages h below
   const int n = r1 - r0;
   const MxRec R = mx_rec(d, d_ff);
   const __amdgpu_buffer_rsrc_t rec = buf_rsrc(slots + (size_t)slot * R.bytes, (uint32_t)R.bytes);
@@ -779,7 +782,7 @@ size_t mx_record_bytes(int d, int d_ff) { return mx_rec(d, d_ff).bytes; }
 
 int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t* slots, const int32_t* group_slot,
                        const int32_t* offsets, const int32_t* perm, int g_begin, int g_end, int max_rows, float* h,
-                       float* out, void* stream, void* const* ev, const int32_t* g_hi) {
+                       float* out, void* stream, void* const* ev, const int32_t* g_lo, const int32_t* g_hi) {
   if (d % 64 || d_ff % 64 || k < 1) return fail(FT_EINVAL, "mx_ffn_rows: need d%64==0 and d_ff%64==0");
   const int ng = g_end - g_begin;
   if (ng <= 0) return FT_OK;
@@ -800,15 +803,15 @@ int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t*
   const int bpg_dn = (d + 4 * rw - 1) / (4 * rw);
 #define FT_MX_UP(NB)                                                                                         \
   timed_launch(mx_gateup_rows_kernel<NB, NB <= 2 ? 2 : 1>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
-               slots, group_slot, offsets, perm, g_begin, bpg_up, h, g_hi)
+               slots, group_slot, offsets, perm, g_begin, bpg_up, h, g_lo, g_hi)
 #define FT_MX_DN(NT, NB, RW)                                                                                 \
   timed_launch_shm(mx_down_rows_kernel<NT, NB, RW>, dim3(ng * bpg_dn), dim3(256),                             \
                    (size_t)mx_down_rows_per_batch(NT, d_ff) * (d_ff / 32) * kHStride * 4, s, ev, 1, d,         \
-                   d_ff, slots, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out, g_hi)
+                   d_ff, slots, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out, g_lo, g_hi)
 #define FT_MX_DN64(NT)                                                                                       \
   timed_launch_shm(mx_down_rows_kernel<NT, 8, 8, true>, dim3(ng * bpg_dn), dim3(256),                          \
                    (size_t)mx_down_rows_per_batch(NT, d_ff) * (d_ff / 32) * kHStride * 4, s, ev, 1, d,         \
-                   d_ff, slots, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out, g_hi)
+                   d_ff, slots, group_slot, offsets, g_begin, bpg_dn, (const float*)h, out, g_lo, g_hi)
 #define FT_MX_ROWS(NT)                                                     \
   if (nbu <= 1) FT_MX_UP(1); else if (nbu <= 2) FT_MX_UP(2); else FT_MX_UP(4);            \
   if (int rc = launched("mx_gateup_rows")) return rc;                      \
