@@ -279,6 +279,9 @@ def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warm
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                 "traffic": stored_traffic("ffn_gateup_rows_kernel", args.workload),
                 "avg_launch_us": round(ms_gu * 1e3, 3), "algorithmic_bytes_per_launch": round(bytes_gu)}
+    if T >= 4:
+        # the library runs the hits' FFN beside the fills for 4 or more tokens
+        roofline["schedule"] = "hits' FFN launched beside fill_kernel: durations include the overlap"
     return res, roofline, (pool, wl, tr, fq, L_phys)
 
 
