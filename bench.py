@@ -252,6 +252,9 @@ def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warm
         "h2d_GB_per_step": stats["h2d_bytes"] / args.steps / 1e9,
         "modelled_floor_ms_per_step": floor_s / args.steps * 1e3 if floor_s is not None else None,
         "host_cpu_branch_ms_per_step": sum(c[4] for c in calls) / args.steps / 1e3,
+        # rate of the host branch over its own work time (records of C per second)
+        "cpu_branch_GBs": (sum(c[3] for c in calls) * S / (sum(c[9] for c in calls) * 1e-6) / 1e9
+                           if calls and sum(c[9] for c in calls) > 0 else None),
         "host_call_us": {
             "route": float(np.mean([c[6] for c in calls])) if calls else 0.0,
             "ctrl": float(np.mean([c[7] for c in calls])) if calls else 0.0,
@@ -283,6 +286,23 @@ def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warm
         # the library runs the hits' FFN beside the fills for 4 or more tokens
         roofline["schedule"] = "hits' FFN launched beside fill_kernel: durations include the overlap"
     return res, roofline, (pool, wl, tr, fq, L_phys)
+
+
+def dma_h2d_rate(torch, nbytes=1 << 31, reps=3):
+    """Rate of a plain pinned host -> device copy (the copy engine path the prefill's
+    layer loads take), best of a few."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    best = 0.0
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src, non_blocking=True)
+        b.record()
+        b.synchronize()
+        best = max(best, nbytes / (a.elapsed_time(b) * 1e-3))
+    del src, dst
+    return best
 
 
 def run_prefill(args, torch, ft, synth, HostPool):
@@ -347,6 +367,7 @@ def run_prefill(args, torch, ft, synth, HostPool):
                 el_off = time.perf_counter() - t2
             finally:
                 ft.ft_destroy(ctx)
+        b_dma = dma_h2d_rate(torch)
     finally:
         pool.free()
     el = t1 - t0
@@ -354,12 +375,24 @@ def run_prefill(args, torch, ft, synth, HostPool):
     fl = prof["flops_gateup"] + prof["flops_down"]
     tflops = fl / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
     by = prof["bytes_gateup"] + prof["bytes_down"]
+    h2d = s.L * s.E * S
+    t_xfer = h2d / b_dma
+    t_comp_last = ms / max(prof["launches"], 1) * 1e-3
+    # attainable at this shape: the weight stream at peak HBM bandwidth times the flops per weight byte
+    ai = fl / max(prof["bytes_gateup"] + prof["bytes_down"], 1.0)
+    attainable = min(MFMA_BF16_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
     return {
         "tok_s": T / el, "s_per_chunk": el, "T": T, "L": s.L, "L_phys": L_phys, "n_slots": N,
-        "h2d_GB": s.L * s.E * S / 1e9, "h2d_GBs_effective": s.L * s.E * S / el / 1e9,
+        "h2d_GB": h2d / 1e9, "h2d_GBs_effective": h2d / el / 1e9,
+        # overlap efficiency (sum of transfer times at the measured copy rate, plus the last
+        # layer's compute) / wall time
+        "dma_h2d_GBs": round(b_dma / 1e9, 2), "transfer_floor_s": round(t_xfer, 4),
+        "overlap_efficiency": round((t_xfer + t_comp_last) / el, 4),
         "ffn_kernel_ms_per_layer": ms / max(prof["launches"], 1),
         "ffn_mfma": {"bound_note": "weight stream: HBM-bound at this shape", "TFLOPs": round(tflops, 1),
                      "frac_of_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "flop_per_byte": round(ai, 1), "attainable_TFLOPs": round(attainable, 1),
+                     "frac_of_attainable": round(tflops / attainable, 4),
                      "GBs": round(by / (ms * 1e-3) / 1e9, 1) if ms > 0 else 0.0,
                      "gateup_ms_per_layer": prof["ms_gateup"] / max(prof["launches"], 1),
                      "down_ms_per_layer": prof["ms_down"] / max(prof["launches"], 1)},
@@ -638,6 +671,7 @@ def run_config2(args, torch, ft, synth, HostPool):
                                             "timed_steps", "B_P_GBs", "B_H_GBs", "frac_q16", "min_fill",
                                             "miss_rate_reads", "fills_per_step", "cpu_experts_per_step",
                                             "h2d_GB_per_step", "modelled_floor_ms_per_step", "host_call_us",
+                                            "cpu_branch_GBs",
                                             "kernels")}
         out["batch1"]["roofline"] = r1
         if args.min_fill0 and args.min_fill != 0:
