@@ -518,7 +518,7 @@ int ft_grouped_ffn(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t k,
   if (form != 1) return fail(FT_EINVAL, "grouped_ffn: form must be 0, 1 or 2");
   return ft::launch_ffn_rows(static_cast<const uint16_t*>(x), d, d_ff, k, static_cast<const uint16_t*>(slots),
                              group_slot, offsets, perm, g_begin, g_end, max_rows_per_group,
-                             static_cast<float*>(h_ws), out, stream);
+                             static_cast<float*>(h_ws), out, stream, nullptr, nullptr, nullptr, T == 1);
 }
 
 size_t ft_grouped_ffn_mx_workspace_bytes(int32_t T, int32_t d, int32_t d_ff, int32_t n_rows) {
@@ -549,7 +549,7 @@ int ft_grouped_ffn_mx(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   if (form == 1)
     return ft::launch_mx_ffn_rows(xb, d, d_ff, k, sl, group_slot, offsets, perm, g_begin, g_end, max_rows_per_group,
-                                  h, out, stream);
+                                  h, out, stream, nullptr, nullptr, nullptr, T == 1);
   if (form == 2)
     return ft::launch_mx_ffn_mfma(xb, T, d, d_ff, k, sl, group_slot, offsets, perm, g_begin, g_end, n_rows, xq, xs, h,
                                   hq, hs, out, stream);
@@ -710,10 +710,10 @@ int ft_moe_decode_layer(ft_ctx_t c, int32_t layer, const void* x, int32_t T, con
     void* const* ev = r ? reinterpret_cast<void* const*>(r->ev) : nullptr;
     if (c->mx)
       return ft::launch_mx_ffn_rows(xs, d, c->shape.d_ff, k, c->slots, c->d_plan->G_slot, c->d_plan->offsets,
-                                    c->d_plan->perm, g0, g1, nt_bound, d_h, d_out, s, ev, g_lo, g_hi);
+                                    c->d_plan->perm, g0, g1, nt_bound, d_h, d_out, s, ev, g_lo, g_hi, T == 1);
     return ft::launch_ffn_rows(xs, d, c->shape.d_ff, k, reinterpret_cast<const uint16_t*>(c->slots),
                                c->d_plan->G_slot, c->d_plan->offsets, c->d_plan->perm, g0, g1, nt_bound, d_h,
-                               d_out, s, ev, g_lo, g_hi);
+                               d_out, s, ev, g_lo, g_hi, T == 1);
   };
   // The fills of F are read by the GPU from the pinned pool over PCIe into the victim
   // slots the device chose, right behind the router.  The grouped FFN of G = H then F
@@ -970,11 +970,11 @@ int capture_decode_graph(ft_decode_graph* g) {
     if ((rc = ft::launch_fill(c->record(l, 0), c->S, E, c->slots, c->cache->n_slots(), c->d_plan, g->cap))) break;
     if (c->mx)
       rc = ft::launch_mx_ffn_rows(xl, d, d_ff, k, c->slots, c->d_plan->G_slot, c->d_plan->offsets, c->d_plan->perm, 0,
-                                  P, T, d_h, d_out, g->cap, nullptr, nullptr, &c->d_plan->n_g);
+                                  P, T, d_h, d_out, g->cap, nullptr, nullptr, &c->d_plan->n_g, T == 1);
     else
       rc = ft::launch_ffn_rows(xl, d, d_ff, k, reinterpret_cast<const uint16_t*>(c->slots), c->d_plan->G_slot,
                                c->d_plan->offsets, c->d_plan->perm, 0, P, T, d_h, d_out, g->cap, nullptr,
-                               nullptr, &c->d_plan->n_g);
+                               nullptr, &c->d_plan->n_g, T == 1);
     if (rc) break;
     // the host node depends on the router alone; captured after the fills and the FFN
     // so that a runtime walking the nodes in capture order submits those first

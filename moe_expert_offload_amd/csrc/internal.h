@@ -100,11 +100,12 @@ int launch_permute(const int32_t* key, int P, int n_groups, int32_t* offsets, in
 // ev (nullable): four hipEvent_t, start/stop of the gate/up kernel then of the down kernel.
 // g_lo, g_hi (nullable, device): when given, only groups from *g_lo and below *g_hi
 // run (the launch covers [g_begin, g_end) as a bound, for plans the host has not
-// seen).
+// seen).  one_token: x holds one token row, every pair's (no permutation lookup).
 int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
                     const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
                     int g_begin, int g_end, int max_rows, float* h, float* out, void* stream,
-                    void* const* ev = nullptr, const int32_t* g_lo = nullptr, const int32_t* g_hi = nullptr);
+                    void* const* ev = nullptr, const int32_t* g_lo = nullptr, const int32_t* g_hi = nullptr,
+                    int one_token = 0);
 
 // MFMA tile grouped FFN: h bf16 [rows, d_ff] (in the fp32-sized workspace), out fp32 [rows, d].
 // n_rows: rows of h and out (offsets[n_groups] at most; bounds the h reads)
@@ -120,7 +121,7 @@ size_t mx_record_bytes(int d, int d_ff);
 int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t* slots, const int32_t* group_slot,
                        const int32_t* offsets, const int32_t* perm, int g_begin, int g_end, int max_rows, float* h,
                        float* out, void* stream, void* const* ev = nullptr, const int32_t* g_lo = nullptr,
-                       const int32_t* g_hi = nullptr);
+                       const int32_t* g_hi = nullptr, int one_token = 0);
 
 // Bytes of an MXFP8 copy of rows x n activations (codes then one scale per 32).
 size_t mx_act_ws_bytes(int rows, int n);

@@ -1033,7 +1033,7 @@ __global__ __launch_bounds__(256) void ffn_gateup_rows_kernel(
     const uint16_t* __restrict__ x, int d, int d_ff, int k, const uint16_t* __restrict__ slots,
     size_t rec_elems, const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, int g_begin, int blocks_per_group, float* __restrict__ h,
-    const int32_t* __restrict__ g_lo, const int32_t* __restrict__ g_hi) {
+    const int32_t* __restrict__ g_lo, const int32_t* __restrict__ g_hi, int one_token) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
@@ -1069,7 +1069,8 @@ __global__ __launch_bounds__(256) void ffn_gateup_rows_kernel(
       }
       if (j0 == 0) {  // token rows, looked up once the first weights are in flight
 #pragma unroll
-        for (int i = 0; i < NT; ++i) xr[i] = (tb + i < n) ? x + (size_t)(perm[r0 + tb + i] / k) * d : nullptr;
+        for (int i = 0; i < NT; ++i)
+          xr[i] = tb + i >= n ? nullptr : one_token ? x : x + (size_t)(perm[r0 + tb + i] / k) * d;
       }
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
@@ -1708,7 +1709,7 @@ inline void timed_launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStrea
 int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
                     const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
                     int g_begin, int g_end, int max_rows, float* h, float* out, void* stream,
-                    void* const* ev, const int32_t* g_lo, const int32_t* g_hi) {
+                    void* const* ev, const int32_t* g_lo, const int32_t* g_hi, int one_token) {
   if (d <= 0 || d_ff <= 0 || d % 8 || d_ff % 8 || k < 1) return fail(FT_EINVAL, "ffn_rows: bad shape");
   const int ng = g_end - g_begin;
   if (ng <= 0) return FT_OK;
@@ -1724,10 +1725,10 @@ int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
 #define FT_ROWS_LAUNCH(NT)                                                                          \
   if (d <= 2048)                                                                                    \
     timed_launch(ffn_gateup_rows_kernel<NT, 4>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
-                 slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_lo, g_hi);             \
+                 slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_lo, g_hi, one_token);             \
   else                                                                                              \
     timed_launch(ffn_gateup_rows_kernel<NT, 8>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
-                 slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_lo, g_hi);             \
+                 slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_lo, g_hi, one_token);             \
   if (int rc = launched("ffn_gateup_rows")) return rc;                                              \
   timed_launch_shm(ffn_down_rows_kernel<NT>, dim3(ng * bpg_dn), dim3(256),                         \
                    (size_t)std::min(NT, std::max(1, 16384 / d_ff)) * d_ff * 4, s, ev, 1, d, d_ff, slots, \

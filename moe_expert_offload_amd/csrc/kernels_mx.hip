@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void mx_gateup_rows_kernel(
     const uint16_t* __restrict__ x, int d, int d_ff, int k, const uint8_t* __restrict__ slots,
     const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
     int g_begin, int blocks_per_group, float* __restrict__ h, const int32_t* __restrict__ g_lo,
-    const int32_t* __restrict__ g_hi) {
+    const int32_t* __restrict__ g_hi, int one_token) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256) void mx_gateup_rows_kernel(
   // one token at a time: its 32 activations per block of the lane are read once and
   // applied to all RG row pairs
   for (int t = 0; t < n; ++t) {
-    const uint16_t* xr = x + (size_t)(perm[r0 + t] / k) * d;
+    const uint16_t* xr = one_token ? x : x + (size_t)(perm[r0 + t] / k) * d;
     uint4 xv[NB][4];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -782,7 +782,8 @@ size_t mx_record_bytes(int d, int d_ff) { return mx_rec(d, d_ff).bytes; }
 
 int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t* slots, const int32_t* group_slot,
                        const int32_t* offsets, const int32_t* perm, int g_begin, int g_end, int max_rows, float* h,
-                       float* out, void* stream, void* const* ev, const int32_t* g_lo, const int32_t* g_hi) {
+                       float* out, void* stream, void* const* ev, const int32_t* g_lo, const int32_t* g_hi,
+                       int one_token) {
   if (d % 64 || d_ff % 64 || k < 1) return fail(FT_EINVAL, "mx_ffn_rows: need d%64==0 and d_ff%64==0");
   const int ng = g_end - g_begin;
   if (ng <= 0) return FT_OK;
@@ -803,7 +804,7 @@ int launch_mx_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint8_t*
   const int bpg_dn = (d + 4 * rw - 1) / (4 * rw);
 #define FT_MX_UP(NB)                                                                                         \
   timed_launch(mx_gateup_rows_kernel<NB, NB <= 2 ? 2 : 1>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
-               slots, group_slot, offsets, perm, g_begin, bpg_up, h, g_lo, g_hi)
+               slots, group_slot, offsets, perm, g_begin, bpg_up, h, g_lo, g_hi, one_token)
 #define FT_MX_DN(NT, NB, RW)                                                                                 \
   timed_launch_shm(mx_down_rows_kernel<NT, NB, RW>, dim3(ng * bpg_dn), dim3(256),                             \
                    (size_t)mx_down_rows_per_batch(NT, d_ff) * (d_ff / 32) * kHStride * 4, s, ev, 1, d,         \
