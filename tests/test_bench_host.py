@@ -1,0 +1,58 @@
+"""CPU tests of bench.py's host-side parts: the modelled floor uses the oracle's pinned
+phase-aware cost model, the committed HBM counter summaries belong to the current gate/up
+kernel source, and the bench refuses more than one GPU before touching any."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+from oracle.qstar import phased_step_time
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_modelled_floor_is_the_oracle_cost_model():
+    b = _bench()
+    rng = np.random.default_rng(5)
+    for _ in range(2000):
+        m = int(rng.integers(0, 17))
+        q = int(rng.integers(0, m + 1))
+        S = float(rng.uniform(1e6, 6e7))
+        B_P = float(rng.uniform(5e9, 7e10))
+        B_H = float(rng.uniform(1e9, 3e11))
+        assert b.phased_time(m, q, S, B_P, B_H) == pytest.approx(phased_step_time(m, q, S, B_P, B_H), rel=1e-12)
+
+
+@pytest.mark.parametrize("workload", ["decode-L43-d4096-E256-top6", "decode-L40-d2048-E128-top8"])
+def test_committed_counters_match_the_current_kernel(workload):
+    """bench.py reports `traffic` only from counters taken on the current gate/up kernel
+    source; the committed summaries must be those."""
+    b = _bench()
+    h = b.kernel_source_hash("ffn_gateup_rows_kernel")
+    assert h is not None and len(h) == 16
+    traffic = b.stored_traffic("ffn_gateup_rows_kernel", workload)
+    assert traffic is not None and traffic > 1e7
+
+
+def test_unknown_kernel_or_workload_has_no_counters():
+    b = _bench()
+    assert b.kernel_source_hash("no_such_kernel") is None
+    assert b.stored_traffic("ffn_gateup_rows_kernel", "no-such-workload") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], cwd=ROOT,
+                       stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
