@@ -30,12 +30,14 @@ def _compare_plan(plan, ref_plan, ref_idx, where):
     assert got["route_slot"] == ref_plan.route_slot.reshape(-1).tolist(), where
 
 
-@pytest.mark.parametrize("key,L_phys,steps,y_every,fq", [
-    ("decode-L40-d2048-E128-top8", 40, 6, 4, 22337),     # 40 layers d=2048 E=128 top-8, batch 1, full pool, cache 37 %
-    ("decode-L40-d2048-E128-top8-b8", 40, 4, 16, 22337),  # same, batch 8
-    ("decode-L43-d4096-E256-top6", 2, 3, 8, 18000),      # 43 layers d=4096 E=256 top-6, batch 1, cache 11 %, aliased pool
+# y is checked on every y_every-th call, and on every layer of every y_step-th step
+@pytest.mark.parametrize("key,L_phys,steps,y_every,y_step,fq", [
+    ("decode-L40-d2048-E128-top8", 40, 6, 4, 0, 22337),     # 40 layers d=2048 E=128 top-8, batch 1, full pool, cache 37 %
+    ("decode-L40-d2048-E128-top8-b8", 40, 4, 16, 0, 22337),  # same, batch 8
+    ("decode-L43-d4096-E256-top6", 2, 9, 0, 8, 18000),      # 43 layers d=4096 E=256 top-6, batch 1, cache 11 %, aliased
+                                                             # pool: decisions on every call, y on every layer of steps 0, 8
 ])
-def test_decode_full_size(key, L_phys, steps, y_every, fq):
+def test_decode_full_size(key, L_phys, steps, y_every, y_step, fq):
     torch = torch_mod()
     wl = synth.WORKLOADS[key]
     s = wl.shape
@@ -62,8 +64,9 @@ def test_decode_full_size(key, L_phys, steps, y_every, fq):
                 idx, g, _ = route(x, wr[l], s.k, allowed)
                 ref_plan = ref_cache.lookup(l, idx, fq, 1, -1)
                 _compare_plan(plan, ref_plan, idx, (st, l))
-                if call % y_every == 0:
-                    ref_y = moe_layer(x, idx, g, lambda e: pool.view[(l % L_phys) * s.E + e], s.d, s.d_ff)
+                if (y_every and call % y_every == 0) or (y_step and st % y_step == 0):
+                    ref_y = moe_layer(x, idx, g, lambda e: pool.view[(l % L_phys) * s.E + e], s.d, s.d_ff,
+                                      workers=8)
                     ok, mx, l1 = within_tolerance(host(y), ref_y)
                     assert ok, (st, l, mx, l1)
                 call += 1
