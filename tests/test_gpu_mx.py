@@ -258,7 +258,8 @@ def test_mx_full_size_prefill_chunk_and_decode():
     """The MXFP4 configuration at full size: d=4096, E=256, top-6, d_ff=2048; one
     8192-token chunk through two layers (double-buffered, aliased pool of two
     physical layers): every routed id bit-exact, y on tokens reaching every expert
-    group and the tile edges; then batch-1 decode steps with the cache of 1210 slots."""
+    group and the tile edges; then 9 batch-1 decode steps over all 43 layers with the cache
+    of 1210 slots: every decision bit-exact, y on every layer of steps 0 and 8."""
     torch = torch_mod()
     wl = synth.WORKLOADS["mxfp4-prefill8k-L43-d4096-E256-top6"]
     s = wl.shape
@@ -295,10 +296,10 @@ def test_mx_full_size_prefill_chunk_and_decode():
             ok, mxe, l1 = within_tolerance(host(y)[sample], ref_y)
             assert ok, (l, mxe, l1)
         wd = synth.WORKLOADS["mxfp4-decode-L43-d4096-E256-top6"]
-        tr = synth.trace_for(wd, steps=2)
+        tr = synth.trace_for(wd, steps=9)
         plan = ft.ft_plan()
-        for st in range(2):
-            for l in (0, 21, 42):
+        for st in range(9):  # decisions on every call; outputs on every layer of steps 0 and 8
+            for l in range(s.L):
                 x = synth.tokens(wd, st, l, T=1)
                 wr = synth.router_weights(wd, l)
                 allowed = allowed_mask(tr[st, l], s.E)
@@ -309,9 +310,10 @@ def test_mx_full_size_prefill_chunk_and_decode():
                 idx, g, _ = route(x, wr, s.k, allowed)
                 ref_plan = ref_cache.lookup(l, idx, 20000, 1, -1)
                 _compare_plan(plan, ref_plan, idx, (st, l))
-                if st == 1:
-                    continue  # outputs on the first step, decisions on both
-                ref_y = mx.moe_layer(x, idx, g, lambda e: pool.view[(l % L_phys) * s.E + e], s.d, s.d_ff)
+                if st % 8:
+                    continue
+                ref_y = mx.moe_layer(x, idx, g, lambda e: pool.view[(l % L_phys) * s.E + e], s.d, s.d_ff,
+                                     workers=8)
                 ok, mxe, l1 = within_tolerance(host(y), ref_y)
                 assert ok, (st, l, mxe, l1)
     finally:
