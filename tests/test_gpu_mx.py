@@ -319,3 +319,53 @@ def test_mx_full_size_prefill_chunk_and_decode():
     finally:
         eng.destroy()
         pool.free()
+
+
+def test_mx_prefill_8k_all_layers_sampled():
+    """The whole 43-layer pass of an 8192-token chunk with MXFP4 experts (scaled MFMA on
+    MXFP8 activations, double buffered over an aliased pool of 2 physical layers): on every
+    layer, the ids the layer call routed and y, for 3 seeded tokens, against the oracle's
+    prefill form; the residency the pass leaves."""
+    torch = torch_mod()
+    wl = synth.WORKLOADS["mxfp4-prefill8k-L43-d4096-E256-top6"]
+    s = wl.shape
+    T = wl.T
+    L_phys = 2
+    _say("mx prefill all layers", wl.name)
+    pool = PinnedPool(s, L_phys * s.E)
+    pool.fill_device_random(wl.seed_key)
+    eng = Engine(s, pool, wl.n_slots, T_max=T, frac_q16=20000, prefill_overlap=1, L_phys=L_phys, cpu_threads=0)
+    try:
+        ref_cache = SlotTable(wl.n_slots, s.L, s.E)
+        ft.ft_moe_prefill_begin(eng.ctx, eng.copy)
+        ref_cache.prefill_begin()
+        rng = np.random.default_rng(53)
+        outs = []
+        for l in range(s.L):
+            xd = synth.tokens_torch(wl.seed_key, 0, l, T, s.d)
+            wr = synth.router_weights(wl, l)
+            y = torch.empty((T, s.d), dtype=torch.float32, device="cuda")
+            ids = torch.empty((T, s.k), dtype=torch.int32, device="cuda")
+            ft.ft_moe_prefill_layer(eng.ctx, l, xd, T, dev_u16(wr), y, copy=eng.copy)
+            ft.ft_layer_routing(eng.ctx, ids, None, T)
+            sample = np.sort(rng.choice(T, size=3, replace=False))
+            sel = torch.from_numpy(sample).cuda()
+            outs.append((l, sample, xd.index_select(0, sel), wr, y.index_select(0, sel), ids.index_select(0, sel)))
+        ft.ft_moe_prefill_end(eng.ctx)
+        ref_cache.prefill_end(s.L)
+        torch.cuda.synchronize()
+        for l, sample, xs, wr, ys, ids in outs:
+            x = host(xs).view(np.uint16)
+            idx, g, _ = route(x, wr, s.k)
+            assert np.array_equal(host(ids), idx), (l, sample)
+            ref_y = mx.moe_layer(x, idx, g, lambda e: pool.view[(l % L_phys) * s.E + e], s.d, s.d_ff,
+                                 form="prefill", workers=8)
+            ok, mxe, l1 = within_tolerance(host(ys), ref_y)
+            assert ok, (l, sample, mxe, l1)
+        res = ref_cache.resident()
+        for l in (0, s.L - 3, s.L - 2, s.L - 1):
+            for e in range(0, s.E, 17):
+                assert ft.ft_expert_cache_where(eng.ctx, l, e) == res.get(l * s.E + e, -1)
+    finally:
+        eng.destroy()
+        pool.free()
