@@ -411,189 +411,223 @@ __global__ __launch_bounds__(256) void mx_quant_act_kernel(const In* __restrict_
 
 // ---- scaled-MFMA grouped FFN ---------------------------------------------------------
 // Block: 256 threads = 4 waves, one per SIMD.  One pass covers up to 256 rows of one
-// expert (8 row subtiles of 32) and a column strip per wave, so every weight byte is
-// read from HBM once per pass, straight into the registers of the one wave that uses
-// it (prefetched three stages ahead).  Token rows (MXFP8 codes and their scales) are
-// staged through LDS (three rotating buffers) and shared by the 4 waves.
-// K runs in stages of 128 elements = two scaled MFMAs.  MFMA i (0, 1) of a stage
+// expert (8 row subtiles of 32) and 256 weight rows ("B columns"), 64 per wave, so
+// every weight byte is read from HBM once per pass.  K runs in stages of 128 elements
+// = two scaled MFMAs per row subtile and column subtile.  MFMA i (0, 1) of a stage
 // takes as its K positions 0..31 the stage's block i and as positions 32..63 its
 // block i + 2 (any pairing is exact as long as both operands and both scales follow
-// it); then a lane's E2M1 codes for a stage are 32 contiguous bytes per weight row.
-constexpr int QM = 256;        // rows per pass
-constexpr int QK = 128;        // K elements per stage
-constexpr int QLD = QK + 16;   // padded LDS row of fp8 codes (bytes)
-#ifndef QDEPTH
-#define QDEPTH 3               // weight stages in flight
-#endif
+// it); then a lane's E2M1 codes for an MFMA are one 16-byte piece of a weight row.
+//
+// All four operand streams of a stage (token-row codes and scales, weight codes and
+// scales) go straight from memory into one LDS stage buffer (`buffer_load ... lds`,
+// no registers in between), two stages ahead, through three buffers of 50 KB.  A wave
+// loads 64 of the token rows (shared by the 4 waves behind the stage barrier) and its
+// own 64 weight rows: 14 loads per wave per stage, one after each of the stage's first
+// MFMAs, waited for by one explicit `s_waitcnt vmcnt` at the top of the stage they
+// feed.  (Loads into registers leave the waits to the compiler, which drains every
+// load at the head of the K loop: the memory latency then lands on every few stages.)
+//
+// Stage buffer (bytes): token-row codes, row r at 128 r with 16-byte piece p at
+// physical piece p ^ swz8(r) | their scales, 4 bytes per row (the stage's 4 blocks) |
+// weight codes, column c at 64 c with piece p at physical piece p ^ swz4(c) | weight
+// scales, 4 bytes per column.  The swizzles put the 8 or 16 lanes of one LDS read
+// phase (consecutive rows, one logical piece) on as many different bank groups.
+constexpr int QM = 256;                    // rows per pass
+constexpr int QK = 128;                    // K elements per stage
+constexpr int QXS = QM * QK;               // offset of the token-row scales in a stage buffer
+constexpr int QWC = QXS + QM * 4;          // offset of the weight codes
+constexpr int QWS = QWC + 256 * (QK / 2);  // offset of the weight scales
+constexpr int QSTAGE = QWS + 256 * 4;      // one stage buffer: 51200 bytes
+constexpr int QNB = 3;                     // stage buffers
+constexpr int QLOADS = 14;                 // loads per wave per stage
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
   const int q = nb >> 3, r = nb & 7, x = b & 7;
   return x * q + (x < r ? x : r) + (b >> 3);
 }
 
-// Token-row staging of one stage: thread tid copies 16 B pieces (row tid/8 + 32j,
-// part tid%8) for j = 0..7, and the 4 scale bytes of row tid.  Rows past the group's
-// end read a valid row instead (their products land in rows that are never stored).
-struct QRowStage {
-  const uint8_t* src[8];
-  const uint8_t* ssrc;
-  uint4 v[8];
-  uint32_t sc;
-  __device__ __forceinline__ void load(int k0) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const uint4*>(src[j] + k0);
-    sc = *reinterpret_cast<const uint32_t*>(ssrc + k0 / 32);
-  }
-  __device__ __forceinline__ void store(uint8_t* buf, uint32_t* sbuf, int tid) const {
-    uint8_t* dst = buf + (tid >> 3) * QLD + (tid & 7) * 16;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(dst + 32 * j * QLD) = v[j];
-    sbuf[tid] = sc;
-  }
-};
+__device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swz4(int c) { return ((c >> 1) ^ (c >> 3)) & 3; }
 
-// A lane's weights for one stage and two column subtiles: codes (2 x 16 B each) and
-// the 4 scale bytes of each of its two weight rows.
-struct QW {
-  uint4 c[4];   // [subtile 0: MFMA 0, 1][subtile 1: MFMA 0, 1]
-  uint32_t s[2];
-};
-
-__device__ __forceinline__ void load_qw(QW& w, const uint8_t* c0, const uint8_t* c1, const uint8_t* s0,
-                                        const uint8_t* s1, int k0) {
-  w.c[0] = *reinterpret_cast<const uint4*>(c0 + k0 / 2);
-  w.c[1] = *reinterpret_cast<const uint4*>(c0 + k0 / 2 + 16);
-  w.c[2] = *reinterpret_cast<const uint4*>(c1 + k0 / 2);
-  w.c[3] = *reinterpret_cast<const uint4*>(c1 + k0 / 2 + 16);
-  w.s[0] = *reinterpret_cast<const uint32_t*>(s0 + k0 / 32);
-  w.s[1] = *reinterpret_cast<const uint32_t*>(s1 + k0 / 32);
+// One load from buffer `rs` at byte offset off + kbytes into LDS at byte address
+// lds + 16 * lane (lds16) or lds + 4 * lane (lds4).  Out-of-range offsets read zeros.
+__device__ __forceinline__ void lds16(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t kbytes, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(off), "s"(rs), "s"(kbytes) : "memory", "m0");
+}
+__device__ __forceinline__ void lds4(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t kbytes, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(off), "s"(rs), "s"(kbytes) : "memory", "m0");
 }
 
-__device__ __forceinline__ v8i_t fp4_operand(uint4 c) {
+// This lane's loads of one pass: buffer resources and byte offsets at K position 0.
+struct QLoads {
+  __amdgpu_buffer_rsrc_t rx, rxs, rw;  // token-row codes, their scales, the expert record
+  uint32_t xo[8], xso, wo[4], wso;
+};
+
+// Load t (0..13) of stage st into the stage buffer at LDS byte address lb: token-row
+// codes of rows 64 w + 8 t .. +7 (t < 8), their scales (rows 64 w .. +63), weight
+// codes of columns 64 w + 16 (t - 9) .. +15, their scales (columns 64 w .. +63).
+__device__ __forceinline__ void q_issue(const QLoads& L, int t, int st, uint32_t lb, int wave) {
+  if (t < 8)
+    lds16(L.rx, L.xo[t], (uint32_t)st * QK, lb + (uint32_t)(8192 * wave + 1024 * t));
+  else if (t == 8)
+    lds4(L.rxs, L.xso, (uint32_t)st * 4, lb + (uint32_t)(QXS + 256 * wave));
+  else if (t < 13)
+    lds16(L.rw, L.wo[t - 9], (uint32_t)st * (QK / 2), lb + (uint32_t)(QWC + 4096 * wave + 1024 * (t - 9)));
+  else
+    lds4(L.rw, L.wso, (uint32_t)st * 4, lb + (uint32_t)(QWS + 256 * wave));
+}
+
+// Lane l of load t covers, for token-row codes, buffer row 64 w + 8 t + l/8 at physical
+// piece l%8, and for weight codes column 64 w + 16 u + l/4 at physical piece l%4; it
+// reads the logical piece stored there.
+__device__ __forceinline__ int q_xrow(int wave, int t, int lane) { return 64 * wave + 8 * t + (lane >> 3); }
+__device__ __forceinline__ int q_xpiece(int r, int lane) { return (lane & 7) ^ swz8(r); }
+__device__ __forceinline__ int q_wcol(int wave, int u, int lane) { return 64 * wave + 16 * u + (lane >> 2); }
+__device__ __forceinline__ int q_wpiece(int c, int lane) { return (lane & 3) ^ swz4(c); }
+
+__device__ __forceinline__ i32x4_t lds_piece(const uint8_t* row, int phys) {
+  return *reinterpret_cast<const i32x4_t*>(row + 16 * phys);
+}
+
+__device__ __forceinline__ v8i_t fp4_operand(i32x4_t c) {
   v8i_t r;
-  r[0] = (int)c.x; r[1] = (int)c.y; r[2] = (int)c.z; r[3] = (int)c.w;
+  r[0] = c.x; r[1] = c.y; r[2] = c.z; r[3] = c.w;
   r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
   return r;
 }
 
-// A operand of one row subtile for both MFMAs of a stage, and the row's 4 scale bytes.
+// A operand of row r for both MFMAs of a stage (lane group g: pieces 2i + g and
+// 2i + g + 4 for MFMA i), and the row's 4 scale bytes.
 struct QA {
   v8i_t f[2];
   uint32_t s;
 };
 
-__device__ __forceinline__ void load_qa(QA& q, const uint8_t* arow, const uint32_t* srow) {
+__device__ __forceinline__ void q_read_a(QA& q, const uint8_t* buf, int r, int g) {
+  const uint8_t* row = buf + 128 * r;
+  const int z = swz8(r);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(arow + 32 * i);
-    const uint4 hi = *reinterpret_cast<const uint4*>(arow + 32 * i + 64);
-    q.f[i][0] = (int)lo.x; q.f[i][1] = (int)lo.y; q.f[i][2] = (int)lo.z; q.f[i][3] = (int)lo.w;
-    q.f[i][4] = (int)hi.x; q.f[i][5] = (int)hi.y; q.f[i][6] = (int)hi.z; q.f[i][7] = (int)hi.w;
+    const i32x4_t lo = lds_piece(row, (2 * i + g) ^ z), hi = lds_piece(row, (2 * i + g + 4) ^ z);
+    q.f[i][0] = lo.x; q.f[i][1] = lo.y; q.f[i][2] = lo.z; q.f[i][3] = lo.w;
+    q.f[i][4] = hi.x; q.f[i][5] = hi.y; q.f[i][6] = hi.z; q.f[i][7] = hi.w;
   }
-  q.s = *srow;
+  q.s = *reinterpret_cast<const uint32_t*>(buf + QXS + 4 * r);
 }
 
-// acc[a][c] += A(subtile a) x B(column subtile c) over one 128-element stage.  q0
-// holds subtile 0's A operand on entry; subtile a + 1 is read from LDS while subtile a
-// multiplies, and during the last subtile the next stage's subtile 0 is read from
-// (sx_next, ss_next) into q0, so the MFMA pipe stays fed across the stage barrier.
-template <int NSUB>
-__device__ __forceinline__ void mx_mfma_stage(f32x16_t (&acc)[8][2], const QW& w, const uint8_t* sx,
-                                              const uint32_t* ss, const uint8_t* sx_next, const uint32_t* ss_next,
-                                              QA& q0, int lane) {
-  const int grp = lane >> 5;
-  const int aoff = (lane & 31) * QLD + 16 * grp;
-  const v8i_t b[4] = {fp4_operand(w.c[0]), fp4_operand(w.c[1]), fp4_operand(w.c[2]), fp4_operand(w.c[3])};
-  // lane group g passes the scales of stage blocks g*2 (MFMA 0) and g*2 + 1 (MFMA 1)
-  const int sh0 = 16 * grp, sh1 = 16 * grp + 8;
-  const int sb[4] = {(int)((w.s[0] >> sh0) & 0xff), (int)((w.s[0] >> sh1) & 0xff), (int)((w.s[1] >> sh0) & 0xff),
-                     (int)((w.s[1] >> sh1) & 0xff)};
-  QA q1;
-#pragma unroll
-  for (int a = 0; a < NSUB; ++a) {
-    QA& cur = (a & 1) ? q1 : q0;
-    QA& nxt = (a & 1) ? q0 : q1;
-    if (a + 1 < NSUB)
-      load_qa(nxt, sx + aoff + (a + 1) * 32 * QLD, ss + (lane & 31) + (a + 1) * 32);
-    else
-      load_qa(nxt, sx_next + aoff, ss_next + (lane & 31));
-    const int sa0 = (cur.s >> sh0) & 0xff, sa1 = (cur.s >> sh1) & 0xff;
-    acc[a][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.f[0], b[0], acc[a][0], 0, 4, 0, sa0, 0, sb[0]);
-    acc[a][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.f[0], b[2], acc[a][1], 0, 4, 0, sa0, 0, sb[2]);
-    acc[a][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.f[1], b[1], acc[a][0], 0, 4, 0, sa1, 0, sb[1]);
-    acc[a][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.f[1], b[3], acc[a][1], 0, 4, 0, sa1, 0, sb[3]);
+// Load t after the MFMA just written, pinned there: the scheduler would otherwise bunch
+// a stage's loads behind its first few MFMAs, where they queue in front of one another.
+template <typename F>
+__device__ __forceinline__ void q_issue_after(int t, F& issue) {
+  if (t < QLOADS) {
+    issue(t);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  if (NSUB & 1) q0 = q1;  // the next stage's subtile 0 landed in q1
 }
 
-constexpr int QBUF = QM * QLD;  // one LDS stage buffer of codes, bytes
-
-// K loop of one pass (K = kdim, a multiple of 128).  Weight pointers are this lane's
-// two rows (codes already offset by 16 * lane group, scales at the row start).
-// Token rows rotate through three LDS buffers: stage s computes from buffer s%3
-// while stage s+2's rows are stored into buffer (s+2)%3.
-template <int NSUB>
-__device__ __forceinline__ void mx_mfma_pass(f32x16_t (&acc)[8][2], QRowStage& rs, uint8_t* sx, uint32_t* ss,
-                                             const uint8_t* c0, const uint8_t* c1, const uint8_t* s0,
-                                             const uint8_t* s1, int kdim, int tid, int lane) {
+// acc[i][j] += A(row subtile i of this wave) x B(column subtile j of this wave) over
+// one stage; load t0 + n of a later stage goes out after the n-th MFMA (while there are
+// loads left).  The four column subtiles take K half 0, then K half 1, so that the two
+// MFMAs into one accumulator are four apart.
+template <typename F>
+__device__ __forceinline__ void q_mma(f32x16_t (&acc)[4][4], const QA& q, int i, const v8i_t (&b)[4][2],
+                                      const int (&sb)[4][2], int g, int t0, F& issue) {
+  const int sa[2] = {(int)((q.s >> (16 * g)) & 0xff), (int)((q.s >> (16 * g + 8)) & 0xff)};
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      acc[a][0][v] = 0.0f;
-      acc[a][1][v] = 0.0f;
+    for (int j = 0; j < 4; ++j) {
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(q.f[h], b[j][h], acc[i][j], 0, 4, 0, sa[h], 0,
+                                                                  sb[j][h]);
+      q_issue_after(t0 + 4 * h + j, issue);
     }
-  int opaque = 0;  // keeps the first weight loads inside the caller's row-pass loop
-  asm volatile("" : "+s"(opaque));
-  c0 += opaque;
-  c1 += opaque;
-  QW wr[QDEPTH];
+}
+
+// One stage held in `buf`.  The 4 waves form a 2 x 2 grid: wave w takes the row
+// subtiles w%2, w%2 + 2, ... (NA of them) and the B columns 128 (w/2) .. +127 (four
+// column subtiles), so each A piece read from LDS feeds 8 MFMAs and each B piece NA x 2.
+// The wave's B operands and scales first, then its row subtiles, subtile i + 1 read from
+// LDS while subtile i multiplies; `issue(t)` sends load t of a later stage.
+template <int NA, typename F>
+__device__ __forceinline__ void q_stage(f32x16_t (&acc)[4][4], const uint8_t* buf, int wave, int lane, F&& issue) {
+  const int m = lane & 31, g = lane >> 5, wr = wave & 1, wc = wave >> 1;
+  v8i_t b[4][2];
+  int sb[4][2];
 #pragma unroll
-  for (int j = 0; j < QDEPTH; ++j) load_qw(wr[j], c0, c1, s0, s1, j * QK);
-  const int klast = kdim - QK;
-  rs.load(0);
-  rs.store(sx, ss, tid);
-  rs.load(min(QK, klast));
-  rs.store(sx + QBUF, ss + QM, tid);
-  rs.load(min(2 * QK, klast));
-  __syncthreads();
-  QA q0;
-  load_qa(q0, sx + (lane & 31) * QLD + 16 * (lane >> 5), ss + (lane & 31));
-  int b = 0;  // LDS buffer of the current stage
-  for (int k0 = 0; k0 < kdim; k0 += QDEPTH * QK) {
+  for (int j = 0; j < 4; ++j) {
+    const int c = 128 * wc + 32 * j + m;
+    const uint8_t* col = buf + QWC + 64 * c;
+    const uint32_t s = *reinterpret_cast<const uint32_t*>(buf + QWS + 4 * c);
 #pragma unroll
-    for (int j = 0; j < QDEPTH; ++j) {
-      if (k0 + j * QK >= kdim) break;
-      const int b1 = b == 2 ? 0 : b + 1, b2 = b1 == 2 ? 0 : b1 + 1;
-      rs.store(sx + b2 * QBUF, ss + b2 * QM, tid);      // rows of stage s + 2
-      rs.load(min(k0 + (j + 3) * QK, klast));           // rows of stage s + 3
-      mx_mfma_stage<NSUB>(acc, wr[j], sx + b * QBUF, ss + b * QM, sx + b1 * QBUF, ss + b1 * QM, q0, lane);
-      load_qw(wr[j], c0, c1, s0, s1, min(k0 + (j + QDEPTH) * QK, klast));
-      // the stage's 15 global loads (9 row pieces, 6 weight pieces) one between each two
-      // MFMAs, so that their issue overlaps the MFMAs instead of queueing in front of them
-#pragma unroll
-      for (int i = 0; i < 15; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-      __syncthreads();
-      b = b1;
+    for (int h = 0; h < 2; ++h) {
+      b[j][h] = fp4_operand(lds_piece(col, (2 * g + h) ^ swz4(c)));
+      sb[j][h] = (int)((s >> (16 * g + 8 * h)) & 0xff);
     }
   }
+  QA q0, q1;
+  q_read_a(q0, buf, 32 * wr + m, g);
+#pragma unroll
+  for (int i = 0; i < NA; i += 2) {
+    if (i + 1 < NA) q_read_a(q1, buf, 32 * (2 * (i + 1) + wr) + m, g);
+    q_mma(acc, q0, i, b, sb, g, 8 * i, issue);
+    if (i + 1 < NA) {
+      if (i + 2 < NA) q_read_a(q0, buf, 32 * (2 * (i + 2) + wr) + m, g);
+      q_mma(acc, q1, i + 1, b, sb, g, 8 * i + 8, issue);
+    }
+  }
+#pragma unroll
+  for (int t = 8 * NA; t < QLOADS; ++t) issue(t);
 }
 
-__device__ __forceinline__ void mx_mfma_pass_n(int nsub, f32x16_t (&acc)[8][2], QRowStage& rs, uint8_t* sx,
-                                               uint32_t* ss, const uint8_t* c0, const uint8_t* c1, const uint8_t* s0,
-                                               const uint8_t* s1, int kdim, int tid, int lane) {
-  switch (nsub) {
-    case 1: mx_mfma_pass<1>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
-    case 2: mx_mfma_pass<2>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
-    case 3: mx_mfma_pass<3>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
-    case 4: mx_mfma_pass<4>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
-    case 5: mx_mfma_pass<5>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
-    case 6: mx_mfma_pass<6>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
-    case 7: mx_mfma_pass<7>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
-    default: mx_mfma_pass<8>(acc, rs, sx, ss, c0, c1, s0, s1, kdim, tid, lane); break;
+// K loop of one pass over nst stages.  Stage s waits for its own loads (issued two
+// stages earlier; only the 14 of stage s + 1 are younger), passes the barrier (every
+// wave's part has landed and stage s - 1, whose buffer the loads of stage s + 2 now
+// overwrite, is done), then multiplies.  Past the last stage the loads re-read it, so
+// that every stage issues the same 14.
+template <int NA>
+__device__ __forceinline__ void q_pass(f32x16_t (&acc)[4][4], const QLoads& L, const uint8_t* sq, uint32_t lds0,
+                                       int nst, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < QLOADS; ++t) q_issue(L, t, 0, lds0, wave);
+#pragma unroll
+  for (int t = 0; t < QLOADS; ++t) q_issue(L, t, min(1, nst - 1), lds0 + QSTAGE, wave);
+  int b = 0;
+  for (int st = 0; st < nst; ++st) {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(QLOADS) : "memory");
+    __syncthreads();
+    const int sn = min(st + 2, nst - 1);
+    const int bn = b == 0 ? 2 : b - 1;  // (st + 2) % 3
+    const uint32_t lbn = lds0 + (uint32_t)(bn * QSTAGE);
+    q_stage<NA>(acc, sq + b * QSTAGE, wave, lane, [&](int t) { q_issue(L, t, sn, lbn, wave); });
+    b = b == 2 ? 0 : b + 1;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // no load is left in flight and every wave is done with the buffers
+}
+
+// na = ceil(nsub / 2) row subtiles per wave; with an odd nsub the waves of the second
+// row take one subtile past the pass's rows (products never stored), which costs no
+// time: the two rows of waves run stage by stage together.
+__device__ __forceinline__ void q_pass_n(int na, f32x16_t (&acc)[4][4], const QLoads& L, const uint8_t* sq,
+                                         uint32_t lds0, int nst, int wave, int lane) {
+  switch (na) {
+    case 1: q_pass<1>(acc, L, sq, lds0, nst, wave, lane); break;
+    case 2: q_pass<2>(acc, L, sq, lds0, nst, wave, lane); break;
+    case 3: q_pass<3>(acc, L, sq, lds0, nst, wave, lane); break;
+    default: q_pass<4>(acc, L, sq, lds0, nst, wave, lane); break;
   }
 }
 
@@ -616,76 +650,95 @@ __device__ __forceinline__ uint32_t mx8_scale(float amax, float* inv) {
 // columns n0 + 32w .. +31 of both W_gate and W_up), written in MXFP8: codes hq
 // [rows, d_ff] and scales hs [rows, d_ff/32] (a wave's 32 columns are one block).
 __global__ __launch_bounds__(256) void mx_gateup_mfma_kernel(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int d, int d_ff, int k,
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int T, int d, int d_ff, int k,
     const uint8_t* __restrict__ slots, const int32_t* __restrict__ group_slot,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, int g_begin, int n_tiles, int n_blocks,
     uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
-  __shared__ __attribute__((aligned(16))) uint8_t sX[3 * QBUF];
-  __shared__ uint32_t sS[3 * QM];
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ[QNB * QSTAGE];
   const int lb = xcd_logical_block(blockIdx.x, n_blocks);
   const int g = g_begin + lb / n_tiles;
   const int n0 = (lb % n_tiles) * 128;
   const int r0 = offsets[g];
   const int n = offsets[g + 1] - r0;
   if (n <= 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const MxRec R = mx_rec(d, d_ff);
   const uint8_t* rec = slots + (size_t)group_slot[g] * R.bytes;
-  const int col = n0 + wave * 32 + (lane & 31);
-  const uint8_t* cg = rec + R.g_codes + (size_t)col * (d / 2) + 32 * grp;
-  const uint8_t* cu = rec + R.u_codes + (size_t)col * (d / 2) + 32 * grp;
-  const uint8_t* sg = rec + R.g_sc + (size_t)col * (d / 32);
-  const uint8_t* su = rec + R.u_sc + (size_t)col * (d / 32);
+  QLoads L;
+  L.rx = buf_rsrc(xq, (uint32_t)((size_t)T * d));
+  L.rxs = buf_rsrc(xs, (uint32_t)((size_t)T * (d / 32)));
+  L.rw = buf_rsrc(rec, (uint32_t)R.bytes);
+  // B column c (column subtile j = (c/32) % 4 of the waves 2 (c/128) + 0, 1): W_gate
+  // for even j, W_up for odd j, row n0 + 64 (c/128) + 32 (j/2) + c%32
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = q_wcol(wave, u, lane);
+    const size_t wrow = (size_t)(n0 + 64 * (c >> 7) + 32 * ((c >> 6) & 1) + (c & 31));
+    L.wo[u] = (uint32_t)(((c >> 5) & 1 ? R.u_codes : R.g_codes) + wrow * (d / 2) + q_wpiece(c, lane) * 16);
+  }
+  {
+    const int c = 64 * wave + lane;
+    const size_t wrow = (size_t)(n0 + 64 * (c >> 7) + 32 * ((c >> 6) & 1) + (c & 31));
+    L.wso = (uint32_t)(((c >> 5) & 1 ? R.u_sc : R.g_sc) + wrow * (d / 32));
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)sQ;
+  const int nst = d / QK;
   for (int m0 = 0; m0 < n; m0 += QM) {
     const int rows = min(QM, n - m0);
     const int nsub = (rows + 31) >> 5;
-    QRowStage rs;
+    // rows past the group's end load a valid row (their products land in rows never stored)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = min((tid >> 3) + 32 * j, rows - 1);
-      rs.src[j] = xq + (size_t)(perm[r0 + m0 + r] / k) * d + (tid & 7) * 16;
+    for (int t = 0; t < 8; ++t) {
+      const int r = q_xrow(wave, t, lane);
+      L.xo[t] = (uint32_t)((size_t)(perm[r0 + m0 + min(r, rows - 1)] / k) * d + q_xpiece(r, lane) * 16);
     }
-    rs.ssrc = xs + (size_t)(perm[r0 + m0 + min(tid, rows - 1)] / k) * (d / 32);
-    f32x16_t acc[8][2];
-    mx_mfma_pass_n(nsub, acc, rs, sX, sS, cg, cu, sg, su, d, tid, lane);
-    // MXFP8 conversion of h: each wave's 32 columns are one block of every row.  A
+    L.xso = (uint32_t)((size_t)(perm[r0 + m0 + min(64 * wave + lane, rows - 1)] / k) * (d / 32));
+    f32x16_t acc[4][4];
+    q_pass_n((nsub + 1) >> 1, acc, L, sQ, lds0, nst, wave, lane);
+    // MXFP8 conversion of h: column subtiles 2p (gate) and 2p + 1 (up) of a wave give
+    // h for the 32 output columns n0 + 64 (w/2) + 32 p, one block of every row.  A
     // 32 x 32 subtile goes through this wave's corner of LDS (the pass ended with a
     // barrier, so the staging buffers are free) so that each lane then holds 16
     // consecutive values of one row: lanes 2r and 2r+1 share row r's block.
-    float* tile = reinterpret_cast<float*>(sX) + wave * 32 * 36;
+    float* tile = reinterpret_cast<float*>(sQ) + wave * 32 * 36;
     int g4 = grp * 4;
     asm volatile("" : "+v"(g4));  // keeps the row indices below out of the prologue
-    const int tr = lane >> 1, th = lane & 1;
+    const int tr = lane >> 1, th = lane & 1, wr = wave & 1, wc = wave >> 1;
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      if (a >= nsub) continue;
+    for (int i = 0; i < 4; ++i) {
+      if (2 * i + wr >= nsub) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        tile[((v >> 2) * 8 + g4 + (v & 3)) * 36 + (lane & 31)] = silu_fast(acc[a][0][v]) * acc[a][1][v];
-      float hv[16];
+      for (int p = 0; p < 2; ++p) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 t4 = *reinterpret_cast<const float4*>(tile + tr * 36 + 16 * th + 4 * q);
-        hv[4 * q] = t4.x; hv[4 * q + 1] = t4.y; hv[4 * q + 2] = t4.z; hv[4 * q + 3] = t4.w;
-      }
-      float amax = 0.0f;
+        for (int v = 0; v < 16; ++v)
+          tile[((v >> 2) * 8 + g4 + (v & 3)) * 36 + (lane & 31)] = silu_fast(acc[i][2 * p][v]) * acc[i][2 * p + 1][v];
+        float hv[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) amax = fmaxf(amax, fabsf(hv[q]));
-      amax = fmaxf(amax, __shfl_xor(amax, 1, WAVE));
-      float inv;
-      const uint32_t sc = mx8_scale(amax, &inv);
-      uint32_t pk[4];
+        for (int q = 0; q < 4; ++q) {
+          const float4 t4 = *reinterpret_cast<const float4*>(tile + tr * 36 + 16 * th + 4 * q);
+          hv[4 * q] = t4.x; hv[4 * q + 1] = t4.y; hv[4 * q + 2] = t4.z; hv[4 * q + 3] = t4.w;
+        }
+        float amax = 0.0f;
 #pragma unroll
-      for (int w4 = 0; w4 < 4; ++w4) {
-        pk[w4] = 0u;
+        for (int q = 0; q < 16; ++q) amax = fmaxf(amax, fabsf(hv[q]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, WAVE));
+        float inv;
+        const uint32_t sc = mx8_scale(amax, &inv);
+        uint32_t pk[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pk[w4] |= (sc ? e4m3_code(hv[4 * w4 + j] * inv) : 0u) << (8 * j);
-      }
-      const int row = a * 32 + tr;
-      if (row < rows) {
-        const size_t gr = (size_t)(r0 + m0 + row);
-        *reinterpret_cast<uint4*>(hq + gr * d_ff + n0 + wave * 32 + 16 * th) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        if (th == 0) hs[gr * (d_ff / 32) + (n0 + wave * 32) / 32] = (uint8_t)sc;
+        for (int w4 = 0; w4 < 4; ++w4) {
+          pk[w4] = 0u;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pk[w4] |= (sc ? e4m3_code(hv[4 * w4 + j] * inv) : 0u) << (8 * j);
+        }
+        const int row = 32 * (2 * i + wr) + tr;
+        const int c0 = n0 + 64 * wc + 32 * p;
+        if (row < rows) {
+          const size_t gr = (size_t)(r0 + m0 + row);
+          *reinterpret_cast<uint4*>(hq + gr * d_ff + c0 + 16 * th) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+          if (th == 0) hs[gr * (d_ff / 32) + c0 / 32] = (uint8_t)sc;
+        }
       }
     }
     __syncthreads();  // the next row pass restages into the same LDS
@@ -695,49 +748,60 @@ __global__ __launch_bounds__(256) void mx_gateup_mfma_kernel(
 // out[i][c] = hq_i . Wd[c] for the 256 columns of this block's strip (wave w: columns
 // n0 + 64w .. +63), h in MXFP8 with rows in perm order.
 __global__ __launch_bounds__(256) void mx_down_mfma_kernel(
-    const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, int d, int d_ff,
+    const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, int n_rows, int d, int d_ff,
     const uint8_t* __restrict__ slots, const int32_t* __restrict__ group_slot,
     const int32_t* __restrict__ offsets, int g_begin, int n_tiles, int n_blocks, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t sX[3 * QBUF];
-  __shared__ uint32_t sS[3 * QM];
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ[QNB * QSTAGE];
   const int lb = xcd_logical_block(blockIdx.x, n_blocks);
   const int g = g_begin + lb / n_tiles;
   const int n0 = (lb % n_tiles) * 256;
   const int r0 = offsets[g];
   const int n = offsets[g + 1] - r0;
   if (n <= 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const MxRec R = mx_rec(d, d_ff);
   const uint8_t* rec = slots + (size_t)group_slot[g] * R.bytes;
-  const int col = n0 + wave * 64 + (lane & 31);
-  const uint8_t* c0 = rec + R.d_codes + (size_t)col * (d_ff / 2) + 32 * grp;
-  const uint8_t* c1 = c0 + (size_t)32 * (d_ff / 2);
-  const uint8_t* s0 = rec + R.d_sc + (size_t)col * (d_ff / 32);
-  const uint8_t* s1 = s0 + (size_t)32 * (d_ff / 32);
+  QLoads L;
+  L.rx = buf_rsrc(hq, (uint32_t)((size_t)n_rows * d_ff));
+  L.rxs = buf_rsrc(hs, (uint32_t)((size_t)n_rows * (d_ff / 32)));
+  L.rw = buf_rsrc(rec, (uint32_t)R.bytes);
+  // B column c is output column n0 + c
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = q_wcol(wave, u, lane);
+    L.wo[u] = (uint32_t)(R.d_codes + (size_t)(n0 + c) * (d_ff / 2) + q_wpiece(c, lane) * 16);
+  }
+  L.wso = (uint32_t)(R.d_sc + (size_t)(n0 + 64 * wave + lane) * (d_ff / 32));
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)sQ;
+  const int nst = d_ff / QK;
+  const int col = n0 + 128 * (wave >> 1) + (lane & 31);  // column subtile j: col + 32 j
   for (int m0 = 0; m0 < n; m0 += QM) {
     const int rows = min(QM, n - m0);
     const int nsub = (rows + 31) >> 5;
-    QRowStage rs;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = min((tid >> 3) + 32 * j, rows - 1);
-      rs.src[j] = hq + (size_t)(r0 + m0 + r) * d_ff + (tid & 7) * 16;
+    for (int t = 0; t < 8; ++t) {
+      const int r = q_xrow(wave, t, lane);
+      L.xo[t] = (uint32_t)((size_t)(r0 + m0 + min(r, rows - 1)) * d_ff + q_xpiece(r, lane) * 16);
     }
-    rs.ssrc = hs + (size_t)(r0 + m0 + min(tid, rows - 1)) * (d_ff / 32);
-    f32x16_t acc[8][2];
-    mx_mfma_pass_n(nsub, acc, rs, sX, sS, c0, c1, s0, s1, d_ff, tid, lane);
+    L.xso = (uint32_t)((size_t)(r0 + m0 + min(64 * wave + lane, rows - 1)) * (d_ff / 32));
+    f32x16_t acc[4][4];
+    q_pass_n((nsub + 1) >> 1, acc, L, sQ, lds0, nst, wave, lane);
     int g4 = grp * 4;
     asm volatile("" : "+v"(g4));
+    const int wr = wave & 1;
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      if (a >= nsub) continue;
+    for (int i = 0; i < 4; ++i) {
+      if (2 * i + wr >= nsub) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = a * 32 + (v >> 2) * 8 + g4 + (v & 3);
+        const int row = 32 * (2 * i + wr) + (v >> 2) * 8 + g4 + (v & 3);
         if (row < rows) {
           float* o = out + (size_t)(r0 + m0 + row) * d + col;
-          o[0] = acc[a][0][v];
-          o[32] = acc[a][1][v];
+          o[0] = acc[i][0][v];
+          o[32] = acc[i][1][v];
+          o[64] = acc[i][2][v];
+          o[96] = acc[i][3][v];
         }
       }
     }
@@ -858,14 +922,17 @@ int launch_mx_ffn_mfma(const uint16_t* x, int T, int d, int d_ff, int k, const u
   if (!aligned16(x) || !aligned16(slots) || !aligned16(xq) || !aligned16(hq) || !aligned16(out) ||
       ((reinterpret_cast<uintptr_t>(xs) | reinterpret_cast<uintptr_t>(hs)) & 3u))
     return fail(FT_EINVAL, "mx_ffn_mfma: unaligned pointer");
+  if ((size_t)T * d >= (1u << 31) || (size_t)n_rows * d_ff >= (1u << 31) || mx_rec(d, d_ff).bytes >= (1u << 31))
+    return fail(FT_EINVAL, "mx_ffn_mfma: activations or a record over 2 GiB");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (int rc = launch_mx_quant_bf16(x, T, d, xq, xs, s)) return rc;
   const int tiles_up = d_ff / 128, nb_up = ng * tiles_up;
-  timed_launch(mx_gateup_mfma_kernel, dim3(nb_up), dim3(256), s, ev, 0, (const uint8_t*)xq, (const uint8_t*)xs, d,
-               d_ff, k, slots, group_slot, offsets, perm, g_begin, tiles_up, nb_up, hq, hs);
+  timed_launch(mx_gateup_mfma_kernel, dim3(nb_up), dim3(256), s, ev, 0, (const uint8_t*)xq, (const uint8_t*)xs, T,
+               d, d_ff, k, slots, group_slot, offsets, perm, g_begin, tiles_up, nb_up, hq, hs);
   if (int rc = launched("mx_gateup_mfma")) return rc;
   const int tiles_dn = d / 256, nb_dn = ng * tiles_dn;
-  timed_launch(mx_down_mfma_kernel, dim3(nb_dn), dim3(256), s, ev, 1, (const uint8_t*)hq, (const uint8_t*)hs, d, d_ff,
+  timed_launch(mx_down_mfma_kernel, dim3(nb_dn), dim3(256), s, ev, 1, (const uint8_t*)hq, (const uint8_t*)hs, n_rows,
+               d, d_ff,
                slots, group_slot, offsets, g_begin, tiles_dn, nb_dn, out);
   return launched("mx_down_mfma");
 }
