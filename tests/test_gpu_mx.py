@@ -124,6 +124,8 @@ def test_mx_grouped_ffn_rows_form(d, d_ff, rows, split):
     (256, 512, [40, 1, 300, 77, 0]),    # more rows than one tile, a single row, an empty group
     (512, 384, [257, 3]),
     (4096, 2048, [96, 260]),            # prefill shape
+    (256, 128, [40, 300, 5]),           # one-stage down items, two-stage gate/up items
+    (512, 1024, [(37 * i) % 300 for i in range(40)]),  # more blocks than compute units
 ])
 def test_mx_grouped_ffn_mfma_form(d, d_ff, rows):
     _mx_ffn_case(2, d, d_ff, rows)
