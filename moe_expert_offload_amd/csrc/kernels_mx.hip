@@ -522,23 +522,29 @@ __device__ __forceinline__ void q_read_a(QA& q, const uint8_t* buf, int r, int g
   q.s = *reinterpret_cast<const uint32_t*>(buf + QXS + 4 * r);
 }
 
-// Load t after the MFMA just written, pinned there: the scheduler would otherwise bunch
-// a stage's loads behind its first few MFMAs, where they queue in front of one another.
+// After MFMA mi of the nm of a stage, the loads t with t nm / 14 == mi, pinned there:
+// the stage's 14 loads spread evenly over its MFMAs.  The 56 loads of a block's stage
+// occupy the compute unit's address unit for about as long as the MFMAs run; bunched,
+// they back up and stall the issuing wave, MFMAs included (the scheduler would bunch
+// them behind the first few MFMAs).
 template <typename F>
-__device__ __forceinline__ void q_issue_after(int t, F& issue) {
-  if (t < QLOADS) {
-    issue(t);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+__device__ __forceinline__ void q_issue_at(int mi, int nm, F& issue) {
+  bool any = false;
+#pragma unroll
+  for (int t = 0; t < QLOADS; ++t)
+    if (t * nm / QLOADS == mi) {
+      issue(t);
+      any = true;
+    }
+  if (any) __builtin_amdgcn_sched_barrier(0);
 }
 
 // acc[i][j] += A(row subtile i of this wave) x B(column subtile j of this wave) over
-// one stage; load t0 + n of a later stage goes out after the n-th MFMA (while there are
-// loads left).  The four column subtiles take K half 0, then K half 1, so that the two
-// MFMAs into one accumulator are four apart.
+// one stage, as MFMAs m0 .. m0 + 7 of the stage's nm.  The four column subtiles take K
+// half 0, then K half 1, so that the two MFMAs into one accumulator are four apart.
 template <typename F>
 __device__ __forceinline__ void q_mma(f32x16_t (&acc)[4][4], const QA& q, int i, const v8i_t (&b)[4][2],
-                                      const int (&sb)[4][2], int g, int t0, F& issue) {
+                                      const int (&sb)[4][2], int g, int m0, int nm, F& issue) {
   const int sa[2] = {(int)((q.s >> (16 * g)) & 0xff), (int)((q.s >> (16 * g + 8)) & 0xff)};
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -546,7 +552,7 @@ __device__ __forceinline__ void q_mma(f32x16_t (&acc)[4][4], const QA& q, int i,
     for (int j = 0; j < 4; ++j) {
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(q.f[h], b[j][h], acc[i][j], 0, 4, 0, sa[h], 0,
                                                                   sb[j][h]);
-      q_issue_after(t0 + 4 * h + j, issue);
+      q_issue_at(m0 + 4 * h + j, nm, issue);
     }
 }
 
@@ -576,14 +582,12 @@ __device__ __forceinline__ void q_stage(f32x16_t (&acc)[4][4], const uint8_t* bu
 #pragma unroll
   for (int i = 0; i < NA; i += 2) {
     if (i + 1 < NA) q_read_a(q1, buf, 32 * (2 * (i + 1) + wr) + m, g);
-    q_mma(acc, q0, i, b, sb, g, 8 * i, issue);
+    q_mma(acc, q0, i, b, sb, g, 8 * i, 8 * NA, issue);
     if (i + 1 < NA) {
       if (i + 2 < NA) q_read_a(q0, buf, 32 * (2 * (i + 2) + wr) + m, g);
-      q_mma(acc, q1, i + 1, b, sb, g, 8 * i + 8, issue);
+      q_mma(acc, q1, i + 1, b, sb, g, 8 * i + 8, 8 * NA, issue);
     }
   }
-#pragma unroll
-  for (int t = 8 * NA; t < QLOADS; ++t) issue(t);
 }
 
 // K loop of one pass over nst stages.  Stage s waits for its own loads (issued two
