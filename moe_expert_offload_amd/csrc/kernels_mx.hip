@@ -411,8 +411,8 @@ __global__ __launch_bounds__(256) void mx_quant_act_kernel(const In* __restrict_
 
 // ---- scaled-MFMA grouped FFN ---------------------------------------------------------
 // Block: 256 threads = 4 waves, one per SIMD.  One pass covers up to 256 rows of one
-// expert (8 row subtiles of 32) and 256 weight rows ("B columns"), 64 per wave, so
-// every weight byte is read from HBM once per pass.  K runs in stages of 128 elements
+// expert (8 row subtiles of 32) and 256 weight rows ("B columns"), so every weight
+// byte is read from HBM once per pass; the waves split them 2 x 2 (see q_stage).  K runs in stages of 128 elements
 // = two scaled MFMAs per row subtile and column subtile.  MFMA i (0, 1) of a stage
 // takes as its K positions 0..31 the stage's block i and as positions 32..63 its
 // block i + 2 (any pairing is exact as long as both operands and both scales follow
@@ -420,11 +420,10 @@ __global__ __launch_bounds__(256) void mx_quant_act_kernel(const In* __restrict_
 //
 // All four operand streams of a stage (token-row codes and scales, weight codes and
 // scales) go straight from memory into one LDS stage buffer (`buffer_load ... lds`,
-// no registers in between), two stages ahead, through three buffers of 50 KB.  A wave
-// loads 64 of the token rows (shared by the 4 waves behind the stage barrier) and its
-// own 64 weight rows: 14 loads per wave per stage, one after each of the stage's first
-// MFMAs, waited for by one explicit `s_waitcnt vmcnt` at the top of the stage they
-// feed.  (Loads into registers leave the waits to the compiler, which drains every
+// no registers in between), two stages ahead, through three buffers of 50 KB.  Wave w
+// loads token rows 64 w .. +63 and B columns 64 w .. +63 (all shared behind the stage
+// barrier): 14 loads per wave per stage, spread over the stage's MFMAs, waited for by
+// one explicit `s_waitcnt vmcnt` at the top of the stage they feed.  (Loads into registers leave the waits to the compiler, which drains every
 // load at the head of the K loop: the memory latency then lands on every few stages.)
 //
 // Stage buffer (bytes): token-row codes, row r at 128 r with 16-byte piece p at
