@@ -113,6 +113,7 @@ def _mx_ffn_case(form, d, d_ff, rows, k=2, split=None, seed=0):
     (256, 512, [1, 3, 0, 2, 8], None),
     (2048, 768, [1] * 6, 2),            # decode shape, hits then fills
     (4096, 2048, [1, 2], None),         # the MXFP4 decode shape
+    (4096, 2048, [1, 1, 1], 1),         # the same at one token per group
     (384, 128, [9, 1], None),
     (256, 4096, [6, 1], None),          # d_ff = 4096: h staged in LDS 4 rows at a time
 ])
