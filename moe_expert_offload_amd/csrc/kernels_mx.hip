@@ -410,9 +410,9 @@ __global__ __launch_bounds__(256) void mx_quant_act_kernel(const In* __restrict_
 }
 
 // ---- scaled-MFMA grouped FFN ---------------------------------------------------------
-// Block: 256 threads = 4 waves, one per SIMD.  One pass covers up to 256 rows of one
+// Block: 512 threads = 8 waves, two per SIMD.  One pass covers up to 256 rows of one
 // expert (8 row subtiles of 32) and 256 weight rows ("B columns"), so every weight
-// byte is read from HBM once per pass; the waves split them 2 x 2 (see q_stage).  K runs in stages of 128 elements
+// byte is read from HBM once per pass; the waves split them 4 x 2 (see q_stage).  K runs in stages of 128 elements
 // = two scaled MFMAs per row subtile and column subtile.  MFMA i (0, 1) of a stage
 // takes as its K positions 0..31 the stage's block i and as positions 32..63 its
 // block i + 2 (any pairing is exact as long as both operands and both scales follow
@@ -421,9 +421,11 @@ __global__ __launch_bounds__(256) void mx_quant_act_kernel(const In* __restrict_
 // All four operand streams of a stage (token-row codes and scales, weight codes and
 // scales) go straight from memory into one LDS stage buffer (`buffer_load ... lds`,
 // no registers in between), two stages ahead, through three buffers of 50 KB.  Wave w
-// loads token rows 64 w .. +63 and B columns 64 w .. +63 (all shared behind the stage
-// barrier): 14 loads per wave per stage, spread over the stage's MFMAs, waited for by
-// one explicit `s_waitcnt vmcnt` at the top of the stage they feed.  (Loads into registers leave the waits to the compiler, which drains every
+// loads token rows 32 w .. +31 and B columns 32 w .. +31, and the scales of 64 token
+// rows (waves 0-3) or 64 B columns (waves 4-7), all shared behind the stage barrier: 7
+// loads per wave per stage, spread over the stage's MFMAs, waited for by one explicit
+// `s_waitcnt vmcnt` at the top of the stage they feed.  With two waves per SIMD, one
+// wave's MFMAs run while the other waits on the issue of its loads.  (Loads into registers leave the waits to the compiler, which drains every
 // load at the head of the K loop: the memory latency then lands on every few stages.)
 //
 // Stage buffer (bytes): token-row codes, row r at 128 r with 16-byte piece p at
@@ -438,7 +440,8 @@ constexpr int QWC = QXS + QM * 4;          // offset of the weight codes
 constexpr int QWS = QWC + 256 * (QK / 2);  // offset of the weight scales
 constexpr int QSTAGE = QWS + 256 * 4;      // one stage buffer: 51200 bytes
 constexpr int QNB = 3;                     // stage buffers
-constexpr int QLOADS = 14;                 // loads per wave per stage
+constexpr int QWAVES = 8;                  // waves per block, two per SIMD
+constexpr int QLOADS = 7;                  // loads per wave per stage
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -466,29 +469,30 @@ __device__ __forceinline__ void lds4(__amdgpu_buffer_rsrc_t rs, uint32_t off, ui
 // This lane's loads of one pass: buffer resources and byte offsets at K position 0.
 struct QLoads {
   __amdgpu_buffer_rsrc_t rx, rxs, rw;  // token-row codes, their scales, the expert record
-  uint32_t xo[8], xso, wo[4], wso;
+  uint32_t xo[4], wo[2], so;           // so: token-row scales (waves 0-3) or weight scales (4-7)
 };
 
-// Load t (0..13) of stage st into the stage buffer at LDS byte address lb: token-row
-// codes of rows 64 w + 8 t .. +7 (t < 8), their scales (rows 64 w .. +63), weight
-// codes of columns 64 w + 16 (t - 9) .. +15, their scales (columns 64 w .. +63).
+// Load t (0..6) of stage st into the stage buffer at LDS byte address lb: token-row
+// codes of rows 32 w + 8 t .. +7 (t < 4), weight codes of columns 32 w + 16 (t - 4)
+// .. +15 (t = 4, 5), and the scales of token rows 64 w .. +63 (waves 0-3) or of weight
+// columns 64 (w - 4) .. +63 (waves 4-7).
 __device__ __forceinline__ void q_issue(const QLoads& L, int t, int st, uint32_t lb, int wave) {
-  if (t < 8)
-    lds16(L.rx, L.xo[t], (uint32_t)st * QK, lb + (uint32_t)(8192 * wave + 1024 * t));
-  else if (t == 8)
-    lds4(L.rxs, L.xso, (uint32_t)st * 4, lb + (uint32_t)(QXS + 256 * wave));
-  else if (t < 13)
-    lds16(L.rw, L.wo[t - 9], (uint32_t)st * (QK / 2), lb + (uint32_t)(QWC + 4096 * wave + 1024 * (t - 9)));
+  if (t < 4)
+    lds16(L.rx, L.xo[t], (uint32_t)st * QK, lb + (uint32_t)(4096 * wave + 1024 * t));
+  else if (t < 6)
+    lds16(L.rw, L.wo[t - 4], (uint32_t)st * (QK / 2), lb + (uint32_t)(QWC + 2048 * wave + 1024 * (t - 4)));
+  else if (wave < 4)
+    lds4(L.rxs, L.so, (uint32_t)st * 4, lb + (uint32_t)(QXS + 256 * wave));
   else
-    lds4(L.rw, L.wso, (uint32_t)st * 4, lb + (uint32_t)(QWS + 256 * wave));
+    lds4(L.rw, L.so, (uint32_t)st * 4, lb + (uint32_t)(QWS + 256 * (wave - 4)));
 }
 
-// Lane l of load t covers, for token-row codes, buffer row 64 w + 8 t + l/8 at physical
-// piece l%8, and for weight codes column 64 w + 16 u + l/4 at physical piece l%4; it
+// Lane l of load t covers, for token-row codes, buffer row 32 w + 8 t + l/8 at physical
+// piece l%8, and for weight codes column 32 w + 16 u + l/4 at physical piece l%4; it
 // reads the logical piece stored there.
-__device__ __forceinline__ int q_xrow(int wave, int t, int lane) { return 64 * wave + 8 * t + (lane >> 3); }
+__device__ __forceinline__ int q_xrow(int wave, int t, int lane) { return 32 * wave + 8 * t + (lane >> 3); }
 __device__ __forceinline__ int q_xpiece(int r, int lane) { return (lane & 7) ^ swz8(r); }
-__device__ __forceinline__ int q_wcol(int wave, int u, int lane) { return 64 * wave + 16 * u + (lane >> 2); }
+__device__ __forceinline__ int q_wcol(int wave, int u, int lane) { return 32 * wave + 16 * u + (lane >> 2); }
 __device__ __forceinline__ int q_wpiece(int c, int lane) { return (lane & 3) ^ swz4(c); }
 
 __device__ __forceinline__ i32x4_t lds_piece(const uint8_t* row, int phys) {
@@ -521,8 +525,8 @@ __device__ __forceinline__ void q_read_a(QA& q, const uint8_t* buf, int r, int g
   q.s = *reinterpret_cast<const uint32_t*>(buf + QXS + 4 * r);
 }
 
-// After MFMA mi of the nm of a stage, the loads t with t nm / 14 == mi, pinned there:
-// the stage's 14 loads spread evenly over its MFMAs.  The 56 loads of a block's stage
+// After MFMA mi of the nm of a stage, the loads t with t nm / 7 == mi, pinned there:
+// the wave's 7 loads spread evenly over its MFMAs.  The 56 loads of a block's stage
 // occupy the compute unit's address unit for about as long as the MFMAs run; bunched,
 // they back up and stall the issuing wave, MFMAs included (the scheduler would bunch
 // them behind the first few MFMAs).
@@ -542,7 +546,7 @@ __device__ __forceinline__ void q_issue_at(int mi, int nm, F& issue) {
 // one stage, as MFMAs m0 .. m0 + 7 of the stage's nm.  The four column subtiles take K
 // half 0, then K half 1, so that the two MFMAs into one accumulator are four apart.
 template <typename F>
-__device__ __forceinline__ void q_mma(f32x16_t (&acc)[4][4], const QA& q, int i, const v8i_t (&b)[4][2],
+__device__ __forceinline__ void q_mma(f32x16_t (&acc)[2][4], const QA& q, int i, const v8i_t (&b)[4][2],
                                       const int (&sb)[4][2], int g, int m0, int nm, F& issue) {
   const int sa[2] = {(int)((q.s >> (16 * g)) & 0xff), (int)((q.s >> (16 * g + 8)) & 0xff)};
 #pragma unroll
@@ -555,14 +559,21 @@ __device__ __forceinline__ void q_mma(f32x16_t (&acc)[4][4], const QA& q, int i,
     }
 }
 
-// One stage held in `buf`.  The 4 waves form a 2 x 2 grid: wave w takes the row
-// subtiles w%2, w%2 + 2, ... (NA of them) and the B columns 128 (w/2) .. +127 (four
-// column subtiles), so each A piece read from LDS feeds 8 MFMAs and each B piece NA x 2.
-// The wave's B operands and scales first, then its row subtiles, subtile i + 1 read from
-// LDS while subtile i multiplies; `issue(t)` sends load t of a later stage.
+// One stage held in `buf`.  The 8 waves form a 4 x 2 grid: wave w takes the row
+// subtiles w/2, w/2 + 4 (NA of them, 0 to 2) and the B columns 128 (w%2) .. +127 (four
+// column subtiles).  The two waves of a SIMD (w and w + 4) then hold row subtiles
+// {q, q + 2, q + 4, q + 6} (q = w%4 / 2) between them, as even a split of the pass's
+// rows over the SIMDs as 32-row subtiles allow.  The wave's B operands and scales first,
+// then its row subtiles, subtile i + 1 read from LDS while subtile i multiplies;
+// `issue(t)` sends load t of a later stage.
 template <int NA, typename F>
-__device__ __forceinline__ void q_stage(f32x16_t (&acc)[4][4], const uint8_t* buf, int wave, int lane, F&& issue) {
-  const int m = lane & 31, g = lane >> 5, wr = wave & 1, wc = wave >> 1;
+__device__ __forceinline__ void q_stage(f32x16_t (&acc)[2][4], const uint8_t* buf, int wave, int lane, F&& issue) {
+  if (NA == 0) {
+#pragma unroll
+    for (int t = 0; t < QLOADS; ++t) issue(t);
+    return;
+  }
+  const int m = lane & 31, g = lane >> 5, wr = wave >> 1, wc = wave & 1;
   v8i_t b[4][2];
   int sb[4][2];
 #pragma unroll
@@ -578,27 +589,21 @@ __device__ __forceinline__ void q_stage(f32x16_t (&acc)[4][4], const uint8_t* bu
   }
   QA q0, q1;
   q_read_a(q0, buf, 32 * wr + m, g);
-#pragma unroll
-  for (int i = 0; i < NA; i += 2) {
-    if (i + 1 < NA) q_read_a(q1, buf, 32 * (2 * (i + 1) + wr) + m, g);
-    q_mma(acc, q0, i, b, sb, g, 8 * i, 8 * NA, issue);
-    if (i + 1 < NA) {
-      if (i + 2 < NA) q_read_a(q0, buf, 32 * (2 * (i + 2) + wr) + m, g);
-      q_mma(acc, q1, i + 1, b, sb, g, 8 * i + 8, 8 * NA, issue);
-    }
-  }
+  if (NA > 1) q_read_a(q1, buf, 32 * (wr + 4) + m, g);
+  q_mma(acc, q0, 0, b, sb, g, 0, 8 * NA, issue);
+  if (NA > 1) q_mma(acc, q1, 1, b, sb, g, 8, 8 * NA, issue);
 }
 
 // K loop of one pass over nst stages.  Stage s waits for its own loads (issued two
-// stages earlier; only the 14 of stage s + 1 are younger), passes the barrier (every
+// stages earlier; only the 7 of stage s + 1 are younger), passes the barrier (every
 // wave's part has landed and stage s - 1, whose buffer the loads of stage s + 2 now
 // overwrite, is done), then multiplies.  Past the last stage the loads re-read it, so
-// that every stage issues the same 14.
+// that every stage issues the same 7.
 template <int NA>
-__device__ __forceinline__ void q_pass(f32x16_t (&acc)[4][4], const QLoads& L, const uint8_t* sq, uint32_t lds0,
+__device__ __forceinline__ void q_pass(f32x16_t (&acc)[2][4], const QLoads& L, const uint8_t* sq, uint32_t lds0,
                                        int nst, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -621,17 +626,20 @@ __device__ __forceinline__ void q_pass(f32x16_t (&acc)[4][4], const QLoads& L, c
   __syncthreads();  // no load is left in flight and every wave is done with the buffers
 }
 
-// na = ceil(nsub / 2) row subtiles per wave; with an odd nsub the waves of the second
-// row take one subtile past the pass's rows (products never stored), which costs no
-// time: the two rows of waves run stage by stage together.
-__device__ __forceinline__ void q_pass_n(int na, f32x16_t (&acc)[4][4], const QLoads& L, const uint8_t* sq,
+// na: row subtiles of this wave (0, 1 or 2; see q_stage).
+__device__ __forceinline__ void q_pass_n(int na, f32x16_t (&acc)[2][4], const QLoads& L, const uint8_t* sq,
                                          uint32_t lds0, int nst, int wave, int lane) {
   switch (na) {
+    case 0: q_pass<0>(acc, L, sq, lds0, nst, wave, lane); break;
     case 1: q_pass<1>(acc, L, sq, lds0, nst, wave, lane); break;
-    case 2: q_pass<2>(acc, L, sq, lds0, nst, wave, lane); break;
-    case 3: q_pass<3>(acc, L, sq, lds0, nst, wave, lane); break;
-    default: q_pass<4>(acc, L, sq, lds0, nst, wave, lane); break;
+    default: q_pass<2>(acc, L, sq, lds0, nst, wave, lane); break;
   }
+}
+
+// Row subtiles of wave w for a pass of nsub: those of w/2 and w/2 + 4 below nsub.
+__device__ __forceinline__ int q_na(int nsub, int wave) {
+  const int wr = wave >> 1;
+  return (wr < nsub ? 1 : 0) + (wr + 4 < nsub ? 1 : 0);
 }
 
 // E8M0 scale code of a block with maximum magnitude amax, and 2^-e to multiply its
@@ -652,7 +660,7 @@ __device__ __forceinline__ uint32_t mx8_scale(float amax, float* inv) {
 // h = silu(x Wg^T) * (x Wu^T) for the 128 columns of this block's strip (wave w:
 // columns n0 + 32w .. +31 of both W_gate and W_up), written in MXFP8: codes hq
 // [rows, d_ff] and scales hs [rows, d_ff/32] (a wave's 32 columns are one block).
-__global__ __launch_bounds__(256) void mx_gateup_mfma_kernel(
+__global__ __launch_bounds__(512) void mx_gateup_mfma_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int T, int d, int d_ff, int k,
     const uint8_t* __restrict__ slots, const int32_t* __restrict__ group_slot,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, int g_begin, int n_tiles, int n_blocks,
@@ -672,18 +680,18 @@ __global__ __launch_bounds__(256) void mx_gateup_mfma_kernel(
   L.rx = buf_rsrc(xq, (uint32_t)((size_t)T * d));
   L.rxs = buf_rsrc(xs, (uint32_t)((size_t)T * (d / 32)));
   L.rw = buf_rsrc(rec, (uint32_t)R.bytes);
-  // B column c (column subtile j = (c/32) % 4 of the waves 2 (c/128) + 0, 1): W_gate
+  // B column c (column subtile j = (c/32) % 4 of the waves with w%2 = c/128): W_gate
   // for even j, W_up for odd j, row n0 + 64 (c/128) + 32 (j/2) + c%32
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < 2; ++u) {
     const int c = q_wcol(wave, u, lane);
     const size_t wrow = (size_t)(n0 + 64 * (c >> 7) + 32 * ((c >> 6) & 1) + (c & 31));
     L.wo[u] = (uint32_t)(((c >> 5) & 1 ? R.u_codes : R.g_codes) + wrow * (d / 2) + q_wpiece(c, lane) * 16);
   }
-  {
-    const int c = 64 * wave + lane;
+  if (wave >= 4) {
+    const int c = 64 * (wave - 4) + lane;
     const size_t wrow = (size_t)(n0 + 64 * (c >> 7) + 32 * ((c >> 6) & 1) + (c & 31));
-    L.wso = (uint32_t)(((c >> 5) & 1 ? R.u_sc : R.g_sc) + wrow * (d / 32));
+    L.so = (uint32_t)(((c >> 5) & 1 ? R.u_sc : R.g_sc) + wrow * (d / 32));
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)sQ;
   const int nst = d / QK;
@@ -692,25 +700,25 @@ __global__ __launch_bounds__(256) void mx_gateup_mfma_kernel(
     const int nsub = (rows + 31) >> 5;
     // rows past the group's end load a valid row (their products land in rows never stored)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 4; ++t) {
       const int r = q_xrow(wave, t, lane);
       L.xo[t] = (uint32_t)((size_t)(perm[r0 + m0 + min(r, rows - 1)] / k) * d + q_xpiece(r, lane) * 16);
     }
-    L.xso = (uint32_t)((size_t)(perm[r0 + m0 + min(64 * wave + lane, rows - 1)] / k) * (d / 32));
-    f32x16_t acc[4][4];
-    q_pass_n((nsub + 1) >> 1, acc, L, sQ, lds0, nst, wave, lane);
+    if (wave < 4) L.so = (uint32_t)((size_t)(perm[r0 + m0 + min(64 * wave + lane, rows - 1)] / k) * (d / 32));
+    f32x16_t acc[2][4];
+    q_pass_n(q_na(nsub, wave), acc, L, sQ, lds0, nst, wave, lane);
     // MXFP8 conversion of h: column subtiles 2p (gate) and 2p + 1 (up) of a wave give
-    // h for the 32 output columns n0 + 64 (w/2) + 32 p, one block of every row.  A
+    // h for the 32 output columns n0 + 64 (w%2) + 32 p, one block of every row.  A
     // 32 x 32 subtile goes through this wave's corner of LDS (the pass ended with a
     // barrier, so the staging buffers are free) so that each lane then holds 16
     // consecutive values of one row: lanes 2r and 2r+1 share row r's block.
     float* tile = reinterpret_cast<float*>(sQ) + wave * 32 * 36;
     int g4 = grp * 4;
     asm volatile("" : "+v"(g4));  // keeps the row indices below out of the prologue
-    const int tr = lane >> 1, th = lane & 1, wr = wave & 1, wc = wave >> 1;
+    const int tr = lane >> 1, th = lane & 1, wr = wave >> 1, wc = wave & 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (2 * i + wr >= nsub) continue;
+    for (int i = 0; i < 2; ++i) {
+      if (wr + 4 * i >= nsub) continue;
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
 #pragma unroll
@@ -735,7 +743,7 @@ __global__ __launch_bounds__(256) void mx_gateup_mfma_kernel(
 #pragma unroll
           for (int j = 0; j < 4; ++j) pk[w4] |= (sc ? e4m3_code(hv[4 * w4 + j] * inv) : 0u) << (8 * j);
         }
-        const int row = 32 * (2 * i + wr) + tr;
+        const int row = 32 * (wr + 4 * i) + tr;
         const int c0 = n0 + 64 * wc + 32 * p;
         if (row < rows) {
           const size_t gr = (size_t)(r0 + m0 + row);
@@ -750,7 +758,7 @@ __global__ __launch_bounds__(256) void mx_gateup_mfma_kernel(
 
 // out[i][c] = hq_i . Wd[c] for the 256 columns of this block's strip (wave w: columns
 // n0 + 64w .. +63), h in MXFP8 with rows in perm order.
-__global__ __launch_bounds__(256) void mx_down_mfma_kernel(
+__global__ __launch_bounds__(512) void mx_down_mfma_kernel(
     const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs, int n_rows, int d, int d_ff,
     const uint8_t* __restrict__ slots, const int32_t* __restrict__ group_slot,
     const int32_t* __restrict__ offsets, int g_begin, int n_tiles, int n_blocks, float* __restrict__ out) {
@@ -771,34 +779,34 @@ __global__ __launch_bounds__(256) void mx_down_mfma_kernel(
   L.rw = buf_rsrc(rec, (uint32_t)R.bytes);
   // B column c is output column n0 + c
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < 2; ++u) {
     const int c = q_wcol(wave, u, lane);
     L.wo[u] = (uint32_t)(R.d_codes + (size_t)(n0 + c) * (d_ff / 2) + q_wpiece(c, lane) * 16);
   }
-  L.wso = (uint32_t)(R.d_sc + (size_t)(n0 + 64 * wave + lane) * (d_ff / 32));
+  if (wave >= 4) L.so = (uint32_t)(R.d_sc + (size_t)(n0 + 64 * (wave - 4) + lane) * (d_ff / 32));
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)sQ;
   const int nst = d_ff / QK;
-  const int col = n0 + 128 * (wave >> 1) + (lane & 31);  // column subtile j: col + 32 j
+  const int col = n0 + 128 * (wave & 1) + (lane & 31);  // column subtile j: col + 32 j
   for (int m0 = 0; m0 < n; m0 += QM) {
     const int rows = min(QM, n - m0);
     const int nsub = (rows + 31) >> 5;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 4; ++t) {
       const int r = q_xrow(wave, t, lane);
       L.xo[t] = (uint32_t)((size_t)(r0 + m0 + min(r, rows - 1)) * d_ff + q_xpiece(r, lane) * 16);
     }
-    L.xso = (uint32_t)((size_t)(r0 + m0 + min(64 * wave + lane, rows - 1)) * (d_ff / 32));
-    f32x16_t acc[4][4];
-    q_pass_n((nsub + 1) >> 1, acc, L, sQ, lds0, nst, wave, lane);
+    if (wave < 4) L.so = (uint32_t)((size_t)(r0 + m0 + min(64 * wave + lane, rows - 1)) * (d_ff / 32));
+    f32x16_t acc[2][4];
+    q_pass_n(q_na(nsub, wave), acc, L, sQ, lds0, nst, wave, lane);
     int g4 = grp * 4;
     asm volatile("" : "+v"(g4));
-    const int wr = wave & 1;
+    const int wr = wave >> 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (2 * i + wr >= nsub) continue;
+    for (int i = 0; i < 2; ++i) {
+      if (wr + 4 * i >= nsub) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = 32 * (2 * i + wr) + (v >> 2) * 8 + g4 + (v & 3);
+        const int row = 32 * (wr + 4 * i) + (v >> 2) * 8 + g4 + (v & 3);
         if (row < rows) {
           float* o = out + (size_t)(r0 + m0 + row) * d + col;
           o[0] = acc[i][0][v];
@@ -930,11 +938,11 @@ int launch_mx_ffn_mfma(const uint16_t* x, int T, int d, int d_ff, int k, const u
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (int rc = launch_mx_quant_bf16(x, T, d, xq, xs, s)) return rc;
   const int tiles_up = d_ff / 128, nb_up = ng * tiles_up;
-  timed_launch(mx_gateup_mfma_kernel, dim3(nb_up), dim3(256), s, ev, 0, (const uint8_t*)xq, (const uint8_t*)xs, T,
+  timed_launch(mx_gateup_mfma_kernel, dim3(nb_up), dim3(64 * QWAVES), s, ev, 0, (const uint8_t*)xq, (const uint8_t*)xs, T,
                d, d_ff, k, slots, group_slot, offsets, perm, g_begin, tiles_up, nb_up, hq, hs);
   if (int rc = launched("mx_gateup_mfma")) return rc;
   const int tiles_dn = d / 256, nb_dn = ng * tiles_dn;
-  timed_launch(mx_down_mfma_kernel, dim3(nb_dn), dim3(256), s, ev, 1, (const uint8_t*)hq, (const uint8_t*)hs, n_rows,
+  timed_launch(mx_down_mfma_kernel, dim3(nb_dn), dim3(64 * QWAVES), s, ev, 1, (const uint8_t*)hq, (const uint8_t*)hs, n_rows,
                d, d_ff,
                slots, group_slot, offsets, g_begin, tiles_dn, nb_dn, out);
   return launched("mx_down_mfma");
