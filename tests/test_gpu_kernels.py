@@ -133,6 +133,7 @@ def test_grouped_ffn_rows_form(d, d_ff, rows, split):
     (256, 512, [40, 1, 300, 77, 0]),    # more rows than one tile, a single row, an empty group
     (4096, 2048, [192, 250, 5]),        # prefill shape
     (2048, 768, [64, 130]),
+    (256, 512, [1100, 3, 0, 20]),       # one expert with five passes of rows (a skewed load)
 ])
 def test_grouped_ffn_mfma_form(d, d_ff, rows):
     _ffn_case(2, d, d_ff, rows)

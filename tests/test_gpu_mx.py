@@ -127,6 +127,7 @@ def test_mx_grouped_ffn_rows_form(d, d_ff, rows, split):
     (4096, 2048, [96, 260]),            # prefill shape
     (256, 128, [40, 300, 5]),           # one-stage down items, two-stage gate/up items
     (512, 1024, [(37 * i) % 300 for i in range(40)]),  # more blocks than compute units
+    (256, 512, [1100, 3, 0, 20]),       # one expert with five passes of rows (a skewed load)
 ])
 def test_mx_grouped_ffn_mfma_form(d, d_ff, rows):
     _mx_ffn_case(2, d, d_ff, rows)
