@@ -412,8 +412,9 @@ __global__ __launch_bounds__(256) void mx_quant_act_kernel(const In* __restrict_
 // ---- scaled-MFMA grouped FFN ---------------------------------------------------------
 // Block: 512 threads = 8 waves, two per SIMD.  One pass covers up to 256 rows of one
 // expert (8 row subtiles of 32) and 256 weight rows ("B columns"), so every weight
-// byte is read from HBM once per pass; the waves split them 4 x 2 (see q_stage).  K runs in stages of 128 elements
-// = two scaled MFMAs per row subtile and column subtile.  MFMA i (0, 1) of a stage
+// byte is read from HBM once per pass; the waves split them 4 x 2 (see q_stage).  K
+// runs in stages of 128 elements = two scaled MFMAs per row subtile and column
+// subtile.  MFMA i (0, 1) of a stage
 // takes as its K positions 0..31 the stage's block i and as positions 32..63 its
 // block i + 2 (any pairing is exact as long as both operands and both scales follow
 // it); then a lane's E2M1 codes for an MFMA are one 16-byte piece of a weight row.
@@ -425,8 +426,9 @@ __global__ __launch_bounds__(256) void mx_quant_act_kernel(const In* __restrict_
 // rows (waves 0-3) or 64 B columns (waves 4-7), all shared behind the stage barrier: 7
 // loads per wave per stage, spread over the stage's MFMAs, waited for by one explicit
 // `s_waitcnt vmcnt` at the top of the stage they feed.  With two waves per SIMD, one
-// wave's MFMAs run while the other waits on the issue of its loads.  (Loads into registers leave the waits to the compiler, which drains every
-// load at the head of the K loop: the memory latency then lands on every few stages.)
+// wave's MFMAs run while the other waits on the issue of its loads.  (Loads into
+// registers leave the waits to the compiler, which drains every load at the head of
+// the K loop: the memory latency then lands on every few stages.)
 //
 // Stage buffer (bytes): token-row codes, row r at 128 r with 16-byte piece p at
 // physical piece p ^ swz8(r) | their scales, 4 bytes per row (the stage's 4 blocks) |
@@ -938,13 +940,12 @@ int launch_mx_ffn_mfma(const uint16_t* x, int T, int d, int d_ff, int k, const u
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (int rc = launch_mx_quant_bf16(x, T, d, xq, xs, s)) return rc;
   const int tiles_up = d_ff / 128, nb_up = ng * tiles_up;
-  timed_launch(mx_gateup_mfma_kernel, dim3(nb_up), dim3(64 * QWAVES), s, ev, 0, (const uint8_t*)xq, (const uint8_t*)xs, T,
-               d, d_ff, k, slots, group_slot, offsets, perm, g_begin, tiles_up, nb_up, hq, hs);
+  timed_launch(mx_gateup_mfma_kernel, dim3(nb_up), dim3(64 * QWAVES), s, ev, 0, (const uint8_t*)xq,
+               (const uint8_t*)xs, T, d, d_ff, k, slots, group_slot, offsets, perm, g_begin, tiles_up, nb_up, hq, hs);
   if (int rc = launched("mx_gateup_mfma")) return rc;
   const int tiles_dn = d / 256, nb_dn = ng * tiles_dn;
-  timed_launch(mx_down_mfma_kernel, dim3(nb_dn), dim3(64 * QWAVES), s, ev, 1, (const uint8_t*)hq, (const uint8_t*)hs, n_rows,
-               d, d_ff,
-               slots, group_slot, offsets, g_begin, tiles_dn, nb_dn, out);
+  timed_launch(mx_down_mfma_kernel, dim3(nb_dn), dim3(64 * QWAVES), s, ev, 1, (const uint8_t*)hq,
+               (const uint8_t*)hs, n_rows, d, d_ff, slots, group_slot, offsets, g_begin, tiles_dn, nb_dn, out);
   return launched("mx_down_mfma");
 }
 
