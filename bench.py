@@ -305,6 +305,42 @@ def dma_h2d_rate(torch, nbytes=1 << 31, reps=3):
     return best
 
 
+def measured_peaks(torch, reps=5):
+    """The box's own ceilings next to the rated ones: an HBM copy of 2 GiB (read + write
+    bytes), a bf16 GEMM of 8192^3 (the library's), and a pinned host -> device copy; medians
+    over `reps` after a warm-up.  (A read stream of LDS-direct loads at one block per compute
+    unit, probed separately, reaches 6.0-6.4 TB/s.)"""
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return sorted(ts)[len(ts) // 2]
+    n = 1 << 31
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    b = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    t_gemm = timed(lambda: torch.matmul(a, b))
+    del a, b
+    return {"hbm_copy_GBs": round(2 * n / t_copy / 1e9, 1),
+            "bf16_gemm_TFLOPs": round(2.0 * m ** 3 / t_gemm / 1e12, 1),
+            "h2d_copy_GBs": round(dma_h2d_rate(torch) / 1e9, 1),
+            "rated": {"hbm_GBs": HBM_PEAK_GBS, "bf16_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                      "fp8_TFLOPs": MFMA_FP8_PEAK_TFLOPS, "pcie_gen5_x16_GBs": 63.0},
+            "note": "copy: read + write bytes of a 2 GiB device copy; GEMM: torch.matmul (hipBLASLt), "
+                    "contiguous operands; host copy: pinned memory by the copy engine"}
+
+
 def run_prefill(args, torch, ft, synth, HostPool):
     wl = synth.WORKLOADS["prefill8k-L43-d4096-E256-top6"]
     s = wl.shape
@@ -735,6 +771,8 @@ def main():
     ap.add_argument("--replay-prompt", type=int, default=512)
     ap.add_argument("--replay-decode", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", dest="peaks", action="store_false", default=True,
+                    help="skip the measured HBM, GEMM and host-copy ceilings")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--cpu-budget-1t-s", type=float, default=8.0)
     ap.add_argument("--counter-calibration", action="store_true",
@@ -782,6 +820,7 @@ def main():
     pre = run_prefill(args, torch, ft, synth, HostPool) if args.prefill else None
     mxr = run_mxfp4(args, torch, ft, synth, HostPool) if args.mxfp4 else None
     rep = run_placement(args, ft, synth) if args.replay else None
+    peaks = measured_peaks(torch) if args.peaks else None
     if dec is None:
         print(json.dumps({"profiling_run": True, "decode_L40": c2, "prefill": pre, "mxfp4": mxr,
                           "placement_replay": rep}), flush=True)
@@ -796,7 +835,7 @@ def main():
                    "pool_physical_layers": dec["L_phys"], "parallelism": "single-gpu"},
         "roofline": roof, "cpu_baseline": cpu, "decode": dec, "decode_graph": gdec, "decode_L40": c2,
         "prefill": pre, "mxfp4": mxr,
-        "placement_replay": rep,
+        "placement_replay": rep, "measured_peaks": peaks,
     }
     print(json.dumps(out), flush=True)
 
