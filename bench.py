@@ -248,6 +248,8 @@ def run_decode(args, torch, ft, synth, HostPool, workload=None, steps=None, warm
         "cpu_threads": args.cpu_threads,
         "miss_rate_reads": 1.0 - stats["read_hits"] / reads,
         "miss_rate_unique": stats["unique_misses"] / max(stats["unique_hits"] + stats["unique_misses"], 1),
+        "trace_reuse": trace_reuse(tr),
+        "miss_rate_context": "the pages' LRU miss rates on their own traces: 16 % and 39 % (context, not a target)",
         "fills_per_step": stats["fills"] / args.steps, "cpu_experts_per_step": stats["cpu_experts"] / args.steps,
         "h2d_GB_per_step": stats["h2d_bytes"] / args.steps / 1e9,
         "modelled_floor_ms_per_step": floor_s / args.steps * 1e3 if floor_s is not None else None,
@@ -303,6 +305,15 @@ def dma_h2d_rate(torch, nbytes=1 << 31, reps=3):
         best = max(best, nbytes / (a.elapsed_time(b) * 1e-3))
     del src, dst
     return best
+
+
+def trace_reuse(tr):
+    """Empirical step-to-step reuse of a routing trace [steps, L, B, k]: the fraction of a
+    step's experts (steps 1..) that its stream also took at the step before (the kept ones
+    plus chance redraws)."""
+    prev, cur = tr[:-1], tr[1:]
+    hit = (cur[..., :, None] == prev[..., None, :]).any(axis=-1)
+    return float(hit.mean()) if hit.size else None
 
 
 def measured_peaks(torch, reps=5):

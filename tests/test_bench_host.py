@@ -56,3 +56,13 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_trace_reuse_counts_experts_kept_from_the_step_before():
+    b = _bench()
+    # one layer, one stream, k = 2: step 1 keeps one of step 0's two experts, step 2 none
+    tr = np.array([[[[1, 2]]], [[[2, 3]]], [[[4, 5]]]], dtype=np.int16)
+    assert b.trace_reuse(tr) == pytest.approx(0.25)
+    # the same expert set in another order counts as fully reused
+    tr = np.array([[[[7, 9, 3]]], [[[3, 7, 9]]]], dtype=np.int16)
+    assert b.trace_reuse(tr) == pytest.approx(1.0)
