@@ -263,7 +263,8 @@ def test_mx_full_size_prefill_chunk_and_decode():
     8192-token chunk through two layers (double-buffered, aliased pool of two
     physical layers): every routed id bit-exact, y on tokens reaching every expert
     group and the tile edges; then 9 batch-1 decode steps over all 43 layers with the cache
-    of 1210 slots: every decision bit-exact, y on every layer of steps 0 and 8."""
+    of 1210 slots, resized at a safe point to 605 slots before step 5: every decision
+    bit-exact, across the resize too, and y on every layer of steps 0 and 8."""
     torch = torch_mod()
     wl = synth.WORKLOADS["mxfp4-prefill8k-L43-d4096-E256-top6"]
     s = wl.shape
@@ -302,7 +303,13 @@ def test_mx_full_size_prefill_chunk_and_decode():
         wd = synth.WORKLOADS["mxfp4-decode-L43-d4096-E256-top6"]
         tr = synth.trace_for(wd, steps=9)
         plan = ft.ft_plan()
+        small = None
         for st in range(9):  # decisions on every call; outputs on every layer of steps 0 and 8
+            if st == 5:
+                torch.cuda.synchronize()
+                small = torch.empty(605 * s.record_bytes, dtype=torch.uint8, device="cuda")
+                assert ft.ft_expert_cache_resize(eng.ctx, small, 605) == ft.FT_OK
+                ref_cache.resize(605)
             for l in range(s.L):
                 x = synth.tokens(wd, st, l, T=1)
                 wr = synth.router_weights(wd, l)
