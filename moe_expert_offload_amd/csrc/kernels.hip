@@ -16,7 +16,10 @@
 #include <cmath>
 #include <mutex>
 
+#include "device_common.h"
 #include "internal.h"
+
+using namespace ft::dev;
 
 namespace {
 
@@ -25,12 +28,6 @@ using ft::DevPlan;
 using ft::plan_term;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-constexpr int WAVE = 64;
-
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -40,39 +37,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Buffer loads over one expert record: a scalar resource (base, size in bytes) and a
-// 32-bit byte offset per lane; the hardware range check returns zeros for offsets
-// past the size, so masked pieces cost no branch (kOOB is past every record).
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-constexpr uint32_t kOOB = 0x80000000u;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
-}
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
-  return v;
-}
-
-// sum of the 8 products of two packed bf16x8 vectors, added into acc (any order)
-__device__ __forceinline__ float dot8(uint4 a, uint4 b, float acc) {
-  acc = fmaf(bf_lo(a.x), bf_lo(b.x), acc);
-  acc = fmaf(bf_hi(a.x), bf_hi(b.x), acc);
-  acc = fmaf(bf_lo(a.y), bf_lo(b.y), acc);
-  acc = fmaf(bf_hi(a.y), bf_hi(b.y), acc);
-  acc = fmaf(bf_lo(a.z), bf_lo(b.z), acc);
-  acc = fmaf(bf_hi(a.z), bf_hi(b.z), acc);
-  acc = fmaf(bf_lo(a.w), bf_lo(b.w), acc);
-  acc = fmaf(bf_hi(a.w), bf_hi(b.w), acc);
-  return acc;
-}
-
-// the same with the packed bf16 dot instruction (fp32 accumulation), no unpacking
+// sum of the 8 products of two packed bf16x8 vectors, added into acc (any order), with
+// the packed bf16 dot instruction (fp32 accumulation), no unpacking
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot8_pk(uint4 a, uint4 b, float acc) {
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x), acc, false);
@@ -94,17 +61,6 @@ __device__ __forceinline__ float dot8_f(uint4 a, float4 h0, float4 h1, float acc
   return acc;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
-// The same through the hardware exp2 and reciprocal (a few ulp), for values that are
-// rounded to bf16 right after (the prefill MFMA epilogue).
-__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
-
-// Blocks are dealt to the 8 XCDs round-robin; remap so that consecutive logical
-// blocks share an XCD (and its L2).
-__device__ __forceinline__ int xcd_logical_block(int b, int nb) {
-  const int q = nb >> 3, r = nb & 7, x = b & 7;
-  return x * q + (x < r ? x : r) + (b >> 3);
-}
 
 // ============================================================================
 // Router
@@ -1221,13 +1177,6 @@ __device__ __forceinline__ bf16x8_t lds_frag_w(const uint16_t* buf, int r, int p
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-// One 16-byte-per-lane load from buffer `rs` at byte offset off + kbytes into LDS
-// at byte address lds + 16 * lane.  Out-of-range offsets read zeros.
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t kbytes, uint32_t lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(m0), "v"(off), "s"(rs), "s"(kbytes) : "memory", "m0");
-}
 
 // Token rows: load q (0..3) of wave w covers buffer rows 16 (4w + q) + lane/4, physical
 // piece lane%4.  Weights: load u (0..7) of wave w covers buffer rows 64w + 8u + lane/8,
@@ -1555,13 +1504,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<float4*>(y + (size_t)t * d + c) = acc;
 }
 
-inline int launched(const char* what) {
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return ft::fail(FT_EHIP, std::string(what) + ": " + hipGetErrorString(e));
-  return FT_OK;
-}
-
-inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 
@@ -1683,29 +1625,6 @@ int launch_permute(const int32_t* key, int P, int n_groups, int32_t* offsets, in
 
 // Launches a kernel with dynamic shared memory; with timing events, start/stop
 // bracket the kernel itself.
-template <typename... KArgs, typename... Args>
-inline void timed_launch_shm(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shm, hipStream_t s,
-                             void* const* ev, int which, Args... args) {
-  if (ev) {
-    hipExtLaunchKernelGGL(kern, grid, block, shm, s, static_cast<hipEvent_t>(ev[2 * which]),
-                          static_cast<hipEvent_t>(ev[2 * which + 1]), 0, args...);
-  } else {
-    hipLaunchKernelGGL(kern, grid, block, shm, s, args...);
-  }
-}
-
-// Launches a kernel; with timing events, start/stop bracket the kernel itself.
-template <typename... KArgs, typename... Args>
-inline void timed_launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t s, void* const* ev,
-                         int which, Args... args) {
-  if (ev) {
-    hipExtLaunchKernelGGL(kern, grid, block, 0, s, static_cast<hipEvent_t>(ev[2 * which]),
-                          static_cast<hipEvent_t>(ev[2 * which + 1]), 0, args...);
-  } else {
-    hipLaunchKernelGGL(kern, grid, block, 0, s, args...);
-  }
-}
-
 int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* slots,
                     const int32_t* group_slot, const int32_t* offsets, const int32_t* perm,
                     int g_begin, int g_end, int max_rows, float* h, float* out, void* stream,

@@ -26,28 +26,14 @@
 #include <climits>
 #include <cmath>
 
+#include "device_common.h"
 #include "internal.h"
+
+using namespace ft::dev;
 
 namespace {
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-constexpr int WAVE = 64;
-
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
-  return v;
-}
-
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
-// The same through the hardware exp2 and reciprocal (a few ulp), for values that are
-// converted to MXFP8 right after (the prefill MFMA epilogue).
-__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // 2^(s - 127) for an E8M0 byte (s < 255).
 __device__ __forceinline__ float e8m0(uint32_t s) { return s ? __uint_as_float(s << 23) : 1.17549435e-38f * 0.5f; }
@@ -71,20 +57,8 @@ __device__ __forceinline__ float word_dot_bf16(uint32_t cw, const uint32_t (&xw)
   return acc;
 }
 
-// sum over the 32 elements of one weight block (16 code bytes) times 32 bf16 activations
-__device__ __forceinline__ float block_dot_bf16(uint4 codes, const uint16_t* __restrict__ xb) {
-  const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
-  float acc = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint4 xv = *reinterpret_cast<const uint4*>(xb + 8 * q);  // 8 bf16 = elements 8q..8q+7
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-    acc = word_dot_bf16(cw[q], xw, acc);
-  }
-  return acc;
-}
-
-// the same with the 32 activations already in registers (4 x 8 bf16)
+// sum over the 32 elements of one weight block (16 code bytes) times 32 bf16
+// activations held in registers (4 x 8 bf16, elements 8q .. 8q + 7 in xv[q])
 __device__ __forceinline__ float block_dot_bf16_r(uint4 codes, const uint4 (&xv)[4]) {
   const uint32_t cw[4] = {codes.x, codes.y, codes.z, codes.w};
   float acc = 0.0f;
@@ -150,18 +124,6 @@ __device__ __host__ inline MxRec mx_rec(int d, int d_ff) {
 // the sum of the row it lies in.  Both read the group's metadata in one round of
 // independent loads, then every code block and scale of the lane through a buffer
 // resource (masked ones read as zeros), before anything the arithmetic needs.
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-constexpr uint32_t kOOB = 0x80000000u;  // past every record: buffer loads return zeros
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
-}
-__device__ __forceinline__ uint32_t buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
-}
 
 template <int NB, int RG>  // NB: blocks per lane and row (d <= 2048 * NB); RG row pairs per wavefront
 __global__ __launch_bounds__(256) void mx_gateup_rows_kernel(
@@ -367,8 +329,6 @@ template <typename In>
 __device__ __forceinline__ float ld_act(const In* p);
 template <>
 __device__ __forceinline__ float ld_act<uint16_t>(const uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
-template <>
-__device__ __forceinline__ float ld_act<float>(const float* p) { return *p; }
 
 template <typename In>
 __global__ __launch_bounds__(256) void mx_quant_act_kernel(const In* __restrict__ in, int rows, int n,
@@ -447,26 +407,9 @@ constexpr int QLOADS = 7;                  // loads per wave per stage
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-__device__ __forceinline__ int xcd_logical_block(int b, int nb) {
-  const int q = nb >> 3, r = nb & 7, x = b & 7;
-  return x * q + (x < r ? x : r) + (b >> 3);
-}
-
 __device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int swz4(int c) { return ((c >> 1) ^ (c >> 3)) & 3; }
 
-// One load from buffer `rs` at byte offset off + kbytes into LDS at byte address
-// lds + 16 * lane (lds16) or lds + 4 * lane (lds4).  Out-of-range offsets read zeros.
-__device__ __forceinline__ void lds16(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t kbytes, uint32_t lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(m0), "v"(off), "s"(rs), "s"(kbytes) : "memory", "m0");
-}
-__device__ __forceinline__ void lds4(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t kbytes, uint32_t lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :: "s"(m0), "v"(off), "s"(rs), "s"(kbytes) : "memory", "m0");
-}
 
 // This lane's loads of one pass: buffer resources and byte offsets at K position 0.
 struct QLoads {
@@ -480,13 +423,13 @@ struct QLoads {
 // columns 64 (w - 4) .. +63 (waves 4-7).
 __device__ __forceinline__ void q_issue(const QLoads& L, int t, int st, uint32_t lb, int wave) {
   if (t < 4)
-    lds16(L.rx, L.xo[t], (uint32_t)st * QK, lb + (uint32_t)(4096 * wave + 1024 * t));
+    lds_load16(L.rx, L.xo[t], (uint32_t)st * QK, lb + (uint32_t)(4096 * wave + 1024 * t));
   else if (t < 6)
-    lds16(L.rw, L.wo[t - 4], (uint32_t)st * (QK / 2), lb + (uint32_t)(QWC + 2048 * wave + 1024 * (t - 4)));
+    lds_load16(L.rw, L.wo[t - 4], (uint32_t)st * (QK / 2), lb + (uint32_t)(QWC + 2048 * wave + 1024 * (t - 4)));
   else if (wave < 4)
-    lds4(L.rxs, L.so, (uint32_t)st * 4, lb + (uint32_t)(QXS + 256 * wave));
+    lds_load4(L.rxs, L.so, (uint32_t)st * 4, lb + (uint32_t)(QXS + 256 * wave));
   else
-    lds4(L.rw, L.so, (uint32_t)st * 4, lb + (uint32_t)(QWS + 256 * (wave - 4)));
+    lds_load4(L.rw, L.so, (uint32_t)st * 4, lb + (uint32_t)(QWS + 256 * (wave - 4)));
 }
 
 // Lane l of load t covers, for token-row codes, buffer row 32 w + 8 t + l/8 at physical
@@ -821,35 +764,6 @@ __global__ __launch_bounds__(512) void mx_down_mfma_kernel(
   }
 }
 
-inline int launched(const char* what) {
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return ft::fail(FT_EHIP, std::string(what) + ": " + hipGetErrorString(e));
-  return FT_OK;
-}
-
-inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-template <typename... KArgs, typename... Args>
-inline void timed_launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t s, void* const* ev, int which,
-                         Args... args) {
-  if (ev) {
-    hipExtLaunchKernelGGL(kern, grid, block, 0, s, static_cast<hipEvent_t>(ev[2 * which]),
-                          static_cast<hipEvent_t>(ev[2 * which + 1]), 0, args...);
-  } else {
-    hipLaunchKernelGGL(kern, grid, block, 0, s, args...);
-  }
-}
-
-template <typename... KArgs, typename... Args>
-inline void timed_launch_shm(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shm, hipStream_t s,
-                             void* const* ev, int which, Args... args) {
-  if (ev) {
-    hipExtLaunchKernelGGL(kern, grid, block, shm, s, static_cast<hipEvent_t>(ev[2 * which]),
-                          static_cast<hipEvent_t>(ev[2 * which + 1]), 0, args...);
-  } else {
-    hipLaunchKernelGGL(kern, grid, block, shm, s, args...);
-  }
-}
 
 }  // namespace
 
