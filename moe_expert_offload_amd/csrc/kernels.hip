@@ -974,9 +974,12 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* key, in
 // ============================================================================
 // Grouped SwiGLU FFN, row-streaming form (few tokens per expert)
 // ============================================================================
-// gate/up: one wavefront per row pair (gate row r, up row r).  Lane l reads the
-// 16-byte pieces l, l+64, ... of each row, so a wavefront streams 1 KB per load;
-// the rows are held in registers while every token of the group is applied to them.
+// gate/up: one wavefront per RG row pairs (gate and up rows r .. r + RG - 1; RG = 2 for
+// one token per group beyond d = 2048, where a wavefront's token row then serves twice
+// the weights: 0.64 -> 0.67 of HBM peak at the 43-layer d = 4096 shape; 1 elsewhere,
+// since at d = 2048 two pairs measured slower).  Lane l reads the 16-byte pieces l,
+// l+64, ... of each row, so a wavefront streams 1 KB per load; the rows are held in
+// registers while every token of the group is applied to them.
 // down: one wavefront per 4 consecutive rows of W_down, read as one contiguous span
 // (6 KB at d_ff = 768), each 16-byte piece added into the sum of the row it lies in;
 // the group's h rows are staged in LDS once per block (64 KB at most per batch).
@@ -984,7 +987,7 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* key, in
 // through a buffer resource (masked pieces read as zeros), weights before anything
 // the arithmetic needs.
 
-template <int NT, int JC>
+template <int NT, int JC, int RG = 1>
 __global__ __launch_bounds__(256) void ffn_gateup_rows_kernel(
     const uint16_t* __restrict__ x, int d, int d_ff, int k, const uint16_t* __restrict__ slots,
     size_t rec_elems, const int32_t* __restrict__ group_slot, const int32_t* __restrict__ offsets,
@@ -993,36 +996,47 @@ __global__ __launch_bounds__(256) void ffn_gateup_rows_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = g_begin + blockIdx.x / blocks_per_group;
-  const int row = (blockIdx.x % blocks_per_group) * 4 + wave;
+  const int row0 = ((blockIdx.x % blocks_per_group) * 4 + wave) * RG;
   const int glo = g_lo != nullptr ? *g_lo : INT_MIN;
   const int ghi = g_hi != nullptr ? *g_hi : INT_MAX;
   const int slot = group_slot[g];
   const int r0 = offsets[g];
   const int r1 = offsets[g + 1];
-  if (row >= d_ff || g < glo || g >= ghi || r1 <= r0) return;
+  if (row0 >= d_ff || g < glo || g >= ghi || r1 <= r0) return;
   const int n = r1 - r0;
   const __amdgpu_buffer_rsrc_t rec = buf_rsrc(slots + (size_t)slot * rec_elems, (uint32_t)(rec_elems * 2));
-  const uint32_t og = (uint32_t)row * (uint32_t)d * 2u;
-  const uint32_t ou = (uint32_t)(d_ff + row) * (uint32_t)d * 2u;
+  uint32_t og[RG], ou[RG];
+  bool rin[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    rin[r] = row0 + r < d_ff;
+    og[r] = (uint32_t)(row0 + r) * (uint32_t)d * 2u;
+    ou[r] = (uint32_t)(d_ff + row0 + r) * (uint32_t)d * 2u;
+  }
   const int J = (d + 511) >> 9;
   for (int tb = 0; tb < n; tb += NT) {
-    float ag[NT], au[NT];
+    float ag[NT][RG], au[NT][RG];
     const uint16_t* xr[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      ag[i] = 0.0f;
-      au[i] = 0.0f;
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        ag[i][r] = 0.0f;
+        au[i][r] = 0.0f;
+      }
       xr[i] = nullptr;
     }
     for (int j0 = 0; j0 < J; j0 += JC) {
-      uint4 gw[JC], uw[JC];
+      uint4 gw[RG][JC], uw[RG][JC];
 #pragma unroll
-      for (int jj = 0; jj < JC; ++jj) {
-        const int i0 = (j0 + jj) * 512 + lane * 8;
-        const bool in = (j0 + jj < J) && i0 < d;
-        gw[jj] = buf_ld16(rec, in ? og + (uint32_t)i0 * 2u : kOOB);
-        uw[jj] = buf_ld16(rec, in ? ou + (uint32_t)i0 * 2u : kOOB);
-      }
+      for (int r = 0; r < RG; ++r)
+#pragma unroll
+        for (int jj = 0; jj < JC; ++jj) {
+          const int i0 = (j0 + jj) * 512 + lane * 8;
+          const bool in = rin[r] && (j0 + jj < J) && i0 < d;
+          gw[r][jj] = buf_ld16(rec, in ? og[r] + (uint32_t)i0 * 2u : kOOB);
+          uw[r][jj] = buf_ld16(rec, in ? ou[r] + (uint32_t)i0 * 2u : kOOB);
+        }
       if (j0 == 0) {  // token rows, looked up once the first weights are in flight
 #pragma unroll
         for (int i = 0; i < NT; ++i)
@@ -1036,8 +1050,11 @@ __global__ __launch_bounds__(256) void ffn_gateup_rows_kernel(
           const int i0 = (j0 + jj) * 512 + lane * 8;
           if ((j0 + jj < J) && i0 < d) {
             const uint4 xv = ld16(xr[i] + i0);
-            ag[i] = dot8_pk(gw[jj], xv, ag[i]);
-            au[i] = dot8_pk(uw[jj], xv, au[i]);
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+              ag[i][r] = dot8_pk(gw[r][jj], xv, ag[i][r]);
+              au[i][r] = dot8_pk(uw[r][jj], xv, au[i][r]);
+            }
           }
         }
       }
@@ -1045,9 +1062,12 @@ __global__ __launch_bounds__(256) void ffn_gateup_rows_kernel(
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       if (tb + i >= n) continue;
-      const float zg = wave_sum(ag[i]);
-      const float zu = wave_sum(au[i]);
-      if (lane == 0) h[(size_t)(r0 + tb + i) * d_ff + row] = silu(zg) * zu;
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        const float zg = wave_sum(ag[i][r]);
+        const float zu = wave_sum(au[i][r]);
+        if (lane == 0 && rin[r]) h[(size_t)(r0 + tb + i) * d_ff + row0 + r] = silu(zg) * zu;
+      }
     }
   }
 }
@@ -1642,7 +1662,10 @@ int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
   const int bpg_dn = (d + 15) / 16;
   const int nt = max_rows <= 1 ? 1 : max_rows <= 2 ? 2 : max_rows <= 4 ? 4 : 8;
 #define FT_ROWS_LAUNCH(NT)                                                                          \
-  if (d <= 2048)                                                                                    \
+  if (NT == 1 && d > 2048)                                                                          \
+    timed_launch(ffn_gateup_rows_kernel<NT, 4, 2>, dim3(ng * ((d_ff + 7) / 8)), dim3(256), s, ev, 0, x, d, d_ff, \
+                 k, slots, rec_elems, group_slot, offsets, perm, g_begin, (d_ff + 7) / 8, h, g_lo, g_hi, one_token); \
+  else if (d <= 2048)                                                                               \
     timed_launch(ffn_gateup_rows_kernel<NT, 4>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
                  slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_lo, g_hi, one_token);             \
   else                                                                                              \
