@@ -410,7 +410,6 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 __device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int swz4(int c) { return ((c >> 1) ^ (c >> 3)) & 3; }
 
-
 // This lane's loads of one pass: buffer resources and byte offsets at K position 0.
 struct QLoads {
   __amdgpu_buffer_rsrc_t rx, rxs, rw;  // token-row codes, their scales, the expert record

@@ -79,6 +79,7 @@ def test_decode_ragged_shape_parity(T):
     (100, 1032, 6, 1), (100, 1032, 6, 3), (100, 1032, 6, 8),
     (256, 1032, 6, 1), (256, 1032, 6, 4), (256, 1032, 6, 8),
     (600, 520, 8, 1), (600, 520, 8, 3), (600, 520, 8, 13),
+    (600, 520, 8, 64),  # the largest call: 64 tokens x 8 = 512 routed pairs
 ])
 def test_decode_router_blocking_parity(E, d, k, T):
     wl = Workload(f"decode-E{E}-d{d}-top{k}", 20 + E % 7, Shape(2, E, d, 64, k), T, 0.5)

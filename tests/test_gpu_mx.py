@@ -154,7 +154,7 @@ def _compare_plan(plan, ref_plan, ref_idx, where):
 MXS = Workload("small-mxfp4", 13, Shape(3, 16, 256, 384, 4, True), 2, 0.5)
 
 
-@pytest.mark.parametrize("fq,T", [(20000, 2), (0, 1), (Q16, 4)])
+@pytest.mark.parametrize("fq,T", [(20000, 2), (0, 1), (Q16, 4), (20000, 64)])
 def test_mx_decode_trace_parity(fq, T):
     """Decode with MXFP4 experts: hits, fills and CPU-branch experts (in-kernel dequantisation)."""
     torch = torch_mod()
@@ -162,7 +162,7 @@ def test_mx_decode_trace_parity(fq, T):
     s = MXS.shape
     pool, wr = _mx_stack(MXS)
     N = 20
-    eng = Engine(s, pool, N, T_max=8, frac_q16=fq, min_fill=1 if fq else 0, max_fetch=-1 if fq else 0,
+    eng = Engine(s, pool, N, T_max=max(T, 8), frac_q16=fq, min_fill=1 if fq else 0, max_fetch=-1 if fq else 0,
                  cpu_threads=4)
     try:
         ref_cache = SlotTable(N, s.L, s.E)
