@@ -982,7 +982,8 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* key, in
 // registers while every token of the group is applied to them.
 // down: one wavefront per 4 consecutive rows of W_down, read as one contiguous span
 // (6 KB at d_ff = 768), each 16-byte piece added into the sum of the row it lies in;
-// the group's h rows are staged in LDS once per block (64 KB at most per batch).
+// the group's h rows are staged in LDS once per block (64 KB at most per batch), their
+// loads leaving together with the wave's first weight pieces.
 // Both read the group's metadata in one round of independent loads and the record
 // through a buffer resource (masked pieces read as zeros), weights before anything
 // the arithmetic needs.
@@ -1098,9 +1099,29 @@ __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
   const int per = min(NT, max(1, 16384 / d_ff));  // token rows per batch: at most 64 KB of h
   for (int tb = 0; tb < n; tb += per) {
     const int nt = min(per, n - tb);
+    const int tot = nt * d_ff;  // floats of h in this batch
+    const float* hb = h + (size_t)(r0 + tb) * d_ff;
+    // The batch's first 16 KB of h (4 pieces per thread, zeros past its end) and the
+    // wave's first 8 weight pieces are all requested before anything waits, h first:
+    // staging h then waits for h alone, and the weights' round trip overlaps it.
+    const __amdgpu_buffer_rsrc_t hrs = buf_rsrc(hb, (uint32_t)tot * 4u);
+    uint4 hv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) hv[u] = buf_ld16(hrs, (uint32_t)(threadIdx.x + 256 * u) * 16u);
+    uint4 wv[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int e0 = jj * 512 + lane * 8;
+      wv[jj] = buf_ld16(rec, (jj < J && e0 < span) ? base + (uint32_t)e0 * 2u : kOOB);
+    }
     __syncthreads();  // the previous batch's h is no longer read
-    for (int i = threadIdx.x * 4; i < nt * d_ff; i += 256 * 4)
-      *reinterpret_cast<float4*>(sh + i) = *reinterpret_cast<const float4*>(h + (size_t)(r0 + tb) * d_ff + i);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = (threadIdx.x + 256 * u) * 4;
+      if (i < tot) *reinterpret_cast<uint4*>(sh + i) = hv[u];
+    }
+    for (int i = (threadIdx.x + 1024) * 4; i < tot; i += 256 * 4)  // batches of more than 16 KB
+      *reinterpret_cast<float4*>(sh + i) = *reinterpret_cast<const float4*>(hb + i);
     __syncthreads();
     float acc[NT][RW];
 #pragma unroll
@@ -1108,11 +1129,12 @@ __global__ __launch_bounds__(256) void ffn_down_rows_kernel(
 #pragma unroll
       for (int r = 0; r < RW; ++r) acc[i][r] = 0.0f;
     for (int j0 = 0; j0 < J; j0 += 8) {
-      uint4 wv[8];
+      if (j0 > 0) {
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int e0 = (j0 + jj) * 512 + lane * 8;
-        wv[jj] = buf_ld16(rec, (j0 + jj < J && e0 < span) ? base + (uint32_t)e0 * 2u : kOOB);
+        for (int jj = 0; jj < 8; ++jj) {
+          const int e0 = (j0 + jj) * 512 + lane * 8;
+          wv[jj] = buf_ld16(rec, (j0 + jj < J && e0 < span) ? base + (uint32_t)e0 * 2u : kOOB);
+        }
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
