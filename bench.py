@@ -741,7 +741,7 @@ def run_config2(args, torch, ft, synth, HostPool):
     return out
 
 
-def main():
+def arg_parser() -> argparse.ArgumentParser:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=128)
@@ -790,7 +790,11 @@ def main():
                     help="only a plain device copy of known size, for rocprofv3 counter scaling")
     ap.add_argument("--skip-headline", action="store_true",
                     help="profiling runs of the other legs only: the headline decode is not run and no value is reported")
-    args = ap.parse_args()
+    return ap
+
+
+def main():
+    args = arg_parser().parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)

@@ -66,3 +66,25 @@ def test_trace_reuse_counts_experts_kept_from_the_step_before():
     # the same expert set in another order counts as fully reused
     tr = np.array([[[[7, 9, 3]]], [[[3, 7, 9]]]], dtype=np.int16)
     assert b.trace_reuse(tr) == pytest.approx(1.0)
+
+
+def test_profile_commands_run_committed_files_with_current_options():
+    """Every rocprofv3 command written in profiles/ runs bench.py (a committed file) with
+    options bench.py still accepts, so each summary can be re-made from the tree."""
+    import glob
+    import shlex
+    b = _bench()
+    seen = 0
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.txt"))):
+        for line in open(path):
+            if "rocprofv3 " not in line or " -- " not in line:
+                continue
+            prog = shlex.split(line.split(" -- ", 1)[1])
+            assert prog[:2] == ["python3", "-u"] and prog[2] == "bench.py", (path, line)
+            assert os.path.exists(os.path.join(ROOT, prog[2]))
+            try:
+                b.arg_parser().parse_args(prog[3:])
+            except SystemExit:
+                pytest.fail(f"{os.path.basename(path)}: bench.py no longer takes {' '.join(prog[3:])}")
+            seen += 1
+    assert seen >= 8
