@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <chrono>
 #include <cstring>
 #include <string>
@@ -156,7 +157,7 @@ struct ft_ctx {
   // device copy of the residency state and the device-side plan ([FT] §4.1)
   ft::DevCache dc{};
   int dev_cap = 0;               // slots the device arrays hold
-  bool dev_dirty = true;         // host state changed since the last upload
+  std::atomic<bool> dev_dirty{true};  // host state changed since the last upload (graph host nodes set it too)
   ft::DevPlan* d_plan = nullptr;  // device
   ft::DevPlan* h_plan = nullptr;  // pinned publication
 
@@ -880,7 +881,10 @@ struct ft_decode_graph {
     int layer;
   };
   std::vector<NodeArg> args;
-  std::atomic<int> status{FT_OK};  // first error a host node met since the last report
+  // first error a host node met since the last report, and its message; the message is
+  // written and read under the lock (host nodes run on the runtime's callback thread)
+  std::atomic<int> status{FT_OK};
+  std::mutex error_lock;
   std::string error;
   ft_plan plan{};
 };
@@ -901,8 +905,11 @@ void decode_graph_host_node(void* p) {
   auto failed = [&](int st, const char* msg, bool) {
     c->cache->clear_residency();
     c->dev_dirty = true;
-    int expected = FT_OK;
-    if (g->status.compare_exchange_strong(expected, st)) g->error = msg;
+    std::lock_guard<std::mutex> lk(g->error_lock);
+    if (g->status.load(std::memory_order_relaxed) == FT_OK) {
+      g->error = msg;
+      g->status.store(st, std::memory_order_release);
+    }
   };
   for (int i = 0; i < P; ++i)
     if (c->h_idx[i] < 0) return failed(FT_EINVAL, "decode graph: a token allows fewer than k experts", false);
@@ -1058,8 +1065,14 @@ int ft_decode_graph_create(ft_ctx_t c, int32_t T, const void* x, const void* con
 
 int ft_decode_graph_status(ft_decode_graph_t g) {
   if (!g) return fail(FT_EINVAL, "decode_graph_status: null");
-  const int st = g->status.exchange(FT_OK);
-  if (st != FT_OK) return fail(st, g->error);
+  std::string msg;
+  int st;
+  {
+    std::lock_guard<std::mutex> lk(g->error_lock);
+    st = g->status.exchange(FT_OK);
+    if (st != FT_OK) msg = g->error;
+  }
+  if (st != FT_OK) return fail(st, msg);
   return FT_OK;
 }
 
