@@ -979,10 +979,10 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* key, in
 // the weights: 0.64 -> 0.67 of HBM peak at the 43-layer d = 4096 shape; 1 elsewhere,
 // since at d = 2048 two pairs measured slower).  Lane l reads the 16-byte pieces l,
 // l+64, ... of each row, so a wavefront streams 1 KB per load; the rows are held in
-// registers while every token of the group is applied to them.  SX (calls of one
-// token, so every group is one row of x): the block stages that row in LDS once and
-// its 4 wavefronts read it from there instead of each loading it from memory, a
-// quarter of the x loads (0.67 -> 0.71 of HBM peak at d = 4096).
+// registers while every token of the group is applied to them.  SX: the block stages
+// the token rows of a batch in LDS once and its 4 wavefronts read them from there
+// instead of each loading them from memory, a quarter of the x loads (one token per
+// call: 0.68 -> 0.71 of HBM peak at d = 4096; 8 tokens: 71 -> 48 us per launch at d = 2048).
 // down: one wavefront per 4 consecutive rows of W_down, read as one contiguous span
 // (6 KB at d_ff = 768), each 16-byte piece added into the sum of the row it lies in;
 // the group's h rows are staged in LDS once per block (64 KB at most per batch), their
@@ -1020,61 +1020,138 @@ __global__ __launch_bounds__(256) void ffn_gateup_rows_kernel(
   }
   const int J = (d + 511) >> 9;
   if constexpr (SX) {
-    // one row per group: the block stages the token row in LDS once (its loads leave
-    // after the wave's first weight pieces), and its 4 wavefronts read it from there
-    extern __shared__ uint4 sxv[];  // d / 8 pieces of 8 bf16
-    const uint16_t* xrow = one_token ? x : x + (size_t)(perm[r0] / k) * d;
-    uint4 gw[RG][JC], uw[RG][JC];
+    // The rows of x of a batch of up to NT tokens of the group are staged in LDS once per
+    // block (their loads leave after the wavefront's first weight pieces) and its 4
+    // wavefronts read them from there instead of each loading them from memory.
+    extern __shared__ uint4 sxv[];  // [NT][d / 8] pieces of 8 bf16
+    const int dp = d >> 3;          // pieces per row
+    if constexpr (NT == 1) {
+      // calls of one token (the launcher's condition): every group is one row of x,
+      // which the block stages once, its loads leaving after the first weight pieces
+      const uint16_t* xrow = one_token ? x : x + (size_t)(perm[r0] / k) * d;
+      uint4 gw[RG][JC], uw[RG][JC];
 #pragma unroll
-    for (int r = 0; r < RG; ++r)
+      for (int r = 0; r < RG; ++r)
 #pragma unroll
-      for (int jj = 0; jj < JC; ++jj) {
-        const int i0 = jj * 512 + lane * 8;
-        const bool in = rin[r] && jj < J && i0 < d;
-        gw[r][jj] = buf_ld16(rec, in ? og[r] + (uint32_t)i0 * 2u : kOOB);
-        uw[r][jj] = buf_ld16(rec, in ? ou[r] + (uint32_t)i0 * 2u : kOOB);
-      }
-    const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(xrow, (uint32_t)d * 2u);
-    uint4 xs[4];
+        for (int jj = 0; jj < JC; ++jj) {
+          const int i0 = jj * 512 + lane * 8;
+          const bool in = rin[r] && jj < J && i0 < d;
+          gw[r][jj] = buf_ld16(rec, in ? og[r] + (uint32_t)i0 * 2u : kOOB);
+          uw[r][jj] = buf_ld16(rec, in ? ou[r] + (uint32_t)i0 * 2u : kOOB);
+        }
+      const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(xrow, (uint32_t)d * 2u);
+      uint4 xs[4];  // d <= 8192: at most 4 pieces per thread
 #pragma unroll
-    for (int u = 0; u < 4; ++u) xs[u] = buf_ld16(xrs, (uint32_t)(threadIdx.x + 256 * u) * 16u);
+      for (int u = 0; u < 4; ++u) xs[u] = buf_ld16(xrs, (uint32_t)(threadIdx.x + 256 * u) * 16u);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if ((int)threadIdx.x + 256 * u < d / 8) sxv[threadIdx.x + 256 * u] = xs[u];
-    __syncthreads();
-    float ag[RG], au[RG];
+      for (int u = 0; u < 4; ++u)
+        if ((int)threadIdx.x + 256 * u < dp) sxv[threadIdx.x + 256 * u] = xs[u];
+      __syncthreads();
+      float ag[RG], au[RG];
 #pragma unroll
-    for (int r = 0; r < RG; ++r) ag[r] = au[r] = 0.0f;
-    for (int j0 = 0; j0 < J; j0 += JC) {
-      if (j0 > 0) {
+      for (int r = 0; r < RG; ++r) ag[r] = au[r] = 0.0f;
+      for (int j0 = 0; j0 < J; j0 += JC) {
+        if (j0 > 0) {
 #pragma unroll
-        for (int r = 0; r < RG; ++r)
+          for (int r = 0; r < RG; ++r)
 #pragma unroll
-          for (int jj = 0; jj < JC; ++jj) {
-            const int i0 = (j0 + jj) * 512 + lane * 8;
-            const bool in = rin[r] && (j0 + jj < J) && i0 < d;
-            gw[r][jj] = buf_ld16(rec, in ? og[r] + (uint32_t)i0 * 2u : kOOB);
-            uw[r][jj] = buf_ld16(rec, in ? ou[r] + (uint32_t)i0 * 2u : kOOB);
-          }
-      }
+            for (int jj = 0; jj < JC; ++jj) {
+              const int i0 = (j0 + jj) * 512 + lane * 8;
+              const bool in = rin[r] && (j0 + jj < J) && i0 < d;
+              gw[r][jj] = buf_ld16(rec, in ? og[r] + (uint32_t)i0 * 2u : kOOB);
+              uw[r][jj] = buf_ld16(rec, in ? ou[r] + (uint32_t)i0 * 2u : kOOB);
+            }
+        }
 #pragma unroll
-      for (int jj = 0; jj < JC; ++jj) {
-        const int i0 = (j0 + jj) * 512 + lane * 8;
-        if ((j0 + jj < J) && i0 < d) {
-          const uint4 xv = sxv[(j0 + jj) * 64 + lane];
+        for (int jj = 0; jj < JC; ++jj) {
+          const int i0 = (j0 + jj) * 512 + lane * 8;
+          if ((j0 + jj < J) && i0 < d) {
+            const uint4 xv = sxv[(j0 + jj) * 64 + lane];
 #pragma unroll
-          for (int r = 0; r < RG; ++r) {
-            ag[r] = dot8_pk(gw[r][jj], xv, ag[r]);
-            au[r] = dot8_pk(uw[r][jj], xv, au[r]);
+            for (int r = 0; r < RG; ++r) {
+              ag[r] = dot8_pk(gw[r][jj], xv, ag[r]);
+              au[r] = dot8_pk(uw[r][jj], xv, au[r]);
+            }
           }
         }
       }
-    }
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      const float zg = wave_sum(ag[r]);
-      const float zu = wave_sum(au[r]);
-      if (lane == 0 && rin[r]) h[(size_t)r0 * d_ff + row0 + r] = silu(zg) * zu;
+      for (int r = 0; r < RG; ++r) {
+        const float zg = wave_sum(ag[r]);
+        const float zu = wave_sum(au[r]);
+        if (lane == 0 && rin[r]) h[(size_t)r0 * d_ff + row0 + r] = silu(zg) * zu;
+      }
+      return;
+    }
+    constexpr int SU = 8;  // staged pieces per thread: NT * d <= 16384 elements
+    for (int tb = 0; tb < n; tb += NT) {
+      const int nt = min(NT, n - tb);
+      uint4 gw[RG][JC], uw[RG][JC];
+#pragma unroll
+      for (int r = 0; r < RG; ++r)
+#pragma unroll
+        for (int jj = 0; jj < JC; ++jj) {
+          const int i0 = jj * 512 + lane * 8;
+          const bool in = rin[r] && jj < J && i0 < d;
+          gw[r][jj] = buf_ld16(rec, in ? og[r] + (uint32_t)i0 * 2u : kOOB);
+          uw[r][jj] = buf_ld16(rec, in ? ou[r] + (uint32_t)i0 * 2u : kOOB);
+        }
+      uint4 xs[SU];
+#pragma unroll
+      for (int u = 0; u < SU; ++u) {
+        const int q = threadIdx.x + 256 * u, i = q / dp;
+        const uint16_t* xrow = one_token ? x : x + (size_t)(perm[r0 + tb + min(i, nt - 1)] / k) * d;
+        xs[u] = q < nt * dp ? ld16(xrow + 8 * (q - i * dp)) : make_uint4(0, 0, 0, 0);
+      }
+      __syncthreads();  // the previous batch's rows are no longer read
+#pragma unroll
+      for (int u = 0; u < SU; ++u)
+        if ((int)threadIdx.x + 256 * u < nt * dp) sxv[threadIdx.x + 256 * u] = xs[u];
+      __syncthreads();
+      float ag[NT][RG], au[NT][RG];
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int r = 0; r < RG; ++r) ag[i][r] = au[i][r] = 0.0f;
+      for (int j0 = 0; j0 < J; j0 += JC) {
+        if (j0 > 0) {
+#pragma unroll
+          for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int jj = 0; jj < JC; ++jj) {
+              const int i0 = (j0 + jj) * 512 + lane * 8;
+              const bool in = rin[r] && (j0 + jj < J) && i0 < d;
+              gw[r][jj] = buf_ld16(rec, in ? og[r] + (uint32_t)i0 * 2u : kOOB);
+              uw[r][jj] = buf_ld16(rec, in ? ou[r] + (uint32_t)i0 * 2u : kOOB);
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < JC; ++jj) {
+          const int i0 = (j0 + jj) * 512 + lane * 8;
+          if ((j0 + jj < J) && i0 < d) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+              if (i >= nt) continue;
+              const uint4 xv = sxv[i * dp + (j0 + jj) * 64 + lane];
+#pragma unroll
+              for (int r = 0; r < RG; ++r) {
+                ag[i][r] = dot8_pk(gw[r][jj], xv, ag[i][r]);
+                au[i][r] = dot8_pk(uw[r][jj], xv, au[i][r]);
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        if (i >= nt) continue;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          const float zg = wave_sum(ag[i][r]);
+          const float zu = wave_sum(au[i][r]);
+          if (lane == 0 && rin[r]) h[(size_t)(r0 + tb + i) * d_ff + row0 + r] = silu(zg) * zu;
+        }
+      }
     }
     return;
   }
@@ -1746,26 +1823,25 @@ int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
   const int bpg_up = (d_ff + 3) / 4;
   const int bpg_dn = (d + 15) / 16;
   const int nt = max_rows <= 1 ? 1 : max_rows <= 2 ? 2 : max_rows <= 4 ? 4 : 8;
-  // one token: each group is that token's row of x, staged in LDS once per block
-  const bool sx = one_token && d <= 8192;
+  // the token rows of a batch staged in LDS once per block: in calls of one token (every
+  // group is its row) up to d = 8192, else while a batch's rows fit 32 KB
+  const bool one_row = one_token && d <= 8192;
+#define FT_GU_ROWS(NT_, JC_, RG_, SX_, BPG_, SHM_)                                                    \
+  timed_launch_shm(ffn_gateup_rows_kernel<NT_, JC_, RG_, SX_>, dim3(ng * (BPG_)), dim3(256), (SHM_), s, ev, 0, \
+                   x, d, d_ff, k, slots, rec_elems, group_slot, offsets, perm, g_begin, (BPG_), h, g_lo, g_hi, \
+                   one_token)
 #define FT_ROWS_LAUNCH(NT)                                                                          \
-  if (NT == 1 && sx && d > 2048)                                                                    \
-    timed_launch_shm(ffn_gateup_rows_kernel<NT, 4, 2, true>, dim3(ng * ((d_ff + 7) / 8)), dim3(256), (size_t)d * 2, \
-                 s, ev, 0, x, d, d_ff, k, slots, rec_elems, group_slot, offsets, perm, g_begin, (d_ff + 7) / 8, h, \
-                 g_lo, g_hi, one_token);                                                            \
-  else if (NT == 1 && sx)                                                                           \
-    timed_launch_shm(ffn_gateup_rows_kernel<NT, 4, 1, true>, dim3(ng * bpg_up), dim3(256), (size_t)d * 2, s, ev, \
-                 0, x, d, d_ff, k, slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_lo, g_hi, \
-                 one_token);                                                                        \
-  else if (NT == 1 && d > 2048)                                                                     \
-    timed_launch(ffn_gateup_rows_kernel<NT, 4, 2>, dim3(ng * ((d_ff + 7) / 8)), dim3(256), s, ev, 0, x, d, d_ff, \
-                 k, slots, rec_elems, group_slot, offsets, perm, g_begin, (d_ff + 7) / 8, h, g_lo, g_hi, one_token); \
-  else if (d <= 2048)                                                                               \
-    timed_launch(ffn_gateup_rows_kernel<NT, 4>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
-                 slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_lo, g_hi, one_token);             \
-  else                                                                                              \
-    timed_launch(ffn_gateup_rows_kernel<NT, 8>, dim3(ng * bpg_up), dim3(256), s, ev, 0, x, d, d_ff, k, \
-                 slots, rec_elems, group_slot, offsets, perm, g_begin, bpg_up, h, g_lo, g_hi, one_token);             \
+  if constexpr (NT == 1) {                                                                          \
+    if (one_row && d > 2048) FT_GU_ROWS(1, 4, 2, true, (d_ff + 7) / 8, (size_t)d * 2);             \
+    else if (one_row) FT_GU_ROWS(1, 4, 1, true, bpg_up, (size_t)d * 2);                             \
+    else if (d > 2048) FT_GU_ROWS(1, 4, 2, false, (d_ff + 7) / 8, 0);                               \
+    else FT_GU_ROWS(1, 4, 1, false, bpg_up, 0);                                                     \
+  } else {                                                                                          \
+    if (NT * d <= 16384 && d <= 2048) FT_GU_ROWS(NT, 4, 1, true, bpg_up, (size_t)NT * d * 2);      \
+    else if (NT * d <= 16384) FT_GU_ROWS(NT, 8, 1, true, bpg_up, (size_t)NT * d * 2);               \
+    else if (d <= 2048) FT_GU_ROWS(NT, 4, 1, false, bpg_up, 0);                                     \
+    else FT_GU_ROWS(NT, 8, 1, false, bpg_up, 0);                                                    \
+  }                                                                                                 \
   if (int rc = launched("ffn_gateup_rows")) return rc;                                              \
   timed_launch_shm(ffn_down_rows_kernel<NT>, dim3(ng * bpg_dn), dim3(256),                         \
                    (size_t)std::min(NT, std::max(1, 16384 / d_ff)) * d_ff * 4, s, ev, 1, d, d_ff, slots, \
@@ -1778,6 +1854,7 @@ int launch_ffn_rows(const uint16_t* x, int d, int d_ff, int k, const uint16_t* s
     default: { FT_ROWS_LAUNCH(8) }
   }
 #undef FT_ROWS_LAUNCH
+#undef FT_GU_ROWS
 }
 
 int launch_ffn_mfma(const uint16_t* x, int T, int d, int d_ff, int k, const uint16_t* slots,
