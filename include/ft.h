@@ -321,7 +321,10 @@ int ft_permute_noalloc(const int32_t* key, int32_t P, int32_t n_groups, int32_t*
  * x: device bf16 [T, d]; out: device fp32 [offsets[n_groups], d] (rows in perm
  * order); h_ws: device, offsets[n_groups] * d_ff * 4 bytes.  form: 0 auto, 1 the
  * bandwidth-bound row-streaming form (few tokens per expert), 2 the MFMA tile form
- * (many tokens per expert; needs d % 256 == 0 and d_ff % 128 == 0). */
+ * (many tokens per expert; needs d % 256 == 0 and d_ff % 128 == 0).
+ * max_rows_per_group: the most rows a group holds; the row form batches that many
+ * tokens per pass over the weights (a group holding more is still computed, in
+ * further passes). */
 int ft_grouped_ffn(const void* x, int32_t T, int32_t d, int32_t d_ff, int32_t k,
                    const void* slots, const int32_t* group_slot, const int32_t* offsets,
                    const int32_t* perm, int32_t n_groups, int32_t g_begin, int32_t g_end,

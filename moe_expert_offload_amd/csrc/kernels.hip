@@ -1027,60 +1027,66 @@ __global__ __launch_bounds__(256) void ffn_gateup_rows_kernel(
     const int dp = d >> 3;          // pieces per row
     if constexpr (NT == 1) {
       // calls of one token (the launcher's condition): every group is one row of x,
-      // which the block stages once, its loads leaving after the first weight pieces
-      const uint16_t* xrow = one_token ? x : x + (size_t)(perm[r0] / k) * d;
-      uint4 gw[RG][JC], uw[RG][JC];
+      // which the block stages once, its loads leaving after the first weight pieces;
+      // a group of more rows (the stated bound not kept) takes them one after another
+      auto one_row = [&](int t) {
+        const uint16_t* xrow = one_token ? x : x + (size_t)(perm[r0 + t] / k) * d;
+        uint4 gw[RG][JC], uw[RG][JC];
 #pragma unroll
-      for (int r = 0; r < RG; ++r)
+        for (int r = 0; r < RG; ++r)
 #pragma unroll
-        for (int jj = 0; jj < JC; ++jj) {
-          const int i0 = jj * 512 + lane * 8;
-          const bool in = rin[r] && jj < J && i0 < d;
-          gw[r][jj] = buf_ld16(rec, in ? og[r] + (uint32_t)i0 * 2u : kOOB);
-          uw[r][jj] = buf_ld16(rec, in ? ou[r] + (uint32_t)i0 * 2u : kOOB);
-        }
-      const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(xrow, (uint32_t)d * 2u);
-      uint4 xs[4];  // d <= 8192: at most 4 pieces per thread
+          for (int jj = 0; jj < JC; ++jj) {
+            const int i0 = jj * 512 + lane * 8;
+            const bool in = rin[r] && jj < J && i0 < d;
+            gw[r][jj] = buf_ld16(rec, in ? og[r] + (uint32_t)i0 * 2u : kOOB);
+            uw[r][jj] = buf_ld16(rec, in ? ou[r] + (uint32_t)i0 * 2u : kOOB);
+          }
+        const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(xrow, (uint32_t)d * 2u);
+        uint4 xs[4];  // d <= 8192: at most 4 pieces per thread
 #pragma unroll
-      for (int u = 0; u < 4; ++u) xs[u] = buf_ld16(xrs, (uint32_t)(threadIdx.x + 256 * u) * 16u);
+        for (int u = 0; u < 4; ++u) xs[u] = buf_ld16(xrs, (uint32_t)(threadIdx.x + 256 * u) * 16u);
+        if (t > 0) __syncthreads();  // the previous row is no longer read
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if ((int)threadIdx.x + 256 * u < dp) sxv[threadIdx.x + 256 * u] = xs[u];
-      __syncthreads();
-      float ag[RG], au[RG];
+        for (int u = 0; u < 4; ++u)
+          if ((int)threadIdx.x + 256 * u < dp) sxv[threadIdx.x + 256 * u] = xs[u];
+        __syncthreads();
+        float ag[RG], au[RG];
 #pragma unroll
-      for (int r = 0; r < RG; ++r) ag[r] = au[r] = 0.0f;
-      for (int j0 = 0; j0 < J; j0 += JC) {
-        if (j0 > 0) {
+        for (int r = 0; r < RG; ++r) ag[r] = au[r] = 0.0f;
+        for (int j0 = 0; j0 < J; j0 += JC) {
+          if (j0 > 0) {
 #pragma unroll
-          for (int r = 0; r < RG; ++r)
+            for (int r = 0; r < RG; ++r)
 #pragma unroll
-            for (int jj = 0; jj < JC; ++jj) {
-              const int i0 = (j0 + jj) * 512 + lane * 8;
-              const bool in = rin[r] && (j0 + jj < J) && i0 < d;
-              gw[r][jj] = buf_ld16(rec, in ? og[r] + (uint32_t)i0 * 2u : kOOB);
-              uw[r][jj] = buf_ld16(rec, in ? ou[r] + (uint32_t)i0 * 2u : kOOB);
-            }
-        }
+              for (int jj = 0; jj < JC; ++jj) {
+                const int i0 = (j0 + jj) * 512 + lane * 8;
+                const bool in = rin[r] && (j0 + jj < J) && i0 < d;
+                gw[r][jj] = buf_ld16(rec, in ? og[r] + (uint32_t)i0 * 2u : kOOB);
+                uw[r][jj] = buf_ld16(rec, in ? ou[r] + (uint32_t)i0 * 2u : kOOB);
+              }
+          }
 #pragma unroll
-        for (int jj = 0; jj < JC; ++jj) {
-          const int i0 = (j0 + jj) * 512 + lane * 8;
-          if ((j0 + jj < J) && i0 < d) {
-            const uint4 xv = sxv[(j0 + jj) * 64 + lane];
+          for (int jj = 0; jj < JC; ++jj) {
+            const int i0 = (j0 + jj) * 512 + lane * 8;
+            if ((j0 + jj < J) && i0 < d) {
+              const uint4 xv = sxv[(j0 + jj) * 64 + lane];
 #pragma unroll
-            for (int r = 0; r < RG; ++r) {
-              ag[r] = dot8_pk(gw[r][jj], xv, ag[r]);
-              au[r] = dot8_pk(uw[r][jj], xv, au[r]);
+              for (int r = 0; r < RG; ++r) {
+                ag[r] = dot8_pk(gw[r][jj], xv, ag[r]);
+                au[r] = dot8_pk(uw[r][jj], xv, au[r]);
+              }
             }
           }
         }
-      }
 #pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        const float zg = wave_sum(ag[r]);
-        const float zu = wave_sum(au[r]);
-        if (lane == 0 && rin[r]) h[(size_t)r0 * d_ff + row0 + r] = silu(zg) * zu;
-      }
+        for (int r = 0; r < RG; ++r) {
+          const float zg = wave_sum(ag[r]);
+          const float zu = wave_sum(au[r]);
+          if (lane == 0 && rin[r]) h[(size_t)(r0 + t) * d_ff + row0 + r] = silu(zg) * zu;
+        }
+      };
+      one_row(0);
+      for (int t = 1; t < n; ++t) one_row(t);
       return;
     }
     constexpr int SU = 8;  // staged pieces per thread: NT * d <= 16384 elements

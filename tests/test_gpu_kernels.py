@@ -84,7 +84,7 @@ def test_permute_bit_exact(P, G):
         assert np.array_equal(host(inv)[:P], r_inv)
 
 
-def _ffn_case(form, d, d_ff, rows, k=2, split=None, seed=0):
+def _ffn_case(form, d, d_ff, rows, k=2, split=None, seed=0, max_rows=None):
     torch = torch_mod()
     _say("ffn", form, d, d_ff, rows, split)
     rng = generator(92, seed, d, d_ff, len(rows))
@@ -102,7 +102,7 @@ def _ffn_case(form, d, d_ff, rows, k=2, split=None, seed=0):
     args = (dev_u16(x), T, d, d_ff, k, dev_u16(recs), dev(group_slot), dev(offsets), dev(pair_ids), G)
     ranges = [(0, G)] if split is None else [(0, split), (split, G)]
     for g0, g1 in ranges:
-        ft.ft_grouped_ffn(*args, g0, g1, max(rows), h, out, form)
+        ft.ft_grouped_ffn(*args, g0, g1, max(rows) if max_rows is None else max_rows, h, out, form)
     torch.cuda.synchronize()
     got = host(out)[:total]
     x64 = bf16_to_f64(x)
@@ -127,6 +127,20 @@ def _ffn_case(form, d, d_ff, rows, k=2, split=None, seed=0):
 ])
 def test_grouped_ffn_rows_form(d, d_ff, rows, split):
     _ffn_case(1, d, d_ff, rows, split=split)
+
+
+# One token (T = 1: every pair is token 0) takes the form that stages the token row in
+# LDS once per block; groups of one row, and groups of more rows than the stated bound of
+# rows per group (the form then takes them one after another).
+@pytest.mark.parametrize("d,d_ff,rows,max_rows", [
+    (4096, 2048, [1, 1, 1, 1], 1),
+    (4096, 2048, [1, 3], 1),
+    (2048, 768, [2, 1, 1], 1),
+    (4096, 2048, [3, 1], 2),            # batched form, a group above the bound
+])
+def test_grouped_ffn_rows_form_one_token(d, d_ff, rows, max_rows):
+    assert sum(rows) == 4
+    _ffn_case(1, d, d_ff, rows, k=4, max_rows=max_rows)
 
 
 @pytest.mark.parametrize("d,d_ff,rows", [
